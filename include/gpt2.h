@@ -1,0 +1,165 @@
+/* gpt2.h -- C ABI of the MI355X (gfx950) GPT-2 training-step library.
+ *
+ * One training step is forward -> backward -> AdamW over a single flat device
+ * arena that the caller allocates once ("1000 行 C 代码完成 GPT-2 训练的 LLM.c":
+ * all memory is taken in one 1D block up front, so nothing is allocated or freed
+ * while training and batches just stream through).  The model is GPT-2 as the
+ * pages describe it: token + position embedding ("GPT-2 from scratch with torch",
+ * token/position embedding), L pre-norm blocks x = x + attn(ln_1(x)),
+ * x = x + mlp(ln_2(x)) (same page, Transformer block), causal multi-head
+ * self-attention with scores scaled by 1/sqrt(head size) (same page, 自注意力;
+ * "从头搭建GPT(Andrej Karpathy) 笔记", attention中为什么要做scaling), a tanh-GELU MLP
+ * of width 4C (前馈网络（MLP）; the GELU formula in the comment thread of
+ * "GPT-2ベースの3000バイトCで実装されたChatGPTクローン"), a final LayerNorm, logits
+ * from the token-embedding matrix (tied lm_head, no bias: 3000-byte C page,
+ * Transformer本体), and mean softmax cross-entropy over all B*T next-token
+ * targets (CSDN notes, 计算loss).
+ *
+ * Conventions for every entry point
+ *  - Returns a gpt2_status; nothing throws across the ABI.  On a non-OK status
+ *    gpt2_last_error() returns a message (thread-local, valid until the next call
+ *    on the same thread).
+ *  - Device pointers are HIP device addresses; `stream` is a hipStream_t passed as
+ *    void* (NULL = the null stream).  Every call only enqueues work on `stream`
+ *    and never synchronises; calls on one arena must be ordered by the caller
+ *    (use one stream).
+ *  - The library never allocates or frees device memory.
+ */
+#ifndef GPT2_MI355X_H
+#define GPT2_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Model hyper-parameters, named as in the llm.c run banner
+ * ("1000 行 C 代码...", 快速开始吧！: max_seq_len, vocab_size, num_layers,
+ * num_heads, channels). */
+typedef struct gpt2_config {
+    int32_t max_seq_len;
+    int32_t vocab_size;
+    int32_t num_layers;
+    int32_t num_heads;
+    int32_t channels;
+} gpt2_config;
+
+/* Arithmetic mode.
+ *  GPT2_FP32: weights, activations and GEMM inputs fp32 (fp32 MFMA).
+ *  GPT2_BF16: bf16 weight copy and bf16 activations as GEMM/attention inputs,
+ *             fp32 accumulation, fp32 master weights, gradients, AdamW moments,
+ *             LayerNorm statistics, attention log-sum-exp and losses. */
+enum gpt2_dtype { GPT2_FP32 = 0, GPT2_BF16 = 1 };
+
+enum gpt2_status {
+    GPT2_OK = 0,
+    GPT2_E_INVAL = -1, /* bad argument or configuration                          */
+    GPT2_E_SIZE = -2,  /* device buffer smaller than gpt2_alloc_arena requires    */
+    GPT2_E_ALIGN = -3, /* device buffer not 256-byte aligned                       */
+    GPT2_E_STATE = -4, /* call out of order (e.g. backward without a loss forward) */
+    GPT2_E_HIP = -5    /* a HIP launch or runtime call failed                      */
+};
+
+typedef struct gpt2_arena gpt2_arena; /* opaque host-side handle */
+
+/* Lays out (and validates) an arena for `cfg` at batch B, sequence length T.
+ *
+ *  cfg          model shape; needs channels % num_heads == 0, channels % 8 == 0,
+ *               head size (channels / num_heads) <= 128, 1 <= T <= max_seq_len,
+ *               B >= 1, vocab_size >= 2.
+ *  dtype        gpt2_dtype.
+ *  device_base  caller-owned device memory (256-byte aligned), or NULL to only
+ *               query the size.  The caller keeps ownership; it must outlive the
+ *               handle and must be zero-filled before the first AdamW step (the
+ *               moments start at zero).
+ *  device_bytes size of device_base.
+ *  required_bytes  (out, may be NULL) bytes the layout needs.
+ *  out          (out) the handle, or NULL on error / size query.
+ * Errors: GPT2_E_INVAL for a bad shape or dtype, GPT2_E_SIZE if device_bytes is
+ * too small, GPT2_E_ALIGN if device_base is misaligned. */
+int gpt2_alloc_arena(const gpt2_config* cfg, int32_t B, int32_t T, int32_t dtype,
+                     void* device_base, size_t device_bytes, size_t* required_bytes,
+                     gpt2_arena** out);
+
+/* Releases the host handle only (never the device memory). NULL is a no-op. */
+int gpt2_free_arena(gpt2_arena* arena);
+
+/* Refreshes every derived copy of the fp32 master parameters (the bf16 working
+ * copy in GPT2_BF16 mode; nothing in GPT2_FP32 mode).  Call after writing the
+ * master parameters directly (e.g. loading weights). */
+int gpt2_sync_weights(gpt2_arena* arena, void* stream);
+
+/* Forward pass.
+ *  d_inputs   device int32 [B, T] token ids, row-major, each in [0, vocab_size).
+ *  d_targets  device int32 [B, T] next-token ids (inputs shifted by one), or NULL.
+ * Without targets the logits [B*T, padded_vocab] are left in GPT2_T_LOGITS.
+ * With targets the fused softmax-cross-entropy writes per-position losses
+ * (GPT2_T_LOSSES), their mean (GPT2_T_LOSS) and overwrites GPT2_T_LOGITS with
+ * d loss / d logits, ready for gpt2_backward.  Ids are not range-checked on the
+ * device: an id outside [0, vocab_size) is undefined behaviour (the Python
+ * binding checks them on the host).  Both arrays must stay valid until the
+ * enqueued work has run (the backward pass reads d_inputs again). */
+int gpt2_forward(gpt2_arena* arena, const int32_t* d_inputs, const int32_t* d_targets, void* stream);
+
+/* Backward pass of the last forward (which must have had targets, else
+ * GPT2_E_STATE).  Overwrites every fp32 parameter gradient (GPT2_T_GRADS): one
+ * micro-batch per step, no accumulation. */
+int gpt2_backward(gpt2_arena* arena, void* stream);
+
+/* AdamW over every parameter ("1000 行 C 代码...": the loop ends with an Adam
+ * update; decoupled weight decay, bias correction, t counted from 1):
+ *   m = beta1 m + (1-beta1) g;  v = beta2 v + (1-beta2) g^2
+ *   theta -= lr * ( m/(1-beta1^t) / (sqrt(v/(1-beta2^t)) + eps) + weight_decay * theta )
+ * then refreshes the bf16 copy (round to nearest even) in GPT2_BF16 mode.
+ * Errors: GPT2_E_INVAL if step < 1. */
+int gpt2_adamw_step(gpt2_arena* arena, float lr, float beta1, float beta2, float eps,
+                    float weight_decay, int32_t step, void* stream);
+
+/* Tensor ids for gpt2_tensor_info.  Model-level tensors ignore `layer`;
+ * per-layer tensors need 0 <= layer < num_layers. */
+enum gpt2_tensor_id {
+    GPT2_T_PARAMS = 0,      /* fp32 [num_parameters] master weights                    */
+    GPT2_T_GRADS = 1,       /* fp32 [num_parameters]                                   */
+    GPT2_T_ADAM_M = 2,      /* fp32 [num_parameters]                                   */
+    GPT2_T_ADAM_V = 3,      /* fp32 [num_parameters]                                   */
+    GPT2_T_PARAMS_BF16 = 4, /* bf16 [num_parameters] working copy (GPT2_BF16 only)     */
+    GPT2_T_ENCODED = 5,     /* act [B*T, C] embedding output                           */
+    GPT2_T_LNF = 6,         /* act [B*T, C] final LayerNorm output                     */
+    GPT2_T_LNF_STATS = 7,   /* fp32 [B*T, 2] (mean, 1/std)                             */
+    GPT2_T_LOGITS = 8,      /* act [B*T, padded_vocab]: logits, or dlogits (see forward) */
+    GPT2_T_LOSSES = 9,      /* fp32 [B*T]                                              */
+    GPT2_T_LOSS = 10,       /* fp32 [1] mean loss                                      */
+    /* per layer */
+    GPT2_T_LN1 = 16,        /* act [B*T, C]                                            */
+    GPT2_T_LN1_STATS = 17,  /* fp32 [B*T, 2]                                           */
+    GPT2_T_QKV = 18,        /* act [B*T, 3C] columns q | k | v, head h at h*hs         */
+    GPT2_T_ATTY = 19,       /* act [B*T, C] attention output, heads side by side       */
+    GPT2_T_ATT_LSE = 20,    /* fp32 [B, NH, T] log-sum-exp of each scaled score row    */
+    GPT2_T_RESIDUAL2 = 21,  /* act [B*T, C] x + attn                                   */
+    GPT2_T_LN2 = 22,        /* act [B*T, C]                                            */
+    GPT2_T_LN2_STATS = 23,  /* fp32 [B*T, 2]                                           */
+    GPT2_T_FCH = 24,        /* act [B*T, 4C] pre-GELU                                  */
+    GPT2_T_FCH_GELU = 25,   /* act [B*T, 4C]                                           */
+    GPT2_T_RESIDUAL3 = 26   /* act [B*T, C] block output                               */
+};
+
+/* Where a tensor lives in the arena.  All outputs may be NULL.
+ *  byte_offset  from device_base (256-byte aligned)
+ *  rows, cols   logical shape; row_stride >= cols elements between rows
+ *  dtype        GPT2_FP32 or GPT2_BF16 ("act" tensors follow the arena dtype)
+ * Errors: GPT2_E_INVAL for an unknown id, a bad layer, or PARAMS_BF16 in fp32 mode. */
+int gpt2_tensor_info(const gpt2_arena* arena, int32_t tensor_id, int32_t layer, size_t* byte_offset,
+                     int64_t* rows, int64_t* cols, int64_t* row_stride, int32_t* dtype);
+
+/* Number of parameters (equals the llm.c banner's num_parameters for GPT-2 124M). */
+int64_t gpt2_num_parameters(const gpt2_config* cfg);
+
+/* Message for the last non-OK status on this thread ("" if none). */
+const char* gpt2_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GPT2_MI355X_H */

@@ -1,0 +1,176 @@
+"""ctypes front end of the GPT-2 training-step oracle (test infrastructure only).
+
+Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The GPU library never imports it, and it
+imports nothing from the GPU library.
+
+Parity status of each oracle function (pins live in tests/test_oracle_pins.py):
+every forward layer, every backward formula and the AdamW update are pinned
+(closed forms, printed integers, invariants, central finite differences and an
+independent autograd cross-check); nothing here is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "gpt2_oracle.cpp")
+LIB = os.path.join(HERE, "libgpt2_oracle.so")
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle into oracle/libgpt2_oracle.so with g++ and OpenMP."""
+    if not force and os.path.exists(LIB):
+        return LIB
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = ["g++", "-O3", "-march=x86-64-v3", "-fopenmp", "-fPIC", "-shared", "-std=c++17",
+           "-Wall", SRC, "-o", tmp]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB):
+            build()
+        L = ctypes.CDLL(LIB)
+        i64, i32, dbl, vp, cp = ctypes.c_int64, ctypes.c_int, ctypes.c_double, ctypes.c_void_p, ctypes.c_char_p
+        L.orc_last_error.restype = cp
+        L.orc_num_parameters.argtypes = [i32] * 5
+        L.orc_num_parameters.restype = i64
+        L.orc_num_activations.argtypes = [i32] * 7
+        L.orc_num_activations.restype = i64
+        L.orc_create.argtypes = [i32] * 8
+        L.orc_create.restype = vp
+        L.orc_destroy.argtypes = [vp]
+        L.orc_set_vec.argtypes = [vp, cp, vp, i64]
+        L.orc_set_vec_f32.argtypes = [vp, cp, vp, i64]
+        L.orc_get_vec.argtypes = [vp, cp, vp, i64]
+        L.orc_act_numel.argtypes = [vp, cp, i32]
+        L.orc_act_numel.restype = i64
+        L.orc_get_act.argtypes = [vp, cp, i32, vp, i64]
+        L.orc_forward.argtypes = [vp, vp, vp]
+        L.orc_forward.restype = dbl
+        L.orc_backward.argtypes = [vp]
+        L.orc_adamw.argtypes = [vp, dbl, dbl, dbl, dbl, dbl, i32]
+        L.orc_gelu.argtypes = [vp, vp, i64]
+        L.orc_gelu_grad.argtypes = [vp, vp, i64]
+        L.orc_num_threads.restype = i32
+        _lib = L
+    return _lib
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def num_parameters(m) -> int:
+    return int(lib().orc_num_parameters(m.vocab_size, m.max_seq_len, m.num_layers, m.num_heads, m.channels))
+
+
+def num_activations(m, B: int, T: int) -> int:
+    return int(lib().orc_num_activations(m.vocab_size, m.max_seq_len, m.num_layers, m.num_heads, m.channels, B, T))
+
+
+def gelu(x) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    y = np.empty_like(x)
+    lib().orc_gelu(_ptr(x), _ptr(y), x.size)
+    return y
+
+
+def gelu_grad(x) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    y = np.empty_like(x)
+    lib().orc_gelu_grad(_ptr(x), _ptr(y), x.size)
+    return y
+
+
+def num_threads() -> int:
+    return int(lib().orc_num_threads())
+
+
+class Oracle:
+    """One oracle model instance: parameters, AdamW state and the plain activation set.
+
+    prec: "f64" (the parity reference) or "f32" (the fp32 CPU trainer).
+    """
+
+    def __init__(self, m, B: int, T: int, prec: str = "f64"):
+        self.m, self.B, self.T = m, B, T
+        p = {"f32": 0, "f64": 1}[prec]
+        h = lib().orc_create(p, m.vocab_size, m.max_seq_len, m.num_layers, m.num_heads, m.channels, B, T)
+        if not h:
+            raise ValueError(lib().orc_last_error().decode())
+        self.h = h
+        self.n_params = num_parameters(m)
+
+    def close(self):
+        if self.h:
+            lib().orc_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def set(self, name: str, values):
+        a = np.asarray(values)
+        if a.dtype == np.float32:
+            a = np.ascontiguousarray(a)
+            rc = lib().orc_set_vec_f32(self.h, name.encode(), _ptr(a), a.size)
+        else:
+            a = np.ascontiguousarray(a, dtype=np.float64)
+            rc = lib().orc_set_vec(self.h, name.encode(), _ptr(a), a.size)
+        if rc:
+            raise ValueError(lib().orc_last_error().decode())
+
+    def get(self, name: str) -> np.ndarray:
+        out = np.empty(self.n_params, dtype=np.float64)
+        if lib().orc_get_vec(self.h, name.encode(), _ptr(out), out.size):
+            raise ValueError(lib().orc_last_error().decode())
+        return out
+
+    def act(self, name: str, layer: int = 0) -> np.ndarray:
+        n = lib().orc_act_numel(self.h, name.encode(), layer)
+        if n < 0:
+            raise KeyError(f"{name}[{layer}]")
+        out = np.empty(n, dtype=np.float64)
+        if lib().orc_get_act(self.h, name.encode(), layer, _ptr(out), n):
+            raise ValueError(lib().orc_last_error().decode())
+        return out
+
+    def forward(self, inputs, targets=None) -> float:
+        inp = np.ascontiguousarray(inputs, dtype=np.int32)
+        assert inp.size == self.B * self.T
+        tgt = None if targets is None else np.ascontiguousarray(targets, dtype=np.int32)
+        loss = lib().orc_forward(self.h, _ptr(inp), None if tgt is None else _ptr(tgt))
+        if loss != loss:
+            raise ValueError(lib().orc_last_error().decode())
+        return float(loss)
+
+    def backward(self):
+        if lib().orc_backward(self.h):
+            raise RuntimeError(lib().orc_last_error().decode())
+
+    def adamw(self, lr, beta1, beta2, eps, weight_decay, step: int):
+        if lib().orc_adamw(self.h, lr, beta1, beta2, eps, weight_decay, step):
+            raise ValueError(lib().orc_last_error().decode())
+
+    def step(self, inputs, targets, w, t: int) -> float:
+        """forward + backward + AdamW with the workload's hyper-parameters; returns the loss."""
+        loss = self.forward(inputs, targets)
+        self.backward()
+        self.adamw(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, t)
+        return loss
