@@ -1,0 +1,177 @@
+#!/usr/bin/env python3
+"""GPT-2 training-step benchmark on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is gpt2_forward (with targets) + gpt2_backward + gpt2_adamw_step over one
+synthetic batch (seeded weights and token ids, inputs resident in HBM before the
+timed region).  Prints ONE JSON line on stdout: whole-job training tokens/s, the
+roofline position of the dominant kernel (timed live with the library's HIP-event
+launch profiler) and the CPU oracle's throughput on a bounded sample.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "train tokens/sec (fwd+bwd+AdamW) GPT-2 124M B=8 T=1024; % MFMA peak"
+PEAK_TFLOPS = {"bf16": 2500.0, "fp32": 157.3}   # MI355X dense MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def model_flops_per_step(m, B, T):
+    """(6 N + 6 L C (T+1)) B T: dense matmul flops of forward+backward for N
+    parameters, plus causal attention counting only unmasked pairs."""
+    import synth
+    N = synth.num_parameters(m)
+    return (6.0 * N + 6.0 * m.num_layers * m.channels * (T + 1)) * B * T
+
+
+def cpu_baseline(w, params, x, y, budget_s=10.0, T_sample=256):
+    """The float oracle on a bounded sample of the workload: the first T_sample
+    tokens of batch row 0, full forward + backward + AdamW, repeated until about
+    budget_s seconds have passed."""
+    import oracle
+    T_sample = min(T_sample, w.T)
+    o = oracle.Oracle(w.model, 1, T_sample, "f32")
+    o.set("params", params)
+    xs, ys = x[:1, :T_sample], y[:1, :T_sample]
+    steps, t0 = 0, time.perf_counter()
+    while True:
+        o.step(xs, ys, w, steps + 1)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or steps >= 20:
+            break
+    o.close()
+    return {"value": steps * T_sample / el, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"float oracle, {steps} full step(s) (fwd+bwd+AdamW) on batch row 0, first {T_sample} "
+                      f"tokens of the {w.name} workload, {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gpt2_124m_b8t1024_bf16")
+    ap.add_argument("--profile-steps", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel-table", default=None, help="write the per-kernel profile as JSON here")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build runs the training step on a single MI355X; "
+              "multi-GPU runs are not part of it.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    from transformer_lm_fwd_amd import Arena, binding
+
+    w = synth.WORKLOADS[args.workload]
+    m = w.model
+    t0 = time.time()
+    params = synth.init_params(m)
+    x, y = synth.inputs_targets(w)
+    log(f"[bench] {w.name}: params generated in {time.time() - t0:.1f} s")
+    torch.cuda.set_device(0)
+    arena = Arena(m, w.B, w.T, w.dtype)
+    arena.load_params(params)
+    xi = torch.from_numpy(x).to(torch.int32).cuda()
+    yi = torch.from_numpy(y).to(torch.int32).cuda()
+    t = 0
+    # warm-up (the first call also checks the id range on the host)
+    for i in range(max(1, args.warmup)):
+        t += 1
+        arena.step(xi, yi, w, t, check_ids=(i == 0))
+    torch.cuda.synchronize()
+    first_loss = arena.loss()
+    log(f"[bench] warm-up done, loss {first_loss:.4f}")
+
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        t += 1
+        arena.step(xi, yi, w, t, check_ids=False)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end)
+    ms_per_step = ms / args.steps
+    loss = arena.loss()
+    if not math.isfinite(loss):
+        raise SystemExit(f"non-finite loss {loss}")
+    tokens = w.B * w.T * args.steps
+    value = tokens / (ms / 1e3)
+    F = model_flops_per_step(m, w.B, w.T)
+    mfma_frac = F / (ms_per_step / 1e3) / (PEAK_TFLOPS[w.dtype] * 1e12)
+    log(f"[bench] {args.steps} steps in {ms:.1f} ms: {ms_per_step:.3f} ms/step, {value:,.0f} tokens/s, "
+        f"model flops {F / 1e12:.3f} TF/step = {mfma_frac * 100:.1f}% of {w.dtype} MFMA peak, loss {loss:.4f}")
+
+    # per-kernel profile of a few more steps (HIP events around every launch)
+    binding.profile(True)
+    for _ in range(args.profile_steps):
+        t += 1
+        arena.step(xi, yi, w, t, check_ids=False)
+    torch.cuda.synchronize()
+    binding.profile(False)
+    stats = binding.profile_read()
+    tot = sum(s["total_ms"] for s in stats)
+    stats.sort(key=lambda s: -s["total_ms"])
+    log(f"[bench] kernel profile over {args.profile_steps} steps ({tot / args.profile_steps:.3f} ms/step in kernels):")
+    for s in stats:
+        avg = s["total_ms"] / s["launches"]
+        tf = s["flops"] / (s["total_ms"] / 1e3) / 1e12 if s["flops"] else 0.0
+        gbs = s["bytes"] / (s["total_ms"] / 1e3) / 1e9
+        log(f"  {s['name']:<28} {s['launches']:6d} launches {s['total_ms'] / args.profile_steps:9.3f} ms/step "
+            f"({100 * s['total_ms'] / tot:5.1f}%) avg {avg * 1e3:9.1f} us  {tf:8.1f} TFLOP/s  {gbs:8.1f} GB/s")
+    if args.kernel_table:
+        with open(args.kernel_table, "w") as f:
+            json.dump({"workload": w.name, "profile_steps": args.profile_steps, "kernels": stats}, f, indent=1)
+    dom = stats[0]
+    avg_s = dom["total_ms"] / dom["launches"] / 1e3
+    if dom["flops"] > 0:
+        achieved = dom["flops"] / dom["launches"] / avg_s / 1e12
+        roof = {"kernel": dom["name"], "bound": "mfma", "achieved": round(achieved, 2),
+                "peak": PEAK_TFLOPS[w.dtype], "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS[w.dtype], 4)}
+    else:
+        achieved = dom["bytes"] / dom["launches"] / avg_s / 1e9
+        roof = {"kernel": dom["name"], "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    roof["avg_launch_us"] = round(avg_s * 1e6, 2)
+    roof["traffic"] = None
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] CPU oracle baseline ...")
+        cpu = cpu_baseline(w, params, x, y)
+        log(f"[bench] CPU oracle: {cpu['value']:.1f} tokens/s on {cpu['cores']} threads")
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded random-init weights, uniform token ids)"
+        if w.tokens == "uniform" else "synthetic (seeded random-init weights, Zipf token ids)",
+        "config": {"workload": w.name, "B": w.B, "T": w.T, "layers": m.num_layers, "heads": m.num_heads,
+                   "channels": m.channels, "vocab": m.vocab_size, "tokens": w.tokens},
+        "mfma_peak_frac": round(mfma_frac, 4), "model_tflop_per_step": round(F / 1e12, 4),
+        "loss": round(loss, 5), "roofline": roof, "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

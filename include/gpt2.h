@@ -156,6 +156,28 @@ int gpt2_tensor_info(const gpt2_arena* arena, int32_t tensor_id, int32_t layer, 
 /* Number of parameters (equals the llm.c banner's num_parameters for GPT-2 124M). */
 int64_t gpt2_num_parameters(const gpt2_config* cfg);
 
+/* Launch profiler (process-wide, all arenas).  gpt2_profile(1) clears earlier
+ * records and starts recording a pair of HIP events on the launching stream around
+ * every kernel launch, tagged with the kernel name and the launch's algorithmic
+ * work (flops of its contractions counting only unmasked attention pairs; bytes
+ * it must read and write at least once).  gpt2_profile(0) stops recording.
+ * At most 32768 launches are recorded per enable.  Timing adds a small per-launch
+ * overhead; the benchmark times its headline figure with profiling off. */
+typedef struct gpt2_kernel_stat {
+    char name[64];
+    int64_t launches;
+    double total_ms;   /* sum of per-launch event durations */
+    double flops;      /* sum of algorithmic flops          */
+    double bytes;      /* sum of algorithmic bytes          */
+} gpt2_kernel_stat;
+
+int gpt2_profile(int enable);
+
+/* Waits for the recorded events and writes one aggregate per kernel name (sorted
+ * by name) into out[0..max_entries); *n_entries receives the number of names.
+ * Errors: GPT2_E_HIP if an event cannot be read. */
+int gpt2_profile_read(gpt2_kernel_stat* out, int32_t max_entries, int32_t* n_entries);
+
 /* Message for the last non-OK status on this thread ("" if none). */
 const char* gpt2_last_error(void);
 

@@ -1,0 +1,72 @@
+"""Helpers shared by the GPU parity tests: run one step on the HIP path and on
+the oracle from the same seeded inputs, and compare with stated metrics."""
+import numpy as np
+
+import synth
+
+# Tolerances (BASELINE workload statement): fp32 -> loss relative error <= 1e-5,
+# logits and every parameter gradient max-norm relative error <= 1e-3;
+# bf16 -> loss absolute error <= 2e-2, cosine of the flat gradient >= 0.999.
+FP32_LOSS_REL = 1e-5
+FP32_MAXREL = 1e-3
+BF16_LOSS_ABS = 2e-2
+BF16_GRAD_COS = 0.999
+
+# oracle activation name -> (tensor id, column selector) of the GPU arena
+ACT_MAP = {
+    "ln1": "T_LN1", "qkv": "T_QKV", "atty": "T_ATTY", "residual2": "T_RESIDUAL2", "ln2": "T_LN2",
+    "fch": "T_FCH", "fch_gelu": "T_FCH_GELU", "residual3": "T_RESIDUAL3",
+}
+
+
+def maxrel(gpu, ref):
+    gpu = np.asarray(gpu, dtype=np.float64).ravel()
+    ref = np.asarray(ref, dtype=np.float64).ravel()
+    den = np.abs(ref).max()
+    return float(np.abs(gpu - ref).max() / den) if den > 0 else float(np.abs(gpu).max())
+
+
+def cosine(a, b):
+    a = np.asarray(a, dtype=np.float64).ravel()
+    b = np.asarray(b, dtype=np.float64).ravel()
+    return float(a @ b / (np.linalg.norm(a) * np.linalg.norm(b)))
+
+
+def to_np(t):
+    import torch
+    return t.detach().to(torch.float32).cpu().numpy()
+
+
+def gpu_arena(w, params, B=None, T=None):
+    from transformer_lm_fwd_amd import Arena
+    a = Arena(w.model, w.B if B is None else B, w.T if T is None else T, w.dtype)
+    a.load_params(params)
+    return a
+
+
+def oracle_model(w, params, B=None, T=None, prec="f64"):
+    import oracle
+    o = oracle.Oracle(w.model, w.B if B is None else B, w.T if T is None else T, prec)
+    o.set("params", params)
+    return o
+
+
+def per_tensor(vec, m):
+    return {name: vec[o:o + n] for name, (o, n) in synth.param_offsets(m).items()}
+
+
+def report(label, d):
+    print(label + ": " + ", ".join(f"{k}={v:.3g}" for k, v in d.items()), flush=True)
+
+
+def rand_params(m, seed=7):
+    """The init recipe plus random LayerNorm gains/shifts and biases, so that no
+    gradient term is multiplied by an exact 0 or 1."""
+    p = synth.init_params(m).astype(np.float64)
+    rng = np.random.default_rng(seed)
+    for name, (o, n) in synth.param_offsets(m).items():
+        if name.endswith(("ln1.w", "ln2.w")) or name == "lnf.w":
+            p[o:o + n] = 1.0 + 0.1 * rng.standard_normal(n)
+        elif name.endswith(".b"):
+            p[o:o + n] = 0.1 * rng.standard_normal(n)
+    return p.astype(np.float32)

@@ -1,0 +1,123 @@
+"""Host-side checks of the C ABI: exported symbols, layout queries and argument
+validation.  No kernel runs here (size queries and rejected arguments never
+touch the GPU), so these run without a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _lib():
+    from transformer_lm_fwd_amd import binding
+    if not os.path.exists(binding.LIB_PATH):
+        from transformer_lm_fwd_amd import build
+        build.build()
+    return binding
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "gpt2.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:int|int64_t|const char\*)\s+(gpt2_\w+)\s*\(", src, re.M)))
+
+
+def test_header_declares_the_four_step_entry_points():
+    names = declared_functions()
+    for n in ("gpt2_alloc_arena", "gpt2_forward", "gpt2_backward", "gpt2_adamw_step"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    b = _lib()
+    L = ctypes.CDLL(b.LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(L, n), n
+    assert set(declared_functions()) == set(b.EXPORTS)
+
+
+def test_num_parameters_matches_generator_layout():
+    b = _lib()
+    for m in (synth.GPT2_TINY_CHAR, synth.GPT2_124M, synth.GPT2_350M, synth.GPT2_1558M):
+        assert b.num_parameters(m) == synth.num_parameters(m)
+    assert b.num_parameters(synth.GPT2_124M) == 124439808
+
+
+def test_arena_size_query_and_monotonicity():
+    b = _lib()
+    m = synth.GPT2_124M
+    fp32 = b.arena_bytes(m, 4, 64, b.GPT2_FP32)
+    bf16 = b.arena_bytes(m, 4, 64, b.GPT2_BF16)
+    assert fp32 > 4 * 4 * 124439808 and bf16 > 0
+    assert b.arena_bytes(m, 8, 1024, b.GPT2_BF16) > bf16
+    # every workload fits a 288 GB device with room to spare
+    for w in synth.WORKLOADS.values():
+        dt = b.GPT2_BF16 if w.dtype == "bf16" else b.GPT2_FP32
+        assert b.arena_bytes(w.model, w.B, w.T, dt) < 64e9
+
+
+@pytest.mark.parametrize("shape,B,T,dtype,msg", [
+    ((1024, 50257, 12, 12, 770), 4, 64, 0, "multiple of num_heads"),
+    ((1024, 50257, 12, 5, 760), 4, 64, 0, "head size"),
+    ((64, 65, 2, 4, 64), 4, 65, 0, "max_seq_len"),
+    ((64, 65, 2, 4, 64), 0, 8, 0, "B >= 1"),
+    ((64, 65, 2, 4, 64), 2, 8, 7, "dtype"),
+    ((64, 1, 2, 4, 64), 2, 8, 0, "non-positive"),
+])
+def test_invalid_configurations_are_rejected(shape, B, T, dtype, msg):
+    b = _lib()
+    cfg = b.gpt2_config(*shape)
+    need = ctypes.c_size_t(0)
+    rc = b.lib().gpt2_alloc_arena(ctypes.byref(cfg), B, T, dtype, None, 0, ctypes.byref(need), None)
+    assert rc == -1
+    assert msg in b.lib().gpt2_last_error().decode()
+
+
+def test_small_or_misaligned_buffers_are_rejected_without_touching_memory():
+    b = _lib()
+    cfg = b.make_config(synth.GPT2_TINY_CHAR)
+    need = b.arena_bytes(synth.GPT2_TINY_CHAR, 4, 32, b.GPT2_FP32)
+    h = ctypes.c_void_p()
+    # a fake, never dereferenced address: validation fails before any use
+    rc = b.lib().gpt2_alloc_arena(ctypes.byref(cfg), 4, 32, 0, ctypes.c_void_p(1 << 40), need - 1, None, ctypes.byref(h))
+    assert rc == -2 and not h.value
+    rc = b.lib().gpt2_alloc_arena(ctypes.byref(cfg), 4, 32, 0, ctypes.c_void_p((1 << 40) + 16), need, None, ctypes.byref(h))
+    assert rc == -3 and not h.value
+
+
+def test_backward_before_forward_is_a_state_error_and_step_must_be_positive():
+    b = _lib()
+    cfg = b.make_config(synth.GPT2_TINY_CHAR)
+    need = b.arena_bytes(synth.GPT2_TINY_CHAR, 4, 32, b.GPT2_FP32)
+    h = ctypes.c_void_p()
+    # a handle over a fake address: only calls that fail validation are made with it
+    assert b.lib().gpt2_alloc_arena(ctypes.byref(cfg), 4, 32, 0, ctypes.c_void_p(1 << 40), need, None, ctypes.byref(h)) == 0
+    try:
+        assert b.lib().gpt2_backward(h, None) == -4
+        assert b.lib().gpt2_adamw_step(h, 1e-4, 0.9, 0.999, 1e-8, 0.0, 0, None) == -1
+        off, rows, cols, ld, dt = (ctypes.c_size_t(), ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64(),
+                                   ctypes.c_int32())
+        assert b.lib().gpt2_tensor_info(h, 8, 0, ctypes.byref(off), ctypes.byref(rows), ctypes.byref(cols),
+                                        ctypes.byref(ld), ctypes.byref(dt)) == 0
+        assert (rows.value, cols.value, ld.value) == (4 * 32, 65, 128) and off.value % 256 == 0
+        assert b.lib().gpt2_tensor_info(h, 18, 2, None, None, None, None, None) == -1   # layer out of range
+        assert b.lib().gpt2_tensor_info(h, 4, 0, None, None, None, None, None) == -1    # no bf16 copy in fp32
+        assert b.lib().gpt2_tensor_info(h, 99, 0, None, None, None, None, None) == -1
+    finally:
+        b.lib().gpt2_free_arena(h)
+
+
+def test_binding_refuses_out_of_range_token_ids_on_the_host():
+    b = _lib()
+    a = b.Arena.__new__(b.Arena)   # no device memory: only the host-side id check is exercised
+    a.m, a.B, a.T = synth.GPT2_TINY_CHAR, 2, 3
+    import numpy as np
+    with pytest.raises(ValueError):
+        a._ids(np.array([[0, 1, 65], [0, 0, 0]]))
+    with pytest.raises(ValueError):
+        a._ids(np.array([[0, 1, -1], [0, 0, 0]]))
+    with pytest.raises(ValueError):
+        a._ids(np.zeros((3, 2), dtype=np.int32))

@@ -1,0 +1,278 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the same
+seeded inputs.  Every case prints its name and shape before it touches the GPU."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import synth
+from synth import ModelShape, Workload
+from parity_util import (BF16_GRAD_COS, BF16_LOSS_ABS, FP32_LOSS_REL, FP32_MAXREL, ACT_MAP, cosine, gpu_arena,
+                         maxrel, oracle_model, per_tensor, rand_params, report, to_np)
+
+pytestmark = pytest.mark.gpu
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def _b():
+    from transformer_lm_fwd_amd import binding
+    return binding
+
+
+def announce(name, w, B=None, T=None):
+    m = w.model
+    print(f"\n[case] {name}: L={m.num_layers} NH={m.num_heads} C={m.channels} V={m.vocab_size} "
+          f"B={w.B if B is None else B} T={w.T if T is None else T} {w.dtype}", flush=True)
+
+
+def fp32_full_compare(w, params, check_acts=True):
+    """forward (logits, activations), loss, backward and one AdamW step, fp32 tolerances."""
+    b = _b()
+    x, y = synth.inputs_targets(w)
+    o = oracle_model(w, params)
+    a = gpu_arena(w, params)
+    m = w.model
+    BT, C = w.B * w.T, m.channels
+    # forward without targets keeps the logits
+    a.forward(x)
+    ref_loss = o.forward(x, y)
+    errs = {"logits": maxrel(to_np(a.tensor(b.T_LOGITS)), o.act("logits"))}
+    if check_acts:
+        errs["encoded"] = maxrel(to_np(a.tensor(b.T_ENCODED)), o.act("encoded"))
+        for l in range(m.num_layers):
+            for name, tid in ACT_MAP.items():
+                errs[f"{name}{l}"] = maxrel(to_np(a.tensor(getattr(b, tid), l)), o.act(name, l))
+            st = to_np(a.tensor(b.T_LN1_STATS, l))
+            errs[f"ln1_mean{l}"] = maxrel(st[:, 0], o.act("ln1_mean", l))
+            errs[f"ln1_rstd{l}"] = maxrel(st[:, 1], o.act("ln1_rstd", l))
+            # attention log-sum-exp from the oracle's stored scaled scores
+            pre = o.act("preatt", l).reshape(w.B, m.num_heads, w.T, w.T)
+            errs[f"lse{l}"] = maxrel(to_np(a.tensor(b.T_ATT_LSE, l)).reshape(w.B, m.num_heads, w.T),
+                                     np.logaddexp.reduce(pre, axis=-1))
+        errs["lnf"] = maxrel(to_np(a.tensor(b.T_LNF)), o.act("lnf"))
+    report("forward maxrel", errs)
+    for k, v in errs.items():
+        assert v <= FP32_MAXREL, (k, v)
+    # loss and per-row losses
+    a.forward(x, y)
+    loss = a.loss()
+    print(f"loss gpu={loss:.9f} oracle={ref_loss:.9f} rel={abs(loss - ref_loss) / abs(ref_loss):.3g}", flush=True)
+    assert abs(loss - ref_loss) <= FP32_LOSS_REL * abs(ref_loss)
+    assert maxrel(to_np(a.tensor(b.T_LOSSES)), o.act("losses")) <= FP32_MAXREL
+    # dlogits (written over the logits)
+    o.backward()
+    dz = to_np(a.tensor(b.T_LOGITS))
+    assert maxrel(dz, o.act("dlogits")) <= FP32_MAXREL
+    a.backward()
+    g_gpu = to_np(a.tensor(b.T_GRADS)).ravel()
+    g_ref = o.get("grads")
+    gerr = {k: maxrel(v, per_tensor(g_ref, m)[k]) for k, v in per_tensor(g_gpu, m).items()}
+    report("grad maxrel", gerr)
+    for k, v in gerr.items():
+        assert v <= FP32_MAXREL, (k, v)
+    # One AdamW step, checked on its own: Adam's first step is g/(|g| + eps), a sign
+    # for every |g| >> eps, so gradients that agree to 1e-6 still flip the update of
+    # entries whose true gradient is ~0.  The oracle's update is therefore applied
+    # to the GPU's own gradients.
+    # The ABI takes fp32 hyper-parameters, so the oracle gets the same fp32 values.
+    o.set("grads", g_gpu.astype(np.float64))
+    p_before = to_np(a.tensor(b.T_PARAMS)).ravel().astype(np.float64)
+    a.adamw_step(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, 1)
+    o.set("params", p_before)
+    hp = [float(np.float32(v)) for v in (w.lr, w.beta1, w.beta2, w.eps, w.weight_decay)]
+    o.adamw(*hp, 1)
+    p_gpu = to_np(a.tensor(b.T_PARAMS)).ravel().astype(np.float64)
+    p_ref = o.get("params")
+    dp = np.abs(p_gpu - p_ref)
+    tol = 1e-5 * w.lr + 2.0 ** -23 * np.abs(p_ref)
+    print(f"adamw max |theta err| = {dp.max():.3g}", flush=True)
+    assert (dp <= tol).all()
+    for name in ("m", "v"):
+        ref = o.get(name)
+        got = to_np(a.tensor(b.T_ADAM_M if name == "m" else b.T_ADAM_V)).ravel()
+        assert maxrel(got, ref) <= 1e-6, name
+    return a, o
+
+
+# ----------------------------------------------------------------------------- fp32 parity
+
+def test_tiny_char_fp32_step_layer_by_layer():
+    w = synth.WORKLOADS["tiny_char_b4t32_fp32"]
+    announce("tiny_char_fp32", w)
+    fp32_full_compare(w, rand_params(w.model))
+
+
+@pytest.mark.parametrize("NH", [8, 4, 1])
+def test_fp32_head_sizes_and_ragged_tiles(NH):
+    # head sizes 16, 32, 128; B*T = 140 and V = 131 are not multiples of any tile
+    w = Workload("ragged", ModelShape(96, 131, 1, NH, 128), 2, 70, "fp32", "uniform", index=21)
+    announce(f"ragged_fp32_hs{128 // NH}", w)
+    fp32_full_compare(w, rand_params(w.model, seed=NH))
+
+
+def test_fp32_single_position():
+    w = Workload("t1", ModelShape(16, 65, 2, 4, 64), 3, 1, "fp32", "uniform", index=22)
+    announce("single_position", w)
+    fp32_full_compare(w, rand_params(w.model, seed=5))
+
+
+def test_gpt2_124m_b4t64_fp32_step_and_ten_step_losses():
+    # The GPT-2 124M shape at the B=4, T=64 split of the llm.c run; one step in full
+    # detail, then 10 consecutive steps on one batch against the stored oracle losses.
+    w = synth.WORKLOADS["gpt2_124m_b4t64_fp32"]
+    announce("gpt2_124m_b4t64_fp32", w)
+    params = synth.init_params(w.model)
+    fp32_full_compare(w, params, check_acts=False)
+    with open(os.path.join(HERE, "golden", "gpt2_124m_b4t64_fp32_steps.json")) as f:
+        gold = json.load(f)["losses"]
+    a = gpu_arena(w, params)
+    x, y = synth.inputs_targets(w)
+    losses = []
+    for t in range(1, 11):
+        a.step(x, y, w, t)
+        losses.append(a.loss())
+    rel = [abs(g - r) / abs(r) for g, r in zip(losses, gold)]
+    print("ten-step losses gpu   :", " ".join(f"{v:.6f}" for v in losses))
+    print("ten-step losses oracle:", " ".join(f"{v:.6f}" for v in gold))
+    print("relative errors       :", " ".join(f"{v:.2g}" for v in rel), flush=True)
+    assert rel[0] <= FP32_LOSS_REL
+    # Adam's early, sign-like updates amplify rounding differences step by step;
+    # later steps keep a looser bound, and the overall decrease must hold.
+    assert max(rel) <= 1e-3
+    assert losses[-1] < losses[0] - 5.0
+
+
+# ----------------------------------------------------------------------------- bf16 parity
+
+def bf16_compare(w, params, seed_label=""):
+    b = _b()
+    x, y = synth.inputs_targets(w)
+    o = oracle_model(w, params)
+    a = gpu_arena(w, params)
+    a.forward(x, y)
+    loss = a.loss()
+    ref = o.forward(x, y)
+    a.backward()
+    o.backward()
+    g = to_np(a.tensor(b.T_GRADS)).ravel()
+    gr = o.get("grads")
+    cos = cosine(g, gr)
+    cos_t = {k: cosine(v, per_tensor(gr, w.model)[k]) for k, v in per_tensor(g, w.model).items()}
+    print(f"bf16 loss gpu={loss:.6f} oracle={ref:.6f} |d|={abs(loss - ref):.3g}; flat grad cosine={cos:.6f}")
+    report("per-tensor cosine", cos_t)
+    assert abs(loss - ref) <= BF16_LOSS_ABS
+    assert cos >= BF16_GRAD_COS
+    assert np.isfinite(g).all()
+    return a, o
+
+
+def test_bf16_small_model_ragged():
+    w = Workload("bf16_small", ModelShape(128, 997, 2, 2, 128), 3, 100, "bf16", "uniform", index=23)
+    announce("bf16_small_ragged", w)
+    bf16_compare(w, rand_params(w.model, seed=23))
+
+
+def test_bf16_tiny_char():
+    w = Workload("bf16_tiny", synth.GPT2_TINY_CHAR, 4, 32, "bf16", "uniform", index=0)
+    announce("bf16_tiny_char", w)
+    bf16_compare(w, rand_params(w.model, seed=1))
+
+
+# ----------------------------------------------------------------------------- properties
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_causality_bitwise_on_gpu(dtype):
+    # "GPT-2 from scratch with torch", 自注意力: a position sees only itself and the past,
+    # so changing later tokens leaves earlier logits bit-identical.
+    b = _b()
+    w = Workload("causal", ModelShape(64, 211, 2, 4, 64), 2, 64, dtype, "uniform", index=24)
+    announce(f"causality_{dtype}", w)
+    a = gpu_arena(w, rand_params(w.model, seed=9))
+    x, _ = synth.inputs_targets(w)
+    a.forward(x)
+    ref = to_np(a.tensor(b.T_LOGITS)).reshape(w.B, w.T, -1).copy()
+    for t in (0, 31, 62):
+        x2 = x.copy()
+        x2[:, t + 1:] = (x2[:, t + 1:] + 13) % w.model.vocab_size
+        a.forward(x2)
+        z = to_np(a.tensor(b.T_LOGITS)).reshape(w.B, w.T, -1)
+        np.testing.assert_array_equal(z[:, :t + 1], ref[:, :t + 1])
+        assert not np.array_equal(z[:, t + 1:], ref[:, t + 1:])
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_step_is_deterministic(dtype):
+    b = _b()
+    w = Workload("det", ModelShape(64, 301, 2, 4, 128), 2, 48, dtype, "zipf", index=25)
+    announce(f"determinism_{dtype}", w)
+    p = rand_params(w.model, seed=10)
+    x, y = synth.inputs_targets(w)
+    outs = []
+    for _ in range(2):
+        a = gpu_arena(w, p)
+        a.forward(x, y)
+        a.backward()
+        outs.append((a.loss(), to_np(a.tensor(b.T_GRADS)).copy()))
+        a.close()
+    assert outs[0][0] == outs[1][0]
+    np.testing.assert_array_equal(outs[0][1], outs[1][1])
+
+
+def test_zero_final_gains_give_ln_V_on_gpu():
+    # "从头搭建GPT(Andrej Karpathy) 笔记", 计算loss: all-zero logits cost exactly ln V, and
+    # d loss / d z = (1/V - onehot)/(B T).
+    b = _b()
+    w = Workload("lnV", ModelShape(32, 65, 1, 4, 64), 4, 32, "fp32", "uniform", index=26)
+    announce("zero_logits", w)
+    p = rand_params(w.model, seed=3)
+    o, n = synth.param_offsets(w.model)["lnf.w"]
+    p[o:o + 2 * n] = 0.0
+    a = gpu_arena(w, p)
+    x, y = synth.inputs_targets(w)
+    a.forward(x, y)
+    assert a.loss() == pytest.approx(math.log(65), rel=1e-6)
+    dz = to_np(a.tensor(b.T_LOGITS))
+    onehot = np.zeros_like(dz)
+    onehot[np.arange(w.B * w.T), y.reshape(-1)] = 1
+    np.testing.assert_allclose(dz, (1 / 65 - onehot) / (w.B * w.T), rtol=1e-5, atol=1e-9)
+
+
+# ----------------------------------------------------------------------------- full size (bench configuration)
+
+def test_gpt2_124m_b8t1024_bf16_full_size_sampled():
+    # The timed configuration.  Sampled outputs the oracle computes one by one:
+    # by causality, positions 0..63 of a sequence depend only on its first 64
+    # tokens, so an oracle run on that prefix gives their losses exactly.
+    b = _b()
+    w = synth.WORKLOADS["gpt2_124m_b8t1024_bf16"]
+    announce("gpt2_124m_b8t1024_bf16 (full size)", w)
+    params = synth.init_params(w.model)
+    x, y = synth.inputs_targets(w)
+    a = gpu_arena(w, params)
+    a.forward(x, y)
+    loss0 = a.loss()
+    losses = to_np(a.tensor(b.T_LOSSES)).reshape(w.B, w.T)
+    t0 = 64
+    for row in (0, w.B - 1):
+        o = oracle_model(w, params, B=1, T=t0)
+        o.forward(x[row:row + 1, :t0], y[row:row + 1, :t0])
+        d = np.abs(losses[row, :t0] - o.act("losses"))
+        print(f"row {row}: max |loss_t - oracle| over t<{t0} = {d.max():.3g}", flush=True)
+        assert d.max() <= BF16_LOSS_ABS
+    # dlogits rows sum to zero (softmax minus one-hot), padding columns are zero
+    dz = a.tensor(b.T_LOGITS)
+    import torch
+    rs = dz.to(torch.float32).sum(dim=1)
+    assert float(rs.abs().max()) <= 1e-6
+    a.backward()
+    g = a.tensor(b.T_GRADS)
+    assert bool(torch.isfinite(g).all())
+    # wpe rows beyond T get no gradient
+    a.adamw_step(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, 1)
+    a.forward(x, y)
+    loss1 = a.loss()
+    print(f"loss before {loss0:.5f} after one step {loss1:.5f}", flush=True)
+    assert loss1 < loss0

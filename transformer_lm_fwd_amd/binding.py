@@ -1,0 +1,214 @@
+"""ctypes binding of the gfx950 GPT-2 training-step library (include/gpt2.h).
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+libgpt2_hip.so.  PyTorch supplies the device arena (one uint8 tensor) and the
+stream.  If the library has not been built this module raises: there is no
+fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "_lib", "libgpt2_hip.so")
+
+GPT2_FP32, GPT2_BF16 = 0, 1
+STATUS = {0: "GPT2_OK", -1: "GPT2_E_INVAL", -2: "GPT2_E_SIZE", -3: "GPT2_E_ALIGN", -4: "GPT2_E_STATE",
+          -5: "GPT2_E_HIP"}
+
+# tensor ids (enum gpt2_tensor_id)
+T_PARAMS, T_GRADS, T_ADAM_M, T_ADAM_V, T_PARAMS_BF16 = 0, 1, 2, 3, 4
+T_ENCODED, T_LNF, T_LNF_STATS, T_LOGITS, T_LOSSES, T_LOSS = 5, 6, 7, 8, 9, 10
+T_LN1, T_LN1_STATS, T_QKV, T_ATTY, T_ATT_LSE, T_RESIDUAL2 = 16, 17, 18, 19, 20, 21
+T_LN2, T_LN2_STATS, T_FCH, T_FCH_GELU, T_RESIDUAL3 = 22, 23, 24, 25, 26
+
+EXPORTS = ("gpt2_alloc_arena", "gpt2_free_arena", "gpt2_sync_weights", "gpt2_forward", "gpt2_backward",
+           "gpt2_adamw_step", "gpt2_tensor_info", "gpt2_num_parameters", "gpt2_profile", "gpt2_profile_read",
+           "gpt2_last_error")
+
+
+class gpt2_config(ctypes.Structure):
+    _fields_ = [("max_seq_len", ctypes.c_int32), ("vocab_size", ctypes.c_int32), ("num_layers", ctypes.c_int32),
+                ("num_heads", ctypes.c_int32), ("channels", ctypes.c_int32)]
+
+
+class gpt2_kernel_stat(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 64), ("launches", ctypes.c_int64), ("total_ms", ctypes.c_double),
+                ("flops", ctypes.c_double), ("bytes", ctypes.c_double)]
+
+
+class Gpt2Error(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"{STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def lib():
+    """Loads libgpt2_hip.so (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run `python -m transformer_lm_fwd_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, sz, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+        cfgp = ctypes.POINTER(gpt2_config)
+        L.gpt2_alloc_arena.argtypes = [cfgp, i32, i32, i32, vp, sz, ctypes.POINTER(sz), ctypes.POINTER(vp)]
+        L.gpt2_free_arena.argtypes = [vp]
+        L.gpt2_sync_weights.argtypes = [vp, vp]
+        L.gpt2_forward.argtypes = [vp, vp, vp, vp]
+        L.gpt2_backward.argtypes = [vp, vp]
+        L.gpt2_adamw_step.argtypes = [vp, f32, f32, f32, f32, f32, i32, vp]
+        L.gpt2_tensor_info.argtypes = [vp, i32, i32, ctypes.POINTER(sz), ctypes.POINTER(i64), ctypes.POINTER(i64),
+                                       ctypes.POINTER(i64), ctypes.POINTER(i32)]
+        L.gpt2_num_parameters.argtypes = [cfgp]
+        L.gpt2_num_parameters.restype = i64
+        L.gpt2_last_error.restype = ctypes.c_char_p
+        L.gpt2_profile.argtypes = [ctypes.c_int]
+        L.gpt2_profile_read.argtypes = [ctypes.POINTER(gpt2_kernel_stat), i32, ctypes.POINTER(i32)]
+        for name in EXPORTS:
+            if name not in ("gpt2_num_parameters", "gpt2_last_error"):
+                L[name].restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(rc):
+    if rc != 0:
+        raise Gpt2Error(rc, lib().gpt2_last_error().decode())
+
+
+def make_config(m) -> gpt2_config:
+    return gpt2_config(m.max_seq_len, m.vocab_size, m.num_layers, m.num_heads, m.channels)
+
+
+def num_parameters(m) -> int:
+    return int(lib().gpt2_num_parameters(ctypes.byref(make_config(m))))
+
+
+def arena_bytes(m, B: int, T: int, dtype: int) -> int:
+    need = ctypes.c_size_t(0)
+    _check(lib().gpt2_alloc_arena(ctypes.byref(make_config(m)), B, T, dtype, None, 0, ctypes.byref(need), None))
+    return int(need.value)
+
+
+def profile(enable: bool) -> None:
+    """Starts (clearing earlier records) or stops the library's launch profiler."""
+    _check(lib().gpt2_profile(1 if enable else 0))
+
+
+def profile_read():
+    """Per-kernel aggregates of the recorded launches (waits for their events):
+    a list of dicts with name, launches, total_ms, flops, bytes."""
+    n = ctypes.c_int32(0)
+    _check(lib().gpt2_profile_read(None, 0, ctypes.byref(n)))
+    arr = (gpt2_kernel_stat * max(1, n.value))()
+    _check(lib().gpt2_profile_read(arr, n.value, ctypes.byref(n)))
+    return [dict(name=r.name.decode(), launches=int(r.launches), total_ms=float(r.total_ms), flops=float(r.flops),
+                 bytes=float(r.bytes)) for r in arr[:n.value]]
+
+
+def _stream_ptr(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+class Arena:
+    """One arena on the current CUDA (HIP) device: parameters, AdamW state,
+    activations and scratch in one zero-filled torch uint8 buffer."""
+
+    def __init__(self, m, B: int, T: int, dtype: str = "bf16", device="cuda"):
+        import torch
+        self.m, self.B, self.T = m, B, T
+        self.dtype = {"fp32": GPT2_FP32, "bf16": GPT2_BF16}[dtype]
+        self.dtype_name = dtype
+        self.nbytes = arena_bytes(m, B, T, self.dtype)
+        self.buf = torch.zeros(self.nbytes + 256, dtype=torch.uint8, device=device)
+        pad = (-self.buf.data_ptr()) % 256
+        self.base = self.buf[pad:pad + self.nbytes]
+        h = ctypes.c_void_p()
+        _check(lib().gpt2_alloc_arena(ctypes.byref(make_config(m)), B, T, self.dtype,
+                                      ctypes.c_void_p(self.base.data_ptr()), self.nbytes, None, ctypes.byref(h)))
+        self.h = h
+        self.n_params = num_parameters(m)
+        self._inputs = None
+        self._targets = None
+
+    def close(self):
+        if getattr(self, "h", None):
+            lib().gpt2_free_arena(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # ------------------------------------------------------------------ tensors
+    def info(self, tensor_id: int, layer: int = 0):
+        off, rows, cols, ld, dt = ctypes.c_size_t(), ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int32()
+        _check(lib().gpt2_tensor_info(self.h, tensor_id, layer, ctypes.byref(off), ctypes.byref(rows),
+                                      ctypes.byref(cols), ctypes.byref(ld), ctypes.byref(dt)))
+        return off.value, rows.value, cols.value, ld.value, dt.value
+
+    def tensor(self, tensor_id: int, layer: int = 0):
+        """A torch view of an arena tensor, shape [rows, row_stride] narrowed to [rows, cols]."""
+        import torch
+        off, rows, cols, ld, dt = self.info(tensor_id, layer)
+        tdt, es = (torch.float32, 4) if dt == GPT2_FP32 else (torch.bfloat16, 2)
+        raw = self.base[off:off + rows * ld * es].view(tdt).view(rows, ld)
+        return raw[:, :cols]
+
+    # ------------------------------------------------------------------ steps
+    def load_params(self, params, stream=None):
+        """Copies a flat fp32 parameter vector into the master weights and refreshes derived copies."""
+        import torch
+        p = torch.as_tensor(params, dtype=torch.float32)
+        assert p.numel() == self.n_params, (p.numel(), self.n_params)
+        self.tensor(T_PARAMS).view(-1).copy_(p.view(-1))
+        _check(lib().gpt2_sync_weights(self.h, _stream_ptr(stream)))
+
+    def _ids(self, x):
+        import torch
+        t = torch.as_tensor(x)
+        if t.dtype != torch.int32:
+            t = t.to(torch.int32)
+        if tuple(t.shape) != (self.B, self.T):
+            raise ValueError(f"token array must have shape {(self.B, self.T)}, got {tuple(t.shape)}")
+        lo, hi = int(t.min()), int(t.max())
+        if lo < 0 or hi >= self.m.vocab_size:
+            raise ValueError(f"token ids must lie in [0, {self.m.vocab_size}), got [{lo}, {hi}]")
+        return t.to(self.base.device).contiguous()
+
+    def forward(self, inputs, targets=None, stream=None, check_ids=True):
+        """check_ids=False skips the host-side id range check (which synchronises);
+        then inputs/targets must already be int32 device tensors of shape (B, T)."""
+        # keep the device token arrays alive for the backward pass
+        if check_ids:
+            self._inputs = self._ids(inputs)
+            self._targets = None if targets is None else self._ids(targets)
+        else:
+            self._inputs, self._targets = inputs, targets
+        _check(lib().gpt2_forward(self.h, ctypes.c_void_p(self._inputs.data_ptr()),
+                                  None if self._targets is None else ctypes.c_void_p(self._targets.data_ptr()),
+                                  _stream_ptr(stream)))
+
+    def backward(self, stream=None):
+        _check(lib().gpt2_backward(self.h, _stream_ptr(stream)))
+
+    def adamw_step(self, lr, beta1, beta2, eps, weight_decay, step: int, stream=None):
+        _check(lib().gpt2_adamw_step(self.h, lr, beta1, beta2, eps, weight_decay, step, _stream_ptr(stream)))
+
+    def loss(self) -> float:
+        return float(self.tensor(T_LOSS).item())
+
+    def step(self, inputs, targets, w, t: int, check_ids=True) -> None:
+        """forward + backward + AdamW with a workload's hyper-parameters."""
+        self.forward(inputs, targets, check_ids=check_ids)
+        self.backward()
+        self.adamw_step(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, t)

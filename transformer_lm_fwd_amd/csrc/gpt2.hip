@@ -1,0 +1,440 @@
+// Host side of the GPT-2 training-step library: arena layout and the C ABI
+// entry points declared in include/gpt2.h.  Every step of the path runs in the
+// kernels of this directory; this file only validates, lays out and enqueues.
+#include <math.h>
+#include <string.h>
+
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/gpt2.h"
+#include "kernels.h"
+
+using namespace gpt2;
+
+namespace {
+
+thread_local std::string g_error;
+
+int fail(int code, const std::string& msg) {
+    g_error = msg;
+    return code;
+}
+
+enum { P_LN1W, P_LN1B, P_QKVW, P_QKVB, P_PROJW, P_PROJB, P_LN2W, P_LN2B, P_FCW, P_FCB, P_FCPW, P_FCPB, P_N };
+
+struct LayerActs {
+    size_t ln1, ln1s, qkv, atty, lse, res2, ln2, ln2s, fch, fchg, res3;
+};
+
+}  // namespace
+
+struct gpt2_arena {
+    gpt2_config cfg;
+    int B, T, dtype, Vp, hs;
+    int64_t nparams;
+    char* base;
+    size_t bytes;
+    size_t act_size;  // bytes per activation element
+    // parameter element offsets
+    int64_t o_wte, o_wpe, o_lnfw, o_lnfb;
+    std::vector<int64_t> o_layer;  // [L * P_N]
+    // byte offsets of regions
+    size_t params, grads, adam_m, adam_v, params16;
+    size_t encoded, lnf, lnfs, logits, losses, loss;
+    std::vector<LayerActs> la;
+    size_t dres, dbuf, dqkv, dfch, dsum, partial, ws;
+    size_t partial_floats, ws_floats;
+    bool loss_ready;
+    const int32_t* inputs;
+};
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int64_t count_params(const gpt2_config& c, int64_t* o_layer, int64_t* o_wte, int64_t* o_wpe, int64_t* o_lnf) {
+    // Layer-major order of the module tree (GPT-2 from scratch with torch, 总体架构):
+    // wte, wpe, per block [ln_1 w,b; c_attn W,b; attn c_proj W,b; ln_2 w,b; c_fc W,b;
+    // mlp c_proj W,b], ln_f w,b.  Weights are (out, in) row-major.
+    const int64_t C = c.channels;
+    const int64_t sz[P_N] = {C, C, 3 * C * C, 3 * C, C * C, C, C, C, 4 * C * C, 4 * C, 4 * C * C, C};
+    int64_t o = 0;
+    if (o_wte) *o_wte = o;
+    o += (int64_t)c.vocab_size * C;
+    if (o_wpe) *o_wpe = o;
+    o += (int64_t)c.max_seq_len * C;
+    for (int l = 0; l < c.num_layers; ++l)
+        for (int i = 0; i < P_N; ++i) {
+            if (o_layer) o_layer[l * P_N + i] = o;
+            o += sz[i];
+        }
+    if (o_lnf) *o_lnf = o;
+    return o + 2 * C;
+}
+
+int validate(const gpt2_config* cfg, int B, int T, int dtype) {
+    if (!cfg) return fail(GPT2_E_INVAL, "cfg is NULL");
+    const gpt2_config& c = *cfg;
+    if (c.channels <= 0 || c.num_heads <= 0 || c.num_layers <= 0 || c.vocab_size < 2 || c.max_seq_len <= 0)
+        return fail(GPT2_E_INVAL, "non-positive model dimension");
+    if (c.channels % c.num_heads) return fail(GPT2_E_INVAL, "channels must be a multiple of num_heads");
+    if (c.channels % 8) return fail(GPT2_E_INVAL, "channels must be a multiple of 8");
+    const int hs = c.channels / c.num_heads;
+    if (hs != 16 && hs != 32 && hs != 64 && hs != 128)
+        return fail(GPT2_E_INVAL, "head size (channels / num_heads) must be 16, 32, 64 or 128");
+    if (c.channels > 2048) return fail(GPT2_E_INVAL, "channels must be <= 2048");
+    if (B < 1 || T < 1 || T > c.max_seq_len) return fail(GPT2_E_INVAL, "need B >= 1 and 1 <= T <= max_seq_len");
+    if ((int64_t)B * T > (1 << 30)) return fail(GPT2_E_INVAL, "B*T too large");
+    if (dtype != GPT2_FP32 && dtype != GPT2_BF16) return fail(GPT2_E_INVAL, "dtype must be GPT2_FP32 or GPT2_BF16");
+    return GPT2_OK;
+}
+
+// Computes every region's offset; returns the total byte size.
+size_t layout(gpt2_arena& a) {
+    const gpt2_config& c = a.cfg;
+    const int64_t C = c.channels, L = c.num_layers, BT = (int64_t)a.B * a.T, NH = c.num_heads;
+    const size_t es = a.act_size;
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = o;
+        o = align_up(o + bytes);
+        return at;
+    };
+    a.params = take(a.nparams * 4);
+    a.grads = take(a.nparams * 4);
+    a.adam_m = take(a.nparams * 4);
+    a.adam_v = take(a.nparams * 4);
+    a.params16 = a.dtype == GPT2_BF16 ? take(a.nparams * 2) : 0;
+    a.encoded = take(BT * C * es);
+    a.la.resize(L);
+    for (int l = 0; l < L; ++l) {
+        LayerActs& x = a.la[l];
+        x.ln1 = take(BT * C * es);
+        x.ln1s = take(BT * 2 * 4);
+        x.qkv = take(BT * 3 * C * es);
+        x.atty = take(BT * C * es);
+        x.lse = take(BT * NH * 4);
+        x.res2 = take(BT * C * es);
+        x.ln2 = take(BT * C * es);
+        x.ln2s = take(BT * 2 * 4);
+        x.fch = take(BT * 4 * C * es);
+        x.fchg = take(BT * 4 * C * es);
+        x.res3 = take(BT * C * es);
+    }
+    a.lnf = take(BT * C * es);
+    a.lnfs = take(BT * 2 * 4);
+    a.logits = take(BT * (int64_t)a.Vp * es);
+    a.losses = take(BT * 4);
+    a.loss = take(4);
+    // backward scratch, reused by every layer
+    a.dres = take(BT * C * es);
+    a.dbuf = take(BT * C * es);
+    a.dqkv = take(BT * 3 * C * es);
+    a.dfch = take(BT * 4 * C * es);
+    a.dsum = take(BT * NH * 4);
+    a.partial_floats = (size_t)512 * 2 * 4 * C;  // LayerNorm (<=512 blocks x 2C) and bias (64 x 4C) partials
+    a.partial = take(a.partial_floats * 4);
+    a.ws_floats = (size_t)16 * 4 * C * C;  // split-K partials of the largest block dW (4C x C), 16 splits
+    a.ws = take(a.ws_floats * 4);
+    return o;
+}
+
+template <class P>
+P* at(const gpt2_arena* a, size_t off) {
+    return (P*)(a->base + off);
+}
+
+int hip_check(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(GPT2_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
+    return GPT2_OK;
+}
+
+#define CHECK(expr, what)                                   \
+    do {                                                    \
+        int rc__ = hip_check((expr), what);                 \
+        if (rc__ != GPT2_OK) return rc__;                   \
+    } while (0)
+
+template <class T>
+struct Model {
+    gpt2_arena* a;
+    hipStream_t s;
+    int C, L, NH, V, Vp, B, S, BT, P;  // S: sequence length
+
+    Model(gpt2_arena* ar, hipStream_t st) : a(ar), s(st) {
+        C = a->cfg.channels; L = a->cfg.num_layers; NH = a->cfg.num_heads; V = a->cfg.vocab_size;
+        Vp = a->Vp; B = a->B; S = a->T; BT = B * S; P = a->cfg.max_seq_len;
+    }
+    float* master(int64_t off) const { return at<float>(a, a->params) + off; }
+    float* grad(int64_t off) const { return at<float>(a, a->grads) + off; }
+    // GEMM weight operand: the bf16 copy in BF16 mode, the master in FP32 mode.
+    const T* weight(int64_t off) const {
+        if (a->dtype == GPT2_BF16) return (const T*)(at<bf16>(a, a->params16) + off);
+        return (const T*)(at<float>(a, a->params) + off);
+    }
+    int64_t lp(int l, int i) const { return a->o_layer[l * P_N + i]; }
+    T* act(size_t off) const { return at<T>(a, off); }
+    float* f32(size_t off) const { return at<float>(a, off); }
+
+    int gemm_call(const void* A, int64_t lda, bool ak, const void* Bm, int64_t ldb, bool bk, void* Cm, int64_t ldc,
+                  int M, int N, int K, int epi, const float* bias = nullptr, const void* R = nullptr,
+                  void* C2 = nullptr) {
+        GemmArgs g;
+        g.A = A; g.B = Bm; g.C = Cm; g.C2 = C2; g.R = R; g.bias = bias;
+        g.M = M; g.N = N; g.K = K; g.lda = lda; g.ldb = ldb; g.ldc = ldc;
+        CHECK(gemm<T>(g, ak, bk, epi, f32(a->ws), a->ws_floats, s), "gemm");
+        return GPT2_OK;
+    }
+
+    int forward(const int32_t* inp, const int32_t* tgt) {
+        CHECK(encoder_forward<T>(act(a->encoded), inp, master(a->o_wte), master(a->o_wpe), BT, S, C, s), "encoder");
+        for (int l = 0; l < L; ++l) {
+            const LayerActs& x = a->la[l];
+            const T* xin = l == 0 ? act(a->encoded) : act(a->la[l - 1].res3);
+            CHECK(layernorm_forward<T>(act(x.ln1), f32(x.ln1s), xin, master(lp(l, P_LN1W)), master(lp(l, P_LN1B)), BT,
+                                       C, s), "ln1");
+            int rc;
+            // qkv = ln1 W_qkv^T + b
+            if ((rc = gemm_call(act(x.ln1), C, true, weight(lp(l, P_QKVW)), C, true, act(x.qkv), 3 * C, BT, 3 * C, C,
+                                EPI_BIAS, master(lp(l, P_QKVB)))))
+                return rc;
+            CHECK(attention_forward<T>(act(x.atty), f32(x.lse), act(x.qkv), B, S, C, NH, s), "attention");
+            // res2 = xin + atty W_proj^T + b
+            if ((rc = gemm_call(act(x.atty), C, true, weight(lp(l, P_PROJW)), C, true, act(x.res2), C, BT, C, C,
+                                EPI_BIAS_RES, master(lp(l, P_PROJB)), xin)))
+                return rc;
+            CHECK(layernorm_forward<T>(act(x.ln2), f32(x.ln2s), act(x.res2), master(lp(l, P_LN2W)),
+                                       master(lp(l, P_LN2B)), BT, C, s), "ln2");
+            // fch = ln2 W_fc^T + b, fchg = gelu(fch)
+            if ((rc = gemm_call(act(x.ln2), C, true, weight(lp(l, P_FCW)), C, true, act(x.fch), 4 * C, BT, 4 * C, C,
+                                EPI_BIAS_GELU, master(lp(l, P_FCB)), nullptr, act(x.fchg))))
+                return rc;
+            // res3 = res2 + fchg W_fcproj^T + b
+            if ((rc = gemm_call(act(x.fchg), 4 * C, true, weight(lp(l, P_FCPW)), 4 * C, true, act(x.res3), C, BT, C,
+                                4 * C, EPI_BIAS_RES, master(lp(l, P_FCPB)), act(x.res2))))
+                return rc;
+        }
+        CHECK(layernorm_forward<T>(act(a->lnf), f32(a->lnfs), act(a->la[L - 1].res3), master(a->o_lnfw),
+                                   master(a->o_lnfb), BT, C, s), "lnf");
+        // logits = lnf wte^T (tied lm_head, no bias); row stride Vp
+        int rc;
+        if ((rc = gemm_call(act(a->lnf), C, true, weight(a->o_wte), C, true, act(a->logits), Vp, BT, V, C, EPI_BIAS)))
+            return rc;
+        if (tgt) {
+            CHECK(crossentropy_fused<T>(act(a->logits), f32(a->losses), tgt, BT, V, Vp, 1.0f / BT, s), "crossentropy");
+            CHECK(mean_loss(f32(a->loss), f32(a->losses), BT, s), "mean loss");
+        }
+        return GPT2_OK;
+    }
+
+    int backward() {
+        int rc;
+        T* dz = act(a->logits);
+        T* dres = act(a->dres);
+        T* dbuf = act(a->dbuf);
+        T* dqkv = act(a->dqkv);
+        T* dfch = act(a->dfch);
+        float* part = f32(a->partial);
+        // lm_head: dlnf = dz wte ; dwte = dz^T lnf (overwrites; the encoder adds later)
+        if ((rc = gemm_call(dz, Vp, true, weight(a->o_wte), C, false, dbuf, C, BT, C, V, EPI_BIAS))) return rc;
+        if ((rc = gemm_call(dz, Vp, false, act(a->lnf), C, false, grad(a->o_wte), C, V, C, BT, EPI_F32))) return rc;
+        CHECK(layernorm_backward<T>(dres, grad(a->o_lnfw), grad(a->o_lnfb), dbuf, act(a->la[L - 1].res3), f32(a->lnfs),
+                                    master(a->o_lnfw), BT, C, part, a->partial_floats, s, false), "lnf backward");
+        for (int l = L - 1; l >= 0; --l) {
+            const LayerActs& x = a->la[l];
+            const T* xin = l == 0 ? act(a->encoded) : act(a->la[l - 1].res3);
+            // mlp c_proj: dfch = (dres W_fcproj) * gelu'(fch); dW = dres^T fchg; db = colsum(dres)
+            if ((rc = gemm_call(dres, C, true, weight(lp(l, P_FCPW)), 4 * C, false, dfch, 4 * C, BT, 4 * C, C,
+                                EPI_GELU_BWD, nullptr, act(x.fch))))
+                return rc;
+            if ((rc = gemm_call(dres, C, false, act(x.fchg), 4 * C, false, grad(lp(l, P_FCPW)), 4 * C, C, 4 * C, BT,
+                                EPI_F32)))
+                return rc;
+            CHECK(bias_grad<T>(grad(lp(l, P_FCPB)), dres, BT, C, C, part, a->partial_floats, s), "fcproj bias");
+            // c_fc: dln2 = dfch W_fc; dW = dfch^T ln2; db = colsum(dfch)
+            if ((rc = gemm_call(dfch, 4 * C, true, weight(lp(l, P_FCW)), C, false, dbuf, C, BT, C, 4 * C, EPI_BIAS)))
+                return rc;
+            if ((rc = gemm_call(dfch, 4 * C, false, act(x.ln2), C, false, grad(lp(l, P_FCW)), C, 4 * C, C, BT,
+                                EPI_F32)))
+                return rc;
+            CHECK(bias_grad<T>(grad(lp(l, P_FCB)), dfch, BT, 4 * C, 4 * C, part, a->partial_floats, s), "fc bias");
+            // ln_2: dres += LN backward
+            CHECK(layernorm_backward<T>(dres, grad(lp(l, P_LN2W)), grad(lp(l, P_LN2B)), dbuf, act(x.res2), f32(x.ln2s),
+                                        master(lp(l, P_LN2W)), BT, C, part, a->partial_floats, s, true), "ln2 backward");
+            // attn c_proj: datty = dres W_proj; dW = dres^T atty; db = colsum(dres)
+            if ((rc = gemm_call(dres, C, true, weight(lp(l, P_PROJW)), C, false, dbuf, C, BT, C, C, EPI_BIAS)))
+                return rc;
+            if ((rc = gemm_call(dres, C, false, act(x.atty), C, false, grad(lp(l, P_PROJW)), C, C, C, BT, EPI_F32)))
+                return rc;
+            CHECK(bias_grad<T>(grad(lp(l, P_PROJB)), dres, BT, C, C, part, a->partial_floats, s), "proj bias");
+            // attention
+            CHECK(attention_backward<T>(dqkv, f32(a->dsum), dbuf, act(x.atty), act(x.qkv), f32(x.lse), B, S, C, NH, s),
+                  "attention backward");
+            // c_attn: dln1 = dqkv W_qkv; dW = dqkv^T ln1; db = colsum(dqkv)
+            if ((rc = gemm_call(dqkv, 3 * C, true, weight(lp(l, P_QKVW)), C, false, dbuf, C, BT, C, 3 * C, EPI_BIAS)))
+                return rc;
+            if ((rc = gemm_call(dqkv, 3 * C, false, act(x.ln1), C, false, grad(lp(l, P_QKVW)), C, 3 * C, C, BT,
+                                EPI_F32)))
+                return rc;
+            CHECK(bias_grad<T>(grad(lp(l, P_QKVB)), dqkv, BT, 3 * C, 3 * C, part, a->partial_floats, s), "qkv bias");
+            // ln_1: dres += LN backward (dres is now d xin)
+            CHECK(layernorm_backward<T>(dres, grad(lp(l, P_LN1W)), grad(lp(l, P_LN1B)), dbuf, xin, f32(x.ln1s),
+                                        master(lp(l, P_LN1W)), BT, C, part, a->partial_floats, s, true), "ln1 backward");
+        }
+        CHECK(encoder_backward<T>(grad(a->o_wte), grad(a->o_wpe), dres, a->inputs, B, S, P, C, s), "encoder backward");
+        return GPT2_OK;
+    }
+};
+
+}  // namespace
+
+extern "C" {
+
+const char* gpt2_last_error(void) { return g_error.c_str(); }
+
+int64_t gpt2_num_parameters(const gpt2_config* cfg) {
+    if (!cfg) return -1;
+    return count_params(*cfg, nullptr, nullptr, nullptr, nullptr);
+}
+
+int gpt2_alloc_arena(const gpt2_config* cfg, int32_t B, int32_t T, int32_t dtype, void* device_base,
+                     size_t device_bytes, size_t* required_bytes, gpt2_arena** out) {
+    if (out) *out = nullptr;
+    int rc = validate(cfg, B, T, dtype);
+    if (rc) return rc;
+    gpt2_arena* a = new (std::nothrow) gpt2_arena();
+    if (!a) return fail(GPT2_E_INVAL, "host allocation failed");
+    a->cfg = *cfg;
+    a->B = B;
+    a->T = T;
+    a->dtype = dtype;
+    a->Vp = (cfg->vocab_size + 63) / 64 * 64;
+    a->hs = cfg->channels / cfg->num_heads;
+    a->act_size = dtype == GPT2_BF16 ? 2 : 4;
+    a->o_layer.resize((size_t)cfg->num_layers * P_N);
+    int64_t o_lnf = 0;
+    a->nparams = count_params(*cfg, a->o_layer.data(), &a->o_wte, &a->o_wpe, &o_lnf);
+    a->o_lnfw = o_lnf;
+    a->o_lnfb = o_lnf + cfg->channels;
+    size_t need = layout(*a);
+    if (required_bytes) *required_bytes = need;
+    if (!device_base) {
+        delete a;
+        return GPT2_OK;
+    }
+    if ((uintptr_t)device_base % kAlign) {
+        delete a;
+        return fail(GPT2_E_ALIGN, "device_base must be 256-byte aligned");
+    }
+    if (device_bytes < need) {
+        delete a;
+        return fail(GPT2_E_SIZE, "device buffer too small: need " + std::to_string(need) + " bytes");
+    }
+    a->base = (char*)device_base;
+    a->bytes = device_bytes;
+    a->loss_ready = false;
+    a->inputs = nullptr;
+    if (!out) {
+        delete a;
+        return fail(GPT2_E_INVAL, "out is NULL");
+    }
+    *out = a;
+    return GPT2_OK;
+}
+
+int gpt2_free_arena(gpt2_arena* a) {
+    delete a;
+    return GPT2_OK;
+}
+
+int gpt2_sync_weights(gpt2_arena* a, void* stream) {
+    if (!a) return fail(GPT2_E_INVAL, "arena is NULL");
+    if (a->dtype == GPT2_BF16)
+        return hip_check(cast_bf16(at<bf16>(a, a->params16), at<float>(a, a->params), a->nparams, (hipStream_t)stream),
+                         "cast");
+    return GPT2_OK;
+}
+
+int gpt2_forward(gpt2_arena* a, const int32_t* d_inputs, const int32_t* d_targets, void* stream) {
+    if (!a || !d_inputs) return fail(GPT2_E_INVAL, "arena and inputs are required");
+    a->loss_ready = false;
+    a->inputs = d_inputs;
+    int rc = a->dtype == GPT2_BF16 ? Model<bf16>(a, (hipStream_t)stream).forward(d_inputs, d_targets)
+                                   : Model<float>(a, (hipStream_t)stream).forward(d_inputs, d_targets);
+    if (rc == GPT2_OK && d_targets) a->loss_ready = true;
+    return rc;
+}
+
+int gpt2_backward(gpt2_arena* a, void* stream) {
+    if (!a) return fail(GPT2_E_INVAL, "arena is NULL");
+    if (!a->loss_ready) return fail(GPT2_E_STATE, "backward needs a preceding forward with targets");
+    a->loss_ready = false;  // dlogits are consumed
+    return a->dtype == GPT2_BF16 ? Model<bf16>(a, (hipStream_t)stream).backward()
+                                 : Model<float>(a, (hipStream_t)stream).backward();
+}
+
+int gpt2_adamw_step(gpt2_arena* a, float lr, float beta1, float beta2, float eps, float weight_decay, int32_t step,
+                    void* stream) {
+    if (!a) return fail(GPT2_E_INVAL, "arena is NULL");
+    if (step < 1) return fail(GPT2_E_INVAL, "step must be >= 1");
+    const float c1 = (float)(1.0 - pow((double)beta1, (double)step));
+    const float c2 = (float)(1.0 - pow((double)beta2, (double)step));
+    bf16* p16 = a->dtype == GPT2_BF16 ? at<bf16>(a, a->params16) : nullptr;
+    return hip_check(adamw(at<float>(a, a->params), at<float>(a, a->grads), at<float>(a, a->adam_m),
+                           at<float>(a, a->adam_v), p16, a->nparams, lr, beta1, beta2, eps, weight_decay, c1, c2,
+                           (hipStream_t)stream),
+                     "adamw");
+}
+
+int gpt2_tensor_info(const gpt2_arena* a, int32_t id, int32_t layer, size_t* byte_offset, int64_t* rows,
+                     int64_t* cols, int64_t* row_stride, int32_t* dtype) {
+    if (!a) return fail(GPT2_E_INVAL, "arena is NULL");
+    const int64_t BT = (int64_t)a->B * a->T, C = a->cfg.channels, NH = a->cfg.num_heads;
+    const int act = a->dtype;
+    size_t off = 0;
+    int64_t r = 0, c = 0, ld = -1;
+    int32_t dt = GPT2_FP32;
+    const bool per_layer = id >= GPT2_T_LN1;
+    if (per_layer && (layer < 0 || layer >= a->cfg.num_layers)) return fail(GPT2_E_INVAL, "layer out of range");
+    const LayerActs* x = per_layer ? &a->la[layer] : nullptr;
+    switch (id) {
+        case GPT2_T_PARAMS: off = a->params; r = 1; c = a->nparams; break;
+        case GPT2_T_GRADS: off = a->grads; r = 1; c = a->nparams; break;
+        case GPT2_T_ADAM_M: off = a->adam_m; r = 1; c = a->nparams; break;
+        case GPT2_T_ADAM_V: off = a->adam_v; r = 1; c = a->nparams; break;
+        case GPT2_T_PARAMS_BF16:
+            if (a->dtype != GPT2_BF16) return fail(GPT2_E_INVAL, "no bf16 copy in fp32 mode");
+            off = a->params16; r = 1; c = a->nparams; dt = GPT2_BF16; break;
+        case GPT2_T_ENCODED: off = a->encoded; r = BT; c = C; dt = act; break;
+        case GPT2_T_LNF: off = a->lnf; r = BT; c = C; dt = act; break;
+        case GPT2_T_LNF_STATS: off = a->lnfs; r = BT; c = 2; break;
+        case GPT2_T_LOGITS: off = a->logits; r = BT; c = a->cfg.vocab_size; ld = a->Vp; dt = act; break;
+        case GPT2_T_LOSSES: off = a->losses; r = BT; c = 1; break;
+        case GPT2_T_LOSS: off = a->loss; r = 1; c = 1; break;
+        case GPT2_T_LN1: off = x->ln1; r = BT; c = C; dt = act; break;
+        case GPT2_T_LN1_STATS: off = x->ln1s; r = BT; c = 2; break;
+        case GPT2_T_QKV: off = x->qkv; r = BT; c = 3 * C; dt = act; break;
+        case GPT2_T_ATTY: off = x->atty; r = BT; c = C; dt = act; break;
+        case GPT2_T_ATT_LSE: off = x->lse; r = (int64_t)a->B * NH; c = a->T; break;
+        case GPT2_T_RESIDUAL2: off = x->res2; r = BT; c = C; dt = act; break;
+        case GPT2_T_LN2: off = x->ln2; r = BT; c = C; dt = act; break;
+        case GPT2_T_LN2_STATS: off = x->ln2s; r = BT; c = 2; break;
+        case GPT2_T_FCH: off = x->fch; r = BT; c = 4 * C; dt = act; break;
+        case GPT2_T_FCH_GELU: off = x->fchg; r = BT; c = 4 * C; dt = act; break;
+        case GPT2_T_RESIDUAL3: off = x->res3; r = BT; c = C; dt = act; break;
+        default: return fail(GPT2_E_INVAL, "unknown tensor id");
+    }
+    if (ld < 0) ld = c;
+    if (byte_offset) *byte_offset = off;
+    if (rows) *rows = r;
+    if (cols) *cols = c;
+    if (row_stride) *row_stride = ld;
+    if (dtype) *dtype = dt;
+    return GPT2_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,88 @@
+// Launch wrappers of the gfx950 kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace gpt2 {
+
+// Records the launch(es) in its lifetime when the launch profiler is on.
+struct ProfScope {
+    ProfScope(hipStream_t s, const char* name, double flops, double bytes);
+    ~ProfScope();
+    int idx;
+    hipStream_t stream;
+};
+
+// ---------------------------------------------------------------- GEMM
+// C[m, n] = epilogue( sum_k A(m, k) * B(n, k) ), fp32 accumulation on MFMA.
+// A(m, k) = A[m*lda + k] when a_kcontig, else A[k*lda + m]; likewise B(n, k).
+enum GemmEpi {
+    EPI_BIAS = 0,       // C = acc + bias[n]            (bias may be null)
+    EPI_BIAS_RES = 1,   // C = R[m, n] + acc + bias[n]  (R has row stride ldc)
+    EPI_BIAS_GELU = 2,  // C = acc + bias[n], C2 = gelu(C)
+    EPI_GELU_BWD = 3,   // C = acc * gelu'(R[m, n])
+    EPI_F32 = 4         // fp32 C = acc (split-K partials or a direct fp32 result)
+};
+
+struct GemmArgs {
+    const void* A;
+    const void* B;
+    void* C;
+    void* C2;
+    const void* R;
+    const float* bias;
+    int M, N, K;
+    int64_t lda, ldb, ldc;
+};
+
+// Returns hipSuccess or the launch error.  T in {float, bf16}: operand type;
+// outputs of EPI_BIAS..EPI_GELU_BWD are T, EPI_F32 writes fp32.
+template <class T>
+hipError_t gemm(const GemmArgs& a, bool a_kcontig, bool b_kcontig, int epi, float* splitk_ws,
+                size_t splitk_ws_floats, hipStream_t s);
+
+// ---------------------------------------------------------------- element-wise / row kernels
+template <class T>
+hipError_t encoder_forward(T* out, const int32_t* tok, const float* wte, const float* wpe, int BT, int T_, int C,
+                           hipStream_t s);
+template <class T>
+hipError_t layernorm_forward(T* out, float* stats, const T* inp, const float* w, const float* b, int N, int C,
+                             hipStream_t s);
+// dres (+)= LN backward dx (accumulate selects += or =); per-block partial (dw, db) sums into `partial`
+// [nblocks][2C], then reduced into dw, db (overwrite).
+template <class T>
+hipError_t layernorm_backward(T* dres, float* dw, float* db, const T* dout, const T* inp, const float* stats,
+                              const float* w, int N, int C, float* partial, size_t partial_floats, hipStream_t s,
+                              bool accumulate);
+// dbias[n] = sum_m dout[m, n] (overwrite), deterministic two-stage.
+template <class T>
+hipError_t bias_grad(float* dbias, const T* dout, int M, int N, int64_t ld, float* partial, size_t partial_floats,
+                     hipStream_t s);
+// Fused softmax cross-entropy: losses[i] = logsumexp(z_i) - z_i[y_i]; z_i is
+// overwritten by (softmax(z_i) - onehot(y_i)) * dscale; padding columns V..ldz-1 zeroed.
+template <class T>
+hipError_t crossentropy_fused(T* logits, float* losses, const int32_t* targets, int N, int V, int64_t ldz,
+                              float dscale, hipStream_t s);
+hipError_t mean_loss(float* loss, const float* losses, int N, hipStream_t s);
+// dwte[tok] += dx rows (deterministic), dwpe[t] = sum_b dx[b, t] for t < T, 0 for T <= t < P.
+template <class T>
+hipError_t encoder_backward(float* dwte, float* dwpe, const T* dx, const int32_t* tok, int B, int T_, int P, int C,
+                            hipStream_t s);
+hipError_t adamw(float* p, const float* g, float* m, float* v, bf16* p16, int64_t n, float lr, float b1, float b2,
+                 float eps, float wd, float c1, float c2, hipStream_t s);
+hipError_t cast_bf16(bf16* out, const float* in, int64_t n, hipStream_t s);
+hipError_t splitk_reduce(float* out, const float* ws, int splits, int64_t n, hipStream_t s);
+
+// ---------------------------------------------------------------- attention
+// qkv [B*T, 3C] (q | k | v, head h at columns h*hs), out [B*T, C], lse fp32 [B, NH, T].
+template <class T>
+hipError_t attention_forward(T* out, float* lse, const T* qkv, int B, int T_, int C, int NH, hipStream_t s);
+// dqkv [B*T, 3C] (overwrite) from dout [B*T, C]; `dsum` fp32 [B, NH, T] scratch.
+template <class T>
+hipError_t attention_backward(T* dqkv, float* dsum, const T* dout, const T* out, const T* qkv, const float* lse,
+                              int B, int T_, int C, int NH, hipStream_t s);
+
+}  // namespace gpt2

@@ -1,0 +1,519 @@
+// Memory-bound kernels of the GPT-2 training step (gfx950, wave64):
+// embedding gather / scatter, LayerNorm forward / backward, bias gradients,
+// fused softmax cross-entropy, AdamW, and small reductions.
+#include "kernels.h"
+
+namespace gpt2 {
+
+static inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+// ============================================================================ encoder
+// "GPT-2 from scratch with torch", token/position embedding: x[b, t] = wte[tok[b, t]] + wpe[t].
+// Reads the fp32 master tables and rounds once to the activation type.
+template <class T>
+__global__ __launch_bounds__(256) void encoder_forward_kernel(T* out, const int32_t* tok, const float* wte,
+                                                              const float* wpe, int BT, int T_, int C) {
+    const int c4 = C / 4;
+    int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)BT * c4) return;
+    int row = (int)(i / c4), c = (int)(i % c4) * 4;
+    int t = row % T_;
+    float4 a = *(const float4*)(wte + (int64_t)tok[row] * C + c);
+    float4 p = *(const float4*)(wpe + (int64_t)t * C + c);
+    T* o = out + (int64_t)row * C + c;
+    o[0] = from_f32<T>(a.x + p.x);
+    o[1] = from_f32<T>(a.y + p.y);
+    o[2] = from_f32<T>(a.z + p.z);
+    o[3] = from_f32<T>(a.w + p.w);
+}
+
+template <class T>
+hipError_t encoder_forward(T* out, const int32_t* tok, const float* wte, const float* wpe, int BT, int T_, int C,
+                           hipStream_t s) {
+    ProfScope prof(s, "encoder_fwd", 0, (double)BT * C * (8 + sizeof(T)));
+    hipLaunchKernelGGL(encoder_forward_kernel<T>, dim3(cdiv((int64_t)BT * (C / 4), 256)), dim3(256), 0, s, out, tok,
+                       wte, wpe, BT, T_, C);
+    return hipGetLastError();
+}
+
+// ============================================================================ LayerNorm forward
+// "GPT-2 from scratch with torch", Transformer block (LayerNorm, eps 1e-5): per row
+// mean and biased variance over C; y = (x - mean) * rstd * w + b.  One wave per row;
+// the row stays in registers between the two statistics passes.
+template <class T, int MAXCH>
+__global__ __launch_bounds__(256) void layernorm_forward_kernel(T* out, float* stats, const T* inp, const float* w,
+                                                                const float* b, int N, int C) {
+    constexpr int KV = Vec16<T>::N;
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= N) return;
+    const T* x = inp + (int64_t)row * C;
+    float v[MAXCH][KV];
+    float sum = 0.f;
+#pragma unroll
+    for (int ch = 0; ch < MAXCH; ++ch) {
+        int c = (ch * 64 + lane) * KV;
+        if (c < C) {
+            unpack16<T>(ld16(x + c), v[ch]);
+#pragma unroll
+            for (int e = 0; e < KV; ++e) sum += v[ch][e];
+        }
+    }
+    const float mean = wave_sum(sum) / C;
+    float sq = 0.f;
+#pragma unroll
+    for (int ch = 0; ch < MAXCH; ++ch) {
+        int c = (ch * 64 + lane) * KV;
+        if (c < C) {
+#pragma unroll
+            for (int e = 0; e < KV; ++e) {
+                float d = v[ch][e] - mean;
+                sq += d * d;
+            }
+        }
+    }
+    const float rstd = 1.0f / sqrtf(wave_sum(sq) / C + 1e-5f);
+    T* y = out + (int64_t)row * C;
+#pragma unroll
+    for (int ch = 0; ch < MAXCH; ++ch) {
+        int c = (ch * 64 + lane) * KV;
+        if (c < C) {
+            float o[KV];
+#pragma unroll
+            for (int e = 0; e < KV; ++e) o[e] = (v[ch][e] - mean) * rstd * w[c + e] + b[c + e];
+            st16(y + c, pack16<T>(o));
+        }
+    }
+    if (lane == 0) {
+        stats[2 * row] = mean;
+        stats[2 * row + 1] = rstd;
+    }
+}
+
+template <class T>
+hipError_t layernorm_forward(T* out, float* stats, const T* inp, const float* w, const float* b, int N, int C,
+                             hipStream_t s) {
+    constexpr int KV = Vec16<T>::N;
+    int ch = cdiv(C, 64 * KV);
+    dim3 grid(cdiv(N, 4)), block(256);
+    ProfScope prof(s, "layernorm_fwd", 0, (double)N * C * 2 * sizeof(T) + 8.0 * N);
+    if (ch <= 1) hipLaunchKernelGGL((layernorm_forward_kernel<T, 1>), grid, block, 0, s, out, stats, inp, w, b, N, C);
+    else if (ch <= 2) hipLaunchKernelGGL((layernorm_forward_kernel<T, 2>), grid, block, 0, s, out, stats, inp, w, b, N, C);
+    else if (ch <= 4) hipLaunchKernelGGL((layernorm_forward_kernel<T, 4>), grid, block, 0, s, out, stats, inp, w, b, N, C);
+    else if (ch <= 8) hipLaunchKernelGGL((layernorm_forward_kernel<T, 8>), grid, block, 0, s, out, stats, inp, w, b, N, C);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+// ============================================================================ LayerNorm backward
+// With xhat = (x - mean) * rstd and dxhat = dy * w:
+//   dx = rstd * (dxhat - mean_c(dxhat) - xhat * mean_c(dxhat * xhat))   (added into dres)
+//   dw = sum_rows dy * xhat,  db = sum_rows dy                          (per-block partials)
+// One wave per row, grid-stride over rows; each lane owns the same columns in
+// every row, so the dw/db partial sums stay in registers.
+template <class T, int MAXCH>
+__global__ __launch_bounds__(256) void layernorm_backward_kernel(T* dres, float* partial, const T* dout, const T* inp,
+                                                                 const float* stats, const float* w, int N, int C,
+                                                                 int accumulate) {
+    constexpr int KV = Vec16<T>::N;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    float pw[MAXCH][KV], pb[MAXCH][KV];
+#pragma unroll
+    for (int ch = 0; ch < MAXCH; ++ch)
+#pragma unroll
+        for (int e = 0; e < KV; ++e) pw[ch][e] = pb[ch][e] = 0.f;
+
+    for (int row = blockIdx.x * 4 + wave; row < N; row += gridDim.x * 4) {
+        const float mean = stats[2 * row], rstd = stats[2 * row + 1];
+        const T* dy = dout + (int64_t)row * C;
+        const T* x = inp + (int64_t)row * C;
+        float g[MAXCH][KV], xh[MAXCH][KV];
+        float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+        for (int ch = 0; ch < MAXCH; ++ch) {
+            int c = (ch * 64 + lane) * KV;
+            if (c < C) {
+                unpack16<T>(ld16(dy + c), g[ch]);
+                unpack16<T>(ld16(x + c), xh[ch]);
+#pragma unroll
+                for (int e = 0; e < KV; ++e) {
+                    xh[ch][e] = (xh[ch][e] - mean) * rstd;
+                    pw[ch][e] += g[ch][e] * xh[ch][e];
+                    pb[ch][e] += g[ch][e];
+                    float dxh = g[ch][e] * w[c + e];
+                    s1 += dxh;
+                    s2 += dxh * xh[ch][e];
+                }
+            }
+        }
+        s1 = wave_sum(s1) / C;
+        s2 = wave_sum(s2) / C;
+        T* dx = dres + (int64_t)row * C;
+#pragma unroll
+        for (int ch = 0; ch < MAXCH; ++ch) {
+            int c = (ch * 64 + lane) * KV;
+            if (c < C) {
+                float prev[KV], o[KV];
+                if (accumulate) unpack16<T>(ld16(dx + c), prev);
+#pragma unroll
+                for (int e = 0; e < KV; ++e) {
+                    float dxh = g[ch][e] * w[c + e];
+                    o[e] = rstd * (dxh - s1 - xh[ch][e] * s2) + (accumulate ? prev[e] : 0.f);
+                }
+                st16(dx + c, pack16<T>(o));
+            }
+        }
+    }
+    // reduce the four waves' column partials through LDS, write this block's row of `partial`
+    __shared__ float red[4][2][64 * KV * MAXCH];
+#pragma unroll
+    for (int ch = 0; ch < MAXCH; ++ch)
+#pragma unroll
+        for (int e = 0; e < KV; ++e) {
+            red[wave][0][(ch * 64 + lane) * KV + e] = pw[ch][e];
+            red[wave][1][(ch * 64 + lane) * KV + e] = pb[ch][e];
+        }
+    __syncthreads();
+    float* out = partial + (int64_t)blockIdx.x * 2 * C;
+    for (int c = threadIdx.x; c < C; c += 256) {
+        out[c] = (red[0][0][c] + red[1][0][c]) + (red[2][0][c] + red[3][0][c]);
+        out[C + c] = (red[0][1][c] + red[1][1][c]) + (red[2][1][c] + red[3][1][c]);
+    }
+}
+
+// out[c] = sum over nb blocks of partial[blk][c] for c < n (fixed order).
+__global__ __launch_bounds__(256) void column_reduce_kernel(float* out0, float* out1, const float* partial, int nb,
+                                                            int n, int split) {
+    int c = blockIdx.x * 256 + threadIdx.x;
+    if (c >= n) return;
+    float acc = 0.f;
+    for (int k = 0; k < nb; ++k) acc += partial[(int64_t)k * n + c];
+    if (c < split) out0[c] = acc;
+    else out1[c - split] = acc;
+}
+
+template <class T>
+hipError_t layernorm_backward(T* dres, float* dw, float* db, const T* dout, const T* inp, const float* stats,
+                              const float* w, int N, int C, float* partial, size_t partial_floats, hipStream_t s,
+                              bool accumulate) {
+    constexpr int KV = Vec16<T>::N;
+    int ch = cdiv(C, 64 * KV);
+    int nb = cdiv(N, 4);
+    if (nb > 512) nb = 512;
+    while ((size_t)nb * 2 * C > partial_floats && nb > 1) nb /= 2;
+    if ((size_t)nb * 2 * C > partial_floats) return hipErrorInvalidValue;
+    dim3 grid(nb), block(256);
+    int acc = accumulate ? 1 : 0;
+    ProfScope prof(s, "layernorm_bwd", 0, (double)N * C * sizeof(T) * (accumulate ? 4 : 3) + 8.0 * N);
+    if (ch <= 1) hipLaunchKernelGGL((layernorm_backward_kernel<T, 1>), grid, block, 0, s, dres, partial, dout, inp, stats, w, N, C, acc);
+    else if (ch <= 2) hipLaunchKernelGGL((layernorm_backward_kernel<T, 2>), grid, block, 0, s, dres, partial, dout, inp, stats, w, N, C, acc);
+    else if (ch <= 4) hipLaunchKernelGGL((layernorm_backward_kernel<T, 4>), grid, block, 0, s, dres, partial, dout, inp, stats, w, N, C, acc);
+    else return hipErrorInvalidValue;
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    ProfScope prof2(s, "column_reduce", 0, 4.0 * nb * 2 * C + 8.0 * C);
+    hipLaunchKernelGGL(column_reduce_kernel, dim3(cdiv(2 * C, 256)), dim3(256), 0, s, dw, db, partial, nb, 2 * C, C);
+    return hipGetLastError();
+}
+
+
+// ============================================================================ bias gradients
+// dbias[n] = sum_m dout[m, n]: blocks of (256 columns x rows/RB), partials reduced in order.
+template <class T>
+__global__ __launch_bounds__(256) void bias_grad_kernel(float* partial, const T* dout, int M, int N, int64_t ld,
+                                                        int rows_per) {
+    int n = blockIdx.x * 256 + threadIdx.x;
+    if (n >= N) return;
+    int r0 = blockIdx.y * rows_per, r1 = min(M, r0 + rows_per);
+    float acc = 0.f;
+    for (int r = r0; r < r1; ++r) acc += to_f32(dout[(int64_t)r * ld + n]);
+    partial[(int64_t)blockIdx.y * N + n] = acc;
+}
+
+template <class T>
+hipError_t bias_grad(float* dbias, const T* dout, int M, int N, int64_t ld, float* partial, size_t partial_floats,
+                     hipStream_t s) {
+    int rb = 64;
+    while ((size_t)rb * N > partial_floats && rb > 1) rb /= 2;
+    if ((size_t)rb * N > partial_floats) return hipErrorInvalidValue;
+    int rows_per = cdiv(M, rb);
+    rb = cdiv(M, rows_per);
+    ProfScope prof(s, "bias_grad", 0, (double)M * N * sizeof(T) + 4.0 * N);
+    hipLaunchKernelGGL(bias_grad_kernel<T>, dim3(cdiv(N, 256), rb), dim3(256), 0, s, partial, dout, M, N, ld, rows_per);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    ProfScope prof2(s, "column_reduce", 0, 4.0 * rb * N + 4.0 * N);
+    hipLaunchKernelGGL(column_reduce_kernel, dim3(cdiv(N, 256)), dim3(256), 0, s, dbias, dbias, partial, rb, N, N);
+    return hipGetLastError();
+}
+
+// ============================================================================ softmax cross-entropy
+// "从头搭建GPT(Andrej Karpathy) 笔记", 计算loss: loss_i = logsumexp(z_i) - z_i[y_i]; the mean
+// over the B*T rows is the training loss, so d loss / d z_i = (softmax(z_i) - onehot(y_i)) / (B*T).
+// One block per row: an online (max, sum) pass, then the gradient overwrites z_i in place.
+__device__ __forceinline__ void online_merge(float& m, float& s, float m2, float s2) {
+    float mn = fmaxf(m, m2);
+    if (mn == -INFINITY) return;
+    s = s * __expf(m - mn) + s2 * __expf(m2 - mn);
+    m = mn;
+}
+
+template <class T>
+__global__ __launch_bounds__(1024) void crossentropy_kernel(T* logits, float* losses, const int32_t* targets, int V,
+                                                            int64_t ldz, float dscale) {
+    constexpr int KV = Vec16<T>::N;
+    const int row = blockIdx.x;
+    T* z = logits + (int64_t)row * ldz;
+    const int nvec = V / KV;  // full 16-byte vectors inside [0, V)
+    float m = -INFINITY, s = 0.f;
+    for (int i = threadIdx.x; i < nvec; i += 1024) {
+        float v[KV];
+        unpack16<T>(ld16(z + i * KV), v);
+        float mx = v[0];
+#pragma unroll
+        for (int e = 1; e < KV; ++e) mx = fmaxf(mx, v[e]);
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < KV; ++e) ss += __expf(v[e] - mx);
+        online_merge(m, s, mx, ss);
+    }
+    for (int i = nvec * KV + threadIdx.x; i < V; i += 1024) online_merge(m, s, to_f32(z[i]), 1.f);
+    // block reduction of (m, s)
+    __shared__ float sm[16], ss_[16];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        float m2 = __shfl_xor(m, o, 64), s2 = __shfl_xor(s, o, 64);
+        online_merge(m, s, m2, s2);
+    }
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) { sm[wave] = m; ss_[wave] = s; }
+    __syncthreads();
+    m = sm[0]; s = ss_[0];
+    for (int w2 = 1; w2 < 16; ++w2) online_merge(m, s, sm[w2], ss_[w2]);
+    const float lse = m + __logf(s);
+    const int y = targets[row];
+    if (threadIdx.x == 0) losses[row] = lse - to_f32(z[y]);
+    __syncthreads();  // z[y] read before it is overwritten
+    for (int i = threadIdx.x; i < nvec; i += 1024) {
+        float v[KV];
+        unpack16<T>(ld16(z + i * KV), v);
+#pragma unroll
+        for (int e = 0; e < KV; ++e) {
+            int col = i * KV + e;
+            v[e] = (__expf(v[e] - lse) - (col == y ? 1.f : 0.f)) * dscale;
+        }
+        st16(z + i * KV, pack16<T>(v));
+    }
+    for (int i = nvec * KV + threadIdx.x; i < (int)ldz; i += 1024) {
+        float g = 0.f;
+        if (i < V) g = (__expf(to_f32(z[i]) - lse) - (i == y ? 1.f : 0.f)) * dscale;
+        z[i] = from_f32<T>(g);
+    }
+}
+
+template <class T>
+hipError_t crossentropy_fused(T* logits, float* losses, const int32_t* targets, int N, int V, int64_t ldz,
+                              float dscale, hipStream_t s) {
+    ProfScope prof(s, "crossentropy", 0, 2.0 * N * ldz * sizeof(T) + 8.0 * N);
+    hipLaunchKernelGGL(crossentropy_kernel<T>, dim3(N), dim3(1024), 0, s, logits, losses, targets, V, ldz, dscale);
+    return hipGetLastError();
+}
+
+__global__ __launch_bounds__(1024) void mean_loss_kernel(float* loss, const float* losses, int N) {
+    float acc = 0.f;
+    for (int i = threadIdx.x; i < N; i += 1024) acc += losses[i];
+    __shared__ float red[16];
+    acc = wave_sum(acc);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float t = 0.f;
+        for (int w = 0; w < 16; ++w) t += red[w];
+        loss[0] = t / N;
+    }
+}
+
+hipError_t mean_loss(float* loss, const float* losses, int N, hipStream_t s) {
+    ProfScope prof(s, "mean_loss", 0, 4.0 * N);
+    hipLaunchKernelGGL(mean_loss_kernel, dim3(1), dim3(1024), 0, s, loss, losses, N);
+    return hipGetLastError();
+}
+
+// ============================================================================ encoder backward
+// dwte[v] += sum of dx rows whose token is v.  The first position holding token v
+// (its "leader") sums every matching row in increasing position order and is the
+// only writer of dwte[v], so the result is deterministic without atomics.
+// Matches are found 256 positions at a time with wave ballots.
+template <class T>
+__global__ __launch_bounds__(256) void encoder_backward_wte_kernel(float* dwte, const T* dx, const int32_t* tok,
+                                                                   int BT, int C) {
+    const int pos = blockIdx.x;
+    const int v = tok[pos];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    __shared__ unsigned long long mask[4];
+    // leader check: no earlier position holds v
+    for (int j0 = 0; j0 < pos; j0 += 256) {
+        int j = j0 + threadIdx.x;
+        int hit = (j < pos) && tok[j] == v;
+        if (__syncthreads_or(hit)) return;
+    }
+    constexpr int MAXC = 8;  // columns per thread: C <= 2048
+    float acc[MAXC];
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) acc[i] = 0.f;
+    for (int j0 = pos; j0 < BT; j0 += 256) {
+        int j = j0 + threadIdx.x;
+        unsigned long long bal = __ballot((j < BT) && tok[j] == v);
+        if (lane == 0) mask[wave] = bal;
+        __syncthreads();
+        for (int w = 0; w < 4; ++w) {
+            unsigned long long mm = mask[w];
+            while (mm) {
+                int bit = __ffsll((long long)mm) - 1;
+                mm &= mm - 1;
+                const T* r = dx + (int64_t)(j0 + w * 64 + bit) * C;
+#pragma unroll
+                for (int i = 0; i < MAXC; ++i) {
+                    int c = threadIdx.x + i * 256;
+                    if (c < C) acc[i] += to_f32(r[c]);
+                }
+            }
+        }
+        __syncthreads();
+    }
+    float* out = dwte + (int64_t)v * C;
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) {
+        int c = threadIdx.x + i * 256;
+        if (c < C) out[c] += acc[i];
+    }
+}
+
+// dwpe[t] = sum_b dx[b, t] for t < T; rows T..P-1 of dwpe get 0.
+template <class T>
+__global__ __launch_bounds__(256) void encoder_backward_wpe_kernel(float* dwpe, const T* dx, int B, int T_, int P,
+                                                                   int C) {
+    int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)P * C) return;
+    int t = (int)(i / C), c = (int)(i % C);
+    float acc = 0.f;
+    if (t < T_)
+        for (int b = 0; b < B; ++b) acc += to_f32(dx[((int64_t)b * T_ + t) * C + c]);
+    dwpe[i] = acc;
+}
+
+template <class T>
+hipError_t encoder_backward(float* dwte, float* dwpe, const T* dx, const int32_t* tok, int B, int T_, int P, int C,
+                            hipStream_t s) {
+    if (C > 8 * 256) return hipErrorInvalidValue;
+    ProfScope prof(s, "encoder_bwd_wte", 0, (double)B * T_ * C * (sizeof(T) + 8.0));
+    hipLaunchKernelGGL(encoder_backward_wte_kernel<T>, dim3(B * T_), dim3(256), 0, s, dwte, dx, tok, B * T_, C);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    ProfScope prof2(s, "encoder_bwd_wpe", 0, (double)B * T_ * C * sizeof(T) + 4.0 * P * C);
+    hipLaunchKernelGGL(encoder_backward_wpe_kernel<T>, dim3(cdiv((int64_t)P * C, 256)), dim3(256), 0, s, dwpe, dx, B,
+                       T_, P, C);
+    return hipGetLastError();
+}
+
+// ============================================================================ AdamW
+// "1000 行 C 代码完成 GPT-2 训练的 LLM.c": the step ends with an Adam update.  Decoupled
+// weight decay with bias correction (c1 = 1 - beta1^t, c2 = 1 - beta2^t):
+//   m = b1 m + (1-b1) g;  v = b2 v + (1-b2) g^2;  p -= lr (m/c1 / (sqrt(v/c2) + eps) + wd p)
+__device__ __forceinline__ void adamw_one(float& p, float g, float& m, float& v, float lr, float b1, float b2,
+                                          float eps, float wd, float c1, float c2) {
+    m = b1 * m + (1.f - b1) * g;
+    v = b2 * v + (1.f - b2) * g * g;
+    float mh = m / c1, vh = v / c2;
+    p -= lr * (mh / (sqrtf(vh) + eps) + wd * p);
+}
+
+__global__ __launch_bounds__(256) void adamw_kernel(float* p, const float* g, float* m, float* v, bf16* p16,
+                                                    int64_t n, float lr, float b1, float b2, float eps, float wd,
+                                                    float c1, float c2) {
+    const int64_t n4 = n / 4;
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += stride) {
+        float4 pp = ((float4*)p)[i], gg = ((const float4*)g)[i], mm = ((float4*)m)[i], vv = ((float4*)v)[i];
+        adamw_one(pp.x, gg.x, mm.x, vv.x, lr, b1, b2, eps, wd, c1, c2);
+        adamw_one(pp.y, gg.y, mm.y, vv.y, lr, b1, b2, eps, wd, c1, c2);
+        adamw_one(pp.z, gg.z, mm.z, vv.z, lr, b1, b2, eps, wd, c1, c2);
+        adamw_one(pp.w, gg.w, mm.w, vv.w, lr, b1, b2, eps, wd, c1, c2);
+        ((float4*)p)[i] = pp;
+        ((float4*)m)[i] = mm;
+        ((float4*)v)[i] = vv;
+        if (p16) {
+            uint2 h;
+            h.x = (uint32_t)f32_to_bf16_bits(pp.x) | ((uint32_t)f32_to_bf16_bits(pp.y) << 16);
+            h.y = (uint32_t)f32_to_bf16_bits(pp.z) | ((uint32_t)f32_to_bf16_bits(pp.w) << 16);
+            ((uint2*)p16)[i] = h;
+        }
+    }
+    // tail (n % 4 elements), handled by the first threads of block 0
+    if (blockIdx.x == 0 && threadIdx.x < (n & 3)) {
+        int64_t i = n4 * 4 + threadIdx.x;
+        float pp = p[i], mm = m[i], vv = v[i];
+        adamw_one(pp, g[i], mm, vv, lr, b1, b2, eps, wd, c1, c2);
+        p[i] = pp; m[i] = mm; v[i] = vv;
+        if (p16) p16[i] = bf16{f32_to_bf16_bits(pp)};
+    }
+}
+
+hipError_t adamw(float* p, const float* g, float* m, float* v, bf16* p16, int64_t n, float lr, float b1, float b2,
+                 float eps, float wd, float c1, float c2, hipStream_t s) {
+    int64_t blocks = (n / 4 + 255) / 256;
+    if (blocks > 256 * 16) blocks = 256 * 16;
+    if (blocks < 1) blocks = 1;
+    ProfScope prof(s, "adamw", 0, (double)n * (28 + (p16 ? 2 : 0)));
+    hipLaunchKernelGGL(adamw_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, g, m, v, p16, n, lr, b1, b2, eps, wd,
+                       c1, c2);
+    return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void cast_bf16_kernel(bf16* out, const float* in, int64_t n) {
+    int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) out[i] = bf16{f32_to_bf16_bits(in[i])};
+}
+
+hipError_t cast_bf16(bf16* out, const float* in, int64_t n, hipStream_t s) {
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    if (blocks < 1) blocks = 1;
+    ProfScope prof(s, "cast_bf16", 0, 6.0 * n);
+    hipLaunchKernelGGL(cast_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, s, out, in, n);
+    return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(float* out, const float* ws, int splits, int64_t n) {
+    int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) {
+        float acc = 0.f;
+        for (int k = 0; k < splits; ++k) acc += ws[(int64_t)k * n + i];
+        out[i] = acc;
+    }
+}
+
+hipError_t splitk_reduce(float* out, const float* ws, int splits, int64_t n, hipStream_t s) {
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    ProfScope prof(s, "splitk_reduce", 0, 4.0 * (splits + 1) * n);
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, s, out, ws, splits, n);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------- instantiations
+#define GPT2_INST(T)                                                                                              \
+    template hipError_t encoder_forward<T>(T*, const int32_t*, const float*, const float*, int, int, int,        \
+                                           hipStream_t);                                                          \
+    template hipError_t layernorm_forward<T>(T*, float*, const T*, const float*, const float*, int, int,         \
+                                             hipStream_t);                                                        \
+    template hipError_t layernorm_backward<T>(T*, float*, float*, const T*, const T*, const float*, const float*, \
+                                              int, int, float*, size_t, hipStream_t, bool);                      \
+    template hipError_t bias_grad<T>(float*, const T*, int, int, int64_t, float*, size_t, hipStream_t);          \
+    template hipError_t crossentropy_fused<T>(T*, float*, const int32_t*, int, int, int64_t, float, hipStream_t); \
+    template hipError_t encoder_backward<T>(float*, float*, const T*, const int32_t*, int, int, int, int,        \
+                                            hipStream_t);
+GPT2_INST(float)
+GPT2_INST(bf16)
+
+}  // namespace gpt2
