@@ -175,6 +175,14 @@ def test_bf16_small_model_ragged():
     bf16_compare(w, rand_params(w.model, seed=23))
 
 
+@pytest.mark.parametrize("T", [1, 33, 64, 129])
+def test_bf16_head64_lengths(T):
+    # head size 64 (the MFMA attention): single position, below / at / past one tile
+    w = Workload("bf16_h64", ModelShape(256, 301, 2, 2, 128), 2, T, "bf16", "uniform", index=27)
+    announce(f"bf16_head64_T{T}", w)
+    bf16_compare(w, rand_params(w.model, seed=T))
+
+
 def test_bf16_tiny_char():
     w = Workload("bf16_tiny", synth.GPT2_TINY_CHAR, 4, 32, "bf16", "uniform", index=0)
     announce("bf16_tiny_char", w)
@@ -183,18 +191,19 @@ def test_bf16_tiny_char():
 
 # ----------------------------------------------------------------------------- properties
 
-@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
-def test_causality_bitwise_on_gpu(dtype):
+@pytest.mark.parametrize("dtype,NH,T", [("fp32", 4, 64), ("bf16", 4, 64), ("bf16", 2, 64), ("bf16", 2, 200)])
+def test_causality_bitwise_on_gpu(dtype, NH, T):
     # "GPT-2 from scratch with torch", 自注意力: a position sees only itself and the past,
     # so changing later tokens leaves earlier logits bit-identical.
     b = _b()
-    w = Workload("causal", ModelShape(64, 211, 2, 4, 64), 2, 64, dtype, "uniform", index=24)
-    announce(f"causality_{dtype}", w)
+    w = Workload("causal", ModelShape(256, 211, 2, NH, 128 if NH == 2 else 64), 2, T, dtype, "uniform",
+                 index=24)
+    announce(f"causality_{dtype}_hs{w.model.channels // NH}", w)
     a = gpu_arena(w, rand_params(w.model, seed=9))
     x, _ = synth.inputs_targets(w)
     a.forward(x)
     ref = to_np(a.tensor(b.T_LOGITS)).reshape(w.B, w.T, -1).copy()
-    for t in (0, 31, 62):
+    for t in (0, 31, T - 2):
         x2 = x.copy()
         x2[:, t + 1:] = (x2[:, t + 1:] + 13) % w.model.vocab_size
         a.forward(x2)
@@ -203,11 +212,11 @@ def test_causality_bitwise_on_gpu(dtype):
         assert not np.array_equal(z[:, t + 1:], ref[:, t + 1:])
 
 
-@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
-def test_step_is_deterministic(dtype):
+@pytest.mark.parametrize("dtype,NH", [("fp32", 4), ("bf16", 4), ("bf16", 2)])
+def test_step_is_deterministic(dtype, NH):
     b = _b()
-    w = Workload("det", ModelShape(64, 301, 2, 4, 128), 2, 48, dtype, "zipf", index=25)
-    announce(f"determinism_{dtype}", w)
+    w = Workload("det", ModelShape(160, 301, 2, NH, 128), 2, 130, dtype, "zipf", index=25)
+    announce(f"determinism_{dtype}_hs{128 // NH}", w)
     p = rand_params(w.model, seed=10)
     x, y = synth.inputs_targets(w)
     outs = []

@@ -275,6 +275,9 @@ static hipError_t attn_bwd_hs(T* dqkv, float* dsum, const T* dout, const T* out,
 
 template <class T>
 hipError_t attention_forward(T* out, float* lse, const T* qkv, int B, int T_, int C, int NH, hipStream_t s) {
+    if constexpr (sizeof(T) == 2) {
+        if (C / NH == 64) return attention_forward_mfma64(out, lse, qkv, B, T_, C, NH, s);
+    }
     switch (C / NH) {
         case 16: return attn_fwd_hs<T, 16>(out, lse, qkv, B, T_, C, NH, s);
         case 32: return attn_fwd_hs<T, 32>(out, lse, qkv, B, T_, C, NH, s);
@@ -287,6 +290,9 @@ hipError_t attention_forward(T* out, float* lse, const T* qkv, int B, int T_, in
 template <class T>
 hipError_t attention_backward(T* dqkv, float* dsum, const T* dout, const T* out, const T* qkv, const float* lse,
                               int B, int T_, int C, int NH, hipStream_t s) {
+    if constexpr (sizeof(T) == 2) {
+        if (C / NH == 64) return attention_backward_mfma64(dqkv, dsum, dout, out, qkv, lse, B, T_, C, NH, s);
+    }
     switch (C / NH) {
         case 16: return attn_bwd_hs<T, 16>(dqkv, dsum, dout, out, qkv, lse, B, T_, C, NH, s);
         case 32: return attn_bwd_hs<T, 32>(dqkv, dsum, dout, out, qkv, lse, B, T_, C, NH, s);

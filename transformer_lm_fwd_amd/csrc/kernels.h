@@ -85,4 +85,10 @@ template <class T>
 hipError_t attention_backward(T* dqkv, float* dsum, const T* dout, const T* out, const T* qkv, const float* lse,
                               int B, int T_, int C, int NH, hipStream_t s);
 
+// MFMA kernels for bf16 operands with head size 64 (used by the two above when they apply).
+hipError_t attention_forward_mfma64(bf16* out, float* lse, const bf16* qkv, int B, int T_, int C, int NH,
+                                    hipStream_t s);
+hipError_t attention_backward_mfma64(bf16* dqkv, float* dsum, const bf16* dout, const bf16* out, const bf16* qkv,
+                                     const float* lse, int B, int T_, int C, int NH, hipStream_t s);
+
 }  // namespace gpt2
