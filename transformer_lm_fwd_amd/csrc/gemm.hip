@@ -26,17 +26,35 @@ namespace gpt2 {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
+// MFMA shapes.  bf16: v_mfma_f32_32x32x16_bf16 (the 16x16x32 form issues at half
+// its rate on gfx950).  Lane l supplies row l % 32 of a 32-row A block (B: column
+// l % 32) with the 8 k values 8*(l/32)..+7 of a 16-wide k slice; its 16
+// accumulators hold column l % 32, rows 8*(i/4) + 4*(l/32) + i%4.
+// fp32: v_mfma_f32_16x16x4_f32, four per 16-byte fragment (lane l: row l % 16,
+// k = 4*(l/16) + e for the e-th instruction); accumulators: column l % 16, rows
+// 4*(l/16) + i.  Only the pairing of A and B k values matters for the sum, so
+// both operands use the same per-lane k offsets.
 template <class T> struct MfmaTraits;
 template <> struct MfmaTraits<bf16> {
-    static constexpr int KSLICE = 32;  // k consumed by one fragment pair
-    __device__ static __forceinline__ f32x4 step(const u32x4& a, const u32x4& b, f32x4 acc) {
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+    static constexpr int TILE = 32, KSLICE = 16, NACC = 16;
+    typedef float acc_t __attribute__((ext_vector_type(16)));
+    __device__ static __forceinline__ int frag_row(int lane) { return lane & 31; }
+    __device__ static __forceinline__ int frag_k(int lane) { return (lane >> 5) * 8; }
+    __device__ static __forceinline__ int out_row(int lane, int i) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
+    __device__ static __forceinline__ int out_col(int lane) { return lane & 31; }
+    __device__ static __forceinline__ acc_t step(const u32x4& a, const u32x4& b, acc_t acc) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                        __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
     }
 };
 template <> struct MfmaTraits<float> {
-    static constexpr int KSLICE = 16;
-    __device__ static __forceinline__ f32x4 step(const u32x4& a, const u32x4& b, f32x4 acc) {
+    static constexpr int TILE = 16, KSLICE = 16, NACC = 4;
+    typedef f32x4 acc_t;
+    __device__ static __forceinline__ int frag_row(int lane) { return lane & 15; }
+    __device__ static __forceinline__ int frag_k(int lane) { return (lane >> 4) * 4; }
+    __device__ static __forceinline__ int out_row(int lane, int i) { return 4 * (lane >> 4) + i; }
+    __device__ static __forceinline__ int out_col(int lane) { return lane & 15; }
+    __device__ static __forceinline__ acc_t step(const u32x4& a, const u32x4& b, acc_t acc) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
             acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[e]), __uint_as_float(b[e]), acc, 0, 0, 0);
@@ -156,19 +174,42 @@ __device__ __forceinline__ void epilogue_store(const GemmArgs& a, float* wsC, in
     }
 }
 
-template <class T, bool AK, bool BKC, int EPI, int BM, int BN, int BK, int WM, int WN>
+// Block -> output tile.  Workgroup i runs on XCD i % 8 (round-robin dispatch), and
+// each XCD has its own L2.  So each XCD is given a contiguous range of tiles, and
+// tiles are numbered in groups of 8 tile-rows walked column by column: the ~64
+// blocks resident on one XCD then cover an 8 x 8 square of tiles and share their
+// A rows and B columns in that XCD's L2.
+__device__ __forceinline__ void tile_order(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
+    const int ntiles = tiles_m * tiles_n;
+    const int q = ntiles / 8, r = ntiles % 8;
+    const int xcd = bid % 8, idx = bid / 8;
+    const int t = xcd * q + min(xcd, r) + idx;
+    constexpr int GM = 8;
+    const int per_group = GM * tiles_n;
+    const int first_m = (t / per_group) * GM;
+    const int gsize = min(tiles_m - first_m, GM);
+    const int in = t % per_group;
+    tm = first_m + in % gsize;
+    tn = in / gsize;
+}
+
+template <class T, bool AK, bool BKC, int EPI, int BM, int BN, int BK, int WM, int WN, bool ORDER = false>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs a, int k_per_split, int64_t split_stride) {
     constexpr int NT = 64 * WM * WN;
     constexpr int KV = Vec16<T>::N;
     constexpr int PITCH = BK + KV;
-    constexpr int TM = BM / WM / 16, TN = BN / WN / 16;
-    constexpr int KSLICE = MfmaTraits<T>::KSLICE;
+    using MT = MfmaTraits<T>;
+    constexpr int MTILE = MT::TILE;
+    constexpr int TM = BM / WM / MTILE, TN = BN / WN / MTILE;
+    constexpr int KSLICE = MT::KSLICE;
     constexpr int SA = BM * PITCH, SB = BN * PITCH;
     __shared__ __attribute__((aligned(16))) T lds[2][SA + SB];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
-    const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+    int tm = blockIdx.y, tn = blockIdx.x;
+    if constexpr (ORDER) tile_order(blockIdx.x, (a.M + BM - 1) / BM, (a.N + BN - 1) / BN, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
     const int kbeg = blockIdx.z * k_per_split;
     const int kend = min(a.K, kbeg + k_per_split);
     const T* A = (const T*)a.A;
@@ -177,11 +218,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs a, int k_pe
     TileLoader<T, AK, BM, BK, NT> la;
     TileLoader<T, BKC, BN, BK, NT> lb;
 
-    f32x4 acc[TM][TN];
+    typename MT::acc_t acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int e = 0; e < MT::NACC; ++e) acc[i][j][e] = 0.f;
 
     const int nk = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
     if (nk > 0) {
@@ -197,20 +240,19 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs a, int k_pe
             la.load(A, a.lda, m0, a.M, kbeg + (kt + 1) * BK, kend, tid);
             lb.load(B, a.ldb, n0, a.N, kbeg + (kt + 1) * BK, kend, tid);
         }
-        const T* sA = lds[cur] + (wm * TM * 16) * PITCH;
-        const T* sB = lds[cur] + SA + (wn * TN * 16) * PITCH;
+        const T* sA = lds[cur] + (wm * TM * MTILE + MT::frag_row(lane)) * PITCH + MT::frag_k(lane);
+        const T* sB = lds[cur] + SA + (wn * TN * MTILE + MT::frag_row(lane)) * PITCH + MT::frag_k(lane);
 #pragma unroll
         for (int ks = 0; ks < BK / KSLICE; ++ks) {
-            const int koff = ks * KSLICE + (lane >> 4) * KV;
             u32x4 fa[TM], fb[TN];
 #pragma unroll
-            for (int i = 0; i < TM; ++i) fa[i] = ld16(sA + (i * 16 + (lane & 15)) * PITCH + koff);
+            for (int i = 0; i < TM; ++i) fa[i] = ld16(sA + i * MTILE * PITCH + ks * KSLICE);
 #pragma unroll
-            for (int j = 0; j < TN; ++j) fb[j] = ld16(sB + (j * 16 + (lane & 15)) * PITCH + koff);
+            for (int j = 0; j < TN; ++j) fb[j] = ld16(sB + j * MTILE * PITCH + ks * KSLICE);
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
-                for (int j = 0; j < TN; ++j) acc[i][j] = MfmaTraits<T>::step(fa[i], fb[j], acc[i][j]);
+                for (int j = 0; j < TN; ++j) acc[i][j] = MT::step(fa[i], fb[j], acc[i][j]);
         }
         if (kt + 1 < nk) {
             la.template store<PITCH>(lds[cur ^ 1], tid);
@@ -226,11 +268,264 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs a, int k_pe
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                int row = m0 + wm * TM * 16 + i * 16 + (lane >> 4) * 4 + r;
-                int col = n0 + wn * TN * 16 + j * 16 + (lane & 15);
+            for (int r = 0; r < MT::NACC; ++r) {
+                const int row = m0 + wm * TM * MTILE + i * MTILE + MT::out_row(lane, r);
+                const int col = n0 + wn * TN * MTILE + j * MTILE + MT::out_col(lane);
                 epilogue_store<T, EPI>(a, wsC, row, col, acc[i][j][r]);
             }
+}
+
+// ---------------------------------------------------------------------------- bf16 kernel (buffer loads)
+// Operands are read with buffer loads whose resource covers exactly the valid
+// rows of each matrix: reads past the end return zero in hardware, so the K loop
+// carries no bounds checks.  Every per-thread offset is computed once; the k step
+// enters as the scalar offset, LDS addresses as immediates.  An n/m-contiguous
+// operand is loaded as 4 (k) x 8 (mn) blocks, transposed with byte permutes and
+// stored k-contiguous.  Requirements (checked by the host): leading dimensions are
+// multiples of 8 elements, and a k-contiguous operand's columns between K and the
+// next multiple of 64 read as zero (true when K % 64 == 0, or when the row padding
+// holds zeros).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bload(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+}
+
+constexpr int GBK = 64;  // k per tile; an LDS tile row is 64 bf16 = 128 bytes = 8 chunks of 16 bytes
+
+// LDS tile layout: row-major, 128-byte rows, no padding; the 16-byte chunk c of
+// row r is stored at position c ^ swz(r).  With swz(r) = (r ^ (r >> 3)) & 7, any 8
+// consecutive rows read at one logical chunk (the MFMA fragment reads), the 8
+// chunks of one row (k-contiguous stores), and rows 8 apart at one chunk (the
+// transposed stores) all fall on distinct banks.
+__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+__device__ __forceinline__ int lds_pos(int r, int chunk) { return r * GBK + ((chunk ^ swz(r)) << 3); }
+
+template <bool KCONTIG, int ROWS, int NT>
+struct BufLoader {
+    // k-contiguous: ROWS x 8 chunks of 16 bytes.  mn-contiguous: (GBK/4) x (ROWS/8)
+    // blocks of 4 k-rows x 8 mn-columns.
+    static constexpr int NCH = ROWS * 8 / NT;
+    static constexpr int NHB = (GBK / 4) * (ROWS / 8) / NT;
+    static_assert(KCONTIG ? (ROWS * 8) % NT == 0 : ((GBK / 4) * (ROWS / 8)) % NT == 0, "tile/threads mismatch");
+    static constexpr int NLD = KCONTIG ? NCH : 4 * NHB;
+    static constexpr int NST = KCONTIG ? NCH : 8 * NHB;
+    uint32_t voff[NLD];
+    int lofs[NST];
+    u32x4 r[NLD];
+    uint32_t kstep;  // bytes of scalar offset per k element
+
+    __device__ __forceinline__ void init(int tid, int row0, int64_t ld) {
+        if constexpr (KCONTIG) {
+#pragma unroll
+            for (int i = 0; i < NCH; ++i) {
+                const int c = tid + i * NT, row = c >> 3, kc = c & 7;
+                voff[i] = (uint32_t)(((int64_t)(row0 + row) * ld + kc * 8) * 2);
+                lofs[i] = lds_pos(row, kc);
+            }
+            kstep = 2;
+        } else {
+#pragma unroll
+            for (int i = 0; i < NHB; ++i) {
+                const int hb = tid + i * NT, kq = hb / (ROWS / 8), mb = hb % (ROWS / 8);
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr)
+                    voff[4 * i + rr] = (uint32_t)(((int64_t)(kq * 4 + rr) * ld + row0 + mb * 8) * 2);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) lofs[8 * i + j] = lds_pos(mb * 8 + j, kq >> 1) + (kq & 1) * 4;
+            }
+            kstep = (uint32_t)(ld * 2);
+        }
+    }
+    __device__ __forceinline__ void load(rsrc_t rs, int k0) {
+        const uint32_t soff = (uint32_t)k0 * kstep;
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) r[i] = bload(rs, voff[i], soff);
+    }
+    __device__ __forceinline__ void store(bf16* lds) {
+        if constexpr (KCONTIG) {
+#pragma unroll
+            for (int i = 0; i < NCH; ++i) st16(lds + lofs[i], r[i]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < NHB; ++i) {
+                const u32x4* q = &r[4 * i];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int w = j >> 1;
+                    const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+                    uint2 v;
+                    v.x = __builtin_amdgcn_perm(q[1][w], q[0][w], sel);
+                    v.y = __builtin_amdgcn_perm(q[3][w], q[2][w], sel);
+                    *(uint2*)(lds + lofs[8 * i + j]) = v;
+                }
+            }
+        }
+    }
+};
+
+template <bool AK, bool BKC, int EPI, int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a, int k_per_split, int64_t split_stride,
+                                                                 uint32_t a_bytes, uint32_t b_bytes) {
+    constexpr int NT = 64 * WM * WN;
+    using MT = MfmaTraits<bf16>;
+    constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
+    constexpr int SA = BM * GBK, STAGE = (BM + BN) * GBK;
+    constexpr int EPITCH = BN + 8;  // fp32 epilogue row pitch
+    constexpr int LDS_ELEMS = (2 * STAGE > BM * EPITCH * 2) ? 2 * STAGE : BM * EPITCH * 2;
+    __shared__ __attribute__((aligned(16))) bf16 lds[LDS_ELEMS];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+    const int kbeg = blockIdx.z * k_per_split;
+    const int kend = min(a.K, kbeg + k_per_split);
+    const int nk = kend > kbeg ? (kend - kbeg + GBK - 1) / GBK : 0;
+    const rsrc_t ra = make_rsrc(a.A, a_bytes), rb = make_rsrc(a.B, b_bytes);
+
+    BufLoader<AK, BM, NT> la;
+    BufLoader<BKC, BN, NT> lb;
+    la.init(tid, m0, a.lda);
+    lb.init(tid, n0, a.ldb);
+
+    MT::acc_t acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+    // fragment offsets: row (block base + lane % 32), logical chunk 2 ks + lane / 32
+    int fa[TM][GBK / 16], fb[TN][GBK / 16];
+#pragma unroll
+    for (int ks = 0; ks < GBK / 16; ++ks) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) fa[i][ks] = lds_pos((wm * TM + i) * 32 + (lane & 31), 2 * ks + (lane >> 5));
+#pragma unroll
+        for (int j = 0; j < TN; ++j) fb[j][ks] = SA + lds_pos((wn * TN + j) * 32 + (lane & 31), 2 * ks + (lane >> 5));
+    }
+    auto compute = [&](const bf16* st) {
+#pragma unroll
+        for (int ks = 0; ks < GBK / 16; ++ks) {
+            u32x4 xa[TM], xb[TN];
+#pragma unroll
+            for (int i = 0; i < TM; ++i) xa[i] = ld16(st + fa[i][ks]);
+#pragma unroll
+            for (int j = 0; j < TN; ++j) xb[j] = ld16(st + fb[j][ks]);
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j) acc[i][j] = MT::step(xa[i], xb[j], acc[i][j]);
+        }
+    };
+
+    if (nk > 0) {
+        la.load(ra, kbeg);
+        lb.load(rb, kbeg);
+        la.store(lds);
+        lb.store(lds + SA);
+    }
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const int cur = (kt & 1) * STAGE;
+        const bool more = kt + 1 < nk;
+        if (more) {
+            la.load(ra, kbeg + (kt + 1) * GBK);
+            lb.load(rb, kbeg + (kt + 1) * GBK);
+        }
+        compute(lds + cur);
+        if (more) {
+            la.store(lds + (STAGE - cur));
+            lb.store(lds + (STAGE - cur) + SA);
+        }
+        __syncthreads();
+    }
+
+    // Epilogue through LDS: the accumulators are written as fp32 rows [row][BN + 8]
+    // (the pad puts the two half-waves of a 32x32 tile on different banks), then
+    // each thread takes 8 consecutive columns of a row, applies the fused epilogue
+    // and writes 16-byte vectors.  Tiles taller than the LDS allows go in passes.
+    constexpr int EP = EPITCH;
+    constexpr int LDS_BYTES = LDS_ELEMS * 2;
+    constexpr int NPASS = (BM * EP * 4 <= LDS_BYTES) ? 1 : (BM / 2 * EP * 4 <= LDS_BYTES) ? 2 : 4;
+    constexpr int EROWS = BM / NPASS;
+    static_assert(EROWS * NPASS == BM && EROWS % 32 == 0, "epilogue pass split");
+    float* ebuf = (float*)lds;
+    float* wsC = nullptr;
+    if constexpr (EPI == EPI_F32) wsC = (float*)a.C + (int64_t)blockIdx.z * split_stride;
+#pragma unroll
+    for (int pass = 0; pass < NPASS; ++pass) {
+        const int r0 = pass * EROWS;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int trow = (wm * TM + i) * 32;  // tile-local first row of this MFMA block
+            if (trow >= r0 && trow < r0 + EROWS) {
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        ebuf[(trow - r0 + MT::out_row(lane, r)) * EP + (wn * TN + j) * 32 + MT::out_col(lane)] =
+                            acc[i][j][r];
+            }
+        }
+        __syncthreads();
+        constexpr int CPR = BN / 8;  // 8-column chunks per row
+        for (int c = tid; c < EROWS * CPR; c += NT) {
+            const int lr = c / CPR, lc = (c % CPR) * 8;
+            const int row = m0 + r0 + lr, col = n0 + lc;
+            if (row >= a.M || col >= a.N) continue;
+            float v[8];
+            const float4 v0 = *(const float4*)(ebuf + lr * EP + lc);
+            const float4 v1 = *(const float4*)(ebuf + lr * EP + lc + 4);
+            v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w;
+            v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
+            const int64_t o = (int64_t)row * a.ldc + col;
+            const bool full = col + 8 <= a.N;
+            if constexpr (EPI == EPI_F32) {
+                if (full) {
+                    *(float4*)(wsC + o) = v0;
+                    *(float4*)(wsC + o + 4) = v1;
+                } else {
+                    for (int e = 0; e < 8 && col + e < a.N; ++e) wsC[o + e] = v[e];
+                }
+            } else {
+                if constexpr (EPI != EPI_GELU_BWD) {
+                    if (a.bias) {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) v[e] += (col + e < a.N) ? a.bias[col + e] : 0.f;
+                    }
+                }
+                float rv[8];
+                if constexpr (EPI == EPI_BIAS_RES || EPI == EPI_GELU_BWD) {
+                    if (full) unpack16<bf16>(ld16((const bf16*)a.R + o), rv);
+                    else
+                        for (int e = 0; e < 8; ++e) rv[e] = (col + e < a.N) ? to_f32(((const bf16*)a.R)[o + e]) : 0.f;
+                }
+                float out2[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    if constexpr (EPI == EPI_BIAS_RES) v[e] += rv[e];
+                    if constexpr (EPI == EPI_BIAS_GELU) out2[e] = gelu_fwd(v[e]);
+                    if constexpr (EPI == EPI_GELU_BWD) v[e] *= gelu_bwd(rv[e]);
+                }
+                bf16* C = (bf16*)a.C;
+                if (full) {
+                    st16(C + o, pack16<bf16>(v));
+                    if constexpr (EPI == EPI_BIAS_GELU) st16((bf16*)a.C2 + o, pack16<bf16>(out2));
+                } else {
+                    for (int e = 0; e < 8 && col + e < a.N; ++e) {
+                        C[o + e] = from_f32<bf16>(v[e]);
+                        if constexpr (EPI == EPI_BIAS_GELU) ((bf16*)a.C2)[o + e] = from_f32<bf16>(out2[e]);
+                    }
+                }
+            }
+        }
+        if (pass + 1 < NPASS) __syncthreads();
+    }
 }
 
 template <class T, bool AK, bool BKC, int EPI>
@@ -250,8 +545,17 @@ static hipError_t launch(const GemmArgs& a, int splits, int k_per_split, int64_t
     const double es = sizeof(T), mn = (double)a.M * a.N;
     const double out_bytes = EPI == EPI_F32 ? 4 * mn : (EPI == EPI_BIAS ? es * mn : 2 * es * mn);
     ProfScope prof(s, gemm_name<T, AK, BKC, EPI>(), 2.0 * mn * a.K, es * ((double)a.M + a.N) * a.K + out_bytes);
-    hipLaunchKernelGGL((gemm_kernel<T, AK, BKC, EPI, BM, BN, BK, WM, WN>), grid, dim3(64 * WM * WN), 0, s, a,
-                       k_per_split, split_stride);
+    if constexpr (sizeof(T) == 2) {
+        // buffer extents in bytes: whole rows of each operand as stored
+        const int64_t ab = (AK ? (int64_t)a.M : (int64_t)a.K) * a.lda * 2;
+        const int64_t bb = (BKC ? (int64_t)a.N : (int64_t)a.K) * a.ldb * 2;
+        if (ab >= (int64_t)1 << 32 || bb >= (int64_t)1 << 32) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((gemm_bf16_kernel<AK, BKC, EPI, 128, 128, 2, 2>), grid, dim3(256), 0, s, a, k_per_split,
+                           split_stride, (uint32_t)ab, (uint32_t)bb);
+    } else {
+        hipLaunchKernelGGL((gemm_kernel<T, AK, BKC, EPI, BM, BN, BK, WM, WN>), grid, dim3(64 * WM * WN), 0, s, a,
+                           k_per_split, split_stride);
+    }
     return hipGetLastError();
 }
 
@@ -268,6 +572,12 @@ template <class T>
 hipError_t gemm(const GemmArgs& a, bool ak, bool bk, int epi, float* ws, size_t ws_floats, hipStream_t s) {
     constexpr int BK = sizeof(T) == 2 ? 64 : 32;
     if (a.M <= 0 || a.N <= 0) return hipSuccess;
+    if constexpr (sizeof(T) == 2) {
+        // 16-byte rows, and k-contiguous operands readable (zero-padded) up to a multiple of 64
+        if (a.lda % 8 || a.ldb % 8 || a.ldc % 8) return hipErrorInvalidValue;
+        const int64_t kpad = (a.K + 63) / 64 * 64;
+        if ((ak && a.lda < kpad) || (bk && a.ldb < kpad)) return hipErrorInvalidValue;
+    }
     if (epi == EPI_F32) {
         // Output fp32 [M, N] with row stride ldc.  Few output tiles and a long K:
         // split K over blockIdx.z into fp32 partials in `ws`, then reduce in a fixed order.

@@ -89,6 +89,11 @@ int validate(const gpt2_config* cfg, int B, int T, int dtype) {
     if (c.channels > 2048) return fail(GPT2_E_INVAL, "channels must be <= 2048");
     if (B < 1 || T < 1 || T > c.max_seq_len) return fail(GPT2_E_INVAL, "need B >= 1 and 1 <= T <= max_seq_len");
     if ((int64_t)B * T > (1 << 30)) return fail(GPT2_E_INVAL, "B*T too large");
+    // GEMM operands are addressed with 32-bit buffer offsets: the largest, the
+    // logits [B*T, vocab rounded up to 64] in bf16 or fp32, must stay below 4 GiB.
+    const int64_t vpad = ((int64_t)c.vocab_size + 63) / 64 * 64;
+    if ((int64_t)B * T * vpad * (dtype == GPT2_BF16 ? 2 : 4) >= ((int64_t)1 << 32))
+        return fail(GPT2_E_INVAL, "B*T*vocab too large for one arena (logits over 4 GiB)");
     if (dtype != GPT2_FP32 && dtype != GPT2_BF16) return fail(GPT2_E_INVAL, "dtype must be GPT2_FP32 or GPT2_BF16");
     return GPT2_OK;
 }

@@ -107,89 +107,156 @@ hipError_t layernorm_forward(T* out, float* stats, const T* inp, const float* w,
 
 // ============================================================================ LayerNorm backward
 // With xhat = (x - mean) * rstd and dxhat = dy * w:
-//   dx = rstd * (dxhat - mean_c(dxhat) - xhat * mean_c(dxhat * xhat))   (added into dres)
-//   dw = sum_rows dy * xhat,  db = sum_rows dy                          (per-block partials)
-// One wave per row, grid-stride over rows; each lane owns the same columns in
-// every row, so the dw/db partial sums stay in registers.
+//   dx = rstd * (dxhat - mean_c(dxhat) - xhat * mean_c(dxhat * xhat))   (written or added into dres)
+//   dw = sum_rows dy * xhat,  db = sum_rows dy                          (column sums, below)
+// dx: one wave per row, the row's dy and x held in registers.
 template <class T, int MAXCH>
-__global__ __launch_bounds__(256) void layernorm_backward_kernel(T* dres, float* partial, const T* dout, const T* inp,
-                                                                 const float* stats, const float* w, int N, int C,
-                                                                 int accumulate) {
+__global__ __launch_bounds__(256) void layernorm_backward_dx_kernel(T* dres, const T* dout, const T* inp,
+                                                                    const float* stats, const float* w, int N, int C,
+                                                                    int accumulate) {
     constexpr int KV = Vec16<T>::N;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    float pw[MAXCH][KV], pb[MAXCH][KV];
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= N) return;
+    const float mean = stats[2 * row], rstd = stats[2 * row + 1];
+    const T* dy = dout + (int64_t)row * C;
+    const T* x = inp + (int64_t)row * C;
+    float g[MAXCH][KV], xh[MAXCH][KV];
+    float s1 = 0.f, s2 = 0.f;
 #pragma unroll
-    for (int ch = 0; ch < MAXCH; ++ch)
+    for (int ch = 0; ch < MAXCH; ++ch) {
+        const int c = (ch * 64 + lane) * KV;
+        if (c < C) {
+            float wv[KV];
+            unpack16<T>(ld16(dy + c), g[ch]);
+            unpack16<T>(ld16(x + c), xh[ch]);
+            unpack16<float>(ld16(w + c), wv);
+            if constexpr (KV == 8) unpack16<float>(ld16(w + c + 4), wv + 4);
 #pragma unroll
-        for (int e = 0; e < KV; ++e) pw[ch][e] = pb[ch][e] = 0.f;
-
-    for (int row = blockIdx.x * 4 + wave; row < N; row += gridDim.x * 4) {
-        const float mean = stats[2 * row], rstd = stats[2 * row + 1];
-        const T* dy = dout + (int64_t)row * C;
-        const T* x = inp + (int64_t)row * C;
-        float g[MAXCH][KV], xh[MAXCH][KV];
-        float s1 = 0.f, s2 = 0.f;
-#pragma unroll
-        for (int ch = 0; ch < MAXCH; ++ch) {
-            int c = (ch * 64 + lane) * KV;
-            if (c < C) {
-                unpack16<T>(ld16(dy + c), g[ch]);
-                unpack16<T>(ld16(x + c), xh[ch]);
-#pragma unroll
-                for (int e = 0; e < KV; ++e) {
-                    xh[ch][e] = (xh[ch][e] - mean) * rstd;
-                    pw[ch][e] += g[ch][e] * xh[ch][e];
-                    pb[ch][e] += g[ch][e];
-                    float dxh = g[ch][e] * w[c + e];
-                    s1 += dxh;
-                    s2 += dxh * xh[ch][e];
-                }
-            }
-        }
-        s1 = wave_sum(s1) / C;
-        s2 = wave_sum(s2) / C;
-        T* dx = dres + (int64_t)row * C;
-#pragma unroll
-        for (int ch = 0; ch < MAXCH; ++ch) {
-            int c = (ch * 64 + lane) * KV;
-            if (c < C) {
-                float prev[KV], o[KV];
-                if (accumulate) unpack16<T>(ld16(dx + c), prev);
-#pragma unroll
-                for (int e = 0; e < KV; ++e) {
-                    float dxh = g[ch][e] * w[c + e];
-                    o[e] = rstd * (dxh - s1 - xh[ch][e] * s2) + (accumulate ? prev[e] : 0.f);
-                }
-                st16(dx + c, pack16<T>(o));
+            for (int e = 0; e < KV; ++e) {
+                xh[ch][e] = (xh[ch][e] - mean) * rstd;
+                g[ch][e] *= wv[e];  // dxhat
+                s1 += g[ch][e];
+                s2 += g[ch][e] * xh[ch][e];
             }
         }
     }
-    // reduce the four waves' column partials through LDS, write this block's row of `partial`
-    __shared__ float red[4][2][64 * KV * MAXCH];
+    s1 = wave_sum(s1) / C;
+    s2 = wave_sum(s2) / C;
+    T* dx = dres + (int64_t)row * C;
 #pragma unroll
-    for (int ch = 0; ch < MAXCH; ++ch)
+    for (int ch = 0; ch < MAXCH; ++ch) {
+        const int c = (ch * 64 + lane) * KV;
+        if (c < C) {
+            float prev[KV], o[KV];
+            if (accumulate) unpack16<T>(ld16(dx + c), prev);
 #pragma unroll
-        for (int e = 0; e < KV; ++e) {
-            red[wave][0][(ch * 64 + lane) * KV + e] = pw[ch][e];
-            red[wave][1][(ch * 64 + lane) * KV + e] = pb[ch][e];
+            for (int e = 0; e < KV; ++e) o[e] = rstd * (g[ch][e] - s1 - xh[ch][e] * s2) + (accumulate ? prev[e] : 0.f);
+            st16(dx + c, pack16<T>(o));
         }
-    __syncthreads();
-    float* out = partial + (int64_t)blockIdx.x * 2 * C;
-    for (int c = threadIdx.x; c < C; c += 256) {
-        out[c] = (red[0][0][c] + red[1][0][c]) + (red[2][0][c] + red[3][0][c]);
-        out[C + c] = (red[0][1][c] + red[1][1][c]) + (red[2][1][c] + red[3][1][c]);
     }
 }
 
-// out[c] = sum over nb blocks of partial[blk][c] for c < n (fixed order).
-__global__ __launch_bounds__(256) void column_reduce_kernel(float* out0, float* out1, const float* partial, int nb,
-                                                            int n, int split) {
-    int c = blockIdx.x * 256 + threadIdx.x;
-    if (c >= n) return;
+// Column sums over M rows (deterministic, two stages).
+// Stage 1: block (x: 64*KV columns, y: a chunk of rows); each lane owns KV columns
+// (one 16-byte load per row), the four waves take interleaved rows, and the block's
+// sums go to partial[blockIdx.y][...].  With LN, xhat is rebuilt from (mean, rstd):
+// partial row = [sum dy * xhat (N) | sum dy (N)]; without, [sum dy (N)].
+template <class T, bool LN>
+__global__ __launch_bounds__(256) void colsum_stage1_kernel(float* partial, const T* dy, const T* x,
+                                                            const float* stats, int M, int N, int64_t ld,
+                                                            int rows_per) {
+    constexpr int KV = Vec16<T>::N;
+    constexpr int NS = LN ? 2 : 1;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int c = (blockIdx.x * 64 + lane) * KV;
+    const int r0 = blockIdx.y * rows_per, r1 = min(M, r0 + rows_per);
+    float sb[KV], sw[KV];
+#pragma unroll
+    for (int e = 0; e < KV; ++e) sb[e] = sw[e] = 0.f;
+    if (c < N) {
+        for (int r = r0 + wave; r < r1; r += 4) {
+            float gv[KV];
+            unpack16<T>(ld16(dy + (int64_t)r * ld + c), gv);
+            if constexpr (LN) {
+                float xv[KV];
+                unpack16<T>(ld16(x + (int64_t)r * ld + c), xv);
+                const float mean = stats[2 * r], rstd = stats[2 * r + 1];
+#pragma unroll
+                for (int e = 0; e < KV; ++e) sw[e] += gv[e] * ((xv[e] - mean) * rstd);
+            }
+#pragma unroll
+            for (int e = 0; e < KV; ++e) sb[e] += gv[e];
+        }
+    }
+    __shared__ float red[4][NS][64 * KV];
+#pragma unroll
+    for (int e = 0; e < KV; ++e) {
+        red[wave][0][lane * KV + e] = sb[e];
+        if constexpr (LN) red[wave][NS - 1][lane * KV + e] = sw[e];
+    }
+    __syncthreads();
+    const int W = NS * N;
+    float* out = partial + (int64_t)blockIdx.y * W;
+    for (int i = threadIdx.x; i < NS * 64 * KV; i += 256) {
+        const int sidx = i / (64 * KV), j = i % (64 * KV);
+        const int col = blockIdx.x * 64 * KV + j;
+        if (col < N) {
+            float v = (red[0][sidx][j] + red[1][sidx][j]) + (red[2][sidx][j] + red[3][sidx][j]);
+            // LN: sums of dy*xhat first (dw), then sums of dy (db)
+            const int dst = LN ? (sidx == 1 ? col : N + col) : col;
+            out[dst] = v;
+        }
+    }
+}
+
+// Stage 2: out[c] = sum over nb partial rows (fixed order).  A block takes 16
+// columns; its 256 threads are 16 columns x 16 row lanes, lane k summing partial
+// rows k, k+16, ...; the 16 lane sums are then added in order.
+__global__ __launch_bounds__(256) void colsum_stage2_kernel(float* out0, float* out1, const float* partial, int nb,
+                                                            int W, int split) {
+    const int cl = threadIdx.x & 15, kl = threadIdx.x >> 4;
+    const int c = blockIdx.x * 16 + cl;
     float acc = 0.f;
-    for (int k = 0; k < nb; ++k) acc += partial[(int64_t)k * n + c];
-    if (c < split) out0[c] = acc;
-    else out1[c - split] = acc;
+    if (c < W) {
+#pragma unroll 4
+        for (int k = kl; k < nb; k += 16) acc += partial[(int64_t)k * W + c];
+    }
+    __shared__ float red[16][16];
+    red[kl][cl] = acc;
+    __syncthreads();
+    if (threadIdx.x < 16 && c < W) {
+        float v = 0.f;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) v += red[k][cl];
+        if (c < split) out0[c] = v;
+        else out1[c - split] = v;
+    }
+}
+
+template <class T, bool LN>
+static hipError_t colsum(float* out0, float* out1, const T* dy, const T* x, const float* stats, int M, int N,
+                         int64_t ld, float* partial, size_t partial_floats, hipStream_t s, const char* name) {
+    constexpr int KV = Vec16<T>::N;
+    const int NS = LN ? 2 : 1;
+    const int bx = cdiv(N, 64 * KV);
+    int rb = 1;
+    while (rb * bx < 1024 && rb < 256) rb *= 2;
+    while ((size_t)rb * NS * N > partial_floats && rb > 1) rb /= 2;
+    if ((size_t)rb * NS * N > partial_floats) return hipErrorInvalidValue;
+    const int rows_per = cdiv(M, rb);
+    rb = cdiv(M, rows_per);
+    {
+        ProfScope prof(s, name, 0, (double)M * N * sizeof(T) * (LN ? 2 : 1) + 4.0 * rb * NS * N);
+        hipLaunchKernelGGL((colsum_stage1_kernel<T, LN>), dim3(bx, rb), dim3(256), 0, s, partial, dy, x, stats, M, N,
+                           ld, rows_per);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    ProfScope prof2(s, "colsum_stage2", 0, 4.0 * rb * NS * N + 4.0 * NS * N);
+    hipLaunchKernelGGL(colsum_stage2_kernel, dim3(cdiv(NS * N, 16)), dim3(256), 0, s, out0, out1, partial, rb, NS * N,
+                       N);
+    return hipGetLastError();
 }
 
 template <class T>
@@ -197,54 +264,29 @@ hipError_t layernorm_backward(T* dres, float* dw, float* db, const T* dout, cons
                               const float* w, int N, int C, float* partial, size_t partial_floats, hipStream_t s,
                               bool accumulate) {
     constexpr int KV = Vec16<T>::N;
-    int ch = cdiv(C, 64 * KV);
-    int nb = cdiv(N, 4);
-    if (nb > 512) nb = 512;
-    while ((size_t)nb * 2 * C > partial_floats && nb > 1) nb /= 2;
-    if ((size_t)nb * 2 * C > partial_floats) return hipErrorInvalidValue;
-    dim3 grid(nb), block(256);
-    int acc = accumulate ? 1 : 0;
-    ProfScope prof(s, "layernorm_bwd", 0, (double)N * C * sizeof(T) * (accumulate ? 4 : 3) + 8.0 * N);
-    if (ch <= 1) hipLaunchKernelGGL((layernorm_backward_kernel<T, 1>), grid, block, 0, s, dres, partial, dout, inp, stats, w, N, C, acc);
-    else if (ch <= 2) hipLaunchKernelGGL((layernorm_backward_kernel<T, 2>), grid, block, 0, s, dres, partial, dout, inp, stats, w, N, C, acc);
-    else if (ch <= 4) hipLaunchKernelGGL((layernorm_backward_kernel<T, 4>), grid, block, 0, s, dres, partial, dout, inp, stats, w, N, C, acc);
-    else return hipErrorInvalidValue;
+    const int ch = cdiv(C, 64 * KV);
+    const dim3 grid(cdiv(N, 4)), block(256);
+    const int acc = accumulate ? 1 : 0;
+    {
+        ProfScope prof(s, "layernorm_bwd_dx", 0, (double)N * C * sizeof(T) * (accumulate ? 4 : 3) + 8.0 * N);
+        if (ch <= 1) hipLaunchKernelGGL((layernorm_backward_dx_kernel<T, 1>), grid, block, 0, s, dres, dout, inp, stats, w, N, C, acc);
+        else if (ch <= 2) hipLaunchKernelGGL((layernorm_backward_dx_kernel<T, 2>), grid, block, 0, s, dres, dout, inp, stats, w, N, C, acc);
+        else if (ch <= 4) hipLaunchKernelGGL((layernorm_backward_dx_kernel<T, 4>), grid, block, 0, s, dres, dout, inp, stats, w, N, C, acc);
+        else if (ch <= 8) hipLaunchKernelGGL((layernorm_backward_dx_kernel<T, 8>), grid, block, 0, s, dres, dout, inp, stats, w, N, C, acc);
+        else return hipErrorInvalidValue;
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    ProfScope prof2(s, "column_reduce", 0, 4.0 * nb * 2 * C + 8.0 * C);
-    hipLaunchKernelGGL(column_reduce_kernel, dim3(cdiv(2 * C, 256)), dim3(256), 0, s, dw, db, partial, nb, 2 * C, C);
-    return hipGetLastError();
+    return colsum<T, true>(dw, db, dout, inp, stats, N, C, C, partial, partial_floats, s, "layernorm_bwd_dwdb");
 }
-
 
 // ============================================================================ bias gradients
-// dbias[n] = sum_m dout[m, n]: blocks of (256 columns x rows/RB), partials reduced in order.
-template <class T>
-__global__ __launch_bounds__(256) void bias_grad_kernel(float* partial, const T* dout, int M, int N, int64_t ld,
-                                                        int rows_per) {
-    int n = blockIdx.x * 256 + threadIdx.x;
-    if (n >= N) return;
-    int r0 = blockIdx.y * rows_per, r1 = min(M, r0 + rows_per);
-    float acc = 0.f;
-    for (int r = r0; r < r1; ++r) acc += to_f32(dout[(int64_t)r * ld + n]);
-    partial[(int64_t)blockIdx.y * N + n] = acc;
-}
-
+// dbias[n] = sum_m dout[m, n] (overwrite).
 template <class T>
 hipError_t bias_grad(float* dbias, const T* dout, int M, int N, int64_t ld, float* partial, size_t partial_floats,
                      hipStream_t s) {
-    int rb = 64;
-    while ((size_t)rb * N > partial_floats && rb > 1) rb /= 2;
-    if ((size_t)rb * N > partial_floats) return hipErrorInvalidValue;
-    int rows_per = cdiv(M, rb);
-    rb = cdiv(M, rows_per);
-    ProfScope prof(s, "bias_grad", 0, (double)M * N * sizeof(T) + 4.0 * N);
-    hipLaunchKernelGGL(bias_grad_kernel<T>, dim3(cdiv(N, 256), rb), dim3(256), 0, s, partial, dout, M, N, ld, rows_per);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    ProfScope prof2(s, "column_reduce", 0, 4.0 * rb * N + 4.0 * N);
-    hipLaunchKernelGGL(column_reduce_kernel, dim3(cdiv(N, 256)), dim3(256), 0, s, dbias, dbias, partial, rb, N, N);
-    return hipGetLastError();
+    return colsum<T, false>(dbias, dbias, dout, (const T*)nullptr, nullptr, M, N, ld, partial, partial_floats, s,
+                            "bias_grad");
 }
 
 // ============================================================================ softmax cross-entropy
