@@ -5,157 +5,204 @@
 // scaling): S = q k^T / sqrt(64), keys after the query masked, softmax per query,
 // O = P V; only the per-query log-sum-exp is kept for the backward pass.
 //
-// Layout tricks (v_mfma_f32_16x16x32_bf16, wave64):
-//  * Scores are computed transposed, S^T = K Q^T, so the accumulator of lane l
-//    holds 4 keys of ONE query (column l % 16).  The 16 A-rows of each score tile
-//    are fed a permuted set of keys so that, over two tiles, lane group g = l / 16
-//    holds the 8 consecutive keys 8g..8g+7 of a 32-key slice.  Those 8
-//    probabilities, packed to bf16, are exactly the B operand of O^T = V^T P^T:
-//    no LDS round trip for P.
-//  * V (and, in the backward pass, Q, dO, K) is also staged transposed in LDS
-//    ([d][key]) so that the matching A/B fragments are single 16-byte reads.
+// MFMA v_mfma_f32_32x32x16_bf16 (wave64): lane l supplies row l % 32 of A (column
+// l % 32 of B) with k values 8*(l/32)..+7 of a 16-wide slice; its 16 accumulators
+// hold column l % 32, rows 8*(i/4) + 4*(l/32) + i%4.
+//  * Scores are computed with the query as the accumulator column (S^T = K Q^T in
+//    the forward pass and for dQ, S = Q K^T with the key as the column for dK/dV).
+//    The 32 A-rows of a score tile are fed a permuted set of rows, perm32(), chosen
+//    so that accumulators 8s..8s+7 of lane group g = l/32 are the 8 consecutive
+//    rows 16s + 8g .. +7: exactly the B (or A) fragment of the next MFMA, whose
+//    reduction runs over those rows.  Probabilities never go through LDS.
+//  * LDS tiles are 64 x 64 bf16 with 128-byte rows and the 16-byte-chunk XOR swizzle
+//    chunk ^ ((row ^ row >> 3) & 7); transposed copies ([d][row]) are built from the
+//    same global loads with byte permutes.
 //  * The backward pass is two kernels -- dK/dV over key tiles and dQ over query
-//    tiles -- each writing its outputs exactly once, so it needs no atomics and
-//    is deterministic.
+//    tiles -- each writing its outputs once: no atomics, deterministic.
 #include "kernels.h"
 
 namespace gpt2 {
 namespace {
 
-constexpr int HS = 64;           // head size handled here
-constexpr int TILE = 64;         // queries (or keys) per block
-constexpr int PITCH = HS + 8;    // LDS row pitch in bf16 elements (144 bytes)
+constexpr int HS = 64;  // head size handled here
 constexpr float LOG2E = 1.4426950408889634f;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-__device__ __forceinline__ f32x4 mfma(const u32x4& a, const u32x4& b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+__device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
                                                    c, 0, 0, 0);
 }
-
+__device__ __forceinline__ f32x16 zero16() {
+    f32x16 z;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) z[i] = 0.f;
+    return z;
+}
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ __forceinline__ uint32_t half_of(const u32x4& v, int e) { return (v[e >> 1] >> ((e & 1) * 16)) & 0xffffu; }
+__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+// element offset of the 16-byte chunk `chunk` of row r in a 64-wide swizzled tile
+__device__ __forceinline__ int pos(int r, int chunk) { return r * 64 + ((chunk ^ swz(r)) << 3); }
+// A-row rho (0..31) of a score tile -> tile row 16(j/2) + 8g + 4(j%2) + t, rho = 8j + 4g + t
+__device__ __forceinline__ int perm32(int rho) {
+    const int j = rho >> 3, g = (rho >> 2) & 1, t = rho & 3;
+    return 16 * (j >> 1) + 8 * g + 4 * (j & 1) + t;
+}
 
-// Copies rows [r0, r0+64) (head slice of 64 bf16) of a strided matrix into LDS
-// [row][PITCH]; rows >= T are zero.  256 threads, two 16-byte chunks each.
-__device__ __forceinline__ void load_rows(bf16* lds, const bf16* g, int64_t ld, int r0, int T, int tid) {
+// A 64-row x 64-column bf16 tile of a strided matrix staged through registers:
+// thread t owns rows 4(t/16)..+3 and columns 4(t%16)..+3 (four 8-byte loads, rows
+// >= T read as zero).  store_n writes the tile as [row][col], store_t as [col][row].
+struct Tile64 {
+    uint2 v[4];
+    __device__ __forceinline__ void load(const bf16* g, int64_t ld, int r0, int T, int tid) {
+        const int cb = tid & 15, rq = tid >> 4;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        int c = tid + i * 256;
-        int row = c >> 3, dc = c & 7;
-        u32x4 v = (r0 + row < T) ? ld16(g + (int64_t)(r0 + row) * ld + dc * 8) : u32x4{0, 0, 0, 0};
-        st16(lds + row * PITCH + dc * 8, v);
+        for (int rr = 0; rr < 4; ++rr) {
+            const int row = r0 + 4 * rq + rr;
+            v[rr] = row < T ? *(const uint2*)(g + (int64_t)row * ld + 4 * cb) : uint2{0u, 0u};
+        }
     }
-}
-
-// Same rows stored transposed: lds[d][row].  Thread = (pair of rows, 8 columns).
-__device__ __forceinline__ void load_rows_t(bf16* lds, const bf16* g, int64_t ld, int r0, int T, int tid) {
-    const int rp = tid >> 3, dc = tid & 7;
-    const int ra = r0 + 2 * rp;
-    u32x4 v0 = (ra < T) ? ld16(g + (int64_t)ra * ld + dc * 8) : u32x4{0, 0, 0, 0};
-    u32x4 v1 = (ra + 1 < T) ? ld16(g + (int64_t)(ra + 1) * ld + dc * 8) : u32x4{0, 0, 0, 0};
-    uint32_t* base = (uint32_t*)lds;
+    __device__ __forceinline__ void store_n(bf16* ln, int tid) const {
+        const int cb = tid & 15, rq = tid >> 4;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) base[((dc * 8 + e) * PITCH + 2 * rp) >> 1] = half_of(v0, e) | (half_of(v1, e) << 16);
+        for (int rr = 0; rr < 4; ++rr) *(uint2*)(ln + pos(4 * rq + rr, cb >> 1) + (cb & 1) * 4) = v[rr];
+    }
+    __device__ __forceinline__ void store_t(bf16* lt, int tid) const {
+        const int cb = tid & 15, rq = tid >> 4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+            const uint32_t w0 = (j >> 1) ? v[0].y : v[0].x, w1 = (j >> 1) ? v[1].y : v[1].x;
+            const uint32_t w2 = (j >> 1) ? v[2].y : v[2].x, w3 = (j >> 1) ? v[3].y : v[3].x;
+            uint2 o;
+            o.x = __builtin_amdgcn_perm(w1, w0, sel);
+            o.y = __builtin_amdgcn_perm(w3, w2, sel);
+            *(uint2*)(lt + pos(4 * cb + j, rq >> 1) + (rq & 1) * 4) = o;
+        }
+    }
+};
+
+// 16-byte fragment of a strided row (zero past T)
+__device__ __forceinline__ u32x4 row_frag(const bf16* g, int64_t ld, int row, int col, int T) {
+    return row < T ? ld16(g + (int64_t)row * ld + col) : u32x4{0u, 0u, 0u, 0u};
 }
 
-// A-row r (0..15) of score tile half `hh` in 32-row slice `sp` maps to row
-//   32 sp + 8 (r / 4) + 4 hh + (r % 4),
-// so accumulator rows 4g+i of halves 0 and 1 are rows 32 sp + 8 g + (0..7).
-__device__ __forceinline__ int perm_row(int sp, int hh, int r) { return 32 * sp + 8 * (r >> 2) + 4 * hh + (r & 3); }
+__device__ __forceinline__ void store4_bf16(bf16* dst, float a, float b, float c, float d) {
+    uint2 v;
+    v.x = pack2_bf16(a, b);
+    v.y = pack2_bf16(c, d);
+    *(uint2*)dst = v;
+}
 
 }  // namespace
 
 // ============================================================================ forward
+// Block: 128 queries (4 waves x 32), key tiles of 64 staged in LDS.
 __global__ __launch_bounds__(256) void attn_fwd_mfma64(bf16* out, float* lse, const bf16* qkv, int T, int C, int NH) {
-    __shared__ __attribute__((aligned(16))) bf16 sK[TILE * PITCH];
-    __shared__ __attribute__((aligned(16))) bf16 sVt[HS * PITCH];
-    const int nqt = (T + TILE - 1) / TILE;
+    __shared__ __attribute__((aligned(16))) bf16 sbuf[2][2 * 64 * 64];  // [stage][K | V^T]
+    const int nqt = (T + 127) / 128;
     const int qt = nqt - 1 - (int)blockIdx.x;  // longest rows first
     const int bh = blockIdx.y, b = bh / NH, h = bh % NH;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r16 = lane & 15, g = lane >> 4;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r32 = lane & 31, g = lane >> 5;
     const int64_t C3 = 3 * (int64_t)C;
     const bf16* base = qkv + (int64_t)b * T * C3;
     const bf16* Qg = base + h * HS;
     const bf16* Kg = base + C + h * HS;
     const bf16* Vg = base + 2 * C + h * HS;
-    const int q0 = qt * TILE, qw = q0 + 16 * w, myq = qw + r16;
-    const float c = 0.125f * LOG2E;  // 1/sqrt(64), in log2 units
+    const int q0 = qt * 128, qw = q0 + 32 * w, myq = qw + r32;
+    const float c = 0.125f * LOG2E;  // 1/sqrt(64) in log2 units
 
-    u32x4 qf[2];
+    u32x4 qf[4];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-        qf[kk] = (myq < T) ? ld16(Qg + (int64_t)myq * C3 + 32 * kk + 8 * g) : u32x4{0, 0, 0, 0};
-    f32x4 o[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int ks = 0; ks < 4; ++ks) qf[ks] = row_frag(Qg, C3, myq, 16 * ks + 8 * g, T);
+    f32x16 o[2] = {zero16(), zero16()};
     float m = -INFINITY, l = 0.f;
 
-    for (int kt = 0; kt <= qt; ++kt) {
-        const int k0 = kt * TILE;
-        __syncthreads();
-        load_rows(sK, Kg, C3, k0, T, tid);
-        load_rows_t(sVt, Vg, C3, k0, T, tid);
-        __syncthreads();
-        if (qw >= T) continue;
-        f32x4 s[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int kr = perm_row(j >> 1, j & 1, r16);
-            s[j] = mfma(ld16(sK + kr * PITCH + 8 * g), qf[0], f32x4{0.f, 0.f, 0.f, 0.f});
-            s[j] = mfma(ld16(sK + kr * PITCH + 32 + 8 * g), qf[1], s[j]);
+    const int kend = min(T, q0 + 128);
+    Tile64 tk, tv;
+    tk.load(Kg, C3, 0, T, tid);
+    tv.load(Vg, C3, 0, T, tid);
+    tk.store_n(sbuf[0], tid);
+    tv.store_t(sbuf[0] + 64 * 64, tid);
+    __syncthreads();
+    for (int k0 = 0, it = 0; k0 < kend; k0 += 64, ++it) {
+        const bf16* sK = sbuf[it & 1];
+        const bf16* sVt = sK + 64 * 64;
+        const bool more = k0 + 64 < kend;
+        if (more) {  // next tile in flight while this one is used
+            tk.load(Kg, C3, k0 + 64, T, tid);
+            tv.load(Vg, C3, k0 + 64, T, tid);
         }
-        const bool edge = (kt == qt) || (k0 + TILE > T);
-        float x[16];
-        float mt = -INFINITY;
+        if (qw < T && k0 <= qw + 31) {  // some key of this tile is visible to this wave
+        const bool edge = (k0 + 63 > qw) || (k0 + 64 > T);
+        float x[32];
 #pragma unroll
-        for (int sp = 0; sp < 2; ++sp)
+        for (int st = 0; st < 2; ++st) {
+            if (k0 + 32 * st > qw + 31) {  // sub-tile entirely in this wave's future
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                float v = s[2 * sp + (e >> 2)][e & 3] * c;
-                const int key = k0 + 32 * sp + 8 * g + e;
-                if (edge && (key > myq || key >= T)) v = -INFINITY;
-                x[sp * 8 + e] = v;
-                mt = fmaxf(mt, v);
+                for (int i = 0; i < 16; ++i) x[16 * st + i] = -INFINITY;
+                continue;
             }
-        mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+            const int kr = 32 * st + perm32(r32);
+            f32x16 s = zero16();
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) s = mfma32(ld16(sK + pos(kr, 2 * ks + g)), qf[ks], s);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                float v = s[i] * c;
+                const int key = k0 + 32 * st + 16 * (i >> 3) + 8 * g + (i & 7);
+                if (edge && (key > myq || key >= T)) v = -INFINITY;
+                x[16 * st + i] = v;
+            }
+        }
+        float mt = x[0];
+#pragma unroll
+        for (int i = 1; i < 32; ++i) mt = fmaxf(mt, x[i]);
         mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
         const float mn = fmaxf(m, mt);
-        const float corr = fast_exp2(m - mn);
-        l *= corr;
+        if (__any(mn > m)) {  // rescale only when some running maximum grew
+            const float corr = fast_exp2(m - mn);
+            l *= corr;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) o[j] *= corr;
-        u32x4 pk[2];
-#pragma unroll
-        for (int sp = 0; sp < 2; ++sp) {
-            float p[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                p[e] = fast_exp2(x[sp * 8 + e] - mn);
-                l += p[e];
+            for (int i = 0; i < 16; ++i) {
+                o[0][i] *= corr;
+                o[1][i] *= corr;
             }
-            pk[sp] = pack16<bf16>(p);
         }
         m = mn;
 #pragma unroll
-        for (int sp = 0; sp < 2; ++sp)
+        for (int s4 = 0; s4 < 4; ++s4) {
+            if (k0 + 16 * s4 > qw + 31) break;  // remaining slices are all masked for this wave
+            float p[8];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) o[j] = mfma(ld16(sVt + (16 * j + r16) * PITCH + 32 * sp + 8 * g), pk[sp], o[j]);
+            for (int e = 0; e < 8; ++e) {
+                p[e] = fast_exp2(x[8 * s4 + e] - mn);
+                l += p[e];
+            }
+            const u32x4 pk = pack16<bf16>(p);
+#pragma unroll
+            for (int dt = 0; dt < 2; ++dt) o[dt] = mfma32(ld16(sVt + pos(32 * dt + r32, 2 * s4 + g)), pk, o[dt]);
+        }
+        }
+        if (more) {
+            tk.store_n(sbuf[(it + 1) & 1], tid);
+            tv.store_t(sbuf[(it + 1) & 1] + 64 * 64, tid);
+        }
+        __syncthreads();
     }
-    l += __shfl_xor(l, 16, 64);
     l += __shfl_xor(l, 32, 64);
     if (myq < T) {
         const float inv = 1.0f / l;
         bf16* y = out + ((int64_t)b * T + myq) * C + h * HS;
+        // o[dt][i]: column (query) r32, row d = 32 dt + 8 (i/4) + 4 g + i%4
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            uint2 v;
-            v.x = (uint32_t)f32_to_bf16_bits(o[j][0] * inv) | ((uint32_t)f32_to_bf16_bits(o[j][1] * inv) << 16);
-            v.y = (uint32_t)f32_to_bf16_bits(o[j][2] * inv) | ((uint32_t)f32_to_bf16_bits(o[j][3] * inv) << 16);
-            *(uint2*)(y + 16 * j + 4 * g) = v;
-        }
+        for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4)
+                store4_bf16(y + 32 * dt + 8 * i4 + 4 * g, o[dt][4 * i4] * inv, o[dt][4 * i4 + 1] * inv,
+                            o[dt][4 * i4 + 2] * inv, o[dt][4 * i4 + 3] * inv);
         if (g == 0) lse[(int64_t)bh * T + myq] = (m + __log2f(l)) / LOG2E;
     }
 }
@@ -182,173 +229,218 @@ __global__ __launch_bounds__(256) void attn_bwd_dsum64(float* dsum, const bf16* 
     dsum[((int64_t)b * NH + h) * T + t] = acc;
 }
 
-// dK, dV for one tile of 64 keys (16 per wave), looping over the query tiles at
-// or after it.  Per 32-query slice: S and dP as [query x key] tiles (A = Q or dO
-// rows permuted, B = the wave's K or V fragments), then dV += P^T dO and
-// dK += dS^T Q with P^T / dS^T as A operands and dO^T / Q^T from LDS as B.
+// dK, dV for 128 keys (4 waves x 32), looping over query tiles of 64 at or after
+// them.  P and dS are [query x key] tiles with the key as accumulator column;
+// dV += P^T dO and dK += dS^T Q then take P^T / dS^T as A operands and dO^T / Q^T
+// (transposed LDS copies) as B operands.
 __global__ __launch_bounds__(256) void attn_bwd_dkdv_mfma64(bf16* dqkv, const bf16* qkv, const bf16* dout,
                                                             const float* lse, const float* dsum, int T, int C,
                                                             int NH) {
-    __shared__ __attribute__((aligned(16))) bf16 sQ[TILE * PITCH];
-    __shared__ __attribute__((aligned(16))) bf16 sG[TILE * PITCH];
-    __shared__ __attribute__((aligned(16))) bf16 sQt[HS * PITCH];
-    __shared__ __attribute__((aligned(16))) bf16 sGt[HS * PITCH];
-    __shared__ float sL[TILE], sD[TILE];
-    const int nqt = (T + TILE - 1) / TILE;
-    const int kt = blockIdx.x;  // key tile 0 has the most query tiles: scheduled first
+    __shared__ __attribute__((aligned(16))) bf16 sbuf[2][4 * 64 * 64];  // [stage][Q | dO | Q^T | dO^T]
+    __shared__ __attribute__((aligned(16))) float sLD[2][2][64];        // [stage][lse*log2e | D]
+    const int kt = blockIdx.x;  // the first key tiles see the most queries: scheduled first
     const int bh = blockIdx.y, b = bh / NH, h = bh % NH;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r16 = lane & 15, g = lane >> 4;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r32 = lane & 31, g = lane >> 5;
     const int64_t C3 = 3 * (int64_t)C;
     const bf16* base = qkv + (int64_t)b * T * C3;
     const bf16* Qg = base + h * HS;
     const bf16* Kg = base + C + h * HS;
     const bf16* Vg = base + 2 * C + h * HS;
     const bf16* Gg = dout + (int64_t)b * T * C + h * HS;
-    const int k0 = kt * TILE, kw = k0 + 16 * w, mykey = kw + r16;
+    const int k0 = kt * 128, kw = k0 + 32 * w, mykey = kw + r32;
     const float c = 0.125f * LOG2E;
 
-    u32x4 kf[2], vf[2];
+    u32x4 kf[4], vf[4];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-        kf[kk] = (mykey < T) ? ld16(Kg + (int64_t)mykey * C3 + 32 * kk + 8 * g) : u32x4{0, 0, 0, 0};
-        vf[kk] = (mykey < T) ? ld16(Vg + (int64_t)mykey * C3 + 32 * kk + 8 * g) : u32x4{0, 0, 0, 0};
+    for (int ks = 0; ks < 4; ++ks) {
+        kf[ks] = row_frag(Kg, C3, mykey, 16 * ks + 8 * g, T);
+        vf[ks] = row_frag(Vg, C3, mykey, 16 * ks + 8 * g, T);
     }
-    f32x4 dk[4], dv[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) dk[j] = dv[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x16 dk[2] = {zero16(), zero16()}, dv[2] = {zero16(), zero16()};
 
-    for (int qt = kt; qt < nqt; ++qt) {
-        const int q0 = qt * TILE;
-        __syncthreads();
-        load_rows(sQ, Qg, C3, q0, T, tid);
-        load_rows(sG, Gg, C, q0, T, tid);
-        load_rows_t(sQt, Qg, C3, q0, T, tid);
-        load_rows_t(sGt, Gg, C, q0, T, tid);
-        if (tid < TILE) {
+    Tile64 tq, tg;
+    float ld_l = 0.f, ld_d = 0.f;
+    auto load_q = [&](int q0) {
+        tq.load(Qg, C3, q0, T, tid);
+        tg.load(Gg, C, q0, T, tid);
+        if (tid < 64) {
             const int q = q0 + tid;
-            sL[tid] = q < T ? lse[(int64_t)bh * T + q] * LOG2E : 0.f;
-            sD[tid] = q < T ? dsum[(int64_t)bh * T + q] : 0.f;
+            ld_l = q < T ? lse[(int64_t)bh * T + q] * LOG2E : 0.f;
+            ld_d = q < T ? dsum[(int64_t)bh * T + q] : 0.f;
         }
-        __syncthreads();
-        if (kw >= T) continue;
-        const bool edge = (qt == kt) || (q0 + TILE > T);
-#pragma unroll
-        for (int sp = 0; sp < 2; ++sp) {
-            f32x4 s2[2], p2[2];
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                const int qr = perm_row(sp, hh, r16);
-                s2[hh] = mfma(ld16(sQ + qr * PITCH + 8 * g), kf[0], f32x4{0.f, 0.f, 0.f, 0.f});
-                s2[hh] = mfma(ld16(sQ + qr * PITCH + 32 + 8 * g), kf[1], s2[hh]);
-                p2[hh] = mfma(ld16(sG + qr * PITCH + 8 * g), vf[0], f32x4{0.f, 0.f, 0.f, 0.f});
-                p2[hh] = mfma(ld16(sG + qr * PITCH + 32 + 8 * g), vf[1], p2[hh]);
-            }
-            float p[8], ds[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int ql = 32 * sp + 8 * g + e;
-                float pv = fast_exp2(s2[e >> 2][e & 3] * c - sL[ql]);
-                if (edge && (q0 + ql >= T || mykey > q0 + ql)) pv = 0.f;
-                p[e] = pv;
-                ds[e] = pv * (p2[e >> 2][e & 3] - sD[ql]);
-            }
-            const u32x4 pp = pack16<bf16>(p), dd = pack16<bf16>(ds);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                dv[j] = mfma(pp, ld16(sGt + (16 * j + r16) * PITCH + 32 * sp + 8 * g), dv[j]);
-                dk[j] = mfma(dd, ld16(sQt + (16 * j + r16) * PITCH + 32 * sp + 8 * g), dk[j]);
-            }
+    };
+    auto store_q = [&](int st) {
+        bf16* b4 = sbuf[st];
+        tq.store_n(b4, tid);
+        tg.store_n(b4 + 64 * 64, tid);
+        tq.store_t(b4 + 2 * 64 * 64, tid);
+        tg.store_t(b4 + 3 * 64 * 64, tid);
+        if (tid < 64) {
+            sLD[st][0][tid] = ld_l;
+            sLD[st][1][tid] = ld_d;
         }
+    };
+    if (k0 < T) {
+        load_q(k0);
+        store_q(0);
     }
-    // dv[j] / dk[j]: column d = 16 j + r16, rows key kw + 4 g + i
+    __syncthreads();
+    for (int q0 = k0, it = 0; q0 < T; q0 += 64, ++it) {
+        const bf16* sQ = sbuf[it & 1];
+        const bf16* sG = sQ + 64 * 64;
+        const bf16* sQt = sQ + 2 * 64 * 64;
+        const bf16* sGt = sQ + 3 * 64 * 64;
+        const float* sL = sLD[it & 1][0];
+        const float* sD = sLD[it & 1][1];
+        const bool more = q0 + 64 < T;
+        if (more) load_q(q0 + 64);
+        if (kw < T && q0 + 63 >= kw) {  // some query of the tile sees this wave's keys
+        const bool edge = (q0 < kw + 31) || (q0 + 64 > T);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int key = kw + 4 * g + i;
+        for (int qs = 0; qs < 2; ++qs) {
+            if (q0 + 32 * qs + 31 < kw) continue;  // sub-tile entirely before this wave's keys
+            const int qr = 32 * qs + perm32(r32);
+            f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                s = mfma32(ld16(sQ + pos(qr, 2 * ks + g)), kf[ks], s);
+                dp = mfma32(ld16(sG + pos(qr, 2 * ks + g)), vf[ks], dp);
+            }
+#pragma unroll
+            for (int sl = 0; sl < 2; ++sl) {
+                float p[8], ds[8];
+                const int qlb = 32 * qs + 16 * sl + 8 * g;  // tile-local first query of this lane's 8
+                const float4 l0 = *(const float4*)&sL[qlb], l1 = *(const float4*)&sL[qlb + 4];
+                const float4 d0 = *(const float4*)&sD[qlb], d1 = *(const float4*)&sD[qlb + 4];
+                const float Lq[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+                const float Dq[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int q = q0 + qlb + e;
+                    float pv = fast_exp2(s[8 * sl + e] * c - Lq[e]);
+                    if (edge && (q >= T || mykey > q)) pv = 0.f;
+                    p[e] = pv;
+                    ds[e] = pv * (dp[8 * sl + e] - Dq[e]);
+                }
+                const u32x4 pp = pack16<bf16>(p), dd = pack16<bf16>(ds);
+                const int ch = 4 * qs + 2 * sl + g;
+#pragma unroll
+                for (int dt = 0; dt < 2; ++dt) {
+                    dv[dt] = mfma32(pp, ld16(sGt + pos(32 * dt + r32, ch)), dv[dt]);
+                    dk[dt] = mfma32(dd, ld16(sQt + pos(32 * dt + r32, ch)), dk[dt]);
+                }
+            }
+        }
+        }
+        if (more) store_q((it + 1) & 1);
+        __syncthreads();
+    }
+    // dv[dt][i] / dk[dt][i]: column d = 32 dt + r32, row key kw + 8 (i/4) + 4 g + i%4
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int key = kw + 8 * (i >> 2) + 4 * g + (i & 3);
         if (key < T) {
             bf16* row = dqkv + ((int64_t)b * T + key) * C3 + h * HS;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                row[C + 16 * j + r16] = from_f32<bf16>(dk[j][i] * 0.125f);
-                row[2 * C + 16 * j + r16] = from_f32<bf16>(dv[j][i]);
+            for (int dt = 0; dt < 2; ++dt) {
+                row[C + 32 * dt + r32] = from_f32<bf16>(dk[dt][i] * 0.125f);
+                row[2 * C + 32 * dt + r32] = from_f32<bf16>(dv[dt][i]);
             }
         }
     }
 }
 
-// dQ for one tile of 64 queries (16 per wave), looping over key tiles up to the
-// diagonal: S^T and dP^T as in the forward pass, dS (query x 8 keys per lane) as
-// the A operand of dQ = dS K with K^T from LDS.
+// dQ for 128 queries (4 waves x 32), looping over key tiles of 64 up to the
+// diagonal: S^T and dP^T as in the forward pass, dS (query x 8 keys per lane) as the
+// A operand of dQ = dS K with K^T from LDS.
 __global__ __launch_bounds__(256) void attn_bwd_dq_mfma64(bf16* dqkv, const bf16* qkv, const bf16* dout,
                                                           const float* lse, const float* dsum, int T, int C, int NH) {
-    __shared__ __attribute__((aligned(16))) bf16 sK[TILE * PITCH];
-    __shared__ __attribute__((aligned(16))) bf16 sV[TILE * PITCH];
-    __shared__ __attribute__((aligned(16))) bf16 sKt[HS * PITCH];
-    const int nqt = (T + TILE - 1) / TILE;
+    __shared__ __attribute__((aligned(16))) bf16 sbuf[2][3 * 64 * 64];  // [stage][K | V | K^T]
+    const int nqt = (T + 127) / 128;
     const int qt = nqt - 1 - (int)blockIdx.x;
     const int bh = blockIdx.y, b = bh / NH, h = bh % NH;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r16 = lane & 15, g = lane >> 4;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r32 = lane & 31, g = lane >> 5;
     const int64_t C3 = 3 * (int64_t)C;
     const bf16* base = qkv + (int64_t)b * T * C3;
     const bf16* Qg = base + h * HS;
     const bf16* Kg = base + C + h * HS;
     const bf16* Vg = base + 2 * C + h * HS;
     const bf16* Gg = dout + (int64_t)b * T * C + h * HS;
-    const int q0 = qt * TILE, qw = q0 + 16 * w, myq = qw + r16;
+    const int q0 = qt * 128, qw = q0 + 32 * w, myq = qw + r32;
     const float c = 0.125f * LOG2E;
 
-    u32x4 qf[2], gf[2];
+    u32x4 qf[4], gf[4];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-        qf[kk] = (myq < T) ? ld16(Qg + (int64_t)myq * C3 + 32 * kk + 8 * g) : u32x4{0, 0, 0, 0};
-        gf[kk] = (myq < T) ? ld16(Gg + (int64_t)myq * C + 32 * kk + 8 * g) : u32x4{0, 0, 0, 0};
+    for (int ks = 0; ks < 4; ++ks) {
+        qf[ks] = row_frag(Qg, C3, myq, 16 * ks + 8 * g, T);
+        gf[ks] = row_frag(Gg, C, myq, 16 * ks + 8 * g, T);
     }
     const float L2 = (myq < T) ? lse[(int64_t)bh * T + myq] * LOG2E : 0.f;
     const float Dq = (myq < T) ? dsum[(int64_t)bh * T + myq] : 0.f;
-    f32x4 dq[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) dq[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x16 dq[2] = {zero16(), zero16()};
 
-    for (int kt = 0; kt <= qt; ++kt) {
-        const int k0 = kt * TILE;
-        __syncthreads();
-        load_rows(sK, Kg, C3, k0, T, tid);
-        load_rows(sV, Vg, C3, k0, T, tid);
-        load_rows_t(sKt, Kg, C3, k0, T, tid);
-        __syncthreads();
-        if (qw >= T) continue;
-        const bool edge = (kt == qt) || (k0 + TILE > T);
-#pragma unroll
-        for (int sp = 0; sp < 2; ++sp) {
-            f32x4 s2[2], p2[2];
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                const int kr = perm_row(sp, hh, r16);
-                s2[hh] = mfma(ld16(sK + kr * PITCH + 8 * g), qf[0], f32x4{0.f, 0.f, 0.f, 0.f});
-                s2[hh] = mfma(ld16(sK + kr * PITCH + 32 + 8 * g), qf[1], s2[hh]);
-                p2[hh] = mfma(ld16(sV + kr * PITCH + 8 * g), gf[0], f32x4{0.f, 0.f, 0.f, 0.f});
-                p2[hh] = mfma(ld16(sV + kr * PITCH + 32 + 8 * g), gf[1], p2[hh]);
-            }
-            float ds[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int key = k0 + 32 * sp + 8 * g + e;
-                float pv = fast_exp2(s2[e >> 2][e & 3] * c - L2);
-                if (edge && (key > myq || key >= T)) pv = 0.f;
-                ds[e] = pv * (p2[e >> 2][e & 3] - Dq);
-            }
-            const u32x4 dd = pack16<bf16>(ds);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) dq[j] = mfma(dd, ld16(sKt + (16 * j + r16) * PITCH + 32 * sp + 8 * g), dq[j]);
+    const int kend = min(T, q0 + 128);
+    Tile64 tk, tv;
+    tk.load(Kg, C3, 0, T, tid);
+    tv.load(Vg, C3, 0, T, tid);
+    tk.store_n(sbuf[0], tid);
+    tv.store_n(sbuf[0] + 64 * 64, tid);
+    tk.store_t(sbuf[0] + 2 * 64 * 64, tid);
+    __syncthreads();
+    for (int k0 = 0, it = 0; k0 < kend; k0 += 64, ++it) {
+        const bf16* sK = sbuf[it & 1];
+        const bf16* sV = sK + 64 * 64;
+        const bf16* sKt = sK + 2 * 64 * 64;
+        const bool more = k0 + 64 < kend;
+        if (more) {
+            tk.load(Kg, C3, k0 + 64, T, tid);
+            tv.load(Vg, C3, k0 + 64, T, tid);
         }
-    }
-    // dq[j]: column d = 16 j + r16, rows query qw + 4 g + i
+        if (qw < T && k0 <= qw + 31) {
+        const bool edge = (k0 + 63 > qw) || (k0 + 64 > T);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int q = qw + 4 * g + i;
+        for (int st = 0; st < 2; ++st) {
+            if (k0 + 32 * st > qw + 31) continue;
+            const int kr = 32 * st + perm32(r32);
+            f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                s = mfma32(ld16(sK + pos(kr, 2 * ks + g)), qf[ks], s);
+                dp = mfma32(ld16(sV + pos(kr, 2 * ks + g)), gf[ks], dp);
+            }
+#pragma unroll
+            for (int sl = 0; sl < 2; ++sl) {
+                float ds[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int key = k0 + 32 * st + 16 * sl + 8 * g + e;
+                    float pv = fast_exp2(s[8 * sl + e] * c - L2);
+                    if (edge && (key > myq || key >= T)) pv = 0.f;
+                    ds[e] = pv * (dp[8 * sl + e] - Dq);
+                }
+                const u32x4 dd = pack16<bf16>(ds);
+                const int ch = 4 * st + 2 * sl + g;
+#pragma unroll
+                for (int dt = 0; dt < 2; ++dt) dq[dt] = mfma32(dd, ld16(sKt + pos(32 * dt + r32, ch)), dq[dt]);
+            }
+        }
+        }
+        if (more) {
+            bf16* nb = sbuf[(it + 1) & 1];
+            tk.store_n(nb, tid);
+            tv.store_n(nb + 64 * 64, tid);
+            tk.store_t(nb + 2 * 64 * 64, tid);
+        }
+        __syncthreads();
+    }
+    // dq[dt][i]: column d = 32 dt + r32, row query qw + 8 (i/4) + 4 g + i%4
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int q = qw + 8 * (i >> 2) + 4 * g + (i & 3);
         if (q < T) {
             bf16* row = dqkv + ((int64_t)b * T + q) * C3 + h * HS;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) row[16 * j + r16] = from_f32<bf16>(dq[j][i] * 0.125f);
+            for (int dt = 0; dt < 2; ++dt) row[32 * dt + r32] = from_f32<bf16>(dq[dt][i] * 0.125f);
         }
     }
 }
@@ -358,7 +450,7 @@ hipError_t attention_forward_mfma64(bf16* out, float* lse, const bf16* qkv, int 
                                     hipStream_t s) {
     const double pairs = (double)B * NH * T * (T + 1) / 2;
     ProfScope prof(s, "attn_fwd_mfma64", 4.0 * HS * pairs, 2.0 * B * T * NH * HS * 4 + 4.0 * B * NH * T);
-    dim3 grid((T + TILE - 1) / TILE, B * NH);
+    dim3 grid((T + 127) / 128, B * NH);
     hipLaunchKernelGGL(attn_fwd_mfma64, grid, dim3(256), 0, s, out, lse, qkv, T, C, NH);
     return hipGetLastError();
 }
@@ -373,16 +465,17 @@ hipError_t attention_backward_mfma64(bf16* dqkv, float* dsum, const bf16* dout, 
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    dim3 grid((T + TILE - 1) / TILE, B * NH);
     {
         ProfScope prof(s, "attn_bwd_dkdv_mfma64", 4.0 * HS * pairs, 6 * io + 8.0 * B * NH * T);
-        hipLaunchKernelGGL(attn_bwd_dkdv_mfma64, grid, dim3(256), 0, s, dqkv, qkv, dout, lse, dsum, T, C, NH);
+        hipLaunchKernelGGL(attn_bwd_dkdv_mfma64, dim3((T + 127) / 128, B * NH), dim3(256), 0, s, dqkv, qkv, dout, lse,
+                           dsum, T, C, NH);
     }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     {
         ProfScope prof(s, "attn_bwd_dq_mfma64", 4.0 * HS * pairs, 5 * io + 8.0 * B * NH * T);
-        hipLaunchKernelGGL(attn_bwd_dq_mfma64, grid, dim3(256), 0, s, dqkv, qkv, dout, lse, dsum, T, C, NH);
+        hipLaunchKernelGGL(attn_bwd_dq_mfma64, dim3((T + 127) / 128, B * NH), dim3(256), 0, s, dqkv, qkv, dout, lse,
+                           dsum, T, C, NH);
     }
     return hipGetLastError();
 }

@@ -14,12 +14,14 @@ struct bf16 {
 __device__ __forceinline__ float to_f32(float v) { return v; }
 __device__ __forceinline__ float to_f32(bf16 v) { return __uint_as_float((uint32_t)v.x << 16); }
 
-// fp32 -> bf16, round to nearest, ties to even (NaN kept quiet).
-__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+// fp32 -> bf16, round to nearest, ties to even: the compiler lowers these
+// conversions to gfx950's v_cvt_pk_bf16_f32 (two values per instruction).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+__device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
+    const f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 template <class T> __device__ __forceinline__ T from_f32(float v);
@@ -55,8 +57,7 @@ template <> __device__ __forceinline__ u32x4 pack16<float>(const float* in) {
 template <> __device__ __forceinline__ u32x4 pack16<bf16>(const float* in) {
     u32x4 v;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        v[i] = (uint32_t)f32_to_bf16_bits(in[2 * i]) | ((uint32_t)f32_to_bf16_bits(in[2 * i + 1]) << 16);
+    for (int i = 0; i < 4; ++i) v[i] = pack2_bf16(in[2 * i], in[2 * i + 1]);
     return v;
 }
 

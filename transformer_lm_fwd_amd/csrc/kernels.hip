@@ -486,8 +486,8 @@ __global__ __launch_bounds__(256) void adamw_kernel(float* p, const float* g, fl
         ((float4*)v)[i] = vv;
         if (p16) {
             uint2 h;
-            h.x = (uint32_t)f32_to_bf16_bits(pp.x) | ((uint32_t)f32_to_bf16_bits(pp.y) << 16);
-            h.y = (uint32_t)f32_to_bf16_bits(pp.z) | ((uint32_t)f32_to_bf16_bits(pp.w) << 16);
+            h.x = pack2_bf16(pp.x, pp.y);
+            h.y = pack2_bf16(pp.z, pp.w);
             ((uint2*)p16)[i] = h;
         }
     }
