@@ -18,6 +18,9 @@
 // 4*(l/16) .. +3 of column l % 16.  The reduction over k does not depend on
 // which k a lane group takes as long as A and B agree, so both read the same
 // k offsets.
+#include <algorithm>
+#include <mutex>
+#include <set>
 #include <string>
 
 #include "kernels.h"
@@ -528,13 +531,20 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a, int
     }
 }
 
+// Profiler name of a launch: layout, epilogue and shape (M x N x K, / splits),
+// interned so the pointer stays valid.
 template <class T, bool AK, bool BKC, int EPI>
-static const char* gemm_name() {
-    static const std::string n = std::string("gemm_") + (sizeof(T) == 2 ? "bf16_" : "f32_") +
-                                 (AK && BKC ? "xwT" : AK ? "dyW" : "dyTx") + "_" +
-                                 (EPI == EPI_BIAS ? "bias" : EPI == EPI_BIAS_RES ? "bias_res" :
-                                  EPI == EPI_BIAS_GELU ? "bias_gelu" : EPI == EPI_GELU_BWD ? "gelu_bwd" : "f32out");
-    return n.c_str();
+static const char* gemm_name(int M, int N, int K, int splits) {
+    static std::mutex mu;
+    static std::set<std::string> names;
+    std::string n = std::string("gemm_") + (sizeof(T) == 2 ? "bf16_" : "f32_") +
+                    (AK && BKC ? "xwT" : AK ? "dyW" : "dyTx") + "_" +
+                    (EPI == EPI_BIAS ? "bias" : EPI == EPI_BIAS_RES ? "bias_res" :
+                     EPI == EPI_BIAS_GELU ? "bias_gelu" : EPI == EPI_GELU_BWD ? "gelu_bwd" : "f32out") +
+                    "_" + std::to_string(M) + "x" + std::to_string(N) + "x" + std::to_string(K);
+    if (splits > 1) n += "/" + std::to_string(splits);
+    std::lock_guard<std::mutex> lk(mu);
+    return names.insert(n).first->c_str();
 }
 
 template <class T, bool AK, bool BKC, int EPI>
@@ -544,7 +554,8 @@ static hipError_t launch(const GemmArgs& a, int splits, int k_per_split, int64_t
     dim3 grid((a.N + BN - 1) / BN, (a.M + BM - 1) / BM, splits);
     const double es = sizeof(T), mn = (double)a.M * a.N;
     const double out_bytes = EPI == EPI_F32 ? 4 * mn : (EPI == EPI_BIAS ? es * mn : 2 * es * mn);
-    ProfScope prof(s, gemm_name<T, AK, BKC, EPI>(), 2.0 * mn * a.K, es * ((double)a.M + a.N) * a.K + out_bytes);
+    ProfScope prof(s, gemm_name<T, AK, BKC, EPI>(a.M, a.N, a.K, splits), 2.0 * mn * a.K,
+                   es * ((double)a.M + a.N) * a.K + out_bytes);
     if constexpr (sizeof(T) == 2) {
         // buffer extents in bytes: whole rows of each operand as stored
         const int64_t ab = (AK ? (int64_t)a.M : (int64_t)a.K) * a.lda * 2;
@@ -581,12 +592,15 @@ hipError_t gemm(const GemmArgs& a, bool ak, bool bk, int epi, float* ws, size_t 
     if (epi == EPI_F32) {
         // Output fp32 [M, N] with row stride ldc.  Few output tiles and a long K:
         // split K over blockIdx.z into fp32 partials in `ws`, then reduce in a fixed order.
-        int tiles = ((a.M + 127) / 128) * ((a.N + 127) / 128);
+        // Up to 512 blocks are resident at once (two per CU): use the most splits that
+        // keep the launch within that, each split at least 8 k-tiles long.
+        const int tiles = ((a.M + 127) / 128) * ((a.N + 127) / 128);
         int splits = 1;
-        if (ws && a.ldc == a.N) {
-            while (splits < 16 && tiles * splits < 512 && a.K / (splits * 2) >= 8 * BK &&
-                   (size_t)(splits * 2) * a.M * a.N <= ws_floats)
-                splits *= 2;
+        if (ws && a.ldc == a.N && tiles < 256) {
+            splits = 512 / tiles;
+            splits = std::min(splits, a.K / (8 * BK));
+            while (splits > 1 && (size_t)splits * a.M * a.N > ws_floats) --splits;
+            splits = std::max(splits, 1);
         }
         if (splits == 1) return dispatch_layout<T, EPI_F32>(a, ak, bk, 1, a.K, 0, s);
         int kps = (a.K + splits - 1) / splits;

@@ -44,10 +44,17 @@ struct gpt2_arena {
     size_t params, grads, adam_m, adam_v, params16;
     size_t encoded, lnf, lnfs, logits, losses, loss;
     std::vector<LayerActs> la;
-    size_t dres, dbuf, dqkv, dfch, dsum, partial, ws;
+    size_t dres[4], dbuf, dqkv[2], dfch[2], dsum, partial, partial_side, ws;
     size_t partial_floats, ws_floats;
     bool loss_ready;
     const int32_t* inputs;
+    // Backward concurrency: parameter-gradient work runs on `side`.  rd_* mark the
+    // side stream's last read of each ring buffer; fork events order side work
+    // after main-stream producers.  Created on the first backward pass.
+    hipStream_t side = nullptr;
+    hipEvent_t rd_res[4] = {}, rd_fch[2] = {}, rd_qkv[2] = {}, ev_wte = nullptr, ev_end = nullptr;
+    hipEvent_t fork[8] = {};
+    int fork_next = 0;
 };
 
 namespace {
@@ -135,14 +142,16 @@ size_t layout(gpt2_arena& a) {
     a.logits = take(BT * (int64_t)a.Vp * es);
     a.losses = take(BT * 4);
     a.loss = take(4);
-    // backward scratch, reused by every layer
-    a.dres = take(BT * C * es);
+    // backward scratch: a ring of four residual-gradient buffers and two of each of
+    // dfch / dqkv, so the main stream never overwrites what the side stream reads
+    for (int i = 0; i < 4; ++i) a.dres[i] = take(BT * C * es);
     a.dbuf = take(BT * C * es);
-    a.dqkv = take(BT * 3 * C * es);
-    a.dfch = take(BT * 4 * C * es);
+    for (int i = 0; i < 2; ++i) a.dqkv[i] = take(BT * 3 * C * es);
+    for (int i = 0; i < 2; ++i) a.dfch[i] = take(BT * 4 * C * es);
     a.dsum = take(BT * NH * 4);
-    a.partial_floats = (size_t)512 * 2 * 4 * C;  // LayerNorm (<=512 blocks x 2C) and bias (64 x 4C) partials
+    a.partial_floats = (size_t)512 * 2 * 4 * C;  // column-sum partials (<= 256 blocks x 4C)
     a.partial = take(a.partial_floats * 4);
+    a.partial_side = take(a.partial_floats * 4);
     a.ws_floats = (size_t)16 * 4 * C * C;  // split-K partials of the largest block dW (4C x C), 16 splits
     a.ws = take(a.ws_floats * 4);
     return o;
@@ -164,11 +173,47 @@ int hip_check(hipError_t e, const char* what) {
         if (rc__ != GPT2_OK) return rc__;                   \
     } while (0)
 
+int ensure_streams(gpt2_arena* a) {
+    if (a->side) return GPT2_OK;
+    if (hipStreamCreateWithFlags(&a->side, hipStreamNonBlocking) != hipSuccess)
+        return fail(GPT2_E_HIP, "cannot create the side stream");
+    auto mk = [](hipEvent_t* e) { return hipEventCreateWithFlags(e, hipEventDisableTiming) == hipSuccess; };
+    bool ok = mk(&a->ev_wte) && mk(&a->ev_end);
+    for (auto& e : a->rd_res) ok = ok && mk(&e);
+    for (auto& e : a->rd_fch) ok = ok && mk(&e);
+    for (auto& e : a->rd_qkv) ok = ok && mk(&e);
+    for (auto& e : a->fork) ok = ok && mk(&e);
+    return ok ? GPT2_OK : fail(GPT2_E_HIP, "cannot create events");
+}
+
+// `to` waits for everything enqueued on `from` so far.
+int stream_wait(gpt2_arena* a, hipStream_t to, hipStream_t from) {
+    hipEvent_t e = a->fork[a->fork_next];
+    a->fork_next = (a->fork_next + 1) % 8;
+    if (hipEventRecord(e, from) != hipSuccess || hipStreamWaitEvent(to, e, 0) != hipSuccess)
+        return fail(GPT2_E_HIP, "stream fork/join failed");
+    return GPT2_OK;
+}
+
+void destroy_streams(gpt2_arena* a) {
+    if (!a->side) return;
+    hipStreamDestroy(a->side);
+    auto rm = [](hipEvent_t e) { if (e) hipEventDestroy(e); };
+    rm(a->ev_wte);
+    rm(a->ev_end);
+    for (auto e : a->rd_res) rm(e);
+    for (auto e : a->rd_fch) rm(e);
+    for (auto e : a->rd_qkv) rm(e);
+    for (auto e : a->fork) rm(e);
+    a->side = nullptr;
+}
+
 template <class T>
 struct Model {
     gpt2_arena* a;
     hipStream_t s;
     int C, L, NH, V, Vp, B, S, BT, P;  // S: sequence length
+    bool split_ok = true;               // main-stream GEMMs may use the split-K workspace
 
     Model(gpt2_arena* ar, hipStream_t st) : a(ar), s(st) {
         C = a->cfg.channels; L = a->cfg.num_layers; NH = a->cfg.num_heads; V = a->cfg.vocab_size;
@@ -191,7 +236,8 @@ struct Model {
         GemmArgs g;
         g.A = A; g.B = Bm; g.C = Cm; g.C2 = C2; g.R = R; g.bias = bias;
         g.M = M; g.N = N; g.K = K; g.lda = lda; g.ldb = ldb; g.ldc = ldc;
-        CHECK(gemm<T>(g, ak, bk, epi, f32(a->ws), a->ws_floats, s), "gemm");
+        // the split-K workspace belongs to the side stream during backward
+        CHECK(gemm<T>(g, ak, bk, epi, split_ok ? f32(a->ws) : nullptr, split_ok ? a->ws_floats : 0, s), "gemm");
         return GPT2_OK;
     }
 
@@ -236,62 +282,110 @@ struct Model {
         return GPT2_OK;
     }
 
+    // Backward.  The main stream `s` runs the chain that feeds the next layer (dX
+    // GEMMs, LayerNorm and attention backward); every parameter-gradient product
+    // (weight GEMMs, bias column sums, the tied-embedding dW) runs on the side
+    // stream, which forks after each producer and is joined at the end.
     int backward() {
         int rc;
+        if ((rc = ensure_streams(a))) return rc;
+        split_ok = false;
+        hipStream_t M = s, SD = a->side;
         T* dz = act(a->logits);
-        T* dres = act(a->dres);
         T* dbuf = act(a->dbuf);
-        T* dqkv = act(a->dqkv);
-        T* dfch = act(a->dfch);
         float* part = f32(a->partial);
-        // lm_head: dlnf = dz wte ; dwte = dz^T lnf (overwrites; the encoder adds later)
+        float* part_side = f32(a->partial_side);
+        auto wait = [&](hipStream_t st, hipEvent_t e) -> int {
+            return hipStreamWaitEvent(st, e, 0) == hipSuccess ? GPT2_OK : fail(GPT2_E_HIP, "hipStreamWaitEvent");
+        };
+        auto mark = [&](hipEvent_t e, hipStream_t st) -> int {
+            return hipEventRecord(e, st) == hipSuccess ? GPT2_OK : fail(GPT2_E_HIP, "hipEventRecord");
+        };
+        // side-stream weight GEMM: dW = dY^T X (fp32, overwrites), db = column sums of dY
+        auto side_dw = [&](const T* dy, int OC, const T* x, int IC, int64_t ow, int64_t ob) -> int {
+            int r;
+            GemmArgs g{};
+            g.A = dy; g.B = x; g.C = grad(ow);
+            g.M = OC; g.N = IC; g.K = BT; g.lda = OC; g.ldb = IC; g.ldc = IC;
+            if ((r = hip_check(gemm<T>(g, false, false, EPI_F32, f32(a->ws), a->ws_floats, SD), "gemm"))) return r;
+            if (ob >= 0)
+                return hip_check(bias_grad<T>(grad(ob), dy, BT, OC, OC, part_side, a->partial_floats, SD), "bias grad");
+            return GPT2_OK;
+        };
+
+        // lm_head: dlnf = dz wte on the main stream; dwte = dz^T lnf (overwrites) on the side
+        if ((rc = stream_wait(a, SD, M))) return rc;
+        {
+            GemmArgs g{};
+            g.A = dz; g.B = act(a->lnf); g.C = grad(a->o_wte);
+            g.M = V; g.N = C; g.K = BT; g.lda = Vp; g.ldb = C; g.ldc = C;
+            CHECK(gemm<T>(g, false, false, EPI_F32, f32(a->ws), a->ws_floats, SD), "gemm");
+        }
+        if ((rc = mark(a->ev_wte, SD))) return rc;
         if ((rc = gemm_call(dz, Vp, true, weight(a->o_wte), C, false, dbuf, C, BT, C, V, EPI_BIAS))) return rc;
-        if ((rc = gemm_call(dz, Vp, false, act(a->lnf), C, false, grad(a->o_wte), C, V, C, BT, EPI_F32))) return rc;
-        CHECK(layernorm_backward<T>(dres, grad(a->o_lnfw), grad(a->o_lnfb), dbuf, act(a->la[L - 1].res3), f32(a->lnfs),
-                                    master(a->o_lnfw), BT, C, part, a->partial_floats, s, false), "lnf backward");
+        int cur = 0;
+        if ((rc = wait(M, a->rd_res[0]))) return rc;
+        CHECK(layernorm_backward<T>(act(a->dres[0]), (const T*)nullptr, grad(a->o_lnfw), grad(a->o_lnfb), dbuf,
+                                    act(a->la[L - 1].res3), f32(a->lnfs), master(a->o_lnfw), BT, C, part,
+                                    a->partial_floats, M), "lnf backward");
         for (int l = L - 1; l >= 0; --l) {
             const LayerActs& x = a->la[l];
             const T* xin = l == 0 ? act(a->encoded) : act(a->la[l - 1].res3);
-            // mlp c_proj: dfch = (dres W_fcproj) * gelu'(fch); dW = dres^T fchg; db = colsum(dres)
-            if ((rc = gemm_call(dres, C, true, weight(lp(l, P_FCPW)), 4 * C, false, dfch, 4 * C, BT, 4 * C, C,
+            const int i_in = cur, i_mid = (cur + 1) % 4, i_out = (cur + 2) % 4, p = l & 1;
+            T* din = act(a->dres[i_in]);
+            T* dmid = act(a->dres[i_mid]);
+            T* dout = act(a->dres[i_out]);
+            T* dfch = act(a->dfch[p]);
+            T* dqkv = act(a->dqkv[p]);
+            // mlp c_proj: side: dW = din^T fchg, db = colsum(din); main: dfch = (din W_fcproj) * gelu'(fch)
+            if ((rc = stream_wait(a, SD, M))) return rc;
+            if ((rc = side_dw(din, C, act(x.fchg), 4 * C, lp(l, P_FCPW), lp(l, P_FCPB)))) return rc;
+            if ((rc = mark(a->rd_res[i_in], SD))) return rc;
+            if ((rc = wait(M, a->rd_fch[p]))) return rc;
+            if ((rc = gemm_call(din, C, true, weight(lp(l, P_FCPW)), 4 * C, false, dfch, 4 * C, BT, 4 * C, C,
                                 EPI_GELU_BWD, nullptr, act(x.fch))))
                 return rc;
-            if ((rc = gemm_call(dres, C, false, act(x.fchg), 4 * C, false, grad(lp(l, P_FCPW)), 4 * C, C, 4 * C, BT,
-                                EPI_F32)))
-                return rc;
-            CHECK(bias_grad<T>(grad(lp(l, P_FCPB)), dres, BT, C, C, part, a->partial_floats, s), "fcproj bias");
-            // c_fc: dln2 = dfch W_fc; dW = dfch^T ln2; db = colsum(dfch)
+            // c_fc: side: dW = dfch^T ln2, db = colsum(dfch); main: dln2 = dfch W_fc
+            if ((rc = stream_wait(a, SD, M))) return rc;
+            if ((rc = side_dw(dfch, 4 * C, act(x.ln2), C, lp(l, P_FCW), lp(l, P_FCB)))) return rc;
+            if ((rc = mark(a->rd_fch[p], SD))) return rc;
             if ((rc = gemm_call(dfch, 4 * C, true, weight(lp(l, P_FCW)), C, false, dbuf, C, BT, C, 4 * C, EPI_BIAS)))
                 return rc;
-            if ((rc = gemm_call(dfch, 4 * C, false, act(x.ln2), C, false, grad(lp(l, P_FCW)), C, 4 * C, C, BT,
-                                EPI_F32)))
+            // ln_2: dmid = din + LN backward
+            if ((rc = wait(M, a->rd_res[i_mid]))) return rc;
+            CHECK(layernorm_backward<T>(dmid, din, grad(lp(l, P_LN2W)), grad(lp(l, P_LN2B)), dbuf, act(x.res2),
+                                        f32(x.ln2s), master(lp(l, P_LN2W)), BT, C, part, a->partial_floats, M),
+                  "ln2 backward");
+            // attn c_proj: side: dW = dmid^T atty, db; main: datty = dmid W_proj
+            if ((rc = stream_wait(a, SD, M))) return rc;
+            if ((rc = side_dw(dmid, C, act(x.atty), C, lp(l, P_PROJW), lp(l, P_PROJB)))) return rc;
+            if ((rc = mark(a->rd_res[i_mid], SD))) return rc;
+            if ((rc = gemm_call(dmid, C, true, weight(lp(l, P_PROJW)), C, false, dbuf, C, BT, C, C, EPI_BIAS)))
                 return rc;
-            CHECK(bias_grad<T>(grad(lp(l, P_FCB)), dfch, BT, 4 * C, 4 * C, part, a->partial_floats, s), "fc bias");
-            // ln_2: dres += LN backward
-            CHECK(layernorm_backward<T>(dres, grad(lp(l, P_LN2W)), grad(lp(l, P_LN2B)), dbuf, act(x.res2), f32(x.ln2s),
-                                        master(lp(l, P_LN2W)), BT, C, part, a->partial_floats, s, true), "ln2 backward");
-            // attn c_proj: datty = dres W_proj; dW = dres^T atty; db = colsum(dres)
-            if ((rc = gemm_call(dres, C, true, weight(lp(l, P_PROJW)), C, false, dbuf, C, BT, C, C, EPI_BIAS)))
-                return rc;
-            if ((rc = gemm_call(dres, C, false, act(x.atty), C, false, grad(lp(l, P_PROJW)), C, C, C, BT, EPI_F32)))
-                return rc;
-            CHECK(bias_grad<T>(grad(lp(l, P_PROJB)), dres, BT, C, C, part, a->partial_floats, s), "proj bias");
             // attention
-            CHECK(attention_backward<T>(dqkv, f32(a->dsum), dbuf, act(x.atty), act(x.qkv), f32(x.lse), B, S, C, NH, s),
+            if ((rc = wait(M, a->rd_qkv[p]))) return rc;
+            CHECK(attention_backward<T>(dqkv, f32(a->dsum), dbuf, act(x.atty), act(x.qkv), f32(x.lse), B, S, C, NH, M),
                   "attention backward");
-            // c_attn: dln1 = dqkv W_qkv; dW = dqkv^T ln1; db = colsum(dqkv)
+            // c_attn: side: dW = dqkv^T ln1, db; main: dln1 = dqkv W_qkv
+            if ((rc = stream_wait(a, SD, M))) return rc;
+            if ((rc = side_dw(dqkv, 3 * C, act(x.ln1), C, lp(l, P_QKVW), lp(l, P_QKVB)))) return rc;
+            if ((rc = mark(a->rd_qkv[p], SD))) return rc;
             if ((rc = gemm_call(dqkv, 3 * C, true, weight(lp(l, P_QKVW)), C, false, dbuf, C, BT, C, 3 * C, EPI_BIAS)))
                 return rc;
-            if ((rc = gemm_call(dqkv, 3 * C, false, act(x.ln1), C, false, grad(lp(l, P_QKVW)), C, 3 * C, C, BT,
-                                EPI_F32)))
-                return rc;
-            CHECK(bias_grad<T>(grad(lp(l, P_QKVB)), dqkv, BT, 3 * C, 3 * C, part, a->partial_floats, s), "qkv bias");
-            // ln_1: dres += LN backward (dres is now d xin)
-            CHECK(layernorm_backward<T>(dres, grad(lp(l, P_LN1W)), grad(lp(l, P_LN1B)), dbuf, xin, f32(x.ln1s),
-                                        master(lp(l, P_LN1W)), BT, C, part, a->partial_floats, s, true), "ln1 backward");
+            // ln_1: dout = dmid + LN backward (= d xin)
+            if ((rc = wait(M, a->rd_res[i_out]))) return rc;
+            CHECK(layernorm_backward<T>(dout, dmid, grad(lp(l, P_LN1W)), grad(lp(l, P_LN1B)), dbuf, xin, f32(x.ln1s),
+                                        master(lp(l, P_LN1W)), BT, C, part, a->partial_floats, M),
+                  "ln1 backward");
+            cur = i_out;
         }
-        CHECK(encoder_backward<T>(grad(a->o_wte), grad(a->o_wpe), dres, a->inputs, B, S, P, C, s), "encoder backward");
-        return GPT2_OK;
+        // embedding: dwte += scatter (after the side stream's lm_head dW), dwpe
+        if ((rc = wait(M, a->ev_wte))) return rc;
+        CHECK(encoder_backward<T>(grad(a->o_wte), grad(a->o_wpe), act(a->dres[cur]), a->inputs, B, S, P, C, M),
+              "encoder backward");
+        // join: everything the side stream enqueued finishes before later main-stream work
+        if ((rc = mark(a->ev_end, SD))) return rc;
+        return wait(M, a->ev_end);
     }
 };
 
@@ -352,6 +446,7 @@ int gpt2_alloc_arena(const gpt2_config* cfg, int32_t B, int32_t T, int32_t dtype
 }
 
 int gpt2_free_arena(gpt2_arena* a) {
+    if (a) destroy_streams(a);
     delete a;
     return GPT2_OK;
 }

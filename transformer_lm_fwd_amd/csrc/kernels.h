@@ -51,12 +51,12 @@ hipError_t encoder_forward(T* out, const int32_t* tok, const float* wte, const f
 template <class T>
 hipError_t layernorm_forward(T* out, float* stats, const T* inp, const float* w, const float* b, int N, int C,
                              hipStream_t s);
-// dres (+)= LN backward dx (accumulate selects += or =); per-block partial (dw, db) sums into `partial`
-// [nblocks][2C], then reduced into dw, db (overwrite).
+// dres = dres_in + LN backward dx (dres_in may be null, or equal to dres); dw, db
+// (overwrite) from column sums through `partial`.
 template <class T>
-hipError_t layernorm_backward(T* dres, float* dw, float* db, const T* dout, const T* inp, const float* stats,
-                              const float* w, int N, int C, float* partial, size_t partial_floats, hipStream_t s,
-                              bool accumulate);
+hipError_t layernorm_backward(T* dres, const T* dres_in, float* dw, float* db, const T* dout, const T* inp,
+                              const float* stats, const float* w, int N, int C, float* partial, size_t partial_floats,
+                              hipStream_t s);
 // dbias[n] = sum_m dout[m, n] (overwrite), deterministic two-stage.
 template <class T>
 hipError_t bias_grad(float* dbias, const T* dout, int M, int N, int64_t ld, float* partial, size_t partial_floats,

@@ -111,9 +111,9 @@ hipError_t layernorm_forward(T* out, float* stats, const T* inp, const float* w,
 //   dw = sum_rows dy * xhat,  db = sum_rows dy                          (column sums, below)
 // dx: one wave per row, the row's dy and x held in registers.
 template <class T, int MAXCH>
-__global__ __launch_bounds__(256) void layernorm_backward_dx_kernel(T* dres, const T* dout, const T* inp,
-                                                                    const float* stats, const float* w, int N, int C,
-                                                                    int accumulate) {
+__global__ __launch_bounds__(256) void layernorm_backward_dx_kernel(T* dres, const T* dres_in, const T* dout,
+                                                                    const T* inp, const float* stats, const float* w,
+                                                                    int N, int C) {
     constexpr int KV = Vec16<T>::N;
     const int lane = threadIdx.x & 63;
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -144,14 +144,17 @@ __global__ __launch_bounds__(256) void layernorm_backward_dx_kernel(T* dres, con
     s1 = wave_sum(s1) / C;
     s2 = wave_sum(s2) / C;
     T* dx = dres + (int64_t)row * C;
+    const T* dxi = dres_in ? dres_in + (int64_t)row * C : nullptr;
 #pragma unroll
     for (int ch = 0; ch < MAXCH; ++ch) {
         const int c = (ch * 64 + lane) * KV;
         if (c < C) {
             float prev[KV], o[KV];
-            if (accumulate) unpack16<T>(ld16(dx + c), prev);
 #pragma unroll
-            for (int e = 0; e < KV; ++e) o[e] = rstd * (g[ch][e] - s1 - xh[ch][e] * s2) + (accumulate ? prev[e] : 0.f);
+            for (int e = 0; e < KV; ++e) prev[e] = 0.f;
+            if (dxi) unpack16<T>(ld16(dxi + c), prev);
+#pragma unroll
+            for (int e = 0; e < KV; ++e) o[e] = rstd * (g[ch][e] - s1 - xh[ch][e] * s2) + prev[e];
             st16(dx + c, pack16<T>(o));
         }
     }
@@ -260,19 +263,18 @@ static hipError_t colsum(float* out0, float* out1, const T* dy, const T* x, cons
 }
 
 template <class T>
-hipError_t layernorm_backward(T* dres, float* dw, float* db, const T* dout, const T* inp, const float* stats,
-                              const float* w, int N, int C, float* partial, size_t partial_floats, hipStream_t s,
-                              bool accumulate) {
+hipError_t layernorm_backward(T* dres, const T* dres_in, float* dw, float* db, const T* dout, const T* inp,
+                              const float* stats, const float* w, int N, int C, float* partial, size_t partial_floats,
+                              hipStream_t s) {
     constexpr int KV = Vec16<T>::N;
     const int ch = cdiv(C, 64 * KV);
     const dim3 grid(cdiv(N, 4)), block(256);
-    const int acc = accumulate ? 1 : 0;
     {
-        ProfScope prof(s, "layernorm_bwd_dx", 0, (double)N * C * sizeof(T) * (accumulate ? 4 : 3) + 8.0 * N);
-        if (ch <= 1) hipLaunchKernelGGL((layernorm_backward_dx_kernel<T, 1>), grid, block, 0, s, dres, dout, inp, stats, w, N, C, acc);
-        else if (ch <= 2) hipLaunchKernelGGL((layernorm_backward_dx_kernel<T, 2>), grid, block, 0, s, dres, dout, inp, stats, w, N, C, acc);
-        else if (ch <= 4) hipLaunchKernelGGL((layernorm_backward_dx_kernel<T, 4>), grid, block, 0, s, dres, dout, inp, stats, w, N, C, acc);
-        else if (ch <= 8) hipLaunchKernelGGL((layernorm_backward_dx_kernel<T, 8>), grid, block, 0, s, dres, dout, inp, stats, w, N, C, acc);
+        ProfScope prof(s, "layernorm_bwd_dx", 0, (double)N * C * sizeof(T) * (dres_in ? 4 : 3) + 8.0 * N);
+        if (ch <= 1) hipLaunchKernelGGL((layernorm_backward_dx_kernel<T, 1>), grid, block, 0, s, dres, dres_in, dout, inp, stats, w, N, C);
+        else if (ch <= 2) hipLaunchKernelGGL((layernorm_backward_dx_kernel<T, 2>), grid, block, 0, s, dres, dres_in, dout, inp, stats, w, N, C);
+        else if (ch <= 4) hipLaunchKernelGGL((layernorm_backward_dx_kernel<T, 4>), grid, block, 0, s, dres, dres_in, dout, inp, stats, w, N, C);
+        else if (ch <= 8) hipLaunchKernelGGL((layernorm_backward_dx_kernel<T, 8>), grid, block, 0, s, dres, dres_in, dout, inp, stats, w, N, C);
         else return hipErrorInvalidValue;
     }
     hipError_t e = hipGetLastError();
@@ -549,8 +551,8 @@ hipError_t splitk_reduce(float* out, const float* ws, int splits, int64_t n, hip
                                            hipStream_t);                                                          \
     template hipError_t layernorm_forward<T>(T*, float*, const T*, const float*, const float*, int, int,         \
                                              hipStream_t);                                                        \
-    template hipError_t layernorm_backward<T>(T*, float*, float*, const T*, const T*, const float*, const float*, \
-                                              int, int, float*, size_t, hipStream_t, bool);                      \
+    template hipError_t layernorm_backward<T>(T*, const T*, float*, float*, const T*, const T*, const float*,   \
+                                              const float*, int, int, float*, size_t, hipStream_t);              \
     template hipError_t bias_grad<T>(float*, const T*, int, int, int64_t, float*, size_t, hipStream_t);          \
     template hipError_t crossentropy_fused<T>(T*, float*, const int32_t*, int, int, int64_t, float, hipStream_t); \
     template hipError_t encoder_backward<T>(float*, float*, const T*, const int32_t*, int, int, int, int,        \
