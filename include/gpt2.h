@@ -105,7 +105,12 @@ int gpt2_forward(gpt2_arena* arena, const int32_t* d_inputs, const int32_t* d_ta
 
 /* Backward pass of the last forward (which must have had targets, else
  * GPT2_E_STATE).  Overwrites every fp32 parameter gradient (GPT2_T_GRADS): one
- * micro-batch per step, no accumulation. */
+ * micro-batch per step, no accumulation.  The parameter-gradient products run on
+ * a second, library-owned stream (created on the first call, destroyed by
+ * gpt2_free_arena) that forks from and joins back into `stream` with events, so
+ * all of the pass is ordered before whatever the caller enqueues on `stream`
+ * next.  Results are bitwise reproducible run to run.  Two passes on the same
+ * arena must not be enqueued on different streams concurrently. */
 int gpt2_backward(gpt2_arena* arena, void* stream);
 
 /* AdamW over every parameter ("1000 行 C 代码...": the loop ends with an Adam
@@ -162,7 +167,10 @@ int64_t gpt2_num_parameters(const gpt2_config* cfg);
  * work (flops of its contractions counting only unmasked attention pairs; bytes
  * it must read and write at least once).  gpt2_profile(0) stops recording.
  * At most 32768 launches are recorded per enable.  Timing adds a small per-launch
- * overhead; the benchmark times its headline figure with profiling off. */
+ * overhead, and while recording, gpt2_backward enqueues all of its work on the
+ * caller's stream (normally it overlaps parameter-gradient work on an internal
+ * second stream) so that each launch's duration is its own; the benchmark times
+ * its headline figure with profiling off. */
 typedef struct gpt2_kernel_stat {
     char name[64];
     int64_t launches;

@@ -278,107 +278,148 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs a, int k_pe
             }
 }
 
-// ---------------------------------------------------------------------------- bf16 kernel (buffer loads)
-// Operands are read with buffer loads whose resource covers exactly the valid
-// rows of each matrix: reads past the end return zero in hardware, so the K loop
-// carries no bounds checks.  Every per-thread offset is computed once; the k step
-// enters as the scalar offset, LDS addresses as immediates.  An n/m-contiguous
-// operand is loaded as 4 (k) x 8 (mn) blocks, transposed with byte permutes and
-// stored k-contiguous.  Requirements (checked by the host): leading dimensions are
-// multiples of 8 elements, and a k-contiguous operand's columns between K and the
-// next multiple of 64 read as zero (true when K % 64 == 0, or when the row padding
-// holds zeros).
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
+// ---------------------------------------------------------------------------- bf16 kernel (LDS DMA)
+// Operands go from global memory straight into LDS with gfx950's buffer loads to
+// LDS (16 bytes per lane, no registers in between).  The buffer resource covers
+// exactly the valid rows of each matrix, so reads past the end return zero and
+// the K loop has no bounds checks.  One such load writes 64 consecutive 16-byte
+// LDS slots (lane order); a tile's layout is chosen by which global chunk each
+// lane fetches.  Two LDS stages: the loads for tile k+1 are in flight while tile
+// k is multiplied; one barrier per tile.
+//   k-contiguous operand: LDS row = one mn index, 64 k = 128 bytes; the 16-byte
+//     chunk c of row r sits at slot c ^ swz(r).  Fragment reads: ds_read_b128.
+//   mn-contiguous operand: LDS row = one k, ROWS mn values; chunk c of row k sits
+//     at slot c ^ hsw(k).  Fragment reads: two ds_read_b64_tr_b16, which hand lane
+//     j of each 16-lane group element e of the 8-byte word addressed by lane
+//     4e + j/4 of that group (element j % 4 of it), i.e. a 4 x 16 transpose: with
+//     lane i addressing (k0 + i/4, n0 + 4 (i%4)), lane j receives k0..k0+3 at n0 + j.
+// Requirements (checked by the host): leading dimensions are multiples of 8
+// elements, and a k-contiguous operand's columns between K and the next multiple
+// of 64 read as zero (true when K % 64 == 0, or when the row padding holds zeros).
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16* lds_v4_t;
 
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ u32x4 bload(rsrc_t r, uint32_t voff, uint32_t soff) {
-    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
-}
 
-constexpr int GBK = 64;  // k per tile; an LDS tile row is 64 bf16 = 128 bytes = 8 chunks of 16 bytes
+constexpr int GBK = 64;  // k per tile
 
-// LDS tile layout: row-major, 128-byte rows, no padding; the 16-byte chunk c of
-// row r is stored at position c ^ swz(r).  With swz(r) = (r ^ (r >> 3)) & 7, any 8
-// consecutive rows read at one logical chunk (the MFMA fragment reads), the 8
-// chunks of one row (k-contiguous stores), and rows 8 apart at one chunk (the
-// transposed stores) all fall on distinct banks.
+// k-contiguous tiles: any 8 consecutive rows read at one logical chunk (fragment
+// reads) and the 8 chunks of one row fall on distinct 16-byte bank groups.
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 __device__ __forceinline__ int lds_pos(int r, int chunk) { return r * GBK + ((chunk ^ swz(r)) << 3); }
+// mn-contiguous tiles: the 4 consecutive k rows one 16-lane group reads (32 bytes
+// each) land on 4 distinct 32-byte bank groups.
+__device__ __forceinline__ int hsw(int k) { return (k & 3) << 1; }
 
-template <bool KCONTIG, int ROWS, int NT>
-struct BufLoader {
-    // k-contiguous: ROWS x 8 chunks of 16 bytes.  mn-contiguous: (GBK/4) x (ROWS/8)
-    // blocks of 4 k-rows x 8 mn-columns.
-    static constexpr int NCH = ROWS * 8 / NT;
-    static constexpr int NHB = (GBK / 4) * (ROWS / 8) / NT;
-    static_assert(KCONTIG ? (ROWS * 8) % NT == 0 : ((GBK / 4) * (ROWS / 8)) % NT == 0, "tile/threads mismatch");
-    static constexpr int NLD = KCONTIG ? NCH : 4 * NHB;
-    static constexpr int NST = KCONTIG ? NCH : 8 * NHB;
-    uint32_t voff[NLD];
-    int lofs[NST];
-    u32x4 r[NLD];
-    uint32_t kstep;  // bytes of scalar offset per k element
+// s_waitcnt vmcnt(N) lgkmcnt(0): all but this wave's N most recent loads into LDS
+// have landed, and its own LDS reads are done.
+template <int N> __device__ __forceinline__ void wait_loads() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
 
-    __device__ __forceinline__ void init(int tid, int row0, int64_t ld) {
-        if constexpr (KCONTIG) {
+// Per-lane global offsets of one operand tile (ROWS mn x 64 k) in 1 KB wave loads.
+template <bool KC, int ROWS, int NW>
+struct DmaTile {
+    static constexpr int NI = ROWS * GBK * 2 / 1024;  // wave loads per tile
+    static_assert(NI % NW == 0, "wave loads per tile must divide among the waves");
+    static constexpr int PW = NI / NW;
+    static constexpr int CPR = ROWS / 8;           // mn-contiguous: chunks per k row
+    static constexpr int RPI = KC ? 8 : 64 / CPR;  // rows per wave load
+    uint32_t voff[PW];
+    uint32_t kstep;  // bytes per k element
+    __device__ __forceinline__ void init(int wave, int lane, int row0, int64_t ld) {
 #pragma unroll
-            for (int i = 0; i < NCH; ++i) {
-                const int c = tid + i * NT, row = c >> 3, kc = c & 7;
-                voff[i] = (uint32_t)(((int64_t)(row0 + row) * ld + kc * 8) * 2);
-                lofs[i] = lds_pos(row, kc);
-            }
-            kstep = 2;
-        } else {
-#pragma unroll
-            for (int i = 0; i < NHB; ++i) {
-                const int hb = tid + i * NT, kq = hb / (ROWS / 8), mb = hb % (ROWS / 8);
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr)
-                    voff[4 * i + rr] = (uint32_t)(((int64_t)(kq * 4 + rr) * ld + row0 + mb * 8) * 2);
-#pragma unroll
-                for (int j = 0; j < 8; ++j) lofs[8 * i + j] = lds_pos(mb * 8 + j, kq >> 1) + (kq & 1) * 4;
-            }
-            kstep = (uint32_t)(ld * 2);
-        }
-    }
-    __device__ __forceinline__ void load(rsrc_t rs, int k0) {
-        const uint32_t soff = (uint32_t)k0 * kstep;
-#pragma unroll
-        for (int i = 0; i < NLD; ++i) r[i] = bload(rs, voff[i], soff);
-    }
-    __device__ __forceinline__ void store(bf16* lds) {
-        if constexpr (KCONTIG) {
-#pragma unroll
-            for (int i = 0; i < NCH; ++i) st16(lds + lofs[i], r[i]);
-        } else {
-#pragma unroll
-            for (int i = 0; i < NHB; ++i) {
-                const u32x4* q = &r[4 * i];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const int w = j >> 1;
-                    const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-                    uint2 v;
-                    v.x = __builtin_amdgcn_perm(q[1][w], q[0][w], sel);
-                    v.y = __builtin_amdgcn_perm(q[3][w], q[2][w], sel);
-                    *(uint2*)(lds + lofs[8 * i + j]) = v;
-                }
+        for (int j = 0; j < PW; ++j) {
+            const int q = wave + NW * j;
+            if constexpr (KC) {
+                const int r = q * 8 + (lane >> 3);
+                const int c = (lane & 7) ^ swz(r);
+                voff[j] = (uint32_t)(((int64_t)(row0 + r) * ld + c * 8) * 2);
+            } else {
+                const int kr = q * RPI + lane / CPR;
+                const int c = (lane % CPR) ^ hsw(kr);
+                voff[j] = (uint32_t)(((int64_t)kr * ld + row0 + c * 8) * 2);
             }
         }
+        kstep = KC ? 2u : (uint32_t)(ld * 2);
     }
 };
 
-template <bool AK, bool BKC, int EPI, int BM, int BN, int WM, int WN>
+// One wave load of 64 x 16 bytes into LDS at the wave-uniform address `lds_addr`
+// (lane i writes lds_addr + 16 i).  Written as inline assembly on purpose: the
+// compiler, seeing an LDS write it cannot place, would otherwise wait for every
+// load in flight before each ds_read_b64_tr_b16, serialising the pipeline.  The
+// kernel orders these loads itself (wait_loads + barrier before a stage is read,
+// lgkmcnt(0) + barrier before a stage is overwritten).
+typedef uint32_t dsc_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ dsc_t make_dsc(const void* base, uint32_t bytes) {
+    const uint64_t b = (uint64_t)base;
+    dsc_t d;
+    d[0] = (uint32_t)b;
+    d[1] = (uint32_t)(b >> 32) & 0xffffu;  // stride 0
+    d[2] = bytes;
+    d[3] = 0x00020000u;
+    return d;
+}
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const dsc_t& d, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(lds_addr), "v"(voff), "s"(d), "s"(soff)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+template <int PW, int NW>
+__device__ __forceinline__ void dma_issue(const dsc_t& d, bf16* tile, const uint32_t* voff, int wave, uint32_t soff) {
+#pragma unroll
+    for (int j = 0; j < PW; ++j) {
+        const uint32_t la = (uint32_t)(uintptr_t)(lds_ptr_t)(tile + (wave + NW * j) * 512);
+        dma16(d, __builtin_amdgcn_readfirstlane(la), voff[j], soff);
+    }
+}
+
+// Byte offsets in a tile of the MFMA fragment at mn offset f0, k slice ks
+// (lane l: mn f0 + l % 32, k 16 ks + 8 (l / 32) .. +7).
+template <bool KC, int ROWS>
+__device__ __forceinline__ void frag_offsets(int lane, int f0, int ks, int* o) {
+    if constexpr (KC) {
+        o[0] = lds_pos(f0 + (lane & 31), 2 * ks + (lane >> 5)) * 2;
+        o[1] = 0;
+    } else {
+        const int g = lane >> 4, i = lane & 15;
+        const int col = f0 + 16 * (g & 1) + 4 * (i & 3);
+        const int k = 16 * ks + 8 * (g >> 1) + (i >> 2);
+        o[0] = k * ROWS * 2 + (((col >> 3) ^ hsw(k)) << 4) + ((col >> 2) & 1) * 8;
+        o[1] = o[0] + 4 * ROWS * 2;  // k + 4 (hsw depends on k % 4 only)
+    }
+}
+template <bool KC>
+__device__ __forceinline__ u32x4 frag_read(const bf16* tile, const int* o) {
+    if constexpr (KC) {
+        return *(const u32x4*)((const char*)tile + o[0]);
+    } else {
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4_t)((const char*)tile + o[0]));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4_t)((const char*)tile + o[1]));
+        u32x4 r;
+        r[0] = (uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
+        r[1] = (uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
+        r[2] = (uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
+        r[3] = (uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
+        return r;
+    }
+}
+
+template <bool AK, bool BKC, int EPI, int BM, int BN, int WM, int WN, int ST = 2>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a, int k_per_split, int64_t split_stride,
                                                                  uint32_t a_bytes, uint32_t b_bytes) {
-    constexpr int NT = 64 * WM * WN;
+    constexpr int NW = WM * WN, NT = 64 * NW;
     using MT = MfmaTraits<bf16>;
     constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
     constexpr int SA = BM * GBK, STAGE = (BM + BN) * GBK;
-    constexpr int EPITCH = BN + 8;  // fp32 epilogue row pitch
-    constexpr int LDS_ELEMS = (2 * STAGE > BM * EPITCH * 2) ? 2 * STAGE : BM * EPITCH * 2;
+    constexpr int LDS_ELEMS = ST * STAGE;
     __shared__ __attribute__((aligned(16))) bf16 lds[LDS_ELEMS];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -387,12 +428,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a, int
     const int kbeg = blockIdx.z * k_per_split;
     const int kend = min(a.K, kbeg + k_per_split);
     const int nk = kend > kbeg ? (kend - kbeg + GBK - 1) / GBK : 0;
-    const rsrc_t ra = make_rsrc(a.A, a_bytes), rb = make_rsrc(a.B, b_bytes);
-
-    BufLoader<AK, BM, NT> la;
-    BufLoader<BKC, BN, NT> lb;
-    la.init(tid, m0, a.lda);
-    lb.init(tid, n0, a.ldb);
+    const dsc_t ra = make_dsc(a.A, a_bytes), rb = make_dsc(a.B, b_bytes);
+    using TA = DmaTile<AK, BM, NW>;
+    using TB = DmaTile<BKC, BN, NW>;
+    TA ta;
+    TB tb;
+    ta.init(wave, lane, m0, a.lda);
+    tb.init(wave, lane, n0, a.ldb);
 
     MT::acc_t acc[TM][TN];
 #pragma unroll
@@ -402,23 +444,22 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a, int
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-    // fragment offsets: row (block base + lane % 32), logical chunk 2 ks + lane / 32
-    int fa[TM][GBK / 16], fb[TN][GBK / 16];
+    int fa[TM][GBK / 16][2], fb[TN][GBK / 16][2];
 #pragma unroll
     for (int ks = 0; ks < GBK / 16; ++ks) {
 #pragma unroll
-        for (int i = 0; i < TM; ++i) fa[i][ks] = lds_pos((wm * TM + i) * 32 + (lane & 31), 2 * ks + (lane >> 5));
+        for (int i = 0; i < TM; ++i) frag_offsets<AK, BM>(lane, (wm * TM + i) * 32, ks, fa[i][ks]);
 #pragma unroll
-        for (int j = 0; j < TN; ++j) fb[j][ks] = SA + lds_pos((wn * TN + j) * 32 + (lane & 31), 2 * ks + (lane >> 5));
+        for (int j = 0; j < TN; ++j) frag_offsets<BKC, BN>(lane, (wn * TN + j) * 32, ks, fb[j][ks]);
     }
     auto compute = [&](const bf16* st) {
 #pragma unroll
         for (int ks = 0; ks < GBK / 16; ++ks) {
             u32x4 xa[TM], xb[TN];
 #pragma unroll
-            for (int i = 0; i < TM; ++i) xa[i] = ld16(st + fa[i][ks]);
+            for (int i = 0; i < TM; ++i) xa[i] = frag_read<AK>(st, fa[i][ks]);
 #pragma unroll
-            for (int j = 0; j < TN; ++j) xb[j] = ld16(st + fb[j][ks]);
+            for (int j = 0; j < TN; ++j) xb[j] = frag_read<BKC>(st + SA, fb[j][ks]);
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -426,43 +467,76 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a, int
         }
     };
 
-    if (nk > 0) {
-        la.load(ra, kbeg);
-        lb.load(rb, kbeg);
-        la.store(lds);
-        lb.store(lds + SA);
+    // ST-stage ring: tiles kt+1 .. kt+ST-1 are in flight while tile kt is multiplied
+    constexpr int LPT = TA::PW + TB::PW;  // wave loads per tile
+#pragma unroll
+    for (int s0 = 0; s0 < ST - 1; ++s0)
+        if (s0 < nk) {
+            const uint32_t k1 = (uint32_t)(kbeg + s0 * GBK);
+            dma_issue<TA::PW, NW>(ra, lds + s0 * STAGE, ta.voff, wave, k1 * ta.kstep);
+            dma_issue<TB::PW, NW>(rb, lds + s0 * STAGE + SA, tb.voff, wave, k1 * tb.kstep);
+        }
+    int cur = 0;  // stage of tile kt
+    for (int kt = 0; kt < nk; ++kt) {
+        // tile kt has landed (every wave waits for its own loads, then the barrier);
+        // every wave is also done with tile kt-1, whose stage the next loads reuse
+        if (kt + ST - 2 < nk) wait_loads<LPT * (ST - 2)>();
+        else wait_loads<0>();
+        __builtin_amdgcn_s_barrier();
+        if (kt + ST - 1 < nk) {
+            const int st = cur == 0 ? ST - 1 : cur - 1;
+            bf16* nxt = lds + st * STAGE;
+            const uint32_t k1 = (uint32_t)(kbeg + (kt + ST - 1) * GBK);
+            dma_issue<TA::PW, NW>(ra, nxt, ta.voff, wave, k1 * ta.kstep);
+            dma_issue<TB::PW, NW>(rb, nxt + SA, tb.voff, wave, k1 * tb.kstep);
+        }
+        compute(lds + cur * STAGE);
+        cur = cur + 1 == ST ? 0 : cur + 1;
     }
     __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = (kt & 1) * STAGE;
-        const bool more = kt + 1 < nk;
-        if (more) {
-            la.load(ra, kbeg + (kt + 1) * GBK);
-            lb.load(rb, kbeg + (kt + 1) * GBK);
-        }
-        compute(lds + cur);
-        if (more) {
-            la.store(lds + (STAGE - cur));
-            lb.store(lds + (STAGE - cur) + SA);
-        }
-        __syncthreads();
-    }
 
     // Epilogue through LDS: the accumulators are written as fp32 rows [row][BN + 8]
     // (the pad puts the two half-waves of a 32x32 tile on different banks), then
     // each thread takes 8 consecutive columns of a row, applies the fused epilogue
-    // and writes 16-byte vectors.  Tiles taller than the LDS allows go in passes.
-    constexpr int EP = EPITCH;
+    // and writes 16-byte vectors.  A thread keeps the same 8 columns for the whole
+    // tile, so its bias values are loaded once; the residual / GELU-input rows of a
+    // pass are all requested before the first is used.  Tiles taller than the LDS
+    // allows go in passes.
+    constexpr int EP = BN + 8;
     constexpr int LDS_BYTES = LDS_ELEMS * 2;
     constexpr int NPASS = (BM * EP * 4 <= LDS_BYTES) ? 1 : (BM / 2 * EP * 4 <= LDS_BYTES) ? 2 : 4;
     constexpr int EROWS = BM / NPASS;
     static_assert(EROWS * NPASS == BM && EROWS % 32 == 0, "epilogue pass split");
+    constexpr int CPR = BN / 8;  // 8-column chunks per row
+    static_assert(NT % CPR == 0 && (EROWS * CPR) % NT == 0, "epilogue chunk mapping");
+    constexpr int ITER = EROWS * CPR / NT, RSTEP = NT / CPR;
+    constexpr bool NEED_R = EPI == EPI_BIAS_RES || EPI == EPI_GELU_BWD;
+    const int lc = (tid % CPR) * 8, lr0 = tid / CPR;
+    const int col = n0 + lc;
+    const bool colok = col < a.N, full = col + 8 <= a.N;
+    float bv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) bv[e] = 0.f;
+    if constexpr (EPI == EPI_BIAS || EPI == EPI_BIAS_RES || EPI == EPI_BIAS_GELU) {
+        if (a.bias && colok) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) bv[e] = (col + e < a.N) ? a.bias[col + e] : 0.f;
+        }
+    }
     float* ebuf = (float*)lds;
     float* wsC = nullptr;
     if constexpr (EPI == EPI_F32) wsC = (float*)a.C + (int64_t)blockIdx.z * split_stride;
 #pragma unroll
     for (int pass = 0; pass < NPASS; ++pass) {
         const int r0 = pass * EROWS;
+        u32x4 rr[NEED_R ? ITER : 1];
+        if constexpr (NEED_R) {
+#pragma unroll
+            for (int it = 0; it < ITER; ++it) {
+                const int row = m0 + r0 + lr0 + it * RSTEP;
+                rr[it] = (row < a.M && full) ? ld16((const bf16*)a.R + (int64_t)row * a.ldc + col) : u32x4{0, 0, 0, 0};
+            }
+        }
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
             const int trow = (wm * TM + i) * 32;  // tile-local first row of this MFMA block
@@ -476,18 +550,17 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a, int
             }
         }
         __syncthreads();
-        constexpr int CPR = BN / 8;  // 8-column chunks per row
-        for (int c = tid; c < EROWS * CPR; c += NT) {
-            const int lr = c / CPR, lc = (c % CPR) * 8;
-            const int row = m0 + r0 + lr, col = n0 + lc;
-            if (row >= a.M || col >= a.N) continue;
+#pragma unroll
+        for (int it = 0; it < ITER; ++it) {
+            const int lr = lr0 + it * RSTEP;
+            const int row = m0 + r0 + lr;
+            if (row >= a.M || !colok) continue;
             float v[8];
             const float4 v0 = *(const float4*)(ebuf + lr * EP + lc);
             const float4 v1 = *(const float4*)(ebuf + lr * EP + lc + 4);
             v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w;
             v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
             const int64_t o = (int64_t)row * a.ldc + col;
-            const bool full = col + 8 <= a.N;
             if constexpr (EPI == EPI_F32) {
                 if (full) {
                     *(float4*)(wsC + o) = v0;
@@ -496,15 +569,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a, int
                     for (int e = 0; e < 8 && col + e < a.N; ++e) wsC[o + e] = v[e];
                 }
             } else {
-                if constexpr (EPI != EPI_GELU_BWD) {
-                    if (a.bias) {
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) v[e] += (col + e < a.N) ? a.bias[col + e] : 0.f;
-                    }
-                }
+                for (int e = 0; e < 8; ++e) v[e] += bv[e];
                 float rv[8];
-                if constexpr (EPI == EPI_BIAS_RES || EPI == EPI_GELU_BWD) {
-                    if (full) unpack16<bf16>(ld16((const bf16*)a.R + o), rv);
+                if constexpr (NEED_R) {
+                    if (full) unpack16<bf16>(rr[it], rv);
                     else
                         for (int e = 0; e < 8; ++e) rv[e] = (col + e < a.N) ? to_f32(((const bf16*)a.R)[o + e]) : 0.f;
                 }
@@ -547,11 +616,13 @@ static const char* gemm_name(int M, int N, int K, int splits) {
     return names.insert(n).first->c_str();
 }
 
+static bool use_tile256(int M, int N, int splits) {
+    return (int64_t)((M + 255) / 256) * ((N + 255) / 256) * splits >= 768;
+}
+
+
 template <class T, bool AK, bool BKC, int EPI>
 static hipError_t launch(const GemmArgs& a, int splits, int k_per_split, int64_t split_stride, hipStream_t s) {
-    constexpr int BM = 128, BN = 128, WM = 2, WN = 2;
-    constexpr int BK = sizeof(T) == 2 ? 64 : 32;
-    dim3 grid((a.N + BN - 1) / BN, (a.M + BM - 1) / BM, splits);
     const double es = sizeof(T), mn = (double)a.M * a.N;
     const double out_bytes = EPI == EPI_F32 ? 4 * mn : (EPI == EPI_BIAS ? es * mn : 2 * es * mn);
     ProfScope prof(s, gemm_name<T, AK, BKC, EPI>(a.M, a.N, a.K, splits), 2.0 * mn * a.K,
@@ -561,9 +632,22 @@ static hipError_t launch(const GemmArgs& a, int splits, int k_per_split, int64_t
         const int64_t ab = (AK ? (int64_t)a.M : (int64_t)a.K) * a.lda * 2;
         const int64_t bb = (BKC ? (int64_t)a.N : (int64_t)a.K) * a.ldb * 2;
         if (ab >= (int64_t)1 << 32 || bb >= (int64_t)1 << 32) return hipErrorInvalidValue;
-        hipLaunchKernelGGL((gemm_bf16_kernel<AK, BKC, EPI, 128, 128, 2, 2>), grid, dim3(256), 0, s, a, k_per_split,
-                           split_stride, (uint32_t)ab, (uint32_t)bb);
+        // Tile shapes (both 8 waves, measured on the step's shapes): 256 x 256 with
+        // waves of 128 x 64 and two stages when there are at least three such tiles
+        // per CU; otherwise 128 x 256 with waves of 64 x 64 and three stages.  Both
+        // hold one block per CU (128 / 144 KB of LDS).
+        if (splits == 1 && use_tile256(a.M, a.N, 1)) {
+            dim3 grid((a.N + 255) / 256, (a.M + 255) / 256, splits);
+            hipLaunchKernelGGL((gemm_bf16_kernel<AK, BKC, EPI, 256, 256, 2, 4, 2>), grid, dim3(512), 0, s, a,
+                               k_per_split, split_stride, (uint32_t)ab, (uint32_t)bb);
+        } else {
+            dim3 grid((a.N + 255) / 256, (a.M + 127) / 128, splits);
+            hipLaunchKernelGGL((gemm_bf16_kernel<AK, BKC, EPI, 128, 256, 2, 4, 3>), grid, dim3(512), 0, s, a,
+                               k_per_split, split_stride, (uint32_t)ab, (uint32_t)bb);
+        }
     } else {
+        constexpr int BM = 128, BN = 128, BK = 32, WM = 2, WN = 2;
+        dim3 grid((a.N + BN - 1) / BN, (a.M + BM - 1) / BM, splits);
         hipLaunchKernelGGL((gemm_kernel<T, AK, BKC, EPI, BM, BN, BK, WM, WN>), grid, dim3(64 * WM * WN), 0, s, a,
                            k_per_split, split_stride);
     }
@@ -591,13 +675,15 @@ hipError_t gemm(const GemmArgs& a, bool ak, bool bk, int epi, float* ws, size_t 
     }
     if (epi == EPI_F32) {
         // Output fp32 [M, N] with row stride ldc.  Few output tiles and a long K:
-        // split K over blockIdx.z into fp32 partials in `ws`, then reduce in a fixed order.
-        // Up to 512 blocks are resident at once (two per CU): use the most splits that
-        // keep the launch within that, each split at least 8 k-tiles long.
-        const int tiles = ((a.M + 127) / 128) * ((a.N + 127) / 128);
+        // split K over blockIdx.z into fp32 partials in `ws`, then reduce in a fixed
+        // order.  bf16: one 128 x 256 block per CU, so aim at 256 blocks; fp32: 128 x
+        // 128 tiles, two per CU.  Each split keeps at least 8 k-tiles.
+        const int tiles = sizeof(T) == 2 ? ((a.M + 127) / 128) * ((a.N + 255) / 256)
+                                         : ((a.M + 127) / 128) * ((a.N + 127) / 128);
+        const int slots = sizeof(T) == 2 ? 256 : 512;
         int splits = 1;
-        if (ws && a.ldc == a.N && tiles < 256) {
-            splits = 512 / tiles;
+        if (ws && a.ldc == a.N && tiles < slots && !(sizeof(T) == 2 && use_tile256(a.M, a.N, 1))) {
+            splits = slots / tiles;
             splits = std::min(splits, a.K / (8 * BK));
             while (splits > 1 && (size_t)splits * a.M * a.N > ws_floats) --splits;
             splits = std::max(splits, 1);

@@ -290,7 +290,7 @@ struct Model {
         int rc;
         if ((rc = ensure_streams(a))) return rc;
         split_ok = false;
-        hipStream_t M = s, SD = a->side;
+        hipStream_t M = s, SD = profiling() ? s : a->side;
         T* dz = act(a->logits);
         T* dbuf = act(a->dbuf);
         float* part = f32(a->partial);

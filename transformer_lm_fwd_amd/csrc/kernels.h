@@ -9,6 +9,10 @@
 namespace gpt2 {
 
 // Records the launch(es) in its lifetime when the launch profiler is on.
+// True while the launch profiler records (the backward pass then runs on one
+// stream so that overlapping launches do not inflate each other's durations).
+bool profiling();
+
 struct ProfScope {
     ProfScope(hipStream_t s, const char* name, double flops, double bytes);
     ~ProfScope();

@@ -41,6 +41,8 @@ hipEvent_t take_event() {
 
 }  // namespace
 
+bool profiling() { return g_on; }
+
 ProfScope::ProfScope(hipStream_t s, const char* name, double flops, double bytes) : idx(-1), stream(s) {
     if (!g_on) return;
     std::lock_guard<std::mutex> lk(g_mu);
