@@ -20,6 +20,7 @@
 //  * The backward pass is two kernels -- dK/dV over key tiles and dQ over query
 //    tiles -- each writing its outputs once: no atomics, deterministic.
 #include "kernels.h"
+#include "lds_dma.h"
 
 namespace gpt2 {
 namespace {
@@ -96,48 +97,123 @@ __device__ __forceinline__ void store4_bf16(bf16* dst, float a, float b, float c
     *(uint2*)dst = v;
 }
 
+
+// ---- LDS-DMA tiles: 64 rows x 64 bf16 (128-byte rows), row-major [row][d].
+// The 16-byte chunk c of row r sits at slot c ^ fsw(r), fsw(r) = 2 (r % 4) + (r / 8) % 2.
+// Row-wise fragment reads (8 lanes reading one chunk of the rows perm32 picks:
+// {0..3, 8..11} + 4j + 16i) and transposed reads (16 lanes reading 32 bytes of 4
+// consecutive rows) both fall on distinct banks.
+__device__ __forceinline__ int fsw(int r) { return ((r & 3) << 1) | ((r >> 3) & 1); }
+
+// Per-lane offsets of one 64 x 64 tile of a row-major matrix (row stride ld
+// elements, columns col0 .. col0 + 63) loaded with 8 wave loads, 2 per wave.
+struct TileDma {
+    static constexpr int PW = 2;
+    uint32_t voff[PW];
+    int w;
+    __device__ __forceinline__ TileDma(int wave, int lane, int64_t col0, int64_t ld) : w(wave) {
+#pragma unroll
+        for (int j = 0; j < PW; ++j) {
+            const int r = (wave + 4 * j) * 8 + (lane >> 3);
+            const int c = (lane & 7) ^ fsw(r);
+            voff[j] = (uint32_t)(((int64_t)r * ld + col0 + c * 8) * 2);
+        }
+    }
+    // rows row0 .. row0 + 63 enter through the scalar offset soff (bytes)
+    __device__ __forceinline__ void issue(const dsc_t& d, bf16* tile, uint32_t soff) const {
+#pragma unroll
+        for (int j = 0; j < PW; ++j) dma16(d, lds_addr(tile + (w + 4 * j) * 512), voff[j], soff);
+    }
+};
+
+// Row-wise A fragment of a score sub-tile: A-row rho = lane % 32 is tile row
+// 32 st + perm32(rho), k = 16 ks + 8 g .. +7 (d).  fsw of those rows depends on the
+// lane only.
+struct FragK {
+    int o[4];  // byte offsets for st = 0; st = 1 adds 32 rows
+    __device__ __forceinline__ FragK(int r32, int g) {
+        const int r = perm32(r32), f = fsw(r);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) o[ks] = r * 128 + (((2 * ks + g) ^ f) << 4);
+    }
+    __device__ __forceinline__ u32x4 read(const bf16* tile, int st, int ks) const {
+        return *(const u32x4*)((const char*)tile + o[ks] + st * 32 * 128);
+    }
+};
+
+// Transposed fragment: operand row = column n = 32 dt + lane % 32 of the tile, its
+// 8 k values = tile rows 16 s + 8 (lane / 32) .. +7.  fsw of the rows a lane
+// addresses depends on the lane only, so per-lane bases cover every (dt, s).
+struct FragT {
+    int o[2];  // byte offset of the first read for dt = 0, 1 at s = 0
+    __device__ __forceinline__ FragT(int lane) {
+        const int gq = lane >> 4, i = lane & 15;
+        const int k = 8 * (gq >> 1) + (i >> 2), f = fsw(k);
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) {
+            const int col = 32 * dt + 16 * (gq & 1) + 4 * (i & 3);
+            o[dt] = k * 128 + (((col >> 3) ^ f) << 4) + ((col >> 2) & 1) * 8;
+        }
+    }
+    __device__ __forceinline__ u32x4 read(const bf16* tile, int dt, int s) const {
+        return read_tr2(tile, o[dt] + s * 16 * 128, o[dt] + s * 16 * 128 + 4 * 128);
+    }
+};
+
 }  // namespace
 
 // ============================================================================ forward
-// Block: 128 queries (4 waves x 32), key tiles of 64 staged in LDS.
+// Block: 128 queries (4 waves x 32).  Key tiles of 64 rows go from global memory
+// straight into LDS (K and V, each [key][d], 8 KB) through a ring of FST stages,
+// so up to FST-1 tiles are in flight while one is used.  K fragments are read
+// row-wise (ds_read_b128), V^T fragments with transposed reads.
+constexpr int FST = 3;
+
 __global__ __launch_bounds__(256) void attn_fwd_mfma64(bf16* out, float* lse, const bf16* qkv, int T, int C, int NH) {
-    __shared__ __attribute__((aligned(16))) bf16 sbuf[2][2 * 64 * 64];  // [stage][K | V^T]
+    __shared__ __attribute__((aligned(1024))) bf16 sbuf[FST][2][64 * 64];  // [stage][K | V]
     const int nqt = (T + 127) / 128;
     const int qt = nqt - 1 - (int)blockIdx.x;  // longest rows first
     const int bh = blockIdx.y, b = bh / NH, h = bh % NH;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r32 = lane & 31, g = lane >> 5;
     const int64_t C3 = 3 * (int64_t)C;
     const bf16* base = qkv + (int64_t)b * T * C3;
-    const bf16* Qg = base + h * HS;
-    const bf16* Kg = base + C + h * HS;
-    const bf16* Vg = base + 2 * C + h * HS;
     const int q0 = qt * 128, qw = q0 + 32 * w, myq = qw + r32;
     const float c = 0.125f * LOG2E;  // 1/sqrt(64) in log2 units
 
     u32x4 qf[4];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qf[ks] = row_frag(Qg, C3, myq, 16 * ks + 8 * g, T);
+    for (int ks = 0; ks < 4; ++ks) qf[ks] = row_frag(base + h * HS, C3, myq, 16 * ks + 8 * g, T);
     f32x16 o[2] = {zero16(), zero16()};
-    float m = -INFINITY, l = 0.f;
+    float m = -INFINITY, l = 0.f;  // running maximum (scaled, log2 units) and sum
 
+    // key tiles: rows of this batch's qkv block; rows >= T read as zero
+    const dsc_t dsc = make_dsc(base, (uint32_t)(T * C3 * 2));
+    const TileDma tk(w, lane, C + h * HS, C3), tv(w, lane, 2 * C + h * HS, C3);
     const int kend = min(T, q0 + 128);
-    Tile64 tk, tv;
-    tk.load(Kg, C3, 0, T, tid);
-    tv.load(Vg, C3, 0, T, tid);
-    tk.store_n(sbuf[0], tid);
-    tv.store_t(sbuf[0] + 64 * 64, tid);
-    __syncthreads();
-    for (int k0 = 0, it = 0; k0 < kend; k0 += 64, ++it) {
-        const bf16* sK = sbuf[it & 1];
-        const bf16* sVt = sK + 64 * 64;
-        const bool more = k0 + 64 < kend;
-        if (more) {  // next tile in flight while this one is used
-            tk.load(Kg, C3, k0 + 64, T, tid);
-            tv.load(Vg, C3, k0 + 64, T, tid);
-        }
-        if (qw < T && k0 <= qw + 31) {  // some key of this tile is visible to this wave
+    const int ntiles = (kend + 63) / 64;
+    const FragK fk(r32, g);
+    const FragT fv(lane);
+    auto issue = [&](int t, int st) {
+        const uint32_t soff = (uint32_t)(64 * t * C3 * 2);
+        tk.issue(dsc, sbuf[st][0], soff);
+        tv.issue(dsc, sbuf[st][1], soff);
+    };
+#pragma unroll
+    for (int s0 = 0; s0 < FST - 1; ++s0)
+        if (s0 < ntiles) issue(s0, s0);
+    int cur = 0;
+    for (int it = 0; it < ntiles; ++it) {
+        if (it + FST - 2 < ntiles) wait_loads<TileDma::PW * 2 * (FST - 2)>();
+        else wait_loads<0>();
+        __builtin_amdgcn_s_barrier();
+        if (it + FST - 1 < ntiles) issue(it + FST - 1, cur == 0 ? FST - 1 : cur - 1);
+        const bf16* sK = sbuf[cur][0];
+        const bf16* sV = sbuf[cur][1];
+        cur = cur + 1 == FST ? 0 : cur + 1;
+        const int k0 = 64 * it;
+        if (qw >= T || k0 > qw + 31) continue;  // no key of this tile is visible to this wave
         const bool edge = (k0 + 63 > qw) || (k0 + 64 > T);
-        float x[32];
+        float x[32];  // raw scores; -inf where masked
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
             if (k0 + 32 * st > qw + 31) {  // sub-tile entirely in this wave's future
@@ -145,23 +221,23 @@ __global__ __launch_bounds__(256) void attn_fwd_mfma64(bf16* out, float* lse, co
                 for (int i = 0; i < 16; ++i) x[16 * st + i] = -INFINITY;
                 continue;
             }
-            const int kr = 32 * st + perm32(r32);
-            f32x16 s = zero16();
+            f32x16 sc = zero16();
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) s = mfma32(ld16(sK + pos(kr, 2 * ks + g)), qf[ks], s);
+            for (int ks = 0; ks < 4; ++ks) sc = mfma32(fk.read(sK, st, ks), qf[ks], sc);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float v = s[i] * c;
-                const int key = k0 + 32 * st + 16 * (i >> 3) + 8 * g + (i & 7);
-                if (edge && (key > myq || key >= T)) v = -INFINITY;
-                x[16 * st + i] = v;
-            }
+            for (int i = 0; i < 16; ++i) x[16 * st + i] = sc[i];
+        }
+        if (edge) {  // key k0 + 8 g + idx is visible iff idx <= lim (idx a constant per element)
+            const int lim = min(myq, T - 1) - k0 - 8 * g;
+#pragma unroll
+            for (int i = 0; i < 32; ++i)
+                if (16 * (i >> 3) + (i & 7) > lim) x[i] = -INFINITY;
         }
         float mt = x[0];
 #pragma unroll
         for (int i = 1; i < 32; ++i) mt = fmaxf(mt, x[i]);
         mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-        const float mn = fmaxf(m, mt);
+        const float mn = fmaxf(m, mt * c);
         if (__any(mn > m)) {  // rescale only when some running maximum grew
             const float corr = fast_exp2(m - mn);
             l *= corr;
@@ -178,19 +254,13 @@ __global__ __launch_bounds__(256) void attn_fwd_mfma64(bf16* out, float* lse, co
             float p[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                p[e] = fast_exp2(x[8 * s4 + e] - mn);
+                p[e] = fast_exp2(__builtin_fmaf(x[8 * s4 + e], c, -mn));
                 l += p[e];
             }
             const u32x4 pk = pack16<bf16>(p);
 #pragma unroll
-            for (int dt = 0; dt < 2; ++dt) o[dt] = mfma32(ld16(sVt + pos(32 * dt + r32, 2 * s4 + g)), pk, o[dt]);
+            for (int dt = 0; dt < 2; ++dt) o[dt] = mfma32(fv.read(sV, dt, s4), pk, o[dt]);
         }
-        }
-        if (more) {
-            tk.store_n(sbuf[(it + 1) & 1], tid);
-            tv.store_t(sbuf[(it + 1) & 1] + 64 * 64, tid);
-        }
-        __syncthreads();
     }
     l += __shfl_xor(l, 32, 64);
     if (myq < T) {

@@ -24,6 +24,7 @@
 #include <string>
 
 #include "kernels.h"
+#include "lds_dma.h"
 
 namespace gpt2 {
 
@@ -296,9 +297,6 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs a, int k_pe
 // Requirements (checked by the host): leading dimensions are multiples of 8
 // elements, and a k-contiguous operand's columns between K and the next multiple
 // of 64 read as zero (true when K % 64 == 0, or when the row padding holds zeros).
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4i16* lds_v4_t;
 
 
 constexpr int GBK = 64;  // k per tile
@@ -311,12 +309,6 @@ __device__ __forceinline__ int lds_pos(int r, int chunk) { return r * GBK + ((ch
 // each) land on 4 distinct 32-byte bank groups.
 __device__ __forceinline__ int hsw(int k) { return (k & 3) << 1; }
 
-// s_waitcnt vmcnt(N) lgkmcnt(0): all but this wave's N most recent loads into LDS
-// have landed, and its own LDS reads are done.
-template <int N> __device__ __forceinline__ void wait_loads() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
-}
 
 // Per-lane global offsets of one operand tile (ROWS mn x 64 k) in 1 KB wave loads.
 template <bool KC, int ROWS, int NW>
@@ -346,38 +338,12 @@ struct DmaTile {
     }
 };
 
-// One wave load of 64 x 16 bytes into LDS at the wave-uniform address `lds_addr`
-// (lane i writes lds_addr + 16 i).  Written as inline assembly on purpose: the
-// compiler, seeing an LDS write it cannot place, would otherwise wait for every
-// load in flight before each ds_read_b64_tr_b16, serialising the pipeline.  The
-// kernel orders these loads itself (wait_loads + barrier before a stage is read,
-// lgkmcnt(0) + barrier before a stage is overwritten).
-typedef uint32_t dsc_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ dsc_t make_dsc(const void* base, uint32_t bytes) {
-    const uint64_t b = (uint64_t)base;
-    dsc_t d;
-    d[0] = (uint32_t)b;
-    d[1] = (uint32_t)(b >> 32) & 0xffffu;  // stride 0
-    d[2] = bytes;
-    d[3] = 0x00020000u;
-    return d;
-}
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(const dsc_t& d, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                 :
-                 : "s"(lds_addr), "v"(voff), "s"(d), "s"(soff)
-                 : "memory", "m0");
-}
-#pragma clang diagnostic pop
 
 template <int PW, int NW>
 __device__ __forceinline__ void dma_issue(const dsc_t& d, bf16* tile, const uint32_t* voff, int wave, uint32_t soff) {
 #pragma unroll
     for (int j = 0; j < PW; ++j) {
-        const uint32_t la = (uint32_t)(uintptr_t)(lds_ptr_t)(tile + (wave + NW * j) * 512);
-        dma16(d, __builtin_amdgcn_readfirstlane(la), voff[j], soff);
+        dma16(d, lds_addr(tile + (wave + NW * j) * 512), voff[j], soff);
     }
 }
 
@@ -401,14 +367,7 @@ __device__ __forceinline__ u32x4 frag_read(const bf16* tile, const int* o) {
     if constexpr (KC) {
         return *(const u32x4*)((const char*)tile + o[0]);
     } else {
-        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4_t)((const char*)tile + o[0]));
-        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4_t)((const char*)tile + o[1]));
-        u32x4 r;
-        r[0] = (uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
-        r[1] = (uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
-        r[2] = (uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
-        r[3] = (uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
-        return r;
+        return read_tr2(tile, o[0], o[1]);
     }
 }
 
