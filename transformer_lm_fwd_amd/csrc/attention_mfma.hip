@@ -14,9 +14,10 @@
 //    so that accumulators 8s..8s+7 of lane group g = l/32 are the 8 consecutive
 //    rows 16s + 8g .. +7: exactly the B (or A) fragment of the next MFMA, whose
 //    reduction runs over those rows.  Probabilities never go through LDS.
-//  * LDS tiles are 64 x 64 bf16 with 128-byte rows and the 16-byte-chunk XOR swizzle
-//    chunk ^ ((row ^ row >> 3) & 7); transposed copies ([d][row]) are built from the
-//    same global loads with byte permutes.
+//  * K/V (forward, dQ) or Q/dO (dK/dV) tiles of 64 rows x 64 bf16 go from global
+//    memory straight into LDS (buffer loads to LDS) through a ring of stages, stored
+//    once as [row][d]; fragments that need the transpose ([d][row]) are read with
+//    ds_read_b64_tr_b16.
 //  * The backward pass is two kernels -- dK/dV over key tiles and dQ over query
 //    tiles -- each writing its outputs once: no atomics, deterministic.
 #include "kernels.h"
@@ -43,47 +44,11 @@ __device__ __forceinline__ f32x16 zero16() {
 }
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
-// element offset of the 16-byte chunk `chunk` of row r in a 64-wide swizzled tile
-__device__ __forceinline__ int pos(int r, int chunk) { return r * 64 + ((chunk ^ swz(r)) << 3); }
 // A-row rho (0..31) of a score tile -> tile row 16(j/2) + 8g + 4(j%2) + t, rho = 8j + 4g + t
 __device__ __forceinline__ int perm32(int rho) {
     const int j = rho >> 3, g = (rho >> 2) & 1, t = rho & 3;
     return 16 * (j >> 1) + 8 * g + 4 * (j & 1) + t;
 }
-
-// A 64-row x 64-column bf16 tile of a strided matrix staged through registers:
-// thread t owns rows 4(t/16)..+3 and columns 4(t%16)..+3 (four 8-byte loads, rows
-// >= T read as zero).  store_n writes the tile as [row][col], store_t as [col][row].
-struct Tile64 {
-    uint2 v[4];
-    __device__ __forceinline__ void load(const bf16* g, int64_t ld, int r0, int T, int tid) {
-        const int cb = tid & 15, rq = tid >> 4;
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            const int row = r0 + 4 * rq + rr;
-            v[rr] = row < T ? *(const uint2*)(g + (int64_t)row * ld + 4 * cb) : uint2{0u, 0u};
-        }
-    }
-    __device__ __forceinline__ void store_n(bf16* ln, int tid) const {
-        const int cb = tid & 15, rq = tid >> 4;
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) *(uint2*)(ln + pos(4 * rq + rr, cb >> 1) + (cb & 1) * 4) = v[rr];
-    }
-    __device__ __forceinline__ void store_t(bf16* lt, int tid) const {
-        const int cb = tid & 15, rq = tid >> 4;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-            const uint32_t w0 = (j >> 1) ? v[0].y : v[0].x, w1 = (j >> 1) ? v[1].y : v[1].x;
-            const uint32_t w2 = (j >> 1) ? v[2].y : v[2].x, w3 = (j >> 1) ? v[3].y : v[3].x;
-            uint2 o;
-            o.x = __builtin_amdgcn_perm(w1, w0, sel);
-            o.y = __builtin_amdgcn_perm(w3, w2, sel);
-            *(uint2*)(lt + pos(4 * cb + j, rq >> 1) + (rq & 1) * 4) = o;
-        }
-    }
-};
 
 // 16-byte fragment of a strided row (zero past T)
 __device__ __forceinline__ u32x4 row_frag(const bf16* g, int64_t ld, int row, int col, int T) {
@@ -278,9 +243,11 @@ __global__ __launch_bounds__(256) void attn_fwd_mfma64(bf16* out, float* lse, co
 }
 
 // ============================================================================ backward
-// D[b, h, q] = sum_d dO[q, d] O[q, d]  (= sum_k P[q, k] dP[q, k])
-__global__ __launch_bounds__(256) void attn_bwd_dsum64(float* dsum, const bf16* dout, const bf16* out, int BT, int T,
-                                                       int C, int NH) {
+// LD[b, h, q] = {lse[q] * log2(e), D[q]},  D[q] = sum_d dO[q, d] O[q, d]
+// (= sum_k P[q, k] dP[q, k]): the per-query values both backward kernels need,
+// side by side so a 64-query tile of them is one 512-byte load.
+__global__ __launch_bounds__(256) void attn_bwd_dsum64(float2* LD, const bf16* dout, const bf16* out,
+                                                       const float* lse, int BT, int T, int C, int NH) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (row, head)
     if (i >= (int64_t)BT * NH) return;
     const int row = (int)(i / NH), h = (int)(i % NH);
@@ -296,114 +263,110 @@ __global__ __launch_bounds__(256) void attn_bwd_dsum64(float* dsum, const bf16* 
         for (int e = 0; e < 8; ++e) acc += x[e] * y[e];
     }
     const int b = row / T, t = row % T;
-    dsum[((int64_t)b * NH + h) * T + t] = acc;
+    const int64_t j = ((int64_t)b * NH + h) * T + t;
+    LD[j] = make_float2(lse[j] * LOG2E, acc);
 }
 
+constexpr int BST = 3;  // LDS stages of the backward kernels
+
 // dK, dV for 128 keys (4 waves x 32), looping over query tiles of 64 at or after
-// them.  P and dS are [query x key] tiles with the key as accumulator column;
-// dV += P^T dO and dK += dS^T Q then take P^T / dS^T as A operands and dO^T / Q^T
-// (transposed LDS copies) as B operands.
+// them.  Q and dO tiles ([q][d]) and their {L, D} values arrive by LDS DMA in a
+// BST-stage ring.  P and dS are [query x key] tiles with the key as accumulator
+// column (A = Q / dO rows, B = this lane's K / V row); dV += P^T dO and
+// dK += dS^T Q take P^T / dS^T as A operands and dO^T / Q^T (transposed reads of
+// the same tiles) as B operands.
 __global__ __launch_bounds__(256) void attn_bwd_dkdv_mfma64(bf16* dqkv, const bf16* qkv, const bf16* dout,
-                                                            const float* lse, const float* dsum, int T, int C,
-                                                            int NH) {
-    __shared__ __attribute__((aligned(16))) bf16 sbuf[2][4 * 64 * 64];  // [stage][Q | dO | Q^T | dO^T]
-    __shared__ __attribute__((aligned(16))) float sLD[2][2][64];        // [stage][lse*log2e | D]
+                                                            const float2* LD, int T, int C, int NH) {
+    __shared__ __attribute__((aligned(1024))) bf16 sbuf[BST][2][64 * 64];  // [stage][Q | dO]
+    __shared__ __attribute__((aligned(1024))) float sLD[BST][256];         // [stage][{L, D} x 64, copy]
     const int kt = blockIdx.x;  // the first key tiles see the most queries: scheduled first
     const int bh = blockIdx.y, b = bh / NH, h = bh % NH;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r32 = lane & 31, g = lane >> 5;
     const int64_t C3 = 3 * (int64_t)C;
     const bf16* base = qkv + (int64_t)b * T * C3;
-    const bf16* Qg = base + h * HS;
-    const bf16* Kg = base + C + h * HS;
-    const bf16* Vg = base + 2 * C + h * HS;
-    const bf16* Gg = dout + (int64_t)b * T * C + h * HS;
     const int k0 = kt * 128, kw = k0 + 32 * w, mykey = kw + r32;
     const float c = 0.125f * LOG2E;
 
     u32x4 kf[4], vf[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-        kf[ks] = row_frag(Kg, C3, mykey, 16 * ks + 8 * g, T);
-        vf[ks] = row_frag(Vg, C3, mykey, 16 * ks + 8 * g, T);
+        kf[ks] = row_frag(base + C + h * HS, C3, mykey, 16 * ks + 8 * g, T);
+        vf[ks] = row_frag(base + 2 * C + h * HS, C3, mykey, 16 * ks + 8 * g, T);
     }
     f32x16 dk[2] = {zero16(), zero16()}, dv[2] = {zero16(), zero16()};
 
-    Tile64 tq, tg;
-    float ld_l = 0.f, ld_d = 0.f;
-    auto load_q = [&](int q0) {
-        tq.load(Qg, C3, q0, T, tid);
-        tg.load(Gg, C, q0, T, tid);
-        if (tid < 64) {
-            const int q = q0 + tid;
-            ld_l = q < T ? lse[(int64_t)bh * T + q] * LOG2E : 0.f;
-            ld_d = q < T ? dsum[(int64_t)bh * T + q] : 0.f;
-        }
+    const dsc_t dq_ = make_dsc(base, (uint32_t)(T * C3 * 2));
+    const dsc_t dg = make_dsc(dout + (int64_t)b * T * C, (uint32_t)((int64_t)T * C * 2));
+    const dsc_t dl = make_dsc(LD + (int64_t)bh * T, (uint32_t)(T * 8));
+    const TileDma tq(w, lane, h * HS, C3), tg(w, lane, h * HS, C);
+    const FragK fk(r32, g);
+    const FragT ft(lane);
+    const int ntiles = k0 < T ? (T - k0 + 63) / 64 : 0;
+    auto issue = [&](int t, int st) {
+        const int q0 = k0 + 64 * t;
+        tq.issue(dq_, sbuf[st][0], (uint32_t)(q0 * C3 * 2));
+        tg.issue(dg, sbuf[st][1], (uint32_t)(q0 * C * 2));
+        if (w == 0) dma16(dl, lds_addr(sLD[st]), (uint32_t)((lane & 31) * 16), (uint32_t)(q0 * 8));
     };
-    auto store_q = [&](int st) {
-        bf16* b4 = sbuf[st];
-        tq.store_n(b4, tid);
-        tg.store_n(b4 + 64 * 64, tid);
-        tq.store_t(b4 + 2 * 64 * 64, tid);
-        tg.store_t(b4 + 3 * 64 * 64, tid);
-        if (tid < 64) {
-            sLD[st][0][tid] = ld_l;
-            sLD[st][1][tid] = ld_d;
+#pragma unroll
+    for (int s0 = 0; s0 < BST - 1; ++s0)
+        if (s0 < ntiles) issue(s0, s0);
+    int cur = 0;
+    for (int it = 0; it < ntiles; ++it) {
+        if (it + BST - 2 < ntiles) {
+            if (w == 0) wait_loads<(2 * TileDma::PW + 1) * (BST - 2)>();
+            else wait_loads<2 * TileDma::PW * (BST - 2)>();
+        } else {
+            wait_loads<0>();
         }
-    };
-    if (k0 < T) {
-        load_q(k0);
-        store_q(0);
-    }
-    __syncthreads();
-    for (int q0 = k0, it = 0; q0 < T; q0 += 64, ++it) {
-        const bf16* sQ = sbuf[it & 1];
-        const bf16* sG = sQ + 64 * 64;
-        const bf16* sQt = sQ + 2 * 64 * 64;
-        const bf16* sGt = sQ + 3 * 64 * 64;
-        const float* sL = sLD[it & 1][0];
-        const float* sD = sLD[it & 1][1];
-        const bool more = q0 + 64 < T;
-        if (more) load_q(q0 + 64);
-        if (kw < T && q0 + 63 >= kw) {  // some query of the tile sees this wave's keys
+        __builtin_amdgcn_s_barrier();
+        if (it + BST - 1 < ntiles) issue(it + BST - 1, cur == 0 ? BST - 1 : cur - 1);
+        const bf16* sQ = sbuf[cur][0];
+        const bf16* sG = sbuf[cur][1];
+        const float* sL = sLD[cur];
+        cur = cur + 1 == BST ? 0 : cur + 1;
+        const int q0 = k0 + 64 * it;
+        if (kw >= T || q0 + 63 < kw) continue;  // no query of the tile sees this wave's keys
         const bool edge = (q0 < kw + 31) || (q0 + 64 > T);
+        // query q0 + 8 g + idx sees this lane's key iff lo <= idx < hi
+        const int lo = mykey - q0 - 8 * g, hi = T - q0 - 8 * g;
 #pragma unroll
         for (int qs = 0; qs < 2; ++qs) {
             if (q0 + 32 * qs + 31 < kw) continue;  // sub-tile entirely before this wave's keys
-            const int qr = 32 * qs + perm32(r32);
-            f32x16 s = zero16(), dp = zero16();
+            f32x16 sc = zero16(), dp = zero16();
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                s = mfma32(ld16(sQ + pos(qr, 2 * ks + g)), kf[ks], s);
-                dp = mfma32(ld16(sG + pos(qr, 2 * ks + g)), vf[ks], dp);
+                sc = mfma32(fk.read(sQ, qs, ks), kf[ks], sc);
+                dp = mfma32(fk.read(sG, qs, ks), vf[ks], dp);
             }
 #pragma unroll
             for (int sl = 0; sl < 2; ++sl) {
-                float p[8], ds[8];
                 const int qlb = 32 * qs + 16 * sl + 8 * g;  // tile-local first query of this lane's 8
-                const float4 l0 = *(const float4*)&sL[qlb], l1 = *(const float4*)&sL[qlb + 4];
-                const float4 d0 = *(const float4*)&sD[qlb], d1 = *(const float4*)&sD[qlb + 4];
-                const float Lq[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
-                const float Dq[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+                float Lq[8], Dq[8];
+#pragma unroll
+                for (int e4 = 0; e4 < 4; ++e4) {
+                    const float4 v = *(const float4*)&sL[2 * qlb + 4 * e4];
+                    Lq[2 * e4] = v.x; Dq[2 * e4] = v.y; Lq[2 * e4 + 1] = v.z; Dq[2 * e4 + 1] = v.w;
+                }
+                float p[8], ds[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const int q = q0 + qlb + e;
-                    float pv = fast_exp2(s[8 * sl + e] * c - Lq[e]);
-                    if (edge && (q >= T || mykey > q)) pv = 0.f;
+                    float pv = fast_exp2(__builtin_fmaf(sc[8 * sl + e], c, -Lq[e]));
+                    if (edge) {
+                        const int idx = 32 * qs + 16 * sl + e;
+                        if (idx < lo || idx >= hi) pv = 0.f;
+                    }
                     p[e] = pv;
                     ds[e] = pv * (dp[8 * sl + e] - Dq[e]);
                 }
                 const u32x4 pp = pack16<bf16>(p), dd = pack16<bf16>(ds);
-                const int ch = 4 * qs + 2 * sl + g;
 #pragma unroll
                 for (int dt = 0; dt < 2; ++dt) {
-                    dv[dt] = mfma32(pp, ld16(sGt + pos(32 * dt + r32, ch)), dv[dt]);
-                    dk[dt] = mfma32(dd, ld16(sQt + pos(32 * dt + r32, ch)), dk[dt]);
+                    dv[dt] = mfma32(pp, ft.read(sG, dt, 2 * qs + sl), dv[dt]);
+                    dk[dt] = mfma32(dd, ft.read(sQ, dt, 2 * qs + sl), dk[dt]);
                 }
             }
         }
-        }
-        if (more) store_q((it + 1) & 1);
-        __syncthreads();
     }
     // dv[dt][i] / dk[dt][i]: column d = 32 dt + r32, row key kw + 8 (i/4) + 4 g + i%4
 #pragma unroll
@@ -421,20 +384,18 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_mfma64(bf16* dqkv, const bf
 }
 
 // dQ for 128 queries (4 waves x 32), looping over key tiles of 64 up to the
-// diagonal: S^T and dP^T as in the forward pass, dS (query x 8 keys per lane) as the
-// A operand of dQ = dS K with K^T from LDS.
+// diagonal (K and V tiles by LDS DMA, as in the forward pass): S^T and dP^T with
+// the query as accumulator column, dS (query x 8 keys per lane) as the A operand
+// of dQ = dS K with K^T fragments read transposed from the K tile.
 __global__ __launch_bounds__(256) void attn_bwd_dq_mfma64(bf16* dqkv, const bf16* qkv, const bf16* dout,
-                                                          const float* lse, const float* dsum, int T, int C, int NH) {
-    __shared__ __attribute__((aligned(16))) bf16 sbuf[2][3 * 64 * 64];  // [stage][K | V | K^T]
+                                                          const float2* LD, int T, int C, int NH) {
+    __shared__ __attribute__((aligned(1024))) bf16 sbuf[BST][2][64 * 64];  // [stage][K | V]
     const int nqt = (T + 127) / 128;
     const int qt = nqt - 1 - (int)blockIdx.x;
     const int bh = blockIdx.y, b = bh / NH, h = bh % NH;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r32 = lane & 31, g = lane >> 5;
     const int64_t C3 = 3 * (int64_t)C;
     const bf16* base = qkv + (int64_t)b * T * C3;
-    const bf16* Qg = base + h * HS;
-    const bf16* Kg = base + C + h * HS;
-    const bf16* Vg = base + 2 * C + h * HS;
     const bf16* Gg = dout + (int64_t)b * T * C + h * HS;
     const int q0 = qt * 128, qw = q0 + 32 * w, myq = qw + r32;
     const float c = 0.125f * LOG2E;
@@ -442,66 +403,62 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_mfma64(bf16* dqkv, const bf16
     u32x4 qf[4], gf[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-        qf[ks] = row_frag(Qg, C3, myq, 16 * ks + 8 * g, T);
+        qf[ks] = row_frag(base + h * HS, C3, myq, 16 * ks + 8 * g, T);
         gf[ks] = row_frag(Gg, C, myq, 16 * ks + 8 * g, T);
     }
-    const float L2 = (myq < T) ? lse[(int64_t)bh * T + myq] * LOG2E : 0.f;
-    const float Dq = (myq < T) ? dsum[(int64_t)bh * T + myq] : 0.f;
+    const float2 ldq = myq < T ? LD[(int64_t)bh * T + myq] : make_float2(0.f, 0.f);
     f32x16 dq[2] = {zero16(), zero16()};
 
+    const dsc_t dsc = make_dsc(base, (uint32_t)(T * C3 * 2));
+    const TileDma tk(w, lane, C + h * HS, C3), tv(w, lane, 2 * C + h * HS, C3);
+    const FragK fk(r32, g);
+    const FragT ft(lane);
     const int kend = min(T, q0 + 128);
-    Tile64 tk, tv;
-    tk.load(Kg, C3, 0, T, tid);
-    tv.load(Vg, C3, 0, T, tid);
-    tk.store_n(sbuf[0], tid);
-    tv.store_n(sbuf[0] + 64 * 64, tid);
-    tk.store_t(sbuf[0] + 2 * 64 * 64, tid);
-    __syncthreads();
-    for (int k0 = 0, it = 0; k0 < kend; k0 += 64, ++it) {
-        const bf16* sK = sbuf[it & 1];
-        const bf16* sV = sK + 64 * 64;
-        const bf16* sKt = sK + 2 * 64 * 64;
-        const bool more = k0 + 64 < kend;
-        if (more) {
-            tk.load(Kg, C3, k0 + 64, T, tid);
-            tv.load(Vg, C3, k0 + 64, T, tid);
-        }
-        if (qw < T && k0 <= qw + 31) {
+    const int ntiles = (kend + 63) / 64;
+    auto issue = [&](int t, int st) {
+        const uint32_t soff = (uint32_t)(64 * t * C3 * 2);
+        tk.issue(dsc, sbuf[st][0], soff);
+        tv.issue(dsc, sbuf[st][1], soff);
+    };
+#pragma unroll
+    for (int s0 = 0; s0 < BST - 1; ++s0)
+        if (s0 < ntiles) issue(s0, s0);
+    int cur = 0;
+    for (int it = 0; it < ntiles; ++it) {
+        if (it + BST - 2 < ntiles) wait_loads<2 * TileDma::PW * (BST - 2)>();
+        else wait_loads<0>();
+        __builtin_amdgcn_s_barrier();
+        if (it + BST - 1 < ntiles) issue(it + BST - 1, cur == 0 ? BST - 1 : cur - 1);
+        const bf16* sK = sbuf[cur][0];
+        const bf16* sV = sbuf[cur][1];
+        cur = cur + 1 == BST ? 0 : cur + 1;
+        const int k0 = 64 * it;
+        if (qw >= T || k0 > qw + 31) continue;
         const bool edge = (k0 + 63 > qw) || (k0 + 64 > T);
+        const int lim = min(myq, T - 1) - k0 - 8 * g;  // key k0 + 8 g + idx visible iff idx <= lim
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
             if (k0 + 32 * st > qw + 31) continue;
-            const int kr = 32 * st + perm32(r32);
-            f32x16 s = zero16(), dp = zero16();
+            f32x16 sc = zero16(), dp = zero16();
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                s = mfma32(ld16(sK + pos(kr, 2 * ks + g)), qf[ks], s);
-                dp = mfma32(ld16(sV + pos(kr, 2 * ks + g)), gf[ks], dp);
+                sc = mfma32(fk.read(sK, st, ks), qf[ks], sc);
+                dp = mfma32(fk.read(sV, st, ks), gf[ks], dp);
             }
 #pragma unroll
             for (int sl = 0; sl < 2; ++sl) {
                 float ds[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const int key = k0 + 32 * st + 16 * sl + 8 * g + e;
-                    float pv = fast_exp2(s[8 * sl + e] * c - L2);
-                    if (edge && (key > myq || key >= T)) pv = 0.f;
-                    ds[e] = pv * (dp[8 * sl + e] - Dq);
+                    float pv = fast_exp2(__builtin_fmaf(sc[8 * sl + e], c, -ldq.x));
+                    if (edge && 32 * st + 16 * sl + e > lim) pv = 0.f;
+                    ds[e] = pv * (dp[8 * sl + e] - ldq.y);
                 }
                 const u32x4 dd = pack16<bf16>(ds);
-                const int ch = 4 * st + 2 * sl + g;
 #pragma unroll
-                for (int dt = 0; dt < 2; ++dt) dq[dt] = mfma32(dd, ld16(sKt + pos(32 * dt + r32, ch)), dq[dt]);
+                for (int dt = 0; dt < 2; ++dt) dq[dt] = mfma32(dd, ft.read(sK, dt, 2 * st + sl), dq[dt]);
             }
         }
-        }
-        if (more) {
-            bf16* nb = sbuf[(it + 1) & 1];
-            tk.store_n(nb, tid);
-            tv.store_n(nb + 64 * 64, tid);
-            tk.store_t(nb + 2 * 64 * 64, tid);
-        }
-        __syncthreads();
     }
     // dq[dt][i]: column d = 32 dt + r32, row query qw + 8 (i/4) + 4 g + i%4
 #pragma unroll
@@ -529,23 +486,23 @@ hipError_t attention_backward_mfma64(bf16* dqkv, float* dsum, const bf16* dout, 
                                      const float* lse, int B, int T, int C, int NH, hipStream_t s) {
     const double pairs = (double)B * NH * T * (T + 1) / 2, io = 2.0 * B * T * NH * HS;
     {
-        ProfScope prof(s, "attn_bwd_dsum64", 0, 2 * io + 4.0 * B * NH * T);
-        hipLaunchKernelGGL(attn_bwd_dsum64, dim3((B * T * NH + 255) / 256), dim3(256), 0, s, dsum, dout, out, B * T,
-                           T, C, NH);
+        ProfScope prof(s, "attn_bwd_dsum64", 0, 2 * io + 12.0 * B * NH * T);
+        hipLaunchKernelGGL(attn_bwd_dsum64, dim3((B * T * NH + 255) / 256), dim3(256), 0, s, (float2*)dsum, dout, out,
+                           lse, B * T, T, C, NH);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     {
         ProfScope prof(s, "attn_bwd_dkdv_mfma64", 4.0 * HS * pairs, 6 * io + 8.0 * B * NH * T);
-        hipLaunchKernelGGL(attn_bwd_dkdv_mfma64, dim3((T + 127) / 128, B * NH), dim3(256), 0, s, dqkv, qkv, dout, lse,
-                           dsum, T, C, NH);
+        hipLaunchKernelGGL(attn_bwd_dkdv_mfma64, dim3((T + 127) / 128, B * NH), dim3(256), 0, s, dqkv, qkv, dout,
+                           (const float2*)dsum, T, C, NH);
     }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     {
         ProfScope prof(s, "attn_bwd_dq_mfma64", 4.0 * HS * pairs, 5 * io + 8.0 * B * NH * T);
-        hipLaunchKernelGGL(attn_bwd_dq_mfma64, dim3((T + 127) / 128, B * NH), dim3(256), 0, s, dqkv, qkv, dout, lse,
-                           dsum, T, C, NH);
+        hipLaunchKernelGGL(attn_bwd_dq_mfma64, dim3((T + 127) / 128, B * NH), dim3(256), 0, s, dqkv, qkv, dout,
+                           (const float2*)dsum, T, C, NH);
     }
     return hipGetLastError();
 }

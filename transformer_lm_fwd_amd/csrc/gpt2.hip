@@ -148,7 +148,7 @@ size_t layout(gpt2_arena& a) {
     a.dbuf = take(BT * C * es);
     for (int i = 0; i < 2; ++i) a.dqkv[i] = take(BT * 3 * C * es);
     for (int i = 0; i < 2; ++i) a.dfch[i] = take(BT * 4 * C * es);
-    a.dsum = take(BT * NH * 4);
+    a.dsum = take(BT * NH * 8);  // per (row, head): {lse log2 e, D} for the head-size-64 kernels
     a.partial_floats = (size_t)512 * 2 * 4 * C;  // column-sum partials (<= 256 blocks x 4C)
     a.partial = take(a.partial_floats * 4);
     a.partial_side = take(a.partial_floats * 4);

@@ -84,7 +84,7 @@ hipError_t splitk_reduce(float* out, const float* ws, int splits, int64_t n, hip
 // qkv [B*T, 3C] (q | k | v, head h at columns h*hs), out [B*T, C], lse fp32 [B, NH, T].
 template <class T>
 hipError_t attention_forward(T* out, float* lse, const T* qkv, int B, int T_, int C, int NH, hipStream_t s);
-// dqkv [B*T, 3C] (overwrite) from dout [B*T, C]; `dsum` fp32 [B, NH, T] scratch.
+// dqkv [B*T, 3C] (overwrite) from dout [B*T, C]; `dsum` fp32 [B, NH, T, 2] scratch.
 template <class T>
 hipError_t attention_backward(T* dqkv, float* dsum, const T* dout, const T* out, const T* qkv, const float* lse,
                               int B, int T_, int C, int NH, hipStream_t s);
