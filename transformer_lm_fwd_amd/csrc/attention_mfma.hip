@@ -137,8 +137,9 @@ constexpr int FST = 3;
 __global__ __launch_bounds__(256) void attn_fwd_mfma64(bf16* out, float* lse, const bf16* qkv, int T, int C, int NH) {
     __shared__ __attribute__((aligned(1024))) bf16 sbuf[FST][2][64 * 64];  // [stage][K | V]
     const int nqt = (T + 127) / 128;
-    const int qt = nqt - 1 - (int)blockIdx.x;  // longest rows first
-    const int bh = blockIdx.y, b = bh / NH, h = bh % NH;
+    // blocks are dispatched x-fastest: every head's longest query tile goes first
+    const int qt = nqt - 1 - (int)blockIdx.y;
+    const int bh = blockIdx.x, b = bh / NH, h = bh % NH;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r32 = lane & 31, g = lane >> 5;
     const int64_t C3 = 3 * (int64_t)C;
     const bf16* base = qkv + (int64_t)b * T * C3;
@@ -279,8 +280,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_mfma64(bf16* dqkv, const bf
                                                             const float2* LD, int T, int C, int NH) {
     __shared__ __attribute__((aligned(1024))) bf16 sbuf[BST][2][64 * 64];  // [stage][Q | dO]
     __shared__ __attribute__((aligned(1024))) float sLD[BST][256];         // [stage][{L, D} x 64, copy]
-    const int kt = blockIdx.x;  // the first key tiles see the most queries: scheduled first
-    const int bh = blockIdx.y, b = bh / NH, h = bh % NH;
+    const int kt = blockIdx.y;  // the first key tiles see the most queries: dispatched first
+    const int bh = blockIdx.x, b = bh / NH, h = bh % NH;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r32 = lane & 31, g = lane >> 5;
     const int64_t C3 = 3 * (int64_t)C;
     const bf16* base = qkv + (int64_t)b * T * C3;
@@ -391,8 +392,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_mfma64(bf16* dqkv, const bf16
                                                           const float2* LD, int T, int C, int NH) {
     __shared__ __attribute__((aligned(1024))) bf16 sbuf[BST][2][64 * 64];  // [stage][K | V]
     const int nqt = (T + 127) / 128;
-    const int qt = nqt - 1 - (int)blockIdx.x;
-    const int bh = blockIdx.y, b = bh / NH, h = bh % NH;
+    const int qt = nqt - 1 - (int)blockIdx.y;  // longest first
+    const int bh = blockIdx.x, b = bh / NH, h = bh % NH;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r32 = lane & 31, g = lane >> 5;
     const int64_t C3 = 3 * (int64_t)C;
     const bf16* base = qkv + (int64_t)b * T * C3;
@@ -477,7 +478,7 @@ hipError_t attention_forward_mfma64(bf16* out, float* lse, const bf16* qkv, int 
                                     hipStream_t s) {
     const double pairs = (double)B * NH * T * (T + 1) / 2;
     ProfScope prof(s, "attn_fwd_mfma64", 4.0 * HS * pairs, 2.0 * B * T * NH * HS * 4 + 4.0 * B * NH * T);
-    dim3 grid((T + 127) / 128, B * NH);
+    dim3 grid(B * NH, (T + 127) / 128);
     hipLaunchKernelGGL(attn_fwd_mfma64, grid, dim3(256), 0, s, out, lse, qkv, T, C, NH);
     return hipGetLastError();
 }
@@ -494,14 +495,14 @@ hipError_t attention_backward_mfma64(bf16* dqkv, float* dsum, const bf16* dout, 
     if (e != hipSuccess) return e;
     {
         ProfScope prof(s, "attn_bwd_dkdv_mfma64", 4.0 * HS * pairs, 6 * io + 8.0 * B * NH * T);
-        hipLaunchKernelGGL(attn_bwd_dkdv_mfma64, dim3((T + 127) / 128, B * NH), dim3(256), 0, s, dqkv, qkv, dout,
+        hipLaunchKernelGGL(attn_bwd_dkdv_mfma64, dim3(B * NH, (T + 127) / 128), dim3(256), 0, s, dqkv, qkv, dout,
                            (const float2*)dsum, T, C, NH);
     }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     {
         ProfScope prof(s, "attn_bwd_dq_mfma64", 4.0 * HS * pairs, 5 * io + 8.0 * B * NH * T);
-        hipLaunchKernelGGL(attn_bwd_dq_mfma64, dim3((T + 127) / 128, B * NH), dim3(256), 0, s, dqkv, qkv, dout,
+        hipLaunchKernelGGL(attn_bwd_dq_mfma64, dim3(B * NH, (T + 127) / 128), dim3(256), 0, s, dqkv, qkv, dout,
                            (const float2*)dsum, T, C, NH);
     }
     return hipGetLastError();
