@@ -251,6 +251,15 @@ def test_zero_final_gains_give_ln_V_on_gpu():
 
 # ----------------------------------------------------------------------------- full size (bench configuration)
 
+_FULL = {}
+
+
+def full_params(w):
+    if w.name not in _FULL:
+        _FULL[w.name] = synth.init_params(w.model)
+    return _FULL[w.name]
+
+
 def test_gpt2_124m_b8t1024_bf16_full_size_sampled():
     # The timed configuration.  Sampled outputs the oracle computes one by one:
     # by causality, positions 0..63 of a sequence depend only on its first 64
@@ -258,7 +267,7 @@ def test_gpt2_124m_b8t1024_bf16_full_size_sampled():
     b = _b()
     w = synth.WORKLOADS["gpt2_124m_b8t1024_bf16"]
     announce("gpt2_124m_b8t1024_bf16 (full size)", w)
-    params = synth.init_params(w.model)
+    params = full_params(w)
     x, y = synth.inputs_targets(w)
     a = gpu_arena(w, params)
     a.forward(x, y)
@@ -285,3 +294,35 @@ def test_gpt2_124m_b8t1024_bf16_full_size_sampled():
     loss1 = a.loss()
     print(f"loss before {loss0:.5f} after one step {loss1:.5f}", flush=True)
     assert loss1 < loss0
+
+
+def test_gpt2_124m_b8t1024_bf16_full_size_gradients_identical_rows():
+    # The timed configuration's backward pass (every kernel at its real shape,
+    # including the split-K tied-embedding dX): with all B rows of the batch equal,
+    # the mean loss and every parameter gradient equal those of one row, which the
+    # oracle computes at B = 1.
+    b = _b()
+    w = synth.WORKLOADS["gpt2_124m_b8t1024_bf16"]
+    announce("gpt2_124m_b8t1024_bf16 identical rows (full size)", w)
+    params = full_params(w)
+    x, y = synth.inputs_targets(w)
+    xs, ys = np.repeat(x[:1], w.B, axis=0), np.repeat(y[:1], w.B, axis=0)
+    a = gpu_arena(w, params)
+    a.forward(xs, ys)
+    loss = a.loss()
+    a.backward()
+    g = to_np(a.tensor(b.T_GRADS)).ravel()
+    a.close()
+    o = oracle_model(w, params, B=1)
+    ref = o.forward(xs[:1], ys[:1])
+    o.backward()
+    gr = o.get("grads")
+    o.close()
+    cos = cosine(g, gr)
+    cos_t = {k: cosine(v, per_tensor(gr, w.model)[k]) for k, v in per_tensor(g, w.model).items()}
+    print(f"full size: loss gpu={loss:.6f} oracle={ref:.6f}; flat grad cosine={cos:.6f}", flush=True)
+    report("per-tensor cosine (lowest 5)", dict(sorted(cos_t.items(), key=lambda kv: kv[1])[:5]))
+    assert abs(loss - ref) <= BF16_LOSS_ABS
+    assert cos >= BF16_GRAD_COS
+    assert min(cos_t.values()) >= 0.99
+    assert np.isfinite(g).all()

@@ -78,17 +78,18 @@ __device__ __forceinline__ float wave_max(float v) {
 
 // GELU, tanh form (the formula quoted in the comment thread of the 3000-byte C
 // GPT-2 page): g(x) = x/2 (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))).  The
-// identity (1 + tanh u)/2 = 1/(1 + exp(-2u)) turns it into one exponential.
+// identity (1 + tanh u)/2 = 1/(1 + exp(-2u)) turns it into one exponential; the
+// reciprocal is the hardware's (v_rcp_f32, about 1 ulp) rather than a full division.
 #define GPT2_SQRT_2_OVER_PI 0.7978845608028654f
 __device__ __forceinline__ float gelu_fwd(float x) {
     float u = GPT2_SQRT_2_OVER_PI * (x + 0.044715f * x * x * x);
-    return x / (1.0f + __expf(-2.0f * u));
+    return x * __builtin_amdgcn_rcpf(1.0f + __expf(-2.0f * u));
 }
 // d/dx g(x) = s + x s (1 - s) 2 u'(x),  s = 1/(1 + exp(-2u)),
 // u'(x) = sqrt(2/pi) (1 + 3 * 0.044715 x^2)  (since (1+tanh u)/2 = s and tanh' = 1 - tanh^2).
 __device__ __forceinline__ float gelu_bwd(float x) {
     float u = GPT2_SQRT_2_OVER_PI * (x + 0.044715f * x * x * x);
-    float s = 1.0f / (1.0f + __expf(-2.0f * u));
+    float s = __builtin_amdgcn_rcpf(1.0f + __expf(-2.0f * u));
     float du = GPT2_SQRT_2_OVER_PI * (1.0f + 3.0f * 0.044715f * x * x);
     return s + x * s * (1.0f - s) * 2.0f * du;
 }

@@ -657,6 +657,30 @@ hipError_t gemm(const GemmArgs& a, bool ak, bool bk, int epi, float* ws, size_t 
         if (e != hipSuccess) return e;
         return splitk_reduce((float*)a.C, ws, splits, (int64_t)a.M * a.N, s);
     }
+    if constexpr (sizeof(T) == 2) {
+        // bf16 output with too few 128 x 256 tiles to fill the chip and a long K (the
+        // tied-embedding dX): split K so the blocks fill whole waves of 256, then sum
+        // the fp32 partials and add the bias in a fixed order.
+        const int tiles = ((a.M + 127) / 128) * ((a.N + 255) / 256);
+        if (epi == EPI_BIAS && ws && tiles < 256 && a.K >= 4096 && a.N % 8 == 0) {
+            auto eff = [&](int sp) { return (double)tiles * sp / (((tiles * sp + 255) / 256) * 256.0); };
+            int best = 1;
+            for (int sp = 2; sp <= 8; ++sp)
+                if (eff(sp) > eff(best) + 0.1 && (size_t)sp * a.M * a.N <= ws_floats) best = sp;
+            if (best > 1) {
+                int kps = (a.K + best - 1) / best;
+                kps = (kps + BK - 1) / BK * BK;
+                const int splits = (a.K + kps - 1) / kps;
+                GemmArgs p = a;
+                p.C = ws;
+                p.ldc = a.N;
+                p.bias = nullptr;
+                hipError_t e = dispatch_layout<T, EPI_F32>(p, ak, bk, splits, kps, (int64_t)a.M * a.N, s);
+                if (e != hipSuccess) return e;
+                return splitk_reduce_bf16((bf16*)a.C, a.ldc, ws, splits, a.M, a.N, a.bias, s);
+            }
+        }
+    }
     switch (epi) {
         case EPI_BIAS: return dispatch_layout<T, EPI_BIAS>(a, ak, bk, 1, a.K, 0, s);
         case EPI_BIAS_RES: return dispatch_layout<T, EPI_BIAS_RES>(a, ak, bk, 1, a.K, 0, s);

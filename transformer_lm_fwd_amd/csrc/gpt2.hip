@@ -44,8 +44,8 @@ struct gpt2_arena {
     size_t params, grads, adam_m, adam_v, params16;
     size_t encoded, lnf, lnfs, logits, losses, loss;
     std::vector<LayerActs> la;
-    size_t dres[4], dbuf, dqkv[2], dfch[2], dsum, partial, partial_side, ws;
-    size_t partial_floats, ws_floats;
+    size_t dres[4], dbuf, dqkv[2], dfch[2], dsum, partial, partial_side, ws, ws_main;
+    size_t partial_floats, ws_floats, ws_main_floats;
     bool loss_ready;
     const int32_t* inputs;
     // Backward concurrency: parameter-gradient work runs on `side`.  rd_* mark the
@@ -154,6 +154,9 @@ size_t layout(gpt2_arena& a) {
     a.partial_side = take(a.partial_floats * 4);
     a.ws_floats = (size_t)16 * 4 * C * C;  // split-K partials of the largest block dW (4C x C), 16 splits
     a.ws = take(a.ws_floats * 4);
+    // main stream's split-K partials: the tied-embedding dX ([B*T, C], K = vocab) in up to 4 splits
+    a.ws_main_floats = (size_t)4 * BT * C;
+    a.ws_main = take(a.ws_main_floats * 4);
     return o;
 }
 
@@ -213,7 +216,6 @@ struct Model {
     gpt2_arena* a;
     hipStream_t s;
     int C, L, NH, V, Vp, B, S, BT, P;  // S: sequence length
-    bool split_ok = true;               // main-stream GEMMs may use the split-K workspace
 
     Model(gpt2_arena* ar, hipStream_t st) : a(ar), s(st) {
         C = a->cfg.channels; L = a->cfg.num_layers; NH = a->cfg.num_heads; V = a->cfg.vocab_size;
@@ -236,8 +238,9 @@ struct Model {
         GemmArgs g;
         g.A = A; g.B = Bm; g.C = Cm; g.C2 = C2; g.R = R; g.bias = bias;
         g.M = M; g.N = N; g.K = K; g.lda = lda; g.ldb = ldb; g.ldc = ldc;
-        // the split-K workspace belongs to the side stream during backward
-        CHECK(gemm<T>(g, ak, bk, epi, split_ok ? f32(a->ws) : nullptr, split_ok ? a->ws_floats : 0, s), "gemm");
+        // main-stream products use their own split-K workspace (the side stream's is busy
+        // during backward)
+        CHECK(gemm<T>(g, ak, bk, epi, f32(a->ws_main), a->ws_main_floats, s), "gemm");
         return GPT2_OK;
     }
 
@@ -289,7 +292,6 @@ struct Model {
     int backward() {
         int rc;
         if ((rc = ensure_streams(a))) return rc;
-        split_ok = false;
         hipStream_t M = s, SD = profiling() ? s : a->side;
         T* dz = act(a->logits);
         T* dbuf = act(a->dbuf);

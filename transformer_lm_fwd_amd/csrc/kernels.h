@@ -79,6 +79,9 @@ hipError_t adamw(float* p, const float* g, float* m, float* v, bf16* p16, int64_
                  float eps, float wd, float c1, float c2, hipStream_t s);
 hipError_t cast_bf16(bf16* out, const float* in, int64_t n, hipStream_t s);
 hipError_t splitk_reduce(float* out, const float* ws, int splits, int64_t n, hipStream_t s);
+// C (bf16 [M, N], row stride ldc) = bias + sum of `splits` dense fp32 M x N partials.
+hipError_t splitk_reduce_bf16(bf16* C, int64_t ldc, const float* ws, int splits, int M, int N, const float* bias,
+                              hipStream_t s);
 
 // ---------------------------------------------------------------- attention
 // qkv [B*T, 3C] (q | k | v, head h at columns h*hs), out [B*T, C], lse fp32 [B, NH, T].

@@ -528,8 +528,22 @@ hipError_t cast_bf16(bf16* out, const float* in, int64_t n, hipStream_t s) {
     return hipGetLastError();
 }
 
+// out[i] = sum over k of ws[k * n + i], in split order (deterministic); four
+// elements per thread when n % 4 == 0.
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(float* out, const float* ws, int splits, int64_t n) {
-    int64_t stride = (int64_t)gridDim.x * 256;
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    if ((n & 3) == 0) {
+        const int64_t n4 = n >> 2;
+        for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += stride) {
+            float4 acc = ((const float4*)ws)[i];
+            for (int k = 1; k < splits; ++k) {
+                const float4 v = ((const float4*)(ws + (int64_t)k * n))[i];
+                acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+            }
+            ((float4*)out)[i] = acc;
+        }
+        return;
+    }
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) {
         float acc = 0.f;
         for (int k = 0; k < splits; ++k) acc += ws[(int64_t)k * n + i];
@@ -538,10 +552,47 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(float* out, const fl
 }
 
 hipError_t splitk_reduce(float* out, const float* ws, int splits, int64_t n, hipStream_t s) {
-    int64_t blocks = (n + 255) / 256;
+    int64_t blocks = ((n & 3) == 0 ? n / 4 : n + 255) / 256 + 1;
     if (blocks > 4096) blocks = 4096;
     ProfScope prof(s, "splitk_reduce", 0, 4.0 * (splits + 1) * n);
     hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, s, out, ws, splits, n);
+    return hipGetLastError();
+}
+
+// C[m, n] (bf16, row stride ldc) = bias[n] + sum over k of ws[k][m][n] (dense M x N
+// partials), 8 columns per thread; N % 8 == 0.
+__global__ __launch_bounds__(256) void splitk_reduce_bf16_kernel(bf16* C, int64_t ldc, const float* ws, int splits,
+                                                                 int M, int N, const float* bias) {
+    const int cpr = N / 8;
+    const int64_t total = (int64_t)M * cpr, mn = (int64_t)M * N;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+        const int m = (int)(i / cpr), n = (int)(i % cpr) * 8;
+        const float* p = ws + (int64_t)m * N + n;
+        float v[8];
+        {
+            const float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
+            v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+        }
+        for (int k = 1; k < splits; ++k) {
+            const float4 a = *(const float4*)(p + k * mn), b = *(const float4*)(p + k * mn + 4);
+            v[0] += a.x; v[1] += a.y; v[2] += a.z; v[3] += a.w; v[4] += b.x; v[5] += b.y; v[6] += b.z; v[7] += b.w;
+        }
+        if (bias) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] += bias[n + e];
+        }
+        st16(C + (int64_t)m * ldc + n, pack16<bf16>(v));
+    }
+}
+
+hipError_t splitk_reduce_bf16(bf16* C, int64_t ldc, const float* ws, int splits, int M, int N, const float* bias,
+                              hipStream_t s) {
+    if (N % 8 || ldc % 8) return hipErrorInvalidValue;
+    int64_t blocks = ((int64_t)M * (N / 8) + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    ProfScope prof(s, "splitk_reduce_bf16", 0, (4.0 * splits + 2) * M * N);
+    hipLaunchKernelGGL(splitk_reduce_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, s, C, ldc, ws, splits, M, N,
+                       bias);
     return hipGetLastError();
 }
 
