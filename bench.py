@@ -67,6 +67,8 @@ def main():
     ap.add_argument("--profile-steps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-table", default=None, help="write the per-kernel profile as JSON here")
+    ap.add_argument("--unfused", action="store_true",
+                    help="call gpt2_backward and gpt2_adamw_step separately instead of gpt2_backward_adamw")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -96,7 +98,7 @@ def main():
     # warm-up (the first call also checks the id range on the host)
     for i in range(max(1, args.warmup)):
         t += 1
-        arena.step(xi, yi, w, t, check_ids=(i == 0))
+        arena.step(xi, yi, w, t, check_ids=(i == 0), fused=not args.unfused)
     torch.cuda.synchronize()
     first_loss = arena.loss()
     log(f"[bench] warm-up done, loss {first_loss:.4f}")
@@ -106,7 +108,7 @@ def main():
     start.record()
     for _ in range(args.steps):
         t += 1
-        arena.step(xi, yi, w, t, check_ids=False)
+        arena.step(xi, yi, w, t, check_ids=False, fused=not args.unfused)
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end)
@@ -125,7 +127,7 @@ def main():
     binding.profile(True)
     for _ in range(args.profile_steps):
         t += 1
-        arena.step(xi, yi, w, t, check_ids=False)
+        arena.step(xi, yi, w, t, check_ids=False, fused=not args.unfused)
     torch.cuda.synchronize()
     binding.profile(False)
     stats = binding.profile_read()

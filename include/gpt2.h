@@ -122,6 +122,16 @@ int gpt2_backward(gpt2_arena* arena, void* stream);
 int gpt2_adamw_step(gpt2_arena* arena, float lr, float beta1, float beta2, float eps,
                     float weight_decay, int32_t step, void* stream);
 
+/* gpt2_backward followed by gpt2_adamw_step, fused: each layer's AdamW update is
+ * enqueued on the backward pass's second stream as soon as that layer's gradients are
+ * complete and the pass no longer reads its weights, so it overlaps the backward pass
+ * of the layers below; the embeddings and ln_f are updated last.  Gradients, moments
+ * and parameters are bitwise identical to the two separate calls.  Same arguments and
+ * errors as gpt2_backward and gpt2_adamw_step (GPT2_E_STATE without a preceding loss
+ * forward, GPT2_E_INVAL if step < 1). */
+int gpt2_backward_adamw(gpt2_arena* arena, float lr, float beta1, float beta2, float eps,
+                        float weight_decay, int32_t step, void* stream);
+
 /* Tensor ids for gpt2_tensor_info.  Model-level tensors ignore `layer`;
  * per-layer tensors need 0 <= layer < num_layers. */
 enum gpt2_tensor_id {

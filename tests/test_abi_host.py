@@ -98,6 +98,8 @@ def test_backward_before_forward_is_a_state_error_and_step_must_be_positive():
     try:
         assert b.lib().gpt2_backward(h, None) == -4
         assert b.lib().gpt2_adamw_step(h, 1e-4, 0.9, 0.999, 1e-8, 0.0, 0, None) == -1
+        assert b.lib().gpt2_backward_adamw(h, 1e-4, 0.9, 0.999, 1e-8, 0.0, 0, None) == -1   # step < 1
+        assert b.lib().gpt2_backward_adamw(h, 1e-4, 0.9, 0.999, 1e-8, 0.0, 1, None) == -4   # no loss forward
         off, rows, cols, ld, dt = (ctypes.c_size_t(), ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64(),
                                    ctypes.c_int32())
         assert b.lib().gpt2_tensor_info(h, 8, 0, ctypes.byref(off), ctypes.byref(rows), ctypes.byref(cols),

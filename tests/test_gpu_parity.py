@@ -230,6 +230,28 @@ def test_step_is_deterministic(dtype, NH):
     np.testing.assert_array_equal(outs[0][1], outs[1][1])
 
 
+@pytest.mark.parametrize("dtype,NH", [("fp32", 4), ("bf16", 2)])
+def test_fused_backward_adamw_matches_separate_calls(dtype, NH):
+    # gpt2_backward_adamw reorders only when each AdamW update runs; gradients,
+    # moments and parameters must be bitwise those of gpt2_backward + gpt2_adamw_step.
+    b = _b()
+    w = Workload("fused", ModelShape(160, 301, 3, NH, 128), 2, 130, dtype, "uniform", index=28)
+    announce(f"fused_backward_adamw_{dtype}", w)
+    p = rand_params(w.model, seed=11)
+    x, y = synth.inputs_targets(w)
+    res = []
+    for fused in (False, True):
+        a = gpu_arena(w, p)
+        for t in (1, 2):
+            a.step(x, y, w, t, fused=fused)
+        a.forward(x, y)
+        res.append([a.loss()] + [to_np(a.tensor(i)).copy() for i in (b.T_PARAMS, b.T_GRADS, b.T_ADAM_M, b.T_ADAM_V)])
+        a.close()
+    assert res[0][0] == res[1][0]
+    for u, f in zip(res[0][1:], res[1][1:]):
+        np.testing.assert_array_equal(u, f)
+
+
 def test_zero_final_gains_give_ln_V_on_gpu():
     # "从头搭建GPT(Andrej Karpathy) 笔记", 计算loss: all-zero logits cost exactly ln V, and
     # d loss / d z = (1/V - onehot)/(B T).

@@ -24,7 +24,7 @@ T_LN1, T_LN1_STATS, T_QKV, T_ATTY, T_ATT_LSE, T_RESIDUAL2 = 16, 17, 18, 19, 20, 
 T_LN2, T_LN2_STATS, T_FCH, T_FCH_GELU, T_RESIDUAL3 = 22, 23, 24, 25, 26
 
 EXPORTS = ("gpt2_alloc_arena", "gpt2_free_arena", "gpt2_sync_weights", "gpt2_forward", "gpt2_backward",
-           "gpt2_adamw_step", "gpt2_tensor_info", "gpt2_num_parameters", "gpt2_profile", "gpt2_profile_read",
+           "gpt2_adamw_step", "gpt2_backward_adamw", "gpt2_tensor_info", "gpt2_num_parameters", "gpt2_profile", "gpt2_profile_read",
            "gpt2_last_error")
 
 
@@ -62,6 +62,7 @@ def lib():
         L.gpt2_forward.argtypes = [vp, vp, vp, vp]
         L.gpt2_backward.argtypes = [vp, vp]
         L.gpt2_adamw_step.argtypes = [vp, f32, f32, f32, f32, f32, i32, vp]
+        L.gpt2_backward_adamw.argtypes = [vp, f32, f32, f32, f32, f32, i32, vp]
         L.gpt2_tensor_info.argtypes = [vp, i32, i32, ctypes.POINTER(sz), ctypes.POINTER(i64), ctypes.POINTER(i64),
                                        ctypes.POINTER(i64), ctypes.POINTER(i32)]
         L.gpt2_num_parameters.argtypes = [cfgp]
@@ -204,11 +205,19 @@ class Arena:
     def adamw_step(self, lr, beta1, beta2, eps, weight_decay, step: int, stream=None):
         _check(lib().gpt2_adamw_step(self.h, lr, beta1, beta2, eps, weight_decay, step, _stream_ptr(stream)))
 
+    def backward_adamw(self, lr, beta1, beta2, eps, weight_decay, step: int, stream=None):
+        """gpt2_backward and gpt2_adamw_step fused (per-layer updates overlap the backward pass)."""
+        _check(lib().gpt2_backward_adamw(self.h, lr, beta1, beta2, eps, weight_decay, step, _stream_ptr(stream)))
+
     def loss(self) -> float:
         return float(self.tensor(T_LOSS).item())
 
-    def step(self, inputs, targets, w, t: int, check_ids=True) -> None:
-        """forward + backward + AdamW with a workload's hyper-parameters."""
+    def step(self, inputs, targets, w, t: int, check_ids=True, fused=True) -> None:
+        """forward + backward + AdamW with a workload's hyper-parameters (fused: the
+        AdamW update overlaps the backward pass; results are bitwise the same)."""
         self.forward(inputs, targets, check_ids=check_ids)
-        self.backward()
-        self.adamw_step(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, t)
+        if fused:
+            self.backward_adamw(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, t)
+        else:
+            self.backward()
+            self.adamw_step(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, t)

@@ -211,6 +211,26 @@ void destroy_streams(gpt2_arena* a) {
     a->side = nullptr;
 }
 
+// AdamW hyper-parameters with the bias corrections of step t folded in.
+struct AdamArgs {
+    float lr, b1, b2, eps, wd, c1, c2;
+};
+
+AdamArgs adam_args(float lr, float b1, float b2, float eps, float wd, int32_t step) {
+    return AdamArgs{lr, b1, b2, eps, wd, (float)(1.0 - pow((double)b1, (double)step)),
+                    (float)(1.0 - pow((double)b2, (double)step))};
+}
+
+// AdamW over parameters [off, off + n) (offsets are multiples of 8: every tensor size is).
+int adamw_range(gpt2_arena* a, const AdamArgs& o, int64_t off, int64_t n, hipStream_t s) {
+    if (n <= 0) return GPT2_OK;
+    bf16* p16 = a->dtype == GPT2_BF16 ? at<bf16>(a, a->params16) + off : nullptr;
+    return hip_check(adamw(at<float>(a, a->params) + off, at<float>(a, a->grads) + off,
+                           at<float>(a, a->adam_m) + off, at<float>(a, a->adam_v) + off, p16, n, o.lr, o.b1, o.b2,
+                           o.eps, o.wd, o.c1, o.c2, s),
+                     "adamw");
+}
+
 template <class T>
 struct Model {
     gpt2_arena* a;
@@ -289,7 +309,11 @@ struct Model {
     // GEMMs, LayerNorm and attention backward); every parameter-gradient product
     // (weight GEMMs, bias column sums, the tied-embedding dW) runs on the side
     // stream, which forks after each producer and is joined at the end.
-    int backward() {
+    // With `opt`, each layer's AdamW update runs on the side stream as soon as the
+    // main stream is done with that layer (its last reader of the layer's weights is
+    // the ln_1 backward), overlapping the backward pass of the layers below; the
+    // embeddings and ln_f are updated after the join.
+    int backward(const AdamArgs* opt = nullptr) {
         int rc;
         if ((rc = ensure_streams(a))) return rc;
         hipStream_t M = s, SD = profiling() ? s : a->side;
@@ -380,6 +404,11 @@ struct Model {
                                         master(lp(l, P_LN1W)), BT, C, part, a->partial_floats, M),
                   "ln1 backward");
             cur = i_out;
+            if (opt) {  // layer l's gradients are complete and its weights no longer read
+                if ((rc = stream_wait(a, SD, M))) return rc;
+                const int64_t beg = lp(l, 0), end = l + 1 < L ? lp(l + 1, 0) : a->o_lnfw;
+                if ((rc = adamw_range(a, *opt, beg, end - beg, SD))) return rc;
+            }
         }
         // embedding: dwte += scatter (after the side stream's lm_head dW), dwpe
         if ((rc = wait(M, a->ev_wte))) return rc;
@@ -387,7 +416,12 @@ struct Model {
               "encoder backward");
         // join: everything the side stream enqueued finishes before later main-stream work
         if ((rc = mark(a->ev_end, SD))) return rc;
-        return wait(M, a->ev_end);
+        if ((rc = wait(M, a->ev_end))) return rc;
+        if (opt) {
+            if ((rc = adamw_range(a, *opt, 0, lp(0, 0), M))) return rc;  // wte, wpe
+            if ((rc = adamw_range(a, *opt, a->o_lnfw, a->nparams - a->o_lnfw, M))) return rc;  // ln_f
+        }
+        return GPT2_OK;
     }
 };
 
@@ -483,13 +517,18 @@ int gpt2_adamw_step(gpt2_arena* a, float lr, float beta1, float beta2, float eps
                     void* stream) {
     if (!a) return fail(GPT2_E_INVAL, "arena is NULL");
     if (step < 1) return fail(GPT2_E_INVAL, "step must be >= 1");
-    const float c1 = (float)(1.0 - pow((double)beta1, (double)step));
-    const float c2 = (float)(1.0 - pow((double)beta2, (double)step));
-    bf16* p16 = a->dtype == GPT2_BF16 ? at<bf16>(a, a->params16) : nullptr;
-    return hip_check(adamw(at<float>(a, a->params), at<float>(a, a->grads), at<float>(a, a->adam_m),
-                           at<float>(a, a->adam_v), p16, a->nparams, lr, beta1, beta2, eps, weight_decay, c1, c2,
-                           (hipStream_t)stream),
-                     "adamw");
+    return adamw_range(a, adam_args(lr, beta1, beta2, eps, weight_decay, step), 0, a->nparams, (hipStream_t)stream);
+}
+
+int gpt2_backward_adamw(gpt2_arena* a, float lr, float beta1, float beta2, float eps, float weight_decay,
+                        int32_t step, void* stream) {
+    if (!a) return fail(GPT2_E_INVAL, "arena is NULL");
+    if (step < 1) return fail(GPT2_E_INVAL, "step must be >= 1");
+    if (!a->loss_ready) return fail(GPT2_E_STATE, "backward needs a preceding forward with targets");
+    a->loss_ready = false;
+    const AdamArgs o = adam_args(lr, beta1, beta2, eps, weight_decay, step);
+    return a->dtype == GPT2_BF16 ? Model<bf16>(a, (hipStream_t)stream).backward(&o)
+                                 : Model<float>(a, (hipStream_t)stream).backward(&o);
 }
 
 int gpt2_tensor_info(const gpt2_arena* a, int32_t id, int32_t layer, size_t* byte_offset, int64_t* rows,
