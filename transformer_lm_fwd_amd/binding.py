@@ -11,7 +11,8 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "_lib", "libgpt2_hip.so")
+# GPT2_HIP_LIB may name another build of the same library (e.g. to compare two builds).
+LIB_PATH = os.environ.get("GPT2_HIP_LIB") or os.path.join(HERE, "_lib", "libgpt2_hip.so")
 
 GPT2_FP32, GPT2_BF16 = 0, 1
 STATUS = {0: "GPT2_OK", -1: "GPT2_E_INVAL", -2: "GPT2_E_SIZE", -3: "GPT2_E_ALIGN", -4: "GPT2_E_STATE",

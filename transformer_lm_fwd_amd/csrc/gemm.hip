@@ -339,12 +339,12 @@ struct DmaTile {
 };
 
 
+// `wtile`: LDS byte address of this wave's first 1 KB slot of the tile (an SGPR);
+// the wave's loads go to slots wave, wave + NW, ...
 template <int PW, int NW>
-__device__ __forceinline__ void dma_issue(const dsc_t& d, bf16* tile, const uint32_t* voff, int wave, uint32_t soff) {
+__device__ __forceinline__ void dma_issue(const dsc_t& d, uint32_t wtile, const uint32_t* voff, uint32_t soff) {
 #pragma unroll
-    for (int j = 0; j < PW; ++j) {
-        dma16(d, lds_addr(tile + (wave + NW * j) * 512), voff[j], soff);
-    }
+    for (int j = 0; j < PW; ++j) dma16(d, wtile + (uint32_t)(NW * j) * 1024u, voff[j], soff);
 }
 
 // Byte offsets in a tile of the MFMA fragment at mn offset f0, k slice ks
@@ -411,29 +411,39 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a, int
 #pragma unroll
         for (int j = 0; j < TN; ++j) frag_offsets<BKC, BN>(lane, (wn * TN + j) * 32, ks, fb[j][ks]);
     }
+    // Fragments of k-slice ks + 1 are read while the MFMAs of slice ks run.
     auto compute = [&](const bf16* st) {
+        u32x4 xa[2][TM], xb[2][TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) xa[0][i] = frag_read<AK>(st, fa[i][0]);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) xb[0][j] = frag_read<BKC>(st + SA, fb[j][0]);
 #pragma unroll
         for (int ks = 0; ks < GBK / 16; ++ks) {
-            u32x4 xa[TM], xb[TN];
+            const int cb = ks & 1, nb = cb ^ 1;
+            if (ks + 1 < GBK / 16) {
 #pragma unroll
-            for (int i = 0; i < TM; ++i) xa[i] = frag_read<AK>(st, fa[i][ks]);
+                for (int i = 0; i < TM; ++i) xa[nb][i] = frag_read<AK>(st, fa[i][ks + 1]);
 #pragma unroll
-            for (int j = 0; j < TN; ++j) xb[j] = frag_read<BKC>(st + SA, fb[j][ks]);
+                for (int j = 0; j < TN; ++j) xb[nb][j] = frag_read<BKC>(st + SA, fb[j][ks + 1]);
+            }
+            __builtin_amdgcn_sched_barrier(0);  // keep those reads ahead of this slice's MFMAs
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
-                for (int j = 0; j < TN; ++j) acc[i][j] = MT::step(xa[i], xb[j], acc[i][j]);
+                for (int j = 0; j < TN; ++j) acc[i][j] = MT::step(xa[cb][i], xb[cb][j], acc[i][j]);
         }
     };
 
     // ST-stage ring: tiles kt+1 .. kt+ST-1 are in flight while tile kt is multiplied
     constexpr int LPT = TA::PW + TB::PW;  // wave loads per tile
+    const uint32_t lbase = __builtin_amdgcn_readfirstlane(lds_addr(lds) + (uint32_t)wave * 1024u);  // this wave
 #pragma unroll
     for (int s0 = 0; s0 < ST - 1; ++s0)
         if (s0 < nk) {
             const uint32_t k1 = (uint32_t)(kbeg + s0 * GBK);
-            dma_issue<TA::PW, NW>(ra, lds + s0 * STAGE, ta.voff, wave, k1 * ta.kstep);
-            dma_issue<TB::PW, NW>(rb, lds + s0 * STAGE + SA, tb.voff, wave, k1 * tb.kstep);
+            dma_issue<TA::PW, NW>(ra, lbase + s0 * STAGE * 2, ta.voff, k1 * ta.kstep);
+            dma_issue<TB::PW, NW>(rb, lbase + (s0 * STAGE + SA) * 2, tb.voff, k1 * tb.kstep);
         }
     int cur = 0;  // stage of tile kt
     for (int kt = 0; kt < nk; ++kt) {
@@ -444,10 +454,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a, int
         __builtin_amdgcn_s_barrier();
         if (kt + ST - 1 < nk) {
             const int st = cur == 0 ? ST - 1 : cur - 1;
-            bf16* nxt = lds + st * STAGE;
+            const uint32_t nxt = lbase + (uint32_t)(st * STAGE * 2);
             const uint32_t k1 = (uint32_t)(kbeg + (kt + ST - 1) * GBK);
-            dma_issue<TA::PW, NW>(ra, nxt, ta.voff, wave, k1 * ta.kstep);
-            dma_issue<TB::PW, NW>(rb, nxt + SA, tb.voff, wave, k1 * tb.kstep);
+            dma_issue<TA::PW, NW>(ra, nxt, ta.voff, k1 * ta.kstep);
+            dma_issue<TB::PW, NW>(rb, nxt + SA * 2, tb.voff, k1 * tb.kstep);
         }
         compute(lds + cur * STAGE);
         cur = cur + 1 == ST ? 0 : cur + 1;
