@@ -305,9 +305,15 @@ constexpr int GBK = 64;  // k per tile
 // reads) and the 8 chunks of one row fall on distinct 16-byte bank groups.
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 __device__ __forceinline__ int lds_pos(int r, int chunk) { return r * GBK + ((chunk ^ swz(r)) << 3); }
-// mn-contiguous tiles: the 4 consecutive k rows one 16-lane group reads (32 bytes
-// each) land on 4 distinct 32-byte bank groups.
+// mn-contiguous tiles (at least 16 chunks per row): chunk c of row k sits at slot
+// c ^ 2 (k % 4) ^ 8 ((c / 2) % 2).  The 4 consecutive k rows one 16-lane group reads
+// (32 bytes each) land on 4 distinct 32-byte bank groups, and the neighbouring group
+// (the next 32 bytes of the same rows) on the other 128-byte half of the banks.
 __device__ __forceinline__ int hsw(int k) { return (k & 3) << 1; }
+__device__ __forceinline__ int mn_slot(int k, int c) { return c ^ hsw(k) ^ (((c >> 1) & 1) << 3); }
+__device__ __forceinline__ int mn_chunk(int k, int slot) {
+    return slot ^ hsw(k) ^ ((((slot >> 1) ^ k) & 1) << 3);
+}
 
 
 // Per-lane global offsets of one operand tile (ROWS mn x 64 k) in 1 KB wave loads.
@@ -317,6 +323,7 @@ struct DmaTile {
     static_assert(NI % NW == 0, "wave loads per tile must divide among the waves");
     static constexpr int PW = NI / NW;
     static constexpr int CPR = ROWS / 8;           // mn-contiguous: chunks per k row
+    static_assert(KC || CPR >= 16, "mn-contiguous tiles need at least 16 chunks per row");
     static constexpr int RPI = KC ? 8 : 64 / CPR;  // rows per wave load
     uint32_t voff[PW];
     uint32_t kstep;  // bytes per k element
@@ -330,7 +337,7 @@ struct DmaTile {
                 voff[j] = (uint32_t)(((int64_t)(row0 + r) * ld + c * 8) * 2);
             } else {
                 const int kr = q * RPI + lane / CPR;
-                const int c = (lane % CPR) ^ hsw(kr);
+                const int c = mn_chunk(kr, lane % CPR);
                 voff[j] = (uint32_t)(((int64_t)kr * ld + row0 + c * 8) * 2);
             }
         }
@@ -358,8 +365,8 @@ __device__ __forceinline__ void frag_offsets(int lane, int f0, int ks, int* o) {
         const int g = lane >> 4, i = lane & 15;
         const int col = f0 + 16 * (g & 1) + 4 * (i & 3);
         const int k = 16 * ks + 8 * (g >> 1) + (i >> 2);
-        o[0] = k * ROWS * 2 + (((col >> 3) ^ hsw(k)) << 4) + ((col >> 2) & 1) * 8;
-        o[1] = o[0] + 4 * ROWS * 2;  // k + 4 (hsw depends on k % 4 only)
+        o[0] = k * ROWS * 2 + (mn_slot(k, col >> 3) << 4) + ((col >> 2) & 1) * 8;
+        o[1] = o[0] + 4 * ROWS * 2;  // k + 4 (the slot depends on k % 4 only)
     }
 }
 template <bool KC>
