@@ -36,6 +36,37 @@ def model_flops_per_step(m, B, T):
     return (6.0 * N + 6.0 * m.num_layers * m.channels * (T + 1)) * B * T
 
 
+def source_digest():
+    """Digest of the library's kernel sources: counter readings taken on other
+    sources do not describe the current kernels."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "transformer_lm_fwd_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the committed FETCH_SIZE / WRITE_SIZE
+    counter summary (profiles/traffic_<workload>.json), scaled by the copy-kernel
+    calibration; None when there is no reading or the kernel sources changed since."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    out = {"traffic": None}
+    if not os.path.exists(path):
+        return out
+    with open(path) as f:
+        t = json.load(f)
+    k = t.get("kernels", {}).get(kernel)
+    if k is None or t.get("source_digest") != source_digest():
+        return out
+    out["traffic"] = round(k["fetch_bytes"] + k["write_bytes"])
+    out["traffic_fetch"] = round(k["fetch_bytes"])
+    out["traffic_write"] = round(k["write_bytes"])
+    return out
+
+
 def cpu_baseline(w, params, x, y, budget_s=10.0, T_sample=256):
     """The float oracle on a bounded sample of the workload: the first T_sample
     tokens of batch row 0, full forward + backward + AdamW, repeated until about
@@ -67,6 +98,9 @@ def main():
     ap.add_argument("--profile-steps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-table", default=None, help="write the per-kernel profile as JSON here")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only copy 1 GiB device-to-device 5 times (a kernel of known traffic for the "
+                         "FETCH_SIZE / WRITE_SIZE counter calibration) and exit")
     ap.add_argument("--unfused", action="store_true",
                     help="call gpt2_backward and gpt2_adamw_step separately instead of gpt2_backward_adamw")
     args = ap.parse_args()
@@ -79,6 +113,16 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copies": 5}), flush=True)
+        return
 
     import synth
     from transformer_lm_fwd_amd import Arena, binding
@@ -133,7 +177,8 @@ def main():
     stats = binding.profile_read()
     tot = sum(s["total_ms"] for s in stats)
     stats.sort(key=lambda s: -s["total_ms"])
-    log(f"[bench] kernel profile over {args.profile_steps} steps ({tot / args.profile_steps:.3f} ms/step in kernels):")
+    log(f"[bench] kernel profile over {args.profile_steps} steps "
+        f"({tot / max(1, args.profile_steps):.3f} ms/step in kernels):")
     for s in stats:
         avg = s["total_ms"] / s["launches"]
         tf = s["flops"] / (s["total_ms"] / 1e3) / 1e12 if s["flops"] else 0.0
@@ -143,18 +188,21 @@ def main():
     if args.kernel_table:
         with open(args.kernel_table, "w") as f:
             json.dump({"workload": w.name, "profile_steps": args.profile_steps, "kernels": stats}, f, indent=1)
-    dom = stats[0]
-    avg_s = dom["total_ms"] / dom["launches"] / 1e3
-    if dom["flops"] > 0:
-        achieved = dom["flops"] / dom["launches"] / avg_s / 1e12
-        roof = {"kernel": dom["name"], "bound": "mfma", "achieved": round(achieved, 2),
-                "peak": PEAK_TFLOPS[w.dtype], "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS[w.dtype], 4)}
-    else:
-        achieved = dom["bytes"] / dom["launches"] / avg_s / 1e9
-        roof = {"kernel": dom["name"], "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
-    roof["avg_launch_us"] = round(avg_s * 1e6, 2)
-    roof["traffic"] = None
+    roof = None
+    if stats:
+        dom = stats[0]
+        avg_s = dom["total_ms"] / dom["launches"] / 1e3
+        if dom["flops"] > 0:
+            achieved = dom["flops"] / dom["launches"] / avg_s / 1e12
+            roof = {"kernel": dom["name"], "bound": "mfma", "achieved": round(achieved, 2),
+                    "peak": PEAK_TFLOPS[w.dtype], "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS[w.dtype], 4)}
+        else:
+            achieved = dom["bytes"] / dom["launches"] / avg_s / 1e9
+            roof = {"kernel": dom["name"], "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
+        roof["avg_launch_us"] = round(avg_s * 1e6, 2)
+        roof["algorithmic_bytes_per_launch"] = round(dom["bytes"] / dom["launches"])
+        roof.update(measured_traffic(w.name, dom["name"]))
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -378,6 +378,24 @@ __device__ __forceinline__ u32x4 frag_read(const bf16* tile, const int* o) {
     }
 }
 
+// Tile of a block.  The grid is one-dimensional, rounded up to a multiple of 8.
+// Blocks are dispatched round-robin over gfx950's 8 XCDs (block i on XCD i % 8),
+// each with its own L2, so XCD x is given the contiguous run x * n/8 .. of the tile
+// sequence, and that sequence walks groups of 8 tile rows column by column: the
+// blocks an XCD runs together share A row-tiles and B column-tiles in its L2
+// instead of every XCD fetching every operand tile.  Returns false for padding.
+__device__ __forceinline__ bool tile_of_block(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
+    constexpr int XCDS = 8, GROUP_M = 8;
+    const int nt = tiles_m * tiles_n, per = (nt + XCDS - 1) / XCDS;
+    const int t = (bid % XCDS) * per + bid / XCDS;
+    if (t >= nt) return false;
+    const int group = t / (GROUP_M * tiles_n), first = group * GROUP_M;
+    const int gm = min(GROUP_M, tiles_m - first), idx = t - group * GROUP_M * tiles_n;
+    tm = first + idx % gm;
+    tn = idx / gm;
+    return true;
+}
+
 template <bool AK, bool BKC, int EPI, int BM, int BN, int WM, int WN, int ST = 2>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a, int k_per_split, int64_t split_stride,
                                                                  uint32_t a_bytes, uint32_t b_bytes) {
@@ -390,7 +408,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a, int
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
-    const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+    int tm, tn;
+    if (!tile_of_block(blockIdx.x, (a.M + BM - 1) / BM, (a.N + BN - 1) / BN, tm, tn)) return;
+    const int m0 = tm * BM, n0 = tn * BN;
     const int kbeg = blockIdx.z * k_per_split;
     const int kend = min(a.K, kbeg + k_per_split);
     const int nk = kend > kbeg ? (kend - kbeg + GBK - 1) / GBK : 0;
@@ -613,11 +633,13 @@ static hipError_t launch(const GemmArgs& a, int splits, int k_per_split, int64_t
         // per CU; otherwise 128 x 256 with waves of 64 x 64 and three stages.  Both
         // hold one block per CU (128 / 144 KB of LDS).
         if (splits == 1 && use_tile256(a.M, a.N, 1)) {
-            dim3 grid((a.N + 255) / 256, (a.M + 255) / 256, splits);
+            const int nt = ((a.N + 255) / 256) * ((a.M + 255) / 256);
+            dim3 grid((nt + 7) / 8 * 8, 1, splits);
             hipLaunchKernelGGL((gemm_bf16_kernel<AK, BKC, EPI, 256, 256, 2, 4, 2>), grid, dim3(512), 0, s, a,
                                k_per_split, split_stride, (uint32_t)ab, (uint32_t)bb);
         } else {
-            dim3 grid((a.N + 255) / 256, (a.M + 127) / 128, splits);
+            const int nt = ((a.N + 255) / 256) * ((a.M + 127) / 128);
+            dim3 grid((nt + 7) / 8 * 8, 1, splits);
             hipLaunchKernelGGL((gemm_bf16_kernel<AK, BKC, EPI, 128, 256, 2, 4, 3>), grid, dim3(512), 0, s, a,
                                k_per_split, split_stride, (uint32_t)ab, (uint32_t)bb);
         }
