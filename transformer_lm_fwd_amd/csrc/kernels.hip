@@ -302,17 +302,29 @@ __device__ __forceinline__ void online_merge(float& m, float& s, float m2, float
     m = mn;
 }
 
+// The first REG 16-byte vectors of each thread's share of the row stay in registers
+// between the two passes, so the logits are read from memory once (rows up to
+// REG * 1024 vectors; longer rows re-read the rest).
 template <class T>
 __global__ __launch_bounds__(1024) void crossentropy_kernel(T* logits, float* losses, const int32_t* targets, int V,
                                                             int64_t ldz, float dscale) {
     constexpr int KV = Vec16<T>::N;
+    constexpr int REG = 64 / KV;  // 64 values per thread: V up to 65536
     const int row = blockIdx.x;
     T* z = logits + (int64_t)row * ldz;
     const int nvec = V / KV;  // full 16-byte vectors inside [0, V)
+    const int y = targets[row];
+    const float zy = to_f32(z[y]);
     float m = -INFINITY, s = 0.f;
-    for (int i = threadIdx.x; i < nvec; i += 1024) {
+    u32x4 keep[REG];
+#pragma unroll
+    for (int r = 0; r < REG; ++r) {
+        const int i = threadIdx.x + r * 1024;
+        if (i < nvec) keep[r] = ld16(z + i * KV);
+    }
+    auto absorb = [&](const u32x4& raw) {
         float v[KV];
-        unpack16<T>(ld16(z + i * KV), v);
+        unpack16<T>(raw, v);
         float mx = v[0];
 #pragma unroll
         for (int e = 1; e < KV; ++e) mx = fmaxf(mx, v[e]);
@@ -320,7 +332,11 @@ __global__ __launch_bounds__(1024) void crossentropy_kernel(T* logits, float* lo
 #pragma unroll
         for (int e = 0; e < KV; ++e) ss += __expf(v[e] - mx);
         online_merge(m, s, mx, ss);
-    }
+    };
+#pragma unroll
+    for (int r = 0; r < REG; ++r)
+        if (threadIdx.x + r * 1024 < nvec) absorb(keep[r]);
+    for (int i = threadIdx.x + REG * 1024; i < nvec; i += 1024) absorb(ld16(z + i * KV));
     for (int i = nvec * KV + threadIdx.x; i < V; i += 1024) online_merge(m, s, to_f32(z[i]), 1.f);
     // block reduction of (m, s)
     __shared__ float sm[16], ss_[16];
@@ -335,19 +351,23 @@ __global__ __launch_bounds__(1024) void crossentropy_kernel(T* logits, float* lo
     m = sm[0]; s = ss_[0];
     for (int w2 = 1; w2 < 16; ++w2) online_merge(m, s, sm[w2], ss_[w2]);
     const float lse = m + __logf(s);
-    const int y = targets[row];
-    if (threadIdx.x == 0) losses[row] = lse - to_f32(z[y]);
-    __syncthreads();  // z[y] read before it is overwritten
-    for (int i = threadIdx.x; i < nvec; i += 1024) {
+    if (threadIdx.x == 0) losses[row] = lse - zy;
+    auto grad = [&](const u32x4& raw, int i) {
         float v[KV];
-        unpack16<T>(ld16(z + i * KV), v);
+        unpack16<T>(raw, v);
 #pragma unroll
         for (int e = 0; e < KV; ++e) {
-            int col = i * KV + e;
+            const int col = i * KV + e;
             v[e] = (__expf(v[e] - lse) - (col == y ? 1.f : 0.f)) * dscale;
         }
         st16(z + i * KV, pack16<T>(v));
+    };
+#pragma unroll
+    for (int r = 0; r < REG; ++r) {
+        const int i = threadIdx.x + r * 1024;
+        if (i < nvec) grad(keep[r], i);
     }
+    for (int i = threadIdx.x + REG * 1024; i < nvec; i += 1024) grad(ld16(z + i * KV), i);
     for (int i = nvec * KV + threadIdx.x; i < (int)ldz; i += 1024) {
         float g = 0.f;
         if (i < V) g = (__expf(to_f32(z[i]) - lse) - (i == y ? 1.f : 0.f)) * dscale;
