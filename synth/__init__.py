@@ -26,6 +26,8 @@ from __future__ import annotations
 import dataclasses
 import math
 
+import os
+
 import numpy as np
 
 GAMMA = np.uint64(0x9E3779B97F4A7C15)
@@ -155,19 +157,28 @@ def num_parameters(m: ModelShape) -> int:
 def init_params(m: ModelShape, seed: int = PARAM_SEED, chunk: int = 1 << 22) -> np.ndarray:
     """The flat fp32 parameter vector.  Element i of a normal-initialised tensor
     is std * normal(seed, i) with i the flat index, so any slice is reproducible
-    on its own."""
+    on its own (chunks are filled by a thread pool; the result does not depend on
+    the order)."""
+    import concurrent.futures
     total = num_parameters(m)
     out = np.empty(total, dtype=np.float32)
+    jobs = []
     o = 0
     for _, n, (kind, val) in param_tensors(m):
         if kind == "const":
             out[o:o + n] = val
         else:
             for s in range(0, n, chunk):
-                e = min(n, s + chunk)
-                idx = np.arange(o + s, o + e, dtype=np.uint64)
-                out[o + s:o + e] = (val * normal(seed, idx)).astype(np.float32)
+                jobs.append((o + s, o + min(n, s + chunk), val))
         o += n
+
+    def fill(job):
+        b, e, val = job
+        out[b:e] = (val * normal(seed, np.arange(b, e, dtype=np.uint64))).astype(np.float32)
+
+    workers = max(1, min(16, len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else 4))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+        list(ex.map(fill, jobs))
     return out
 
 

@@ -11,6 +11,11 @@ FP32_LOSS_REL = 1e-5
 FP32_MAXREL = 1e-3
 BF16_LOSS_ABS = 2e-2
 BF16_GRAD_COS = 0.999
+# Loss of a single position (derived, not stated): bf16 rounds each activation to
+# 2^-9 relative; over 24-48 layers a single position's loss drifts by a few 1e-2
+# (measured up to 0.034 at 48 layers), while the mean over positions stays within
+# BF16_LOSS_ABS.
+BF16_POS_LOSS_ABS = 1e-1
 
 # oracle activation name -> (tensor id, column selector) of the GPU arena
 ACT_MAP = {
