@@ -378,6 +378,10 @@ __device__ __forceinline__ u32x4 frag_read(const bf16* tile, const int* o) {
     }
 }
 
+#ifndef GEMM_GROUP_M
+#define GEMM_GROUP_M 8  // tile rows per group in the per-XCD tile order
+#endif
+
 // Tile of a block.  The grid is one-dimensional, rounded up to a multiple of 8.
 // Blocks are dispatched round-robin over gfx950's 8 XCDs (block i on XCD i % 8),
 // each with its own L2, so XCD x is given the contiguous run x * n/8 .. of the tile
@@ -385,7 +389,7 @@ __device__ __forceinline__ u32x4 frag_read(const bf16* tile, const int* o) {
 // blocks an XCD runs together share A row-tiles and B column-tiles in its L2
 // instead of every XCD fetching every operand tile.  Returns false for padding.
 __device__ __forceinline__ bool tile_of_block(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
-    constexpr int XCDS = 8, GROUP_M = 8;
+    constexpr int XCDS = 8, GROUP_M = GEMM_GROUP_M;
     const int nt = tiles_m * tiles_n, per = (nt + XCDS - 1) / XCDS;
     const int t = (bid % XCDS) * per + bid / XCDS;
     if (t >= nt) return false;

@@ -61,6 +61,13 @@ template <class T>
 hipError_t layernorm_backward(T* dres, const T* dres_in, float* dw, float* db, const T* dout, const T* inp,
                               const float* stats, const float* w, int N, int C, float* partial, size_t partial_floats,
                               hipStream_t s);
+// The two halves of layernorm_backward, for callers that run them on different streams.
+template <class T>
+hipError_t layernorm_backward_dx(T* dres, const T* dres_in, const T* dout, const T* inp, const float* stats,
+                                 const float* w, int N, int C, hipStream_t s);
+template <class T>
+hipError_t layernorm_param_grads(float* dw, float* db, const T* dout, const T* inp, const float* stats, int N, int C,
+                                 float* partial, size_t partial_floats, hipStream_t s);
 // dbias[n] = sum_m dout[m, n] (overwrite), deterministic two-stage.
 template <class T>
 hipError_t bias_grad(float* dbias, const T* dout, int M, int N, int64_t ld, float* partial, size_t partial_floats,

@@ -263,23 +263,33 @@ static hipError_t colsum(float* out0, float* out1, const T* dy, const T* x, cons
 }
 
 template <class T>
-hipError_t layernorm_backward(T* dres, const T* dres_in, float* dw, float* db, const T* dout, const T* inp,
-                              const float* stats, const float* w, int N, int C, float* partial, size_t partial_floats,
-                              hipStream_t s) {
+hipError_t layernorm_backward_dx(T* dres, const T* dres_in, const T* dout, const T* inp, const float* stats,
+                                 const float* w, int N, int C, hipStream_t s) {
     constexpr int KV = Vec16<T>::N;
     const int ch = cdiv(C, 64 * KV);
     const dim3 grid(cdiv(N, 4)), block(256);
-    {
-        ProfScope prof(s, "layernorm_bwd_dx", 0, (double)N * C * sizeof(T) * (dres_in ? 4 : 3) + 8.0 * N);
-        if (ch <= 1) hipLaunchKernelGGL((layernorm_backward_dx_kernel<T, 1>), grid, block, 0, s, dres, dres_in, dout, inp, stats, w, N, C);
-        else if (ch <= 2) hipLaunchKernelGGL((layernorm_backward_dx_kernel<T, 2>), grid, block, 0, s, dres, dres_in, dout, inp, stats, w, N, C);
-        else if (ch <= 4) hipLaunchKernelGGL((layernorm_backward_dx_kernel<T, 4>), grid, block, 0, s, dres, dres_in, dout, inp, stats, w, N, C);
-        else if (ch <= 8) hipLaunchKernelGGL((layernorm_backward_dx_kernel<T, 8>), grid, block, 0, s, dres, dres_in, dout, inp, stats, w, N, C);
-        else return hipErrorInvalidValue;
-    }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    ProfScope prof(s, "layernorm_bwd_dx", 0, (double)N * C * sizeof(T) * (dres_in ? 4 : 3) + 8.0 * N);
+    if (ch <= 1) hipLaunchKernelGGL((layernorm_backward_dx_kernel<T, 1>), grid, block, 0, s, dres, dres_in, dout, inp, stats, w, N, C);
+    else if (ch <= 2) hipLaunchKernelGGL((layernorm_backward_dx_kernel<T, 2>), grid, block, 0, s, dres, dres_in, dout, inp, stats, w, N, C);
+    else if (ch <= 4) hipLaunchKernelGGL((layernorm_backward_dx_kernel<T, 4>), grid, block, 0, s, dres, dres_in, dout, inp, stats, w, N, C);
+    else if (ch <= 8) hipLaunchKernelGGL((layernorm_backward_dx_kernel<T, 8>), grid, block, 0, s, dres, dres_in, dout, inp, stats, w, N, C);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+template <class T>
+hipError_t layernorm_param_grads(float* dw, float* db, const T* dout, const T* inp, const float* stats, int N, int C,
+                                 float* partial, size_t partial_floats, hipStream_t s) {
     return colsum<T, true>(dw, db, dout, inp, stats, N, C, C, partial, partial_floats, s, "layernorm_bwd_dwdb");
+}
+
+template <class T>
+hipError_t layernorm_backward(T* dres, const T* dres_in, float* dw, float* db, const T* dout, const T* inp,
+                              const float* stats, const float* w, int N, int C, float* partial, size_t partial_floats,
+                              hipStream_t s) {
+    hipError_t e = layernorm_backward_dx<T>(dres, dres_in, dout, inp, stats, w, N, C, s);
+    if (e != hipSuccess) return e;
+    return layernorm_param_grads<T>(dw, db, dout, inp, stats, N, C, partial, partial_floats, s);
 }
 
 // ============================================================================ bias gradients
@@ -624,6 +634,10 @@ hipError_t splitk_reduce_bf16(bf16* C, int64_t ldc, const float* ws, int splits,
                                              hipStream_t);                                                        \
     template hipError_t layernorm_backward<T>(T*, const T*, float*, float*, const T*, const T*, const float*,   \
                                               const float*, int, int, float*, size_t, hipStream_t);              \
+    template hipError_t layernorm_backward_dx<T>(T*, const T*, const T*, const T*, const float*, const float*,   \
+                                                 int, int, hipStream_t);                                         \
+    template hipError_t layernorm_param_grads<T>(float*, float*, const T*, const T*, const float*, int, int,     \
+                                                 float*, size_t, hipStream_t);                                    \
     template hipError_t bias_grad<T>(float*, const T*, int, int, int64_t, float*, size_t, hipStream_t);          \
     template hipError_t crossentropy_fused<T>(T*, float*, const int32_t*, int, int, int64_t, float, hipStream_t); \
     template hipError_t encoder_backward<T>(float*, float*, const T*, const int32_t*, int, int, int, int,        \
