@@ -351,15 +351,16 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_mfma64(bf16* dqkv, const bf
                 }
                 float p[8], ds[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    float pv = fast_exp2(__builtin_fmaf(sc[8 * sl + e], c, -Lq[e]));
-                    if (edge) {
+                for (int e = 0; e < 8; ++e) p[e] = fast_exp2(__builtin_fmaf(sc[8 * sl + e], c, -Lq[e]));
+                if (edge) {  // wave-uniform: only tiles on the diagonal or past T mask
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
                         const int idx = 32 * qs + 16 * sl + e;
-                        if (idx < lo || idx >= hi) pv = 0.f;
+                        if (idx < lo || idx >= hi) p[e] = 0.f;
                     }
-                    p[e] = pv;
-                    ds[e] = pv * (dp[8 * sl + e] - Dq[e]);
                 }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ds[e] = p[e] * (dp[8 * sl + e] - Dq[e]);
                 const u32x4 pp = pack16<bf16>(p), dd = pack16<bf16>(ds);
 #pragma unroll
                 for (int dt = 0; dt < 2; ++dt) {
@@ -448,13 +449,16 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_mfma64(bf16* dqkv, const bf16
             }
 #pragma unroll
             for (int sl = 0; sl < 2; ++sl) {
-                float ds[8];
+                float pv[8], ds[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    float pv = fast_exp2(__builtin_fmaf(sc[8 * sl + e], c, -ldq.x));
-                    if (edge && 32 * st + 16 * sl + e > lim) pv = 0.f;
-                    ds[e] = pv * (dp[8 * sl + e] - ldq.y);
+                for (int e = 0; e < 8; ++e) pv[e] = fast_exp2(__builtin_fmaf(sc[8 * sl + e], c, -ldq.x));
+                if (edge) {  // wave-uniform
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (32 * st + 16 * sl + e > lim) pv[e] = 0.f;
                 }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ds[e] = pv[e] * (dp[8 * sl + e] - ldq.y);
                 const u32x4 dd = pack16<bf16>(ds);
 #pragma unroll
                 for (int dt = 0; dt < 2; ++dt) dq[dt] = mfma32(dd, ft.read(sK, dt, 2 * st + sl), dq[dt]);
