@@ -244,30 +244,10 @@ __global__ __launch_bounds__(256) void attn_fwd_mfma64(bf16* out, float* lse, co
 }
 
 // ============================================================================ backward
-// LD[b, h, q] = {lse[q] * log2(e), D[q]},  D[q] = sum_d dO[q, d] O[q, d]
-// (= sum_k P[q, k] dP[q, k]): the per-query values both backward kernels need,
-// side by side so a 64-query tile of them is one 512-byte load.
-__global__ __launch_bounds__(256) void attn_bwd_dsum64(float2* LD, const bf16* dout, const bf16* out,
-                                                       const float* lse, int BT, int T, int C, int NH) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (row, head)
-    if (i >= (int64_t)BT * NH) return;
-    const int row = (int)(i / NH), h = (int)(i % NH);
-    const bf16* a = dout + (int64_t)row * C + h * HS;
-    const bf16* o = out + (int64_t)row * C + h * HS;
-    float acc = 0.f;
-#pragma unroll
-    for (int d = 0; d < HS; d += 8) {
-        float x[8], y[8];
-        unpack16<bf16>(ld16(a + d), x);
-        unpack16<bf16>(ld16(o + d), y);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc += x[e] * y[e];
-    }
-    const int b = row / T, t = row % T;
-    const int64_t j = ((int64_t)b * NH + h) * T + t;
-    LD[j] = make_float2(lse[j] * LOG2E, acc);
-}
-
+// The per-query values both backward kernels need -- LD[b, h, q] = {lse[q] log2 e,
+// D[q]} with D[q] = sum_d dO[q, d] O[q, d] (= sum_k P[q, k] dP[q, k]) -- are
+// computed by the dQ kernel, which runs first, and stored side by side so that a
+// 64-query tile of them is one load for the dK/dV kernel.
 constexpr int BST = 3;  // LDS stages of the backward kernels
 
 // dK, dV for 128 keys (4 waves x 32), looping over query tiles of 64 at or after
@@ -390,7 +370,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_mfma64(bf16* dqkv, const bf
 // the query as accumulator column, dS (query x 8 keys per lane) as the A operand
 // of dQ = dS K with K^T fragments read transposed from the K tile.
 __global__ __launch_bounds__(256) void attn_bwd_dq_mfma64(bf16* dqkv, const bf16* qkv, const bf16* dout,
-                                                          const float2* LD, int T, int C, int NH) {
+                                                          const bf16* out, const float* lse, float2* LD, int T,
+                                                          int C, int NH) {
     __shared__ __attribute__((aligned(1024))) bf16 sbuf[BST][2][64 * 64];  // [stage][K | V]
     const int nqt = (T + 127) / 128;
     const int qt = nqt - 1 - (int)blockIdx.y;  // longest first
@@ -408,7 +389,21 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_mfma64(bf16* dqkv, const bf16
         qf[ks] = row_frag(base + h * HS, C3, myq, 16 * ks + 8 * g, T);
         gf[ks] = row_frag(Gg, C, myq, 16 * ks + 8 * g, T);
     }
-    const float2 ldq = myq < T ? LD[(int64_t)bh * T + myq] : make_float2(0.f, 0.f);
+    // D = sum_d dO[q, d] O[q, d]: this lane holds 32 of the 64 dims (the same as its
+    // dO fragments), the lane 32 apart the other 32.  {lse log2 e, D} is stored for
+    // the dK/dV kernel, which runs next.
+    float dpart = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        float gv[8], ov[8];
+        unpack16<bf16>(gf[ks], gv);
+        unpack16<bf16>(row_frag(out + (int64_t)b * T * C + h * HS, C, myq, 16 * ks + 8 * g, T), ov);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dpart += gv[e] * ov[e];
+    }
+    const float Dq = dpart + __shfl_xor(dpart, 32, 64);
+    const float2 ldq = make_float2(myq < T ? lse[(int64_t)bh * T + myq] * LOG2E : 0.f, Dq);
+    if (g == 0 && myq < T) LD[(int64_t)bh * T + myq] = ldq;
     f32x16 dq[2] = {zero16(), zero16()};
 
     const dsc_t dsc = make_dsc(base, (uint32_t)(T * C3 * 2));
@@ -491,22 +486,15 @@ hipError_t attention_backward_mfma64(bf16* dqkv, float* dsum, const bf16* dout, 
                                      const float* lse, int B, int T, int C, int NH, hipStream_t s) {
     const double pairs = (double)B * NH * T * (T + 1) / 2, io = 2.0 * B * T * NH * HS;
     {
-        ProfScope prof(s, "attn_bwd_dsum64", 0, 2 * io + 12.0 * B * NH * T);
-        hipLaunchKernelGGL(attn_bwd_dsum64, dim3((B * T * NH + 255) / 256), dim3(256), 0, s, (float2*)dsum, dout, out,
-                           lse, B * T, T, C, NH);
+        ProfScope prof(s, "attn_bwd_dq_mfma64", 4.0 * HS * pairs, 6 * io + 12.0 * B * NH * T);
+        hipLaunchKernelGGL(attn_bwd_dq_mfma64, dim3(B * NH, (T + 127) / 128), dim3(256), 0, s, dqkv, qkv, dout, out,
+                           lse, (float2*)dsum, T, C, NH);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     {
         ProfScope prof(s, "attn_bwd_dkdv_mfma64", 4.0 * HS * pairs, 6 * io + 8.0 * B * NH * T);
         hipLaunchKernelGGL(attn_bwd_dkdv_mfma64, dim3(B * NH, (T + 127) / 128), dim3(256), 0, s, dqkv, qkv, dout,
-                           (const float2*)dsum, T, C, NH);
-    }
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    {
-        ProfScope prof(s, "attn_bwd_dq_mfma64", 4.0 * HS * pairs, 5 * io + 8.0 * B * NH * T);
-        hipLaunchKernelGGL(attn_bwd_dq_mfma64, dim3(B * NH, (T + 127) / 128), dim3(256), 0, s, dqkv, qkv, dout,
                            (const float2*)dsum, T, C, NH);
     }
     return hipGetLastError();
