@@ -44,7 +44,7 @@ struct gpt2_arena {
     size_t params, grads, adam_m, adam_v, params16;
     size_t encoded, lnf, lnfs, logits, losses, loss;
     std::vector<LayerActs> la;
-    size_t dres[4], dbuf, dqkv[2], dfch[2], dsum, partial, partial_side, ws, ws_main;
+    size_t dres[4], dbuf, dqkv[2], dfch[2], dsum, partial, partial_side, ws, ws_main, census;
     size_t partial_floats, ws_floats, ws_main_floats;
     bool loss_ready;
     const int32_t* inputs;
@@ -157,6 +157,7 @@ size_t layout(gpt2_arena& a) {
     // main stream's split-K partials: the tied-embedding dX ([B*T, C], K = vocab) in up to 4 splits
     a.ws_main_floats = (size_t)4 * BT * C;
     a.ws_main = take(a.ws_main_floats * 4);
+    a.census = take((size_t)2 * a.cfg.vocab_size * 4);  // per token: first position, count (embedding backward)
     return o;
 }
 
@@ -315,6 +316,8 @@ struct Model {
     // embeddings and ln_f are updated after the join.
     int backward(const AdamArgs* opt = nullptr) {
         int rc;
+        if (!a->side)  // first backward pass on this arena: arm the token census
+            CHECK(token_census_reset(at<int>(a, a->census), at<int>(a, a->census) + V, V, s), "census reset");
         if ((rc = ensure_streams(a))) return rc;
         hipStream_t M = s, SD = profiling() ? s : a->side;
         T* dz = act(a->logits);
@@ -412,7 +415,8 @@ struct Model {
         }
         // embedding: dwte += scatter (after the side stream's lm_head dW), dwpe
         if ((rc = wait(M, a->ev_wte))) return rc;
-        CHECK(encoder_backward<T>(grad(a->o_wte), grad(a->o_wpe), act(a->dres[cur]), a->inputs, B, S, P, C, M),
+        CHECK(encoder_backward<T>(grad(a->o_wte), grad(a->o_wpe), act(a->dres[cur]), a->inputs, B, S, P, C,
+                                  at<int>(a, a->census), at<int>(a, a->census) + V, M),
               "encoder backward");
         // join: everything the side stream enqueued finishes before later main-stream work
         if ((rc = mark(a->ev_end, SD))) return rc;

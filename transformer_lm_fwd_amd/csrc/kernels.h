@@ -79,9 +79,11 @@ hipError_t crossentropy_fused(T* logits, float* losses, const int32_t* targets, 
                               float dscale, hipStream_t s);
 hipError_t mean_loss(float* loss, const float* losses, int N, hipStream_t s);
 // dwte[tok] += dx rows (deterministic), dwpe[t] = sum_b dx[b, t] for t < T, 0 for T <= t < P.
+// first / count: int [V] scratch, INT_MAX / 0 on entry (token_census_reset) and on return.
 template <class T>
 hipError_t encoder_backward(float* dwte, float* dwpe, const T* dx, const int32_t* tok, int B, int T_, int P, int C,
-                            hipStream_t s);
+                            int* first, int* count, hipStream_t s);
+hipError_t token_census_reset(int* first, int* count, int V, hipStream_t s);
 hipError_t adamw(float* p, const float* g, float* m, float* v, bf16* p16, int64_t n, float lr, float b1, float b2,
                  float eps, float wd, float c1, float c2, hipStream_t s);
 hipError_t cast_bf16(bf16* out, const float* in, int64_t n, hipStream_t s);

@@ -416,51 +416,82 @@ hipError_t mean_loss(float* loss, const float* losses, int N, hipStream_t s) {
 // ============================================================================ encoder backward
 // dwte[v] += sum of dx rows whose token is v.  The first position holding token v
 // (its "leader") sums every matching row in increasing position order and is the
-// only writer of dwte[v], so the result is deterministic without atomics.
-// Matches are found 256 positions at a time with wave ballots.
+// only writer of dwte[v], so the result is deterministic without atomics on the
+// sums.  A first pass records, per token, its first position (atomic minimum) and
+// its number of occurrences (atomic add) -- both independent of thread order -- so a
+// position learns whether it leads in O(1), and a leader of a token seen once adds
+// its own row without scanning.  Repeated tokens are matched 256 positions at a time
+// with wave ballots.  The leader re-arms first[v] / count[v] for the next call.
+__global__ __launch_bounds__(256) void token_census_kernel(int* first, int* count, const int32_t* tok, int BT) {
+    const int p = blockIdx.x * 256 + threadIdx.x;
+    if (p >= BT) return;
+    atomicMin(&first[tok[p]], p);
+    atomicAdd(&count[tok[p]], 1);
+}
+
 template <class T>
 __global__ __launch_bounds__(256) void encoder_backward_wte_kernel(float* dwte, const T* dx, const int32_t* tok,
-                                                                   int BT, int C) {
+                                                                   int* first, int* count, int BT, int C) {
     const int pos = blockIdx.x;
     const int v = tok[pos];
+    if (first[v] != pos) return;  // block-uniform
+    const int n = count[v];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    __shared__ unsigned long long mask[4];
-    // leader check: no earlier position holds v
-    for (int j0 = 0; j0 < pos; j0 += 256) {
-        int j = j0 + threadIdx.x;
-        int hit = (j < pos) && tok[j] == v;
-        if (__syncthreads_or(hit)) return;
-    }
     constexpr int MAXC = 8;  // columns per thread: C <= 2048
     float acc[MAXC];
 #pragma unroll
-    for (int i = 0; i < MAXC; ++i) acc[i] = 0.f;
-    for (int j0 = pos; j0 < BT; j0 += 256) {
-        int j = j0 + threadIdx.x;
-        unsigned long long bal = __ballot((j < BT) && tok[j] == v);
-        if (lane == 0) mask[wave] = bal;
-        __syncthreads();
-        for (int w = 0; w < 4; ++w) {
-            unsigned long long mm = mask[w];
-            while (mm) {
-                int bit = __ffsll((long long)mm) - 1;
-                mm &= mm - 1;
-                const T* r = dx + (int64_t)(j0 + w * 64 + bit) * C;
+    for (int i = 0; i < MAXC; ++i) {
+        const int c = threadIdx.x + i * 256;
+        acc[i] = c < C ? to_f32(dx[(int64_t)pos * C + c]) : 0.f;
+    }
+    if (n > 1) {
+        __shared__ unsigned long long mask[4];
+        int found = 1;
+        for (int j0 = pos + 1; j0 < BT && found < n; j0 += 256) {
+            const int j = j0 + threadIdx.x;
+            const unsigned long long bal = __ballot((j < BT) && tok[j] == v);
+            if (lane == 0) mask[wave] = bal;
+            __syncthreads();
+            for (int w = 0; w < 4; ++w) {
+                unsigned long long mm = mask[w];
+                while (mm) {
+                    const int bit = __ffsll((long long)mm) - 1;
+                    mm &= mm - 1;
+                    const T* r = dx + (int64_t)(j0 + w * 64 + bit) * C;
 #pragma unroll
-                for (int i = 0; i < MAXC; ++i) {
-                    int c = threadIdx.x + i * 256;
-                    if (c < C) acc[i] += to_f32(r[c]);
+                    for (int i = 0; i < MAXC; ++i) {
+                        const int c = threadIdx.x + i * 256;
+                        if (c < C) acc[i] += to_f32(r[c]);
+                    }
+                    ++found;
                 }
             }
+            __syncthreads();
         }
-        __syncthreads();
     }
     float* out = dwte + (int64_t)v * C;
 #pragma unroll
     for (int i = 0; i < MAXC; ++i) {
-        int c = threadIdx.x + i * 256;
+        const int c = threadIdx.x + i * 256;
         if (c < C) out[c] += acc[i];
     }
+    if (threadIdx.x == 0) {
+        first[v] = 0x7fffffff;
+        count[v] = 0;
+    }
+}
+
+__global__ void token_census_reset_kernel(int* first, int* count, int V) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < V) {
+        first[i] = 0x7fffffff;
+        count[i] = 0;
+    }
+}
+
+hipError_t token_census_reset(int* first, int* count, int V, hipStream_t s) {
+    hipLaunchKernelGGL(token_census_reset_kernel, dim3(cdiv(V, 256)), dim3(256), 0, s, first, count, V);
+    return hipGetLastError();
 }
 
 // dwpe[t] = sum_b dx[b, t] for t < T; rows T..P-1 of dwpe get 0.
@@ -478,11 +509,20 @@ __global__ __launch_bounds__(256) void encoder_backward_wpe_kernel(float* dwpe, 
 
 template <class T>
 hipError_t encoder_backward(float* dwte, float* dwpe, const T* dx, const int32_t* tok, int B, int T_, int P, int C,
-                            hipStream_t s) {
+                            int* first, int* count, hipStream_t s) {
     if (C > 8 * 256) return hipErrorInvalidValue;
-    ProfScope prof(s, "encoder_bwd_wte", 0, (double)B * T_ * C * (sizeof(T) + 8.0));
-    hipLaunchKernelGGL(encoder_backward_wte_kernel<T>, dim3(B * T_), dim3(256), 0, s, dwte, dx, tok, B * T_, C);
+    {
+        ProfScope prof(s, "token_census", 0, 4.0 * B * T_);
+        hipLaunchKernelGGL(token_census_kernel, dim3(cdiv(B * T_, 256)), dim3(256), 0, s, first, count, tok, B * T_);
+    }
     hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    {
+        ProfScope prof(s, "encoder_bwd_wte", 0, (double)B * T_ * C * (sizeof(T) + 8.0));
+        hipLaunchKernelGGL(encoder_backward_wte_kernel<T>, dim3(B * T_), dim3(256), 0, s, dwte, dx, tok, first, count,
+                           B * T_, C);
+    }
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
     ProfScope prof2(s, "encoder_bwd_wpe", 0, (double)B * T_ * C * sizeof(T) + 4.0 * P * C);
     hipLaunchKernelGGL(encoder_backward_wpe_kernel<T>, dim3(cdiv((int64_t)P * C, 256)), dim3(256), 0, s, dwpe, dx, B,
@@ -640,8 +680,8 @@ hipError_t splitk_reduce_bf16(bf16* C, int64_t ldc, const float* ws, int splits,
                                                  float*, size_t, hipStream_t);                                    \
     template hipError_t bias_grad<T>(float*, const T*, int, int, int64_t, float*, size_t, hipStream_t);          \
     template hipError_t crossentropy_fused<T>(T*, float*, const int32_t*, int, int, int64_t, float, hipStream_t); \
-    template hipError_t encoder_backward<T>(float*, float*, const T*, const int32_t*, int, int, int, int,        \
-                                            hipStream_t);
+    template hipError_t encoder_backward<T>(float*, float*, const T*, const int32_t*, int, int, int, int, int*,  \
+                                            int*, hipStream_t);
 GPT2_INST(float)
 GPT2_INST(bf16)
 
