@@ -78,9 +78,14 @@ __global__ __launch_bounds__(256) void layernorm_forward_kernel(T* out, float* s
     for (int ch = 0; ch < MAXCH; ++ch) {
         int c = (ch * 64 + lane) * KV;
         if (c < C) {
-            float o[KV];
+            float o[KV], wv[KV], bv[KV];
 #pragma unroll
-            for (int e = 0; e < KV; ++e) o[e] = (v[ch][e] - mean) * rstd * w[c + e] + b[c + e];
+            for (int e = 0; e < KV; e += 4) {  // C % 8 == 0: 16-byte aligned fp32 gains and shifts
+                *(float4*)&wv[e] = *(const float4*)(w + c + e);
+                *(float4*)&bv[e] = *(const float4*)(b + c + e);
+            }
+#pragma unroll
+            for (int e = 0; e < KV; ++e) o[e] = (v[ch][e] - mean) * rstd * wv[e] + bv[e];
             st16(y + c, pack16<T>(o));
         }
     }
@@ -123,6 +128,13 @@ __global__ __launch_bounds__(256) void layernorm_backward_dx_kernel(T* dres, con
     const T* x = inp + (int64_t)row * C;
     float g[MAXCH][KV], xh[MAXCH][KV];
     float s1 = 0.f, s2 = 0.f;
+    const T* dxi = dres_in ? dres_in + (int64_t)row * C : nullptr;
+    u32x4 prev_raw[MAXCH];  // the residual gradient to add, requested before the reductions
+#pragma unroll
+    for (int ch = 0; ch < MAXCH; ++ch) {
+        const int c = (ch * 64 + lane) * KV;
+        prev_raw[ch] = (dxi && c < C) ? ld16(dxi + c) : u32x4{0u, 0u, 0u, 0u};
+    }
 #pragma unroll
     for (int ch = 0; ch < MAXCH; ++ch) {
         const int c = (ch * 64 + lane) * KV;
@@ -144,15 +156,12 @@ __global__ __launch_bounds__(256) void layernorm_backward_dx_kernel(T* dres, con
     s1 = wave_sum(s1) / C;
     s2 = wave_sum(s2) / C;
     T* dx = dres + (int64_t)row * C;
-    const T* dxi = dres_in ? dres_in + (int64_t)row * C : nullptr;
 #pragma unroll
     for (int ch = 0; ch < MAXCH; ++ch) {
         const int c = (ch * 64 + lane) * KV;
         if (c < C) {
             float prev[KV], o[KV];
-#pragma unroll
-            for (int e = 0; e < KV; ++e) prev[e] = 0.f;
-            if (dxi) unpack16<T>(ld16(dxi + c), prev);
+            unpack16<T>(prev_raw[ch], prev);
 #pragma unroll
             for (int e = 0; e < KV; ++e) o[e] = rstd * (g[ch][e] - s1 - xh[ch][e] * s2) + prev[e];
             st16(dx + c, pack16<T>(o));
