@@ -476,6 +476,17 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a, int
             dma_issue<TA::PW, NW>(ra, lbase + s0 * STAGE * 2, ta.voff, k1 * ta.kstep);
             dma_issue<TB::PW, NW>(rb, lbase + (s0 * STAGE + SA) * 2, tb.voff, k1 * tb.kstep);
         }
+    // Row sums of op(A) (the bias gradient of a weight-gradient product), taken by
+    // the blocks of the first column tile from the A tiles in LDS: thread t owns the
+    // 8 m values of chunk t % RCPR and adds the k rows t / RCPR + RROWS p.
+    constexpr bool RS = !AK && EPI == EPI_F32;
+    constexpr int RCPR = BM / 8, RROWS = NT / RCPR;
+    static_assert(!RS || (NT % RCPR == 0 && GBK % RROWS == 0), "row-sum thread mapping");
+    const bool do_rs = RS && a.rowsum && n0 == 0;
+    float rs[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) rs[e] = 0.f;
+
     int cur = 0;  // stage of tile kt
     for (int kt = 0; kt < nk; ++kt) {
         // tile kt has landed (every wave waits for its own loads, then the barrier);
@@ -490,10 +501,39 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a, int
             dma_issue<TA::PW, NW>(ra, nxt, ta.voff, k1 * ta.kstep);
             dma_issue<TB::PW, NW>(rb, nxt + SA * 2, tb.voff, k1 * tb.kstep);
         }
+        if constexpr (RS) {
+            if (do_rs) {
+                const bf16* at = lds + cur * STAGE;
+                const int c = tid % RCPR;
+#pragma unroll
+                for (int p = 0; p < GBK / RROWS; ++p) {
+                    const int kr = tid / RCPR + p * RROWS;
+                    float v[8];
+                    unpack16<bf16>(*(const u32x4*)(at + kr * BM + mn_slot(kr, c) * 8), v);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) rs[e] += v[e];
+                }
+            }
+        }
         compute(lds + cur * STAGE);
         cur = cur + 1 == ST ? 0 : cur + 1;
     }
     __syncthreads();
+    if constexpr (RS) {
+        if (do_rs) {  // block-uniform
+            float* red = (float*)lds;
+            const int c = tid % RCPR, g = tid / RCPR;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) red[g * BM + c * 8 + e] = rs[e];
+            __syncthreads();
+            if (tid < BM && m0 + tid < a.M) {
+                float v = 0.f;
+                for (int h = 0; h < RROWS; ++h) v += red[h * BM + tid];
+                a.rowsum[blockIdx.z * split_stride + m0 + tid] = v;
+            }
+            __syncthreads();
+        }
+    }
 
     // Epilogue through LDS: the accumulators are written as fp32 rows [row][BN + 8]
     // (the pad puts the two half-waves of a 32x32 tile on different banks), then
@@ -683,11 +723,15 @@ hipError_t gemm(const GemmArgs& a, bool ak, bool bk, int epi, float* ws, size_t 
         const int tiles = sizeof(T) == 2 ? ((a.M + 127) / 128) * ((a.N + 255) / 256)
                                          : ((a.M + 127) / 128) * ((a.N + 127) / 128);
         const int slots = sizeof(T) == 2 ? 256 : 512;
+        // With row sums, each split's partials are [M x N | M], so the sums of the
+        // bias gradient stored right after its weight gradient reduce in the same pass.
+        if (a.rowsum && (sizeof(T) != 2 || ak)) return hipErrorInvalidValue;
+        const int64_t mn = (int64_t)a.M * a.N, ss = mn + (a.rowsum ? (a.M + 3) / 4 * 4 : 0);
         int splits = 1;
         if (ws && a.ldc == a.N && tiles < slots && !(sizeof(T) == 2 && use_tile256(a.M, a.N, 1))) {
             splits = slots / tiles;
             splits = std::min(splits, a.K / (8 * BK));
-            while (splits > 1 && (size_t)splits * a.M * a.N > ws_floats) --splits;
+            while (splits > 1 && (size_t)splits * ss > ws_floats) --splits;
             splits = std::max(splits, 1);
         }
         if (splits == 1) return dispatch_layout<T, EPI_F32>(a, ak, bk, 1, a.K, 0, s);
@@ -696,9 +740,14 @@ hipError_t gemm(const GemmArgs& a, bool ak, bool bk, int epi, float* ws, size_t 
         splits = (a.K + kps - 1) / kps;
         GemmArgs p = a;
         p.C = ws;
-        hipError_t e = dispatch_layout<T, EPI_F32>(p, ak, bk, splits, kps, (int64_t)a.M * a.N, s);
+        if (a.rowsum) p.rowsum = ws + mn;
+        hipError_t e = dispatch_layout<T, EPI_F32>(p, ak, bk, splits, kps, ss, s);
         if (e != hipSuccess) return e;
-        return splitk_reduce((float*)a.C, ws, splits, (int64_t)a.M * a.N, s);
+        if (a.rowsum && a.rowsum == (float*)a.C + mn)
+            return splitk_reduce((float*)a.C, ws, splits, mn + a.M, ss, s);
+        e = splitk_reduce((float*)a.C, ws, splits, mn, ss, s);
+        if (e != hipSuccess || !a.rowsum) return e;
+        return splitk_reduce(a.rowsum, ws + mn, splits, a.M, ss, s);
     }
     if constexpr (sizeof(T) == 2) {
         // bf16 output with too few 128 x 256 tiles to fill the chip and a long K (the
@@ -718,6 +767,7 @@ hipError_t gemm(const GemmArgs& a, bool ak, bool bk, int epi, float* ws, size_t 
                 p.C = ws;
                 p.ldc = a.N;
                 p.bias = nullptr;
+                p.rowsum = nullptr;
                 hipError_t e = dispatch_layout<T, EPI_F32>(p, ak, bk, splits, kps, (int64_t)a.M * a.N, s);
                 if (e != hipSuccess) return e;
                 return splitk_reduce_bf16((bf16*)a.C, a.ldc, ws, splits, a.M, a.N, a.bias, s);

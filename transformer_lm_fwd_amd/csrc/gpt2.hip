@@ -256,7 +256,7 @@ struct Model {
     int gemm_call(const void* A, int64_t lda, bool ak, const void* Bm, int64_t ldb, bool bk, void* Cm, int64_t ldc,
                   int M, int N, int K, int epi, const float* bias = nullptr, const void* R = nullptr,
                   void* C2 = nullptr) {
-        GemmArgs g;
+        GemmArgs g{};
         g.A = A; g.B = Bm; g.C = Cm; g.C2 = C2; g.R = R; g.bias = bias;
         g.M = M; g.N = N; g.K = K; g.lda = lda; g.ldb = ldb; g.ldc = ldc;
         // main-stream products use their own split-K workspace (the side stream's is busy
@@ -324,20 +324,35 @@ struct Model {
         T* dbuf = act(a->dbuf);
         float* part = f32(a->partial);
         float* part_side = f32(a->partial_side);
+        // A buffer-release event not yet recorded in this pass was last recorded by an
+        // earlier pass, whose side-stream work the main stream has already joined, so
+        // waiting on it is skipped.  This keeps every wait inside the pass, which also
+        // lets a caller capture the pass into a graph.
+        hipEvent_t marked[16];
+        int nmarked = 0;
         auto wait = [&](hipStream_t st, hipEvent_t e) -> int {
+            bool live = false;
+            for (int i = 0; i < nmarked; ++i) live |= marked[i] == e;
+            if (!live) return GPT2_OK;
             return hipStreamWaitEvent(st, e, 0) == hipSuccess ? GPT2_OK : fail(GPT2_E_HIP, "hipStreamWaitEvent");
         };
         auto mark = [&](hipEvent_t e, hipStream_t st) -> int {
+            bool seen = false;
+            for (int i = 0; i < nmarked; ++i) seen |= marked[i] == e;
+            if (!seen) marked[nmarked++] = e;
             return hipEventRecord(e, st) == hipSuccess ? GPT2_OK : fail(GPT2_E_HIP, "hipEventRecord");
         };
         // side-stream weight GEMM: dW = dY^T X (fp32, overwrites), db = column sums of dY
+        // (bf16: taken inside the GEMM from its dY tiles; fp32: a separate reduction)
         auto side_dw = [&](const T* dy, int OC, const T* x, int IC, int64_t ow, int64_t ob) -> int {
             int r;
+            constexpr bool fused_db = sizeof(T) == 2;
             GemmArgs g{};
             g.A = dy; g.B = x; g.C = grad(ow);
             g.M = OC; g.N = IC; g.K = BT; g.lda = OC; g.ldb = IC; g.ldc = IC;
+            if (fused_db && ob >= 0) g.rowsum = grad(ob);
             if ((r = hip_check(gemm<T>(g, false, false, EPI_F32, f32(a->ws), a->ws_floats, SD), "gemm"))) return r;
-            if (ob >= 0)
+            if (!fused_db && ob >= 0)
                 return hip_check(bias_grad<T>(grad(ob), dy, BT, OC, OC, part_side, a->partial_floats, SD), "bias grad");
             return GPT2_OK;
         };

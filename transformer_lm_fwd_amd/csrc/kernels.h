@@ -38,6 +38,10 @@ struct GemmArgs {
     void* C2;
     const void* R;
     const float* bias;
+    // EPI_F32 with an m-contiguous A (bf16 only): if non-null, also receives the row
+    // sums of op(A) over k, rowsum[m] = sum_k op(A)[m, k] (fp32, overwritten) - the
+    // bias gradient of a weight-gradient product dW = dY^T X.
+    float* rowsum;
     int M, N, K;
     int64_t lda, ldb, ldc;
 };
@@ -87,7 +91,8 @@ hipError_t token_census_reset(int* first, int* count, int V, hipStream_t s);
 hipError_t adamw(float* p, const float* g, float* m, float* v, bf16* p16, int64_t n, float lr, float b1, float b2,
                  float eps, float wd, float c1, float c2, hipStream_t s);
 hipError_t cast_bf16(bf16* out, const float* in, int64_t n, hipStream_t s);
-hipError_t splitk_reduce(float* out, const float* ws, int splits, int64_t n, hipStream_t s);
+// out[i] = sum over k < splits of ws[k * stride + i], i < n (fixed order).
+hipError_t splitk_reduce(float* out, const float* ws, int splits, int64_t n, int64_t stride, hipStream_t s);
 // C (bf16 [M, N], row stride ldc) = bias + sum of `splits` dense fp32 M x N partials.
 hipError_t splitk_reduce_bf16(bf16* C, int64_t ldc, const float* ws, int splits, int M, int N, const float* bias,
                               hipStream_t s);

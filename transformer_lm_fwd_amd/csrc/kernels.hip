@@ -609,32 +609,35 @@ hipError_t cast_bf16(bf16* out, const float* in, int64_t n, hipStream_t s) {
 
 // out[i] = sum over k of ws[k * n + i], in split order (deterministic); four
 // elements per thread when n % 4 == 0.
-__global__ __launch_bounds__(256) void splitk_reduce_kernel(float* out, const float* ws, int splits, int64_t n) {
-    const int64_t stride = (int64_t)gridDim.x * 256;
-    if ((n & 3) == 0) {
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(float* out, const float* ws, int splits, int64_t n,
+                                                            int64_t ld, bool vec4) {
+    const int64_t step = (int64_t)gridDim.x * 256;
+    if (vec4) {  // n, ld multiples of 4 and both pointers 16-byte aligned
         const int64_t n4 = n >> 2;
-        for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += stride) {
+        for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += step) {
             float4 acc = ((const float4*)ws)[i];
             for (int k = 1; k < splits; ++k) {
-                const float4 v = ((const float4*)(ws + (int64_t)k * n))[i];
+                const float4 v = ((const float4*)(ws + (int64_t)k * ld))[i];
                 acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
             }
             ((float4*)out)[i] = acc;
         }
         return;
     }
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += step) {
         float acc = 0.f;
-        for (int k = 0; k < splits; ++k) acc += ws[(int64_t)k * n + i];
+        for (int k = 0; k < splits; ++k) acc += ws[(int64_t)k * ld + i];
         out[i] = acc;
     }
 }
 
-hipError_t splitk_reduce(float* out, const float* ws, int splits, int64_t n, hipStream_t s) {
-    int64_t blocks = ((n & 3) == 0 ? n / 4 : n + 255) / 256 + 1;
+hipError_t splitk_reduce(float* out, const float* ws, int splits, int64_t n, int64_t stride, hipStream_t s) {
+    const bool vec4 = n % 4 == 0 && stride % 4 == 0 && (uintptr_t)out % 16 == 0 && (uintptr_t)ws % 16 == 0;
+    int64_t blocks = (vec4 ? n / 4 : n + 255) / 256 + 1;
     if (blocks > 4096) blocks = 4096;
     ProfScope prof(s, "splitk_reduce", 0, 4.0 * (splits + 1) * n);
-    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, s, out, ws, splits, n);
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, s, out, ws, splits, n, stride,
+                       vec4);
     return hipGetLastError();
 }
 
