@@ -231,7 +231,7 @@ __global__ __launch_bounds__(256) void colsum_stage2_kernel(float* out0, float* 
     const int c = blockIdx.x * 16 + cl;
     float acc = 0.f;
     if (c < W) {
-#pragma unroll 4
+#pragma unroll 16
         for (int k = kl; k < nb; k += 16) acc += partial[(int64_t)k * W + c];
     }
     __shared__ float red[16][16];
@@ -292,13 +292,138 @@ hipError_t layernorm_param_grads(float* dw, float* db, const T* dout, const T* i
     return colsum<T, true>(dw, db, dout, inp, stats, N, C, C, partial, partial_floats, s, "layernorm_bwd_dwdb");
 }
 
+// dx and the parameter-gradient partials in one pass: each of the 8 waves takes RPW
+// rows (row = (block * RPW + i) * 8 + wave), computing dx as above while it adds
+// dy * xhat and dy into per-lane column sums; the loads of row i + 1 are issued
+// before row i is reduced.  The block's eight wave sums (added in a fixed order)
+// form partial row blockIdx.x = [sum dy * xhat (C) | sum dy (C)]; the second
+// column-sum stage adds the partial rows.
+template <class T, int MAXCH, int RPW>
+__global__ __launch_bounds__(512) void layernorm_backward_fused_kernel(T* dres, float* partial, const T* dres_in,
+                                                                       const T* dout, const T* inp,
+                                                                       const float* stats, const float* w, int N,
+                                                                       int C) {
+    constexpr int KV = Vec16<T>::N;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    float wv[MAXCH][KV], aw[MAXCH][KV], ab[MAXCH][KV];
+#pragma unroll
+    for (int ch = 0; ch < MAXCH; ++ch) {
+        const int c = (ch * 64 + lane) * KV;
+#pragma unroll
+        for (int e = 0; e < KV; ++e) {
+            aw[ch][e] = ab[ch][e] = 0.f;
+            wv[ch][e] = 0.f;
+        }
+        if (c < C) {
+#pragma unroll
+            for (int e = 0; e < KV; e += 4) *(float4*)&wv[ch][e] = *(const float4*)(w + c + e);
+        }
+    }
+    const u32x4 z4 = {0u, 0u, 0u, 0u};
+    u32x4 rg[MAXCH], rx[MAXCH], rp[MAXCH];  // raw dy, x, residual gradient of the current row
+    auto issue = [&](int row) {
+#pragma unroll
+        for (int ch = 0; ch < MAXCH; ++ch) {
+            const int c = (ch * 64 + lane) * KV;
+            const bool ok = row < N && c < C;
+            rg[ch] = ok ? ld16(dout + (int64_t)row * C + c) : z4;
+            rx[ch] = ok ? ld16(inp + (int64_t)row * C + c) : z4;
+            rp[ch] = (ok && dres_in) ? ld16(dres_in + (int64_t)row * C + c) : z4;
+        }
+    };
+    const int row0 = blockIdx.x * RPW * 8 + wave;
+    issue(row0);
+#pragma unroll 1
+    for (int i = 0; i < RPW; ++i) {
+        const int row = row0 + 8 * i;
+        float g[MAXCH][KV], xh[MAXCH][KV], prev[MAXCH][KV];
+#pragma unroll
+        for (int ch = 0; ch < MAXCH; ++ch) {
+            unpack16<T>(rg[ch], g[ch]);
+            unpack16<T>(rx[ch], xh[ch]);
+            unpack16<T>(rp[ch], prev[ch]);
+        }
+        if (i + 1 < RPW) issue(row + 8);
+        if (row >= N) break;  // wave-uniform; later rows are past the end too
+        const float mean = stats[2 * row], rstd = stats[2 * row + 1];
+        float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+        for (int ch = 0; ch < MAXCH; ++ch)
+#pragma unroll
+            for (int e = 0; e < KV; ++e) {  // lanes past C hold zeros and add nothing
+                xh[ch][e] = (xh[ch][e] - mean) * rstd;
+                aw[ch][e] += g[ch][e] * xh[ch][e];
+                ab[ch][e] += g[ch][e];
+                g[ch][e] *= wv[ch][e];  // dxhat
+                s1 += g[ch][e];
+                s2 += g[ch][e] * xh[ch][e];
+            }
+        s1 = wave_sum(s1) / C;
+        s2 = wave_sum(s2) / C;
+        T* dx = dres + (int64_t)row * C;
+#pragma unroll
+        for (int ch = 0; ch < MAXCH; ++ch) {
+            const int c = (ch * 64 + lane) * KV;
+            if (c < C) {
+                float o[KV];
+#pragma unroll
+                for (int e = 0; e < KV; ++e) o[e] = rstd * (g[ch][e] - s1 - xh[ch][e] * s2) + prev[ch][e];
+                st16(dx + c, pack16<T>(o));
+            }
+        }
+    }
+    __shared__ float red[8][2][MAXCH * 64 * KV];
+#pragma unroll
+    for (int ch = 0; ch < MAXCH; ++ch)
+#pragma unroll
+        for (int e = 0; e < KV; ++e) {
+            red[wave][0][(ch * 64 + lane) * KV + e] = aw[ch][e];
+            red[wave][1][(ch * 64 + lane) * KV + e] = ab[ch][e];
+        }
+    __syncthreads();
+    float* out = partial + (int64_t)blockIdx.x * 2 * C;
+    for (int i = threadIdx.x; i < 2 * C; i += 512) {
+        const int sidx = i / C, c = i % C;
+        out[i] = ((red[0][sidx][c] + red[1][sidx][c]) + (red[2][sidx][c] + red[3][sidx][c])) +
+                 ((red[4][sidx][c] + red[5][sidx][c]) + (red[6][sidx][c] + red[7][sidx][c]));
+    }
+}
+
 template <class T>
 hipError_t layernorm_backward(T* dres, const T* dres_in, float* dw, float* db, const T* dout, const T* inp,
                               const float* stats, const float* w, int N, int C, float* partial, size_t partial_floats,
                               hipStream_t s) {
-    hipError_t e = layernorm_backward_dx<T>(dres, dres_in, dout, inp, stats, w, N, C, s);
+    constexpr int KV = Vec16<T>::N;
+    const int ch = cdiv(C, 64 * KV);
+    // rows per wave: about 256 blocks for the step's 8192 rows, fewer rows for small inputs
+    int rpw = 1;
+    while (rpw < 4 && (int64_t)cdiv(N, 8 * rpw) > 256) rpw *= 2;
+    while ((size_t)cdiv(N, 8 * rpw) * 2 * C > partial_floats && rpw < 64) rpw *= 2;
+    const int nb = cdiv(N, 8 * rpw);
+    if ((size_t)nb * 2 * C > partial_floats || ch > 2 || (rpw != 1 && rpw != 2 && rpw != 4)) {
+        hipError_t e = layernorm_backward_dx<T>(dres, dres_in, dout, inp, stats, w, N, C, s);
+        if (e != hipSuccess) return e;
+        return layernorm_param_grads<T>(dw, db, dout, inp, stats, N, C, partial, partial_floats, s);
+    }
+    {
+        ProfScope prof(s, "layernorm_bwd", 0, (double)N * C * sizeof(T) * (dres_in ? 4 : 3) + 8.0 * N + 8.0 * nb * C);
+#define LNB_LAUNCH(MC, R)                                                                                             \
+    hipLaunchKernelGGL((layernorm_backward_fused_kernel<T, MC, R>), dim3(nb), dim3(512), 0, s, dres, partial, dres_in, \
+                       dout, inp, stats, w, N, C)
+#define LNB_RPW(MC)                            \
+    if (rpw == 1) LNB_LAUNCH(MC, 1);           \
+    else if (rpw == 2) LNB_LAUNCH(MC, 2);      \
+    else LNB_LAUNCH(MC, 4);
+        if (ch <= 1) { LNB_RPW(1) }
+        else { LNB_RPW(2) }
+#undef LNB_RPW
+#undef LNB_LAUNCH
+    }
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return layernorm_param_grads<T>(dw, db, dout, inp, stats, N, C, partial, partial_floats, s);
+    ProfScope prof2(s, "colsum_stage2", 0, 4.0 * nb * 2 * C + 8.0 * C);
+    hipLaunchKernelGGL(colsum_stage2_kernel, dim3(cdiv(2 * C, 16)), dim3(256), 0, s, dw, db, partial, nb, 2 * C, C);
+    return hipGetLastError();
 }
 
 // ============================================================================ bias gradients
