@@ -443,7 +443,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a, int
         for (int j = 0; j < TN; ++j) frag_offsets<BKC, BN>(lane, (wn * TN + j) * 32, ks, fb[j][ks]);
     }
     // Fragments of k-slice ks + 1 are read while the MFMAs of slice ks run.
-    auto compute = [&](const bf16* st) {
+    // `dma(ks)` issues the share of the next tile's loads that goes with k-slice ks.
+    auto compute = [&](const bf16* st, auto&& dma) {
         u32x4 xa[2][TM], xb[2][TN];
 #pragma unroll
         for (int i = 0; i < TM; ++i) xa[0][i] = frag_read<AK>(st, fa[i][0]);
@@ -458,6 +459,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a, int
 #pragma unroll
                 for (int j = 0; j < TN; ++j) xb[nb][j] = frag_read<BKC>(st + SA, fb[j][ks + 1]);
             }
+            dma(ks);
             __builtin_amdgcn_sched_barrier(0);  // keep those reads ahead of this slice's MFMAs
 #pragma unroll
             for (int i = 0; i < TM; ++i)
@@ -494,13 +496,24 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a, int
         if (kt + ST - 2 < nk) wait_loads<LPT * (ST - 2)>();
         else wait_loads<0>();
         __builtin_amdgcn_s_barrier();
-        if (kt + ST - 1 < nk) {
-            const int st = cur == 0 ? ST - 1 : cur - 1;
-            const uint32_t nxt = lbase + (uint32_t)(st * STAGE * 2);
-            const uint32_t k1 = (uint32_t)(kbeg + (kt + ST - 1) * GBK);
-            dma_issue<TA::PW, NW>(ra, nxt, ta.voff, k1 * ta.kstep);
-            dma_issue<TB::PW, NW>(rb, nxt + SA * 2, tb.voff, k1 * tb.kstep);
-        }
+        // The next tile's loads: with three or more stages they go out spread over this
+        // tile's k-slices (evening out the load and LDS-write traffic); with two, the
+        // one tile of slack is needed and they all go out first.
+        constexpr int SPREAD = ST >= 3 ? GBK / 16 : 1;
+        const bool more = kt + ST - 1 < nk;
+        const int nst = cur == 0 ? ST - 1 : cur - 1;
+        const uint32_t nxt = lbase + (uint32_t)(nst * STAGE * 2);
+        const uint32_t k1 = (uint32_t)(kbeg + (kt + ST - 1) * GBK);
+        auto dma = [&](int ks) {
+            if (!more) return;
+#pragma unroll
+            for (int j = 0; j < TA::PW; ++j)
+                if (j % SPREAD == ks) dma16(ra, nxt + (uint32_t)(NW * j) * 1024u, ta.voff[j], k1 * ta.kstep);
+#pragma unroll
+            for (int j = 0; j < TB::PW; ++j)
+                if ((TA::PW + j) % SPREAD == ks)
+                    dma16(rb, nxt + (uint32_t)(SA * 2 + NW * j * 1024), tb.voff[j], k1 * tb.kstep);
+        };
         if constexpr (RS) {
             if (do_rs) {
                 const bf16* at = lds + cur * STAGE;
@@ -515,7 +528,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a, int
                 }
             }
         }
-        compute(lds + cur * STAGE);
+        compute(lds + cur * STAGE, dma);
         cur = cur + 1 == ST ? 0 : cur + 1;
     }
     __syncthreads();
