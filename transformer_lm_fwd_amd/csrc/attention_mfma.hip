@@ -20,11 +20,27 @@
 //    ds_read_b64_tr_b16.
 //  * The backward pass is two kernels -- dK/dV over key tiles and dQ over query
 //    tiles -- each writing its outputs once: no atomics, deterministic.
+#include <type_traits>
+#include <utility>
+
 #include "kernels.h"
 #include "lds_dma.h"
 
 namespace gpt2 {
 namespace {
+
+// Runs tile(it, std::integral_constant<int, it % NST>{}) for it = 0 .. n-1: the loop
+// is unrolled NST times so that the LDS stage of each copy is a constant (its
+// fragment addresses fold into the instructions' immediate offsets).
+template <int NST, class F, int... S>
+__device__ __forceinline__ void stage_loop_impl(int n, F&& tile, std::integer_sequence<int, S...>) {
+    int it = 0;
+    for (; it + NST <= n; it += NST) (tile(it + S, std::integral_constant<int, S>{}), ...);
+    ((it + S < n ? tile(it + S, std::integral_constant<int, S>{}) : void()), ...);
+}
+template <int NST, class F> __device__ __forceinline__ void stage_loop(int n, F&& tile) {
+    stage_loop_impl<NST>(n, tile, std::make_integer_sequence<int, NST>{});
+}
 
 constexpr int HS = 64;  // head size handled here
 constexpr float LOG2E = 1.4426950408889634f;
@@ -130,9 +146,10 @@ struct FragT {
 // ============================================================================ forward
 // Block: 128 queries (4 waves x 32).  Key tiles of 64 rows go from global memory
 // straight into LDS (K and V, each [key][d], 8 KB) through a ring of FST stages,
-// so up to FST-1 tiles are in flight while one is used.  K fragments are read
+// so up to FST-1 tiles are in flight while one is used; two stages (32 KB) leave
+// room for four blocks per CU.  K fragments are read
 // row-wise (ds_read_b128), V^T fragments with transposed reads.
-constexpr int FST = 3;
+constexpr int FST = 2;
 
 __global__ __launch_bounds__(256) void attn_fwd_mfma64(bf16* out, float* lse, const bf16* qkv, int T, int C, int NH) {
     __shared__ __attribute__((aligned(1024))) bf16 sbuf[FST][2][64 * 64];  // [stage][K | V]
@@ -167,17 +184,16 @@ __global__ __launch_bounds__(256) void attn_fwd_mfma64(bf16* out, float* lse, co
 #pragma unroll
     for (int s0 = 0; s0 < FST - 1; ++s0)
         if (s0 < ntiles) issue(s0, s0);
-    int cur = 0;
-    for (int it = 0; it < ntiles; ++it) {
+    stage_loop<FST>(ntiles, [&](int it, auto stage) {
+        constexpr int cur = decltype(stage)::value;
         if (it + FST - 2 < ntiles) wait_loads<TileDma::PW * 2 * (FST - 2)>();
         else wait_loads<0>();
         __builtin_amdgcn_s_barrier();
         if (it + FST - 1 < ntiles) issue(it + FST - 1, cur == 0 ? FST - 1 : cur - 1);
         const bf16* sK = sbuf[cur][0];
         const bf16* sV = sbuf[cur][1];
-        cur = cur + 1 == FST ? 0 : cur + 1;
         const int k0 = 64 * it;
-        if (qw >= T || k0 > qw + 31) continue;  // no key of this tile is visible to this wave
+        if (qw >= T || k0 > qw + 31) return;  // no key of this tile is visible to this wave
         const bool edge = (k0 + 63 > qw) || (k0 + 64 > T);
         float x[32];  // raw scores; -inf where masked
 #pragma unroll
@@ -227,7 +243,7 @@ __global__ __launch_bounds__(256) void attn_fwd_mfma64(bf16* out, float* lse, co
 #pragma unroll
             for (int dt = 0; dt < 2; ++dt) o[dt] = mfma32(fv.read(sV, dt, s4), pk, o[dt]);
         }
-    }
+    });
     l += __shfl_xor(l, 32, 64);
     if (myq < T) {
         const float inv = 1.0f / l;
@@ -256,8 +272,10 @@ constexpr int BST = 3;  // LDS stages of the backward kernels
 // column (A = Q / dO rows, B = this lane's K / V row); dV += P^T dO and
 // dK += dS^T Q take P^T / dS^T as A operands and dO^T / Q^T (transposed reads of
 // the same tiles) as B operands.
-__global__ __launch_bounds__(256) void attn_bwd_dkdv_mfma64(bf16* dqkv, const bf16* qkv, const bf16* dout,
-                                                            const float2* LD, int T, int C, int NH) {
+// Register budget for three waves per SIMD (170 VGPRs; the kernel would otherwise
+// take ~180 and run two).
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void attn_bwd_dkdv_mfma64(
+    bf16* dqkv, const bf16* qkv, const bf16* dout, const float2* LD, int T, int C, int NH) {
     __shared__ __attribute__((aligned(1024))) bf16 sbuf[BST][2][64 * 64];  // [stage][Q | dO]
     __shared__ __attribute__((aligned(1024))) float sLD[BST][256];         // [stage][{L, D} x 64, copy]
     const int kt = blockIdx.y;  // the first key tiles see the most queries: dispatched first
