@@ -196,6 +196,65 @@ int gpt2_profile(int enable);
  * Errors: GPT2_E_HIP if an event cannot be read. */
 int gpt2_profile_read(gpt2_kernel_stat* out, int32_t max_entries, int32_t* n_entries);
 
+/* ---------------------------------------------------------------- generation
+ * Incremental next-token prediction with a key/value cache
+ * ("GPT-2ベースの3000バイトCで実装されたChatGPTクローン", KVキャッシュ方式: after N tokens
+ * have been run, token N+1 needs only its own row; the earlier rows' results are kept
+ * where they were written instead of being recomputed).  A generation state borrows
+ * an arena's parameters (bf16 arenas with head size 64) and keeps, in its own
+ * caller-owned device memory, the q|k|v rows of every layer for `batch` sequences of
+ * up to `max_len` tokens ([L][batch][max_len][3C] bf16) plus the decode scratch.
+ * All sequences of a state advance together (one shared length). */
+typedef struct gpt2_gen gpt2_gen; /* opaque host-side handle */
+
+/* Lays out a generation state over `arena`.
+ *  batch        1..16 sequences; max_len 1..cfg.max_seq_len positions.
+ *  device_base  caller-owned device memory (256-byte aligned) or NULL to only query
+ *               the size (*required_bytes); it must outlive the handle.  No
+ *               zero-filling is needed.
+ * The arena must outlive the handle.  Errors: GPT2_E_INVAL (NULL arena, fp32 arena,
+ * head size other than 64, batch or max_len out of range, out NULL), GPT2_E_ALIGN,
+ * GPT2_E_SIZE (device_bytes too small). */
+int gpt2_gen_alloc(gpt2_arena* arena, int32_t batch, int32_t max_len, void* device_base, size_t device_bytes,
+                   size_t* required_bytes, gpt2_gen** out);
+
+/* Frees the host handle only (never device memory). */
+int gpt2_gen_free(gpt2_gen* gen);
+
+/* Current length of the cached sequences (0 before the first prefill; -1 for NULL). */
+int gpt2_gen_length(const gpt2_gen* gen);
+
+/* Runs the prompt d_tokens (device int32 [batch, n], row-major) through the full
+ * forward pass in the arena's activation buffers (needs batch * n <= arena B * T;
+ * the arena's training activations are overwritten, so a later gpt2_backward needs
+ * a new gpt2_forward with targets), copies every layer's q|k|v rows into the cache,
+ * sets the length to n, and writes the next-token logits of each sequence (position
+ * n - 1, the forward pass's bf16 logits widened) to d_logits (device fp32 [batch, V]).
+ * Errors: GPT2_E_INVAL (NULL argument), GPT2_E_SIZE (n outside 1..max_len or too many
+ * rows for the arena), GPT2_E_HIP. */
+int gpt2_gen_prefill(gpt2_gen* gen, const int32_t* d_tokens, int32_t n, float* d_logits, void* stream);
+
+/* Appends one token per sequence (d_tokens: device int32 [batch]) at position
+ * length: runs that row through every layer (its q|k|v row is written into the
+ * cache, attention reads cache rows 0..length), writes the next-token logits
+ * (device fp32 [batch, V], fp32 accumulation, no bf16 rounding) and increments the
+ * length.  Errors: GPT2_E_INVAL (NULL argument), GPT2_E_STATE (no prefill yet),
+ * GPT2_E_SIZE (length == max_len), GPT2_E_HIP. */
+int gpt2_gen_decode(gpt2_gen* gen, const int32_t* d_tokens, float* d_logits, void* stream);
+
+/* Top-k sampling on the host ("GPT-2 from scratch with torch", 生成样本: keep the k
+ * highest logits, softmax over them, draw one token).  For each of `rows` rows of
+ * host fp32 logits (row stride ld >= V): rank the tokens by logit (equal logits: the
+ * lower id first; NaN ranks last), keep the first min(k, V), weight them
+ * w_i = exp((z_i - z_max) / temperature) in double precision, and return the first
+ * kept token, in rank order, whose running weight sum exceeds uniforms[r] * sum(w).
+ * A leading logit that is not finite returns the leader.  uniforms: host fp32 [rows]
+ * in [0, 1) (the caller's random numbers); tokens_out: host int32 [rows].
+ * Errors: GPT2_E_INVAL for NULL pointers, rows < 0, V < 1, ld < V, k < 1,
+ * temperature not finite and > 0, or a uniform outside [0, 1). */
+int gpt2_sample_topk(const float* logits, int32_t rows, int32_t V, int64_t ld, int32_t k, float temperature,
+                     const float* uniforms, int32_t* tokens_out);
+
 /* Message for the last non-OK status on this thread ("" if none). */
 const char* gpt2_last_error(void);
 

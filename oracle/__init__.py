@@ -4,10 +4,13 @@ Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package.  The GPU library never imports it, and it
 imports nothing from the GPU library.
 
-Parity status of each oracle function (pins live in tests/test_oracle_pins.py):
-every forward layer, every backward formula and the AdamW update are pinned
-(closed forms, printed integers, invariants, central finite differences and an
-independent autograd cross-check); nothing here is "parity unpinned".
+Parity status of each oracle function (pins live in tests/test_oracle_pins.py and
+tests/test_sampling.py): every forward layer, every backward formula, the AdamW
+update and top-k sampling are pinned (closed forms, printed integers, invariants,
+central finite differences and an independent autograd cross-check); nothing here
+is "parity unpinned".  Incremental generation has no function of its own here: the
+next-token logits after a prefix are the forward pass's logits at the prefix's last
+position.
 """
 from __future__ import annotations
 
@@ -174,3 +177,21 @@ class Oracle:
         self.backward()
         self.adamw(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, t)
         return loss
+
+
+def sample_topk(logits, k: int, temperature: float, u: float) -> int:
+    """Top-k sampling of one row ("GPT-2 from scratch with torch", 生成样本): keep the k
+    highest logits (equal logits: the lower token id first), turn them into
+    probabilities with a softmax at the given temperature, and draw by inverse
+    transform with the caller's uniform u in [0, 1): the first kept token, in
+    descending order, whose cumulative probability exceeds u."""
+    z = np.asarray(logits, dtype=np.float64).reshape(-1)
+    z = np.where(np.isnan(z), -np.inf, z)
+    order = np.lexsort((np.arange(z.size), -z))[:min(k, z.size)]  # by -z, then by id
+    top = z[order]
+    if not np.isfinite(top[0]):
+        return int(order[0])
+    w = np.exp((top - top[0]) / float(temperature))
+    cum = np.cumsum(w)
+    i = int(np.searchsorted(cum, float(np.float32(u)) * cum[-1], side="right"))
+    return int(order[min(i, order.size - 1)])

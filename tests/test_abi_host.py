@@ -123,3 +123,56 @@ def test_binding_refuses_out_of_range_token_ids_on_the_host():
         a._ids(np.array([[0, 1, -1], [0, 0, 0]]))
     with pytest.raises(ValueError):
         a._ids(np.zeros((3, 2), dtype=np.int32))
+
+
+def test_generation_state_validation_without_touching_memory():
+    b = _lib()
+    shape64 = synth.ModelShape(256, 301, 2, 2, 128)   # head size 64
+    h = ctypes.c_void_p()
+    need = ctypes.c_size_t()
+    lib = b.lib()
+    # fp32 arena: generation is refused
+    cfg = b.make_config(shape64)
+    n32 = b.arena_bytes(shape64, 2, 64, b.GPT2_FP32)
+    assert lib.gpt2_alloc_arena(ctypes.byref(cfg), 2, 64, 0, ctypes.c_void_p(1 << 40), n32, None, ctypes.byref(h)) == 0
+    try:
+        assert lib.gpt2_gen_alloc(h, 2, 64, None, 0, ctypes.byref(need), None) == -1
+    finally:
+        lib.gpt2_free_arena(h)
+    # bf16 arena with head size 16: refused
+    cfg16 = b.make_config(synth.GPT2_TINY_CHAR)
+    n16 = b.arena_bytes(synth.GPT2_TINY_CHAR, 2, 32, b.GPT2_BF16)
+    assert lib.gpt2_alloc_arena(ctypes.byref(cfg16), 2, 32, 1, ctypes.c_void_p(1 << 40), n16, None, ctypes.byref(h)) == 0
+    try:
+        assert lib.gpt2_gen_alloc(h, 1, 8, None, 0, ctypes.byref(need), None) == -1
+    finally:
+        lib.gpt2_free_arena(h)
+    nb = b.arena_bytes(shape64, 2, 64, b.GPT2_BF16)
+    assert lib.gpt2_alloc_arena(ctypes.byref(cfg), 2, 64, 1, ctypes.c_void_p(1 << 40), nb, None, ctypes.byref(h)) == 0
+    try:
+        assert lib.gpt2_gen_alloc(None, 2, 64, None, 0, ctypes.byref(need), None) == -1
+        for batch, max_len in [(0, 8), (17, 8), (2, 0), (2, 257)]:
+            assert lib.gpt2_gen_alloc(h, batch, max_len, None, 0, ctypes.byref(need), None) == -1, (batch, max_len)
+        # size query: the cache ([L][batch][max_len][3C] bf16) dominates and grows with both
+        assert lib.gpt2_gen_alloc(h, 2, 64, None, 0, ctypes.byref(need), None) == 0
+        n1 = need.value
+        assert n1 >= 2 * 2 * 64 * 3 * 128 * 2
+        assert lib.gpt2_gen_alloc(h, 4, 64, None, 0, ctypes.byref(need), None) == 0 and need.value > n1
+        g = ctypes.c_void_p()
+        assert lib.gpt2_gen_alloc(h, 2, 64, ctypes.c_void_p(1 << 41), n1 - 1, None, ctypes.byref(g)) == -2
+        assert lib.gpt2_gen_alloc(h, 2, 64, ctypes.c_void_p((1 << 41) + 64), n1, None, ctypes.byref(g)) == -3
+        assert not g.value
+        # a state over a fake address: only calls that fail validation are made with it
+        assert lib.gpt2_gen_alloc(h, 2, 64, ctypes.c_void_p(1 << 41), n1, None, ctypes.byref(g)) == 0
+        try:
+            assert lib.gpt2_gen_length(g) == 0
+            fake = ctypes.c_void_p(1 << 42)
+            assert lib.gpt2_gen_decode(g, fake, fake, None) == -4        # no prefill yet
+            assert lib.gpt2_gen_prefill(g, fake, 0, fake, None) == -2    # empty prompt
+            assert lib.gpt2_gen_prefill(g, fake, 65, fake, None) == -2   # longer than max_len
+            assert lib.gpt2_gen_prefill(g, None, 4, fake, None) == -1
+        finally:
+            lib.gpt2_gen_free(g)
+        assert lib.gpt2_gen_length(None) == -1
+    finally:
+        lib.gpt2_free_arena(h)

@@ -25,8 +25,9 @@ T_LN1, T_LN1_STATS, T_QKV, T_ATTY, T_ATT_LSE, T_RESIDUAL2 = 16, 17, 18, 19, 20, 
 T_LN2, T_LN2_STATS, T_FCH, T_FCH_GELU, T_RESIDUAL3 = 22, 23, 24, 25, 26
 
 EXPORTS = ("gpt2_alloc_arena", "gpt2_free_arena", "gpt2_sync_weights", "gpt2_forward", "gpt2_backward",
-           "gpt2_adamw_step", "gpt2_backward_adamw", "gpt2_tensor_info", "gpt2_num_parameters", "gpt2_profile", "gpt2_profile_read",
-           "gpt2_last_error")
+           "gpt2_adamw_step", "gpt2_backward_adamw", "gpt2_tensor_info", "gpt2_num_parameters", "gpt2_profile",
+           "gpt2_profile_read", "gpt2_gen_alloc", "gpt2_gen_free", "gpt2_gen_length", "gpt2_gen_prefill",
+           "gpt2_gen_decode", "gpt2_sample_topk", "gpt2_last_error")
 
 
 class gpt2_config(ctypes.Structure):
@@ -71,6 +72,12 @@ def lib():
         L.gpt2_last_error.restype = ctypes.c_char_p
         L.gpt2_profile.argtypes = [ctypes.c_int]
         L.gpt2_profile_read.argtypes = [ctypes.POINTER(gpt2_kernel_stat), i32, ctypes.POINTER(i32)]
+        L.gpt2_gen_alloc.argtypes = [vp, i32, i32, vp, sz, ctypes.POINTER(sz), ctypes.POINTER(vp)]
+        L.gpt2_gen_free.argtypes = [vp]
+        L.gpt2_gen_length.argtypes = [vp]
+        L.gpt2_gen_prefill.argtypes = [vp, vp, i32, vp, vp]
+        L.gpt2_gen_decode.argtypes = [vp, vp, vp, vp]
+        L.gpt2_sample_topk.argtypes = [vp, i32, i32, i64, i32, f32, vp, vp]
         for name in EXPORTS:
             if name not in ("gpt2_num_parameters", "gpt2_last_error"):
                 L[name].restype = ctypes.c_int
@@ -222,3 +229,85 @@ class Arena:
         else:
             self.backward()
             self.adamw_step(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, t)
+
+
+class Generator:
+    """Incremental generation with a key/value cache over an Arena's parameters
+    (bf16, head size 64): `batch` sequences of up to `max_len` tokens advancing
+    together.  prefill / decode return the next-token logits as a device fp32
+    tensor [batch, vocab_size]."""
+
+    def __init__(self, arena: Arena, batch: int, max_len: int):
+        import torch
+        self.arena, self.batch, self.max_len = arena, batch, max_len
+        need = ctypes.c_size_t(0)
+        _check(lib().gpt2_gen_alloc(arena.h, batch, max_len, None, 0, ctypes.byref(need), None))
+        self.nbytes = int(need.value)
+        self.buf = torch.empty(self.nbytes + 256, dtype=torch.uint8, device=arena.base.device)
+        pad = (-self.buf.data_ptr()) % 256
+        self.base = self.buf[pad:pad + self.nbytes]
+        h = ctypes.c_void_p()
+        _check(lib().gpt2_gen_alloc(arena.h, batch, max_len, ctypes.c_void_p(self.base.data_ptr()), self.nbytes,
+                                    None, ctypes.byref(h)))
+        self.h = h
+        self.logits = torch.empty(batch, arena.m.vocab_size, dtype=torch.float32, device=arena.base.device)
+        self._tok = None
+
+    def close(self):
+        if getattr(self, "h", None):
+            lib().gpt2_gen_free(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def length(self) -> int:
+        return int(lib().gpt2_gen_length(self.h))
+
+    def _ids(self, x, shape):
+        import torch
+        t = torch.as_tensor(x)
+        if t.dtype != torch.int32:
+            t = t.to(torch.int32)
+        if tuple(t.shape) != shape:
+            raise ValueError(f"token array must have shape {shape}, got {tuple(t.shape)}")
+        lo, hi = int(t.min()), int(t.max())
+        if lo < 0 or hi >= self.arena.m.vocab_size:
+            raise ValueError(f"token ids must lie in [0, {self.arena.m.vocab_size}), got [{lo}, {hi}]")
+        return t.to(self.base.device).contiguous()
+
+    def prefill(self, tokens, stream=None, check_ids=True):
+        """tokens [batch, n]; returns the logits of position n - 1 (device fp32)."""
+        t = self._ids(tokens, (self.batch, int(tokens.shape[1]))) if check_ids else tokens
+        self._tok = t
+        _check(lib().gpt2_gen_prefill(self.h, ctypes.c_void_p(t.data_ptr()), int(t.shape[1]),
+                                      ctypes.c_void_p(self.logits.data_ptr()), _stream_ptr(stream)))
+        return self.logits
+
+    def decode(self, tokens, stream=None, check_ids=True):
+        """tokens [batch] (the token at the current length); returns the next logits."""
+        t = self._ids(tokens, (self.batch,)) if check_ids else tokens
+        self._tok = t
+        _check(lib().gpt2_gen_decode(self.h, ctypes.c_void_p(t.data_ptr()), ctypes.c_void_p(self.logits.data_ptr()),
+                                     _stream_ptr(stream)))
+        return self.logits
+
+
+def sample_topk(logits, k: int, temperature: float, uniforms):
+    """gpt2_sample_topk on host arrays: logits float32 [rows, V] (C-contiguous rows),
+    uniforms float32 [rows] in [0, 1); returns int32 [rows]."""
+    import numpy as np
+    z = np.ascontiguousarray(logits, dtype=np.float32)
+    if z.ndim != 2:
+        raise ValueError("logits must be 2-D [rows, V]")
+    u = np.ascontiguousarray(uniforms, dtype=np.float32).reshape(-1)
+    if u.size != z.shape[0]:
+        raise ValueError("one uniform per row is required")
+    out = np.empty(z.shape[0], dtype=np.int32)
+    _check(lib().gpt2_sample_topk(z.ctypes.data, z.shape[0], z.shape[1], z.shape[1], k, temperature, u.ctypes.data,
+                                  out.ctypes.data))
+    return out

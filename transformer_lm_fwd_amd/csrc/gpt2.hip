@@ -4,6 +4,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
+#include <cmath>
 #include <new>
 #include <string>
 #include <vector>
@@ -55,6 +57,16 @@ struct gpt2_arena {
     hipEvent_t rd_res[4] = {}, rd_fch[2] = {}, rd_qkv[2] = {}, ev_wte = nullptr, ev_end = nullptr;
     hipEvent_t fork[8] = {};
     int fork_next = 0;
+};
+
+// Incremental generation over an arena's parameters (bf16): the key/value cache holds
+// every layer's q|k|v rows of each sequence, [L][batch][max_len][3C].
+struct gpt2_gen {
+    gpt2_arena* a;
+    int batch, max_len, len;
+    bool ready;
+    char* base;
+    size_t cache, res[3], ln, stats, atty, fchg, lnf;
 };
 
 namespace {
@@ -238,9 +250,12 @@ struct Model {
     hipStream_t s;
     int C, L, NH, V, Vp, B, S, BT, P;  // S: sequence length
 
-    Model(gpt2_arena* ar, hipStream_t st) : a(ar), s(st) {
+    Model(gpt2_arena* ar, hipStream_t st) : Model(ar, st, ar->B, ar->T) {}
+    // A forward pass over Be sequences of length Se in the arena's buffers (Be * Se <=
+    // B * T): rows stay dense, [Be * Se, .], so every kernel sees an ordinary batch.
+    Model(gpt2_arena* ar, hipStream_t st, int Be, int Se) : a(ar), s(st) {
         C = a->cfg.channels; L = a->cfg.num_layers; NH = a->cfg.num_heads; V = a->cfg.vocab_size;
-        Vp = a->Vp; B = a->B; S = a->T; BT = B * S; P = a->cfg.max_seq_len;
+        Vp = a->Vp; B = Be; S = Se; BT = B * S; P = a->cfg.max_seq_len;
     }
     float* master(int64_t off) const { return at<float>(a, a->params) + off; }
     float* grad(int64_t off) const { return at<float>(a, a->grads) + off; }
@@ -594,6 +609,188 @@ int gpt2_tensor_info(const gpt2_arena* a, int32_t id, int32_t layer, size_t* byt
     if (cols) *cols = c;
     if (row_stride) *row_stride = ld;
     if (dtype) *dtype = dt;
+    return GPT2_OK;
+}
+
+// ---------------------------------------------------------------- generation
+int gpt2_gen_alloc(gpt2_arena* a, int32_t batch, int32_t max_len, void* device_base, size_t device_bytes,
+                   size_t* required_bytes, gpt2_gen** out) {
+    if (out) *out = nullptr;
+    if (!a) return fail(GPT2_E_INVAL, "arena is NULL");
+    if (a->dtype != GPT2_BF16) return fail(GPT2_E_INVAL, "generation needs a bf16 arena");
+    if (a->hs != 64) return fail(GPT2_E_INVAL, "generation needs head size 64");
+    if (batch < 1 || batch > 16) return fail(GPT2_E_INVAL, "batch must be in 1..16");
+    if (max_len < 1 || max_len > a->cfg.max_seq_len) return fail(GPT2_E_INVAL, "max_len must be in 1..max_seq_len");
+    const size_t C = a->cfg.channels, L = a->cfg.num_layers, Bg = batch;
+    gpt2_gen g{};
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        const size_t r = o;
+        o = align_up(o + bytes);
+        return r;
+    };
+    g.cache = take(L * Bg * max_len * 3 * C * 2);
+    for (auto& r : g.res) r = take(Bg * C * 2);
+    g.ln = take(Bg * C * 2);
+    g.stats = take(Bg * 2 * 4);
+    g.atty = take(Bg * C * 2);
+    g.fchg = take(Bg * 4 * C * 2);
+    g.lnf = take(Bg * C * 2);
+    if (required_bytes) *required_bytes = o;
+    if (!device_base) return GPT2_OK;
+    if ((uintptr_t)device_base % kAlign) return fail(GPT2_E_ALIGN, "device_base must be 256-byte aligned");
+    if (device_bytes < o) return fail(GPT2_E_SIZE, "device buffer too small: need " + std::to_string(o) + " bytes");
+    if (!out) return fail(GPT2_E_INVAL, "out is NULL");
+    gpt2_gen* h = new (std::nothrow) gpt2_gen(g);
+    if (!h) return fail(GPT2_E_INVAL, "host allocation failed");
+    h->a = a;
+    h->batch = batch;
+    h->max_len = max_len;
+    h->len = 0;
+    h->ready = false;
+    h->base = (char*)device_base;
+    *out = h;
+    return GPT2_OK;
+}
+
+int gpt2_gen_free(gpt2_gen* g) {
+    delete g;
+    return GPT2_OK;
+}
+
+int gpt2_gen_length(const gpt2_gen* g) { return g ? g->len : -1; }
+
+int gpt2_gen_prefill(gpt2_gen* g, const int32_t* d_tokens, int32_t n, float* d_logits, void* stream) {
+    if (!g || !d_tokens || !d_logits) return fail(GPT2_E_INVAL, "generation state, tokens and logits are required");
+    gpt2_arena* a = g->a;
+    if (n < 1 || n > g->max_len) return fail(GPT2_E_SIZE, "prompt length must be in 1..max_len");
+    if ((int64_t)g->batch * n > (int64_t)a->B * a->T)
+        return fail(GPT2_E_SIZE, "batch * prompt length exceeds the arena's B * T rows");
+    hipStream_t s = (hipStream_t)stream;
+    g->ready = false;
+    a->loss_ready = false;  // the arena's activations now describe the prompt
+    a->inputs = nullptr;
+    Model<bf16> m(a, s, g->batch, n);
+    int rc = m.forward(d_tokens, nullptr);
+    if (rc) return rc;
+    const size_t C3 = 3 * (size_t)a->cfg.channels;
+    for (int l = 0; l < a->cfg.num_layers; ++l) {
+        char* dst = g->base + g->cache + (size_t)l * g->batch * g->max_len * C3 * 2;
+        if (hipMemcpy2DAsync(dst, (size_t)g->max_len * C3 * 2, at<bf16>(a, a->la[l].qkv), (size_t)n * C3 * 2,
+                             (size_t)n * C3 * 2, g->batch, hipMemcpyDeviceToDevice, s) != hipSuccess)
+            return fail(GPT2_E_HIP, "cache copy failed");
+    }
+    CHECK(logits_rows(d_logits, at<bf16>(a, a->logits), g->batch, a->cfg.vocab_size, a->Vp, n, n - 1, s), "logits");
+    g->len = n;
+    g->ready = true;
+    return GPT2_OK;
+}
+
+int gpt2_gen_decode(gpt2_gen* g, const int32_t* d_tokens, float* d_logits, void* stream) {
+    if (!g || !d_tokens || !d_logits) return fail(GPT2_E_INVAL, "generation state, tokens and logits are required");
+    if (!g->ready) return fail(GPT2_E_STATE, "decode needs a preceding prefill");
+    if (g->len >= g->max_len) return fail(GPT2_E_SIZE, "the cache is full (length == max_len)");
+    gpt2_arena* a = g->a;
+    hipStream_t s = (hipStream_t)stream;
+    const int C = a->cfg.channels, L = a->cfg.num_layers, NH = a->cfg.num_heads, V = a->cfg.vocab_size;
+    const int Bg = g->batch, t = g->len;
+    const int64_t C3 = 3 * (int64_t)C, row = (int64_t)g->max_len * C3;
+    auto buf = [&](size_t off) { return (bf16*)(g->base + off); };
+    const float* master = at<float>(a, a->params);
+    const bf16* w16 = at<bf16>(a, a->params16);
+    auto lp = [&](int l, int i) { return a->o_layer[l * P_N + i]; };
+    auto skinny = [&](const bf16* x, int64_t ldx, int64_t woff, int N, int K, void* Cout, int64_t ldc, bf16* C2,
+                      const bf16* R, const float* bias, int epi) -> int {
+        SkinnyArgs k{};
+        k.x = x; k.ldx = ldx; k.W = w16 + woff; k.ldw = K; k.C = Cout; k.ldc = ldc; k.C2 = C2;
+        k.R = R; k.ldr = C; k.bias = bias; k.M = Bg; k.N = N; k.K = K;
+        return hip_check(skinny_gemm(k, epi, s), "skinny gemm");
+    };
+    int rc;
+    // x = wte[token] + wpe[t] for the one new row of every sequence
+    CHECK(encoder_forward<bf16>(buf(g->res[0]), d_tokens, master + a->o_wte, master + a->o_wpe, Bg, 1, C, s, t),
+          "encoder");
+    int cur = 0;
+    for (int l = 0; l < L; ++l) {
+        bf16* xin = buf(g->res[cur]);
+        bf16* res2 = buf(g->res[(cur + 1) % 3]);
+        bf16* res3 = buf(g->res[(cur + 2) % 3]);
+        bf16* cache = buf(g->cache) + (int64_t)l * Bg * row;
+        float* st = (float*)(g->base + g->stats);
+        CHECK(layernorm_forward<bf16>(buf(g->ln), st, xin, master + lp(l, P_LN1W), master + lp(l, P_LN1B), Bg, C, s),
+              "ln1");
+        // q|k|v of the new rows straight into cache row t of each sequence
+        if ((rc = skinny(buf(g->ln), C, lp(l, P_QKVW), 3 * C, C, cache + (int64_t)t * C3, row, nullptr, nullptr,
+                         master + lp(l, P_QKVB), EPI_BIAS)))
+            return rc;
+        CHECK(attention_decode(buf(g->atty), cache, Bg, t + 1, C, NH, row, s), "attention");
+        if ((rc = skinny(buf(g->atty), C, lp(l, P_PROJW), C, C, res2, C, nullptr, xin, master + lp(l, P_PROJB),
+                         EPI_BIAS_RES)))
+            return rc;
+        CHECK(layernorm_forward<bf16>(buf(g->ln), st, res2, master + lp(l, P_LN2W), master + lp(l, P_LN2B), Bg, C, s),
+              "ln2");
+        if ((rc = skinny(buf(g->ln), C, lp(l, P_FCW), 4 * C, C, nullptr, 4 * C, buf(g->fchg), nullptr,
+                         master + lp(l, P_FCB), EPI_BIAS_GELU)))
+            return rc;
+        if ((rc = skinny(buf(g->fchg), 4 * C, lp(l, P_FCPW), C, 4 * C, res3, C, nullptr, res2,
+                         master + lp(l, P_FCPB), EPI_BIAS_RES)))
+            return rc;
+        cur = (cur + 2) % 3;
+    }
+    CHECK(layernorm_forward<bf16>(buf(g->lnf), (float*)(g->base + g->stats), buf(g->res[cur]), master + a->o_lnfw,
+                                  master + a->o_lnfb, Bg, C, s),
+          "lnf");
+    // next-token logits (tied lm_head), fp32 [batch, V]
+    if ((rc = skinny(buf(g->lnf), C, a->o_wte, V, C, d_logits, V, nullptr, nullptr, nullptr, EPI_F32))) return rc;
+    g->len = t + 1;
+    return GPT2_OK;
+}
+
+// Host-side top-k sampling ("GPT-2 from scratch with torch", 生成样本): keep the k largest
+// logits of a row (equal logits: the lower token id first), weight them by
+// exp((z - z_max) / temperature), and take the first of them, in descending order,
+// whose running sum of weights exceeds u * (sum of weights).
+int gpt2_sample_topk(const float* logits, int32_t rows, int32_t V, int64_t ld, int32_t k, float temperature,
+                     const float* uniforms, int32_t* tokens_out) {
+    if (!logits || !uniforms || !tokens_out) return fail(GPT2_E_INVAL, "logits, uniforms and tokens_out are required");
+    if (rows < 0 || V < 1 || ld < V) return fail(GPT2_E_INVAL, "bad logits shape");
+    if (k < 1) return fail(GPT2_E_INVAL, "k must be >= 1");
+    if (!(temperature > 0.f) || !std::isfinite(temperature)) return fail(GPT2_E_INVAL, "temperature must be > 0");
+    const int kk = std::min(k, V);
+    std::vector<int32_t> idx(V);
+    for (int32_t r = 0; r < rows; ++r) {
+        const float u = uniforms[r];
+        if (!(u >= 0.f && u < 1.f)) return fail(GPT2_E_INVAL, "uniforms must lie in [0, 1)");
+        const float* z = logits + (int64_t)r * ld;
+        auto key = [&](int32_t i) { return std::isnan(z[i]) ? -INFINITY : z[i]; };  // NaN ranks last
+        for (int32_t i = 0; i < V; ++i) idx[i] = i;
+        std::partial_sort(idx.begin(), idx.begin() + kk, idx.end(), [&](int32_t x, int32_t y) {
+            const float a = key(x), b = key(y);
+            return a > b || (a == b && x < y);
+        });
+        const double zmax = key(idx[0]);
+        if (!std::isfinite(zmax)) {  // an infinite logit leads, or nothing is finite: take the leader
+            tokens_out[r] = idx[0];
+            continue;
+        }
+        std::vector<double> w(kk);
+        double total = 0.0;
+        for (int i = 0; i < kk; ++i) {
+            w[i] = std::exp(((double)key(idx[i]) - zmax) / (double)temperature);
+            total += w[i];
+        }
+        const double target = (double)u * total;
+        double run = 0.0;
+        int32_t pick = idx[kk - 1];
+        for (int i = 0; i < kk; ++i) {
+            run += w[i];
+            if (run > target) {
+                pick = idx[i];
+                break;
+            }
+        }
+        tokens_out[r] = pick;
+    }
     return GPT2_OK;
 }
 

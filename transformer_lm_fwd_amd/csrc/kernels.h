@@ -55,7 +55,7 @@ hipError_t gemm(const GemmArgs& a, bool a_kcontig, bool b_kcontig, int epi, floa
 // ---------------------------------------------------------------- element-wise / row kernels
 template <class T>
 hipError_t encoder_forward(T* out, const int32_t* tok, const float* wte, const float* wpe, int BT, int T_, int C,
-                           hipStream_t s);
+                           hipStream_t s, int pos0 = 0);
 template <class T>
 hipError_t layernorm_forward(T* out, float* stats, const T* inp, const float* w, const float* b, int N, int C,
                              hipStream_t s);
@@ -111,5 +111,32 @@ hipError_t attention_forward_mfma64(bf16* out, float* lse, const bf16* qkv, int 
                                     hipStream_t s);
 hipError_t attention_backward_mfma64(bf16* dqkv, float* dsum, const bf16* dout, const bf16* out, const bf16* qkv,
                                      const float* lse, int B, int T_, int C, int NH, hipStream_t s);
+
+// ---------------------------------------------------------------- generation (bf16)
+// Skinny product for the rows of a decode step: C[m, n] = epilogue(sum_k x[m, k] W[n, k]),
+// M <= 16, W [N, K] row-major; epilogues EPI_BIAS, EPI_BIAS_RES (+ R[m, n], row stride
+// ldr), EPI_BIAS_GELU (C = pre-activation if non-null, C2 = gelu, both row stride ldc)
+// and EPI_F32 (fp32 C = acc + bias).  K, ldx, ldw multiples of 8.
+struct SkinnyArgs {
+    const bf16* x;
+    int64_t ldx;
+    const bf16* W;
+    int64_t ldw;
+    void* C;
+    int64_t ldc;
+    bf16* C2;
+    const bf16* R;
+    int64_t ldr;
+    const float* bias;
+    int M, N, K;
+};
+hipError_t skinny_gemm(const SkinnyArgs& a, int epi, hipStream_t s);
+// y [batch, C] = attention of the query in cache row len-1 of each sequence over cache
+// rows 0 .. len-1 (q | k | v rows of 3C, sequence b at cache + b * bstride); head size 64.
+hipError_t attention_decode(bf16* y, const bf16* cache, int batch, int len, int C, int NH, int64_t bstride,
+                            hipStream_t s);
+// out fp32 [R, V] = rows (r * row_stride + row_offset) of bf16 logits with row stride ldl.
+hipError_t logits_rows(float* out, const bf16* logits, int R, int V, int64_t ldl, int row_stride, int row_offset,
+                       hipStream_t s);
 
 }  // namespace gpt2

@@ -12,12 +12,12 @@ static inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 // Reads the fp32 master tables and rounds once to the activation type.
 template <class T>
 __global__ __launch_bounds__(256) void encoder_forward_kernel(T* out, const int32_t* tok, const float* wte,
-                                                              const float* wpe, int BT, int T_, int C) {
+                                                              const float* wpe, int BT, int T_, int C, int pos0) {
     const int c4 = C / 4;
     int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= (int64_t)BT * c4) return;
     int row = (int)(i / c4), c = (int)(i % c4) * 4;
-    int t = row % T_;
+    int t = pos0 + row % T_;
     float4 a = *(const float4*)(wte + (int64_t)tok[row] * C + c);
     float4 p = *(const float4*)(wpe + (int64_t)t * C + c);
     T* o = out + (int64_t)row * C + c;
@@ -29,10 +29,10 @@ __global__ __launch_bounds__(256) void encoder_forward_kernel(T* out, const int3
 
 template <class T>
 hipError_t encoder_forward(T* out, const int32_t* tok, const float* wte, const float* wpe, int BT, int T_, int C,
-                           hipStream_t s) {
+                           hipStream_t s, int pos0) {
     ProfScope prof(s, "encoder_fwd", 0, (double)BT * C * (8 + sizeof(T)));
     hipLaunchKernelGGL(encoder_forward_kernel<T>, dim3(cdiv((int64_t)BT * (C / 4), 256)), dim3(256), 0, s, out, tok,
-                       wte, wpe, BT, T_, C);
+                       wte, wpe, BT, T_, C, pos0);
     return hipGetLastError();
 }
 
@@ -806,7 +806,7 @@ hipError_t splitk_reduce_bf16(bf16* C, int64_t ldc, const float* ws, int splits,
 // ---------------------------------------------------------------------------- instantiations
 #define GPT2_INST(T)                                                                                              \
     template hipError_t encoder_forward<T>(T*, const int32_t*, const float*, const float*, int, int, int,        \
-                                           hipStream_t);                                                          \
+                                           hipStream_t, int);                                                     \
     template hipError_t layernorm_forward<T>(T*, float*, const T*, const float*, const float*, int, int,         \
                                              hipStream_t);                                                        \
     template hipError_t layernorm_backward<T>(T*, const T*, float*, float*, const T*, const T*, const float*,   \
