@@ -103,6 +103,11 @@ def main():
                          "FETCH_SIZE / WRITE_SIZE counter calibration) and exit")
     ap.add_argument("--unfused", action="store_true",
                     help="call gpt2_backward and gpt2_adamw_step separately instead of gpt2_backward_adamw")
+    ap.add_argument("--decode", action="store_true",
+                    help="measure incremental generation instead of training: prefill a prompt, then time "
+                         "--steps one-row decode steps per sequence (prints its own JSON line)")
+    ap.add_argument("--decode-batch", type=int, default=8)
+    ap.add_argument("--prompt", type=int, default=512)
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -126,6 +131,9 @@ def main():
 
     import synth
     from transformer_lm_fwd_amd import Arena, binding
+
+    if args.decode:
+        return decode_bench(args)
 
     w = synth.WORKLOADS[args.workload]
     m = w.model
@@ -219,6 +227,119 @@ def main():
                    "channels": m.channels, "vocab": m.vocab_size, "tokens": w.tokens},
         "mfma_peak_frac": round(mfma_frac, 4), "model_tflop_per_step": round(F / 1e12, 4),
         "loss": round(loss, 5), "roofline": roof, "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def decode_bytes_per_step(m, batch, ctx):
+    """HBM bytes one decode step must move at least: every weight matrix once (bf16:
+    the four block products of each layer and the tied lm_head), the cached keys and
+    values of every layer ([batch, ctx, 2C] bf16), and the fp32 logits written."""
+    C, L, V = m.channels, m.num_layers, m.vocab_size
+    weights = 2.0 * (L * 12 * C * C + V * C)
+    kv = 2.0 * L * batch * ctx * 2 * C
+    return weights + kv + 4.0 * batch * V
+
+
+def decode_bench(args):
+    import numpy as np
+    import torch
+    import synth
+    from transformer_lm_fwd_amd import Arena, Generator, binding
+
+    w = synth.WORKLOADS[args.workload]
+    m = w.model
+    batch, n, steps = args.decode_batch, args.prompt, args.steps
+    name = f"gpt2_124m_decode_b{batch}_ctx{n}" if m == synth.GPT2_124M else f"{w.name}_decode_b{batch}_ctx{n}"
+    t0 = time.time()
+    params = synth.init_params(m)
+    prompt = synth.token_windows(w, B=batch, T=n)[:, :n]
+    log(f"[bench] {name}: params generated in {time.time() - t0:.1f} s")
+    torch.cuda.set_device(0)
+    arena = Arena(m, batch, n, w.dtype)
+    arena.load_params(params)
+    gen = Generator(arena, batch, min(m.max_seq_len, n + steps + max(1, args.warmup) + 1))
+    tok = torch.from_numpy(np.ascontiguousarray(prompt)).to(torch.int32).cuda()
+    # the tokens fed to the decode steps: the next ids of the same synthetic stream (the
+    # cost of a step does not depend on them; the timed region runs library kernels only)
+    feed = synth.token_windows(w, B=batch, T=n + steps + args.warmup + 1)[:, n:]
+    feed = [torch.from_numpy(np.ascontiguousarray(feed[:, i])).to(torch.int32).cuda() for i in range(feed.shape[1])]
+
+    # warm-up: a prefill and a few steps, then restart the cache with the same prompt
+    gen.prefill(tok)
+    for i in range(max(1, args.warmup)):
+        gen.decode(feed[i], check_ids=False)
+    torch.cuda.synchronize()
+    gen.prefill(tok)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        gen.decode(feed[i], check_ids=False)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end)
+    ms_per_step = ms / steps
+    value = batch * steps / (ms / 1e3)
+    ctx_mean = n + (steps + 1) / 2.0  # cached positions read, averaged over the timed steps
+    bytes_step = decode_bytes_per_step(m, batch, ctx_mean)
+    gbs = bytes_step / (ms_per_step / 1e3) / 1e9
+    log(f"[bench] {steps} decode steps in {ms:.2f} ms: {ms_per_step * 1e3:.1f} us/step, {value:,.0f} tokens/s, "
+        f"{bytes_step / 1e6:.1f} MB/step at least = {gbs:.0f} GB/s ({100 * gbs / PEAK_HBM_GBS:.1f}% of HBM peak)")
+
+    # per-kernel profile of the same number of steps, after restarting the cache
+    gen.prefill(tok)
+    torch.cuda.synchronize()
+    binding.profile(True)
+    pk = max(1, min(args.profile_steps * 8, steps))
+    for i in range(pk):
+        gen.decode(feed[i], check_ids=False)
+    torch.cuda.synchronize()
+    binding.profile(False)
+    stats = sorted(binding.profile_read(), key=lambda s: -s["total_ms"])
+    tot = sum(s["total_ms"] for s in stats)
+    log(f"[bench] kernel profile over {pk} decode steps ({tot / pk * 1e3:.1f} us/step in kernels):")
+    for s in stats:
+        avg = s["total_ms"] / s["launches"]
+        gb = s["bytes"] / (s["total_ms"] / 1e3) / 1e9
+        log(f"  {s['name']:<20} {s['launches']:6d} launches {s['total_ms'] / pk * 1e3:8.1f} us/step "
+            f"({100 * s['total_ms'] / tot:5.1f}%) avg {avg * 1e3:7.2f} us  {gb:8.1f} GB/s")
+    if args.kernel_table:
+        with open(args.kernel_table, "w") as f:
+            json.dump({"workload": name, "profile_steps": pk, "kernels": stats}, f, indent=1)
+    dom = stats[0] if stats else None
+    roof = {"kernel": "decode step (all kernels)", "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes_per_step": round(bytes_step),
+            "traffic": None}
+    if dom:
+        avg_s = dom["total_ms"] / dom["launches"] / 1e3
+        roof["dominant_kernel"] = {"kernel": dom["name"], "avg_launch_us": round(avg_s * 1e6, 2),
+                                   "achieved_gbs": round(dom["bytes"] / dom["launches"] / avg_s / 1e9, 1)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        T_s = 128
+        o = oracle.Oracle(m, 1, T_s, "f32")
+        o.set("params", params)
+        t1, reps = time.perf_counter(), 0
+        while reps < 1 or time.perf_counter() - t1 < 10.0:
+            o.forward(prompt[:1, :T_s])  # the oracle's next-token logits: a forward over the prefix
+            reps += 1
+        el = time.perf_counter() - t1
+        cpu = {"value": round(reps / el, 4), "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+               "sample": f"next-token logits of one sequence from a {T_s}-token prefix (a full forward pass, "
+                         f"the oracle has no cache), {reps} repetitions"}
+        log(f"[bench] CPU oracle: {cpu['value']} tokens/s")
+
+    out = {
+        "metric": f"decode tokens/sec (KV cache) GPT-2 124M batch {batch}, context {n}->{n + steps}",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic (seeded random-init weights, uniform token ids for prompt and continuation)",
+        "config": {"workload": name, "batch": batch, "prompt": n, "layers": m.num_layers, "heads": m.num_heads,
+                   "channels": m.channels, "vocab": m.vocab_size},
+        "roofline": roof, "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
 

@@ -213,7 +213,7 @@ typedef struct gpt2_gen gpt2_gen; /* opaque host-side handle */
  *               the size (*required_bytes); it must outlive the handle.  No
  *               zero-filling is needed.
  * The arena must outlive the handle.  Errors: GPT2_E_INVAL (NULL arena, fp32 arena,
- * head size other than 64, batch or max_len out of range, out NULL), GPT2_E_ALIGN,
+ * head size other than 64, channels > 2048, batch or max_len out of range, out NULL), GPT2_E_ALIGN,
  * GPT2_E_SIZE (device_bytes too small). */
 int gpt2_gen_alloc(gpt2_arena* arena, int32_t batch, int32_t max_len, void* device_base, size_t device_bytes,
                    size_t* required_bytes, gpt2_gen** out);

@@ -6,115 +6,210 @@
 // sequence through every layer: the matrix products become skinny (a handful of rows
 // against a full weight matrix, bound by reading the weights), and attention is one
 // query against the cached keys and values of its sequence.
+#include <algorithm>
+
 #include "kernels.h"
 
 namespace gpt2 {
 
 // ============================================================================ skinny GEMM
-// y[m, n] = epilogue( sum_k x[m, k] W[n, k] ) for the M <= 16 rows of a decode step.
-// W is [N, K] row-major (out, in) - each output column is one contiguous weight row.
-// Block: 4 waves; a wave takes 8 columns, 8 lanes per column, and a lane reads 16
-// bytes of its row per step, so every column is read as 128-byte segments.  x goes
-// through LDS in K chunks of 1024 and is read back 16 bytes at a time (the lanes of
-// different columns read the same chunk: a broadcast).  The 8 lanes of a column
-// then combine their sums by butterfly shuffles and lane j writes rows j, j + 8.
-constexpr int SK_MAXM = 16, SK_KC = 1024;
+// y[m, n] = epilogue( sum_k x'[m, k] W[n, k] ) for the M <= 16 rows of a decode step,
+// W [N, K] row-major (out, in): each output column is one contiguous weight row, and the
+// product is bound by reading W once.  On the matrix core: v_mfma_f32_16x16x32_bf16
+// with the 16 (zero-padded) rows of x' as A and 16 weight rows as B - lane l supplies
+// row / column l % 16 with the 8 k values 8 (l / 16) .. +7, i.e. one 16-byte load of its
+// weight row per 32 k, and its accumulators hold column l % 16, rows 4 (l / 16) .. +3.
+// Block = 4 waves on 16 columns; wave w takes the 32-k steps w, w + 4, .. so the
+// weight rows stream in from four waves at once.  x' goes through LDS in chunks of up
+// to 2048 k; per chunk a wave first issues all of its weight loads (up to 16 per lane),
+// then the block stages x' (loads issued eight at a time before their stores), then
+// the wave multiplies.  The four waves' sums are added through LDS and each thread
+// applies the epilogue to one (row, column).
+// With LayerNorm gains / shifts, x' = LayerNorm(x): the whole rows are staged (one
+// chunk, K <= 2048), each row's mean and rstd (biased variance, eps 1e-5, two passes;
+// wave w takes rows w, w + 4, ..) come from LDS, and the rows are normalised in place
+// and rounded to bf16 like the forward pass's LayerNorm output.  Every block repeats
+// this small prologue, which pays for products with few blocks (qkv, c_fc) but not for
+// the lm_head's thousands: that one takes a separately normalised input.
+constexpr int SK_MAXM = 16, SK_KC = 2048, SK_LN_MAXK = 2048, SK_WL = 16;  // weight loads per lane per chunk
 
-template <int EPI>
+typedef __bf16 sk_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float sk_f32x4 __attribute__((ext_vector_type(4)));
+
+template <int EPI, bool LN>
 __global__ __launch_bounds__(256) void skinny_gemm_kernel(SkinnyArgs a) {
-    __shared__ __attribute__((aligned(16))) bf16 xs[SK_MAXM][SK_KC];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int gl = lane & 7;
-    const int n = (blockIdx.x * 4 + wave) * 8 + (lane >> 3);
-    float acc[SK_MAXM];
-#pragma unroll
-    for (int m = 0; m < SK_MAXM; ++m) acc[m] = 0.f;
+    extern __shared__ __attribute__((aligned(16))) bf16 xs[];  // [M][chunk]
+    __shared__ float red[4][16][17];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int col = lane & 15, kq = lane >> 4;
+    const int n = blockIdx.x * 16 + col;
+    const int KC = LN ? a.K : min(a.K, SK_KC);
     const bf16* wrow = a.W + (int64_t)min(n, a.N - 1) * a.ldw;
-    for (int k0 = 0; k0 < a.K; k0 += SK_KC) {
-        const int kc = min(SK_KC, a.K - k0), cpr = kc / 8;
-        __syncthreads();  // the previous chunk is no longer read
-        for (int i = tid; i < a.M * cpr; i += 256) {
-            const int m = i / cpr, c = i % cpr;
-            *(u32x4*)&xs[m][c * 8] = ld16(a.x + (int64_t)m * a.ldx + k0 + c * 8);
+    float gv[8], bv[8];  // LayerNorm gains / shifts of this thread's 8-column chunk (LN: K <= 2048)
+    if constexpr (LN) {
+        if (8 * tid < a.K) {
+#pragma unroll
+            for (int e = 0; e < 8; e += 4) {
+                *(float4*)&gv[e] = *(const float4*)(a.ln_w + 8 * tid + e);
+                *(float4*)&bv[e] = *(const float4*)(a.ln_b + 8 * tid + e);
+            }
         }
-        __syncthreads();
-        if (n < a.N) {
-            for (int kk = gl * 8; kk < kc; kk += 64) {
-                float w8[8];
-                unpack16<bf16>(ld16(wrow + k0 + kk), w8);
+    }
+    sk_f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < a.K; k0 += KC) {
+        const int kc = min(KC, a.K - k0), cpr = kc / 8, nch = a.M * cpr;
+        const int nsteps = (kc + 31) / 32;  // 32-k steps of the chunk; this wave takes w, w + 4, ..
+        for (int sb = w; sb < nsteps; sb += 4 * SK_WL) {
+            u32x4 wv[SK_WL];
 #pragma unroll
-                for (int m = 0; m < SK_MAXM; ++m) {
-                    if (m < a.M) {
-                        float x8[8];
-                        unpack16<bf16>(*(const u32x4*)&xs[m][kk], x8);
+            for (int j = 0; j < SK_WL; ++j) {
+                const int kk = 32 * (sb + 4 * j) + 8 * kq;
+                wv[j] = (n < a.N && kk < kc) ? ld16(wrow + k0 + kk) : u32x4{0u, 0u, 0u, 0u};
+            }
+            if (sb == w) {  // first batch of the chunk: stage x' while the loads are in flight
+                __syncthreads();  // the previous chunk is no longer read
+                for (int b0 = 0; b0 < nch; b0 += 256 * 8) {
+                    u32x4 t[8];
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) acc[m] = __builtin_fmaf(w8[e], x8[e], acc[m]);
+                    for (int j = 0; j < 8; ++j) {
+                        const int i = b0 + 256 * j + tid;
+                        t[j] = i < nch ? ld16(a.x + (int64_t)(i / cpr) * a.ldx + k0 + (i % cpr) * 8)
+                                       : u32x4{0u, 0u, 0u, 0u};
                     }
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const int i = b0 + 256 * j + tid;
+                        if (i < nch) *(u32x4*)&xs[(i / cpr) * kc + (i % cpr) * 8] = t[j];
+                    }
+                }
+                __syncthreads();
+                if constexpr (LN) {
+                    // wave w takes rows w, w + 4, ..: two passes (mean, then the variance about it)
+                    __shared__ float stat[SK_MAXM][2];
+                    float part[SK_MAXM / 4], mean[SK_MAXM / 4];
+#pragma unroll
+                    for (int r = 0; r < SK_MAXM / 4; ++r) {
+                        const int m = w + 4 * r;
+                        part[r] = 0.f;
+                        if (m < a.M)
+                            for (int k = lane * 8; k < kc; k += 512) {
+                                float v[8];
+                                unpack16<bf16>(*(const u32x4*)(xs + m * kc + k), v);
+#pragma unroll
+                                for (int e = 0; e < 8; ++e) part[r] += v[e];
+                            }
+                    }
+#pragma unroll
+                    for (int r = 0; r < SK_MAXM / 4; ++r) mean[r] = wave_sum(part[r]) / kc;
+#pragma unroll
+                    for (int r = 0; r < SK_MAXM / 4; ++r) {
+                        const int m = w + 4 * r;
+                        part[r] = 0.f;
+                        if (m < a.M)
+                            for (int k = lane * 8; k < kc; k += 512) {
+                                float v[8];
+                                unpack16<bf16>(*(const u32x4*)(xs + m * kc + k), v);
+#pragma unroll
+                                for (int e = 0; e < 8; ++e) part[r] += (v[e] - mean[r]) * (v[e] - mean[r]);
+                            }
+                    }
+#pragma unroll
+                    for (int r = 0; r < SK_MAXM / 4; ++r) {
+                        const float var = wave_sum(part[r]) / kc;
+                        const int m = w + 4 * r;
+                        if (lane == 0 && m < a.M) {
+                            stat[m][0] = mean[r];
+                            stat[m][1] = 1.0f / sqrtf(var + 1e-5f);
+                        }
+                    }
+                    __syncthreads();
+                    // thread t normalises the 8-column chunk t of every row
+                    if (tid < cpr) {
+                        for (int m = 0; m < a.M; ++m) {
+                            float f[8];
+                            unpack16<bf16>(*(const u32x4*)&xs[m * kc + 8 * tid], f);
+                            const float mu = stat[m][0], rstd = stat[m][1];
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) f[e] = (f[e] - mu) * rstd * gv[e] + bv[e];
+                            *(u32x4*)&xs[m * kc + 8 * tid] = pack16<bf16>(f);
+                        }
+                    }
+                    __syncthreads();
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < SK_WL; ++j) {
+                const int kk = 32 * (sb + 4 * j) + 8 * kq;
+                if (32 * (sb + 4 * j) < kc) {  // wave-uniform
+                    const u32x4 xa = (col < a.M && kk < kc) ? *(const u32x4*)&xs[col * kc + kk] : u32x4{0u, 0u, 0u, 0u};
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(sk_bf16x8, xa),
+                                                                  __builtin_bit_cast(sk_bf16x8, wv[j]), acc, 0, 0, 0);
                 }
             }
         }
     }
+    // acc[i]: row 4 kq + i, column col (of this wave's share of k)
 #pragma unroll
-    for (int m = 0; m < SK_MAXM; ++m) {
-        acc[m] += __shfl_xor(acc[m], 1, 64);
-        acc[m] += __shfl_xor(acc[m], 2, 64);
-        acc[m] += __shfl_xor(acc[m], 4, 64);
-    }
-    if (n >= a.N) return;
-    const float bias = a.bias ? a.bias[n] : 0.f;
-#pragma unroll
-    for (int r = 0; r < SK_MAXM / 8; ++r) {
-        const int m = gl + 8 * r;
-        if (m >= a.M) continue;
-        // lane gl holds every row's total; pick row m without dynamic register indexing
-        float v = 0.f;
-#pragma unroll
-        for (int j = 0; j < SK_MAXM; ++j)
-            if (j == m) v = acc[j];
-        v += bias;
-        const int64_t o = (int64_t)m * a.ldc + n;
-        if constexpr (EPI == EPI_F32) {
-            ((float*)a.C)[o] = v;
-        } else {
-            if constexpr (EPI == EPI_BIAS_RES) v += to_f32(a.R[(int64_t)m * a.ldr + n]);
-            if constexpr (EPI == EPI_BIAS_GELU) {
-                if (a.C2) a.C2[o] = from_f32<bf16>(gelu_fwd(v));
-            }
-            if (a.C) ((bf16*)a.C)[o] = from_f32<bf16>(v);
+    for (int i = 0; i < 4; ++i) red[w][4 * kq + i][col] = acc[i];
+    __syncthreads();
+    const int m = tid >> 4, cn = tid & 15, nn = blockIdx.x * 16 + cn;
+    if (m >= a.M || nn >= a.N) return;
+    float v = (red[0][m][cn] + red[1][m][cn]) + (red[2][m][cn] + red[3][m][cn]);
+    if (a.bias) v += a.bias[nn];
+    const int64_t o = (int64_t)m * a.ldc + nn;
+    if constexpr (EPI == EPI_F32) {
+        ((float*)a.C)[o] = v;
+    } else {
+        if constexpr (EPI == EPI_BIAS_RES) v += to_f32(a.R[(int64_t)m * a.ldr + nn]);
+        if constexpr (EPI == EPI_BIAS_GELU) {
+            if (a.C2) a.C2[o] = from_f32<bf16>(gelu_fwd(v));
         }
+        if (a.C) ((bf16*)a.C)[o] = from_f32<bf16>(v);
     }
+}
+
+template <bool LN>
+static hipError_t skinny_launch(const SkinnyArgs& a, int epi, hipStream_t s) {
+    const dim3 grid((a.N + 15) / 16);
+    const size_t lds = (size_t)a.M * (LN ? a.K : std::min(a.K, SK_KC)) * 2;
+    switch (epi) {
+        case EPI_BIAS: hipLaunchKernelGGL((skinny_gemm_kernel<EPI_BIAS, LN>), grid, dim3(256), lds, s, a); break;
+        case EPI_BIAS_RES: hipLaunchKernelGGL((skinny_gemm_kernel<EPI_BIAS_RES, LN>), grid, dim3(256), lds, s, a); break;
+        case EPI_BIAS_GELU: hipLaunchKernelGGL((skinny_gemm_kernel<EPI_BIAS_GELU, LN>), grid, dim3(256), lds, s, a); break;
+        case EPI_F32: hipLaunchKernelGGL((skinny_gemm_kernel<EPI_F32, LN>), grid, dim3(256), lds, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 hipError_t skinny_gemm(const SkinnyArgs& a, int epi, hipStream_t s) {
     if (a.M <= 0 || a.N <= 0) return hipSuccess;
     if (a.M > SK_MAXM || a.K % 8 || a.ldx % 8 || a.ldw % 8) return hipErrorInvalidValue;
-    const dim3 grid((a.N + 31) / 32);
+    if ((a.ln_w != nullptr) != (a.ln_b != nullptr)) return hipErrorInvalidValue;
+    if (a.ln_w && (a.K > SK_LN_MAXK || (uintptr_t)a.ln_w % 16 || (uintptr_t)a.ln_b % 16)) return hipErrorInvalidValue;
     ProfScope prof(s, "skinny_gemm", 2.0 * a.M * a.N * a.K,
                    2.0 * a.N * a.K + 2.0 * a.M * a.K + (epi == EPI_F32 ? 4.0 : 2.0) * a.M * a.N);
-    switch (epi) {
-        case EPI_BIAS: hipLaunchKernelGGL(skinny_gemm_kernel<EPI_BIAS>, grid, dim3(256), 0, s, a); break;
-        case EPI_BIAS_RES: hipLaunchKernelGGL(skinny_gemm_kernel<EPI_BIAS_RES>, grid, dim3(256), 0, s, a); break;
-        case EPI_BIAS_GELU: hipLaunchKernelGGL(skinny_gemm_kernel<EPI_BIAS_GELU>, grid, dim3(256), 0, s, a); break;
-        case EPI_F32: hipLaunchKernelGGL(skinny_gemm_kernel<EPI_F32>, grid, dim3(256), 0, s, a); break;
-        default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
+    return a.ln_w ? skinny_launch<true>(a, epi, s) : skinny_launch<false>(a, epi, s);
 }
 
 // ============================================================================ decode attention
 // One query per (sequence, head) against cached keys/values 0 .. len-1, head size 64
 // ("GPT-2 from scratch with torch", 自注意力: softmax(q k^T / sqrt(hs)) v; the new row sees
 // every cached position, so no mask is needed).  Cache rows are the q|k|v rows the
-// qkv product wrote, [batch][max_len][3C].  Block (b, h): 4 waves take key chunks of
-// 64 in turn; lane j scores key 64c + j (its key row read as 8 x 16 bytes against the
-// query held in registers), the wave keeps a running maximum and sum (online softmax),
-// and o[d] (lane = d) adds p_j v_j[d] over the chunk, p_j broadcast by shuffle and
-// v_j read as one 128-byte row per key.  The four waves' states are merged through LDS.
-__global__ __launch_bounds__(256) void attn_decode64_kernel(bf16* y, const bf16* cache, int len, int C, int NH,
+// qkv product wrote, [batch][max_len][3C].  Block (b, h): ADW waves take key chunks of
+// 64 in turn.  Scores: lane j takes key 64c + j, its key row read as 8 x 16 bytes
+// against the query held in registers; the wave keeps a running maximum and sum
+// (online softmax).  P V: lane (g, d8) = (lane / 8, lane % 8) adds p_key v_key[8 d8 ..
+// 8 d8 + 7] for the keys g, g + 8, .. of the chunk (16-byte V reads, p by shuffle), and
+// the 8 key groups are combined by shuffles at the end.  The waves' states are merged
+// through LDS.
+constexpr int ADW = 8;
+__global__ __launch_bounds__(64 * ADW) void attn_decode64_kernel(bf16* y, const bf16* cache, int len, int C, int NH,
                                                             int64_t bstride) {
     constexpr int HS = 64;
     const int b = blockIdx.x / NH, h = blockIdx.x % NH;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int kg = lane >> 3, d8 = lane & 7;
     const int64_t C3 = 3 * (int64_t)C;
     const bf16* base = cache + (int64_t)b * bstride;
     const float c = 0.125f * 1.4426950408889634f;  // 1/sqrt(64) in log2 units
@@ -122,17 +217,29 @@ __global__ __launch_bounds__(256) void attn_decode64_kernel(bf16* y, const bf16*
     const bf16* qrow = base + (int64_t)(len - 1) * C3 + h * HS;
 #pragma unroll
     for (int i = 0; i < 8; ++i) q[i] = ld16(qrow + 8 * i);
-    float m = -INFINITY, l = 0.f, o = 0.f;
-    for (int k0 = 64 * w; k0 < len; k0 += 256) {
+    float m = -INFINITY, l = 0.f, o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = 0.f;
+    for (int k0 = 64 * w; k0 < len; k0 += 64 * ADW) {
         const int key = k0 + lane;
+        // this lane's 8 V rows (keys k0 + kg + 8 i) are requested before the scores
+        u32x4 vr[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int vk = k0 + kg + 8 * i;
+            vr[i] = vk < len ? ld16(base + (int64_t)vk * C3 + 2 * C + h * HS + 8 * d8) : u32x4{0u, 0u, 0u, 0u};
+        }
         float s = -INFINITY;
         if (key < len) {
             const bf16* krow = base + (int64_t)key * C3 + C + h * HS;
+            u32x4 kr[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) kr[i] = ld16(krow + 8 * i);
             float dot = 0.f;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 float kv[8], qv[8];
-                unpack16<bf16>(ld16(krow + 8 * i), kv);
+                unpack16<bf16>(kr[i], kv);
                 unpack16<bf16>(q[i], qv);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) dot = __builtin_fmaf(qv[e], kv[e], dot);
@@ -143,27 +250,43 @@ __global__ __launch_bounds__(256) void attn_decode64_kernel(bf16* y, const bf16*
         const float corr = __builtin_amdgcn_exp2f(m - mn);  // m = -inf at first: corr = 0
         const float p = key < len ? __builtin_amdgcn_exp2f(s - mn) : 0.f;
         l = l * corr + p;
-        o *= corr;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] *= corr;
         m = mn;
-        const int nk = min(64, len - k0);
-        const bf16* vcol = base + (int64_t)k0 * C3 + 2 * C + h * HS + lane;
-        for (int j = 0; j < nk; ++j) o = __builtin_fmaf(__shfl(p, j, 64), to_f32(vcol[(int64_t)j * C3]), o);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float pk = __shfl(p, kg + 8 * i, 64);  // 0 for keys past len
+            float v[8];
+            unpack16<bf16>(vr[i], v);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] = __builtin_fmaf(pk, v[e], o[e]);
+        }
+    }
+    // the 8 key groups (lanes d8, d8 + 8, ..) hold partial sums of the same dims
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        o[e] += __shfl_xor(o[e], 8, 64);
+        o[e] += __shfl_xor(o[e], 16, 64);
+        o[e] += __shfl_xor(o[e], 32, 64);
     }
     l = wave_sum(l);
-    __shared__ float sm[4], sl[4], so[4][HS];
+    __shared__ float sm[ADW], sl[ADW], so[ADW][HS];
     if (lane == 0) {
         sm[w] = m;
         sl[w] = l;
     }
-    so[w][lane] = o;
+    if (kg == 0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) so[w][8 * d8 + e] = o[e];
+    }
     __syncthreads();
     if (w == 0) {
         float M = sm[0];
 #pragma unroll
-        for (int i = 1; i < 4; ++i) M = fmaxf(M, sm[i]);
+        for (int i = 1; i < ADW; ++i) M = fmaxf(M, sm[i]);
         float L = 0.f, O = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < ADW; ++i) {
             const float f = sm[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sm[i] - M);  // waves without keys
             L += sl[i] * f;
             O += so[i][lane] * f;
@@ -176,7 +299,7 @@ hipError_t attention_decode(bf16* y, const bf16* cache, int batch, int len, int 
                             hipStream_t s) {
     if (C / NH != 64 || len < 1) return hipErrorInvalidValue;
     ProfScope prof(s, "attn_decode64", 4.0 * batch * C * len, 4.0 * batch * C * len + 4.0 * batch * C);
-    hipLaunchKernelGGL(attn_decode64_kernel, dim3(batch * NH), dim3(256), 0, s, y, cache, len, C, NH, bstride);
+    hipLaunchKernelGGL(attn_decode64_kernel, dim3(batch * NH), dim3(64 * ADW), 0, s, y, cache, len, C, NH, bstride);
     return hipGetLastError();
 }
 

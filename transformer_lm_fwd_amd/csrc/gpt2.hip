@@ -66,7 +66,7 @@ struct gpt2_gen {
     int batch, max_len, len;
     bool ready;
     char* base;
-    size_t cache, res[3], ln, stats, atty, fchg, lnf;
+    size_t cache, res[3], atty, fchg, lnf, stats;
 };
 
 namespace {
@@ -621,6 +621,7 @@ int gpt2_gen_alloc(gpt2_arena* a, int32_t batch, int32_t max_len, void* device_b
     if (a->hs != 64) return fail(GPT2_E_INVAL, "generation needs head size 64");
     if (batch < 1 || batch > 16) return fail(GPT2_E_INVAL, "batch must be in 1..16");
     if (max_len < 1 || max_len > a->cfg.max_seq_len) return fail(GPT2_E_INVAL, "max_len must be in 1..max_seq_len");
+    if (a->cfg.channels > 2048) return fail(GPT2_E_INVAL, "generation needs channels <= 2048");
     const size_t C = a->cfg.channels, L = a->cfg.num_layers, Bg = batch;
     gpt2_gen g{};
     size_t o = 0;
@@ -631,11 +632,10 @@ int gpt2_gen_alloc(gpt2_arena* a, int32_t batch, int32_t max_len, void* device_b
     };
     g.cache = take(L * Bg * max_len * 3 * C * 2);
     for (auto& r : g.res) r = take(Bg * C * 2);
-    g.ln = take(Bg * C * 2);
-    g.stats = take(Bg * 2 * 4);
     g.atty = take(Bg * C * 2);
     g.fchg = take(Bg * 4 * C * 2);
     g.lnf = take(Bg * C * 2);
+    g.stats = take(Bg * 2 * 4);
     if (required_bytes) *required_bytes = o;
     if (!device_base) return GPT2_OK;
     if ((uintptr_t)device_base % kAlign) return fail(GPT2_E_ALIGN, "device_base must be 256-byte aligned");
@@ -699,11 +699,16 @@ int gpt2_gen_decode(gpt2_gen* g, const int32_t* d_tokens, float* d_logits, void*
     const float* master = at<float>(a, a->params);
     const bf16* w16 = at<bf16>(a, a->params16);
     auto lp = [&](int l, int i) { return a->o_layer[l * P_N + i]; };
-    auto skinny = [&](const bf16* x, int64_t ldx, int64_t woff, int N, int K, void* Cout, int64_t ldc, bf16* C2,
-                      const bf16* R, const float* bias, int epi) -> int {
+    // x' = LayerNorm(x) with the gains / shifts at `ln` (if >= 0), then x' W^T
+    auto skinny = [&](const bf16* x, int64_t ldx, int64_t ln, int64_t woff, int N, int K, void* Cout, int64_t ldc,
+                      bf16* C2, const bf16* R, const float* bias, int epi) -> int {
         SkinnyArgs k{};
         k.x = x; k.ldx = ldx; k.W = w16 + woff; k.ldw = K; k.C = Cout; k.ldc = ldc; k.C2 = C2;
         k.R = R; k.ldr = C; k.bias = bias; k.M = Bg; k.N = N; k.K = K;
+        if (ln >= 0) {
+            k.ln_w = master + ln;
+            k.ln_b = master + ln + K;
+        }
         return hip_check(skinny_gemm(k, epi, s), "skinny gemm");
     };
     int rc;
@@ -716,32 +721,29 @@ int gpt2_gen_decode(gpt2_gen* g, const int32_t* d_tokens, float* d_logits, void*
         bf16* res2 = buf(g->res[(cur + 1) % 3]);
         bf16* res3 = buf(g->res[(cur + 2) % 3]);
         bf16* cache = buf(g->cache) + (int64_t)l * Bg * row;
-        float* st = (float*)(g->base + g->stats);
-        CHECK(layernorm_forward<bf16>(buf(g->ln), st, xin, master + lp(l, P_LN1W), master + lp(l, P_LN1B), Bg, C, s),
-              "ln1");
-        // q|k|v of the new rows straight into cache row t of each sequence
-        if ((rc = skinny(buf(g->ln), C, lp(l, P_QKVW), 3 * C, C, cache + (int64_t)t * C3, row, nullptr, nullptr,
-                         master + lp(l, P_QKVB), EPI_BIAS)))
+        // ln_1, then q|k|v of the new rows straight into cache row t of each sequence
+        if ((rc = skinny(xin, C, lp(l, P_LN1W), lp(l, P_QKVW), 3 * C, C, cache + (int64_t)t * C3, row, nullptr,
+                         nullptr, master + lp(l, P_QKVB), EPI_BIAS)))
             return rc;
         CHECK(attention_decode(buf(g->atty), cache, Bg, t + 1, C, NH, row, s), "attention");
-        if ((rc = skinny(buf(g->atty), C, lp(l, P_PROJW), C, C, res2, C, nullptr, xin, master + lp(l, P_PROJB),
+        if ((rc = skinny(buf(g->atty), C, -1, lp(l, P_PROJW), C, C, res2, C, nullptr, xin, master + lp(l, P_PROJB),
                          EPI_BIAS_RES)))
             return rc;
-        CHECK(layernorm_forward<bf16>(buf(g->ln), st, res2, master + lp(l, P_LN2W), master + lp(l, P_LN2B), Bg, C, s),
-              "ln2");
-        if ((rc = skinny(buf(g->ln), C, lp(l, P_FCW), 4 * C, C, nullptr, 4 * C, buf(g->fchg), nullptr,
+        // ln_2, c_fc + GELU
+        if ((rc = skinny(res2, C, lp(l, P_LN2W), lp(l, P_FCW), 4 * C, C, nullptr, 4 * C, buf(g->fchg), nullptr,
                          master + lp(l, P_FCB), EPI_BIAS_GELU)))
             return rc;
-        if ((rc = skinny(buf(g->fchg), 4 * C, lp(l, P_FCPW), C, 4 * C, res3, C, nullptr, res2,
+        if ((rc = skinny(buf(g->fchg), 4 * C, -1, lp(l, P_FCPW), C, 4 * C, res3, C, nullptr, res2,
                          master + lp(l, P_FCPB), EPI_BIAS_RES)))
             return rc;
         cur = (cur + 2) % 3;
     }
+    // ln_f on its own (the lm_head product has thousands of blocks), then the next-token
+    // logits (tied lm_head), fp32 [batch, V]
     CHECK(layernorm_forward<bf16>(buf(g->lnf), (float*)(g->base + g->stats), buf(g->res[cur]), master + a->o_lnfw,
                                   master + a->o_lnfb, Bg, C, s),
           "lnf");
-    // next-token logits (tied lm_head), fp32 [batch, V]
-    if ((rc = skinny(buf(g->lnf), C, a->o_wte, V, C, d_logits, V, nullptr, nullptr, nullptr, EPI_F32))) return rc;
+    if ((rc = skinny(buf(g->lnf), C, -1, a->o_wte, V, C, d_logits, V, nullptr, nullptr, nullptr, EPI_F32))) return rc;
     g->len = t + 1;
     return GPT2_OK;
 }

@@ -116,7 +116,8 @@ hipError_t attention_backward_mfma64(bf16* dqkv, float* dsum, const bf16* dout, 
 // Skinny product for the rows of a decode step: C[m, n] = epilogue(sum_k x[m, k] W[n, k]),
 // M <= 16, W [N, K] row-major; epilogues EPI_BIAS, EPI_BIAS_RES (+ R[m, n], row stride
 // ldr), EPI_BIAS_GELU (C = pre-activation if non-null, C2 = gelu, both row stride ldc)
-// and EPI_F32 (fp32 C = acc + bias).  K, ldx, ldw multiples of 8.
+// and EPI_F32 (fp32 C = acc + bias).  K, ldx, ldw multiples of 8 (and with ln_w, the
+// gains / shifts 16-byte aligned).
 struct SkinnyArgs {
     const bf16* x;
     int64_t ldx;
@@ -128,6 +129,9 @@ struct SkinnyArgs {
     const bf16* R;
     int64_t ldr;
     const float* bias;
+    // non-null: x is replaced by LayerNorm(x) with these fp32 gains / shifts [K]
+    const float* ln_w;
+    const float* ln_b;
     int M, N, K;
 };
 hipError_t skinny_gemm(const SkinnyArgs& a, int epi, hipStream_t s);
