@@ -45,6 +45,15 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(SkinnyArgs a) {
     const int n = blockIdx.x * 16 + col;
     const int KC = LN ? a.K : min(a.K, SK_KC);
     const bf16* wrow = a.W + (int64_t)min(n, a.N - 1) * a.ldw;
+    // this thread's epilogue element (row tid / 16, column tid % 16): its bias and
+    // residual are requested now, not after the reduction
+    const int em = tid >> 4, en = blockIdx.x * 16 + (tid & 15);
+    const bool eok = em < a.M && en < a.N;
+    const float ebias = (eok && a.bias) ? a.bias[en] : 0.f;
+    float eres = 0.f;
+    if constexpr (EPI == EPI_BIAS_RES) {
+        if (eok) eres = to_f32(a.R[(int64_t)em * a.ldr + en]);
+    }
     float gv[8], bv[8];  // LayerNorm gains / shifts of this thread's 8-column chunk (LN: K <= 2048)
     if constexpr (LN) {
         if (8 * tid < a.K) {
@@ -152,15 +161,15 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(SkinnyArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) red[w][4 * kq + i][col] = acc[i];
     __syncthreads();
-    const int m = tid >> 4, cn = tid & 15, nn = blockIdx.x * 16 + cn;
-    if (m >= a.M || nn >= a.N) return;
-    float v = (red[0][m][cn] + red[1][m][cn]) + (red[2][m][cn] + red[3][m][cn]);
-    if (a.bias) v += a.bias[nn];
-    const int64_t o = (int64_t)m * a.ldc + nn;
+    if (!eok) return;
+    const int cn = tid & 15;
+    float v = (red[0][em][cn] + red[1][em][cn]) + (red[2][em][cn] + red[3][em][cn]);
+    v += ebias;
+    const int64_t o = (int64_t)em * a.ldc + en;
     if constexpr (EPI == EPI_F32) {
         ((float*)a.C)[o] = v;
     } else {
-        if constexpr (EPI == EPI_BIAS_RES) v += to_f32(a.R[(int64_t)m * a.ldr + nn]);
+        if constexpr (EPI == EPI_BIAS_RES) v += eres;
         if constexpr (EPI == EPI_BIAS_GELU) {
             if (a.C2) a.C2[o] = from_f32<bf16>(gelu_fwd(v));
         }
