@@ -49,6 +49,7 @@ struct gpt2_arena {
     size_t dres[4], dbuf, dqkv[2], dfch[2], dsum, partial, partial_side, ws, ws_main, census;
     size_t partial_floats, ws_floats, ws_main_floats;
     bool loss_ready;
+    bool census_armed = false;  // the token census holds its idle state (set by the first backward)
     const int32_t* inputs;
     // Backward concurrency: parameter-gradient work runs on `side`.  rd_* mark the
     // side stream's last read of each ring buffer; fork events order side work
@@ -331,8 +332,10 @@ struct Model {
     // embeddings and ln_f are updated after the join.
     int backward(const AdamArgs* opt = nullptr) {
         int rc;
-        if (!a->side)  // first backward pass on this arena: arm the token census
+        if (!a->census_armed) {  // first backward pass on this arena: arm the token census
             CHECK(token_census_reset(at<int>(a, a->census), at<int>(a, a->census) + V, V, s), "census reset");
+            a->census_armed = true;
+        }
         if ((rc = ensure_streams(a))) return rc;
         hipStream_t M = s, SD = profiling() ? s : a->side;
         T* dz = act(a->logits);
