@@ -255,6 +255,52 @@ int gpt2_gen_decode(gpt2_gen* gen, const int32_t* d_tokens, float* d_logits, voi
 int gpt2_sample_topk(const float* logits, int32_t rows, int32_t V, int64_t ld, int32_t k, float temperature,
                      const float* uniforms, int32_t* tokens_out);
 
+/* ---------------------------------------------------------------- files (host memory only)
+ * Token streams ("1000 行 C 代码完成 GPT-2 训练的 LLM.c", 快速开始吧: a .bin file is a raw
+ * stream of int32 GPT-2 token ids).  Batch i of B sequences of T tokens is the B*T + 1
+ * ids starting at id i*B*T: inputs are its first B*T ids, targets the same shifted by
+ * one, row-major [B, T].  A stream of n ids holds n / (B*T) batches (the page's run
+ * banner: 32768 ids -> 128 batches, 305260 -> 1192, at B*T = 256); if the last batch's
+ * final target would lie past the end it is id 0 (the stream wraps). */
+
+/* Number of int32 ids in the file, or a negative status (GPT2_E_INVAL: cannot open;
+ * GPT2_E_SIZE: the size is not a multiple of 4 bytes). */
+int64_t gpt2_tokens_count(const char* path);
+
+/* Reads batch `batch` into host int32 inputs / targets [B*T] each.  Errors:
+ * GPT2_E_INVAL (NULL argument, B or T < 1, cannot open), GPT2_E_SIZE (batch outside
+ * 0 .. num_batches - 1, short read). */
+int gpt2_tokens_batch(const char* path, int32_t B, int32_t T, int64_t batch, int32_t* inputs, int32_t* targets);
+
+/* Parameter orders of a flat fp32 weight array: the arena's (layer blocks in numeric
+ * order) and the order of weight files that sort their layers by name
+ * ("GPT-2ベースの3000バイトCで実装されたChatGPTクローン", 重みの読み込み: the blocks of
+ * layers 0, 1, 10, 11, 2, .. as the decimal indices sort as text).  Everything else -
+ * wte, wpe before the layers, ln_f after them, the tensors inside a layer block - is in
+ * the same place in both. */
+enum gpt2_param_order { GPT2_ORDER_NUMERIC = 0, GPT2_ORDER_LEXICOGRAPHIC = 1 };
+
+/* dst (host fp32 [gpt2_num_parameters]) = src reordered from one layer order to the
+ * other.  Errors: GPT2_E_INVAL for a bad config, NULL or identical arrays, unknown order. */
+int gpt2_params_permute(const gpt2_config* cfg, const float* src, float* dst, int32_t from_order, int32_t to_order);
+
+/* Checkpoint file: a 64-byte header (int32 magic "GPT2", version 1, the five config
+ * fields, has-moments flag, AdamW step, 7 zeros) followed by the fp32 parameters in the
+ * arena's order and, if m and v are given, the two AdamW moment arrays.  Host arrays of
+ * gpt2_num_parameters(cfg) floats; m and v both or neither.  Written to path + ".tmp"
+ * and renamed.  Errors: GPT2_E_INVAL (bad arguments, cannot create), GPT2_E_SIZE (write
+ * failed). */
+int gpt2_checkpoint_write(const char* path, const gpt2_config* cfg, int32_t step, const float* params,
+                          const float* m, const float* v);
+
+/* Reads a checkpoint written by gpt2_checkpoint_write for the same model shape into
+ * params (and m, v when both are non-NULL and the file has moments); *step and
+ * *has_moments (each may be NULL) receive the header's values.  Errors: GPT2_E_INVAL
+ * (bad arguments, cannot open, not a checkpoint, different model shape), GPT2_E_SIZE
+ * (short read). */
+int gpt2_checkpoint_read(const char* path, const gpt2_config* cfg, int32_t* step, float* params, float* m, float* v,
+                         int32_t* has_moments);
+
 /* Message for the last non-OK status on this thread ("" if none). */
 const char* gpt2_last_error(void);
 

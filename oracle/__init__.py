@@ -8,7 +8,8 @@ Parity status of each oracle function (pins live in tests/test_oracle_pins.py an
 tests/test_sampling.py): every forward layer, every backward formula, the AdamW
 update and top-k sampling are pinned (closed forms, printed integers, invariants,
 central finite differences and an independent autograd cross-check); nothing here
-is "parity unpinned".  Incremental generation has no function of its own here: the
+is "parity unpinned" (token batches and the layer order of weight files are pinned in
+tests/test_io.py).  Incremental generation has no function of its own here: the
 next-token logits after a prefix are the forward pass's logits at the prefix's last
 position.
 """
@@ -195,3 +196,41 @@ def sample_topk(logits, k: int, temperature: float, u: float) -> int:
     cum = np.cumsum(w)
     i = int(np.searchsorted(cum, float(np.float32(u)) * cum[-1], side="right"))
     return int(order[min(i, order.size - 1)])
+
+
+def token_batch(ids, B: int, T: int, i: int):
+    """Batch i of a token stream ("1000 行 C 代码完成 GPT-2 训练的 LLM.c", 快速开始吧: a raw
+    int32 id stream): the B*T + 1 ids from i*B*T on, the stream read as a circle; inputs
+    are the first B*T, targets the next B*T, both [B, T].  There are len(ids) // (B*T)
+    batches."""
+    ids = np.asarray(ids, dtype=np.int32)
+    n, bt = ids.size, B * T
+    if not 0 <= i < n // bt:
+        raise IndexError(i)
+    win = ids[(i * bt + np.arange(bt + 1)) % n]
+    return win[:-1].reshape(B, T), win[1:].reshape(B, T)
+
+
+def lexicographic_layer_order(L: int):
+    """The layers as a weight file that sorts them by name stores them
+    ("GPT-2ベースの3000バイトCで実装されたChatGPTクローン", 重みの読み込み): by the text of
+    the decimal index."""
+    return sorted(range(L), key=str)
+
+
+def permute_layers(m, params, to_lexicographic: bool):
+    """A flat parameter array (layer-major: wte, wpe, the layer blocks, ln_f) with its
+    layer blocks moved between numeric and lexicographic layer order."""
+    C, L = m.channels, m.num_layers
+    head = (m.vocab_size + m.max_seq_len) * C
+    block = 12 * C * C + 13 * C
+    p = np.asarray(params)
+    blocks = [p[head + l * block: head + (l + 1) * block] for l in range(L)]
+    order = lexicographic_layer_order(L)
+    if to_lexicographic:
+        new = [blocks[l] for l in order]
+    else:
+        new = [None] * L
+        for k, l in enumerate(order):
+            new[l] = blocks[k]
+    return np.concatenate([p[:head]] + new + [p[head + L * block:]])

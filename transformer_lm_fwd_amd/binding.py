@@ -27,7 +27,9 @@ T_LN2, T_LN2_STATS, T_FCH, T_FCH_GELU, T_RESIDUAL3 = 22, 23, 24, 25, 26
 EXPORTS = ("gpt2_alloc_arena", "gpt2_free_arena", "gpt2_sync_weights", "gpt2_forward", "gpt2_backward",
            "gpt2_adamw_step", "gpt2_backward_adamw", "gpt2_tensor_info", "gpt2_num_parameters", "gpt2_profile",
            "gpt2_profile_read", "gpt2_gen_alloc", "gpt2_gen_free", "gpt2_gen_length", "gpt2_gen_prefill",
-           "gpt2_gen_decode", "gpt2_sample_topk", "gpt2_last_error")
+           "gpt2_gen_decode", "gpt2_sample_topk", "gpt2_tokens_count", "gpt2_tokens_batch",
+           "gpt2_params_permute", "gpt2_checkpoint_write", "gpt2_checkpoint_read", "gpt2_last_error")
+GPT2_ORDER_NUMERIC, GPT2_ORDER_LEXICOGRAPHIC = 0, 1
 
 
 class gpt2_config(ctypes.Structure):
@@ -78,8 +80,15 @@ def lib():
         L.gpt2_gen_prefill.argtypes = [vp, vp, i32, vp, vp]
         L.gpt2_gen_decode.argtypes = [vp, vp, vp, vp]
         L.gpt2_sample_topk.argtypes = [vp, i32, i32, i64, i32, f32, vp, vp]
+        cp = ctypes.c_char_p
+        L.gpt2_tokens_count.argtypes = [cp]
+        L.gpt2_tokens_count.restype = i64
+        L.gpt2_tokens_batch.argtypes = [cp, i32, i32, i64, vp, vp]
+        L.gpt2_params_permute.argtypes = [cfgp, vp, vp, i32, i32]
+        L.gpt2_checkpoint_write.argtypes = [cp, cfgp, i32, vp, vp, vp]
+        L.gpt2_checkpoint_read.argtypes = [cp, cfgp, ctypes.POINTER(i32), vp, vp, vp, ctypes.POINTER(i32)]
         for name in EXPORTS:
-            if name not in ("gpt2_num_parameters", "gpt2_last_error"):
+            if name not in ("gpt2_num_parameters", "gpt2_last_error", "gpt2_tokens_count"):
                 L[name].restype = ctypes.c_int
         _lib = L
     return _lib
@@ -220,6 +229,44 @@ class Arena:
     def loss(self) -> float:
         return float(self.tensor(T_LOSS).item())
 
+    def eval_loss(self, path: str, num_batches: int, first: int = 0) -> float:
+        """Mean forward loss over batches first .. first + num_batches - 1 of an int32
+        token file (the validation loss of a training run; no backward pass)."""
+        total = 0.0
+        for i in range(first, first + num_batches):
+            x, y = tokens_batch(path, self.B, self.T, i)
+            self.forward(x, y)
+            total += self.loss()
+        return total / num_batches
+
+    # ------------------------------------------------------------------ checkpoints
+    def save_checkpoint(self, path: str, step: int, moments: bool = True) -> None:
+        """Master weights (and the AdamW moments) to a checkpoint file (gpt2_checkpoint_write)."""
+        import numpy as np
+        p = self.tensor(T_PARAMS).cpu().numpy().reshape(-1)
+        m = self.tensor(T_ADAM_M).cpu().numpy().reshape(-1) if moments else None
+        v = self.tensor(T_ADAM_V).cpu().numpy().reshape(-1) if moments else None
+        arrs = [np.ascontiguousarray(a, dtype=np.float32) if a is not None else None for a in (p, m, v)]
+        _check(lib().gpt2_checkpoint_write(path.encode(), ctypes.byref(make_config(self.m)), step,
+                                           *[a.ctypes.data if a is not None else None for a in arrs]))
+
+    def load_checkpoint(self, path: str, stream=None) -> int:
+        """Reads a checkpoint into the master weights (and moments, if the file has them),
+        refreshes the bf16 copy, and returns the file's AdamW step."""
+        import numpy as np
+        import torch
+        n = self.n_params
+        p, m, v = (np.empty(n, np.float32) for _ in range(3))
+        step, has = ctypes.c_int32(0), ctypes.c_int32(0)
+        _check(lib().gpt2_checkpoint_read(path.encode(), ctypes.byref(make_config(self.m)), ctypes.byref(step),
+                                          p.ctypes.data, m.ctypes.data, v.ctypes.data, ctypes.byref(has)))
+        self.tensor(T_PARAMS).view(-1).copy_(torch.from_numpy(p))
+        if has.value:
+            self.tensor(T_ADAM_M).view(-1).copy_(torch.from_numpy(m))
+            self.tensor(T_ADAM_V).view(-1).copy_(torch.from_numpy(v))
+        _check(lib().gpt2_sync_weights(self.h, _stream_ptr(stream)))
+        return int(step.value)
+
     def step(self, inputs, targets, w, t: int, check_ids=True, fused=True) -> None:
         """forward + backward + AdamW with a workload's hyper-parameters (fused: the
         AdamW update overlaps the backward pass; results are bitwise the same)."""
@@ -311,3 +358,29 @@ def sample_topk(logits, k: int, temperature: float, uniforms):
     _check(lib().gpt2_sample_topk(z.ctypes.data, z.shape[0], z.shape[1], z.shape[1], k, temperature, u.ctypes.data,
                                   out.ctypes.data))
     return out
+
+
+def tokens_count(path: str) -> int:
+    n = int(lib().gpt2_tokens_count(path.encode()))
+    if n < 0:
+        _check(n)
+    return n
+
+
+def tokens_batch(path: str, B: int, T: int, batch: int):
+    """Batch `batch` of an int32 token file: (inputs, targets), int32 [B, T] each."""
+    import numpy as np
+    x = np.empty((B, T), np.int32)
+    y = np.empty((B, T), np.int32)
+    _check(lib().gpt2_tokens_batch(path.encode(), B, T, batch, x.ctypes.data, y.ctypes.data))
+    return x, y
+
+
+def params_permute(m, params, from_order: int, to_order: int):
+    """A flat fp32 parameter array reordered between layer orders (gpt2_params_permute)."""
+    import numpy as np
+    src = np.ascontiguousarray(params, dtype=np.float32)
+    dst = np.empty_like(src)
+    _check(lib().gpt2_params_permute(ctypes.byref(make_config(m)), src.ctypes.data, dst.ctypes.data, from_order,
+                                     to_order))
+    return dst

@@ -24,6 +24,12 @@ int fail(int code, const std::string& msg) {
     return code;
 }
 
+}  // namespace
+
+int gpt2::report_error(int code, const char* msg) { return fail(code, msg); }
+
+namespace {
+
 enum { P_LN1W, P_LN1B, P_QKVW, P_QKVB, P_PROJW, P_PROJB, P_LN2W, P_LN2B, P_FCW, P_FCB, P_FCPW, P_FCPB, P_N };
 
 struct LayerActs {

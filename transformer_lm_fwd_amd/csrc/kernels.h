@@ -8,6 +8,9 @@
 
 namespace gpt2 {
 
+// Sets the message gpt2_last_error() returns and returns `code` (host code of the library).
+int report_error(int code, const char* msg);
+
 // Records the launch(es) in its lifetime when the launch profiler is on.
 // True while the launch profiler records (the backward pass then runs on one
 // stream so that overlapping launches do not inflate each other's durations).
