@@ -301,6 +301,68 @@ int gpt2_checkpoint_write(const char* path, const gpt2_config* cfg, int32_t step
 int gpt2_checkpoint_read(const char* path, const gpt2_config* cfg, int32_t* step, float* params, float* m, float* v,
                          int32_t* has_moments);
 
+/* ---------------------------------------------------------------------------
+ * Products below 16 bits: MX FP8.  The llm.c page ("1000 行 C 代码完成 GPT-2 训练的
+ * LLM.c", the paragraph on extensions after the CUDA port) names taking the trainer's
+ * precision down to fp16 and below as the next step.  Below 16 bits this library uses
+ * the block-scaled 8-bit format gfx950's matrix cores take natively (OCP MXFP8):
+ *  - an element is an E4M3 code (sign, 4 exponent bits with bias 7, 3 mantissa bits;
+ *    subnormals at exponent 0; S.1111.111 is NaN; largest magnitude 448);
+ *  - 32 consecutive values along k share one scale 2^e, stored as the byte e + 127;
+ *  - e is the smallest integer with max|x| <= 448 * 2^e over the block (clamped to
+ *    [-127, 127]; an all-zero block has e = -127), and each code is x / 2^e rounded
+ *    to the nearest E4M3 value, ties to the even mantissa (the sign is kept: small
+ *    negatives give -0).
+ * Layouts: codes of a [rows, K] matrix are rows of Kp = K rounded up to 128 bytes
+ * (zero codes past K) with a row stride of at least Kp; scales are
+ * [Kp / 128][rows][4] bytes - byte j of row r's word in k-stage t is the scale of
+ * k-block 4t + j - so that a tile of rows streams its scales in one piece.
+ * --------------------------------------------------------------------------- */
+
+/* GEMM formats of an arena's forward products. */
+enum gpt2_gemm_format {
+    GPT2_GEMM_BF16 = 0,  /* the arena's dtype (default)                                   */
+    GPT2_GEMM_MXFP8 = 1, /* the block (qkv, attention projection, fc, fc projection) and
+                            lm_head products of gpt2_forward / gpt2_gen_prefill run on MX
+                            codes; everything else, and the backward pass, unchanged */
+};
+
+/* Gives a bf16 arena the device memory the MX format needs: codes and scales of the
+ * forward weights (made from the bf16 weight copy at the first MX forward after any
+ * change of the weights: gpt2_sync_weights, gpt2_adamw_step, gpt2_backward_adamw) and
+ * one buffer for the quantized input of the product at hand.  device_base NULL: only
+ * *required_bytes is set.  The memory stays the caller's; it must outlive the arena's
+ * use of the MX format.  Errors: GPT2_E_INVAL (NULL arena, not GPT2_BF16),
+ * GPT2_E_ALIGN (not 256-byte aligned), GPT2_E_SIZE (too small). */
+int gpt2_mx_attach(gpt2_arena* arena, void* device_base, size_t device_bytes, size_t* required_bytes);
+
+/* Selects the format of the forward products.  Errors: GPT2_E_INVAL (unknown format),
+ * GPT2_E_STATE (GPT2_GEMM_MXFP8 before gpt2_mx_attach). */
+int gpt2_set_gemm_format(gpt2_arena* arena, int32_t format);
+
+/* MX quantization: device bf16 x [rows, K] (row stride ldx elements) -> device codes
+ * [rows, Kp] (row stride ldq bytes) and scales [Kp / 128][rows][4] bytes, as defined
+ * above.  Needs K % 8 == 0, ldx >= K (a multiple of 8), ldq >= Kp (a multiple of 16);
+ * inputs finite.  Errors: GPT2_E_INVAL, GPT2_E_HIP. */
+int gpt2_mx_quantize(const void* d_x, int64_t ldx, int32_t rows, int32_t K, void* d_codes, int64_t ldq,
+                     void* d_scales, void* stream);
+
+/* Epilogues of gpt2_mx_gemm (bias may be NULL for none). */
+enum gpt2_mx_epilogue {
+    GPT2_EPI_BIAS = 0,      /* C = A B^T + bias                                    */
+    GPT2_EPI_BIAS_RES = 1,  /* C = residual + A B^T + bias (residual [M, ldc])     */
+    GPT2_EPI_BIAS_GELU = 2, /* C = A B^T + bias, C2 = GELU(C) (C2 [M, ldc])         */
+};
+
+/* The block-scaled product C = A B^T on MX operands, fp32 accumulation, bf16 output:
+ * A codes [M, K] (row stride lda bytes) with scales d_sa [K / 128][M][4], B codes
+ * [N, K] (ldb) with scales d_sb [K / 128][N][4]; K a multiple of 128 (pad with zero
+ * codes), lda / ldb multiples of 16, ldc (elements) >= N and a multiple of 8; bias
+ * fp32 [N].  Errors: GPT2_E_INVAL, GPT2_E_SIZE (operands over 4 GiB), GPT2_E_HIP. */
+int gpt2_mx_gemm(const void* d_qa, const void* d_sa, int64_t lda, const void* d_qb, const void* d_sb, int64_t ldb,
+                 void* d_c, int64_t ldc, int32_t M, int32_t N, int32_t K, int32_t epilogue, const float* d_bias,
+                 const void* d_residual, void* d_c2, void* stream);
+
 /* Message for the last non-OK status on this thread ("" if none). */
 const char* gpt2_last_error(void);
 

@@ -28,8 +28,11 @@ EXPORTS = ("gpt2_alloc_arena", "gpt2_free_arena", "gpt2_sync_weights", "gpt2_for
            "gpt2_adamw_step", "gpt2_backward_adamw", "gpt2_tensor_info", "gpt2_num_parameters", "gpt2_profile",
            "gpt2_profile_read", "gpt2_gen_alloc", "gpt2_gen_free", "gpt2_gen_length", "gpt2_gen_prefill",
            "gpt2_gen_decode", "gpt2_sample_topk", "gpt2_tokens_count", "gpt2_tokens_batch",
-           "gpt2_params_permute", "gpt2_checkpoint_write", "gpt2_checkpoint_read", "gpt2_last_error")
+           "gpt2_params_permute", "gpt2_checkpoint_write", "gpt2_checkpoint_read", "gpt2_mx_attach",
+           "gpt2_set_gemm_format", "gpt2_mx_quantize", "gpt2_mx_gemm", "gpt2_last_error")
 GPT2_ORDER_NUMERIC, GPT2_ORDER_LEXICOGRAPHIC = 0, 1
+GPT2_GEMM_BF16, GPT2_GEMM_MXFP8 = 0, 1
+GPT2_EPI_BIAS, GPT2_EPI_BIAS_RES, GPT2_EPI_BIAS_GELU = 0, 1, 2
 
 
 class gpt2_config(ctypes.Structure):
@@ -87,6 +90,10 @@ def lib():
         L.gpt2_params_permute.argtypes = [cfgp, vp, vp, i32, i32]
         L.gpt2_checkpoint_write.argtypes = [cp, cfgp, i32, vp, vp, vp]
         L.gpt2_checkpoint_read.argtypes = [cp, cfgp, ctypes.POINTER(i32), vp, vp, vp, ctypes.POINTER(i32)]
+        L.gpt2_mx_attach.argtypes = [vp, vp, sz, ctypes.POINTER(sz)]
+        L.gpt2_set_gemm_format.argtypes = [vp, i32]
+        L.gpt2_mx_quantize.argtypes = [vp, i64, i32, i32, vp, i64, vp, vp]
+        L.gpt2_mx_gemm.argtypes = [vp, vp, i64, vp, vp, i64, vp, i64, i32, i32, i32, i32, vp, vp, vp, vp]
         for name in EXPORTS:
             if name not in ("gpt2_num_parameters", "gpt2_last_error", "gpt2_tokens_count"):
                 L[name].restype = ctypes.c_int
@@ -267,6 +274,20 @@ class Arena:
         _check(lib().gpt2_sync_weights(self.h, _stream_ptr(stream)))
         return int(step.value)
 
+    # ------------------------------------------------------------------ MX FP8 products
+    def set_gemm_format(self, fmt: int) -> None:
+        """GPT2_GEMM_BF16 or GPT2_GEMM_MXFP8 for the forward products; the first switch to
+        MXFP8 gives the arena its MX memory (a torch uint8 buffer on the same device)."""
+        import torch
+        if fmt == GPT2_GEMM_MXFP8 and getattr(self, "_mx", None) is None:
+            need = ctypes.c_size_t(0)
+            _check(lib().gpt2_mx_attach(self.h, None, 0, ctypes.byref(need)))
+            buf = torch.empty(int(need.value) + 256, dtype=torch.uint8, device=self.base.device)
+            pad = (-buf.data_ptr()) % 256
+            _check(lib().gpt2_mx_attach(self.h, ctypes.c_void_p(buf.data_ptr() + pad), int(need.value), None))
+            self._mx = buf
+        _check(lib().gpt2_set_gemm_format(self.h, fmt))
+
     def step(self, inputs, targets, w, t: int, check_ids=True, fused=True) -> None:
         """forward + backward + AdamW with a workload's hyper-parameters (fused: the
         AdamW update overlaps the backward pass; results are bitwise the same)."""
@@ -384,3 +405,37 @@ def params_permute(m, params, from_order: int, to_order: int):
     _check(lib().gpt2_params_permute(ctypes.byref(make_config(m)), src.ctypes.data, dst.ctypes.data, from_order,
                                      to_order))
     return dst
+
+
+def mx_quantize(x, stream=None):
+    """MX FP8 quantization (gpt2_mx_quantize) of a device bf16 tensor [rows, K]:
+    returns (codes uint8 [rows, Kp], scales uint8 [Kp / 128, rows, 4]), Kp = K rounded up to 128."""
+    import torch
+    assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
+    R, K = x.shape
+    Kp = (K + 127) // 128 * 128
+    q = torch.empty(R, Kp, dtype=torch.uint8, device=x.device)
+    sc = torch.empty(Kp // 128, R, 4, dtype=torch.uint8, device=x.device)
+    _check(lib().gpt2_mx_quantize(ctypes.c_void_p(x.data_ptr()), x.stride(0), R, K, ctypes.c_void_p(q.data_ptr()),
+                                  Kp, ctypes.c_void_p(sc.data_ptr()), _stream_ptr(stream)))
+    return q, sc
+
+
+def mx_gemm(qa, sa, qb, sb, epilogue=GPT2_EPI_BIAS, bias=None, residual=None, stream=None):
+    """C = A B^T (+ epilogue) on MX operands (gpt2_mx_gemm): qa [M, K], qb [N, K] uint8
+    codes with scales [K / 128, rows, 4]; returns bf16 C [M, N] (and GELU(C) for
+    GPT2_EPI_BIAS_GELU)."""
+    import torch
+    M, K = qa.shape
+    N = qb.shape[0]
+    ldc = (N + 7) // 8 * 8
+    c = torch.empty(M, ldc, dtype=torch.bfloat16, device=qa.device)
+    c2 = torch.empty_like(c) if epilogue == GPT2_EPI_BIAS_GELU else None
+    if residual is not None:
+        r = torch.zeros(M, ldc, dtype=torch.bfloat16, device=qa.device)
+        r[:, :N] = residual
+        residual = r
+    ptr = (lambda t: None if t is None else ctypes.c_void_p(t.data_ptr()))
+    _check(lib().gpt2_mx_gemm(ptr(qa), ptr(sa), qa.stride(0), ptr(qb), ptr(sb), qb.stride(0), ptr(c), ldc, M, N, K,
+                              epilogue, ptr(bias), ptr(residual), ptr(c2), _stream_ptr(stream)))
+    return (c[:, :N], c2[:, :N]) if c2 is not None else c[:, :N]

@@ -400,13 +400,23 @@ __device__ __forceinline__ bool tile_of_block(int bid, int tiles_m, int tiles_n,
     return true;
 }
 
-template <bool AK, bool BKC, int EPI, int BM, int BN, int WM, int WN, int ST = 2>
+// MX = true: the operands are MX FP8 (E4M3 codes, one E8M0 scale per 32 k) instead of
+// bf16.  The tiles hold the same bytes (a 64-element bf16 k-tile is a 128-code MX
+// k-tile), so loads, swizzles and fragment offsets are shared: k below counts 2-byte
+// units.  v_mfma_scale_f32_32x32x64_f8f6f4 takes from lane l (group g = l / 32) the
+// 16 bytes at k 16 g and the 16 at k 32 + 16 g of its 64-code slice - the fragments of
+// two consecutive bf16 slices - and the scale of k-block g of its row (A) or column
+// (B), one byte of a 32-bit register picked by op_sel.  Each stage also holds the
+// scale words of its rows (1 KB for A, 1 KB for B), loaded by waves 0 and 1.
+template <bool AK, bool BKC, int EPI, int BM, int BN, int WM, int WN, int ST = 2, bool MX = false>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a, int k_per_split, int64_t split_stride,
                                                                  uint32_t a_bytes, uint32_t b_bytes) {
     constexpr int NW = WM * WN, NT = 64 * NW;
     using MT = MfmaTraits<bf16>;
     constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
-    constexpr int SA = BM * GBK, STAGE = (BM + BN) * GBK;
+    static_assert(!MX || (AK && BKC && BM <= 256 && BN <= 256 && NW >= 2), "MX: forward layout, <= 256 rows per scale load");
+    constexpr int SCALE_ELEMS = MX ? 1024 : 0;  // 2 KB of scale words per stage
+    constexpr int SA = BM * GBK, STAGE = (BM + BN) * GBK + SCALE_ELEMS;
     constexpr int LDS_ELEMS = ST * STAGE;
     __shared__ __attribute__((aligned(16))) bf16 lds[LDS_ELEMS];
 
@@ -419,6 +429,24 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a, int
     const int kend = min(a.K, kbeg + k_per_split);
     const int nk = kend > kbeg ? (kend - kbeg + GBK - 1) / GBK : 0;
     const dsc_t ra = make_dsc(a.A, a_bytes), rb = make_dsc(a.B, b_bytes);
+    // MX scale words: wave 0 loads A's, wave 1 B's (64 lanes x 16 bytes = 256 rows)
+    const int wv = __builtin_amdgcn_readfirstlane(wave);  // the wave index, known to be uniform
+    dsc_t rsc{};
+    uint32_t srow0 = 0, sstride = 0;
+    if constexpr (MX) {
+        const uint32_t nstage = (uint32_t)(a.K / GBK);  // k-stages of the whole product
+        if (wv == 0) rsc = make_dsc(a.sa, nstage * (uint32_t)a.srows_a * 4u), srow0 = m0, sstride = (uint32_t)a.srows_a;
+        if (wv == 1) rsc = make_dsc(a.sb, nstage * (uint32_t)a.srows_b * 4u), srow0 = n0, sstride = (uint32_t)a.srows_b;
+    }
+    // `wstage`: this wave's 1 KB slot address in the stage (stage base + wave KB), so
+    // wave 0 lands on the A scale words and wave 1 on B's
+    auto scale_issue = [&](uint32_t wstage, int ktile) {
+        if constexpr (MX) {
+            if (wv < 2)
+                dma16(rsc, wstage + (uint32_t)((BM + BN) * GBK * 2), (uint32_t)lane * 16u,
+                      ((uint32_t)ktile * sstride + srow0) * 4u);
+        }
+    };
     using TA = DmaTile<AK, BM, NW>;
     using TB = DmaTile<BKC, BN, NW>;
     TA ta;
@@ -444,6 +472,53 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a, int
     }
     // Fragments of k-slice ks + 1 are read while the MFMAs of slice ks run.
     // `dma(ks)` issues the share of the next tile's loads that goes with k-slice ks.
+    // MX: two 64-code MFMAs per stage, each on the fragments of bf16 slices 2 s and
+    // 2 s + 1; lane group g's scale byte for k-block 2 s + g of the stage is byte 2 s
+    // of its row's stage word shifted right by 8 g.
+    auto compute_mx = [&](const bf16* st, auto&& dma) {
+        typedef int v8i __attribute__((ext_vector_type(8)));
+        const uint32_t* swa = (const uint32_t*)(st + (BM + BN) * GBK);
+        const uint32_t* swb = swa + 256;
+        const int sh = 8 * (lane >> 5);
+        uint32_t sca[TM], scb[TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) sca[i] = swa[(wm * TM + i) * 32 + (lane & 31)] >> sh;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) scb[j] = swb[(wn * TN + j) * 32 + (lane & 31)] >> sh;
+        v8i xa[2][TM], xb[2][TN];
+        auto rd = [&](int buf, int sl) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const u32x4 lo = frag_read<AK>(st, fa[i][2 * sl]), hi = frag_read<AK>(st, fa[i][2 * sl + 1]);
+                xa[buf][i] = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+            }
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const u32x4 lo = frag_read<BKC>(st + SA, fb[j][2 * sl]), hi = frag_read<BKC>(st + SA, fb[j][2 * sl + 1]);
+                xb[buf][j] = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+            }
+        };
+        rd(0, 0);
+        rd(1, 1);
+        dma(0);
+        dma(1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(xa[0][i], xb[0][j], acc[i][j], 0, 0, 0,
+                                                                            (int)sca[i], 0, (int)scb[j]);
+        dma(2);
+        dma(3);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(xa[1][i], xb[1][j], acc[i][j], 0, 0, 2,
+                                                                            (int)sca[i], 2, (int)scb[j]);
+    };
     auto compute = [&](const bf16* st, auto&& dma) {
         u32x4 xa[2][TM], xb[2][TN];
 #pragma unroll
@@ -475,6 +550,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a, int
     for (int s0 = 0; s0 < ST - 1; ++s0)
         if (s0 < nk) {
             const uint32_t k1 = (uint32_t)(kbeg + s0 * GBK);
+            scale_issue(lbase + s0 * STAGE * 2, kbeg / GBK + s0);
             dma_issue<TA::PW, NW>(ra, lbase + s0 * STAGE * 2, ta.voff, k1 * ta.kstep);
             dma_issue<TB::PW, NW>(rb, lbase + (s0 * STAGE + SA) * 2, tb.voff, k1 * tb.kstep);
         }
@@ -506,6 +582,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a, int
         const uint32_t k1 = (uint32_t)(kbeg + (kt + ST - 1) * GBK);
         auto dma = [&](int ks) {
             if (!more) return;
+            if (ks == 0) scale_issue(nxt, kbeg / GBK + kt + ST - 1);
 #pragma unroll
             for (int j = 0; j < TA::PW; ++j)
                 if (j % SPREAD == ks) dma16(ra, nxt + (uint32_t)(NW * j) * 1024u, ta.voff[j], k1 * ta.kstep);
@@ -528,7 +605,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a, int
                 }
             }
         }
-        compute(lds + cur * STAGE, dma);
+        if constexpr (MX) compute_mx(lds + cur * STAGE, dma);
+        else compute(lds + cur * STAGE, dma);
         cur = cur + 1 == ST ? 0 : cur + 1;
     }
     __syncthreads();
@@ -792,6 +870,55 @@ hipError_t gemm(const GemmArgs& a, bool ak, bool bk, int epi, float* ws, size_t 
         case EPI_BIAS_RES: return dispatch_layout<T, EPI_BIAS_RES>(a, ak, bk, 1, a.K, 0, s);
         case EPI_BIAS_GELU: return dispatch_layout<T, EPI_BIAS_GELU>(a, ak, bk, 1, a.K, 0, s);
         case EPI_GELU_BWD: return dispatch_layout<T, EPI_GELU_BWD>(a, ak, bk, 1, a.K, 0, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int EPI>
+static hipError_t launch_mx(const GemmArgs& e, int K, uint32_t ab, uint32_t bb, hipStream_t s) {
+    static std::mutex mu;
+    static std::set<std::string> names;
+    const char* name;
+    {
+        std::string n = std::string("gemm_mxfp8_xwT_") +
+                        (EPI == EPI_BIAS ? "bias" : EPI == EPI_BIAS_RES ? "bias_res" : "bias_gelu") + "_" +
+                        std::to_string(e.M) + "x" + std::to_string(e.N) + "x" + std::to_string(K);
+        std::lock_guard<std::mutex> lk(mu);
+        name = names.insert(n).first->c_str();
+    }
+    const double mn = (double)e.M * e.N;
+    const double out_bytes = EPI == EPI_BIAS ? 2 * mn : 4 * mn;
+    ProfScope prof(s, name, 2.0 * mn * K, ((double)e.M + e.N) * K * (1.0 + 1.0 / 32) + out_bytes);
+    // The bf16 128 x 256 tile with three stages (150 KB of LDS with the scale words).
+    // The 256 x 256 tile does not fit: an MX operand fragment is twice a bf16 one, and
+    // its 128 x 64 wave tiles would spill.
+    const int nt = ((e.N + 255) / 256) * ((e.M + 127) / 128);
+    hipLaunchKernelGGL((gemm_bf16_kernel<true, true, EPI, 128, 256, 2, 4, 3, true>), dim3((nt + 7) / 8 * 8),
+                       dim3(512), 0, s, e, e.K, (int64_t)0, ab, bb);
+    return hipGetLastError();
+}
+
+hipError_t gemm_mx(const GemmArgs& a, int epi, hipStream_t s) {
+    if (a.M <= 0 || a.N <= 0) return hipSuccess;
+    if (a.K <= 0 || a.K % 128 || a.lda % 16 || a.ldb % 16 || a.ldc % 8 || a.lda < a.K || a.ldb < a.K)
+        return hipErrorInvalidValue;
+    if (!a.A || !a.B || !a.C || !a.sa || !a.sb || a.srows_a < a.M || a.srows_b < a.N) return hipErrorInvalidValue;
+    if (epi == EPI_BIAS_RES && !a.R) return hipErrorInvalidValue;
+    if (epi == EPI_BIAS_GELU && !a.C2) return hipErrorInvalidValue;
+    const int64_t ab = (int64_t)a.M * a.lda, bb = (int64_t)a.N * a.ldb;
+    const int64_t sab = (int64_t)(a.K / 128) * a.srows_a * 4, sbb = (int64_t)(a.K / 128) * a.srows_b * 4;
+    if (ab >= (int64_t)1 << 32 || bb >= (int64_t)1 << 32 || sab >= (int64_t)1 << 32 || sbb >= (int64_t)1 << 32)
+        return hipErrorInvalidValue;
+    // the kernel counts k and leading dimensions in 2-byte units (two codes)
+    GemmArgs e = a;
+    e.K = a.K / 2;
+    e.lda = a.lda / 2;
+    e.ldb = a.ldb / 2;
+    e.rowsum = nullptr;
+    switch (epi) {
+        case EPI_BIAS: return launch_mx<EPI_BIAS>(e, a.K, (uint32_t)ab, (uint32_t)bb, s);
+        case EPI_BIAS_RES: return launch_mx<EPI_BIAS_RES>(e, a.K, (uint32_t)ab, (uint32_t)bb, s);
+        case EPI_BIAS_GELU: return launch_mx<EPI_BIAS_GELU>(e, a.K, (uint32_t)ab, (uint32_t)bb, s);
     }
     return hipErrorInvalidValue;
 }

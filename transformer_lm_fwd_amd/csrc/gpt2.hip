@@ -64,6 +64,15 @@ struct gpt2_arena {
     hipEvent_t rd_res[4] = {}, rd_fch[2] = {}, rd_qkv[2] = {}, ev_wte = nullptr, ev_end = nullptr;
     hipEvent_t fork[8] = {};
     int fork_next = 0;
+    // MX FP8 forward products (caller memory from gpt2_mx_attach): E4M3 codes and
+    // block scales of the forward weights, made from the bf16 copy whenever it has
+    // changed, and one buffer for the quantized activation of the product at hand.
+    int gemm_format = GPT2_GEMM_BF16;
+    char* mx = nullptr;
+    size_t mx_bytes = 0;
+    bool mx_stale = true;
+    std::vector<size_t> mxq, mxs;  // [L * 4 + 1]: qkv, proj, fc, fc-proj per layer, then wte
+    size_t mx_act_q = 0, mx_act_s = 0;
 };
 
 // Incremental generation over an arena's parameters (bf16): the key/value cache holds
@@ -185,6 +194,41 @@ P* at(const gpt2_arena* a, size_t off) {
     return (P*)(a->base + off);
 }
 
+int64_t round128(int64_t k) { return (k + 127) / 128 * 128; }
+
+// Rows and k of the MX forward weights: index l * 4 + {0 qkv, 1 proj, 2 fc, 3 fc-proj}, then wte.
+void mx_weight_shape(const gpt2_arena& a, int i, int64_t* rows, int64_t* k) {
+    const int64_t C = a.cfg.channels;
+    const int L = a.cfg.num_layers;
+    if (i == 4 * L) { *rows = a.cfg.vocab_size; *k = C; return; }
+    const int64_t r[4] = {3 * C, C, 4 * C, C}, kk[4] = {C, C, C, 4 * C};
+    *rows = r[i % 4];
+    *k = kk[i % 4];
+}
+
+// Offsets within the MX memory; returns its byte size.
+size_t mx_layout(gpt2_arena& a) {
+    const int L = a.cfg.num_layers;
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = o;
+        o = align_up(o + bytes);
+        return at;
+    };
+    a.mxq.assign(4 * L + 1, 0);
+    a.mxs.assign(4 * L + 1, 0);
+    for (int i = 0; i <= 4 * L; ++i) {
+        int64_t rows, k;
+        mx_weight_shape(a, i, &rows, &k);
+        a.mxq[i] = take((size_t)rows * round128(k));
+        a.mxs[i] = take((size_t)rows * round128(k) / 32);
+    }
+    const int64_t BT = (int64_t)a.B * a.T, k4 = round128(4 * (int64_t)a.cfg.channels);
+    a.mx_act_q = take((size_t)BT * k4);
+    a.mx_act_s = take((size_t)BT * k4 / 32);
+    return o;
+}
+
 int hip_check(hipError_t e, const char* what) {
     if (e != hipSuccess) return fail(GPT2_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
     return GPT2_OK;
@@ -287,7 +331,49 @@ struct Model {
         return GPT2_OK;
     }
 
+    uint8_t* mxp(size_t off) const { return (uint8_t*)(a->mx + off); }
+
+    // MX codes and scales of the forward weights from the bf16 copy.
+    int mx_refresh() {
+        const bf16* w16 = at<bf16>(a, a->params16);
+        for (int i = 0; i <= 4 * L; ++i) {
+            int64_t rows, k;
+            mx_weight_shape(*a, i, &rows, &k);
+            static constexpr int which[4] = {P_QKVW, P_PROJW, P_FCW, P_FCPW};
+            const int64_t off = i == 4 * L ? a->o_wte : lp(i / 4, which[i % 4]);
+            CHECK(mx_quantize(w16 + off, k, (int)rows, (int)k, mxp(a->mxq[i]), round128(k), mxp(a->mxs[i]), s),
+                  "mx weights");
+        }
+        a->mx_stale = false;
+        return GPT2_OK;
+    }
+
+    // A forward product Y = X W^T (+ epilogue) with X [BT, K] dense and W (N, K) at
+    // parameter offset w_off (MX index wi).  With the MX FP8 format, X is quantized
+    // into the arena's MX buffer first and the product runs on the MX codes.
+    int fwd_gemm(const T* X, int K, int64_t w_off, int wi, int N, T* Y, int64_t ldc, int epi,
+                 const float* bias = nullptr, const void* R = nullptr, void* C2 = nullptr) {
+        if constexpr (sizeof(T) == 2) {
+            if (a->gemm_format == GPT2_GEMM_MXFP8) {
+                const int64_t Kp = round128(K);
+                uint8_t *q = mxp(a->mx_act_q), *sc = mxp(a->mx_act_s);
+                CHECK(mx_quantize((const bf16*)X, K, BT, K, q, Kp, sc, s), "mx quantize");
+                GemmArgs g{};
+                g.A = q; g.B = mxp(a->mxq[wi]); g.C = Y; g.C2 = C2; g.R = R; g.bias = bias;
+                g.M = BT; g.N = N; g.K = (int)Kp; g.lda = Kp; g.ldb = Kp; g.ldc = ldc;
+                g.sa = sc; g.sb = mxp(a->mxs[wi]); g.srows_a = BT; g.srows_b = N;
+                CHECK(gemm_mx(g, epi, s), "mx gemm");
+                return GPT2_OK;
+            }
+        }
+        return gemm_call(X, K, true, weight(w_off), K, true, Y, ldc, BT, N, K, epi, bias, R, C2);
+    }
+
     int forward(const int32_t* inp, const int32_t* tgt) {
+        if (a->gemm_format == GPT2_GEMM_MXFP8 && a->mx_stale) {
+            int rc = mx_refresh();
+            if (rc) return rc;
+        }
         CHECK(encoder_forward<T>(act(a->encoded), inp, master(a->o_wte), master(a->o_wpe), BT, S, C, s), "encoder");
         for (int l = 0; l < L; ++l) {
             const LayerActs& x = a->la[l];
@@ -296,30 +382,30 @@ struct Model {
                                        C, s), "ln1");
             int rc;
             // qkv = ln1 W_qkv^T + b
-            if ((rc = gemm_call(act(x.ln1), C, true, weight(lp(l, P_QKVW)), C, true, act(x.qkv), 3 * C, BT, 3 * C, C,
-                                EPI_BIAS, master(lp(l, P_QKVB)))))
+            if ((rc = fwd_gemm(act(x.ln1), C, lp(l, P_QKVW), 4 * l, 3 * C, act(x.qkv), 3 * C, EPI_BIAS,
+                               master(lp(l, P_QKVB)))))
                 return rc;
             CHECK(attention_forward<T>(act(x.atty), f32(x.lse), act(x.qkv), B, S, C, NH, s), "attention");
             // res2 = xin + atty W_proj^T + b
-            if ((rc = gemm_call(act(x.atty), C, true, weight(lp(l, P_PROJW)), C, true, act(x.res2), C, BT, C, C,
-                                EPI_BIAS_RES, master(lp(l, P_PROJB)), xin)))
+            if ((rc = fwd_gemm(act(x.atty), C, lp(l, P_PROJW), 4 * l + 1, C, act(x.res2), C, EPI_BIAS_RES,
+                               master(lp(l, P_PROJB)), xin)))
                 return rc;
             CHECK(layernorm_forward<T>(act(x.ln2), f32(x.ln2s), act(x.res2), master(lp(l, P_LN2W)),
                                        master(lp(l, P_LN2B)), BT, C, s), "ln2");
             // fch = ln2 W_fc^T + b, fchg = gelu(fch)
-            if ((rc = gemm_call(act(x.ln2), C, true, weight(lp(l, P_FCW)), C, true, act(x.fch), 4 * C, BT, 4 * C, C,
-                                EPI_BIAS_GELU, master(lp(l, P_FCB)), nullptr, act(x.fchg))))
+            if ((rc = fwd_gemm(act(x.ln2), C, lp(l, P_FCW), 4 * l + 2, 4 * C, act(x.fch), 4 * C, EPI_BIAS_GELU,
+                               master(lp(l, P_FCB)), nullptr, act(x.fchg))))
                 return rc;
             // res3 = res2 + fchg W_fcproj^T + b
-            if ((rc = gemm_call(act(x.fchg), 4 * C, true, weight(lp(l, P_FCPW)), 4 * C, true, act(x.res3), C, BT, C,
-                                4 * C, EPI_BIAS_RES, master(lp(l, P_FCPB)), act(x.res2))))
+            if ((rc = fwd_gemm(act(x.fchg), 4 * C, lp(l, P_FCPW), 4 * l + 3, C, act(x.res3), C, EPI_BIAS_RES,
+                               master(lp(l, P_FCPB)), act(x.res2))))
                 return rc;
         }
         CHECK(layernorm_forward<T>(act(a->lnf), f32(a->lnfs), act(a->la[L - 1].res3), master(a->o_lnfw),
                                    master(a->o_lnfb), BT, C, s), "lnf");
         // logits = lnf wte^T (tied lm_head, no bias); row stride Vp
         int rc;
-        if ((rc = gemm_call(act(a->lnf), C, true, weight(a->o_wte), C, true, act(a->logits), Vp, BT, V, C, EPI_BIAS)))
+        if ((rc = fwd_gemm(act(a->lnf), C, a->o_wte, 4 * L, V, act(a->logits), Vp, EPI_BIAS)))
             return rc;
         if (tgt) {
             CHECK(crossentropy_fused<T>(act(a->logits), f32(a->losses), tgt, BT, V, Vp, 1.0f / BT, s), "crossentropy");
@@ -532,6 +618,7 @@ int gpt2_free_arena(gpt2_arena* a) {
 
 int gpt2_sync_weights(gpt2_arena* a, void* stream) {
     if (!a) return fail(GPT2_E_INVAL, "arena is NULL");
+    a->mx_stale = true;
     if (a->dtype == GPT2_BF16)
         return hip_check(cast_bf16(at<bf16>(a, a->params16), at<float>(a, a->params), a->nparams, (hipStream_t)stream),
                          "cast");
@@ -560,6 +647,7 @@ int gpt2_adamw_step(gpt2_arena* a, float lr, float beta1, float beta2, float eps
                     void* stream) {
     if (!a) return fail(GPT2_E_INVAL, "arena is NULL");
     if (step < 1) return fail(GPT2_E_INVAL, "step must be >= 1");
+    a->mx_stale = true;
     return adamw_range(a, adam_args(lr, beta1, beta2, eps, weight_decay, step), 0, a->nparams, (hipStream_t)stream);
 }
 
@@ -569,9 +657,76 @@ int gpt2_backward_adamw(gpt2_arena* a, float lr, float beta1, float beta2, float
     if (step < 1) return fail(GPT2_E_INVAL, "step must be >= 1");
     if (!a->loss_ready) return fail(GPT2_E_STATE, "backward needs a preceding forward with targets");
     a->loss_ready = false;
+    a->mx_stale = true;
     const AdamArgs o = adam_args(lr, beta1, beta2, eps, weight_decay, step);
     return a->dtype == GPT2_BF16 ? Model<bf16>(a, (hipStream_t)stream).backward(&o)
                                  : Model<float>(a, (hipStream_t)stream).backward(&o);
+}
+
+int gpt2_mx_attach(gpt2_arena* a, void* device_base, size_t device_bytes, size_t* required_bytes) {
+    if (!a) return fail(GPT2_E_INVAL, "arena is NULL");
+    if (a->dtype != GPT2_BF16) return fail(GPT2_E_INVAL, "MX FP8 products need a bf16 arena");
+    const size_t need = mx_layout(*a);
+    if (required_bytes) *required_bytes = need;
+    if (!device_base) return GPT2_OK;
+    if ((uintptr_t)device_base % kAlign) return fail(GPT2_E_ALIGN, "device_base must be 256-byte aligned");
+    if (device_bytes < need) return fail(GPT2_E_SIZE, "MX buffer too small: need " + std::to_string(need) + " bytes");
+    a->mx = (char*)device_base;
+    a->mx_bytes = device_bytes;
+    a->mx_stale = true;
+    return GPT2_OK;
+}
+
+int gpt2_set_gemm_format(gpt2_arena* a, int32_t format) {
+    if (!a) return fail(GPT2_E_INVAL, "arena is NULL");
+    if (format == GPT2_GEMM_BF16) {
+        a->gemm_format = format;
+        return GPT2_OK;
+    }
+    if (format != GPT2_GEMM_MXFP8) return fail(GPT2_E_INVAL, "unknown GEMM format");
+    if (!a->mx) return fail(GPT2_E_STATE, "GPT2_GEMM_MXFP8 needs memory from gpt2_mx_attach");
+    a->gemm_format = format;
+    a->mx_stale = true;
+    return GPT2_OK;
+}
+
+int gpt2_mx_quantize(const void* d_x, int64_t ldx, int32_t rows, int32_t K, void* d_codes, int64_t ldq,
+                     void* d_scales, void* stream) {
+    if (rows < 0 || K < 0) return fail(GPT2_E_INVAL, "negative size");
+    if (rows == 0 || K == 0) return GPT2_OK;
+    if (!d_x || !d_codes || !d_scales) return fail(GPT2_E_INVAL, "x, codes and scales are required");
+    if (K % 8 || ldx < K || ldx % 8 || ldq < round128(K) || ldq % 16)
+        return fail(GPT2_E_INVAL, "need K % 8 == 0, ldx >= K (a multiple of 8), ldq >= K rounded up to 128 (a multiple of 16)");
+    return hip_check(mx_quantize((const bf16*)d_x, ldx, rows, K, (uint8_t*)d_codes, ldq, (uint8_t*)d_scales,
+                                 (hipStream_t)stream),
+                     "mx_quantize");
+}
+
+int gpt2_mx_gemm(const void* d_qa, const void* d_sa, int64_t lda, const void* d_qb, const void* d_sb, int64_t ldb,
+                 void* d_c, int64_t ldc, int32_t M, int32_t N, int32_t K, int32_t epilogue, const float* d_bias,
+                 const void* d_residual, void* d_c2, void* stream) {
+    if (M < 0 || N < 0 || K < 0) return fail(GPT2_E_INVAL, "negative size");
+    if (M == 0 || N == 0) return GPT2_OK;
+    if (K == 0 || K % 128) return fail(GPT2_E_INVAL, "K must be a positive multiple of 128 (zero-padded codes)");
+    if (lda < K || ldb < K || lda % 16 || ldb % 16 || ldc < N || ldc % 8)
+        return fail(GPT2_E_INVAL, "need lda, ldb >= K (multiples of 16) and ldc >= N (a multiple of 8)");
+    if (!d_qa || !d_sa || !d_qb || !d_sb || !d_c) return fail(GPT2_E_INVAL, "operands and output are required");
+    int epi;
+    switch (epilogue) {
+        case GPT2_EPI_BIAS: epi = EPI_BIAS; break;
+        case GPT2_EPI_BIAS_RES: epi = EPI_BIAS_RES; break;
+        case GPT2_EPI_BIAS_GELU: epi = EPI_BIAS_GELU; break;
+        default: return fail(GPT2_E_INVAL, "unknown epilogue");
+    }
+    if (epi == EPI_BIAS_RES && !d_residual) return fail(GPT2_E_INVAL, "GPT2_EPI_BIAS_RES needs the residual");
+    if (epi == EPI_BIAS_GELU && !d_c2) return fail(GPT2_E_INVAL, "GPT2_EPI_BIAS_GELU needs the second output");
+    if ((int64_t)M * lda >= ((int64_t)1 << 32) || (int64_t)N * ldb >= ((int64_t)1 << 32))
+        return fail(GPT2_E_SIZE, "operands over 4 GiB");
+    GemmArgs g{};
+    g.A = d_qa; g.B = d_qb; g.C = d_c; g.C2 = d_c2; g.R = d_residual; g.bias = d_bias;
+    g.M = M; g.N = N; g.K = K; g.lda = lda; g.ldb = ldb; g.ldc = ldc;
+    g.sa = (const uint8_t*)d_sa; g.sb = (const uint8_t*)d_sb; g.srows_a = M; g.srows_b = N;
+    return hip_check(gemm_mx(g, epi, (hipStream_t)stream), "mx gemm");
 }
 
 int gpt2_tensor_info(const gpt2_arena* a, int32_t id, int32_t layer, size_t* byte_offset, int64_t* rows,

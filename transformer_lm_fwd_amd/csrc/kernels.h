@@ -47,6 +47,12 @@ struct GemmArgs {
     float* rowsum;
     int M, N, K;
     int64_t lda, ldb, ldc;
+    // MX FP8 operands (gemm_mx only): E8M0 block scales of A and B, laid out
+    // [K / 128][rows][4] bytes (byte j of row r's word in k-stage t: the scale of
+    // k-block 4 t + j), with srows_a / srows_b rows per k-stage.
+    const uint8_t* sa;
+    const uint8_t* sb;
+    int64_t srows_a, srows_b;
 };
 
 // Returns hipSuccess or the launch error.  T in {float, bf16}: operand type;
@@ -97,6 +103,20 @@ hipError_t cast_bf16(bf16* out, const float* in, int64_t n, hipStream_t s);
 // out[i] = sum over k < splits of ws[k * stride + i], i < n (fixed order).
 hipError_t splitk_reduce(float* out, const float* ws, int splits, int64_t n, int64_t stride, hipStream_t s);
 // C (bf16 [M, N], row stride ldc) = bias + sum of `splits` dense fp32 M x N partials.
+// MX FP8 ("1000 行 C 代码完成 GPT-2 训练的 LLM.c": precision below 16 bits).  E4M3
+// codes with one power-of-two scale per 32 values along k.
+// mx_quantize: x bf16 [R, K] (row stride ldx elements, K % 8 == 0) -> q [R, Kp] codes
+// (row stride ldq bytes, Kp = K rounded up to 128, zero codes past K) and the scales
+// sc [Kp / 128][R][4] (see GemmArgs).  Scale of a block: the smallest 2^e with
+// amax <= 448 * 2^e (e in [-127, 127], all-zero blocks -127); codes: x / 2^e rounded
+// to nearest even.
+hipError_t mx_quantize(const bf16* x, int64_t ldx, int R, int K, uint8_t* q, int64_t ldq, uint8_t* sc,
+                       hipStream_t s);
+// C = A B^T (+ the epilogue) for MX operands: A codes [M, K] (lda bytes), B codes
+// [N, K] (ldb bytes), K a multiple of 128 (zero-padded), lda / ldb multiples of 16;
+// scales a.sa / a.sb; output bf16 with EPI_BIAS, EPI_BIAS_RES or EPI_BIAS_GELU.
+hipError_t gemm_mx(const GemmArgs& a, int epi, hipStream_t s);
+
 hipError_t splitk_reduce_bf16(bf16* C, int64_t ldc, const float* ws, int splits, int M, int N, const float* bias,
                               hipStream_t s);
 

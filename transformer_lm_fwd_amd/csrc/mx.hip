@@ -1,0 +1,87 @@
+// MX FP8 quantization: bf16 rows -> E4M3 codes with one shared power-of-two scale
+// per 32 consecutive values ("1000 行 C 代码完成 GPT-2 训练的 LLM.c": the precision
+// step below 16 bits; the block-scaled E4M3 format is the one gfx950's matrix cores
+// take natively, v_mfma_scale_f32_32x32x64_f8f6f4).
+//
+// Scale of a block with largest magnitude amax: the smallest 2^e with amax <= 448 2^e,
+// so nothing is clipped; e is clamped to E8M0's [-127, 127] and an all-zero block
+// gets -127.  Elements: x 2^-e rounded to the nearest E4M3 value, ties to the even
+// mantissa, by v_cvt_pk_fp8_f32 (gfx950 converts to the OCP E4M3 encoding with the
+// rounding mode's round-to-nearest-even).
+//
+// Layout written (what the MX GEMM streams into LDS): codes [R, Kp] with row stride
+// ldq bytes, Kp = K rounded up to 128 and zero codes past K; scales
+// [Kp / 128][R][4] bytes, so one k-stage of 128 codes of a run of rows has its
+// scales in one contiguous run of 4-byte words.
+#include "kernels.h"
+
+namespace gpt2 {
+
+namespace {
+
+// Exponent e of the scale: the smallest integer with amax <= 448 2^e.  For a normal
+// amax = 1.m 2^E, amax / 2^(E-8) = 1.m 2^8 lies in [256, 512) and exceeds 448 = 1.75 2^8
+// exactly when the 23-bit mantissa field exceeds 0x600000.
+__device__ __forceinline__ int mx_exponent(float amax) {
+    const uint32_t b = __float_as_uint(amax);
+    if (amax == 0.f) return -127;
+    const int E = (int)((b >> 23) & 0xFF) - 127;  // subnormal amax: far below the clamp
+    int e = E - 8 + ((b & 0x7FFFFF) > 0x600000 ? 1 : 0);
+    return e < -127 ? -127 : e > 127 ? 127 : e;
+}
+
+// One thread: 8 consecutive values of a row; 4 threads: one block of 32; 16 threads:
+// one k-stage of 128 (their scales leave as one 4-byte word).
+__global__ __launch_bounds__(256) void mx_quantize_kernel(const bf16* __restrict__ x, int64_t ldx, int R, int K,
+                                                          int Kp, uint8_t* __restrict__ q, int64_t ldq,
+                                                          uint8_t* __restrict__ sc) {
+    const int cpr = Kp / 8;  // chunks per row (a multiple of 16)
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const bool live = idx < (int64_t)R * cpr;  // a whole 16-lane group is live or not
+    const int row = live ? (int)(idx / cpr) : 0, c = live ? (int)(idx % cpr) : 0;
+    const int k0 = c * 8;
+    float v[8];
+    if (live && k0 < K) {
+        unpack16<bf16>(ld16(x + (int64_t)row * ldx + k0), v);  // K % 8 == 0: all 8 or none
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = 0.f;
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1));
+    amax = fmaxf(amax, __shfl_xor(amax, 2));
+    const int ex = mx_exponent(amax);
+    uint32_t w[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const float a0 = __builtin_amdgcn_ldexpf(v[4 * h + 0], -ex), a1 = __builtin_amdgcn_ldexpf(v[4 * h + 1], -ex);
+        const float a2 = __builtin_amdgcn_ldexpf(v[4 * h + 2], -ex), a3 = __builtin_amdgcn_ldexpf(v[4 * h + 3], -ex);
+        int r = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, 0, false);
+        r = __builtin_amdgcn_cvt_pk_fp8_f32(a2, a3, r, true);
+        w[h] = (uint32_t)r;
+    }
+    // scale bytes of the stage's 4 blocks, gathered by the stage's first lane
+    const uint32_t sb = (uint32_t)(ex + 127);
+    const uint32_t s1 = __shfl_down(sb, 4), s2 = __shfl_down(sb, 8), s3 = __shfl_down(sb, 12);
+    if (!live) return;
+    *(uint2*)(q + (int64_t)row * ldq + k0) = make_uint2(w[0], w[1]);
+    if ((c & 15) == 0) *(uint32_t*)(sc + ((int64_t)(c / 16) * R + row) * 4) = sb | (s1 << 8) | (s2 << 16) | (s3 << 24);
+}
+
+}  // namespace
+
+hipError_t mx_quantize(const bf16* x, int64_t ldx, int R, int K, uint8_t* q, int64_t ldq, uint8_t* sc,
+                       hipStream_t s) {
+    if (R <= 0 || K <= 0) return hipSuccess;
+    const int Kp = (K + 127) / 128 * 128;
+    if (K % 8 || ldx < K || ldx % 8 || ldq < Kp || ldq % 16) return hipErrorInvalidValue;
+    const int64_t threads = (int64_t)R * (Kp / 8);
+    ProfScope prof(s, "mx_quantize", 0.0, (double)R * K * 2 + (double)R * Kp + (double)R * Kp / 32);
+    hipLaunchKernelGGL(mx_quantize_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, x, ldx, R, K,
+                       Kp, q, ldq, sc);
+    return hipGetLastError();
+}
+
+}  // namespace gpt2
