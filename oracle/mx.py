@@ -52,7 +52,7 @@ _POS_VALS = E4M3[_POS_CODES]
 
 def e4m3_encode(v):
     """Nearest E4M3 code to each value (ties: the code with the even mantissa; above
-    448 in magnitude: 448)."""
+    448 in magnitude: 448; the sign bit is the input's, so small negatives give -0)."""
     v = np.asarray(v, dtype=np.float64)
     a = np.minimum(np.abs(v), MAX_E4M3)
     hi = np.clip(np.searchsorted(_POS_VALS, a, side="left"), 0, _POS_VALS.size - 1)
@@ -60,8 +60,8 @@ def e4m3_encode(v):
     dlo, dhi = a - _POS_VALS[lo], _POS_VALS[hi] - a
     pick_hi = (dhi < dlo) | ((dhi == dlo) & (_POS_CODES[hi] % 2 == 0))
     code = np.where(pick_hi, _POS_CODES[hi], _POS_CODES[lo])
-    neg = np.signbit(v) & (code != 0)
-    return (code | (neg.astype(np.int64) << 7)).astype(np.uint8)
+    # the sign is kept, also when the magnitude rounds to zero (-0 is code 0x80)
+    return (code | (np.signbit(v).astype(np.int64) << 7)).astype(np.uint8)
 
 
 def block_exponent(amax):
