@@ -340,6 +340,16 @@ int gpt2_mx_attach(gpt2_arena* arena, void* device_base, size_t device_bytes, si
  * GPT2_E_STATE (GPT2_GEMM_MXFP8 before gpt2_mx_attach). */
 int gpt2_set_gemm_format(gpt2_arena* arena, int32_t format);
 
+/* The arena's MX input buffers, as byte offsets into the memory given to
+ * gpt2_mx_attach: codes [rows, ld] and scales [ld / 128][rows][4] of
+ *  GPT2_MX_BUF_INPUT - the C-wide product inputs (LayerNorm outputs, attention
+ *                      output); after a forward pass: ln_f's output,
+ *  GPT2_MX_BUF_GELU  - the 4C-wide GELU output; after a forward pass: the last layer's.
+ * rows = B*T.  Errors: GPT2_E_INVAL, GPT2_E_STATE (no MX memory). */
+enum gpt2_mx_buffer_id { GPT2_MX_BUF_INPUT = 0, GPT2_MX_BUF_GELU = 1 };
+int gpt2_mx_buffer(const gpt2_arena* arena, int32_t which, size_t* codes_offset, size_t* scales_offset,
+                   int64_t* rows, int64_t* ld);
+
 /* MX quantization: device bf16 x [rows, K] (row stride ldx elements) -> device codes
  * [rows, Kp] (row stride ldq bytes) and scales [Kp / 128][rows][4] bytes, as defined
  * above.  Needs K % 8 == 0, ldx >= K (a multiple of 8), ldq >= Kp (a multiple of 16);

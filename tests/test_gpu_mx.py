@@ -212,3 +212,26 @@ def test_mx_weights_follow_every_update():
     r.forward(x, y)
     np.testing.assert_array_equal(to_np(r.tensor(b.T_LOGITS)), z1)
     assert losses[-1] < losses[0]   # training through MX forward products still lowers the loss
+
+
+def test_producer_written_codes_equal_the_quantizer_of_the_stored_activations():
+    # In MX mode LayerNorm and the fc product's GELU epilogue write the codes of their
+    # bf16 outputs themselves; they must be exactly what gpt2_mx_quantize makes of the
+    # stored activations (and so, by the test above, what the oracle makes).
+    from transformer_lm_fwd_amd import binding as b
+    for m, B, T in [(ModelShape(160, 301, 2, 2, 128), 2, 64), (ModelShape(64, 97, 1, 3, 96), 3, 40)]:
+        w = Workload("mx_fused", m, B, T, "bf16", "uniform", index=52)
+        announce("mx_fused_codes", C=m.channels, B=B, T=T)
+        x, y = synth.inputs_targets(w)
+        a = gpu_arena(w, rand_params(m, seed=52))
+        a.set_gemm_format(b.GPT2_GEMM_MXFP8)
+        a.forward(x, y)
+        q, sc = a.mx_buffer(b.GPT2_MX_BUF_INPUT)
+        rq, rs = b.mx_quantize(a.tensor(b.T_LNF))
+        np.testing.assert_array_equal(to_np(q), to_np(rq))
+        np.testing.assert_array_equal(to_np(sc), to_np(rs))
+        if (4 * m.channels) % 128 == 0:
+            q, sc = a.mx_buffer(b.GPT2_MX_BUF_GELU)
+            rq, rs = b.mx_quantize(a.tensor(b.T_FCH_GELU, m.num_layers - 1))
+            np.testing.assert_array_equal(to_np(q), to_np(rq))
+            np.testing.assert_array_equal(to_np(sc), to_np(rs))

@@ -29,10 +29,11 @@ EXPORTS = ("gpt2_alloc_arena", "gpt2_free_arena", "gpt2_sync_weights", "gpt2_for
            "gpt2_profile_read", "gpt2_gen_alloc", "gpt2_gen_free", "gpt2_gen_length", "gpt2_gen_prefill",
            "gpt2_gen_decode", "gpt2_sample_topk", "gpt2_tokens_count", "gpt2_tokens_batch",
            "gpt2_params_permute", "gpt2_checkpoint_write", "gpt2_checkpoint_read", "gpt2_mx_attach",
-           "gpt2_set_gemm_format", "gpt2_mx_quantize", "gpt2_mx_gemm", "gpt2_last_error")
+           "gpt2_set_gemm_format", "gpt2_mx_buffer", "gpt2_mx_quantize", "gpt2_mx_gemm", "gpt2_last_error")
 GPT2_ORDER_NUMERIC, GPT2_ORDER_LEXICOGRAPHIC = 0, 1
 GPT2_GEMM_BF16, GPT2_GEMM_MXFP8 = 0, 1
 GPT2_EPI_BIAS, GPT2_EPI_BIAS_RES, GPT2_EPI_BIAS_GELU = 0, 1, 2
+GPT2_MX_BUF_INPUT, GPT2_MX_BUF_GELU = 0, 1
 
 
 class gpt2_config(ctypes.Structure):
@@ -92,6 +93,8 @@ def lib():
         L.gpt2_checkpoint_read.argtypes = [cp, cfgp, ctypes.POINTER(i32), vp, vp, vp, ctypes.POINTER(i32)]
         L.gpt2_mx_attach.argtypes = [vp, vp, sz, ctypes.POINTER(sz)]
         L.gpt2_set_gemm_format.argtypes = [vp, i32]
+        L.gpt2_mx_buffer.argtypes = [vp, i32, ctypes.POINTER(sz), ctypes.POINTER(sz), ctypes.POINTER(i64),
+                                     ctypes.POINTER(i64)]
         L.gpt2_mx_quantize.argtypes = [vp, i64, i32, i32, vp, i64, vp, vp]
         L.gpt2_mx_gemm.argtypes = [vp, vp, i64, vp, vp, i64, vp, i64, i32, i32, i32, i32, vp, vp, vp, vp]
         for name in EXPORTS:
@@ -287,6 +290,18 @@ class Arena:
             _check(lib().gpt2_mx_attach(self.h, ctypes.c_void_p(buf.data_ptr() + pad), int(need.value), None))
             self._mx = buf
         _check(lib().gpt2_set_gemm_format(self.h, fmt))
+
+    def mx_buffer(self, which: int):
+        """Views (codes [rows, ld] uint8, scales [ld / 128, rows, 4] uint8) of one of the
+        arena's MX input buffers (gpt2_mx_buffer)."""
+        qo, so, rows, ld = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_int64(), ctypes.c_int64()
+        _check(lib().gpt2_mx_buffer(self.h, which, ctypes.byref(qo), ctypes.byref(so), ctypes.byref(rows),
+                                    ctypes.byref(ld)))
+        pad = (-self._mx.data_ptr()) % 256
+        base = self._mx[pad:]
+        r, k = rows.value, ld.value
+        return (base[qo.value:qo.value + r * k].view(r, k),
+                base[so.value:so.value + r * k // 32].view(k // 128, r, 4))
 
     def step(self, inputs, targets, w, t: int, check_ids=True, fused=True) -> None:
         """forward + backward + AdamW with a workload's hyper-parameters (fused: the

@@ -25,6 +25,7 @@
 
 #include "kernels.h"
 #include "lds_dma.h"
+#include "mx_quant.h"
 
 namespace gpt2 {
 
@@ -718,7 +719,19 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a, int
                 bf16* C = (bf16*)a.C;
                 if (full) {
                     st16(C + o, pack16<bf16>(v));
-                    if constexpr (EPI == EPI_BIAS_GELU) st16((bf16*)a.C2 + o, pack16<bf16>(out2));
+                    if constexpr (EPI == EPI_BIAS_GELU) {
+                        st16((bf16*)a.C2 + o, pack16<bf16>(out2));
+                        // MX codes of the stored GELU output: 4 consecutive threads hold a
+                        // 32-block, 16 a 128-column stage (the host asks for this only when
+                        // N % 128 == 0, so a 16-thread group is wholly inside or outside N)
+                        if (a.q2) {
+                            round_bf16_8(out2);
+                            uint32_t cw[2];
+                            const uint32_t word = mx_stage_word(mx_quant8(out2, cw));
+                            *(uint2*)(a.q2 + (int64_t)row * a.ldq2 + col) = make_uint2(cw[0], cw[1]);
+                            if ((tid & 15) == 0) *(uint32_t*)(a.s2 + ((int64_t)(col / 128) * a.M + row) * 4) = word;
+                        }
+                    }
                 } else {
                     for (int e = 0; e < 8 && col + e < a.N; ++e) {
                         C[o + e] = from_f32<bf16>(v[e]);
@@ -900,6 +913,7 @@ static hipError_t launch_mx(const GemmArgs& e, int K, uint32_t ab, uint32_t bb, 
 
 hipError_t gemm_mx(const GemmArgs& a, int epi, hipStream_t s) {
     if (a.M <= 0 || a.N <= 0) return hipSuccess;
+    if (a.q2 && (epi != EPI_BIAS_GELU || a.N % 128 || !a.s2 || a.ldq2 < a.N || a.ldq2 % 16)) return hipErrorInvalidValue;
     if (a.K <= 0 || a.K % 128 || a.lda % 16 || a.ldb % 16 || a.ldc % 8 || a.lda < a.K || a.ldb < a.K)
         return hipErrorInvalidValue;
     if (!a.A || !a.B || !a.C || !a.sa || !a.sb || a.srows_a < a.M || a.srows_b < a.N) return hipErrorInvalidValue;

@@ -72,7 +72,8 @@ struct gpt2_arena {
     size_t mx_bytes = 0;
     bool mx_stale = true;
     std::vector<size_t> mxq, mxs;  // [L * 4 + 1]: qkv, proj, fc, fc-proj per layer, then wte
-    size_t mx_act_q = 0, mx_act_s = 0;
+    size_t mx_in_q = 0, mx_in_s = 0;    // codes of a C-wide product input (LayerNorm, attention)
+    size_t mx_act_q = 0, mx_act_s = 0;  // codes of the 4C-wide GELU output
 };
 
 // Incremental generation over an arena's parameters (bf16): the key/value cache holds
@@ -223,7 +224,9 @@ size_t mx_layout(gpt2_arena& a) {
         a.mxq[i] = take((size_t)rows * round128(k));
         a.mxs[i] = take((size_t)rows * round128(k) / 32);
     }
-    const int64_t BT = (int64_t)a.B * a.T, k4 = round128(4 * (int64_t)a.cfg.channels);
+    const int64_t BT = (int64_t)a.B * a.T, k1 = round128(a.cfg.channels), k4 = round128(4 * (int64_t)a.cfg.channels);
+    a.mx_in_q = take((size_t)BT * k1);
+    a.mx_in_s = take((size_t)BT * k1 / 32);
     a.mx_act_q = take((size_t)BT * k4);
     a.mx_act_s = take((size_t)BT * k4 / 32);
     return o;
@@ -348,20 +351,38 @@ struct Model {
         return GPT2_OK;
     }
 
+    bool mx_on() const { return sizeof(T) == 2 && a->gemm_format == GPT2_GEMM_MXFP8; }
+    // MX codes of a product input: `codes` in buffer (q, s) with row stride ldq.
+    struct MxBuf {
+        uint8_t* q = nullptr;
+        uint8_t* s = nullptr;
+        int64_t ld = 0;
+    };
+    MxBuf mx_in() const { return mx_on() ? MxBuf{mxp(a->mx_in_q), mxp(a->mx_in_s), round128(C)} : MxBuf{}; }
+    MxBuf mx_gelu() const {
+        // the fc epilogue writes the GELU codes itself when 4C is a multiple of 128
+        return mx_on() && (4 * C) % 128 == 0 ? MxBuf{mxp(a->mx_act_q), mxp(a->mx_act_s), round128(4 * C)} : MxBuf{};
+    }
+
     // A forward product Y = X W^T (+ epilogue) with X [BT, K] dense and W (N, K) at
-    // parameter offset w_off (MX index wi).  With the MX FP8 format, X is quantized
-    // into the arena's MX buffer first and the product runs on the MX codes.
+    // parameter offset w_off (MX index wi).  With the MX FP8 format the product runs on
+    // MX codes: those of X already made by its producer (`in`), else quantized here
+    // into the matching buffer; `out2` asks the GELU epilogue for its output's codes.
     int fwd_gemm(const T* X, int K, int64_t w_off, int wi, int N, T* Y, int64_t ldc, int epi,
-                 const float* bias = nullptr, const void* R = nullptr, void* C2 = nullptr) {
+                 const float* bias = nullptr, const void* R = nullptr, void* C2 = nullptr, MxBuf in = {},
+                 MxBuf out2 = {}) {
         if constexpr (sizeof(T) == 2) {
-            if (a->gemm_format == GPT2_GEMM_MXFP8) {
+            if (mx_on()) {
                 const int64_t Kp = round128(K);
-                uint8_t *q = mxp(a->mx_act_q), *sc = mxp(a->mx_act_s);
-                CHECK(mx_quantize((const bf16*)X, K, BT, K, q, Kp, sc, s), "mx quantize");
+                if (!in.q) {
+                    in = K == C ? MxBuf{mxp(a->mx_in_q), mxp(a->mx_in_s), Kp} : MxBuf{mxp(a->mx_act_q), mxp(a->mx_act_s), Kp};
+                    CHECK(mx_quantize((const bf16*)X, K, BT, K, in.q, in.ld, in.s, s), "mx quantize");
+                }
                 GemmArgs g{};
-                g.A = q; g.B = mxp(a->mxq[wi]); g.C = Y; g.C2 = C2; g.R = R; g.bias = bias;
-                g.M = BT; g.N = N; g.K = (int)Kp; g.lda = Kp; g.ldb = Kp; g.ldc = ldc;
-                g.sa = sc; g.sb = mxp(a->mxs[wi]); g.srows_a = BT; g.srows_b = N;
+                g.A = in.q; g.B = mxp(a->mxq[wi]); g.C = Y; g.C2 = C2; g.R = R; g.bias = bias;
+                g.M = BT; g.N = N; g.K = (int)Kp; g.lda = in.ld; g.ldb = Kp; g.ldc = ldc;
+                g.sa = in.s; g.sb = mxp(a->mxs[wi]); g.srows_a = BT; g.srows_b = N;
+                g.q2 = out2.q; g.s2 = out2.s; g.ldq2 = out2.ld;
                 CHECK(gemm_mx(g, epi, s), "mx gemm");
                 return GPT2_OK;
             }
@@ -378,12 +399,13 @@ struct Model {
         for (int l = 0; l < L; ++l) {
             const LayerActs& x = a->la[l];
             const T* xin = l == 0 ? act(a->encoded) : act(a->la[l - 1].res3);
+            const MxBuf mi = mx_in(), mg = mx_gelu();
             CHECK(layernorm_forward<T>(act(x.ln1), f32(x.ln1s), xin, master(lp(l, P_LN1W)), master(lp(l, P_LN1B)), BT,
-                                       C, s), "ln1");
+                                       C, s, mi.q, mi.ld, mi.s), "ln1");
             int rc;
             // qkv = ln1 W_qkv^T + b
             if ((rc = fwd_gemm(act(x.ln1), C, lp(l, P_QKVW), 4 * l, 3 * C, act(x.qkv), 3 * C, EPI_BIAS,
-                               master(lp(l, P_QKVB)))))
+                               master(lp(l, P_QKVB)), nullptr, nullptr, mi)))
                 return rc;
             CHECK(attention_forward<T>(act(x.atty), f32(x.lse), act(x.qkv), B, S, C, NH, s), "attention");
             // res2 = xin + atty W_proj^T + b
@@ -391,21 +413,23 @@ struct Model {
                                master(lp(l, P_PROJB)), xin)))
                 return rc;
             CHECK(layernorm_forward<T>(act(x.ln2), f32(x.ln2s), act(x.res2), master(lp(l, P_LN2W)),
-                                       master(lp(l, P_LN2B)), BT, C, s), "ln2");
+                                       master(lp(l, P_LN2B)), BT, C, s, mi.q, mi.ld, mi.s), "ln2");
             // fch = ln2 W_fc^T + b, fchg = gelu(fch)
             if ((rc = fwd_gemm(act(x.ln2), C, lp(l, P_FCW), 4 * l + 2, 4 * C, act(x.fch), 4 * C, EPI_BIAS_GELU,
-                               master(lp(l, P_FCB)), nullptr, act(x.fchg))))
+                               master(lp(l, P_FCB)), nullptr, act(x.fchg), mi, mg)))
                 return rc;
             // res3 = res2 + fchg W_fcproj^T + b
             if ((rc = fwd_gemm(act(x.fchg), 4 * C, lp(l, P_FCPW), 4 * l + 3, C, act(x.res3), C, EPI_BIAS_RES,
-                               master(lp(l, P_FCPB)), act(x.res2))))
+                               master(lp(l, P_FCPB)), act(x.res2), nullptr, mg)))
                 return rc;
         }
+        const MxBuf mi = mx_in();
         CHECK(layernorm_forward<T>(act(a->lnf), f32(a->lnfs), act(a->la[L - 1].res3), master(a->o_lnfw),
-                                   master(a->o_lnfb), BT, C, s), "lnf");
+                                   master(a->o_lnfb), BT, C, s, mi.q, mi.ld, mi.s), "lnf");
         // logits = lnf wte^T (tied lm_head, no bias); row stride Vp
         int rc;
-        if ((rc = fwd_gemm(act(a->lnf), C, a->o_wte, 4 * L, V, act(a->logits), Vp, EPI_BIAS)))
+        if ((rc = fwd_gemm(act(a->lnf), C, a->o_wte, 4 * L, V, act(a->logits), Vp, EPI_BIAS, nullptr, nullptr, nullptr,
+                           mi)))
             return rc;
         if (tgt) {
             CHECK(crossentropy_fused<T>(act(a->logits), f32(a->losses), tgt, BT, V, Vp, 1.0f / BT, s), "crossentropy");
@@ -687,6 +711,26 @@ int gpt2_set_gemm_format(gpt2_arena* a, int32_t format) {
     if (!a->mx) return fail(GPT2_E_STATE, "GPT2_GEMM_MXFP8 needs memory from gpt2_mx_attach");
     a->gemm_format = format;
     a->mx_stale = true;
+    return GPT2_OK;
+}
+
+int gpt2_mx_buffer(const gpt2_arena* a, int32_t which, size_t* codes_offset, size_t* scales_offset, int64_t* rows,
+                   int64_t* ld) {
+    if (!a || !codes_offset || !scales_offset || !rows || !ld) return fail(GPT2_E_INVAL, "NULL argument");
+    if (!a->mx) return fail(GPT2_E_STATE, "no MX memory attached");
+    const int64_t C = a->cfg.channels;
+    *rows = (int64_t)a->B * a->T;
+    if (which == GPT2_MX_BUF_INPUT) {
+        *codes_offset = a->mx_in_q;
+        *scales_offset = a->mx_in_s;
+        *ld = round128(C);
+    } else if (which == GPT2_MX_BUF_GELU) {
+        *codes_offset = a->mx_act_q;
+        *scales_offset = a->mx_act_s;
+        *ld = round128(4 * C);
+    } else {
+        return fail(GPT2_E_INVAL, "unknown MX buffer");
+    }
     return GPT2_OK;
 }
 

@@ -53,6 +53,12 @@ struct GemmArgs {
     const uint8_t* sa;
     const uint8_t* sb;
     int64_t srows_a, srows_b;
+    // EPI_BIAS_GELU with q2 non-null (N a multiple of 128, bf16 output): also the MX
+    // codes of the bf16 GELU output, q2 [M, N] (row stride ldq2 bytes), and their
+    // scales s2 [N / 128][M][4] - the input of a following MX product.
+    uint8_t* q2;
+    uint8_t* s2;
+    int64_t ldq2;
 };
 
 // Returns hipSuccess or the launch error.  T in {float, bf16}: operand type;
@@ -66,8 +72,10 @@ template <class T>
 hipError_t encoder_forward(T* out, const int32_t* tok, const float* wte, const float* wpe, int BT, int T_, int C,
                            hipStream_t s, int pos0 = 0);
 template <class T>
+// bf16 only: mxq / mxs non-null also write the output's MX FP8 codes [N, Kp] (row
+// stride ldq bytes, Kp = C rounded up to 128) and scales [Kp / 128][N][4].
 hipError_t layernorm_forward(T* out, float* stats, const T* inp, const float* w, const float* b, int N, int C,
-                             hipStream_t s);
+                             hipStream_t s, uint8_t* mxq = nullptr, int64_t ldq = 0, uint8_t* mxs = nullptr);
 // dres = dres_in + LN backward dx (dres_in may be null, or equal to dres); dw, db
 // (overwrite) from column sums through `partial`.
 template <class T>

@@ -2,6 +2,7 @@
 // embedding gather / scatter, LayerNorm forward / backward, bias gradients,
 // fused softmax cross-entropy, AdamW, and small reductions.
 #include "kernels.h"
+#include "mx_quant.h"
 
 namespace gpt2 {
 
@@ -40,9 +41,13 @@ hipError_t encoder_forward(T* out, const int32_t* tok, const float* wte, const f
 // "GPT-2 from scratch with torch", Transformer block (LayerNorm, eps 1e-5): per row
 // mean and biased variance over C; y = (x - mean) * rstd * w + b.  One wave per row;
 // the row stays in registers between the two statistics passes.
-template <class T, int MAXCH>
+// MXO: also writes the MX FP8 codes and block scales of the (bf16-rounded) output,
+// q [N, Kp] (row stride ldq bytes), sc [Kp / 128][N][4], for a following MX product;
+// lane l's 8 values are chunk 64 ch + l, so 4 lanes hold a 32-block and 16 a stage.
+template <class T, int MAXCH, bool MXO = false>
 __global__ __launch_bounds__(256) void layernorm_forward_kernel(T* out, float* stats, const T* inp, const float* w,
-                                                                const float* b, int N, int C) {
+                                                                const float* b, int N, int C, uint8_t* q = nullptr,
+                                                                int64_t ldq = 0, uint8_t* sc = nullptr) {
     constexpr int KV = Vec16<T>::N;
     const int lane = threadIdx.x & 63;
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -74,6 +79,40 @@ __global__ __launch_bounds__(256) void layernorm_forward_kernel(T* out, float* s
     }
     const float rstd = 1.0f / sqrtf(wave_sum(sq) / C + 1e-5f);
     T* y = out + (int64_t)row * C;
+    if constexpr (MXO) {
+        static_assert(KV == 8, "MX output from bf16 rows");
+        const int Kp = (C + 127) / 128 * 128;
+#pragma unroll
+        for (int ch = 0; ch < MAXCH; ++ch) {
+            const int c = (ch * 64 + lane) * KV;
+            float o[KV];
+#pragma unroll
+            for (int e = 0; e < KV; ++e) o[e] = 0.f;
+            if (c < C) {
+                float wv[KV], bv[KV];
+#pragma unroll
+                for (int e = 0; e < KV; e += 4) {
+                    *(float4*)&wv[e] = *(const float4*)(w + c + e);
+                    *(float4*)&bv[e] = *(const float4*)(b + c + e);
+                }
+#pragma unroll
+                for (int e = 0; e < KV; ++e) o[e] = (v[ch][e] - mean) * rstd * wv[e] + bv[e];
+                round_bf16_8(o);
+                st16(y + c, pack16<T>(o));
+            }
+            uint32_t cw[2];
+            const uint32_t word = mx_stage_word(mx_quant8(o, cw));
+            if (c < Kp) {
+                *(uint2*)(q + (int64_t)row * ldq + c) = make_uint2(cw[0], cw[1]);
+                if ((lane & 15) == 0) *(uint32_t*)(sc + ((int64_t)(c / 128) * N + row) * 4) = word;
+            }
+        }
+        if (lane == 0) {
+            stats[2 * row] = mean;
+            stats[2 * row + 1] = rstd;
+        }
+        return;
+    }
 #pragma unroll
     for (int ch = 0; ch < MAXCH; ++ch) {
         int c = (ch * 64 + lane) * KV;
@@ -97,10 +136,25 @@ __global__ __launch_bounds__(256) void layernorm_forward_kernel(T* out, float* s
 
 template <class T>
 hipError_t layernorm_forward(T* out, float* stats, const T* inp, const float* w, const float* b, int N, int C,
-                             hipStream_t s) {
+                             hipStream_t s, uint8_t* mxq, int64_t ldq, uint8_t* mxs) {
     constexpr int KV = Vec16<T>::N;
     int ch = cdiv(C, 64 * KV);
     dim3 grid(cdiv(N, 4)), block(256);
+    if constexpr (sizeof(T) == 2) {
+        if (mxq) {
+            if (!mxs || ldq < (C + 127) / 128 * 128 || ldq % 16) return hipErrorInvalidValue;
+            ProfScope prof(s, "layernorm_fwd_mx", 0, (double)N * C * 2 * sizeof(T) + 8.0 * N + N * C * (1 + 1 / 32.));
+            if (ch <= 1)
+                hipLaunchKernelGGL((layernorm_forward_kernel<T, 1, true>), grid, block, 0, s, out, stats, inp, w, b, N, C, mxq, ldq, mxs);
+            else if (ch <= 2)
+                hipLaunchKernelGGL((layernorm_forward_kernel<T, 2, true>), grid, block, 0, s, out, stats, inp, w, b, N, C, mxq, ldq, mxs);
+            else if (ch <= 4)
+                hipLaunchKernelGGL((layernorm_forward_kernel<T, 4, true>), grid, block, 0, s, out, stats, inp, w, b, N, C, mxq, ldq, mxs);
+            else return hipErrorInvalidValue;
+            return hipGetLastError();
+        }
+    }
+    if (mxq) return hipErrorInvalidValue;
     ProfScope prof(s, "layernorm_fwd", 0, (double)N * C * 2 * sizeof(T) + 8.0 * N);
     if (ch <= 1) hipLaunchKernelGGL((layernorm_forward_kernel<T, 1>), grid, block, 0, s, out, stats, inp, w, b, N, C);
     else if (ch <= 2) hipLaunchKernelGGL((layernorm_forward_kernel<T, 2>), grid, block, 0, s, out, stats, inp, w, b, N, C);
@@ -808,7 +862,7 @@ hipError_t splitk_reduce_bf16(bf16* C, int64_t ldc, const float* ws, int splits,
     template hipError_t encoder_forward<T>(T*, const int32_t*, const float*, const float*, int, int, int,        \
                                            hipStream_t, int);                                                     \
     template hipError_t layernorm_forward<T>(T*, float*, const T*, const float*, const float*, int, int,         \
-                                             hipStream_t);                                                        \
+                                             hipStream_t, uint8_t*, int64_t, uint8_t*);                          \
     template hipError_t layernorm_backward<T>(T*, const T*, float*, float*, const T*, const T*, const float*,   \
                                               const float*, int, int, float*, size_t, hipStream_t);              \
     template hipError_t layernorm_backward_dx<T>(T*, const T*, const T*, const T*, const float*, const float*,   \

@@ -14,21 +14,11 @@
 // [Kp / 128][R][4] bytes, so one k-stage of 128 codes of a run of rows has its
 // scales in one contiguous run of 4-byte words.
 #include "kernels.h"
+#include "mx_quant.h"
 
 namespace gpt2 {
 
 namespace {
-
-// Exponent e of the scale: the smallest integer with amax <= 448 2^e.  For a normal
-// amax = 1.m 2^E, amax / 2^(E-8) = 1.m 2^8 lies in [256, 512) and exceeds 448 = 1.75 2^8
-// exactly when the 23-bit mantissa field exceeds 0x600000.
-__device__ __forceinline__ int mx_exponent(float amax) {
-    const uint32_t b = __float_as_uint(amax);
-    if (amax == 0.f) return -127;
-    const int E = (int)((b >> 23) & 0xFF) - 127;  // subnormal amax: far below the clamp
-    int e = E - 8 + ((b & 0x7FFFFF) > 0x600000 ? 1 : 0);
-    return e < -127 ? -127 : e > 127 ? 127 : e;
-}
 
 // One thread: 8 consecutive values of a row; 4 threads: one block of 32; 16 threads:
 // one k-stage of 128 (their scales leave as one 4-byte word).
@@ -47,27 +37,11 @@ __global__ __launch_bounds__(256) void mx_quantize_kernel(const bf16* __restrict
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = 0.f;
     }
-    float amax = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
-    amax = fmaxf(amax, __shfl_xor(amax, 1));
-    amax = fmaxf(amax, __shfl_xor(amax, 2));
-    const int ex = mx_exponent(amax);
     uint32_t w[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const float a0 = __builtin_amdgcn_ldexpf(v[4 * h + 0], -ex), a1 = __builtin_amdgcn_ldexpf(v[4 * h + 1], -ex);
-        const float a2 = __builtin_amdgcn_ldexpf(v[4 * h + 2], -ex), a3 = __builtin_amdgcn_ldexpf(v[4 * h + 3], -ex);
-        int r = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, 0, false);
-        r = __builtin_amdgcn_cvt_pk_fp8_f32(a2, a3, r, true);
-        w[h] = (uint32_t)r;
-    }
-    // scale bytes of the stage's 4 blocks, gathered by the stage's first lane
-    const uint32_t sb = (uint32_t)(ex + 127);
-    const uint32_t s1 = __shfl_down(sb, 4), s2 = __shfl_down(sb, 8), s3 = __shfl_down(sb, 12);
+    const uint32_t word = mx_stage_word(mx_quant8(v, w));
     if (!live) return;
     *(uint2*)(q + (int64_t)row * ldq + k0) = make_uint2(w[0], w[1]);
-    if ((c & 15) == 0) *(uint32_t*)(sc + ((int64_t)(c / 16) * R + row) * 4) = sb | (s1 << 8) | (s2 << 16) | (s3 << 24);
+    if ((c & 15) == 0) *(uint32_t*)(sc + ((int64_t)(c / 16) * R + row) * 4) = word;
 }
 
 }  // namespace
