@@ -106,6 +106,9 @@ def main():
     ap.add_argument("--decode", action="store_true",
                     help="measure incremental generation instead of training: prefill a prompt, then time "
                          "--steps one-row decode steps per sequence (prints its own JSON line)")
+    ap.add_argument("--mxfp8", action="store_true",
+                    help="time the forward pass (with the loss) with MX FP8 block and lm_head products beside the "
+                         "bf16 forward (prints its own JSON line)")
     ap.add_argument("--decode-batch", type=int, default=8)
     ap.add_argument("--prompt", type=int, default=512)
     args = ap.parse_args()
@@ -134,6 +137,8 @@ def main():
 
     if args.decode:
         return decode_bench(args)
+    if args.mxfp8:
+        return mx_forward_bench(args)
 
     w = synth.WORKLOADS[args.workload]
     m = w.model
@@ -339,6 +344,101 @@ def decode_bench(args):
         "dtype": w.dtype, "data": "synthetic (seeded random-init weights, uniform token ids for prompt and continuation)",
         "config": {"workload": name, "batch": batch, "prompt": n, "layers": m.num_layers, "heads": m.num_heads,
                    "channels": m.channels, "vocab": m.vocab_size},
+        "roofline": roof, "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def mx_forward_bench(args):
+    """Forward passes (logits and mean loss, no backward) of the workload with the
+    block and lm_head products in MX FP8, timed beside the same passes in bf16."""
+    import numpy as np
+    import torch
+    import synth
+    from transformer_lm_fwd_amd import Arena, binding
+
+    w = synth.WORKLOADS[args.workload]
+    m = w.model
+    t0 = time.time()
+    params = synth.init_params(m)
+    x, y = synth.inputs_targets(w)
+    log(f"[bench] {w.name}: inputs generated in {time.time() - t0:.1f} s")
+    torch.cuda.set_device(0)
+    arena = Arena(m, w.B, w.T, "bf16")
+    arena.load_params(params)
+    xt = torch.from_numpy(np.ascontiguousarray(x)).to(torch.int32).cuda()
+    yt = torch.from_numpy(np.ascontiguousarray(y)).to(torch.int32).cuda()
+
+    def timed(fmt):
+        arena.set_gemm_format(fmt)
+        for _ in range(max(1, args.warmup)):
+            arena.forward(xt, yt, check_ids=False)
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(args.steps):
+            arena.forward(xt, yt, check_ids=False)
+        end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / args.steps, arena.loss()
+
+    ms_bf, loss_bf = timed(binding.GPT2_GEMM_BF16)
+    ms_mx, loss_mx = timed(binding.GPT2_GEMM_MXFP8)
+    tokens = w.B * w.T
+    value = tokens / (ms_mx / 1e3)
+    log(f"[bench] forward: bf16 {ms_bf:.3f} ms ({tokens / ms_bf:,.0f}K tok/s, loss {loss_bf:.5f}); "
+        f"mxfp8 {ms_mx:.3f} ms ({tokens / ms_mx:,.0f}K tok/s, loss {loss_mx:.5f})")
+
+    binding.profile(True)
+    pk = max(1, args.profile_steps)
+    for _ in range(pk):
+        arena.forward(xt, yt, check_ids=False)
+    torch.cuda.synchronize()
+    binding.profile(False)
+    stats = sorted(binding.profile_read(), key=lambda s: -s["total_ms"])
+    tot = sum(s["total_ms"] for s in stats)
+    log(f"[bench] kernel profile over {pk} MX forward passes ({tot / pk:.3f} ms/pass in kernels):")
+    for s in stats:
+        avg = s["total_ms"] / s["launches"]
+        tf = s["flops"] / (s["total_ms"] / 1e3) / 1e12
+        log(f"  {s['name']:<44} {s['launches']:5d} launches {s['total_ms'] / pk:7.3f} ms/pass "
+            f"({100 * s['total_ms'] / tot:5.1f}%) avg {avg * 1e3:8.2f} us  {tf:7.1f} TFLOP/s")
+    if args.kernel_table:
+        with open(args.kernel_table, "w") as f:
+            json.dump({"workload": w.name + "_mxfp8_forward", "profile_steps": pk, "kernels": stats}, f, indent=1)
+    dom = next(s for s in stats if s["name"].startswith("gemm_mxfp8"))
+    avg_s = dom["total_ms"] / dom["launches"] / 1e3
+    ach = dom["flops"] / dom["launches"] / avg_s / 1e12
+    roof = {"kernel": dom["name"], "bound": "mfma", "achieved": round(ach, 1), "peak": 5000.0, "unit": "TFLOP/s",
+            "frac": round(ach / 5000.0, 4), "traffic": None, "avg_launch_us": round(avg_s * 1e6, 2),
+            "flops_per_launch": dom["flops"] / dom["launches"]}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        T_s = min(256, w.T)
+        o = oracle.Oracle(m, 1, T_s, "f32")
+        o.set("params", params)
+        t1, reps = time.perf_counter(), 0
+        while reps < 1 or time.perf_counter() - t1 < 10.0:
+            o.forward(x[:1, :T_s], y[:1, :T_s])
+            reps += 1
+        el = time.perf_counter() - t1
+        cpu = {"value": round(reps * T_s / el, 2), "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+               "sample": f"float oracle forward with loss (no quantization) on batch row 0, first {T_s} tokens, "
+                         f"{reps} repetitions"}
+        log(f"[bench] CPU oracle: {cpu['value']} tokens/s")
+
+    out = {
+        "metric": "forward tokens/sec (logits + loss) GPT-2 124M B=8 T=1024, MX FP8 block and lm_head products",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_mx, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "mxfp8", "data": "synthetic (seeded random-init weights, uniform token ids)",
+        "config": {"workload": w.name + "_mxfp8_forward", "batch": w.B, "seq_len": w.T, "layers": m.num_layers,
+                   "heads": m.num_heads, "channels": m.channels, "vocab": m.vocab_size},
+        "bf16_forward": {"ms_per_step": round(ms_bf, 5), "value": round(tokens / (ms_bf / 1e3), 1),
+                         "loss": loss_bf},
+        "mxfp8_loss": loss_mx,
         "roofline": roof, "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
