@@ -66,6 +66,9 @@ def lib():
         L.orc_forward.restype = dbl
         L.orc_backward.argtypes = [vp]
         L.orc_adamw.argtypes = [vp, dbl, dbl, dbl, dbl, dbl, i32]
+        L.orc_set_rotary.argtypes = [vp, ctypes.c_int, ctypes.c_double]
+        L.orc_rope.argtypes = [vp, vp, ctypes.c_int, ctypes.c_int, vp, ctypes.c_double, ctypes.c_int]
+        L.orc_rope.restype = None
         L.orc_gelu.argtypes = [vp, vp, i64]
         L.orc_gelu_grad.argtypes = [vp, vp, i64]
         L.orc_num_threads.restype = i32
@@ -89,6 +92,17 @@ def gelu(x) -> np.ndarray:
     x = np.ascontiguousarray(x, dtype=np.float64)
     y = np.empty_like(x)
     lib().orc_gelu(_ptr(x), _ptr(y), x.size)
+    return y
+
+
+def rope(x, pos, base: float = 10000.0, inverse: bool = False) -> np.ndarray:
+    """Rotary position embedding of head vectors x [rows, hs] at positions pos [rows]
+    (float64; see orc_rope)."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    rows, hs = x.shape
+    p = np.ascontiguousarray(pos, dtype=np.int32).reshape(rows)
+    y = np.empty_like(x)
+    lib().orc_rope(_ptr(x), _ptr(y), rows, hs, _ptr(p), float(base), 1 if inverse else 0)
     return y
 
 
@@ -163,6 +177,11 @@ class Oracle:
         if loss != loss:
             raise ValueError(lib().orc_last_error().decode())
         return float(loss)
+
+    def set_rotary(self, on: bool = True, base: float = 10000.0):
+        """Rotary position embedding (RoFormer) instead of the learned wpe."""
+        if lib().orc_set_rotary(self.h, 1 if on else 0, float(base)):
+            raise ValueError(lib().orc_last_error().decode())
 
     def backward(self):
         if lib().orc_backward(self.h):

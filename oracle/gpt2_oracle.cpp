@@ -163,8 +163,12 @@ static void encoder_forward(R* out, const int* inp, const R* wte, const R* wpe, 
     for (int b = 0; b < B; ++b)
         for (int t = 0; t < T; ++t) {
             const R* we = wte + (int64_t)inp[b * T + t] * C;
-            const R* pe = wpe + (int64_t)t * C;
             R* o = out + ((int64_t)b * T + t) * C;
+            if (!wpe) {  // rotary position embedding: no learned position vector
+                for (int c = 0; c < C; ++c) o[c] = we[c];
+                continue;
+            }
+            const R* pe = wpe + (int64_t)t * C;
             for (int c = 0; c < C; ++c) o[c] = we[c] + pe[c];
         }
 }
@@ -305,8 +309,10 @@ static void encoder_backward(R* dwte, R* dwpe, const R* dout, const int* inp, in
         for (int t = 0; t < T; ++t) {
             const R* d = dout + ((int64_t)b * T + t) * C;
             R* dw = dwte + (int64_t)inp[b * T + t] * C;
+            for (int c = 0; c < C; ++c) dw[c] += d[c];
+            if (!dwpe) continue;  // rotary: wpe is not used and keeps a zero gradient
             R* dp = dwpe + (int64_t)t * C;
-            for (int c = 0; c < C; ++c) { dw[c] += d[c]; dp[c] += d[c]; }
+            for (int c = 0; c < C; ++c) dp[c] += d[c];
         }
 }
 
@@ -440,6 +446,42 @@ static void crossentropy_softmax_backward(R* dlogits, const R* probs, const int*
     }
 }
 
+// ----------------------------------------------------------------------------- rotary position embedding
+// RoFormer's rotary position embedding (named in "GPT-2 from scratch with torch", token
+// and position embedding, as the newer alternative to learned position vectors, after
+// Su et al. 2021): a head vector x at position m has each pair (x[2i], x[2i+1]) turned
+// by the angle m * theta_i, theta_i = base^(-2i / hs):
+//   x'[2i]   = x[2i] cos(m theta_i) - x[2i+1] sin(m theta_i)
+//   x'[2i+1] = x[2i] sin(m theta_i) + x[2i+1] cos(m theta_i)
+// Applied to the query and key heads (not the values) before the scores.  The
+// backward pass turns the gradients back by -m theta_i (a rotation's transpose).
+// Angles are taken in double whatever R is.
+template <class R>
+static void rope_head(R* out, const R* x, int hs, int m, double base, int sign) {
+    for (int i = 0; i < hs / 2; ++i) {
+        const double th = std::pow(base, -2.0 * i / hs), a = sign * (double)m * th;
+        const double c = std::cos(a), sn = std::sin(a);
+        const double x0 = x[2 * i], x1 = x[2 * i + 1];
+        out[2 * i] = (R)(x0 * c - x1 * sn);
+        out[2 * i + 1] = (R)(x0 * sn + x1 * c);
+    }
+}
+
+// qkv [B*T, 3C] (q | k | v, head h at columns h*hs of each third) -> out with q and k
+// of every head turned for its position t; v copied.  sign -1: the inverse turn.
+template <class R>
+static void rope_qkv(R* out, const R* qkv, int B, int T, int C, int NH, double base, int sign) {
+    const int hs = C / NH;
+    const int64_t C3 = 3 * (int64_t)C;
+    for (int b = 0; b < B; ++b)
+        for (int t = 0; t < T; ++t) {
+            const R* x = qkv + ((int64_t)b * T + t) * C3;
+            R* o = out + ((int64_t)b * T + t) * C3;
+            for (int h = 0; h < 2 * NH; ++h) rope_head(o + h * hs, x + h * hs, hs, t, base, sign);
+            for (int c = 2 * C; c < 3 * C; ++c) o[c] = x[c];
+        }
+}
+
 // ----------------------------------------------------------------------------- model
 
 struct ModelBase {
@@ -457,6 +499,12 @@ struct Model : ModelBase {
     std::vector<int> inputs, targets;
     bool have_targets = false, have_forward = false;
     R loss = -1;
+    // rotary position embedding (off: learned wpe).  qkv_rot[l]: the attention's
+    // q | k | v with q and k turned; outside the plain activation set.
+    bool rotary = false;
+    double rope_base = 10000.0;
+    std::vector<std::vector<R>> qkv_rot;
+    std::vector<R> dqkv_rot;
 
     Model(const Shape& sh, int b, int t) {
         s = sh; B = b; T = t;
@@ -477,12 +525,18 @@ struct Model : ModelBase {
         std::memcpy(inputs.data(), inp, sizeof(int) * BT);
         have_targets = tgt != nullptr;
         if (tgt) std::memcpy(targets.data(), tgt, sizeof(int) * BT);
-        encoder_forward(A(A_ENCODED), inp, P.wte, P.wpe, B, T, C);
+        encoder_forward(A(A_ENCODED), inp, P.wte, rotary ? (const R*)nullptr : P.wpe, B, T, C);
+        if (rotary) qkv_rot.assign(L, std::vector<R>((size_t)3 * BT * C));
         for (int l = 0; l < L; ++l) {
             const R* x = l == 0 ? A(A_ENCODED) : A(A_RESIDUAL3, l - 1);
             layernorm_forward(A(A_LN1, l), A(A_LN1_MEAN, l), A(A_LN1_RSTD, l), x, P.t[LN1W][l], P.t[LN1B][l], BT, C);
             matmul_forward(A(A_QKV, l), A(A_LN1, l), P.t[QKVW][l], P.t[QKVB][l], BT, C, 3 * C);
-            attention_forward(A(A_ATTY, l), A(A_PREATT, l), A(A_ATT, l), A(A_QKV, l), B, T, C, NH);
+            const R* qkv = A(A_QKV, l);
+            if (rotary) {
+                rope_qkv(qkv_rot[l].data(), A(A_QKV, l), B, T, C, NH, rope_base, +1);
+                qkv = qkv_rot[l].data();
+            }
+            attention_forward(A(A_ATTY, l), A(A_PREATT, l), A(A_ATT, l), qkv, B, T, C, NH);
             matmul_forward(A(A_ATTPROJ, l), A(A_ATTY, l), P.t[PROJW][l], P.t[PROJB][l], BT, C, C);
             residual_forward(A(A_RESIDUAL2, l), x, A(A_ATTPROJ, l), BT * C);
             layernorm_forward(A(A_LN2, l), A(A_LN2_MEAN, l), A(A_LN2_RSTD, l), A(A_RESIDUAL2, l), P.t[LN2W][l], P.t[LN2B][l], BT, C);
@@ -537,13 +591,21 @@ struct Model : ModelBase {
             for (int64_t i = 0; i < BT * C; ++i) { dx[i] += dres2[i]; dA(A_ATTPROJ, l)[i] += dres2[i]; }
             matmul_backward(dA(A_ATTY, l), G.t[PROJW][l], G.t[PROJB][l], dA(A_ATTPROJ, l), A(A_ATTY, l),
                             P.t[PROJW][l], BT, C, C);
-            attention_backward(dA(A_QKV, l), dA(A_PREATT, l), dA(A_ATT, l), dA(A_ATTY, l), A(A_QKV, l), A(A_ATT, l),
-                               B, T, C, NH);
+            if (rotary) {
+                // gradients reach the turned q | k | v, then turn back to the qkv product's output
+                dqkv_rot.assign((size_t)3 * BT * C, R(0));
+                attention_backward(dqkv_rot.data(), dA(A_PREATT, l), dA(A_ATT, l), dA(A_ATTY, l), qkv_rot[l].data(),
+                                   A(A_ATT, l), B, T, C, NH);
+                rope_qkv(dA(A_QKV, l), dqkv_rot.data(), B, T, C, NH, rope_base, -1);
+            } else {
+                attention_backward(dA(A_QKV, l), dA(A_PREATT, l), dA(A_ATT, l), dA(A_ATTY, l), A(A_QKV, l),
+                                   A(A_ATT, l), B, T, C, NH);
+            }
             matmul_backward(dA(A_LN1, l), G.t[QKVW][l], G.t[QKVB][l], dA(A_QKV, l), A(A_LN1, l), P.t[QKVW][l], BT, C, 3 * C);
             layernorm_backward(dx, G.t[LN1W][l], G.t[LN1B][l], dA(A_LN1, l), x, P.t[LN1W][l],
                                A(A_LN1_MEAN, l), A(A_LN1_RSTD, l), BT, C);
         }
-        encoder_backward(G.wte, G.wpe, dA(A_ENCODED), inputs.data(), B, T, C);
+        encoder_backward(G.wte, rotary ? (R*)nullptr : G.wpe, dA(A_ENCODED), inputs.data(), B, T, C);
         return 0;
     }
 
@@ -575,6 +637,11 @@ struct Model : ModelBase {
 
     // Activation ("name") or activation gradient ("dname") pointer and size.
     R* act(const char* name, int layer, int64_t* n) {
+        if (!strcmp(name, "qkv_rot")) {  // rotary mode, after a forward pass
+            if (layer < 0 || layer >= (int)qkv_rot.size()) return nullptr;
+            *n = (int64_t)qkv_rot[layer].size();
+            return qkv_rot[layer].data();
+        }
         bool grad = name[0] == 'd' && strcmp(name, "d") != 0;
         const char* nm = grad ? name + 1 : name;
         for (int a = 0; a < NACT; ++a)
@@ -688,6 +755,18 @@ double orc_forward(void* h, const int* inputs, const int* targets) {
         }
     ORC_DISPATCH(h, { M->forward(inputs, targets); out = (double)M->loss; });
     return out;
+}
+
+// Rotary position embedding on (1) or off (0, learned wpe) for the following passes.
+int orc_set_rotary(void* h, int on, double base) {
+    if (!(base > 1.0)) { g_err = "rotary base must exceed 1"; return -1; }
+    ORC_DISPATCH(h, { M->rotary = on != 0; M->rope_base = base; M->have_forward = false; M->qkv_rot.clear(); });
+    return 0;
+}
+
+// y[r] = x[r] (one head vector of hs values) turned for position pos[r]; inverse turns back.
+void orc_rope(const double* x, double* y, int rows, int hs, const int* pos, double base, int inverse) {
+    for (int r = 0; r < rows; ++r) rope_head(y + (int64_t)r * hs, x + (int64_t)r * hs, hs, pos[r], base, inverse ? -1 : 1);
 }
 
 int orc_backward(void* h) {

@@ -4,7 +4,7 @@ import numpy as np
 
 import synth
 
-# Tolerances (BASELINE workload statement): fp32 -> loss relative error <= 1e-5,
+# Tolerances (stated with the measured workloads): fp32 -> loss relative error <= 1e-5,
 # logits and every parameter gradient max-norm relative error <= 1e-3;
 # bf16 -> loss absolute error <= 2e-2, cosine of the flat gradient >= 0.999.
 FP32_LOSS_REL = 1e-5
