@@ -301,6 +301,19 @@ int gpt2_checkpoint_write(const char* path, const gpt2_config* cfg, int32_t step
 int gpt2_checkpoint_read(const char* path, const gpt2_config* cfg, int32_t* step, float* params, float* m, float* v,
                          int32_t* has_moments);
 
+/* Position encoding of an arena's model.
+ *  GPT2_POS_LEARNED: x = wte[token] + wpe[position] (GPT-2; the default).
+ *  GPT2_POS_ROTARY:  rotary position embedding ("GPT-2 from scratch with torch", token
+ *    and position embedding, names RoPE - Su et al. 2021 - as the newer alternative):
+ *    x = wte[token]; after the qkv product the pair (x[2i], x[2i+1]) of every query and
+ *    key head at position m is turned by the angle m * base^(-2i / head size); values
+ *    are untouched.  wpe stays in the parameter array, unused, with a zero gradient.
+ * Applies to gpt2_forward, gpt2_backward(_adamw) and generation.  Switching to
+ * GPT2_POS_ROTARY builds the arena's cos / sin table on `stream` (float64 angles).
+ * Errors: GPT2_E_INVAL (NULL arena, unknown mode, base not finite or <= 1), GPT2_E_HIP. */
+enum gpt2_position_encoding { GPT2_POS_LEARNED = 0, GPT2_POS_ROTARY = 1 };
+int gpt2_set_position_encoding(gpt2_arena* arena, int32_t mode, float base, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Products below 16 bits: MX FP8.  The llm.c page ("1000 行 C 代码完成 GPT-2 训练的
  * LLM.c", the paragraph on extensions after the CUDA port) names taking the trainer's

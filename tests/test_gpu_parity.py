@@ -28,12 +28,17 @@ def announce(name, w, B=None, T=None):
           f"B={w.B if B is None else B} T={w.T if T is None else T} {w.dtype}", flush=True)
 
 
-def fp32_full_compare(w, params, check_acts=True):
-    """forward (logits, activations), loss, backward and one AdamW step, fp32 tolerances."""
+def fp32_full_compare(w, params, check_acts=True, rotary=False):
+    """forward (logits, activations), loss, backward and one AdamW step, fp32 tolerances.
+    rotary: both sides with the rotary position embedding (the GPU's qkv activation then
+    holds the turned q and k, the oracle's "qkv_rot")."""
     b = _b()
     x, y = synth.inputs_targets(w)
     o = oracle_model(w, params)
     a = gpu_arena(w, params)
+    if rotary:
+        o.set_rotary(True)
+        a.set_position_encoding(b.GPT2_POS_ROTARY)
     m = w.model
     BT, C = w.B * w.T, m.channels
     # forward without targets keeps the logits
@@ -44,7 +49,8 @@ def fp32_full_compare(w, params, check_acts=True):
         errs["encoded"] = maxrel(to_np(a.tensor(b.T_ENCODED)), o.act("encoded"))
         for l in range(m.num_layers):
             for name, tid in ACT_MAP.items():
-                errs[f"{name}{l}"] = maxrel(to_np(a.tensor(getattr(b, tid), l)), o.act(name, l))
+                ref_name = "qkv_rot" if (rotary and name == "qkv") else name
+                errs[f"{name}{l}"] = maxrel(to_np(a.tensor(getattr(b, tid), l)), o.act(ref_name, l))
             st = to_np(a.tensor(b.T_LN1_STATS, l))
             errs[f"ln1_mean{l}"] = maxrel(st[:, 0], o.act("ln1_mean", l))
             errs[f"ln1_rstd{l}"] = maxrel(st[:, 1], o.act("ln1_rstd", l))
@@ -147,11 +153,14 @@ def test_gpt2_124m_b4t64_fp32_step_and_ten_step_losses():
 
 # ----------------------------------------------------------------------------- bf16 parity
 
-def bf16_compare(w, params, seed_label=""):
+def bf16_compare(w, params, seed_label="", rotary=False):
     b = _b()
     x, y = synth.inputs_targets(w)
     o = oracle_model(w, params)
     a = gpu_arena(w, params)
+    if rotary:
+        o.set_rotary(True)
+        a.set_position_encoding(b.GPT2_POS_ROTARY)
     a.forward(x, y)
     loss = a.loss()
     ref = o.forward(x, y)

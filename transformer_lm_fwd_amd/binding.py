@@ -28,10 +28,12 @@ EXPORTS = ("gpt2_alloc_arena", "gpt2_free_arena", "gpt2_sync_weights", "gpt2_for
            "gpt2_adamw_step", "gpt2_backward_adamw", "gpt2_tensor_info", "gpt2_num_parameters", "gpt2_profile",
            "gpt2_profile_read", "gpt2_gen_alloc", "gpt2_gen_free", "gpt2_gen_length", "gpt2_gen_prefill",
            "gpt2_gen_decode", "gpt2_sample_topk", "gpt2_tokens_count", "gpt2_tokens_batch",
-           "gpt2_params_permute", "gpt2_checkpoint_write", "gpt2_checkpoint_read", "gpt2_mx_attach",
+           "gpt2_params_permute", "gpt2_checkpoint_write", "gpt2_checkpoint_read", "gpt2_set_position_encoding",
+           "gpt2_mx_attach",
            "gpt2_set_gemm_format", "gpt2_mx_buffer", "gpt2_mx_quantize", "gpt2_mx_gemm", "gpt2_last_error")
 GPT2_ORDER_NUMERIC, GPT2_ORDER_LEXICOGRAPHIC = 0, 1
 GPT2_GEMM_BF16, GPT2_GEMM_MXFP8 = 0, 1
+GPT2_POS_LEARNED, GPT2_POS_ROTARY = 0, 1
 GPT2_EPI_BIAS, GPT2_EPI_BIAS_RES, GPT2_EPI_BIAS_GELU = 0, 1, 2
 GPT2_MX_BUF_INPUT, GPT2_MX_BUF_GELU = 0, 1
 
@@ -91,6 +93,7 @@ def lib():
         L.gpt2_params_permute.argtypes = [cfgp, vp, vp, i32, i32]
         L.gpt2_checkpoint_write.argtypes = [cp, cfgp, i32, vp, vp, vp]
         L.gpt2_checkpoint_read.argtypes = [cp, cfgp, ctypes.POINTER(i32), vp, vp, vp, ctypes.POINTER(i32)]
+        L.gpt2_set_position_encoding.argtypes = [vp, i32, f32, vp]
         L.gpt2_mx_attach.argtypes = [vp, vp, sz, ctypes.POINTER(sz)]
         L.gpt2_set_gemm_format.argtypes = [vp, i32]
         L.gpt2_mx_buffer.argtypes = [vp, i32, ctypes.POINTER(sz), ctypes.POINTER(sz), ctypes.POINTER(i64),
@@ -276,6 +279,10 @@ class Arena:
             self.tensor(T_ADAM_V).view(-1).copy_(torch.from_numpy(v))
         _check(lib().gpt2_sync_weights(self.h, _stream_ptr(stream)))
         return int(step.value)
+
+    def set_position_encoding(self, mode: int, base: float = 10000.0, stream=None) -> None:
+        """GPT2_POS_LEARNED (wpe) or GPT2_POS_ROTARY (rotary q / k turns; base of the frequencies)."""
+        _check(lib().gpt2_set_position_encoding(self.h, mode, base, _stream_ptr(stream)))
 
     # ------------------------------------------------------------------ MX FP8 products
     def set_gemm_format(self, fmt: int) -> None:

@@ -67,6 +67,9 @@ struct gpt2_arena {
     // MX FP8 forward products (caller memory from gpt2_mx_attach): E4M3 codes and
     // block scales of the forward weights, made from the bf16 copy whenever it has
     // changed, and one buffer for the quantized activation of the product at hand.
+    // position encoding: learned wpe (default) or rotary (cos / sin table at `rope`)
+    int pos_enc = GPT2_POS_LEARNED;
+    size_t rope = 0;
     int gemm_format = GPT2_GEMM_BF16;
     char* mx = nullptr;
     size_t mx_bytes = 0;
@@ -187,6 +190,7 @@ size_t layout(gpt2_arena& a) {
     a.ws_main_floats = (size_t)4 * BT * C;
     a.ws_main = take(a.ws_main_floats * 4);
     a.census = take((size_t)2 * a.cfg.vocab_size * 4);  // per token: first position, count (embedding backward)
+    a.rope = take((size_t)a.cfg.max_seq_len * (a.hs / 2) * 8);  // rotary cos / sin table [P][hs / 2]
     return o;
 }
 
@@ -335,6 +339,8 @@ struct Model {
     }
 
     uint8_t* mxp(size_t off) const { return (uint8_t*)(a->mx + off); }
+    bool rotary() const { return a->pos_enc == GPT2_POS_ROTARY; }
+    const float2* rope_tab() const { return at<float2>(a, a->rope); }
 
     // MX codes and scales of the forward weights from the bf16 copy.
     int mx_refresh() {
@@ -395,7 +401,9 @@ struct Model {
             int rc = mx_refresh();
             if (rc) return rc;
         }
-        CHECK(encoder_forward<T>(act(a->encoded), inp, master(a->o_wte), master(a->o_wpe), BT, S, C, s), "encoder");
+        CHECK(encoder_forward<T>(act(a->encoded), inp, master(a->o_wte), rotary() ? nullptr : master(a->o_wpe), BT, S,
+                                 C, s),
+              "encoder");
         for (int l = 0; l < L; ++l) {
             const LayerActs& x = a->la[l];
             const T* xin = l == 0 ? act(a->encoded) : act(a->la[l - 1].res3);
@@ -407,6 +415,8 @@ struct Model {
             if ((rc = fwd_gemm(act(x.ln1), C, lp(l, P_QKVW), 4 * l, 3 * C, act(x.qkv), 3 * C, EPI_BIAS,
                                master(lp(l, P_QKVB)), nullptr, nullptr, mi)))
                 return rc;
+            if (rotary())  // turn q and k of every head for its position (in place)
+                CHECK(rope_apply<T>(act(x.qkv), 3 * C, BT, 2 * C, C / NH, S, 0, rope_tab(), false, s), "rope");
             CHECK(attention_forward<T>(act(x.atty), f32(x.lse), act(x.qkv), B, S, C, NH, s), "attention");
             // res2 = xin + atty W_proj^T + b
             if ((rc = fwd_gemm(act(x.atty), C, lp(l, P_PROJW), 4 * l + 1, C, act(x.res2), C, EPI_BIAS_RES,
@@ -544,6 +554,8 @@ struct Model {
             if ((rc = wait(M, a->rd_qkv[p]))) return rc;
             CHECK(attention_backward<T>(dqkv, f32(a->dsum), dbuf, act(x.atty), act(x.qkv), f32(x.lse), B, S, C, NH, M),
                   "attention backward");
+            if (rotary())  // gradients of the turned q, k -> of the qkv product's output
+                CHECK(rope_apply<T>(dqkv, 3 * C, BT, 2 * C, C / NH, S, 0, rope_tab(), true, M), "rope backward");
             // c_attn: side: dW = dqkv^T ln1, db; main: dln1 = dqkv W_qkv
             if ((rc = stream_wait(a, SD, M))) return rc;
             if ((rc = side_dw(dqkv, 3 * C, act(x.ln1), C, lp(l, P_QKVW), lp(l, P_QKVB)))) return rc;
@@ -565,7 +577,7 @@ struct Model {
         // embedding: dwte += scatter (after the side stream's lm_head dW), dwpe
         if ((rc = wait(M, a->ev_wte))) return rc;
         CHECK(encoder_backward<T>(grad(a->o_wte), grad(a->o_wpe), act(a->dres[cur]), a->inputs, B, S, P, C,
-                                  at<int>(a, a->census), at<int>(a, a->census) + V, M),
+                                  at<int>(a, a->census), at<int>(a, a->census) + V, M, !rotary()),
               "encoder backward");
         // join: everything the side stream enqueued finishes before later main-stream work
         if ((rc = mark(a->ev_end, SD))) return rc;
@@ -685,6 +697,21 @@ int gpt2_backward_adamw(gpt2_arena* a, float lr, float beta1, float beta2, float
     const AdamArgs o = adam_args(lr, beta1, beta2, eps, weight_decay, step);
     return a->dtype == GPT2_BF16 ? Model<bf16>(a, (hipStream_t)stream).backward(&o)
                                  : Model<float>(a, (hipStream_t)stream).backward(&o);
+}
+
+int gpt2_set_position_encoding(gpt2_arena* a, int32_t mode, float base, void* stream) {
+    if (!a) return fail(GPT2_E_INVAL, "arena is NULL");
+    if (mode == GPT2_POS_LEARNED) {
+        a->pos_enc = mode;
+        return GPT2_OK;
+    }
+    if (mode != GPT2_POS_ROTARY) return fail(GPT2_E_INVAL, "unknown position encoding");
+    if (!(base > 1.f) || !std::isfinite(base)) return fail(GPT2_E_INVAL, "rotary base must be finite and > 1");
+    int rc = hip_check(rope_table(at<float2>(a, a->rope), a->cfg.max_seq_len, a->hs, (double)base, (hipStream_t)stream),
+                       "rope table");
+    if (rc) return rc;
+    a->pos_enc = mode;
+    return GPT2_OK;
 }
 
 int gpt2_mx_attach(gpt2_arena* a, void* device_base, size_t device_bytes, size_t* required_bytes) {
@@ -921,7 +948,9 @@ int gpt2_gen_decode(gpt2_gen* g, const int32_t* d_tokens, float* d_logits, void*
     };
     int rc;
     // x = wte[token] + wpe[t] for the one new row of every sequence
-    CHECK(encoder_forward<bf16>(buf(g->res[0]), d_tokens, master + a->o_wte, master + a->o_wpe, Bg, 1, C, s, t),
+    const bool rot = a->pos_enc == GPT2_POS_ROTARY;
+    CHECK(encoder_forward<bf16>(buf(g->res[0]), d_tokens, master + a->o_wte, rot ? nullptr : master + a->o_wpe, Bg, 1,
+                                C, s, t),
           "encoder");
     int cur = 0;
     for (int l = 0; l < L; ++l) {
@@ -933,6 +962,10 @@ int gpt2_gen_decode(gpt2_gen* g, const int32_t* d_tokens, float* d_logits, void*
         if ((rc = skinny(xin, C, lp(l, P_LN1W), lp(l, P_QKVW), 3 * C, C, cache + (int64_t)t * C3, row, nullptr,
                          nullptr, master + lp(l, P_QKVB), EPI_BIAS)))
             return rc;
+        if (rot)  // the new rows' q and k, all at position t
+            CHECK(rope_apply<bf16>(cache + (int64_t)t * C3, row, Bg, 2 * C, C / NH, 1, t, at<float2>(a, a->rope), false,
+                                   s),
+                  "rope");
         CHECK(attention_decode(buf(g->atty), cache, Bg, t + 1, C, NH, row, s), "attention");
         if ((rc = skinny(buf(g->atty), C, -1, lp(l, P_PROJW), C, C, res2, C, nullptr, xin, master + lp(l, P_PROJB),
                          EPI_BIAS_RES)))

@@ -103,7 +103,7 @@ hipError_t mean_loss(float* loss, const float* losses, int N, hipStream_t s);
 // first / count: int [V] scratch, INT_MAX / 0 on entry (token_census_reset) and on return.
 template <class T>
 hipError_t encoder_backward(float* dwte, float* dwpe, const T* dx, const int32_t* tok, int B, int T_, int P, int C,
-                            int* first, int* count, hipStream_t s);
+                            int* first, int* count, hipStream_t s, bool wpe_used = true);
 hipError_t token_census_reset(int* first, int* count, int V, hipStream_t s);
 hipError_t adamw(float* p, const float* g, float* m, float* v, bf16* p16, int64_t n, float lr, float b1, float b2,
                  float eps, float wd, float c1, float c2, hipStream_t s);
@@ -124,6 +124,15 @@ hipError_t mx_quantize(const bf16* x, int64_t ldx, int R, int K, uint8_t* q, int
 // [N, K] (ldb bytes), K a multiple of 128 (zero-padded), lda / ldb multiples of 16;
 // scales a.sa / a.sb; output bf16 with EPI_BIAS, EPI_BIAS_RES or EPI_BIAS_GELU.
 hipError_t gemm_mx(const GemmArgs& a, int epi, hipStream_t s);
+
+// Rotary position embedding: tab [P][hs / 2] (cos, sin) of m base^(-2i / hs), built in
+// float64; rope_apply turns, in place, the pairs of the first ncols columns (whole
+// heads of size hs) of rows x[r] (row stride ld) for position pos0 + r % period
+// (inverse: turns back).
+hipError_t rope_table(float2* tab, int P, int hs, double base, hipStream_t s);
+template <class T>
+hipError_t rope_apply(T* x, int64_t ld, int rows, int ncols, int hs, int period, int pos0, const float2* tab,
+                      bool inverse, hipStream_t s);
 
 hipError_t splitk_reduce_bf16(bf16* C, int64_t ldc, const float* ws, int splits, int M, int N, const float* bias,
                               hipStream_t s);

@@ -20,7 +20,8 @@ __global__ __launch_bounds__(256) void encoder_forward_kernel(T* out, const int3
     int row = (int)(i / c4), c = (int)(i % c4) * 4;
     int t = pos0 + row % T_;
     float4 a = *(const float4*)(wte + (int64_t)tok[row] * C + c);
-    float4 p = *(const float4*)(wpe + (int64_t)t * C + c);
+    // no wpe: positions enter through the rotary embedding of the queries and keys
+    float4 p = wpe ? *(const float4*)(wpe + (int64_t)t * C + c) : make_float4(0.f, 0.f, 0.f, 0.f);
     T* o = out + (int64_t)row * C + c;
     o[0] = from_f32<T>(a.x + p.x);
     o[1] = from_f32<T>(a.y + p.y);
@@ -697,7 +698,7 @@ __global__ __launch_bounds__(256) void encoder_backward_wpe_kernel(float* dwpe, 
 
 template <class T>
 hipError_t encoder_backward(float* dwte, float* dwpe, const T* dx, const int32_t* tok, int B, int T_, int P, int C,
-                            int* first, int* count, hipStream_t s) {
+                            int* first, int* count, hipStream_t s, bool wpe_used) {
     if (C > 8 * 256) return hipErrorInvalidValue;
     {
         ProfScope prof(s, "token_census", 0, 4.0 * B * T_);
@@ -713,8 +714,9 @@ hipError_t encoder_backward(float* dwte, float* dwpe, const T* dx, const int32_t
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     ProfScope prof2(s, "encoder_bwd_wpe", 0, (double)B * T_ * C * sizeof(T) + 4.0 * P * C);
+    // an unused wpe (rotary positions) gets a zero gradient: no row t < 0 exists
     hipLaunchKernelGGL(encoder_backward_wpe_kernel<T>, dim3(cdiv((int64_t)P * C, 256)), dim3(256), 0, s, dwpe, dx, B,
-                       T_, P, C);
+                       wpe_used ? T_ : 0, P, C);
     return hipGetLastError();
 }
 
@@ -872,7 +874,7 @@ hipError_t splitk_reduce_bf16(bf16* C, int64_t ldc, const float* ws, int splits,
     template hipError_t bias_grad<T>(float*, const T*, int, int, int64_t, float*, size_t, hipStream_t);          \
     template hipError_t crossentropy_fused<T>(T*, float*, const int32_t*, int, int, int64_t, float, hipStream_t); \
     template hipError_t encoder_backward<T>(float*, float*, const T*, const int32_t*, int, int, int, int, int*,  \
-                                            int*, hipStream_t);
+                                            int*, hipStream_t, bool);
 GPT2_INST(float)
 GPT2_INST(bf16)
 
