@@ -67,7 +67,7 @@ def measured_traffic(workload, kernel):
     return out
 
 
-def cpu_baseline(w, params, x, y, budget_s=10.0, T_sample=256):
+def cpu_baseline(w, params, x, y, budget_s=10.0, T_sample=256, rotary=False):
     """The float oracle on a bounded sample of the workload: the first T_sample
     tokens of batch row 0, full forward + backward + AdamW, repeated until about
     budget_s seconds have passed."""
@@ -75,6 +75,8 @@ def cpu_baseline(w, params, x, y, budget_s=10.0, T_sample=256):
     T_sample = min(T_sample, w.T)
     o = oracle.Oracle(w.model, 1, T_sample, "f32")
     o.set("params", params)
+    if rotary:
+        o.set_rotary(True)
     xs, ys = x[:1, :T_sample], y[:1, :T_sample]
     steps, t0 = 0, time.perf_counter()
     while True:
@@ -106,6 +108,8 @@ def main():
     ap.add_argument("--decode", action="store_true",
                     help="measure incremental generation instead of training: prefill a prompt, then time "
                          "--steps one-row decode steps per sequence (prints its own JSON line)")
+    ap.add_argument("--rotary", action="store_true",
+                    help="the training step with the rotary position embedding instead of the learned wpe")
     ap.add_argument("--mxfp8", action="store_true",
                     help="time the forward pass (with the loss) with MX FP8 block and lm_head products beside the "
                          "bf16 forward (prints its own JSON line)")
@@ -149,6 +153,8 @@ def main():
     torch.cuda.set_device(0)
     arena = Arena(m, w.B, w.T, w.dtype)
     arena.load_params(params)
+    if args.rotary:
+        arena.set_position_encoding(binding.GPT2_POS_ROTARY)
     xi = torch.from_numpy(x).to(torch.int32).cuda()
     yi = torch.from_numpy(y).to(torch.int32).cuda()
     t = 0
@@ -215,24 +221,41 @@ def main():
                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
         roof["avg_launch_us"] = round(avg_s * 1e6, 2)
         roof["algorithmic_bytes_per_launch"] = round(dom["bytes"] / dom["launches"])
-        roof.update(measured_traffic(w.name, dom["name"]))
+        roof.update(measured_traffic(w.name + ("_rotary" if args.rotary else ""), dom["name"]))
+
+    rope = None
+    if args.rotary:  # the rotary turns: elementwise, HBM-bound (q | k columns read and written in place)
+        rope = {}
+        for s in stats:
+            if s["name"] in ("rope_fwd", "rope_bwd"):
+                avg_s = s["total_ms"] / s["launches"] / 1e3
+                gbs = s["bytes"] / s["launches"] / avg_s / 1e9
+                rope[s["name"]] = {"avg_launch_us": round(avg_s * 1e6, 2), "bytes_per_launch": round(s["bytes"] / s["launches"]),
+                                   "achieved_gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+                                   "ms_per_step": round(s["total_ms"] / args.profile_steps, 4)}
 
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline ...")
-        cpu = cpu_baseline(w, params, x, y)
+        cpu = cpu_baseline(w, params, x, y, rotary=args.rotary)
         log(f"[bench] CPU oracle: {cpu['value']:.1f} tokens/s on {cpu['cores']} threads")
 
+    metric, wname = METRIC, w.name
+    if args.rotary:
+        metric = METRIC.replace("GPT-2 124M", "GPT-2 124M with rotary positions")
+        wname = w.name + "_rotary"
     out = {
-        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "metric": metric, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded random-init weights, uniform token ids)"
         if w.tokens == "uniform" else "synthetic (seeded random-init weights, Zipf token ids)",
-        "config": {"workload": w.name, "B": w.B, "T": w.T, "layers": m.num_layers, "heads": m.num_heads,
+        "config": {"workload": wname, "B": w.B, "T": w.T, "layers": m.num_layers, "heads": m.num_heads,
                    "channels": m.channels, "vocab": m.vocab_size, "tokens": w.tokens},
         "mfma_peak_frac": round(mfma_frac, 4), "model_tflop_per_step": round(F / 1e12, 4),
         "loss": round(loss, 5), "roofline": roof, "cpu_baseline": cpu,
     }
+    if rope is not None:
+        out["rope_kernels"] = rope
     print(json.dumps(out), flush=True)
 
 

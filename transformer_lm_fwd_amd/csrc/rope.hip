@@ -8,6 +8,8 @@
 // fp32.  The turn is done in place on the q | k columns of the qkv rows after the
 // qkv product (forward, and for each decode row), and turned back on the gradients
 // the attention backward leaves there.
+#include <algorithm>
+
 #include "kernels.h"
 
 namespace gpt2 {
@@ -64,7 +66,10 @@ hipError_t rope_apply(T* x, int64_t ld, int rows, int ncols, int hs, int period,
     constexpr int KV = Vec16<T>::N;
     if (rows <= 0) return hipSuccess;
     if (hs % KV || ncols % hs || ld % KV || period <= 0 || pos0 < 0) return hipErrorInvalidValue;
-    ProfScope prof(s, inverse ? "rope_bwd" : "rope_fwd", 0, 2.0 * rows * ncols * sizeof(T) + 4.0 * rows * ncols);
+    // algorithmic bytes: the q | k columns read and written once, and the table rows of
+    // the positions present (read once; the rows are reused across sequences)
+    const double table = (double)std::min(period, rows) * (hs / 2) * 8;
+    ProfScope prof(s, inverse ? "rope_bwd" : "rope_fwd", 0, 2.0 * rows * ncols * sizeof(T) + table);
     const int64_t threads = (int64_t)rows * (ncols / KV);
     hipLaunchKernelGGL(rope_kernel<T>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, x, ld, rows, ncols, hs,
                        period, pos0, tab, inverse ? -1.f : 1.f);
