@@ -66,6 +66,14 @@ def lib():
         L.orc_forward.restype = dbl
         L.orc_backward.argtypes = [vp]
         L.orc_adamw.argtypes = [vp, dbl, dbl, dbl, dbl, dbl, i32]
+        L.orc_create_block.argtypes = [ctypes.c_int] * 9
+        L.orc_create_block.restype = vp
+        L.orc_num_parameters_block.argtypes = [ctypes.c_int] * 6
+        L.orc_num_parameters_block.restype = i64
+        L.orc_silu.argtypes = [vp, vp, i64]
+        L.orc_silu.restype = None
+        L.orc_silu_grad.argtypes = [vp, vp, i64]
+        L.orc_silu_grad.restype = None
         L.orc_set_rotary.argtypes = [vp, ctypes.c_int, ctypes.c_double]
         L.orc_rope.argtypes = [vp, vp, ctypes.c_int, ctypes.c_int, vp, ctypes.c_double, ctypes.c_int]
         L.orc_rope.restype = None
@@ -81,7 +89,24 @@ def _ptr(a: np.ndarray):
 
 
 def num_parameters(m) -> int:
-    return int(lib().orc_num_parameters(m.vocab_size, m.max_seq_len, m.num_layers, m.num_heads, m.channels))
+    block = {"gpt2": 0, "llama": 1}[getattr(m, "block", "gpt2")]
+    return int(lib().orc_num_parameters_block(m.vocab_size, m.max_seq_len, m.num_layers, m.num_heads, m.channels,
+                                              block))
+
+
+def silu(x) -> np.ndarray:
+    """silu(x) = x sigmoid(x), the gate of the Llama-style block's SwiGLU MLP."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    y = np.empty_like(x)
+    lib().orc_silu(_ptr(x), _ptr(y), x.size)
+    return y
+
+
+def silu_grad(x) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    y = np.empty_like(x)
+    lib().orc_silu_grad(_ptr(x), _ptr(y), x.size)
+    return y
 
 
 def num_activations(m, B: int, T: int) -> int:
@@ -126,7 +151,8 @@ class Oracle:
     def __init__(self, m, B: int, T: int, prec: str = "f64"):
         self.m, self.B, self.T = m, B, T
         p = {"f32": 0, "f64": 1}[prec]
-        h = lib().orc_create(p, m.vocab_size, m.max_seq_len, m.num_layers, m.num_heads, m.channels, B, T)
+        block = {"gpt2": 0, "llama": 1}[getattr(m, "block", "gpt2")]
+        h = lib().orc_create_block(p, m.vocab_size, m.max_seq_len, m.num_layers, m.num_heads, m.channels, B, T, block)
         if not h:
             raise ValueError(lib().orc_last_error().decode())
         self.h = h

@@ -53,7 +53,18 @@ namespace {
 
 struct Shape {
     int V, P, L, NH, C;  // vocab_size, max_seq_len, num_layers, num_heads, channels
+    int block = 0;       // 0: GPT-2 block; 1: Llama-style block (see llama_hidden)
 };
+
+// Llama-style block ([llm.c]: the layers to add for Llama-2-type models; [torch-R]
+// names RoPE): x = x + attn(rms_1(x)), x = x + swiglu_mlp(rms_2(x)), no biases, the
+// rotary position embedding instead of wpe.  RMSNorm: y = x / sqrt(mean(x^2) + eps) * w.
+// SwiGLU MLP of width H: down( silu(x W_gate^T) * (x W_up^T) ), silu(g) = g sigmoid(g);
+// the gate and up weights are stored interleaved, row 2j = gate_j, row 2j + 1 = up_j, so
+// the product's output holds (g_j, u_j) in columns 2j, 2j + 1.  H = 8C/3 rounded up to
+// a multiple of 64 (about the parameter count of a 4C GELU MLP).  The final norm is an
+// RMSNorm; the lm_head stays tied to wte; wpe stays in the array, unused.
+static int64_t llama_hidden(int64_t C) { return 64 * ((C + 23) / 24); }
 
 // ----------------------------------------------------------------------------- parameter list
 // Layer-major order following the module tree of [torch-R] 总体架构 / Transformer block:
@@ -62,6 +73,13 @@ enum PIdx { LN1W, LN1B, QKVW, QKVB, PROJW, PROJB, LN2W, LN2B, FCW, FCB, FCPW, FC
 
 static void layer_param_sizes(const Shape& s, int64_t out[NPL]) {
     int64_t C = s.C;
+    if (s.block == 1) {  // no biases, RMSNorm gains only, gate|up and down
+        const int64_t H = llama_hidden(C);
+        for (int i = 0; i < NPL; ++i) out[i] = 0;
+        out[LN1W] = C; out[QKVW] = 3 * C * C; out[PROJW] = C * C; out[LN2W] = C;
+        out[FCW] = 2 * H * C; out[FCPW] = C * H;
+        return;
+    }
     out[LN1W] = C;         out[LN1B] = C;
     out[QKVW] = 3 * C * C; out[QKVB] = 3 * C;
     out[PROJW] = C * C;    out[PROJB] = C;
@@ -76,7 +94,7 @@ static int64_t count_params(const Shape& s) {
     int64_t n = (int64_t)s.V * s.C + (int64_t)s.P * s.C;
     for (int l = 0; l < s.L; ++l)
         for (int i = 0; i < NPL; ++i) n += per[i];
-    return n + 2 * (int64_t)s.C;
+    return n + (s.block == 1 ? 1 : 2) * (int64_t)s.C;  // final norm: w (and b for LayerNorm)
 }
 
 template <class R>
@@ -96,7 +114,7 @@ struct Params {
         for (int l = 0; l < s.L; ++l)
             for (int i = 0; i < NPL; ++i) { t[i][l] = p; p += per[i]; }
         lnfw = p; p += s.C;
-        lnfb = p; p += s.C;
+        lnfb = p; p += s.block == 1 ? 0 : s.C;
     }
 };
 
@@ -127,7 +145,8 @@ static int64_t act_size(const Shape& s, int B, int T, int a) {
             return BT;
         case A_QKV: return 3 * BT * C;
         case A_PREATT: case A_ATT: return (int64_t)B * s.NH * T * T;
-        case A_FCH: case A_FCH_GELU: return 4 * BT * C;
+        case A_FCH: return s.block == 1 ? 2 * BT * llama_hidden(C) : 4 * BT * C;
+        case A_FCH_GELU: return s.block == 1 ? BT * llama_hidden(C) : 4 * BT * C;
         case A_LOGITS: case A_PROBS: return BT * s.V;
     }
     return 0;
@@ -193,6 +212,45 @@ static void layernorm_forward(R* out, R* mean, R* rstd, const R* inp, const R* w
         mean[i] = m;
         rstd[i] = r;
     }
+}
+
+// RMSNorm (Llama-style block): y = x * rstd * w, rstd = 1 / sqrt(mean_c(x^2) + eps),
+// eps = 1e-5 as for LayerNorm; mean[] is written as 0.
+template <class R>
+static void rmsnorm_forward(R* out, R* mean, R* rstd, const R* inp, const R* w, int64_t N, int C) {
+    const R eps = R(1e-5);
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < N; ++i) {
+        const R* x = inp + i * C;
+        R ms = 0;
+        for (int c = 0; c < C; ++c) ms += x[c] * x[c];
+        ms /= C;
+        const R r = R(1) / std::sqrt(ms + eps);
+        R* o = out + i * C;
+        for (int c = 0; c < C; ++c) o[c] = x[c] * r * w[c];
+        mean[i] = 0;
+        rstd[i] = r;
+    }
+}
+
+template <class R>
+static inline R silu(R g) { return g / (R(1) + std::exp(-g)); }
+// d silu / dg = sigma(g) (1 + g (1 - sigma(g)))
+template <class R>
+static inline R silu_grad(R g) {
+    const R sg = R(1) / (R(1) + std::exp(-g));
+    return sg * (R(1) + g * (R(1) - sg));
+}
+
+// SwiGLU: gu [N, 2H] holds (g_j, u_j) in columns 2j, 2j+1; out [N, H] = silu(g) * u.
+template <class R>
+static void swiglu_forward(R* out, const R* gu, int64_t N, int64_t H) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < N; ++i)
+        for (int64_t j = 0; j < H; ++j) {
+            const R g = gu[i * 2 * H + 2 * j], u = gu[i * 2 * H + 2 * j + 1];
+            out[i * H + j] = silu(g) * u;
+        }
 }
 
 // Dot product with eight interleaved partial sums (a fixed summation order).
@@ -359,6 +417,39 @@ static void layernorm_backward(R* dinp, R* dw, R* db, const R* dout, const R* in
 
 // Linear backward for out = inp * w^T + bias:
 //   dinp = dout * w,  dw = dout^T * inp,  dbias = column sums of dout.
+// RMSNorm backward, from y = xhat * w with xhat = x * rstd:
+//   dxhat = dy * w,  dx = rstd * (dxhat - xhat * mean_c(dxhat * xhat)),  dw = sum_rows dy * xhat
+template <class R>
+static void rmsnorm_backward(R* dinp, R* dw, const R* dout, const R* inp, const R* w, const R* rstd, int64_t N,
+                             int C) {
+    for (int64_t i = 0; i < N; ++i) {
+        const R* dy = dout + i * C;
+        const R* x = inp + i * C;
+        const R r = rstd[i];
+        R m = 0;
+        for (int c = 0; c < C; ++c) m += dy[c] * w[c] * x[c] * r;
+        m /= C;
+        R* dx = dinp + i * C;
+        for (int c = 0; c < C; ++c) {
+            const R xh = x[c] * r;
+            dx[c] += r * (dy[c] * w[c] - xh * m);
+            dw[c] += dy[c] * xh;
+        }
+    }
+}
+
+// SwiGLU backward: dg = dh u silu'(g), du = dh silu(g), into the interleaved columns.
+template <class R>
+static void swiglu_backward(R* dgu, const R* dout, const R* gu, int64_t N, int64_t H) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < N; ++i)
+        for (int64_t j = 0; j < H; ++j) {
+            const R g = gu[i * 2 * H + 2 * j], u = gu[i * 2 * H + 2 * j + 1], dh = dout[i * H + j];
+            dgu[i * 2 * H + 2 * j] += dh * u * silu_grad(g);
+            dgu[i * 2 * H + 2 * j + 1] += dh * silu(g);
+        }
+}
+
 template <class R>
 static void matmul_backward(R* dinp, R* dw, R* dbias, const R* dout, const R* inp, const R* w,
                             int64_t N, int IC, int OC) {
@@ -525,28 +616,41 @@ struct Model : ModelBase {
         std::memcpy(inputs.data(), inp, sizeof(int) * BT);
         have_targets = tgt != nullptr;
         if (tgt) std::memcpy(targets.data(), tgt, sizeof(int) * BT);
+        const bool llama = s.block == 1;
+        const int64_t H = llama_hidden(C);
+        auto bias = [&](int k, int l) -> const R* { return llama ? nullptr : P.t[k][l]; };
+        auto norm = [&](R* out, R* mean, R* rstd, const R* x, const R* w, const R* b) {
+            if (llama) rmsnorm_forward(out, mean, rstd, x, w, BT, C);
+            else layernorm_forward(out, mean, rstd, x, w, b, BT, C);
+        };
         encoder_forward(A(A_ENCODED), inp, P.wte, rotary ? (const R*)nullptr : P.wpe, B, T, C);
         if (rotary) qkv_rot.assign(L, std::vector<R>((size_t)3 * BT * C));
         for (int l = 0; l < L; ++l) {
             const R* x = l == 0 ? A(A_ENCODED) : A(A_RESIDUAL3, l - 1);
-            layernorm_forward(A(A_LN1, l), A(A_LN1_MEAN, l), A(A_LN1_RSTD, l), x, P.t[LN1W][l], P.t[LN1B][l], BT, C);
-            matmul_forward(A(A_QKV, l), A(A_LN1, l), P.t[QKVW][l], P.t[QKVB][l], BT, C, 3 * C);
+            norm(A(A_LN1, l), A(A_LN1_MEAN, l), A(A_LN1_RSTD, l), x, P.t[LN1W][l], P.t[LN1B][l]);
+            matmul_forward(A(A_QKV, l), A(A_LN1, l), P.t[QKVW][l], bias(QKVB, l), BT, C, 3 * C);
             const R* qkv = A(A_QKV, l);
             if (rotary) {
                 rope_qkv(qkv_rot[l].data(), A(A_QKV, l), B, T, C, NH, rope_base, +1);
                 qkv = qkv_rot[l].data();
             }
             attention_forward(A(A_ATTY, l), A(A_PREATT, l), A(A_ATT, l), qkv, B, T, C, NH);
-            matmul_forward(A(A_ATTPROJ, l), A(A_ATTY, l), P.t[PROJW][l], P.t[PROJB][l], BT, C, C);
+            matmul_forward(A(A_ATTPROJ, l), A(A_ATTY, l), P.t[PROJW][l], bias(PROJB, l), BT, C, C);
             residual_forward(A(A_RESIDUAL2, l), x, A(A_ATTPROJ, l), BT * C);
-            layernorm_forward(A(A_LN2, l), A(A_LN2_MEAN, l), A(A_LN2_RSTD, l), A(A_RESIDUAL2, l), P.t[LN2W][l], P.t[LN2B][l], BT, C);
-            matmul_forward(A(A_FCH, l), A(A_LN2, l), P.t[FCW][l], P.t[FCB][l], BT, C, 4 * C);
-            gelu_forward(A(A_FCH_GELU, l), A(A_FCH, l), BT * 4 * C);
-            matmul_forward(A(A_FCPROJ, l), A(A_FCH_GELU, l), P.t[FCPW][l], P.t[FCPB][l], BT, 4 * C, C);
+            norm(A(A_LN2, l), A(A_LN2_MEAN, l), A(A_LN2_RSTD, l), A(A_RESIDUAL2, l), P.t[LN2W][l], P.t[LN2B][l]);
+            if (llama) {
+                matmul_forward(A(A_FCH, l), A(A_LN2, l), P.t[FCW][l], (const R*)nullptr, BT, C, (int)(2 * H));
+                swiglu_forward(A(A_FCH_GELU, l), A(A_FCH, l), BT, H);
+                matmul_forward(A(A_FCPROJ, l), A(A_FCH_GELU, l), P.t[FCPW][l], (const R*)nullptr, BT, (int)H, C);
+            } else {
+                matmul_forward(A(A_FCH, l), A(A_LN2, l), P.t[FCW][l], P.t[FCB][l], BT, C, 4 * C);
+                gelu_forward(A(A_FCH_GELU, l), A(A_FCH, l), BT * 4 * C);
+                matmul_forward(A(A_FCPROJ, l), A(A_FCH_GELU, l), P.t[FCPW][l], P.t[FCPB][l], BT, 4 * C, C);
+            }
             residual_forward(A(A_RESIDUAL3, l), A(A_RESIDUAL2, l), A(A_FCPROJ, l), BT * C);
         }
         const R* xL = A(A_RESIDUAL3, L - 1);
-        layernorm_forward(A(A_LNF), A(A_LNF_MEAN), A(A_LNF_RSTD), xL, P.lnfw, P.lnfb, BT, C);
+        norm(A(A_LNF), A(A_LNF_MEAN), A(A_LNF_RSTD), xL, P.lnfw, P.lnfb);
         // [c3000] Transformer本体 / [torch-R] 输出: logits = final hidden state times the
         // token-embedding matrix (tied lm_head, no bias).
         matmul_forward(A(A_LOGITS), A(A_LNF), P.wte, (const R*)nullptr, BT, C, V);
@@ -570,10 +674,16 @@ struct Model : ModelBase {
         std::fill(grads.begin(), grads.end(), R(0));
         std::fill(dA.mem.begin(), dA.mem.end(), R(0));
         crossentropy_softmax_backward(dA(A_LOGITS), A(A_PROBS), targets.data(), BT, V);
+        const bool llama = s.block == 1;
+        const int64_t H = llama_hidden(C);
+        auto gbias = [&](int k, int l) -> R* { return llama ? nullptr : G.t[k][l]; };
+        auto norm_bwd = [&](R* dx, R* dw, R* db, const R* dy, const R* x, const R* w, const R* mean, const R* rstd) {
+            if (llama) rmsnorm_backward(dx, dw, dy, x, w, rstd, BT, C);
+            else layernorm_backward(dx, dw, db, dy, x, w, mean, rstd, BT, C);
+        };
         matmul_backward(dA(A_LNF), G.wte, (R*)nullptr, dA(A_LOGITS), A(A_LNF), P.wte, BT, C, V);
         R* dxL = dA(A_RESIDUAL3, L - 1);
-        layernorm_backward(dxL, G.lnfw, G.lnfb, dA(A_LNF), A(A_RESIDUAL3, L - 1), P.lnfw,
-                           A(A_LNF_MEAN), A(A_LNF_RSTD), BT, C);
+        norm_bwd(dxL, G.lnfw, G.lnfb, dA(A_LNF), A(A_RESIDUAL3, L - 1), P.lnfw, A(A_LNF_MEAN), A(A_LNF_RSTD));
         for (int l = L - 1; l >= 0; --l) {
             const R* x = l == 0 ? A(A_ENCODED) : A(A_RESIDUAL3, l - 1);
             R* dx = l == 0 ? dA(A_ENCODED) : dA(A_RESIDUAL3, l - 1);
@@ -581,15 +691,24 @@ struct Model : ModelBase {
             // residual3 = residual2 + fcproj: the gradient reaches both unchanged
             R* dres2 = dA(A_RESIDUAL2, l);
             for (int64_t i = 0; i < BT * C; ++i) { dres2[i] += dres3[i]; dA(A_FCPROJ, l)[i] += dres3[i]; }
-            matmul_backward(dA(A_FCH_GELU, l), G.t[FCPW][l], G.t[FCPB][l], dA(A_FCPROJ, l), A(A_FCH_GELU, l),
-                            P.t[FCPW][l], BT, 4 * C, C);
-            gelu_backward(dA(A_FCH, l), A(A_FCH, l), dA(A_FCH_GELU, l), BT * 4 * C);
-            matmul_backward(dA(A_LN2, l), G.t[FCW][l], G.t[FCB][l], dA(A_FCH, l), A(A_LN2, l), P.t[FCW][l], BT, C, 4 * C);
-            layernorm_backward(dres2, G.t[LN2W][l], G.t[LN2B][l], dA(A_LN2, l), A(A_RESIDUAL2, l), P.t[LN2W][l],
-                               A(A_LN2_MEAN, l), A(A_LN2_RSTD, l), BT, C);
+            if (llama) {
+                matmul_backward(dA(A_FCH_GELU, l), G.t[FCPW][l], (R*)nullptr, dA(A_FCPROJ, l), A(A_FCH_GELU, l),
+                                P.t[FCPW][l], BT, (int)H, C);
+                swiglu_backward(dA(A_FCH, l), dA(A_FCH_GELU, l), A(A_FCH, l), BT, H);
+                matmul_backward(dA(A_LN2, l), G.t[FCW][l], (R*)nullptr, dA(A_FCH, l), A(A_LN2, l), P.t[FCW][l], BT, C,
+                                (int)(2 * H));
+            } else {
+                matmul_backward(dA(A_FCH_GELU, l), G.t[FCPW][l], G.t[FCPB][l], dA(A_FCPROJ, l), A(A_FCH_GELU, l),
+                                P.t[FCPW][l], BT, 4 * C, C);
+                gelu_backward(dA(A_FCH, l), A(A_FCH, l), dA(A_FCH_GELU, l), BT * 4 * C);
+                matmul_backward(dA(A_LN2, l), G.t[FCW][l], G.t[FCB][l], dA(A_FCH, l), A(A_LN2, l), P.t[FCW][l], BT, C,
+                                4 * C);
+            }
+            norm_bwd(dres2, G.t[LN2W][l], G.t[LN2B][l], dA(A_LN2, l), A(A_RESIDUAL2, l), P.t[LN2W][l],
+                     A(A_LN2_MEAN, l), A(A_LN2_RSTD, l));
             // residual2 = x + attproj
             for (int64_t i = 0; i < BT * C; ++i) { dx[i] += dres2[i]; dA(A_ATTPROJ, l)[i] += dres2[i]; }
-            matmul_backward(dA(A_ATTY, l), G.t[PROJW][l], G.t[PROJB][l], dA(A_ATTPROJ, l), A(A_ATTY, l),
+            matmul_backward(dA(A_ATTY, l), G.t[PROJW][l], gbias(PROJB, l), dA(A_ATTPROJ, l), A(A_ATTY, l),
                             P.t[PROJW][l], BT, C, C);
             if (rotary) {
                 // gradients reach the turned q | k | v, then turn back to the qkv product's output
@@ -601,9 +720,10 @@ struct Model : ModelBase {
                 attention_backward(dA(A_QKV, l), dA(A_PREATT, l), dA(A_ATT, l), dA(A_ATTY, l), A(A_QKV, l),
                                    A(A_ATT, l), B, T, C, NH);
             }
-            matmul_backward(dA(A_LN1, l), G.t[QKVW][l], G.t[QKVB][l], dA(A_QKV, l), A(A_LN1, l), P.t[QKVW][l], BT, C, 3 * C);
-            layernorm_backward(dx, G.t[LN1W][l], G.t[LN1B][l], dA(A_LN1, l), x, P.t[LN1W][l],
-                               A(A_LN1_MEAN, l), A(A_LN1_RSTD, l), BT, C);
+            matmul_backward(dA(A_LN1, l), G.t[QKVW][l], gbias(QKVB, l), dA(A_QKV, l), A(A_LN1, l), P.t[QKVW][l], BT, C,
+                            3 * C);
+            norm_bwd(dx, G.t[LN1W][l], G.t[LN1B][l], dA(A_LN1, l), x, P.t[LN1W][l], A(A_LN1_MEAN, l),
+                     A(A_LN1_RSTD, l));
         }
         encoder_backward(G.wte, rotary ? (R*)nullptr : G.wpe, dA(A_ENCODED), inputs.data(), B, T, C);
         return 0;
@@ -672,15 +792,16 @@ int64_t orc_num_activations(int V, int P, int L, int NH, int C, int B, int T) {
 }
 
 // prec: 0 = float, 1 = double.  Returns NULL on invalid shapes or allocation failure.
-void* orc_create(int prec, int V, int P, int L, int NH, int C, int B, int T) {
-    if (V < 1 || P < 1 || L < 1 || NH < 1 || C < 1 || C % NH || B < 1 || T < 1 || T > P) {
+// block: 0 GPT-2, 1 Llama-style (which always uses the rotary position embedding).
+void* orc_create_block(int prec, int V, int P, int L, int NH, int C, int B, int T, int block) {
+    if (V < 1 || P < 1 || L < 1 || NH < 1 || C < 1 || C % NH || B < 1 || T < 1 || T > P || block < 0 || block > 1) {
         g_err = "invalid shape";
         return nullptr;
     }
-    Shape s{V, P, L, NH, C};
+    Shape s{V, P, L, NH, C, block};
     try {
-        if (prec == 0) { auto* m = new Model<float>(s, B, T); m->prec = 0; return m; }
-        if (prec == 1) { auto* m = new Model<double>(s, B, T); m->prec = 1; return m; }
+        if (prec == 0) { auto* m = new Model<float>(s, B, T); m->prec = 0; m->rotary = block == 1; return m; }
+        if (prec == 1) { auto* m = new Model<double>(s, B, T); m->prec = 1; m->rotary = block == 1; return m; }
     } catch (const std::bad_alloc&) {
         g_err = "out of host memory";
         return nullptr;
@@ -688,6 +809,17 @@ void* orc_create(int prec, int V, int P, int L, int NH, int C, int B, int T) {
     g_err = "prec must be 0 or 1";
     return nullptr;
 }
+
+void* orc_create(int prec, int V, int P, int L, int NH, int C, int B, int T) {
+    return orc_create_block(prec, V, P, L, NH, C, B, T, 0);
+}
+
+int64_t orc_num_parameters_block(int V, int P, int L, int NH, int C, int block) {
+    return count_params(Shape{V, P, L, NH, C, block});
+}
+
+void orc_silu(const double* x, double* y, int64_t n) { for (int64_t i = 0; i < n; ++i) y[i] = silu(x[i]); }
+void orc_silu_grad(const double* x, double* y, int64_t n) { for (int64_t i = 0; i < n; ++i) y[i] = silu_grad(x[i]); }
 
 void orc_destroy(void* h) { delete (ModelBase*)h; }
 
@@ -760,6 +892,7 @@ double orc_forward(void* h, const int* inputs, const int* targets) {
 // Rotary position embedding on (1) or off (0, learned wpe) for the following passes.
 int orc_set_rotary(void* h, int on, double base) {
     if (!(base > 1.0)) { g_err = "rotary base must exceed 1"; return -1; }
+    if (!on && ((ModelBase*)h)->s.block == 1) { g_err = "the Llama-style block always uses rotary positions"; return -1; }
     ORC_DISPATCH(h, { M->rotary = on != 0; M->rope_base = base; M->have_forward = false; M->qkv_rot.clear(); });
     return 0;
 }

@@ -48,6 +48,12 @@ class ModelShape:
     num_layers: int
     num_heads: int
     channels: int
+    block: str = "gpt2"   # "gpt2", or "llama": RMSNorm, no biases, SwiGLU MLP, rotary positions
+
+
+def llama_hidden(C: int) -> int:
+    """SwiGLU width of the Llama-style block: 8C/3 rounded up to a multiple of 64."""
+    return 64 * ((C + 23) // 24)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -73,6 +79,8 @@ GPT2_TINY_CHAR = ModelShape(32, 65, 2, 4, 64)
 GPT2_124M = ModelShape(1024, 50257, 12, 12, 768)
 GPT2_350M = ModelShape(1024, 50257, 24, 16, 1024)
 GPT2_1558M = ModelShape(1024, 50257, 48, 25, 1600)
+# a Llama-style model of GPT-2 124M's size (C 768, 12 layers, 12 heads, SwiGLU width 2048)
+LLAMA_124M = ModelShape(1024, 50257, 12, 12, 768, "llama")
 
 WORKLOADS = {
     "tiny_char_b4t32_fp32": Workload("tiny_char_b4t32_fp32", GPT2_TINY_CHAR, 4, 32, "fp32", "uniform", index=0),
@@ -80,6 +88,7 @@ WORKLOADS = {
     "gpt2_124m_b8t1024_bf16": Workload("gpt2_124m_b8t1024_bf16", GPT2_124M, 8, 1024, "bf16", "uniform", index=2),
     "gpt2_350m_b8t1024_bf16_zipf": Workload("gpt2_350m_b8t1024_bf16_zipf", GPT2_350M, 8, 1024, "bf16", "zipf", index=3),
     "gpt2_1558m_b4t1024_bf16": Workload("gpt2_1558m_b4t1024_bf16", GPT2_1558M, 4, 1024, "bf16", "uniform", index=4),
+    "llama_124m_b8t1024_bf16": Workload("llama_124m_b8t1024_bf16", LLAMA_124M, 8, 1024, "bf16", "uniform", index=5),
 }
 
 
@@ -122,6 +131,20 @@ def param_tensors(m: ModelShape):
     std_res = 0.02 / math.sqrt(2 * L)
     out = [("wte", m.vocab_size * C, ("normal", std)),
            ("wpe", m.max_seq_len * C, ("normal", std))]
+    if m.block == "llama":
+        # RMSNorm gains, no biases; gate|up interleaved by row (2j gate, 2j+1 up); wpe unused
+        H = llama_hidden(C)
+        for l in range(L):
+            out += [
+                (f"h{l}.rms1.w", C, ("const", 1.0)),
+                (f"h{l}.qkv.w", 3 * C * C, ("normal", std)),
+                (f"h{l}.proj.w", C * C, ("normal", std_res)),
+                (f"h{l}.rms2.w", C, ("const", 1.0)),
+                (f"h{l}.gateup.w", 2 * H * C, ("normal", std)),
+                (f"h{l}.down.w", C * H, ("normal", std_res)),
+            ]
+        out += [("rmsf.w", C, ("const", 1.0))]
+        return out
     for l in range(L):
         out += [
             (f"h{l}.ln1.w", C, ("const", 1.0)),
