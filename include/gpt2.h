@@ -301,7 +301,30 @@ int gpt2_checkpoint_write(const char* path, const gpt2_config* cfg, int32_t step
 int gpt2_checkpoint_read(const char* path, const gpt2_config* cfg, int32_t* step, float* params, float* m, float* v,
                          int32_t* has_moments);
 
-/* Position encoding of an arena's model.
+/* Block types.
+ *  GPT2_BLOCK_GPT2:  the GPT-2 block described at the top of this file.
+ *  GPT2_BLOCK_LLAMA: a Llama-style block ("1000 行 C 代码完成 GPT-2 训练的 LLM.c" lists
+ *    RoPE and the layers of Llama-2-type models as the next additions):
+ *    x = x + attn(rms_1(x)), x = x + down(silu(g) * u) with (g | u) = rms_2(x) W_gu^T;
+ *    RMSNorm y = x / sqrt(mean(x^2) + 1e-5) * w; no biases; the rotary position
+ *    embedding (base 10000 unless set otherwise) instead of wpe; a final RMSNorm and
+ *    the tied lm_head.  The MLP width is H = 8C/3 rounded up to a multiple of 64.
+ *    Parameters, layer-major: wte, wpe (kept, unused, zero gradient), per layer
+ *    [rms_1 w (C); qkv W (3C x C); proj W (C x C); rms_2 w (C); gate|up W (2H x C, row
+ *    2j the gate of hidden unit j, row 2j+1 its up); down W (C x H)], final rms w (C).
+ *    Not available with it: MX products and generation (GPT2_E_INVAL); checkpoint files
+ *    describe GPT-2 arenas. */
+enum gpt2_block { GPT2_BLOCK_GPT2 = 0, GPT2_BLOCK_LLAMA = 1 };
+
+/* Parameter count of a block type (-1 for a NULL cfg or unknown block). */
+int64_t gpt2_num_parameters_block(const gpt2_config* cfg, int32_t block);
+
+/* gpt2_alloc_arena with a block type; GPT2_BLOCK_GPT2 is gpt2_alloc_arena itself.
+ * Errors as gpt2_alloc_arena, and GPT2_E_INVAL for an unknown block. */
+int gpt2_alloc_arena_block(const gpt2_config* cfg, int32_t block, int32_t B, int32_t T, int32_t dtype,
+                           void* device_base, size_t device_bytes, size_t* required_bytes, gpt2_arena** out);
+
+/* Position encoding of an arena's model (GPT2_BLOCK_LLAMA: always rotary).
  *  GPT2_POS_LEARNED: x = wte[token] + wpe[position] (GPT-2; the default).
  *  GPT2_POS_ROTARY:  rotary position embedding ("GPT-2 from scratch with torch", token
  *    and position embedding, names RoPE - Su et al. 2021 - as the newer alternative):

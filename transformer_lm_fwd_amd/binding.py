@@ -29,11 +29,13 @@ EXPORTS = ("gpt2_alloc_arena", "gpt2_free_arena", "gpt2_sync_weights", "gpt2_for
            "gpt2_profile_read", "gpt2_gen_alloc", "gpt2_gen_free", "gpt2_gen_length", "gpt2_gen_prefill",
            "gpt2_gen_decode", "gpt2_sample_topk", "gpt2_tokens_count", "gpt2_tokens_batch",
            "gpt2_params_permute", "gpt2_checkpoint_write", "gpt2_checkpoint_read", "gpt2_set_position_encoding",
+           "gpt2_num_parameters_block", "gpt2_alloc_arena_block",
            "gpt2_mx_attach",
            "gpt2_set_gemm_format", "gpt2_mx_buffer", "gpt2_mx_quantize", "gpt2_mx_gemm", "gpt2_last_error")
 GPT2_ORDER_NUMERIC, GPT2_ORDER_LEXICOGRAPHIC = 0, 1
 GPT2_GEMM_BF16, GPT2_GEMM_MXFP8 = 0, 1
 GPT2_POS_LEARNED, GPT2_POS_ROTARY = 0, 1
+GPT2_BLOCK_GPT2, GPT2_BLOCK_LLAMA = 0, 1
 GPT2_EPI_BIAS, GPT2_EPI_BIAS_RES, GPT2_EPI_BIAS_GELU = 0, 1, 2
 GPT2_MX_BUF_INPUT, GPT2_MX_BUF_GELU = 0, 1
 
@@ -94,6 +96,9 @@ def lib():
         L.gpt2_checkpoint_write.argtypes = [cp, cfgp, i32, vp, vp, vp]
         L.gpt2_checkpoint_read.argtypes = [cp, cfgp, ctypes.POINTER(i32), vp, vp, vp, ctypes.POINTER(i32)]
         L.gpt2_set_position_encoding.argtypes = [vp, i32, f32, vp]
+        L.gpt2_num_parameters_block.argtypes = [cfgp, i32]
+        L.gpt2_num_parameters_block.restype = i64
+        L.gpt2_alloc_arena_block.argtypes = [cfgp, i32, i32, i32, i32, vp, sz, ctypes.POINTER(sz), ctypes.POINTER(vp)]
         L.gpt2_mx_attach.argtypes = [vp, vp, sz, ctypes.POINTER(sz)]
         L.gpt2_set_gemm_format.argtypes = [vp, i32]
         L.gpt2_mx_buffer.argtypes = [vp, i32, ctypes.POINTER(sz), ctypes.POINTER(sz), ctypes.POINTER(i64),
@@ -101,7 +106,7 @@ def lib():
         L.gpt2_mx_quantize.argtypes = [vp, i64, i32, i32, vp, i64, vp, vp]
         L.gpt2_mx_gemm.argtypes = [vp, vp, i64, vp, vp, i64, vp, i64, i32, i32, i32, i32, vp, vp, vp, vp]
         for name in EXPORTS:
-            if name not in ("gpt2_num_parameters", "gpt2_last_error", "gpt2_tokens_count"):
+            if name not in ("gpt2_num_parameters", "gpt2_num_parameters_block", "gpt2_last_error", "gpt2_tokens_count"):
                 L[name].restype = ctypes.c_int
         _lib = L
     return _lib
@@ -116,13 +121,19 @@ def make_config(m) -> gpt2_config:
     return gpt2_config(m.max_seq_len, m.vocab_size, m.num_layers, m.num_heads, m.channels)
 
 
+def block_of(m) -> int:
+    """GPT2_BLOCK_* of a model shape (its `block` field: "gpt2" or "llama")."""
+    return {"gpt2": GPT2_BLOCK_GPT2, "llama": GPT2_BLOCK_LLAMA}[getattr(m, "block", "gpt2")]
+
+
 def num_parameters(m) -> int:
-    return int(lib().gpt2_num_parameters(ctypes.byref(make_config(m))))
+    return int(lib().gpt2_num_parameters_block(ctypes.byref(make_config(m)), block_of(m)))
 
 
 def arena_bytes(m, B: int, T: int, dtype: int) -> int:
     need = ctypes.c_size_t(0)
-    _check(lib().gpt2_alloc_arena(ctypes.byref(make_config(m)), B, T, dtype, None, 0, ctypes.byref(need), None))
+    _check(lib().gpt2_alloc_arena_block(ctypes.byref(make_config(m)), block_of(m), B, T, dtype, None, 0,
+                                        ctypes.byref(need), None))
     return int(need.value)
 
 
@@ -162,8 +173,9 @@ class Arena:
         pad = (-self.buf.data_ptr()) % 256
         self.base = self.buf[pad:pad + self.nbytes]
         h = ctypes.c_void_p()
-        _check(lib().gpt2_alloc_arena(ctypes.byref(make_config(m)), B, T, self.dtype,
-                                      ctypes.c_void_p(self.base.data_ptr()), self.nbytes, None, ctypes.byref(h)))
+        _check(lib().gpt2_alloc_arena_block(ctypes.byref(make_config(m)), block_of(m), B, T, self.dtype,
+                                            ctypes.c_void_p(self.base.data_ptr()), self.nbytes, None,
+                                            ctypes.byref(h)))
         self.h = h
         self.n_params = num_parameters(m)
         self._inputs = None
@@ -256,6 +268,8 @@ class Arena:
     def save_checkpoint(self, path: str, step: int, moments: bool = True) -> None:
         """Master weights (and the AdamW moments) to a checkpoint file (gpt2_checkpoint_write)."""
         import numpy as np
+        if block_of(self.m) != GPT2_BLOCK_GPT2:
+            raise ValueError("checkpoint files describe GPT-2 arenas")
         p = self.tensor(T_PARAMS).cpu().numpy().reshape(-1)
         m = self.tensor(T_ADAM_M).cpu().numpy().reshape(-1) if moments else None
         v = self.tensor(T_ADAM_V).cpu().numpy().reshape(-1) if moments else None
@@ -268,6 +282,8 @@ class Arena:
         refreshes the bf16 copy, and returns the file's AdamW step."""
         import numpy as np
         import torch
+        if block_of(self.m) != GPT2_BLOCK_GPT2:
+            raise ValueError("checkpoint files describe GPT-2 arenas")
         n = self.n_params
         p, m, v = (np.empty(n, np.float32) for _ in range(3))
         step, has = ctypes.c_int32(0), ctypes.c_int32(0)

@@ -41,6 +41,11 @@ struct LayerActs {
 struct gpt2_arena {
     gpt2_config cfg;
     int B, T, dtype, Vp, hs;
+    // block type: GPT2_BLOCK_GPT2, or GPT2_BLOCK_LLAMA (RMSNorm, no biases, SwiGLU MLP of
+    // width H, rotary positions); F1 / F2: widths of the MLP's first product / activation
+    int block = GPT2_BLOCK_GPT2;
+    int64_t H = 0, F1 = 0, F2 = 0;
+    bool rope_ready = false;  // the rotary table has been built
     int64_t nparams;
     char* base;
     size_t bytes;
@@ -52,7 +57,7 @@ struct gpt2_arena {
     size_t params, grads, adam_m, adam_v, params16;
     size_t encoded, lnf, lnfs, logits, losses, loss;
     std::vector<LayerActs> la;
-    size_t dres[4], dbuf, dqkv[2], dfch[2], dsum, partial, partial_side, ws, ws_main, census;
+    size_t dres[4], dbuf, dqkv[2], dfch[2], dh, dsum, partial, partial_side, ws, ws_main, census;
     size_t partial_floats, ws_floats, ws_main_floats;
     bool loss_ready;
     bool census_armed = false;  // the token census holds its idle state (set by the first backward)
@@ -95,12 +100,21 @@ constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-int64_t count_params(const gpt2_config& c, int64_t* o_layer, int64_t* o_wte, int64_t* o_wpe, int64_t* o_lnf) {
+// SwiGLU width of the Llama-style block: 8C/3 rounded up to a multiple of 64.
+int64_t llama_hidden(int64_t C) { return 64 * ((C + 23) / 24); }
+
+int64_t count_params(const gpt2_config& c, int64_t* o_layer, int64_t* o_wte, int64_t* o_wpe, int64_t* o_lnf,
+                     int block = GPT2_BLOCK_GPT2) {
     // Layer-major order of the module tree (GPT-2 from scratch with torch, 总体架构):
     // wte, wpe, per block [ln_1 w,b; c_attn W,b; attn c_proj W,b; ln_2 w,b; c_fc W,b;
-    // mlp c_proj W,b], ln_f w,b.  Weights are (out, in) row-major.
-    const int64_t C = c.channels;
-    const int64_t sz[P_N] = {C, C, 3 * C * C, 3 * C, C * C, C, C, C, 4 * C * C, 4 * C, 4 * C * C, C};
+    // mlp c_proj W,b], ln_f w,b.  Weights are (out, in) row-major.  The Llama-style
+    // block keeps the slots with the biases and shifts empty: [rms_1 w; qkv W; proj W;
+    // rms_2 w; gate|up W (2H x C, gate and up rows interleaved); down W (C x H)], then
+    // the final RMSNorm's w.
+    const int64_t C = c.channels, H = llama_hidden(C);
+    const int64_t gsz[P_N] = {C, C, 3 * C * C, 3 * C, C * C, C, C, C, 4 * C * C, 4 * C, 4 * C * C, C};
+    const int64_t lsz[P_N] = {C, 0, 3 * C * C, 0, C * C, 0, C, 0, 2 * H * C, 0, C * H, 0};
+    const int64_t* sz = block == GPT2_BLOCK_LLAMA ? lsz : gsz;
     int64_t o = 0;
     if (o_wte) *o_wte = o;
     o += (int64_t)c.vocab_size * C;
@@ -112,7 +126,7 @@ int64_t count_params(const gpt2_config& c, int64_t* o_layer, int64_t* o_wte, int
             o += sz[i];
         }
     if (o_lnf) *o_lnf = o;
-    return o + 2 * C;
+    return o + (block == GPT2_BLOCK_LLAMA ? 1 : 2) * C;
 }
 
 int validate(const gpt2_config* cfg, int B, int T, int dtype) {
@@ -165,8 +179,8 @@ size_t layout(gpt2_arena& a) {
         x.res2 = take(BT * C * es);
         x.ln2 = take(BT * C * es);
         x.ln2s = take(BT * 2 * 4);
-        x.fch = take(BT * 4 * C * es);
-        x.fchg = take(BT * 4 * C * es);
+        x.fch = take(BT * a.F1 * es);
+        x.fchg = take(BT * a.F2 * es);
         x.res3 = take(BT * C * es);
     }
     a.lnf = take(BT * C * es);
@@ -179,12 +193,13 @@ size_t layout(gpt2_arena& a) {
     for (int i = 0; i < 4; ++i) a.dres[i] = take(BT * C * es);
     a.dbuf = take(BT * C * es);
     for (int i = 0; i < 2; ++i) a.dqkv[i] = take(BT * 3 * C * es);
-    for (int i = 0; i < 2; ++i) a.dfch[i] = take(BT * 4 * C * es);
+    for (int i = 0; i < 2; ++i) a.dfch[i] = take(BT * a.F1 * es);
+    a.dh = a.block == GPT2_BLOCK_LLAMA ? take(BT * a.H * es) : 0;  // SwiGLU output gradient
     a.dsum = take(BT * NH * 8);  // per (row, head): {lse log2 e, D} for the head-size-64 kernels
     a.partial_floats = (size_t)512 * 2 * 4 * C;  // column-sum partials (<= 256 blocks x 4C)
     a.partial = take(a.partial_floats * 4);
     a.partial_side = take(a.partial_floats * 4);
-    a.ws_floats = (size_t)16 * 4 * C * C;  // split-K partials of the largest block dW (4C x C), 16 splits
+    a.ws_floats = (size_t)16 * std::max<int64_t>(4 * C, 2 * a.H) * C;  // split-K partials of the largest dW, 16 splits
     a.ws = take(a.ws_floats * 4);
     // main stream's split-K partials: the tied-embedding dX ([B*T, C], K = vocab) in up to 4 splits
     a.ws_main_floats = (size_t)4 * BT * C;
@@ -340,7 +355,12 @@ struct Model {
 
     uint8_t* mxp(size_t off) const { return (uint8_t*)(a->mx + off); }
     bool rotary() const { return a->pos_enc == GPT2_POS_ROTARY; }
+    bool llama() const { return a->block == GPT2_BLOCK_LLAMA; }
+    // a bias / shift parameter of the block, or null for the Llama-style block (none)
+    const float* pb(int64_t off) const { return llama() ? nullptr : master(off); }
+    float* gb(int64_t off) const { return llama() ? nullptr : grad(off); }
     const float2* rope_tab() const { return at<float2>(a, a->rope); }
+    float2* rope_tab_mut() const { return at<float2>(a, a->rope); }
 
     // MX codes and scales of the forward weights from the bf16 copy.
     int mx_refresh() {
@@ -401,6 +421,10 @@ struct Model {
             int rc = mx_refresh();
             if (rc) return rc;
         }
+        if (rotary() && !a->rope_ready) {  // Llama-style arenas: the table with the default base
+            CHECK(rope_table(rope_tab_mut(), P, C / NH, 10000.0, s), "rope table");
+            a->rope_ready = true;
+        }
         CHECK(encoder_forward<T>(act(a->encoded), inp, master(a->o_wte), rotary() ? nullptr : master(a->o_wpe), BT, S,
                                  C, s),
               "encoder");
@@ -408,22 +432,35 @@ struct Model {
             const LayerActs& x = a->la[l];
             const T* xin = l == 0 ? act(a->encoded) : act(a->la[l - 1].res3);
             const MxBuf mi = mx_in(), mg = mx_gelu();
-            CHECK(layernorm_forward<T>(act(x.ln1), f32(x.ln1s), xin, master(lp(l, P_LN1W)), master(lp(l, P_LN1B)), BT,
-                                       C, s, mi.q, mi.ld, mi.s), "ln1");
+            CHECK(layernorm_forward<T>(act(x.ln1), f32(x.ln1s), xin, master(lp(l, P_LN1W)), pb(lp(l, P_LN1B)), BT, C,
+                                       s, mi.q, mi.ld, mi.s, llama()),
+                  "ln1");
             int rc;
             // qkv = ln1 W_qkv^T + b
             if ((rc = fwd_gemm(act(x.ln1), C, lp(l, P_QKVW), 4 * l, 3 * C, act(x.qkv), 3 * C, EPI_BIAS,
-                               master(lp(l, P_QKVB)), nullptr, nullptr, mi)))
+                               pb(lp(l, P_QKVB)), nullptr, nullptr, mi)))
                 return rc;
             if (rotary())  // turn q and k of every head for its position (in place)
                 CHECK(rope_apply<T>(act(x.qkv), 3 * C, BT, 2 * C, C / NH, S, 0, rope_tab(), false, s), "rope");
             CHECK(attention_forward<T>(act(x.atty), f32(x.lse), act(x.qkv), B, S, C, NH, s), "attention");
             // res2 = xin + atty W_proj^T + b
             if ((rc = fwd_gemm(act(x.atty), C, lp(l, P_PROJW), 4 * l + 1, C, act(x.res2), C, EPI_BIAS_RES,
-                               master(lp(l, P_PROJB)), xin)))
+                               pb(lp(l, P_PROJB)), xin)))
                 return rc;
             CHECK(layernorm_forward<T>(act(x.ln2), f32(x.ln2s), act(x.res2), master(lp(l, P_LN2W)),
-                                       master(lp(l, P_LN2B)), BT, C, s, mi.q, mi.ld, mi.s), "ln2");
+                                       pb(lp(l, P_LN2B)), BT, C, s, mi.q, mi.ld, mi.s, llama()),
+                  "ln2");
+            if (llama()) {
+                // (g | u) = ln2 W_gu^T (interleaved), h = silu(g) u, res3 = res2 + h W_down^T
+                const int H = (int)a->H;
+                if ((rc = fwd_gemm(act(x.ln2), C, lp(l, P_FCW), 4 * l + 2, 2 * H, act(x.fch), 2 * H, EPI_BIAS)))
+                    return rc;
+                CHECK(swiglu_forward<T>(act(x.fchg), act(x.fch), BT, H, s), "swiglu");
+                if ((rc = fwd_gemm(act(x.fchg), H, lp(l, P_FCPW), 4 * l + 3, C, act(x.res3), C, EPI_BIAS_RES, nullptr,
+                                   act(x.res2))))
+                    return rc;
+                continue;
+            }
             // fch = ln2 W_fc^T + b, fchg = gelu(fch)
             if ((rc = fwd_gemm(act(x.ln2), C, lp(l, P_FCW), 4 * l + 2, 4 * C, act(x.fch), 4 * C, EPI_BIAS_GELU,
                                master(lp(l, P_FCB)), nullptr, act(x.fchg), mi, mg)))
@@ -435,7 +472,8 @@ struct Model {
         }
         const MxBuf mi = mx_in();
         CHECK(layernorm_forward<T>(act(a->lnf), f32(a->lnfs), act(a->la[L - 1].res3), master(a->o_lnfw),
-                                   master(a->o_lnfb), BT, C, s, mi.q, mi.ld, mi.s), "lnf");
+                                   pb(a->o_lnfb), BT, C, s, mi.q, mi.ld, mi.s, llama()),
+              "lnf");
         // logits = lnf wte^T (tied lm_head, no bias); row stride Vp
         int rc;
         if ((rc = fwd_gemm(act(a->lnf), C, a->o_wte, 4 * L, V, act(a->logits), Vp, EPI_BIAS, nullptr, nullptr, nullptr,
@@ -513,9 +551,12 @@ struct Model {
         if ((rc = gemm_call(dz, Vp, true, weight(a->o_wte), C, false, dbuf, C, BT, C, V, EPI_BIAS))) return rc;
         int cur = 0;
         if ((rc = wait(M, a->rd_res[0]))) return rc;
-        CHECK(layernorm_backward<T>(act(a->dres[0]), (const T*)nullptr, grad(a->o_lnfw), grad(a->o_lnfb), dbuf,
+        CHECK(layernorm_backward<T>(act(a->dres[0]), (const T*)nullptr, grad(a->o_lnfw), gb(a->o_lnfb), dbuf,
                                     act(a->la[L - 1].res3), f32(a->lnfs), master(a->o_lnfw), BT, C, part,
-                                    a->partial_floats, M), "lnf backward");
+                                    a->partial_floats, M, llama()),
+              "lnf backward");
+        const int64_t F1 = a->F1, F2 = a->F2;
+        auto bias_off = [&](int64_t off) -> int64_t { return llama() ? -1 : off; };
         for (int l = L - 1; l >= 0; --l) {
             const LayerActs& x = a->la[l];
             const T* xin = l == 0 ? act(a->encoded) : act(a->la[l - 1].res3);
@@ -527,26 +568,34 @@ struct Model {
             T* dqkv = act(a->dqkv[p]);
             // mlp c_proj: side: dW = din^T fchg, db = colsum(din); main: dfch = (din W_fcproj) * gelu'(fch)
             if ((rc = stream_wait(a, SD, M))) return rc;
-            if ((rc = side_dw(din, C, act(x.fchg), 4 * C, lp(l, P_FCPW), lp(l, P_FCPB)))) return rc;
+            if ((rc = side_dw(din, C, act(x.fchg), (int)F2, lp(l, P_FCPW), bias_off(lp(l, P_FCPB))))) return rc;
             if ((rc = mark(a->rd_res[i_in], SD))) return rc;
             if ((rc = wait(M, a->rd_fch[p]))) return rc;
-            if ((rc = gemm_call(din, C, true, weight(lp(l, P_FCPW)), 4 * C, false, dfch, 4 * C, BT, 4 * C, C,
-                                EPI_GELU_BWD, nullptr, act(x.fch))))
+            if (llama()) {  // dh = din W_down, then (dg | du) from silu(g) u
+                const int H = (int)a->H;
+                T* dh = act(a->dh);
+                if ((rc = gemm_call(din, C, true, weight(lp(l, P_FCPW)), H, false, dh, H, BT, H, C, EPI_BIAS)))
+                    return rc;
+                CHECK(swiglu_backward<T>(dfch, dh, act(x.fch), BT, H, M), "swiglu backward");
+            } else if ((rc = gemm_call(din, C, true, weight(lp(l, P_FCPW)), 4 * C, false, dfch, 4 * C, BT, 4 * C, C,
+                                       EPI_GELU_BWD, nullptr, act(x.fch)))) {
                 return rc;
+            }
             // c_fc: side: dW = dfch^T ln2, db = colsum(dfch); main: dln2 = dfch W_fc
             if ((rc = stream_wait(a, SD, M))) return rc;
-            if ((rc = side_dw(dfch, 4 * C, act(x.ln2), C, lp(l, P_FCW), lp(l, P_FCB)))) return rc;
+            if ((rc = side_dw(dfch, (int)F1, act(x.ln2), C, lp(l, P_FCW), bias_off(lp(l, P_FCB))))) return rc;
             if ((rc = mark(a->rd_fch[p], SD))) return rc;
-            if ((rc = gemm_call(dfch, 4 * C, true, weight(lp(l, P_FCW)), C, false, dbuf, C, BT, C, 4 * C, EPI_BIAS)))
+            if ((rc = gemm_call(dfch, F1, true, weight(lp(l, P_FCW)), C, false, dbuf, C, BT, C, (int)F1, EPI_BIAS)))
                 return rc;
             // ln_2: dmid = din + LN backward
             if ((rc = wait(M, a->rd_res[i_mid]))) return rc;
-            CHECK(layernorm_backward<T>(dmid, din, grad(lp(l, P_LN2W)), grad(lp(l, P_LN2B)), dbuf, act(x.res2),
-                                        f32(x.ln2s), master(lp(l, P_LN2W)), BT, C, part, a->partial_floats, M),
+            CHECK(layernorm_backward<T>(dmid, din, grad(lp(l, P_LN2W)), gb(lp(l, P_LN2B)), dbuf, act(x.res2),
+                                        f32(x.ln2s), master(lp(l, P_LN2W)), BT, C, part, a->partial_floats, M,
+                                        llama()),
                   "ln2 backward");
             // attn c_proj: side: dW = dmid^T atty, db; main: datty = dmid W_proj
             if ((rc = stream_wait(a, SD, M))) return rc;
-            if ((rc = side_dw(dmid, C, act(x.atty), C, lp(l, P_PROJW), lp(l, P_PROJB)))) return rc;
+            if ((rc = side_dw(dmid, C, act(x.atty), C, lp(l, P_PROJW), bias_off(lp(l, P_PROJB))))) return rc;
             if ((rc = mark(a->rd_res[i_mid], SD))) return rc;
             if ((rc = gemm_call(dmid, C, true, weight(lp(l, P_PROJW)), C, false, dbuf, C, BT, C, C, EPI_BIAS)))
                 return rc;
@@ -558,14 +607,14 @@ struct Model {
                 CHECK(rope_apply<T>(dqkv, 3 * C, BT, 2 * C, C / NH, S, 0, rope_tab(), true, M), "rope backward");
             // c_attn: side: dW = dqkv^T ln1, db; main: dln1 = dqkv W_qkv
             if ((rc = stream_wait(a, SD, M))) return rc;
-            if ((rc = side_dw(dqkv, 3 * C, act(x.ln1), C, lp(l, P_QKVW), lp(l, P_QKVB)))) return rc;
+            if ((rc = side_dw(dqkv, 3 * C, act(x.ln1), C, lp(l, P_QKVW), bias_off(lp(l, P_QKVB))))) return rc;
             if ((rc = mark(a->rd_qkv[p], SD))) return rc;
             if ((rc = gemm_call(dqkv, 3 * C, true, weight(lp(l, P_QKVW)), C, false, dbuf, C, BT, C, 3 * C, EPI_BIAS)))
                 return rc;
             // ln_1: dout = dmid + LN backward (= d xin)
             if ((rc = wait(M, a->rd_res[i_out]))) return rc;
-            CHECK(layernorm_backward<T>(dout, dmid, grad(lp(l, P_LN1W)), grad(lp(l, P_LN1B)), dbuf, xin, f32(x.ln1s),
-                                        master(lp(l, P_LN1W)), BT, C, part, a->partial_floats, M),
+            CHECK(layernorm_backward<T>(dout, dmid, grad(lp(l, P_LN1W)), gb(lp(l, P_LN1B)), dbuf, xin, f32(x.ln1s),
+                                        master(lp(l, P_LN1W)), BT, C, part, a->partial_floats, M, llama()),
                   "ln1 backward");
             cur = i_out;
             if (opt) {  // layer l's gradients are complete and its weights no longer read
@@ -601,11 +650,22 @@ int64_t gpt2_num_parameters(const gpt2_config* cfg) {
     return count_params(*cfg, nullptr, nullptr, nullptr, nullptr);
 }
 
+int64_t gpt2_num_parameters_block(const gpt2_config* cfg, int32_t block) {
+    if (!cfg || (block != GPT2_BLOCK_GPT2 && block != GPT2_BLOCK_LLAMA)) return -1;
+    return count_params(*cfg, nullptr, nullptr, nullptr, nullptr, block);
+}
+
 int gpt2_alloc_arena(const gpt2_config* cfg, int32_t B, int32_t T, int32_t dtype, void* device_base,
                      size_t device_bytes, size_t* required_bytes, gpt2_arena** out) {
+    return gpt2_alloc_arena_block(cfg, GPT2_BLOCK_GPT2, B, T, dtype, device_base, device_bytes, required_bytes, out);
+}
+
+int gpt2_alloc_arena_block(const gpt2_config* cfg, int32_t block, int32_t B, int32_t T, int32_t dtype,
+                           void* device_base, size_t device_bytes, size_t* required_bytes, gpt2_arena** out) {
     if (out) *out = nullptr;
     int rc = validate(cfg, B, T, dtype);
     if (rc) return rc;
+    if (block != GPT2_BLOCK_GPT2 && block != GPT2_BLOCK_LLAMA) return fail(GPT2_E_INVAL, "unknown block type");
     gpt2_arena* a = new (std::nothrow) gpt2_arena();
     if (!a) return fail(GPT2_E_INVAL, "host allocation failed");
     a->cfg = *cfg;
@@ -615,11 +675,16 @@ int gpt2_alloc_arena(const gpt2_config* cfg, int32_t B, int32_t T, int32_t dtype
     a->Vp = (cfg->vocab_size + 63) / 64 * 64;
     a->hs = cfg->channels / cfg->num_heads;
     a->act_size = dtype == GPT2_BF16 ? 2 : 4;
+    a->block = block;
+    a->H = llama_hidden(cfg->channels);
+    a->F1 = block == GPT2_BLOCK_LLAMA ? 2 * a->H : 4 * (int64_t)cfg->channels;
+    a->F2 = block == GPT2_BLOCK_LLAMA ? a->H : 4 * (int64_t)cfg->channels;
+    if (block == GPT2_BLOCK_LLAMA) a->pos_enc = GPT2_POS_ROTARY;  // table built by the first forward pass
     a->o_layer.resize((size_t)cfg->num_layers * P_N);
     int64_t o_lnf = 0;
-    a->nparams = count_params(*cfg, a->o_layer.data(), &a->o_wte, &a->o_wpe, &o_lnf);
+    a->nparams = count_params(*cfg, a->o_layer.data(), &a->o_wte, &a->o_wpe, &o_lnf, block);
     a->o_lnfw = o_lnf;
-    a->o_lnfb = o_lnf + cfg->channels;
+    a->o_lnfb = o_lnf + cfg->channels;  // (Llama-style: no final shift; unused)
     size_t need = layout(*a);
     if (required_bytes) *required_bytes = need;
     if (!device_base) {
@@ -702,6 +767,7 @@ int gpt2_backward_adamw(gpt2_arena* a, float lr, float beta1, float beta2, float
 int gpt2_set_position_encoding(gpt2_arena* a, int32_t mode, float base, void* stream) {
     if (!a) return fail(GPT2_E_INVAL, "arena is NULL");
     if (mode == GPT2_POS_LEARNED) {
+        if (a->block == GPT2_BLOCK_LLAMA) return fail(GPT2_E_INVAL, "the Llama-style block uses rotary positions");
         a->pos_enc = mode;
         return GPT2_OK;
     }
@@ -711,11 +777,13 @@ int gpt2_set_position_encoding(gpt2_arena* a, int32_t mode, float base, void* st
                        "rope table");
     if (rc) return rc;
     a->pos_enc = mode;
+    a->rope_ready = true;
     return GPT2_OK;
 }
 
 int gpt2_mx_attach(gpt2_arena* a, void* device_base, size_t device_bytes, size_t* required_bytes) {
     if (!a) return fail(GPT2_E_INVAL, "arena is NULL");
+    if (a->block != GPT2_BLOCK_GPT2) return fail(GPT2_E_INVAL, "MX products are built for the GPT-2 block");
     if (a->dtype != GPT2_BF16) return fail(GPT2_E_INVAL, "MX FP8 products need a bf16 arena");
     const size_t need = mx_layout(*a);
     if (required_bytes) *required_bytes = need;
@@ -735,6 +803,7 @@ int gpt2_set_gemm_format(gpt2_arena* a, int32_t format) {
         return GPT2_OK;
     }
     if (format != GPT2_GEMM_MXFP8) return fail(GPT2_E_INVAL, "unknown GEMM format");
+    if (a->block != GPT2_BLOCK_GPT2) return fail(GPT2_E_INVAL, "MX products are built for the GPT-2 block");
     if (!a->mx) return fail(GPT2_E_STATE, "GPT2_GEMM_MXFP8 needs memory from gpt2_mx_attach");
     a->gemm_format = format;
     a->mx_stale = true;
@@ -833,8 +902,8 @@ int gpt2_tensor_info(const gpt2_arena* a, int32_t id, int32_t layer, size_t* byt
         case GPT2_T_RESIDUAL2: off = x->res2; r = BT; c = C; dt = act; break;
         case GPT2_T_LN2: off = x->ln2; r = BT; c = C; dt = act; break;
         case GPT2_T_LN2_STATS: off = x->ln2s; r = BT; c = 2; break;
-        case GPT2_T_FCH: off = x->fch; r = BT; c = 4 * C; dt = act; break;
-        case GPT2_T_FCH_GELU: off = x->fchg; r = BT; c = 4 * C; dt = act; break;
+        case GPT2_T_FCH: off = x->fch; r = BT; c = a->F1; dt = act; break;
+        case GPT2_T_FCH_GELU: off = x->fchg; r = BT; c = a->F2; dt = act; break;
         case GPT2_T_RESIDUAL3: off = x->res3; r = BT; c = C; dt = act; break;
         default: return fail(GPT2_E_INVAL, "unknown tensor id");
     }
@@ -853,6 +922,7 @@ int gpt2_gen_alloc(gpt2_arena* a, int32_t batch, int32_t max_len, void* device_b
     if (out) *out = nullptr;
     if (!a) return fail(GPT2_E_INVAL, "arena is NULL");
     if (a->dtype != GPT2_BF16) return fail(GPT2_E_INVAL, "generation needs a bf16 arena");
+    if (a->block != GPT2_BLOCK_GPT2) return fail(GPT2_E_INVAL, "generation is built for the GPT-2 block");
     if (a->hs != 64) return fail(GPT2_E_INVAL, "generation needs head size 64");
     if (batch < 1 || batch > 16) return fail(GPT2_E_INVAL, "batch must be in 1..16");
     if (max_len < 1 || max_len > a->cfg.max_seq_len) return fail(GPT2_E_INVAL, "max_len must be in 1..max_seq_len");

@@ -74,18 +74,20 @@ hipError_t encoder_forward(T* out, const int32_t* tok, const float* wte, const f
 template <class T>
 // bf16 only: mxq / mxs non-null also write the output's MX FP8 codes [N, Kp] (row
 // stride ldq bytes, Kp = C rounded up to 128) and scales [Kp / 128][N][4].
+// rms: RMSNorm (mean taken as 0, statistics (0, rstd)); b may be null.
 hipError_t layernorm_forward(T* out, float* stats, const T* inp, const float* w, const float* b, int N, int C,
-                             hipStream_t s, uint8_t* mxq = nullptr, int64_t ldq = 0, uint8_t* mxs = nullptr);
+                             hipStream_t s, uint8_t* mxq = nullptr, int64_t ldq = 0, uint8_t* mxs = nullptr,
+                             bool rms = false);
 // dres = dres_in + LN backward dx (dres_in may be null, or equal to dres); dw, db
 // (overwrite) from column sums through `partial`.
 template <class T>
 hipError_t layernorm_backward(T* dres, const T* dres_in, float* dw, float* db, const T* dout, const T* inp,
                               const float* stats, const float* w, int N, int C, float* partial, size_t partial_floats,
-                              hipStream_t s);
+                              hipStream_t s, bool rms = false);  // rms: RMSNorm, db may be null
 // The two halves of layernorm_backward, for callers that run them on different streams.
 template <class T>
 hipError_t layernorm_backward_dx(T* dres, const T* dres_in, const T* dout, const T* inp, const float* stats,
-                                 const float* w, int N, int C, hipStream_t s);
+                                 const float* w, int N, int C, hipStream_t s, bool rms = false);
 template <class T>
 hipError_t layernorm_param_grads(float* dw, float* db, const T* dout, const T* inp, const float* stats, int N, int C,
                                  float* partial, size_t partial_floats, hipStream_t s);
@@ -133,6 +135,14 @@ hipError_t rope_table(float2* tab, int P, int hs, double base, hipStream_t s);
 template <class T>
 hipError_t rope_apply(T* x, int64_t ld, int rows, int ncols, int hs, int period, int pos0, const float2* tab,
                       bool inverse, hipStream_t s);
+
+// SwiGLU MLP of the Llama-style block: gu [N, 2H] holds (gate, up) of hidden unit j in
+// columns 2j, 2j+1; forward h [N, H] = silu(g) * u; backward dgu = (dh u silu'(g),
+// dh silu(g)) (overwrites).  H % 8 == 0.
+template <class T>
+hipError_t swiglu_forward(T* h, const T* gu, int N, int H, hipStream_t s);
+template <class T>
+hipError_t swiglu_backward(T* dgu, const T* dh, const T* gu, int N, int H, hipStream_t s);
 
 hipError_t splitk_reduce_bf16(bf16* C, int64_t ldc, const float* ws, int splits, int M, int N, const float* bias,
                               hipStream_t s);

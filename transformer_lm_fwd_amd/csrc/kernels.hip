@@ -45,10 +45,13 @@ hipError_t encoder_forward(T* out, const int32_t* tok, const float* wte, const f
 // MXO: also writes the MX FP8 codes and block scales of the (bf16-rounded) output,
 // q [N, Kp] (row stride ldq bytes), sc [Kp / 128][N][4], for a following MX product;
 // lane l's 8 values are chunk 64 ch + l, so 4 lanes hold a 32-block and 16 a stage.
+// rms: RMSNorm (Llama-style block) - the mean is taken as 0 (the statistics hold
+// mean 0 and 1 / sqrt(mean(x^2) + eps)); b may be null (no shift).
 template <class T, int MAXCH, bool MXO = false>
 __global__ __launch_bounds__(256) void layernorm_forward_kernel(T* out, float* stats, const T* inp, const float* w,
                                                                 const float* b, int N, int C, uint8_t* q = nullptr,
-                                                                int64_t ldq = 0, uint8_t* sc = nullptr) {
+                                                                int64_t ldq = 0, uint8_t* sc = nullptr,
+                                                                bool rms = false) {
     constexpr int KV = Vec16<T>::N;
     const int lane = threadIdx.x & 63;
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -65,7 +68,7 @@ __global__ __launch_bounds__(256) void layernorm_forward_kernel(T* out, float* s
             for (int e = 0; e < KV; ++e) sum += v[ch][e];
         }
     }
-    const float mean = wave_sum(sum) / C;
+    const float mean = rms ? 0.f : wave_sum(sum) / C;
     float sq = 0.f;
 #pragma unroll
     for (int ch = 0; ch < MAXCH; ++ch) {
@@ -94,7 +97,7 @@ __global__ __launch_bounds__(256) void layernorm_forward_kernel(T* out, float* s
 #pragma unroll
                 for (int e = 0; e < KV; e += 4) {
                     *(float4*)&wv[e] = *(const float4*)(w + c + e);
-                    *(float4*)&bv[e] = *(const float4*)(b + c + e);
+                    *(float4*)&bv[e] = b ? *(const float4*)(b + c + e) : make_float4(0.f, 0.f, 0.f, 0.f);
                 }
 #pragma unroll
                 for (int e = 0; e < KV; ++e) o[e] = (v[ch][e] - mean) * rstd * wv[e] + bv[e];
@@ -122,7 +125,7 @@ __global__ __launch_bounds__(256) void layernorm_forward_kernel(T* out, float* s
 #pragma unroll
             for (int e = 0; e < KV; e += 4) {  // C % 8 == 0: 16-byte aligned fp32 gains and shifts
                 *(float4*)&wv[e] = *(const float4*)(w + c + e);
-                *(float4*)&bv[e] = *(const float4*)(b + c + e);
+                *(float4*)&bv[e] = b ? *(const float4*)(b + c + e) : make_float4(0.f, 0.f, 0.f, 0.f);
             }
 #pragma unroll
             for (int e = 0; e < KV; ++e) o[e] = (v[ch][e] - mean) * rstd * wv[e] + bv[e];
@@ -137,7 +140,7 @@ __global__ __launch_bounds__(256) void layernorm_forward_kernel(T* out, float* s
 
 template <class T>
 hipError_t layernorm_forward(T* out, float* stats, const T* inp, const float* w, const float* b, int N, int C,
-                             hipStream_t s, uint8_t* mxq, int64_t ldq, uint8_t* mxs) {
+                             hipStream_t s, uint8_t* mxq, int64_t ldq, uint8_t* mxs, bool rms) {
     constexpr int KV = Vec16<T>::N;
     int ch = cdiv(C, 64 * KV);
     dim3 grid(cdiv(N, 4)), block(256);
@@ -146,21 +149,21 @@ hipError_t layernorm_forward(T* out, float* stats, const T* inp, const float* w,
             if (!mxs || ldq < (C + 127) / 128 * 128 || ldq % 16) return hipErrorInvalidValue;
             ProfScope prof(s, "layernorm_fwd_mx", 0, (double)N * C * 2 * sizeof(T) + 8.0 * N + N * C * (1 + 1 / 32.));
             if (ch <= 1)
-                hipLaunchKernelGGL((layernorm_forward_kernel<T, 1, true>), grid, block, 0, s, out, stats, inp, w, b, N, C, mxq, ldq, mxs);
+                hipLaunchKernelGGL((layernorm_forward_kernel<T, 1, true>), grid, block, 0, s, out, stats, inp, w, b, N, C, mxq, ldq, mxs, rms);
             else if (ch <= 2)
-                hipLaunchKernelGGL((layernorm_forward_kernel<T, 2, true>), grid, block, 0, s, out, stats, inp, w, b, N, C, mxq, ldq, mxs);
+                hipLaunchKernelGGL((layernorm_forward_kernel<T, 2, true>), grid, block, 0, s, out, stats, inp, w, b, N, C, mxq, ldq, mxs, rms);
             else if (ch <= 4)
-                hipLaunchKernelGGL((layernorm_forward_kernel<T, 4, true>), grid, block, 0, s, out, stats, inp, w, b, N, C, mxq, ldq, mxs);
+                hipLaunchKernelGGL((layernorm_forward_kernel<T, 4, true>), grid, block, 0, s, out, stats, inp, w, b, N, C, mxq, ldq, mxs, rms);
             else return hipErrorInvalidValue;
             return hipGetLastError();
         }
     }
     if (mxq) return hipErrorInvalidValue;
     ProfScope prof(s, "layernorm_fwd", 0, (double)N * C * 2 * sizeof(T) + 8.0 * N);
-    if (ch <= 1) hipLaunchKernelGGL((layernorm_forward_kernel<T, 1>), grid, block, 0, s, out, stats, inp, w, b, N, C);
-    else if (ch <= 2) hipLaunchKernelGGL((layernorm_forward_kernel<T, 2>), grid, block, 0, s, out, stats, inp, w, b, N, C);
-    else if (ch <= 4) hipLaunchKernelGGL((layernorm_forward_kernel<T, 4>), grid, block, 0, s, out, stats, inp, w, b, N, C);
-    else if (ch <= 8) hipLaunchKernelGGL((layernorm_forward_kernel<T, 8>), grid, block, 0, s, out, stats, inp, w, b, N, C);
+    if (ch <= 1) hipLaunchKernelGGL((layernorm_forward_kernel<T, 1>), grid, block, 0, s, out, stats, inp, w, b, N, C, nullptr, 0, nullptr, rms);
+    else if (ch <= 2) hipLaunchKernelGGL((layernorm_forward_kernel<T, 2>), grid, block, 0, s, out, stats, inp, w, b, N, C, nullptr, 0, nullptr, rms);
+    else if (ch <= 4) hipLaunchKernelGGL((layernorm_forward_kernel<T, 4>), grid, block, 0, s, out, stats, inp, w, b, N, C, nullptr, 0, nullptr, rms);
+    else if (ch <= 8) hipLaunchKernelGGL((layernorm_forward_kernel<T, 8>), grid, block, 0, s, out, stats, inp, w, b, N, C, nullptr, 0, nullptr, rms);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }
@@ -170,10 +173,11 @@ hipError_t layernorm_forward(T* out, float* stats, const T* inp, const float* w,
 //   dx = rstd * (dxhat - mean_c(dxhat) - xhat * mean_c(dxhat * xhat))   (written or added into dres)
 //   dw = sum_rows dy * xhat,  db = sum_rows dy                          (column sums, below)
 // dx: one wave per row, the row's dy and x held in registers.
+// rms: RMSNorm's backward - without the mean_c(dxhat) term (the statistics' mean is 0).
 template <class T, int MAXCH>
 __global__ __launch_bounds__(256) void layernorm_backward_dx_kernel(T* dres, const T* dres_in, const T* dout,
                                                                     const T* inp, const float* stats, const float* w,
-                                                                    int N, int C) {
+                                                                    int N, int C, bool rms) {
     constexpr int KV = Vec16<T>::N;
     const int lane = threadIdx.x & 63;
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -208,7 +212,7 @@ __global__ __launch_bounds__(256) void layernorm_backward_dx_kernel(T* dres, con
             }
         }
     }
-    s1 = wave_sum(s1) / C;
+    s1 = rms ? 0.f : wave_sum(s1) / C;
     s2 = wave_sum(s2) / C;
     T* dx = dres + (int64_t)row * C;
 #pragma unroll
@@ -297,7 +301,7 @@ __global__ __launch_bounds__(256) void colsum_stage2_kernel(float* out0, float* 
 #pragma unroll
         for (int k = 0; k < 16; ++k) v += red[k][cl];
         if (c < split) out0[c] = v;
-        else out1[c - split] = v;
+        else if (out1) out1[c - split] = v;  // null: no shift parameter (RMSNorm)
     }
 }
 
@@ -328,15 +332,15 @@ static hipError_t colsum(float* out0, float* out1, const T* dy, const T* x, cons
 
 template <class T>
 hipError_t layernorm_backward_dx(T* dres, const T* dres_in, const T* dout, const T* inp, const float* stats,
-                                 const float* w, int N, int C, hipStream_t s) {
+                                 const float* w, int N, int C, hipStream_t s, bool rms) {
     constexpr int KV = Vec16<T>::N;
     const int ch = cdiv(C, 64 * KV);
     const dim3 grid(cdiv(N, 4)), block(256);
     ProfScope prof(s, "layernorm_bwd_dx", 0, (double)N * C * sizeof(T) * (dres_in ? 4 : 3) + 8.0 * N);
-    if (ch <= 1) hipLaunchKernelGGL((layernorm_backward_dx_kernel<T, 1>), grid, block, 0, s, dres, dres_in, dout, inp, stats, w, N, C);
-    else if (ch <= 2) hipLaunchKernelGGL((layernorm_backward_dx_kernel<T, 2>), grid, block, 0, s, dres, dres_in, dout, inp, stats, w, N, C);
-    else if (ch <= 4) hipLaunchKernelGGL((layernorm_backward_dx_kernel<T, 4>), grid, block, 0, s, dres, dres_in, dout, inp, stats, w, N, C);
-    else if (ch <= 8) hipLaunchKernelGGL((layernorm_backward_dx_kernel<T, 8>), grid, block, 0, s, dres, dres_in, dout, inp, stats, w, N, C);
+    if (ch <= 1) hipLaunchKernelGGL((layernorm_backward_dx_kernel<T, 1>), grid, block, 0, s, dres, dres_in, dout, inp, stats, w, N, C, rms);
+    else if (ch <= 2) hipLaunchKernelGGL((layernorm_backward_dx_kernel<T, 2>), grid, block, 0, s, dres, dres_in, dout, inp, stats, w, N, C, rms);
+    else if (ch <= 4) hipLaunchKernelGGL((layernorm_backward_dx_kernel<T, 4>), grid, block, 0, s, dres, dres_in, dout, inp, stats, w, N, C, rms);
+    else if (ch <= 8) hipLaunchKernelGGL((layernorm_backward_dx_kernel<T, 8>), grid, block, 0, s, dres, dres_in, dout, inp, stats, w, N, C, rms);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }
@@ -357,7 +361,7 @@ template <class T, int MAXCH, int RPW>
 __global__ __launch_bounds__(512) void layernorm_backward_fused_kernel(T* dres, float* partial, const T* dres_in,
                                                                        const T* dout, const T* inp,
                                                                        const float* stats, const float* w, int N,
-                                                                       int C) {
+                                                                       int C, bool rms) {
     constexpr int KV = Vec16<T>::N;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     float wv[MAXCH][KV], aw[MAXCH][KV], ab[MAXCH][KV];
@@ -413,7 +417,7 @@ __global__ __launch_bounds__(512) void layernorm_backward_fused_kernel(T* dres, 
                 s1 += g[ch][e];
                 s2 += g[ch][e] * xh[ch][e];
             }
-        s1 = wave_sum(s1) / C;
+        s1 = rms ? 0.f : wave_sum(s1) / C;
         s2 = wave_sum(s2) / C;
         T* dx = dres + (int64_t)row * C;
 #pragma unroll
@@ -447,7 +451,7 @@ __global__ __launch_bounds__(512) void layernorm_backward_fused_kernel(T* dres, 
 template <class T>
 hipError_t layernorm_backward(T* dres, const T* dres_in, float* dw, float* db, const T* dout, const T* inp,
                               const float* stats, const float* w, int N, int C, float* partial, size_t partial_floats,
-                              hipStream_t s) {
+                              hipStream_t s, bool rms) {
     constexpr int KV = Vec16<T>::N;
     const int ch = cdiv(C, 64 * KV);
     // rows per wave: about 256 blocks for the step's 8192 rows, fewer rows for small inputs
@@ -456,7 +460,7 @@ hipError_t layernorm_backward(T* dres, const T* dres_in, float* dw, float* db, c
     while ((size_t)cdiv(N, 8 * rpw) * 2 * C > partial_floats && rpw < 64) rpw *= 2;
     const int nb = cdiv(N, 8 * rpw);
     if ((size_t)nb * 2 * C > partial_floats || ch > 2 || (rpw != 1 && rpw != 2 && rpw != 4)) {
-        hipError_t e = layernorm_backward_dx<T>(dres, dres_in, dout, inp, stats, w, N, C, s);
+        hipError_t e = layernorm_backward_dx<T>(dres, dres_in, dout, inp, stats, w, N, C, s, rms);
         if (e != hipSuccess) return e;
         return layernorm_param_grads<T>(dw, db, dout, inp, stats, N, C, partial, partial_floats, s);
     }
@@ -464,7 +468,7 @@ hipError_t layernorm_backward(T* dres, const T* dres_in, float* dw, float* db, c
         ProfScope prof(s, "layernorm_bwd", 0, (double)N * C * sizeof(T) * (dres_in ? 4 : 3) + 8.0 * N + 8.0 * nb * C);
 #define LNB_LAUNCH(MC, R)                                                                                             \
     hipLaunchKernelGGL((layernorm_backward_fused_kernel<T, MC, R>), dim3(nb), dim3(512), 0, s, dres, partial, dres_in, \
-                       dout, inp, stats, w, N, C)
+                       dout, inp, stats, w, N, C, rms)
 #define LNB_RPW(MC)                            \
     if (rpw == 1) LNB_LAUNCH(MC, 1);           \
     else if (rpw == 2) LNB_LAUNCH(MC, 2);      \
@@ -864,11 +868,11 @@ hipError_t splitk_reduce_bf16(bf16* C, int64_t ldc, const float* ws, int splits,
     template hipError_t encoder_forward<T>(T*, const int32_t*, const float*, const float*, int, int, int,        \
                                            hipStream_t, int);                                                     \
     template hipError_t layernorm_forward<T>(T*, float*, const T*, const float*, const float*, int, int,         \
-                                             hipStream_t, uint8_t*, int64_t, uint8_t*);                          \
+                                             hipStream_t, uint8_t*, int64_t, uint8_t*, bool);                    \
     template hipError_t layernorm_backward<T>(T*, const T*, float*, float*, const T*, const T*, const float*,   \
-                                              const float*, int, int, float*, size_t, hipStream_t);              \
+                                              const float*, int, int, float*, size_t, hipStream_t, bool);              \
     template hipError_t layernorm_backward_dx<T>(T*, const T*, const T*, const T*, const float*, const float*,   \
-                                                 int, int, hipStream_t);                                         \
+                                                 int, int, hipStream_t, bool);                                   \
     template hipError_t layernorm_param_grads<T>(float*, float*, const T*, const T*, const float*, int, int,     \
                                                  float*, size_t, hipStream_t);                                    \
     template hipError_t bias_grad<T>(float*, const T*, int, int, int64_t, float*, size_t, hipStream_t);          \
