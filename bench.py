@@ -224,10 +224,10 @@ def main():
         roof.update(measured_traffic(w.name + ("_rotary" if args.rotary else ""), dom["name"]))
 
     rope = None
-    if args.rotary:  # the rotary turns: elementwise, HBM-bound (q | k columns read and written in place)
+    if args.rotary or getattr(m, "block", "gpt2") == "llama":  # the rotary turns and SwiGLU: elementwise, HBM-bound
         rope = {}
         for s in stats:
-            if s["name"] in ("rope_fwd", "rope_bwd"):
+            if s["name"] in ("rope_fwd", "rope_bwd", "swiglu_fwd", "swiglu_bwd"):
                 avg_s = s["total_ms"] / s["launches"] / 1e3
                 gbs = s["bytes"] / s["launches"] / avg_s / 1e9
                 rope[s["name"]] = {"avg_launch_us": round(avg_s * 1e6, 2), "bytes_per_launch": round(s["bytes"] / s["launches"]),
@@ -237,13 +237,15 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline ...")
-        cpu = cpu_baseline(w, params, x, y, rotary=args.rotary)
+        cpu = cpu_baseline(w, params, x, y, rotary=args.rotary and getattr(m, "block", "gpt2") == "gpt2")
         log(f"[bench] CPU oracle: {cpu['value']:.1f} tokens/s on {cpu['cores']} threads")
 
     metric, wname = METRIC, w.name
     if args.rotary:
         metric = METRIC.replace("GPT-2 124M", "GPT-2 124M with rotary positions")
         wname = w.name + "_rotary"
+    if getattr(m, "block", "gpt2") == "llama":
+        metric = METRIC.replace("GPT-2 124M", "Llama-style 124M (RMSNorm, SwiGLU 2048, rotary)")
     out = {
         "metric": metric, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
@@ -255,7 +257,7 @@ def main():
         "loss": round(loss, 5), "roofline": roof, "cpu_baseline": cpu,
     }
     if rope is not None:
-        out["rope_kernels"] = rope
+        out["elementwise_kernels"] = rope
     print(json.dumps(out), flush=True)
 
 
