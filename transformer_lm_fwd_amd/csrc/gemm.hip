@@ -409,7 +409,9 @@ __device__ __forceinline__ bool tile_of_block(int bid, int tiles_m, int tiles_n,
 // two consecutive bf16 slices - and the scale of k-block g of its row (A) or column
 // (B), one byte of a 32-bit register picked by op_sel.  Each stage also holds the
 // scale words of its rows (1 KB for A, 1 KB for B), loaded by waves 0 and 1.
-template <bool AK, bool BKC, int EPI, int BM, int BN, int WM, int WN, int ST = 2, bool MX = false>
+// XTRA: the bias epilogue's options (GemmArgs rope / swiglu / swiglu_gu) are compiled in
+// only for the products that use them.
+template <bool AK, bool BKC, int EPI, int BM, int BN, int WM, int WN, int ST = 2, bool MX = false, bool XTRA = false>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a, int k_per_split, int64_t split_stride,
                                                                  uint32_t a_bytes, uint32_t b_bytes) {
     constexpr int NW = WM * WN, NT = 64 * NW;
@@ -703,6 +705,19 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a, int
             } else {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) v[e] += bv[e];
+                if constexpr (EPI == EPI_BIAS && XTRA) {
+                    if (a.rope && full && col < a.rope_cols) {  // col and rope_hs are multiples of 8
+                        const float2* tr =
+                            a.rope + (int64_t)(row % a.rope_period) * (a.rope_hs / 2) + (col % a.rope_hs) / 2;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const float2 cs = tr[j];
+                            const float x0 = v[2 * j], x1 = v[2 * j + 1];
+                            v[2 * j] = x0 * cs.x - x1 * cs.y;
+                            v[2 * j + 1] = x0 * cs.y + x1 * cs.x;
+                        }
+                    }
+                }
                 float rv[8];
                 if constexpr (NEED_R) {
                     if (full) unpack16<bf16>(rr[it], rv);
@@ -717,8 +732,41 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a, int
                     if constexpr (EPI == EPI_GELU_BWD) v[e] *= gelu_bwd(rv[e]);
                 }
                 bf16* C = (bf16*)a.C;
+                if constexpr (EPI == EPI_BIAS && XTRA) {
+                    if (a.swiglu_gu && full) {  // SwiGLU backward: 8 hidden units' dh -> 16 (dg, du)
+                        const int64_t o2 = (int64_t)row * 2 * a.ld_swiglu + 2 * col;
+                        float gu[16], d[16];
+                        unpack16<bf16>(ld16(a.swiglu_gu + o2), gu);
+                        unpack16<bf16>(ld16(a.swiglu_gu + o2 + 8), gu + 8);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const float g = gu[2 * e], u = gu[2 * e + 1], sg = 1.f / (1.f + __expf(-g));
+                            d[2 * e] = v[e] * u * sg * (1.f + g * (1.f - sg));
+                            d[2 * e + 1] = v[e] * g * sg;
+                        }
+                        st16(a.swiglu + o2, pack16<bf16>(d));
+                        st16(a.swiglu + o2 + 8, pack16<bf16>(d + 8));
+                        continue;
+                    }
+                }
                 if (full) {
                     st16(C + o, pack16<bf16>(v));
+                    if constexpr (EPI == EPI_BIAS && XTRA) {
+                        if (a.swiglu) {  // 4 (gate, up) pairs -> 4 hidden units
+                            float gu[8], h[8];
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) gu[e] = v[e];
+                            round_bf16_8(gu);
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) {
+                                const float g = gu[2 * j];
+                                h[j] = g / (1.f + __expf(-g)) * gu[2 * j + 1];
+                                h[4 + j] = 0.f;
+                            }
+                            const u32x4 pk = pack16<bf16>(h);
+                            *(uint2*)(a.swiglu + (int64_t)row * a.ld_swiglu + col / 2) = make_uint2(pk[0], pk[1]);
+                        }
+                    }
                     if constexpr (EPI == EPI_BIAS_GELU) {
                         st16((bf16*)a.C2 + o, pack16<bf16>(out2));
                         // MX codes of the stored GELU output: 4 consecutive threads hold a
@@ -780,6 +828,15 @@ static hipError_t launch(const GemmArgs& a, int splits, int k_per_split, int64_t
         // waves of 128 x 64 and two stages when there are at least three such tiles
         // per CU; otherwise 128 x 256 with waves of 64 x 64 and three stages.  Both
         // hold one block per CU (128 / 144 KB of LDS).
+        if constexpr (EPI == EPI_BIAS) {
+            if (a.rope || a.swiglu) {  // the extras' instance (128 x 256 tiles)
+                const int nt = ((a.N + 255) / 256) * ((a.M + 127) / 128);
+                dim3 grid((nt + 7) / 8 * 8, 1, splits);
+                hipLaunchKernelGGL((gemm_bf16_kernel<AK, BKC, EPI, 128, 256, 2, 4, 3, false, true>), grid, dim3(512), 0,
+                                   s, a, k_per_split, split_stride, (uint32_t)ab, (uint32_t)bb);
+                return hipGetLastError();
+            }
+        }
         if (splits == 1 && use_tile256(a.M, a.N, 1)) {
             const int nt = ((a.N + 255) / 256) * ((a.M + 255) / 256);
             dim3 grid((nt + 7) / 8 * 8, 1, splits);
@@ -813,6 +870,11 @@ template <class T>
 hipError_t gemm(const GemmArgs& a, bool ak, bool bk, int epi, float* ws, size_t ws_floats, hipStream_t s) {
     constexpr int BK = sizeof(T) == 2 ? 64 : 32;
     if (a.M <= 0 || a.N <= 0) return hipSuccess;
+    const bool extras = a.rope || a.swiglu;
+    // the forward extras need the (x, W^T) layout; the SwiGLU backward rides on dh = dY W
+    if (extras && (sizeof(T) != 2 || epi != EPI_BIAS || !ak || (bk && a.swiglu_gu) || (!bk && !a.swiglu_gu) ||
+                   a.N % 8))
+        return hipErrorInvalidValue;
     if constexpr (sizeof(T) == 2) {
         // 16-byte rows, and k-contiguous operands readable (zero-padded) up to a multiple of 64
         if (a.lda % 8 || a.ldb % 8 || a.ldc % 8) return hipErrorInvalidValue;
@@ -858,7 +920,7 @@ hipError_t gemm(const GemmArgs& a, bool ak, bool bk, int epi, float* ws, size_t 
         // tied-embedding dX): split K so the blocks fill whole waves of 256, then sum
         // the fp32 partials and add the bias in a fixed order.
         const int tiles = ((a.M + 127) / 128) * ((a.N + 255) / 256);
-        if (epi == EPI_BIAS && ws && tiles < 256 && a.K >= 4096 && a.N % 8 == 0) {
+        if (epi == EPI_BIAS && ws && !extras && tiles < 256 && a.K >= 4096 && a.N % 8 == 0) {
             auto eff = [&](int sp) { return (double)tiles * sp / (((tiles * sp + 255) / 256) * 256.0); };
             int best = 1;
             for (int sp = 2; sp <= 8; ++sp)
@@ -906,6 +968,13 @@ static hipError_t launch_mx(const GemmArgs& e, int K, uint32_t ab, uint32_t bb, 
     // The 256 x 256 tile does not fit: an MX operand fragment is twice a bf16 one, and
     // its 128 x 64 wave tiles would spill.
     const int nt = ((e.N + 255) / 256) * ((e.M + 127) / 128);
+    if constexpr (EPI == EPI_BIAS) {
+        if (e.rope || e.swiglu) {
+            hipLaunchKernelGGL((gemm_bf16_kernel<true, true, EPI, 128, 256, 2, 4, 3, true, true>),
+                               dim3((nt + 7) / 8 * 8), dim3(512), 0, s, e, e.K, (int64_t)0, ab, bb);
+            return hipGetLastError();
+        }
+    }
     hipLaunchKernelGGL((gemm_bf16_kernel<true, true, EPI, 128, 256, 2, 4, 3, true>), dim3((nt + 7) / 8 * 8),
                        dim3(512), 0, s, e, e.K, (int64_t)0, ab, bb);
     return hipGetLastError();

@@ -341,12 +341,27 @@ struct Model {
     T* act(size_t off) const { return at<T>(a, off); }
     float* f32(size_t off) const { return at<float>(a, off); }
 
+    // Options of the bf16 / MX products' bias epilogue: the rotary turn of the q|k
+    // columns and the SwiGLU output of a gate|up product (GemmArgs).
+    struct EpiExtra {
+        const float2* rope = nullptr;
+        int period = 0, hs = 0, cols = 0;
+        bf16* swiglu = nullptr;
+        int64_t ld_swiglu = 0;
+        const bf16* swiglu_gu = nullptr;  // backward: the saved (gate, up) pairs
+    };
+    static void apply_extra(GemmArgs& g, const EpiExtra& e) {
+        g.rope = e.rope; g.rope_period = e.period; g.rope_hs = e.hs; g.rope_cols = e.cols;
+        g.swiglu = e.swiglu; g.ld_swiglu = e.ld_swiglu; g.swiglu_gu = e.swiglu_gu;
+    }
+
     int gemm_call(const void* A, int64_t lda, bool ak, const void* Bm, int64_t ldb, bool bk, void* Cm, int64_t ldc,
                   int M, int N, int K, int epi, const float* bias = nullptr, const void* R = nullptr,
-                  void* C2 = nullptr) {
+                  void* C2 = nullptr, const EpiExtra& ex = EpiExtra{}) {
         GemmArgs g{};
         g.A = A; g.B = Bm; g.C = Cm; g.C2 = C2; g.R = R; g.bias = bias;
         g.M = M; g.N = N; g.K = K; g.lda = lda; g.ldb = ldb; g.ldc = ldc;
+        apply_extra(g, ex);
         // main-stream products use their own split-K workspace (the side stream's is busy
         // during backward)
         CHECK(gemm<T>(g, ak, bk, epi, f32(a->ws_main), a->ws_main_floats, s), "gemm");
@@ -396,7 +411,7 @@ struct Model {
     // into the matching buffer; `out2` asks the GELU epilogue for its output's codes.
     int fwd_gemm(const T* X, int K, int64_t w_off, int wi, int N, T* Y, int64_t ldc, int epi,
                  const float* bias = nullptr, const void* R = nullptr, void* C2 = nullptr, MxBuf in = {},
-                 MxBuf out2 = {}) {
+                 MxBuf out2 = {}, const EpiExtra& ex = EpiExtra{}) {
         if constexpr (sizeof(T) == 2) {
             if (mx_on()) {
                 const int64_t Kp = round128(K);
@@ -409,11 +424,12 @@ struct Model {
                 g.M = BT; g.N = N; g.K = (int)Kp; g.lda = in.ld; g.ldb = Kp; g.ldc = ldc;
                 g.sa = in.s; g.sb = mxp(a->mxs[wi]); g.srows_a = BT; g.srows_b = N;
                 g.q2 = out2.q; g.s2 = out2.s; g.ldq2 = out2.ld;
+                apply_extra(g, ex);
                 CHECK(gemm_mx(g, epi, s), "mx gemm");
                 return GPT2_OK;
             }
         }
-        return gemm_call(X, K, true, weight(w_off), K, true, Y, ldc, BT, N, K, epi, bias, R, C2);
+        return gemm_call(X, K, true, weight(w_off), K, true, Y, ldc, BT, N, K, epi, bias, R, C2, ex);
     }
 
     int forward(const int32_t* inp, const int32_t* tgt) {
@@ -437,10 +453,14 @@ struct Model {
                   "ln1");
             int rc;
             // qkv = ln1 W_qkv^T + b
+            // with rotary positions the bf16 products turn q and k in their epilogue
+            const bool fuse_rope = rotary() && sizeof(T) == 2;
+            EpiExtra rx;
+            if (fuse_rope) rx.rope = rope_tab(), rx.period = S, rx.hs = C / NH, rx.cols = 2 * C;
             if ((rc = fwd_gemm(act(x.ln1), C, lp(l, P_QKVW), 4 * l, 3 * C, act(x.qkv), 3 * C, EPI_BIAS,
-                               pb(lp(l, P_QKVB)), nullptr, nullptr, mi)))
+                               pb(lp(l, P_QKVB)), nullptr, nullptr, mi, MxBuf{}, rx)))
                 return rc;
-            if (rotary())  // turn q and k of every head for its position (in place)
+            if (rotary() && !fuse_rope)  // turn q and k of every head for its position (in place)
                 CHECK(rope_apply<T>(act(x.qkv), 3 * C, BT, 2 * C, C / NH, S, 0, rope_tab(), false, s), "rope");
             CHECK(attention_forward<T>(act(x.atty), f32(x.lse), act(x.qkv), B, S, C, NH, s), "attention");
             // res2 = xin + atty W_proj^T + b
@@ -453,9 +473,12 @@ struct Model {
             if (llama()) {
                 // (g | u) = ln2 W_gu^T (interleaved), h = silu(g) u, res3 = res2 + h W_down^T
                 const int H = (int)a->H;
-                if ((rc = fwd_gemm(act(x.ln2), C, lp(l, P_FCW), 4 * l + 2, 2 * H, act(x.fch), 2 * H, EPI_BIAS)))
+                EpiExtra sx;  // bf16: the product's epilogue writes h itself
+                if (sizeof(T) == 2) sx.swiglu = (bf16*)act(x.fchg), sx.ld_swiglu = H;
+                if ((rc = fwd_gemm(act(x.ln2), C, lp(l, P_FCW), 4 * l + 2, 2 * H, act(x.fch), 2 * H, EPI_BIAS, nullptr,
+                                   nullptr, nullptr, MxBuf{}, MxBuf{}, sx)))
                     return rc;
-                CHECK(swiglu_forward<T>(act(x.fchg), act(x.fch), BT, H, s), "swiglu");
+                if (sizeof(T) != 2) CHECK(swiglu_forward<T>(act(x.fchg), act(x.fch), BT, H, s), "swiglu");
                 if ((rc = fwd_gemm(act(x.fchg), H, lp(l, P_FCPW), 4 * l + 3, C, act(x.res3), C, EPI_BIAS_RES, nullptr,
                                    act(x.res2))))
                     return rc;
@@ -574,9 +597,12 @@ struct Model {
             if (llama()) {  // dh = din W_down, then (dg | du) from silu(g) u
                 const int H = (int)a->H;
                 T* dh = act(a->dh);
-                if ((rc = gemm_call(din, C, true, weight(lp(l, P_FCPW)), H, false, dh, H, BT, H, C, EPI_BIAS)))
+                EpiExtra bx;  // bf16: the dX product's epilogue writes (dg | du) itself
+                if (sizeof(T) == 2) bx.swiglu = (bf16*)dfch, bx.ld_swiglu = H, bx.swiglu_gu = (const bf16*)act(x.fch);
+                if ((rc = gemm_call(din, C, true, weight(lp(l, P_FCPW)), H, false, dh, H, BT, H, C, EPI_BIAS, nullptr,
+                                    nullptr, nullptr, bx)))
                     return rc;
-                CHECK(swiglu_backward<T>(dfch, dh, act(x.fch), BT, H, M), "swiglu backward");
+                if (sizeof(T) != 2) CHECK(swiglu_backward<T>(dfch, dh, act(x.fch), BT, H, M), "swiglu backward");
             } else if ((rc = gemm_call(din, C, true, weight(lp(l, P_FCPW)), 4 * C, false, dfch, 4 * C, BT, 4 * C, C,
                                        EPI_GELU_BWD, nullptr, act(x.fch)))) {
                 return rc;

@@ -59,6 +59,19 @@ struct GemmArgs {
     uint8_t* q2;
     uint8_t* s2;
     int64_t ldq2;
+    // EPI_BIAS extras of the bf16 (and MX) products, each off when null:
+    //  rope: turn the pairs of columns < rope_cols (whole heads of rope_hs) of row m by
+    //        the (cos, sin) row of position m % rope_period (the rotary embedding);
+    //  swiglu: columns (2j, 2j+1) are (gate, up) of hidden unit j: also write
+    //        silu(gate) * up (from the bf16-rounded pair) to swiglu[m * ld_swiglu + j].
+    //  swiglu_gu (backward): the product is dh; instead of storing it, read the (gate, up)
+    //        pairs of hidden units j from swiglu_gu[m * 2 ld_swiglu + 2j, + 1] and write
+    //        (dh u silu'(g), dh silu(g)) to swiglu[m * 2 ld_swiglu + 2j, + 1].
+    const float2* rope;
+    int rope_period, rope_hs, rope_cols;
+    bf16* swiglu;
+    int64_t ld_swiglu;
+    const bf16* swiglu_gu;
 };
 
 // Returns hipSuccess or the launch error.  T in {float, bf16}: operand type;
