@@ -113,6 +113,8 @@ def main():
     ap.add_argument("--mxfp8", action="store_true",
                     help="time the forward pass (with the loss) with MX FP8 block and lm_head products beside the "
                          "bf16 forward (prints its own JSON line)")
+    ap.add_argument("--io", action="store_true",
+                    help="time the host I/O of a run: token-file batches, checkpoint write / read (own JSON line)")
     ap.add_argument("--decode-batch", type=int, default=8)
     ap.add_argument("--prompt", type=int, default=512)
     args = ap.parse_args()
@@ -143,6 +145,8 @@ def main():
         return decode_bench(args)
     if args.mxfp8:
         return mx_forward_bench(args)
+    if args.io:
+        return io_bench(args)
 
     w = synth.WORKLOADS[args.workload]
     m = w.model
@@ -370,6 +374,77 @@ def decode_bench(args):
         "config": {"workload": name, "batch": batch, "prompt": n, "layers": m.num_layers, "heads": m.num_heads,
                    "channels": m.channels, "vocab": m.vocab_size},
         "roofline": roof, "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def io_bench(args):
+    """Host I/O around the step for the workload's model: batches of B x (T + 1) ids read
+    from an int32 token file (a synthetic stream of 64 batches), and a checkpoint of the
+    master weights and both AdamW moments written, read back and loaded into the arena."""
+    import tempfile
+    import numpy as np
+    import torch
+    import synth
+    from transformer_lm_fwd_amd import Arena, binding
+
+    w = synth.WORKLOADS[args.workload]
+    m = w.model
+    nb = 64
+    ids = synth.token_windows(w, seed=7, B=nb * w.B, T=w.T).reshape(-1)[:nb * w.B * w.T + 1].astype(np.int32)
+    tmp = tempfile.mkdtemp(prefix="gpt2_io_")
+    tok = os.path.join(tmp, "train.bin")
+    ids.tofile(tok)
+    steps = max(1, args.steps)
+    t0 = time.perf_counter()
+    for i in range(steps * 4):
+        binding.tokens_batch(tok, w.B, w.T, i % nb)
+    el = time.perf_counter() - t0
+    batches_s = steps * 4 / el
+    tok_bytes = w.B * (w.T + 1) * 4
+    log(f"[bench] token batches: {batches_s:,.0f} batches/s = {batches_s * w.B * w.T / 1e6:.1f} M tokens/s "
+        f"({batches_s * tok_bytes / 1e9:.2f} GB/s of ids)")
+
+    torch.cuda.set_device(0)
+    arena = Arena(m, w.B, w.T, w.dtype)
+    arena.load_params(synth.init_params(m))
+    torch.cuda.synchronize()
+    ck = os.path.join(tmp, "ck.bin")
+    nbytes = 3 * 4 * arena.n_params + 64
+    t0 = time.perf_counter()
+    arena.save_checkpoint(ck, 1)
+    t_w = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    arena.load_checkpoint(ck)
+    torch.cuda.synchronize()
+    t_r = time.perf_counter() - t0
+    log(f"[bench] checkpoint {nbytes / 1e9:.2f} GB: save {t_w:.3f} s ({nbytes / t_w / 1e9:.2f} GB/s incl. device "
+        f"copies), load {t_r:.3f} s ({nbytes / t_r / 1e9:.2f} GB/s incl. device copies)")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        t0, reps = time.perf_counter(), 0
+        while reps < 16 or time.perf_counter() - t0 < 2.0:
+            oracle.token_batch(ids, w.B, w.T, reps % nb)
+            reps += 1
+        el2 = time.perf_counter() - t0
+        cpu = {"value": round(reps / el2, 1), "unit": "batches/s", "cores": 1, "kind": "oracle",
+               "sample": f"oracle.token_batch on the same in-memory stream ({reps} batches of {w.B} x {w.T + 1} ids)"}
+        log(f"[bench] oracle batches: {cpu['value']} batches/s")
+    for f in (tok, ck):
+        os.remove(f)
+    os.rmdir(tmp)
+    out = {
+        "metric": f"token-file batches/sec ({w.B} x {w.T + 1} int32 ids per batch); checkpoint GB/s",
+        "value": round(batches_s, 1), "unit": "batches/s", "n_gpus": 1, "steps": steps * 4, "warmup": 0,
+        "ms_per_step": round(1e3 / batches_s, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int32", "data": "synthetic (seeded uniform token ids written to a temporary file)",
+        "config": {"workload": w.name + "_io", "batch": w.B, "seq_len": w.T, "file_batches": nb,
+                   "checkpoint_bytes": nbytes},
+        "checkpoint": {"save_s": round(t_w, 4), "load_s": round(t_r, 4), "save_gbs": round(nbytes / t_w / 1e9, 3),
+                       "load_gbs": round(nbytes / t_r / 1e9, 3)},
+        "roofline": None, "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
 
