@@ -58,10 +58,12 @@ def compare(got, ref, label):
     assert err <= GEN_LOGIT_ABS and cos >= GEN_ROW_COS, label
 
 
-@pytest.mark.parametrize("batch,n,steps", [(3, 17, 12), (1, 1, 20), (16, 5, 4)])
-def test_prefill_and_decode_match_the_oracle_forward(batch, n, steps):
+@pytest.mark.parametrize("batch,n,steps,C", [(3, 17, 12, 128), (1, 1, 20, 128), (16, 5, 4, 128), (8, 6, 5, 64),
+                                             (16, 3, 3, 768)])
+def test_prefill_and_decode_match_the_oracle_forward(batch, n, steps, C):
+    # C = 64: products with fewer 32-k steps than waves; C = 128 and 768: split-K products
     from transformer_lm_fwd_amd import Generator
-    m = ModelShape(256, 301, 2, 2, 128)  # head size 64
+    m = ModelShape(256, 301, 2, C // 64, C)  # head size 64
     w = Workload("gen_small", m, batch, 32, "bf16", "uniform", index=31)
     announce("gen_small", m, batch, n, f"steps={steps}")
     params = rand_params(m, seed=31)

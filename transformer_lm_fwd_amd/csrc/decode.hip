@@ -21,10 +21,11 @@ namespace gpt2 {
 // weight row per 32 k, and its accumulators hold column l % 16, rows 4 (l / 16) .. +3.
 // Block = 4 waves on 16 columns; wave w takes the 32-k steps w, w + 4, .. so the
 // weight rows stream in from four waves at once.  x' goes through LDS in chunks of up
-// to 2048 k; per chunk a wave first issues all of its weight loads (up to 16 per lane),
-// then the block stages x' (loads issued eight at a time before their stores), then
-// the wave multiplies.  The four waves' sums are added through LDS and each thread
-// applies the epilogue to one (row, column).
+// to 2048 k; per chunk a wave first issues its first batch of weight loads (up to 16
+// per lane), then every wave - also one with no step in this chunk - takes part in
+// staging x' (loads issued eight at a time before their stores), then the wave
+// multiplies.  The four waves' sums are added through LDS and each thread applies the
+// epilogue to one (row, column).
 // With LayerNorm gains / shifts, x' = LayerNorm(x): the whole rows are staged (one
 // chunk, K <= 2048), each row's mean and rstd (biased variance, eps 1e-5, two passes;
 // wave w takes rows w, w + 4, ..) come from LDS, and the rows are normalised in place
@@ -68,84 +69,89 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(SkinnyArgs a) {
     for (int k0 = 0; k0 < a.K; k0 += KC) {
         const int kc = min(KC, a.K - k0), cpr = kc / 8, nch = a.M * cpr;
         const int nsteps = (kc + 31) / 32;  // 32-k steps of the chunk; this wave takes w, w + 4, ..
-        for (int sb = w; sb < nsteps; sb += 4 * SK_WL) {
-            u32x4 wv[SK_WL];
+        // this wave's first batch of weight loads (zeros past the chunk: a wave with no
+        // 32-k step still takes part in the staging and its barriers)
+        u32x4 wv[SK_WL];
+        auto load_batch = [&](int sb) {
 #pragma unroll
             for (int j = 0; j < SK_WL; ++j) {
                 const int kk = 32 * (sb + 4 * j) + 8 * kq;
                 wv[j] = (n < a.N && kk < kc) ? ld16(wrow + k0 + kk) : u32x4{0u, 0u, 0u, 0u};
             }
-            if (sb == w) {  // first batch of the chunk: stage x' while the loads are in flight
-                __syncthreads();  // the previous chunk is no longer read
-                for (int b0 = 0; b0 < nch; b0 += 256 * 8) {
-                    u32x4 t[8];
+        };
+        load_batch(w);
+        // stage x' while the loads are in flight (every wave, every chunk)
+        __syncthreads();  // the previous chunk is no longer read
+        for (int b0 = 0; b0 < nch; b0 += 256 * 8) {
+            u32x4 t[8];
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const int i = b0 + 256 * j + tid;
-                        t[j] = i < nch ? ld16(a.x + (int64_t)(i / cpr) * a.ldx + k0 + (i % cpr) * 8)
-                                       : u32x4{0u, 0u, 0u, 0u};
+            for (int j = 0; j < 8; ++j) {
+                const int i = b0 + 256 * j + tid;
+                t[j] = i < nch ? ld16(a.x + (int64_t)(i / cpr) * a.ldx + k0 + (i % cpr) * 8)
+                               : u32x4{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int i = b0 + 256 * j + tid;
+                if (i < nch) *(u32x4*)&xs[(i / cpr) * kc + (i % cpr) * 8] = t[j];
+            }
+        }
+        __syncthreads();
+        if constexpr (LN) {
+            // wave w takes rows w, w + 4, ..: two passes (mean, then the variance about it)
+            __shared__ float stat[SK_MAXM][2];
+            float part[SK_MAXM / 4], mean[SK_MAXM / 4];
+#pragma unroll
+            for (int r = 0; r < SK_MAXM / 4; ++r) {
+                const int m = w + 4 * r;
+                part[r] = 0.f;
+                if (m < a.M)
+                    for (int k = lane * 8; k < kc; k += 512) {
+                        float v[8];
+                        unpack16<bf16>(*(const u32x4*)(xs + m * kc + k), v);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) part[r] += v[e];
                     }
+            }
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const int i = b0 + 256 * j + tid;
-                        if (i < nch) *(u32x4*)&xs[(i / cpr) * kc + (i % cpr) * 8] = t[j];
+            for (int r = 0; r < SK_MAXM / 4; ++r) mean[r] = wave_sum(part[r]) / kc;
+#pragma unroll
+            for (int r = 0; r < SK_MAXM / 4; ++r) {
+                const int m = w + 4 * r;
+                part[r] = 0.f;
+                if (m < a.M)
+                    for (int k = lane * 8; k < kc; k += 512) {
+                        float v[8];
+                        unpack16<bf16>(*(const u32x4*)(xs + m * kc + k), v);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) part[r] += (v[e] - mean[r]) * (v[e] - mean[r]);
                     }
-                }
-                __syncthreads();
-                if constexpr (LN) {
-                    // wave w takes rows w, w + 4, ..: two passes (mean, then the variance about it)
-                    __shared__ float stat[SK_MAXM][2];
-                    float part[SK_MAXM / 4], mean[SK_MAXM / 4];
+            }
 #pragma unroll
-                    for (int r = 0; r < SK_MAXM / 4; ++r) {
-                        const int m = w + 4 * r;
-                        part[r] = 0.f;
-                        if (m < a.M)
-                            for (int k = lane * 8; k < kc; k += 512) {
-                                float v[8];
-                                unpack16<bf16>(*(const u32x4*)(xs + m * kc + k), v);
-#pragma unroll
-                                for (int e = 0; e < 8; ++e) part[r] += v[e];
-                            }
-                    }
-#pragma unroll
-                    for (int r = 0; r < SK_MAXM / 4; ++r) mean[r] = wave_sum(part[r]) / kc;
-#pragma unroll
-                    for (int r = 0; r < SK_MAXM / 4; ++r) {
-                        const int m = w + 4 * r;
-                        part[r] = 0.f;
-                        if (m < a.M)
-                            for (int k = lane * 8; k < kc; k += 512) {
-                                float v[8];
-                                unpack16<bf16>(*(const u32x4*)(xs + m * kc + k), v);
-#pragma unroll
-                                for (int e = 0; e < 8; ++e) part[r] += (v[e] - mean[r]) * (v[e] - mean[r]);
-                            }
-                    }
-#pragma unroll
-                    for (int r = 0; r < SK_MAXM / 4; ++r) {
-                        const float var = wave_sum(part[r]) / kc;
-                        const int m = w + 4 * r;
-                        if (lane == 0 && m < a.M) {
-                            stat[m][0] = mean[r];
-                            stat[m][1] = 1.0f / sqrtf(var + 1e-5f);
-                        }
-                    }
-                    __syncthreads();
-                    // thread t normalises the 8-column chunk t of every row
-                    if (tid < cpr) {
-                        for (int m = 0; m < a.M; ++m) {
-                            float f[8];
-                            unpack16<bf16>(*(const u32x4*)&xs[m * kc + 8 * tid], f);
-                            const float mu = stat[m][0], rstd = stat[m][1];
-#pragma unroll
-                            for (int e = 0; e < 8; ++e) f[e] = (f[e] - mu) * rstd * gv[e] + bv[e];
-                            *(u32x4*)&xs[m * kc + 8 * tid] = pack16<bf16>(f);
-                        }
-                    }
-                    __syncthreads();
+            for (int r = 0; r < SK_MAXM / 4; ++r) {
+                const float var = wave_sum(part[r]) / kc;
+                const int m = w + 4 * r;
+                if (lane == 0 && m < a.M) {
+                    stat[m][0] = mean[r];
+                    stat[m][1] = 1.0f / sqrtf(var + 1e-5f);
                 }
             }
+            __syncthreads();
+            // thread t normalises the 8-column chunk t of every row
+            if (tid < cpr) {
+                for (int m = 0; m < a.M; ++m) {
+                    float f[8];
+                    unpack16<bf16>(*(const u32x4*)&xs[m * kc + 8 * tid], f);
+                    const float mu = stat[m][0], rstd = stat[m][1];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) f[e] = (f[e] - mu) * rstd * gv[e] + bv[e];
+                    *(u32x4*)&xs[m * kc + 8 * tid] = pack16<bf16>(f);
+                }
+            }
+            __syncthreads();
+        }
+        for (int sb = w; sb < nsteps; sb += 4 * SK_WL) {
+            if (sb != w) load_batch(sb);
 #pragma unroll
             for (int j = 0; j < SK_WL; ++j) {
                 const int kk = 32 * (sb + 4 * j) + 8 * kq;
@@ -161,9 +167,9 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(SkinnyArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) red[w][4 * kq + i][col] = acc[i];
     __syncthreads();
-    if (!eok) return;
     const int cn = tid & 15;
-    float v = (red[0][em][cn] + red[1][em][cn]) + (red[2][em][cn] + red[3][em][cn]);
+    float v = eok ? (red[0][em][cn] + red[1][em][cn]) + (red[2][em][cn] + red[3][em][cn]) : 0.f;
+    if (!eok) return;
     v += ebias;
     const int64_t o = (int64_t)em * a.ldc + en;
     if constexpr (EPI == EPI_F32) {
