@@ -75,3 +75,9 @@ def test_llama_refusals():
             call()
     with pytest.raises(ValueError):
         a.save_checkpoint("/tmp/never_written.bin", 0)
+
+
+def test_fp32_llama_single_position():
+    w = Workload("llama_t1", ModelShape(16, 97, 2, 2, 64, "llama"), 3, 1, "fp32", "uniform", index=75)
+    announce("llama_fp32_T1", w)
+    fp32_full_compare(w, llama_params(w.model, 75), rotary=True)

@@ -235,3 +235,54 @@ def test_producer_written_codes_equal_the_quantizer_of_the_stored_activations():
             rq, rs = b.mx_quantize(a.tensor(b.T_FCH_GELU, m.num_layers - 1))
             np.testing.assert_array_equal(to_np(q), to_np(rq))
             np.testing.assert_array_equal(to_np(sc), to_np(rs))
+
+
+def test_empty_calls_are_no_ops():
+    import ctypes
+    from transformer_lm_fwd_amd import binding as b
+    L = b.lib()
+    p = ctypes.c_void_p(16)
+    assert L.gpt2_mx_quantize(p, 8, 0, 64, p, 128, p, None) == 0
+    assert L.gpt2_mx_quantize(p, 8, 5, 0, p, 128, p, None) == 0
+    assert L.gpt2_mx_gemm(p, p, 128, p, p, 128, p, 64, 0, 64, 128, 0, None, None, None, None) == 0
+    assert L.gpt2_mx_gemm(p, p, 128, p, p, 128, p, 64, 4, 0, 128, 0, None, None, None, None) == 0
+
+
+@pytest.mark.parametrize("B,T", [(1, 1), (3, 37)])
+def test_mx_forward_single_position_and_ragged_rows(B, T):
+    # B*T = 1 and 111 rows: one partial 128-row tile of every MX product
+    m = ModelShape(64, 301, 2, 2, 128)
+    w = Workload("mx_edge", m, B, T, "bf16", "uniform", index=53)
+    announce("mx_forward_edge", B=B, T=T)
+    params = rand_params(m, seed=53)
+    x, y = synth.inputs_targets(w)
+    (bf_loss, bf_z), (mx_loss, mx_z), ref_loss, ref = _forward_case(w, params, x, y)
+    V = m.vocab_size
+    cos = min(cosine(mx_z[r, :V], ref[r]) for r in range(ref.shape[0]))
+    print(f"loss oracle {ref_loss:.6f} mxfp8 {mx_loss:.6f}; min row cosine {cos:.6f}", flush=True)
+    assert abs(mx_loss - ref_loss) <= MX_LOSS_REL * ref_loss and cos >= MX_LOGIT_COS
+
+
+def test_mx_forward_gpt2_350m_full_size_against_the_bf16_path():
+    # GPT-2 350M at B=8, T=1024 (beyond the oracle at this size): the MX forward must keep
+    # the bf16 forward's logits' direction and loss within the format's tolerance
+    from transformer_lm_fwd_amd import binding as b
+    w = synth.WORKLOADS["gpt2_350m_b8t1024_bf16_zipf"]
+    announce("mx_forward_350m", B=w.B, T=w.T)
+    x, y = synth.inputs_targets(w)
+    a = gpu_arena(w, synth.init_params(w.model))
+    rows = np.unique(np.r_[0, w.B * w.T - 1, np.random.default_rng(1).integers(0, w.B * w.T, 62)])
+    V = w.model.vocab_size
+
+    def run():
+        a.forward(x)
+        z = to_np(a.tensor(b.T_LOGITS)[rows]).astype(np.float64)[:, :V]
+        a.forward(x, y)
+        return a.loss(), z
+
+    lb, zb = run()
+    a.set_gemm_format(b.GPT2_GEMM_MXFP8)
+    lm, zm = run()
+    cos = min(cosine(zm[i], zb[i]) for i in range(len(rows)))
+    print(f"350M loss bf16 {lb:.5f} mxfp8 {lm:.5f}; min sampled row cosine {cos:.6f}", flush=True)
+    assert abs(lm - lb) <= MX_LOSS_REL * lb and cos >= MX_LOGIT_COS
