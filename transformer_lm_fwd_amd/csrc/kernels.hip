@@ -47,94 +47,112 @@ hipError_t encoder_forward(T* out, const int32_t* tok, const float* wte, const f
 // lane l's 8 values are chunk 64 ch + l, so 4 lanes hold a 32-block and 16 a stage.
 // rms: RMSNorm (Llama-style block) - the mean is taken as 0 (the statistics hold
 // mean 0 and 1 / sqrt(mean(x^2) + eps)); b may be null (no shift).
-template <class T, int MAXCH, bool MXO = false>
+// Each wave takes RPW consecutive rows; the next row's loads go out before the current
+// row is reduced, and the gains / shifts are loaded once per wave.
+// MXO: also writes the MX FP8 codes and block scales of the (bf16-rounded) output,
+// q [N, Kp] (row stride ldq bytes), sc [Kp / 128][N][4], for a following MX product;
+// lane l's 8 values are chunk 64 ch + l, so 4 lanes hold a 32-block and 16 a stage.
+#ifndef LNF_RPW
+#define LNF_RPW 1
+#endif
+template <class T, int MAXCH, bool MXO = false, int RPW = LNF_RPW>
 __global__ __launch_bounds__(256) void layernorm_forward_kernel(T* out, float* stats, const T* inp, const float* w,
                                                                 const float* b, int N, int C, uint8_t* q = nullptr,
                                                                 int64_t ldq = 0, uint8_t* sc = nullptr,
                                                                 bool rms = false) {
     constexpr int KV = Vec16<T>::N;
     const int lane = threadIdx.x & 63;
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= N) return;
-    const T* x = inp + (int64_t)row * C;
-    float v[MAXCH][KV];
-    float sum = 0.f;
+    const int row0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW;
+    if (row0 >= N) return;
+    float wv[MAXCH][KV], bv[MAXCH][KV];
 #pragma unroll
     for (int ch = 0; ch < MAXCH; ++ch) {
-        int c = (ch * 64 + lane) * KV;
-        if (c < C) {
-            unpack16<T>(ld16(x + c), v[ch]);
+        const int c = (ch * 64 + lane) * KV;
 #pragma unroll
-            for (int e = 0; e < KV; ++e) sum += v[ch][e];
-        }
-    }
-    const float mean = rms ? 0.f : wave_sum(sum) / C;
-    float sq = 0.f;
-#pragma unroll
-    for (int ch = 0; ch < MAXCH; ++ch) {
-        int c = (ch * 64 + lane) * KV;
+        for (int e = 0; e < KV; ++e) wv[ch][e] = bv[ch][e] = 0.f;
         if (c < C) {
 #pragma unroll
-            for (int e = 0; e < KV; ++e) {
-                float d = v[ch][e] - mean;
-                sq += d * d;
+            for (int e = 0; e < KV; e += 4) {  // C % 8 == 0: 16-byte aligned fp32 gains and shifts
+                *(float4*)&wv[ch][e] = *(const float4*)(w + c + e);
+                if (b) *(float4*)&bv[ch][e] = *(const float4*)(b + c + e);
             }
         }
     }
-    const float rstd = 1.0f / sqrtf(wave_sum(sq) / C + 1e-5f);
-    T* y = out + (int64_t)row * C;
-    if constexpr (MXO) {
-        static_assert(KV == 8, "MX output from bf16 rows");
-        const int Kp = (C + 127) / 128 * 128;
+    u32x4 raw[MAXCH];
+    auto issue = [&](int row) {
 #pragma unroll
         for (int ch = 0; ch < MAXCH; ++ch) {
             const int c = (ch * 64 + lane) * KV;
-            float o[KV];
+            raw[ch] = (row < N && c < C) ? ld16(inp + (int64_t)row * C + c) : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    issue(row0);
+#pragma unroll 1
+    for (int i = 0; i < RPW; ++i) {
+        const int row = row0 + i;
+        if (row >= N) break;  // wave-uniform
+        float v[MAXCH][KV];
+        float sum = 0.f;
 #pragma unroll
-            for (int e = 0; e < KV; ++e) o[e] = 0.f;
+        for (int ch = 0; ch < MAXCH; ++ch) {
+            unpack16<T>(raw[ch], v[ch]);  // zeros past C
+#pragma unroll
+            for (int e = 0; e < KV; ++e) sum += v[ch][e];
+        }
+        if (i + 1 < RPW) issue(row + 1);
+        const float mean = rms ? 0.f : wave_sum(sum) / C;
+        float sq = 0.f;
+#pragma unroll
+        for (int ch = 0; ch < MAXCH; ++ch) {
+            const int c = (ch * 64 + lane) * KV;
             if (c < C) {
-                float wv[KV], bv[KV];
 #pragma unroll
-                for (int e = 0; e < KV; e += 4) {
-                    *(float4*)&wv[e] = *(const float4*)(w + c + e);
-                    *(float4*)&bv[e] = b ? *(const float4*)(b + c + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+                for (int e = 0; e < KV; ++e) {
+                    const float d = v[ch][e] - mean;
+                    sq += d * d;
                 }
-#pragma unroll
-                for (int e = 0; e < KV; ++e) o[e] = (v[ch][e] - mean) * rstd * wv[e] + bv[e];
-                round_bf16_8(o);
-                st16(y + c, pack16<T>(o));
             }
-            uint32_t cw[2];
-            const uint32_t word = mx_stage_word(mx_quant8(o, cw));
-            if (c < Kp) {
-                *(uint2*)(q + (int64_t)row * ldq + c) = make_uint2(cw[0], cw[1]);
-                if ((lane & 15) == 0) *(uint32_t*)(sc + ((int64_t)(c / 128) * N + row) * 4) = word;
+        }
+        const float rstd = 1.0f / sqrtf(wave_sum(sq) / C + 1e-5f);
+        T* y = out + (int64_t)row * C;
+        if constexpr (MXO) {
+            static_assert(KV == 8, "MX output from bf16 rows");
+            const int Kp = (C + 127) / 128 * 128;
+#pragma unroll
+            for (int ch = 0; ch < MAXCH; ++ch) {
+                const int c = (ch * 64 + lane) * KV;
+                float o[KV];
+#pragma unroll
+                for (int e = 0; e < KV; ++e) o[e] = 0.f;
+                if (c < C) {
+#pragma unroll
+                    for (int e = 0; e < KV; ++e) o[e] = (v[ch][e] - mean) * rstd * wv[ch][e] + bv[ch][e];
+                    round_bf16_8(o);
+                    st16(y + c, pack16<T>(o));
+                }
+                uint32_t cw[2];
+                const uint32_t word = mx_stage_word(mx_quant8(o, cw));
+                if (c < Kp) {
+                    *(uint2*)(q + (int64_t)row * ldq + c) = make_uint2(cw[0], cw[1]);
+                    if ((lane & 15) == 0) *(uint32_t*)(sc + ((int64_t)(c / 128) * N + row) * 4) = word;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int ch = 0; ch < MAXCH; ++ch) {
+                const int c = (ch * 64 + lane) * KV;
+                if (c < C) {
+                    float o[KV];
+#pragma unroll
+                    for (int e = 0; e < KV; ++e) o[e] = (v[ch][e] - mean) * rstd * wv[ch][e] + bv[ch][e];
+                    st16(y + c, pack16<T>(o));
+                }
             }
         }
         if (lane == 0) {
             stats[2 * row] = mean;
             stats[2 * row + 1] = rstd;
         }
-        return;
-    }
-#pragma unroll
-    for (int ch = 0; ch < MAXCH; ++ch) {
-        int c = (ch * 64 + lane) * KV;
-        if (c < C) {
-            float o[KV], wv[KV], bv[KV];
-#pragma unroll
-            for (int e = 0; e < KV; e += 4) {  // C % 8 == 0: 16-byte aligned fp32 gains and shifts
-                *(float4*)&wv[e] = *(const float4*)(w + c + e);
-                *(float4*)&bv[e] = b ? *(const float4*)(b + c + e) : make_float4(0.f, 0.f, 0.f, 0.f);
-            }
-#pragma unroll
-            for (int e = 0; e < KV; ++e) o[e] = (v[ch][e] - mean) * rstd * wv[e] + bv[e];
-            st16(y + c, pack16<T>(o));
-        }
-    }
-    if (lane == 0) {
-        stats[2 * row] = mean;
-        stats[2 * row + 1] = rstd;
     }
 }
 
@@ -143,7 +161,7 @@ hipError_t layernorm_forward(T* out, float* stats, const T* inp, const float* w,
                              hipStream_t s, uint8_t* mxq, int64_t ldq, uint8_t* mxs, bool rms) {
     constexpr int KV = Vec16<T>::N;
     int ch = cdiv(C, 64 * KV);
-    dim3 grid(cdiv(N, 4)), block(256);
+    dim3 grid(cdiv(N, 4 * LNF_RPW)), block(256);
     if constexpr (sizeof(T) == 2) {
         if (mxq) {
             if (!mxs || ldq < (C + 127) / 128 * 128 || ldq % 16) return hipErrorInvalidValue;
