@@ -562,6 +562,11 @@ struct Model {
             return GPT2_OK;
         };
 
+        // which token ids the batch holds (the embedding backward's census, and with `opt`
+        // the split of wte's AdamW update into absent rows, early, and present rows, last)
+        int* census_first = at<int>(a, a->census);
+        int* census_count = census_first + V;
+        CHECK(token_census(census_first, census_count, a->inputs, BT, M), "token census");
         // lm_head: dlnf = dz wte on the main stream; dwte = dz^T lnf (overwrites) on the side
         if ((rc = stream_wait(a, SD, M))) return rc;
         {
@@ -570,8 +575,20 @@ struct Model {
             g.M = V; g.N = C; g.K = BT; g.lda = Vp; g.ldb = C; g.ldc = C;
             CHECK(gemm<T>(g, false, false, EPI_F32, f32(a->ws), a->ws_floats, SD), "gemm");
         }
-        if ((rc = mark(a->ev_wte, SD))) return rc;
+        if (!opt && (rc = mark(a->ev_wte, SD))) return rc;
         if ((rc = gemm_call(dz, Vp, true, weight(a->o_wte), C, false, dbuf, C, BT, C, V, EPI_BIAS))) return rc;
+        AdamwRows wte_opt{};
+        if (opt) {
+            // rows of wte no token of the batch touches have their final gradient now: update
+            // them on the side stream once the main stream's dX product has read wte
+            wte_opt = AdamwRows{master(a->o_wte), at<float>(a, a->adam_m) + a->o_wte,
+                                at<float>(a, a->adam_v) + a->o_wte,
+                                a->dtype == GPT2_BF16 ? at<bf16>(a, a->params16) + a->o_wte : nullptr,
+                                opt->lr, opt->b1, opt->b2, opt->eps, opt->wd, opt->c1, opt->c2};
+            if ((rc = stream_wait(a, SD, M))) return rc;
+            CHECK(adamw_rows_absent(wte_opt, grad(a->o_wte), census_count, V, C, SD), "adamw wte");
+            if ((rc = mark(a->ev_wte, SD))) return rc;
+        }
         int cur = 0;
         if ((rc = wait(M, a->rd_res[0]))) return rc;
         CHECK(layernorm_backward<T>(act(a->dres[0]), (const T*)nullptr, grad(a->o_lnfw), gb(a->o_lnfb), dbuf,
@@ -651,14 +668,15 @@ struct Model {
         }
         // embedding: dwte += scatter (after the side stream's lm_head dW), dwpe
         if ((rc = wait(M, a->ev_wte))) return rc;
+        // (with `opt` the present rows of wte get their AdamW update as their gradient completes)
         CHECK(encoder_backward<T>(grad(a->o_wte), grad(a->o_wpe), act(a->dres[cur]), a->inputs, B, S, P, C,
-                                  at<int>(a, a->census), at<int>(a, a->census) + V, M, !rotary()),
+                                  census_first, census_count, M, !rotary(), wte_opt),
               "encoder backward");
         // join: everything the side stream enqueued finishes before later main-stream work
         if ((rc = mark(a->ev_end, SD))) return rc;
         if ((rc = wait(M, a->ev_end))) return rc;
         if (opt) {
-            if ((rc = adamw_range(a, *opt, 0, lp(0, 0), M))) return rc;  // wte, wpe
+            if ((rc = adamw_range(a, *opt, a->o_wpe, lp(0, 0) - a->o_wpe, M))) return rc;  // wpe (wte: above)
             if ((rc = adamw_range(a, *opt, a->o_lnfw, a->nparams - a->o_lnfw, M))) return rc;  // ln_f
         }
         return GPT2_OK;

@@ -116,9 +116,25 @@ hipError_t crossentropy_fused(T* logits, float* losses, const int32_t* targets, 
 hipError_t mean_loss(float* loss, const float* losses, int N, hipStream_t s);
 // dwte[tok] += dx rows (deterministic), dwpe[t] = sum_b dx[b, t] for t < T, 0 for T <= t < P.
 // first / count: int [V] scratch, INT_MAX / 0 on entry (token_census_reset) and on return.
+// AdamW of a parameter range inside another kernel (p null: no update).
+struct AdamwRows {
+    float* p;
+    float* m;
+    float* v;
+    bf16* p16;
+    float lr, b1, b2, eps, wd, c1, c2;
+};
+// token_census: first position and count of every token id of tok [BT] (the census
+// must hold its idle state: first = INT_MAX, count = 0; encoder_backward restores it).
+hipError_t token_census(int* first, int* count, const int32_t* tok, int BT, hipStream_t s);
+// Needs the census of tok.  With opt.p set, each present token's row of wte gets its
+// AdamW update right after its gradient is complete.
 template <class T>
 hipError_t encoder_backward(float* dwte, float* dwpe, const T* dx, const int32_t* tok, int B, int T_, int P, int C,
-                            int* first, int* count, hipStream_t s, bool wpe_used = true);
+                            int* first, int* count, hipStream_t s, bool wpe_used = true,
+                            const AdamwRows& opt = AdamwRows{});
+// AdamW over the rows r < rows (C values each) of a matrix whose count[r] == 0.
+hipError_t adamw_rows_absent(const AdamwRows& o, const float* g, const int* count, int rows, int C, hipStream_t s);
 hipError_t token_census_reset(int* first, int* count, int V, hipStream_t s);
 hipError_t adamw(float* p, const float* g, float* m, float* v, bf16* p16, int64_t n, float lr, float b1, float b2,
                  float eps, float wd, float c1, float c2, hipStream_t s);

@@ -640,9 +640,27 @@ __global__ __launch_bounds__(256) void token_census_kernel(int* first, int* coun
     atomicAdd(&count[tok[p]], 1);
 }
 
+// AdamW of one parameter ("1000 行 C 代码完成 GPT-2 训练的 LLM.c": the step ends with an
+// Adam update).  Decoupled weight decay with bias correction (c1 = 1 - beta1^t,
+// c2 = 1 - beta2^t): m = b1 m + (1-b1) g;  v = b2 v + (1-b2) g^2;
+// p -= lr (m/c1 / (sqrt(v/c2) + eps) + wd p)
+// Every rounding is spelled out (fused multiply-adds, correctly rounded divisions and
+// square root), so each kernel that applies the update - the whole-array pass, the
+// absent-rows pass, the embedding scatter - produces the same bits whatever the
+// compiler would otherwise contract.
+__device__ __forceinline__ void adamw_one(float& p, float g, float& m, float& v, float lr, float b1, float b2,
+                                          float eps, float wd, float c1, float c2) {
+    m = __fmaf_rn(b1, m, (1.f - b1) * g);
+    v = __fmaf_rn(b2, v, ((1.f - b2) * g) * g);
+    const float mh = __fdiv_rn(m, c1), vh = __fdiv_rn(v, c2);
+    const float u = __fmaf_rn(wd, p, __fdiv_rn(mh, __fsqrt_rn(vh) + eps));
+    p = __fmaf_rn(-lr, u, p);
+}
+
 template <class T>
 __global__ __launch_bounds__(256) void encoder_backward_wte_kernel(float* dwte, const T* dx, const int32_t* tok,
-                                                                   int* first, int* count, int BT, int C) {
+                                                                   int* first, int* count, int BT, int C,
+                                                                   AdamwRows opt) {
     const int pos = blockIdx.x;
     const int v = tok[pos];
     if (first[v] != pos) return;  // block-uniform
@@ -684,12 +702,65 @@ __global__ __launch_bounds__(256) void encoder_backward_wte_kernel(float* dwte, 
 #pragma unroll
     for (int i = 0; i < MAXC; ++i) {
         const int c = threadIdx.x + i * 256;
-        if (c < C) out[c] += acc[i];
+        if (c < C) {
+            const float g = out[c] + acc[i];
+            out[c] = g;
+            if (opt.p) {  // the row's gradient is complete: its AdamW update
+                const int64_t o = (int64_t)v * C + c;
+                float pp = opt.p[o], mm = opt.m[o], vv = opt.v[o];
+                adamw_one(pp, g, mm, vv, opt.lr, opt.b1, opt.b2, opt.eps, opt.wd, opt.c1, opt.c2);
+                opt.p[o] = pp;
+                opt.m[o] = mm;
+                opt.v[o] = vv;
+                if (opt.p16) opt.p16[o] = from_f32<bf16>(pp);
+            }
+        }
     }
     if (threadIdx.x == 0) {
         first[v] = 0x7fffffff;
         count[v] = 0;
     }
+}
+
+// AdamW over the rows of a matrix that no token of the batch touched (count == 0):
+// their gradient is final before the embedding scatter.  Thread: 4 values of a row.
+__global__ __launch_bounds__(256) void adamw_rows_absent_kernel(AdamwRows o, const float* g, const int* count, int rows,
+                                                                int C) {
+    const int c4 = C / 4;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)rows * c4) return;
+    const int r = (int)(i / c4);
+    if (count[r] != 0) return;
+    float4 pp = ((float4*)o.p)[i], mm = ((float4*)o.m)[i], vv = ((float4*)o.v)[i];
+    const float4 gg = ((const float4*)g)[i];
+    adamw_one(pp.x, gg.x, mm.x, vv.x, o.lr, o.b1, o.b2, o.eps, o.wd, o.c1, o.c2);
+    adamw_one(pp.y, gg.y, mm.y, vv.y, o.lr, o.b1, o.b2, o.eps, o.wd, o.c1, o.c2);
+    adamw_one(pp.z, gg.z, mm.z, vv.z, o.lr, o.b1, o.b2, o.eps, o.wd, o.c1, o.c2);
+    adamw_one(pp.w, gg.w, mm.w, vv.w, o.lr, o.b1, o.b2, o.eps, o.wd, o.c1, o.c2);
+    ((float4*)o.p)[i] = pp;
+    ((float4*)o.m)[i] = mm;
+    ((float4*)o.v)[i] = vv;
+    if (o.p16) {
+        uint2 h;
+        h.x = pack2_bf16(pp.x, pp.y);
+        h.y = pack2_bf16(pp.z, pp.w);
+        ((uint2*)o.p16)[i] = h;
+    }
+}
+
+hipError_t adamw_rows_absent(const AdamwRows& o, const float* g, const int* count, int rows, int C, hipStream_t s) {
+    if (rows <= 0) return hipSuccess;
+    if (C % 4) return hipErrorInvalidValue;
+    ProfScope prof(s, "adamw_wte_absent", 0, (double)rows * C * 30.0);
+    hipLaunchKernelGGL(adamw_rows_absent_kernel, dim3(cdiv((int64_t)rows * (C / 4), 256)), dim3(256), 0, s, o, g,
+                       count, rows, C);
+    return hipGetLastError();
+}
+
+hipError_t token_census(int* first, int* count, const int32_t* tok, int BT, hipStream_t s) {
+    ProfScope prof(s, "token_census", 0, 4.0 * BT);
+    hipLaunchKernelGGL(token_census_kernel, dim3(cdiv(BT, 256)), dim3(256), 0, s, first, count, tok, BT);
+    return hipGetLastError();
 }
 
 __global__ void token_census_reset_kernel(int* first, int* count, int V) {
@@ -720,18 +791,13 @@ __global__ __launch_bounds__(256) void encoder_backward_wpe_kernel(float* dwpe, 
 
 template <class T>
 hipError_t encoder_backward(float* dwte, float* dwpe, const T* dx, const int32_t* tok, int B, int T_, int P, int C,
-                            int* first, int* count, hipStream_t s, bool wpe_used) {
+                            int* first, int* count, hipStream_t s, bool wpe_used, const AdamwRows& opt) {
     if (C > 8 * 256) return hipErrorInvalidValue;
-    {
-        ProfScope prof(s, "token_census", 0, 4.0 * B * T_);
-        hipLaunchKernelGGL(token_census_kernel, dim3(cdiv(B * T_, 256)), dim3(256), 0, s, first, count, tok, B * T_);
-    }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    hipError_t e;
     {
         ProfScope prof(s, "encoder_bwd_wte", 0, (double)B * T_ * C * (sizeof(T) + 8.0));
         hipLaunchKernelGGL(encoder_backward_wte_kernel<T>, dim3(B * T_), dim3(256), 0, s, dwte, dx, tok, first, count,
-                           B * T_, C);
+                           B * T_, C, opt);
     }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -746,13 +812,7 @@ hipError_t encoder_backward(float* dwte, float* dwpe, const T* dx, const int32_t
 // "1000 行 C 代码完成 GPT-2 训练的 LLM.c": the step ends with an Adam update.  Decoupled
 // weight decay with bias correction (c1 = 1 - beta1^t, c2 = 1 - beta2^t):
 //   m = b1 m + (1-b1) g;  v = b2 v + (1-b2) g^2;  p -= lr (m/c1 / (sqrt(v/c2) + eps) + wd p)
-__device__ __forceinline__ void adamw_one(float& p, float g, float& m, float& v, float lr, float b1, float b2,
-                                          float eps, float wd, float c1, float c2) {
-    m = b1 * m + (1.f - b1) * g;
-    v = b2 * v + (1.f - b2) * g * g;
-    float mh = m / c1, vh = v / c2;
-    p -= lr * (mh / (sqrtf(vh) + eps) + wd * p);
-}
+// (adamw_one is defined with the embedding backward, which also applies it)
 
 __global__ __launch_bounds__(256) void adamw_kernel(float* p, const float* g, float* m, float* v, bf16* p16,
                                                     int64_t n, float lr, float b1, float b2, float eps, float wd,
@@ -896,7 +956,7 @@ hipError_t splitk_reduce_bf16(bf16* C, int64_t ldc, const float* ws, int splits,
     template hipError_t bias_grad<T>(float*, const T*, int, int, int64_t, float*, size_t, hipStream_t);          \
     template hipError_t crossentropy_fused<T>(T*, float*, const int32_t*, int, int, int64_t, float, hipStream_t); \
     template hipError_t encoder_backward<T>(float*, float*, const T*, const int32_t*, int, int, int, int, int*,  \
-                                            int*, hipStream_t, bool);
+                                            int*, hipStream_t, bool, const AdamwRows&);
 GPT2_INST(float)
 GPT2_INST(bf16)
 
