@@ -19,28 +19,32 @@ namespace gpt2 {
 // with the 16 (zero-padded) rows of x' as A and 16 weight rows as B - lane l supplies
 // row / column l % 16 with the 8 k values 8 (l / 16) .. +7, i.e. one 16-byte load of its
 // weight row per 32 k, and its accumulators hold column l % 16, rows 4 (l / 16) .. +3.
-// Block = 4 waves on 16 columns; wave w takes the 32-k steps w, w + 4, .. so the
-// weight rows stream in from four waves at once.  x' goes through LDS in chunks of up
+// Block = NW (8) waves on 16 columns; wave w takes the 32-k steps w, w + NW, .. so the
+// weight rows stream in from all waves at once.  x' goes through LDS in chunks of up
 // to 2048 k; per chunk a wave first issues its first batch of weight loads (up to 16
 // per lane), then every wave - also one with no step in this chunk - takes part in
 // staging x' (loads issued eight at a time before their stores), then the wave
-// multiplies.  The four waves' sums are added through LDS and each thread applies the
+// multiplies.  The waves' sums are added through LDS and each thread applies the
 // epilogue to one (row, column).
 // With LayerNorm gains / shifts, x' = LayerNorm(x): the whole rows are staged (one
 // chunk, K <= 2048), each row's mean and rstd (biased variance, eps 1e-5, two passes;
-// wave w takes rows w, w + 4, ..) come from LDS, and the rows are normalised in place
+// wave w takes rows w, w + NW, ..) come from LDS, and the rows are normalised in place
 // and rounded to bf16 like the forward pass's LayerNorm output.  Every block repeats
 // this small prologue, which pays for products with few blocks (qkv, c_fc) but not for
 // the lm_head's thousands: that one takes a separately normalised input.
+#ifndef SK_NW
+#define SK_NW 8  // waves per block
+#endif
 constexpr int SK_MAXM = 16, SK_KC = 2048, SK_LN_MAXK = 2048, SK_WL = 16;  // weight loads per lane per chunk
+constexpr int NW = SK_NW, NT = 64 * SK_NW;
 
 typedef __bf16 sk_bf16x8 __attribute__((ext_vector_type(8)));
 typedef float sk_f32x4 __attribute__((ext_vector_type(4)));
 
 template <int EPI, bool LN>
-__global__ __launch_bounds__(256) void skinny_gemm_kernel(SkinnyArgs a) {
+__global__ __launch_bounds__(NT) void skinny_gemm_kernel(SkinnyArgs a) {
     extern __shared__ __attribute__((aligned(16))) bf16 xs[];  // [M][chunk]
-    __shared__ float red[4][16][17];
+    __shared__ float red[NW][16][17];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int col = lane & 15, kq = lane >> 4;
     const int n = blockIdx.x * 16 + col;
@@ -68,42 +72,42 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(SkinnyArgs a) {
     sk_f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int k0 = 0; k0 < a.K; k0 += KC) {
         const int kc = min(KC, a.K - k0), cpr = kc / 8, nch = a.M * cpr;
-        const int nsteps = (kc + 31) / 32;  // 32-k steps of the chunk; this wave takes w, w + 4, ..
+        const int nsteps = (kc + 31) / 32;  // 32-k steps of the chunk; this wave takes w, w + NW, ..
         // this wave's first batch of weight loads (zeros past the chunk: a wave with no
         // 32-k step still takes part in the staging and its barriers)
         u32x4 wv[SK_WL];
         auto load_batch = [&](int sb) {
 #pragma unroll
             for (int j = 0; j < SK_WL; ++j) {
-                const int kk = 32 * (sb + 4 * j) + 8 * kq;
+                const int kk = 32 * (sb + NW * j) + 8 * kq;
                 wv[j] = (n < a.N && kk < kc) ? ld16(wrow + k0 + kk) : u32x4{0u, 0u, 0u, 0u};
             }
         };
         load_batch(w);
         // stage x' while the loads are in flight (every wave, every chunk)
         __syncthreads();  // the previous chunk is no longer read
-        for (int b0 = 0; b0 < nch; b0 += 256 * 8) {
+        for (int b0 = 0; b0 < nch; b0 += NT * 8) {
             u32x4 t[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const int i = b0 + 256 * j + tid;
+                const int i = b0 + NT * j + tid;
                 t[j] = i < nch ? ld16(a.x + (int64_t)(i / cpr) * a.ldx + k0 + (i % cpr) * 8)
                                : u32x4{0u, 0u, 0u, 0u};
             }
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const int i = b0 + 256 * j + tid;
+                const int i = b0 + NT * j + tid;
                 if (i < nch) *(u32x4*)&xs[(i / cpr) * kc + (i % cpr) * 8] = t[j];
             }
         }
         __syncthreads();
         if constexpr (LN) {
-            // wave w takes rows w, w + 4, ..: two passes (mean, then the variance about it)
+            // wave w takes rows w, w + NW, ..: two passes (mean, then the variance about it)
             __shared__ float stat[SK_MAXM][2];
-            float part[SK_MAXM / 4], mean[SK_MAXM / 4];
+            float part[SK_MAXM / NW], mean[SK_MAXM / NW];
 #pragma unroll
-            for (int r = 0; r < SK_MAXM / 4; ++r) {
-                const int m = w + 4 * r;
+            for (int r = 0; r < SK_MAXM / NW; ++r) {
+                const int m = w + NW * r;
                 part[r] = 0.f;
                 if (m < a.M)
                     for (int k = lane * 8; k < kc; k += 512) {
@@ -114,10 +118,10 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(SkinnyArgs a) {
                     }
             }
 #pragma unroll
-            for (int r = 0; r < SK_MAXM / 4; ++r) mean[r] = wave_sum(part[r]) / kc;
+            for (int r = 0; r < SK_MAXM / NW; ++r) mean[r] = wave_sum(part[r]) / kc;
 #pragma unroll
-            for (int r = 0; r < SK_MAXM / 4; ++r) {
-                const int m = w + 4 * r;
+            for (int r = 0; r < SK_MAXM / NW; ++r) {
+                const int m = w + NW * r;
                 part[r] = 0.f;
                 if (m < a.M)
                     for (int k = lane * 8; k < kc; k += 512) {
@@ -128,9 +132,9 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(SkinnyArgs a) {
                     }
             }
 #pragma unroll
-            for (int r = 0; r < SK_MAXM / 4; ++r) {
+            for (int r = 0; r < SK_MAXM / NW; ++r) {
                 const float var = wave_sum(part[r]) / kc;
-                const int m = w + 4 * r;
+                const int m = w + NW * r;
                 if (lane == 0 && m < a.M) {
                     stat[m][0] = mean[r];
                     stat[m][1] = 1.0f / sqrtf(var + 1e-5f);
@@ -150,12 +154,12 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(SkinnyArgs a) {
             }
             __syncthreads();
         }
-        for (int sb = w; sb < nsteps; sb += 4 * SK_WL) {
+        for (int sb = w; sb < nsteps; sb += NW * SK_WL) {
             if (sb != w) load_batch(sb);
 #pragma unroll
             for (int j = 0; j < SK_WL; ++j) {
-                const int kk = 32 * (sb + 4 * j) + 8 * kq;
-                if (32 * (sb + 4 * j) < kc) {  // wave-uniform
+                const int kk = 32 * (sb + NW * j) + 8 * kq;
+                if (32 * (sb + NW * j) < kc) {  // wave-uniform
                     const u32x4 xa = (col < a.M && kk < kc) ? *(const u32x4*)&xs[col * kc + kk] : u32x4{0u, 0u, 0u, 0u};
                     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(sk_bf16x8, xa),
                                                                   __builtin_bit_cast(sk_bf16x8, wv[j]), acc, 0, 0, 0);
@@ -168,7 +172,10 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(SkinnyArgs a) {
     for (int i = 0; i < 4; ++i) red[w][4 * kq + i][col] = acc[i];
     __syncthreads();
     const int cn = tid & 15;
-    float v = eok ? (red[0][em][cn] + red[1][em][cn]) + (red[2][em][cn] + red[3][em][cn]) : 0.f;
+    float v = 0.f;
+    if (eok)
+#pragma unroll
+        for (int q = 0; q < NW; ++q) v += red[q][em][cn];
     if (!eok) return;
     v += ebias;
     const int64_t o = (int64_t)em * a.ldc + en;
@@ -188,10 +195,10 @@ static hipError_t skinny_launch(const SkinnyArgs& a, int epi, hipStream_t s) {
     const dim3 grid((a.N + 15) / 16);
     const size_t lds = (size_t)a.M * (LN ? a.K : std::min(a.K, SK_KC)) * 2;
     switch (epi) {
-        case EPI_BIAS: hipLaunchKernelGGL((skinny_gemm_kernel<EPI_BIAS, LN>), grid, dim3(256), lds, s, a); break;
-        case EPI_BIAS_RES: hipLaunchKernelGGL((skinny_gemm_kernel<EPI_BIAS_RES, LN>), grid, dim3(256), lds, s, a); break;
-        case EPI_BIAS_GELU: hipLaunchKernelGGL((skinny_gemm_kernel<EPI_BIAS_GELU, LN>), grid, dim3(256), lds, s, a); break;
-        case EPI_F32: hipLaunchKernelGGL((skinny_gemm_kernel<EPI_F32, LN>), grid, dim3(256), lds, s, a); break;
+        case EPI_BIAS: hipLaunchKernelGGL((skinny_gemm_kernel<EPI_BIAS, LN>), grid, dim3(NT), lds, s, a); break;
+        case EPI_BIAS_RES: hipLaunchKernelGGL((skinny_gemm_kernel<EPI_BIAS_RES, LN>), grid, dim3(NT), lds, s, a); break;
+        case EPI_BIAS_GELU: hipLaunchKernelGGL((skinny_gemm_kernel<EPI_BIAS_GELU, LN>), grid, dim3(NT), lds, s, a); break;
+        case EPI_F32: hipLaunchKernelGGL((skinny_gemm_kernel<EPI_F32, LN>), grid, dim3(NT), lds, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
