@@ -81,6 +81,24 @@ def test_prefill_and_decode_match_the_oracle_forward(batch, n, steps, C):
         assert np.all(chosen >= ref[:, pos, :].max(1) - 2 * GEN_LOGIT_ABS)
 
 
+@pytest.mark.parametrize("n,steps", [(250, 12), (500, 30)])
+def test_decode_over_long_contexts_matches_the_oracle_forward(n, steps):
+    # hundreds of cached keys: every wave of the decode attention takes several 64-key
+    # chunks, the last one ragged, and its online softmax rescales across them
+    from transformer_lm_fwd_amd import Generator
+    m = ModelShape(1024, 301, 2, 2, 128)
+    batch = 3
+    w = Workload("gen_small", m, batch, n + steps, "bf16", "uniform", index=35)
+    announce("gen_long", m, batch, n, f"steps={steps}")
+    params = rand_params(m, seed=35)
+    a = gpu_arena(w, params, B=batch, T=n)
+    gen = Generator(a, batch, n + steps)
+    seq, got = greedy_run(gen, prompt_tokens(w, batch, n, seed=200 + n), steps)
+    ref = oracle_logits(w, params, seq)
+    for i, g in enumerate(got):
+        compare(g, ref[:, n - 1 + i, :], f"position {n - 1 + i}")
+
+
 def test_decode_matches_the_gpu_full_forward_and_stops_at_max_len():
     from transformer_lm_fwd_amd import Generator, Gpt2Error
     m = ModelShape(256, 301, 2, 2, 128)

@@ -219,15 +219,18 @@ hipError_t skinny_gemm(const SkinnyArgs& a, int epi, hipStream_t s) {
 // ("GPT-2 from scratch with torch", 自注意力: softmax(q k^T / sqrt(hs)) v; the new row sees
 // every cached position, so no mask is needed).  Cache rows are the q|k|v rows the
 // qkv product wrote, [batch][max_len][3C].  Block (b, h): ADW waves take key chunks of
-// 64 in turn.  Scores: lane j takes key 64c + j, its key row read as 8 x 16 bytes
-// against the query held in registers; the wave keeps a running maximum and sum
-// (online softmax).  P V: lane (g, d8) = (lane / 8, lane % 8) adds p_key v_key[8 d8 ..
-// 8 d8 + 7] for the keys g, g + 8, .. of the chunk (16-byte V reads, p by shuffle), and
-// the 8 key groups are combined by shuffles at the end.  The waves' states are merged
-// through LDS.
-constexpr int ADW = 8;
+// 64 in turn.  Lane (g, d8) = (lane / 8, lane % 8) reads 16 bytes (dims 8 d8 ..
+// 8 d8 + 7) of the K and V rows of keys g, g + 8, .., so each row is one 128-byte run
+// read by eight lanes; a score is summed over those eight lanes by shuffles, and the
+// wave keeps a running maximum and sum (online softmax) while each lane adds p v over
+// its own keys.  The 8 key groups are combined by shuffles at the end and the waves'
+// states are merged through LDS.  (Splitting long contexts over several blocks per
+// (sequence, head), with a kernel merging the blocks' softmax states, measured no faster
+// at batch 1 and slower at batch 8: the kernel is bound by its memory round trips, not by
+// the number of blocks.)
+constexpr int ADW = 8;  // waves per (sequence, head) block
 __global__ __launch_bounds__(64 * ADW) void attn_decode64_kernel(bf16* y, const bf16* cache, int len, int C, int NH,
-                                                            int64_t bstride) {
+                                                                 int64_t bstride) {
     constexpr int HS = 64;
     const int b = blockIdx.x / NH, h = blockIdx.x % NH;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -235,54 +238,61 @@ __global__ __launch_bounds__(64 * ADW) void attn_decode64_kernel(bf16* y, const 
     const int64_t C3 = 3 * (int64_t)C;
     const bf16* base = cache + (int64_t)b * bstride;
     const float c = 0.125f * 1.4426950408889634f;  // 1/sqrt(64) in log2 units
-    u32x4 q[8];
-    const bf16* qrow = base + (int64_t)(len - 1) * C3 + h * HS;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) q[i] = ld16(qrow + 8 * i);
+    // lane (kg, d8) owns dims 8 d8 .. 8 d8 + 7 of keys k0 + kg + 8 i (i < 8): eight lanes
+    // read one 128-byte K or V row together, and a key's score is summed over its eight
+    // lanes, which then all hold it, next to the V row it weighs.
+    float qf[8];
+    unpack16<bf16>(ld16(base + (int64_t)(len - 1) * C3 + h * HS + 8 * d8), qf);
     float m = -INFINITY, l = 0.f, o[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = 0.f;
     for (int k0 = 64 * w; k0 < len; k0 += 64 * ADW) {
-        const int key = k0 + lane;
-        // this lane's 8 V rows (keys k0 + kg + 8 i) are requested before the scores
-        u32x4 vr[8];
+        u32x4 kr[8], vr[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const int vk = k0 + kg + 8 * i;
-            vr[i] = vk < len ? ld16(base + (int64_t)vk * C3 + 2 * C + h * HS + 8 * d8) : u32x4{0u, 0u, 0u, 0u};
+            const int key = k0 + kg + 8 * i;
+            const bf16* row = base + (int64_t)key * C3 + C + h * HS + 8 * d8;
+            kr[i] = key < len ? ld16(row) : u32x4{0u, 0u, 0u, 0u};
+            vr[i] = key < len ? ld16(row + C) : u32x4{0u, 0u, 0u, 0u};
         }
-        float s = -INFINITY;
-        if (key < len) {
-            const bf16* krow = base + (int64_t)key * C3 + C + h * HS;
-            u32x4 kr[8];
+        float s[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) kr[i] = ld16(krow + 8 * i);
+        for (int i = 0; i < 8; ++i) {
+            float kv[8];
+            unpack16<bf16>(kr[i], kv);
             float dot = 0.f;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                float kv[8], qv[8];
-                unpack16<bf16>(kr[i], kv);
-                unpack16<bf16>(q[i], qv);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) dot = __builtin_fmaf(qv[e], kv[e], dot);
-            }
-            s = dot * c;
+            for (int e = 0; e < 8; ++e) dot = __builtin_fmaf(qf[e], kv[e], dot);
+            s[i] = dot;
         }
-        const float mn = fmaxf(m, wave_max(s));
-        const float corr = __builtin_amdgcn_exp2f(m - mn);  // m = -inf at first: corr = 0
-        const float p = key < len ? __builtin_amdgcn_exp2f(s - mn) : 0.f;
-        l = l * corr + p;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] *= corr;
-        m = mn;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const float pk = __shfl(p, kg + 8 * i, 64);  // 0 for keys past len
+            s[i] += __shfl_xor(s[i], 1, 64);
+            s[i] += __shfl_xor(s[i], 2, 64);
+            s[i] += __shfl_xor(s[i], 4, 64);
+        }
+        float smax = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            s[i] = k0 + kg + 8 * i < len ? s[i] * c : -INFINITY;
+            smax = fmaxf(smax, s[i]);
+        }
+        const float mn = fmaxf(m, wave_max(smax));  // finite: key k0 < len
+        const float corr = __builtin_amdgcn_exp2f(m - mn);  // m = -inf at first: corr = 0
+        float psum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] *= corr;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float p = __builtin_amdgcn_exp2f(s[i] - mn);  // 0 for keys past len
+            psum += p;
             float v[8];
             unpack16<bf16>(vr[i], v);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) o[e] = __builtin_fmaf(pk, v[e], o[e]);
+            for (int e = 0; e < 8; ++e) o[e] = __builtin_fmaf(p, v[e], o[e]);
         }
+        l = l * corr + psum;
+        m = mn;
     }
     // the 8 key groups (lanes d8, d8 + 8, ..) hold partial sums of the same dims
 #pragma unroll
@@ -291,7 +301,7 @@ __global__ __launch_bounds__(64 * ADW) void attn_decode64_kernel(bf16* y, const 
         o[e] += __shfl_xor(o[e], 16, 64);
         o[e] += __shfl_xor(o[e], 32, 64);
     }
-    l = wave_sum(l);
+    l = wave_sum(l) * 0.125f;  // each key's weight was counted by its eight lanes
     __shared__ float sm[ADW], sl[ADW], so[ADW][HS];
     if (lane == 0) {
         sm[w] = m;
