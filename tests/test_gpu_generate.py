@@ -99,6 +99,24 @@ def test_decode_over_long_contexts_matches_the_oracle_forward(n, steps):
         compare(g, ref[:, n - 1 + i, :], f"position {n - 1 + i}")
 
 
+@pytest.mark.parametrize("batch", [1, 16])
+def test_decode_with_a_wide_vocabulary(batch):
+    # an lm_head of 20011 columns: 1251 blocks of 16 columns, the last one ragged, at one
+    # and at the largest number of rows the skinny product takes
+    from transformer_lm_fwd_amd import Generator
+    m = ModelShape(64, 20011, 1, 2, 128)
+    n, steps = 5, 3
+    w = Workload("gen_wide", m, batch, n + steps, "bf16", "uniform", index=36)
+    announce("gen_wide_vocab", m, batch, n, f"steps={steps}")
+    params = rand_params(m, seed=36)
+    a = gpu_arena(w, params, B=batch, T=n)
+    gen = Generator(a, batch, n + steps)
+    seq, got = greedy_run(gen, prompt_tokens(w, batch, n, seed=300 + batch), steps)
+    ref = oracle_logits(w, params, seq)
+    for i, g in enumerate(got):
+        compare(g, ref[:, n - 1 + i, :], f"position {n - 1 + i}")
+
+
 def test_decode_matches_the_gpu_full_forward_and_stops_at_max_len():
     from transformer_lm_fwd_amd import Generator, Gpt2Error
     m = ModelShape(256, 301, 2, 2, 128)
