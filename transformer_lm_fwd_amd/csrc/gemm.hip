@@ -379,18 +379,19 @@ __device__ __forceinline__ u32x4 frag_read(const bf16* tile, const int* o) {
     }
 }
 
-#ifndef GEMM_GROUP_M
-#define GEMM_GROUP_M 8  // tile rows per group in the per-XCD tile order
-#endif
-
 // Tile of a block.  The grid is one-dimensional, rounded up to a multiple of 8.
 // Blocks are dispatched round-robin over gfx950's 8 XCDs (block i on XCD i % 8),
 // each with its own L2, so XCD x is given the contiguous run x * n/8 .. of the tile
-// sequence, and that sequence walks groups of 8 tile rows column by column: the
+// sequence, and that sequence walks groups of GROUP_M tile rows column by column: the
 // blocks an XCD runs together share A row-tiles and B column-tiles in its L2
 // instead of every XCD fetching every operand tile.  Returns false for padding.
-__device__ __forceinline__ bool tile_of_block(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
-    constexpr int XCDS = 8, GROUP_M = GEMM_GROUP_M;
+// GROUP_M (measured on the step's shapes): 4 for products with a short K (at most
+// 1024 per block) and at most 32 column tiles - the qkv, c_fc and c_fc-input-gradient
+// products, 5-12 % faster than with 8 - and 8 otherwise: the vocabulary-sized products
+// and the split-K weight gradients are 2-3 % slower with 4.
+__device__ __forceinline__ bool tile_of_block(int bid, int tiles_m, int tiles_n, int k_per_block, int& tm, int& tn) {
+    constexpr int XCDS = 8;
+    const int GROUP_M = (k_per_block <= 1024 && tiles_n <= 32) ? 4 : 8;
     const int nt = tiles_m * tiles_n, per = (nt + XCDS - 1) / XCDS;
     const int t = (bid % XCDS) * per + bid / XCDS;
     if (t >= nt) return false;
@@ -426,7 +427,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a, int
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
     int tm, tn;
-    if (!tile_of_block(blockIdx.x, (a.M + BM - 1) / BM, (a.N + BN - 1) / BN, tm, tn)) return;
+    if (!tile_of_block(blockIdx.x, (a.M + BM - 1) / BM, (a.N + BN - 1) / BN, min(a.K, k_per_split), tm, tn)) return;
     const int m0 = tm * BM, n0 = tn * BN;
     const int kbeg = blockIdx.z * k_per_split;
     const int kend = min(a.K, kbeg + k_per_split);
