@@ -67,28 +67,41 @@ def measured_traffic(workload, kernel):
     return out
 
 
-def cpu_baseline(w, params, x, y, budget_s=10.0, T_sample=256, rotary=False):
-    """The float oracle on a bounded sample of the workload: the first T_sample
-    tokens of batch row 0, full forward + backward + AdamW, repeated until about
-    budget_s seconds have passed."""
+def cpu_baseline(w, params, x, y, rotary=False, steps=2, threads_alt=8):
+    """The float oracle on one whole sequence of the workload: batch row 0, all T
+    positions, full forward + backward + AdamW, `steps` steps with one OpenMP thread
+    per host core this process may run on, then one step with `threads_alt` threads
+    (the thread count of the pages' CPU run).  Tokens/s = T / step time; the step's
+    fixed costs (AdamW over every parameter) are spread over T tokens instead of B*T,
+    and attention is at the workload's full length."""
     import oracle
-    T_sample = min(T_sample, w.T)
-    o = oracle.Oracle(w.model, 1, T_sample, "f32")
+    cores = len(os.sched_getaffinity(0))
+    o = oracle.Oracle(w.model, 1, w.T, "f32")
     o.set("params", params)
     if rotary:
         o.set_rotary(True)
-    xs, ys = x[:1, :T_sample], y[:1, :T_sample]
-    steps, t0 = 0, time.perf_counter()
-    while True:
-        o.step(xs, ys, w, steps + 1)
-        steps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or steps >= 20:
-            break
+    xs, ys = x[:1], y[:1]
+
+    def timed(threads, n):
+        oracle.set_num_threads(threads)
+        used = oracle.num_threads()
+        times = []
+        for _ in range(n):
+            t0 = time.perf_counter()
+            o.step(xs, ys, w, len(times) + 1)
+            times.append(time.perf_counter() - t0)
+        return used, min(times), times
+
+    used, best, times = timed(cores, steps)
+    used8, best8, _ = timed(threads_alt, 1)
     o.close()
-    return {"value": steps * T_sample / el, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"float oracle, {steps} full step(s) (fwd+bwd+AdamW) on batch row 0, first {T_sample} "
-                      f"tokens of the {w.name} workload, {el:.1f} s"}
+    oracle.set_num_threads(cores)
+    return {"value": round(w.T / best, 2), "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "sample": f"float oracle, full step (fwd+bwd+AdamW) on batch row 0 of the {w.name} workload "
+                      f"(B=1, T={w.T}), fastest of {steps} steps on {used} threads "
+                      f"({', '.join(f'{t:.2f}' for t in times)} s)",
+            "at_8_threads": {"value": round(w.T / best8, 2), "unit": "tokens/s", "cores": used8,
+                             "step_s": round(best8, 3)}}
 
 
 def main():
@@ -227,6 +240,16 @@ def main():
         roof["algorithmic_bytes_per_launch"] = round(dom["bytes"] / dom["launches"])
         roof.update(measured_traffic(w.name + ("_rotary" if args.rotary else ""), dom["name"]))
 
+    # the matrix cores' sustained rate on this machine (register operands, no memory traffic)
+    probe = {"bf16_32x32x16": round(binding.mfma_peak(binding.MFMA_BF16_32X32X16), 1),
+             "bf16_16x16x32": round(binding.mfma_peak(binding.MFMA_BF16_16X16X32), 1),
+             "mxfp8_32x32x64": round(binding.mfma_peak(binding.MFMA_MXFP8_32X32X64), 1), "unit": "TFLOP/s"}
+    log(f"[bench] MFMA probe: {probe}")
+    measured_peak = probe["bf16_32x32x16"] if w.dtype == "bf16" else None
+    if roof is not None and roof["bound"] == "mfma" and measured_peak:
+        roof["measured_peak"] = measured_peak
+        roof["frac_measured_peak"] = round(roof["achieved"] / measured_peak, 4)
+
     rope = None
     if args.rotary or getattr(m, "block", "gpt2") == "llama":  # the rotary turns and SwiGLU: elementwise, HBM-bound
         rope = {}
@@ -258,6 +281,8 @@ def main():
         "config": {"workload": wname, "B": w.B, "T": w.T, "layers": m.num_layers, "heads": m.num_heads,
                    "channels": m.channels, "vocab": m.vocab_size, "tokens": w.tokens},
         "mfma_peak_frac": round(mfma_frac, 4), "model_tflop_per_step": round(F / 1e12, 4),
+        "mfma_peak_frac_measured": round(F / (ms_per_step / 1e3) / (measured_peak * 1e12), 4)
+        if measured_peak else None, "mfma_probe": probe,
         "loss": round(loss, 5), "roofline": roof, "cpu_baseline": cpu,
     }
     if rope is not None:

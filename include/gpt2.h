@@ -196,6 +196,18 @@ int gpt2_profile(int enable);
  * Errors: GPT2_E_HIP if an event cannot be read. */
 int gpt2_profile_read(gpt2_kernel_stat* out, int32_t max_entries, int32_t* n_entries);
 
+/* Matrix-core rate probe (measurement only).  Launches, on `stream`, a kernel in
+ * which every wave of 8 per SIMD issues independent chains of one MFMA form on
+ * register operands (no memory traffic), times four launches with HIP events,
+ * waits for them, and writes the fastest of the last three as TFLOP/s (dense,
+ * 2 flops per multiply-add) to *tflops: the rate the chip sustains at the clock
+ * it holds under that load, next to which the published peak is the upper bound.
+ *  kind 0: v_mfma_f32_32x32x16_bf16; 1: v_mfma_f32_16x16x32_bf16;
+ *       2: v_mfma_scale_f32_32x32x64_f8f6f4 with E4M3 operands.
+ * Synchronises the stream.  Errors: GPT2_E_INVAL (NULL tflops, unknown kind),
+ * GPT2_E_HIP (launch or event failure). */
+int gpt2_mfma_peak(int32_t kind, double* tflops, void* stream);
+
 /* ---------------------------------------------------------------- generation
  * Incremental next-token prediction with a key/value cache
  * ("GPT-2ベースの3000バイトCで実装されたChatGPTクローン", KVキャッシュ方式: after N tokens

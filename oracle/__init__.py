@@ -80,6 +80,8 @@ def lib():
         L.orc_gelu.argtypes = [vp, vp, i64]
         L.orc_gelu_grad.argtypes = [vp, vp, i64]
         L.orc_num_threads.restype = i32
+        L.orc_set_num_threads.argtypes = [i32]
+        L.orc_set_num_threads.restype = None
         _lib = L
     return _lib
 
@@ -140,6 +142,11 @@ def gelu_grad(x) -> np.ndarray:
 
 def num_threads() -> int:
     return int(lib().orc_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """OpenMP threads for the oracle's later calls (results do not depend on it)."""
+    lib().orc_set_num_threads(int(n))
 
 
 class Oracle:

@@ -934,4 +934,14 @@ int orc_num_threads() {
 #endif
 }
 
+// Threads for the loops that follow (the CPU-baseline timing runs at two counts);
+// results do not depend on it.
+void orc_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 }  // extern "C"

@@ -32,9 +32,14 @@ def maxrel(gpu, ref):
 
 
 def cosine(a, b):
+    """Cosine of two vectors; two all-zero vectors agree (1.0), one all-zero vector
+    against a non-zero one does not (0.0)."""
     a = np.asarray(a, dtype=np.float64).ravel()
     b = np.asarray(b, dtype=np.float64).ravel()
-    return float(a @ b / (np.linalg.norm(a) * np.linalg.norm(b)))
+    na, nb = np.linalg.norm(a), np.linalg.norm(b)
+    if na == 0.0 or nb == 0.0:
+        return 1.0 if na == nb else 0.0
+    return float(a @ b / (na * nb))
 
 
 def to_np(t):

@@ -410,10 +410,35 @@ def test_gpt2_350m_b8t1024_bf16_zipf_full_size():
     assert min(cos_t.values()) >= 0.99
 
 
+def _mem_available_bytes():
+    with open("/proc/meminfo") as f:
+        for line in f:
+            if line.startswith("MemAvailable:"):
+                return int(line.split()[1]) * 1024
+    return 0
+
+
+def _identical_rows_T(w, full_T, margin=48 << 30):
+    """The longest sequence (full_T, else a power-of-two fraction of it, at least 128)
+    whose float-oracle run at B = 1 fits in the host memory available now, next to the
+    test's own copies of parameters and gradients (`margin`)."""
+    import oracle
+    n = synth.num_parameters(w.model)
+    avail = _mem_available_bytes()
+    T = full_T
+    while T > 128:
+        need = 4 * (2 * oracle.num_activations(w.model, 1, T) + 4 * n) + margin
+        if need <= avail:
+            break
+        T //= 2
+    return T, avail
+
+
 def test_gpt2_1558m_b4t1024_bf16_full_size():
     # 48 layers, 25 heads of 64, C = 1600 (GEMM tiles ragged in N and M): sampled
-    # prefix losses, finite gradients, zero-sum dlogits rows, and a decrease after
-    # one AdamW step.
+    # prefix losses, zero-sum dlogits rows, and a decrease after one AdamW step; then
+    # the backward pass with all B rows equal to row 0, whose mean loss and parameter
+    # gradients equal those of that one row, against the float oracle at B = 1.
     b = _b()
     w = synth.WORKLOADS["gpt2_1558m_b4t1024_bf16"]
     announce("gpt2_1558m_b4t1024_bf16 (full size)", w)
@@ -434,3 +459,28 @@ def test_gpt2_1558m_b4t1024_bf16_full_size():
     a.close()
     print(f"1.5B: loss before {loss0:.5f} after one step {loss1:.5f}", flush=True)
     assert loss1 < loss0
+
+    # identical rows: the GPU step at B = 4 and the oracle at B = 1, same T
+    T, avail = _identical_rows_T(w, w.T)
+    print(f"1.5B identical rows at T={T} (host memory available {avail / 2**30:.0f} GiB)", flush=True)
+    xs, ys = np.repeat(x[:1, :T], w.B, axis=0), np.repeat(y[:1, :T], w.B, axis=0)
+    a = gpu_arena(w, params, T=T)
+    a.forward(xs, ys)
+    loss = a.loss()
+    a.backward()
+    g = to_np(a.tensor(b.T_GRADS)).ravel()
+    a.close()
+    torch.cuda.empty_cache()
+    o = oracle_model(w, params, B=1, T=T, prec="f32")
+    ref = o.forward(xs[:1], ys[:1])
+    o.backward()
+    gr = o.get("grads")
+    o.close()
+    cos = cosine(g, gr)
+    cos_t = {k: cosine(v, per_tensor(gr, w.model)[k]) for k, v in per_tensor(g, w.model).items()}
+    print(f"1.5B identical rows: loss gpu={loss:.6f} oracle={ref:.6f}; flat grad cosine={cos:.6f}", flush=True)
+    report("per-tensor cosine (lowest 5)", dict(sorted(cos_t.items(), key=lambda kv: kv[1])[:5]))
+    assert abs(loss - ref) <= BF16_LOSS_ABS
+    assert cos >= BF16_GRAD_COS
+    assert min(cos_t.values()) >= 0.99
+    assert np.isfinite(g).all()

@@ -31,7 +31,8 @@ EXPORTS = ("gpt2_alloc_arena", "gpt2_free_arena", "gpt2_sync_weights", "gpt2_for
            "gpt2_params_permute", "gpt2_checkpoint_write", "gpt2_checkpoint_read", "gpt2_set_position_encoding",
            "gpt2_num_parameters_block", "gpt2_alloc_arena_block",
            "gpt2_mx_attach",
-           "gpt2_set_gemm_format", "gpt2_mx_buffer", "gpt2_mx_quantize", "gpt2_mx_gemm", "gpt2_last_error")
+           "gpt2_set_gemm_format", "gpt2_mx_buffer", "gpt2_mx_quantize", "gpt2_mx_gemm", "gpt2_mfma_peak",
+           "gpt2_last_error")
 GPT2_ORDER_NUMERIC, GPT2_ORDER_LEXICOGRAPHIC = 0, 1
 GPT2_GEMM_BF16, GPT2_GEMM_MXFP8 = 0, 1
 GPT2_POS_LEARNED, GPT2_POS_ROTARY = 0, 1
@@ -82,6 +83,7 @@ def lib():
         L.gpt2_last_error.restype = ctypes.c_char_p
         L.gpt2_profile.argtypes = [ctypes.c_int]
         L.gpt2_profile_read.argtypes = [ctypes.POINTER(gpt2_kernel_stat), i32, ctypes.POINTER(i32)]
+        L.gpt2_mfma_peak.argtypes = [i32, ctypes.POINTER(ctypes.c_double), vp]
         L.gpt2_gen_alloc.argtypes = [vp, i32, i32, vp, sz, ctypes.POINTER(sz), ctypes.POINTER(vp)]
         L.gpt2_gen_free.argtypes = [vp]
         L.gpt2_gen_length.argtypes = [vp]
@@ -151,6 +153,16 @@ def profile_read():
     _check(lib().gpt2_profile_read(arr, n.value, ctypes.byref(n)))
     return [dict(name=r.name.decode(), launches=int(r.launches), total_ms=float(r.total_ms), flops=float(r.flops),
                  bytes=float(r.bytes)) for r in arr[:n.value]]
+
+
+MFMA_BF16_32X32X16, MFMA_BF16_16X16X32, MFMA_MXFP8_32X32X64 = 0, 1, 2
+
+
+def mfma_peak(kind: int = MFMA_BF16_32X32X16, stream=None) -> float:
+    """Sustained TFLOP/s of one MFMA form over the whole chip (gpt2_mfma_peak)."""
+    out = ctypes.c_double(0.0)
+    _check(lib().gpt2_mfma_peak(int(kind), ctypes.byref(out), _stream_ptr(stream)))
+    return float(out.value)
 
 
 def _stream_ptr(stream):

@@ -518,6 +518,20 @@ struct Model {
     // the ln_1 backward), overlapping the backward pass of the layers below; the
     // embeddings and ln_f are updated after the join.
     int backward(const AdamArgs* opt = nullptr) {
+        // The census arrays return to their idle state only when the embedding backward
+        // runs; a pass that stops early (an error) leaves them holding its counts, so the
+        // next pass must clear them first.
+        struct Disarm {
+            gpt2_arena* a;
+            bool done = false;
+            ~Disarm() { if (!done) a->census_armed = false; }
+        } disarm{a};
+        int rc = run_backward(opt);
+        disarm.done = rc == GPT2_OK;
+        return rc;
+    }
+
+    int run_backward(const AdamArgs* opt) {
         int rc;
         if (!a->census_armed) {  // first backward pass on this arena: arm the token census
             CHECK(token_census_reset(at<int>(a, a->census), at<int>(a, a->census) + V, V, s), "census reset");

@@ -4,6 +4,7 @@
 // elapsed times per name.  Recording stops silently after kMaxRecords launches.
 #include <string.h>
 
+#include <algorithm>
 #include <map>
 #include <mutex>
 #include <string>
@@ -103,6 +104,122 @@ int gpt2_profile_read(gpt2_kernel_stat* out, int32_t max_entries, int32_t* n_ent
     }
     if (n_entries) *n_entries = n;
     return GPT2_OK;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- matrix-core rate probe
+// Every wave runs `iters` rounds of NCH independent MFMA chains on register operands
+// (no memory traffic), so the launch measures the sustained issue rate of one MFMA
+// form over the whole chip at the clock it holds under that load.  The accumulators
+// are stored only when `sink` is non-null and the flag is set, which the compiler
+// cannot know, so the chains are not removed.
+namespace gpt2 {
+namespace {
+
+typedef __bf16 bf16x8_p __attribute__((ext_vector_type(8)));
+typedef float f32x16_p __attribute__((ext_vector_type(16)));
+typedef float f32x4_p __attribute__((ext_vector_type(4)));
+typedef int i32x8_p __attribute__((ext_vector_type(8)));
+
+constexpr int NCH = 4;
+
+template <int KIND>
+__global__ __launch_bounds__(256) void mfma_rate_kernel(int iters, float* sink, int store) {
+    const int lane = threadIdx.x & 63;
+    if constexpr (KIND == 0 || KIND == 2) {
+        f32x16_p acc[NCH];
+#pragma unroll
+        for (int c = 0; c < NCH; ++c)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[c][e] = 0.f;
+        if constexpr (KIND == 0) {
+            bf16x8_p a, b;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) a[e] = (__bf16)(float)(lane + e), b[e] = (__bf16)(float)(lane - e);
+            for (int i = 0; i < iters; ++i)
+#pragma unroll
+                for (int c = 0; c < NCH; ++c) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
+        } else {
+            i32x8_p a, b;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) a[e] = 0x38383838 + lane, b[e] = 0x30303030 + e;
+            for (int i = 0; i < iters; ++i)
+#pragma unroll
+                for (int c = 0; c < NCH; ++c)
+                    acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[c], 0, 0, 0, 127, 0, 127);
+        }
+        if (store && sink) {
+            float s = 0.f;
+#pragma unroll
+            for (int c = 0; c < NCH; ++c)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) s += acc[c][e];
+            sink[blockIdx.x * 256 + threadIdx.x] = s;
+        }
+    } else {
+        f32x4_p acc[NCH];
+#pragma unroll
+        for (int c = 0; c < NCH; ++c)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[c][e] = 0.f;
+        bf16x8_p a, b;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a[e] = (__bf16)(float)(lane + e), b[e] = (__bf16)(float)(lane - e);
+        for (int i = 0; i < iters; ++i)
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[c], 0, 0, 0);
+        if (store && sink) {
+            float s = 0.f;
+#pragma unroll
+            for (int c = 0; c < NCH; ++c)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) s += acc[c][e];
+            sink[blockIdx.x * 256 + threadIdx.x] = s;
+        }
+    }
+}
+
+}  // namespace
+}  // namespace gpt2
+
+extern "C" {
+
+int gpt2_mfma_peak(int32_t kind, double* tflops, void* stream) {
+    using namespace gpt2;
+    if (!tflops) return report_error(GPT2_E_INVAL, "tflops is NULL");
+    if (kind < 0 || kind > 2) return report_error(GPT2_E_INVAL, "kind must be 0 (bf16 32x32x16), 1 (bf16 16x16x32) or 2 (MX fp8 32x32x64)");
+    hipStream_t s = (hipStream_t)stream;
+    // 8 blocks of 4 waves per CU (256 CUs): 8 waves per SIMD
+    const int blocks = 2048, iters = kind == 2 ? 1024 : 2048;
+    const double flops_per_mfma = kind == 0 ? 32768.0 : kind == 1 ? 16384.0 : 131072.0;
+    const double flops = flops_per_mfma * NCH * iters * (blocks * 4.0);
+    hipEvent_t e0, e1;
+    if (hipEventCreate(&e0) != hipSuccess) return report_error(GPT2_E_HIP, "hipEventCreate");
+    if (hipEventCreate(&e1) != hipSuccess) {
+        hipEventDestroy(e0);
+        return report_error(GPT2_E_HIP, "hipEventCreate");
+    }
+    double best = 0.0;
+    int rc = GPT2_OK;
+    for (int rep = 0; rep < 4 && rc == GPT2_OK; ++rep) {  // the first launch warms the clock up
+        hipEventRecord(e0, s);
+        if (kind == 0) hipLaunchKernelGGL(mfma_rate_kernel<0>, dim3(blocks), dim3(256), 0, s, iters, (float*)nullptr, 0);
+        else if (kind == 1) hipLaunchKernelGGL(mfma_rate_kernel<1>, dim3(blocks), dim3(256), 0, s, iters, (float*)nullptr, 0);
+        else hipLaunchKernelGGL(mfma_rate_kernel<2>, dim3(blocks), dim3(256), 0, s, iters, (float*)nullptr, 0);
+        hipEventRecord(e1, s);
+        float ms = 0.f;
+        if (hipGetLastError() != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
+            hipEventElapsedTime(&ms, e0, e1) != hipSuccess) {
+            rc = report_error(GPT2_E_HIP, "mfma probe launch failed");
+            break;
+        }
+        if (rep > 0 && ms > 0.f) best = std::max(best, flops / (ms * 1e-3) / 1e12);
+    }
+    hipEventDestroy(e0);
+    hipEventDestroy(e1);
+    *tflops = best;
+    return rc;
 }
 
 }  // extern "C"
