@@ -197,7 +197,7 @@ int gpt2_profile(int enable);
 int gpt2_profile_read(gpt2_kernel_stat* out, int32_t max_entries, int32_t* n_entries);
 
 /* Matrix-core rate probe (measurement only).  Launches, on `stream`, a kernel in
- * which every wave of 8 per SIMD issues independent chains of one MFMA form on
+ * which every wave of 2 per SIMD issues independent chains of one MFMA form on
  * register operands (no memory traffic), times four launches with HIP events,
  * waits for them, and writes the fastest of the last three as TFLOP/s (dense,
  * 2 flops per multiply-add) to *tflops: the rate the chip sustains at the clock

@@ -144,10 +144,10 @@ def test_gpt2_124m_b4t64_fp32_step_and_ten_step_losses():
     print("ten-step losses gpu   :", " ".join(f"{v:.6f}" for v in losses))
     print("ten-step losses oracle:", " ".join(f"{v:.6f}" for v in gold))
     print("relative errors       :", " ".join(f"{v:.2g}" for v in rel), flush=True)
-    assert rel[0] <= FP32_LOSS_REL
-    # Adam's early, sign-like updates amplify rounding differences step by step;
-    # later steps keep a looser bound, and the overall decrease must hold.
-    assert max(rel) <= 1e-3
+    # The stated fp32 bound holds at every step (measured: at most 5.3e-6, at step 6).
+    # The loss is not monotone here on either side (the oracle rises from step 6 to 7
+    # on these synthetic inputs); the overall decrease must hold.
+    assert max(rel) <= FP32_LOSS_REL
     assert losses[-1] < losses[0] - 5.0
 
 

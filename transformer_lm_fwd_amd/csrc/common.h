@@ -78,20 +78,27 @@ __device__ __forceinline__ float wave_max(float v) {
 
 // GELU, tanh form (the formula quoted in the comment thread of the 3000-byte C
 // GPT-2 page): g(x) = x/2 (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))).  The
-// identity (1 + tanh u)/2 = 1/(1 + exp(-2u)) turns it into one exponential; the
-// reciprocal is the hardware's (v_rcp_f32, about 1 ulp) rather than a full division.
+// identity (1 + tanh u)/2 = 1/(1 + exp(-2u)) = 1/(1 + 2^a), a = -2 u log2(e), turns
+// it into one base-2 exponential (v_exp_f32) and one reciprocal (v_rcp_f32, about
+// 1 ulp), with a = x (k0 + k1 x^2) evaluated as one multiply-add and a multiply.
+// Far in either tail 2^a is 0 or +inf, and g is x or -0, its limits.
 #define GPT2_SQRT_2_OVER_PI 0.7978845608028654f
+#define GPT2_GELU_K0 (-2.0f * 1.4426950408889634f * GPT2_SQRT_2_OVER_PI)
+#define GPT2_GELU_K1 (GPT2_GELU_K0 * 0.044715f)
 __device__ __forceinline__ float gelu_fwd(float x) {
-    float u = GPT2_SQRT_2_OVER_PI * (x + 0.044715f * x * x * x);
-    return x * __builtin_amdgcn_rcpf(1.0f + __expf(-2.0f * u));
+    const float a = x * __builtin_fmaf(x * x, GPT2_GELU_K1, GPT2_GELU_K0);
+    return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(a));
 }
 // d/dx g(x) = s + x s (1 - s) 2 u'(x),  s = 1/(1 + exp(-2u)),
-// u'(x) = sqrt(2/pi) (1 + 3 * 0.044715 x^2)  (since (1+tanh u)/2 = s and tanh' = 1 - tanh^2).
+// u'(x) = sqrt(2/pi) (1 + 3 * 0.044715 x^2)  (since (1+tanh u)/2 = s and tanh' = 1 - tanh^2),
+// evaluated as s (1 + w q) with w = x (1 - s) = x - s x and q = 2 u'(x).
 __device__ __forceinline__ float gelu_bwd(float x) {
-    float u = GPT2_SQRT_2_OVER_PI * (x + 0.044715f * x * x * x);
-    float s = __builtin_amdgcn_rcpf(1.0f + __expf(-2.0f * u));
-    float du = GPT2_SQRT_2_OVER_PI * (1.0f + 3.0f * 0.044715f * x * x);
-    return s + x * s * (1.0f - s) * 2.0f * du;
+    const float x2 = x * x;
+    const float a = x * __builtin_fmaf(x2, GPT2_GELU_K1, GPT2_GELU_K0);
+    const float s = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(a));
+    const float q = __builtin_fmaf(x2, 2.0f * GPT2_SQRT_2_OVER_PI * 3.0f * 0.044715f, 2.0f * GPT2_SQRT_2_OVER_PI);
+    const float w = __builtin_fmaf(-s, x, x);
+    return s * __builtin_fmaf(w, q, 1.0f);
 }
 
 }  // namespace gpt2

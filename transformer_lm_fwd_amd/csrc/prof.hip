@@ -190,8 +190,9 @@ int gpt2_mfma_peak(int32_t kind, double* tflops, void* stream) {
     if (!tflops) return report_error(GPT2_E_INVAL, "tflops is NULL");
     if (kind < 0 || kind > 2) return report_error(GPT2_E_INVAL, "kind must be 0 (bf16 32x32x16), 1 (bf16 16x16x32) or 2 (MX fp8 32x32x64)");
     hipStream_t s = (hipStream_t)stream;
-    // 8 blocks of 4 waves per CU (256 CUs): 8 waves per SIMD
-    const int blocks = 2048, iters = kind == 2 ? 1024 : 2048;
+    // 2 blocks of 4 waves per CU (256 CUs): two waves per SIMD, each with NCH
+    // independent chains (more waves per SIMD only add issue contention)
+    const int blocks = 512, iters = kind == 2 ? 4096 : 8192;
     const double flops_per_mfma = kind == 0 ? 32768.0 : kind == 1 ? 16384.0 : 131072.0;
     const double flops = flops_per_mfma * NCH * iters * (blocks * 4.0);
     hipEvent_t e0, e1;
