@@ -254,6 +254,24 @@ int gpt2_gen_prefill(gpt2_gen* gen, const int32_t* d_tokens, int32_t n, float* d
  * GPT2_E_SIZE (length == max_len), GPT2_E_HIP. */
 int gpt2_gen_decode(gpt2_gen* gen, const int32_t* d_tokens, float* d_logits, void* stream);
 
+/* Allocation-free decode step, for callers that cannot allocate device memory or
+ * bring a workspace: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, results and errors as gpt2_gen_decode (the same
+ * kernels, bit-identical logits), but the step's row buffers (residual rows, attention
+ * and GELU outputs, final LayerNorm rows and statistics: about 20 * batch * channels
+ * bytes) live in a static device array of the library, 384 KiB on each GPU, held
+ * until the process ends, instead of in the generation state's memory (its key/value
+ * cache is still used).  The array is looked up on the calling thread's current
+ * device, which must be the device of `g`'s memory and of `stream`; the first call on
+ * a device looks up that device's copy.  Every call on one GPU shares its array:
+ * calls that overlap on one GPU (other streams, other threads) race and must be
+ * serialised by the caller.  Nothing in the array needs clearing: each step writes
+ * every row it reads.  Allocates nothing (no hipMalloc / hipFree).
+ * Errors: as gpt2_gen_decode; GPT2_E_SIZE when batch * channels needs more than the
+ * array holds (batch * channels above about 19660), checked before any GPU call;
+ * GPT2_E_HIP if the array's device address cannot be looked up. */
+int gpt2_gen_decode_noalloc(gpt2_gen* g, const int32_t* d_tokens, float* d_logits, void* stream);
+
 /* Top-k sampling on the host ("GPT-2 from scratch with torch", 生成样本: keep the k
  * highest logits, softmax over them, draw one token).  For each of `rows` rows of
  * host fp32 logits (row stride ld >= V): rank the tokens by logit (equal logits: the

@@ -176,3 +176,32 @@ def test_generation_state_validation_without_touching_memory():
         assert lib.gpt2_gen_length(None) == -1
     finally:
         lib.gpt2_free_arena(h)
+
+
+def test_decode_noalloc_rejects_rows_beyond_its_static_array_without_touching_memory():
+    # C = 1600 (head size 64): batch 16 needs about 512 KiB of decode rows, more than the
+    # 384 KiB static array, and is refused before any GPU call; batch 12 fits and then
+    # fails the state check (no prefill yet).
+    b = _lib()
+    lib = b.lib()
+    m = synth.ModelShape(16, 301, 1, 25, 1600)
+    cfg = b.make_config(m)
+    h = ctypes.c_void_p()
+    n = b.arena_bytes(m, 16, 4, b.GPT2_BF16)
+    assert lib.gpt2_alloc_arena(ctypes.byref(cfg), 16, 4, 1, ctypes.c_void_p(1 << 40), n, None, ctypes.byref(h)) == 0
+    try:
+        fake = ctypes.c_void_p(1 << 42)
+        assert lib.gpt2_gen_decode_noalloc(None, fake, fake, None) == -1
+        for batch, rc in ((16, -2), (12, -4)):
+            need = ctypes.c_size_t()
+            assert lib.gpt2_gen_alloc(h, batch, 4, None, 0, ctypes.byref(need), None) == 0
+            g = ctypes.c_void_p()
+            assert lib.gpt2_gen_alloc(h, batch, 4, ctypes.c_void_p(1 << 41), need.value, None, ctypes.byref(g)) == 0
+            try:
+                assert lib.gpt2_gen_decode_noalloc(g, fake, fake, None) == rc, batch
+                if rc == -2:
+                    assert b"static scratch" in lib.gpt2_last_error()
+            finally:
+                lib.gpt2_gen_free(g)
+    finally:
+        lib.gpt2_free_arena(h)

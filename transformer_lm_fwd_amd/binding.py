@@ -31,7 +31,7 @@ EXPORTS = ("gpt2_alloc_arena", "gpt2_free_arena", "gpt2_sync_weights", "gpt2_for
            "gpt2_params_permute", "gpt2_checkpoint_write", "gpt2_checkpoint_read", "gpt2_set_position_encoding",
            "gpt2_num_parameters_block", "gpt2_alloc_arena_block",
            "gpt2_mx_attach",
-           "gpt2_set_gemm_format", "gpt2_mx_buffer", "gpt2_mx_quantize", "gpt2_mx_gemm", "gpt2_mfma_peak",
+           "gpt2_set_gemm_format", "gpt2_mx_buffer", "gpt2_mx_quantize", "gpt2_mx_gemm", "gpt2_mfma_peak", "gpt2_gen_decode_noalloc",
            "gpt2_last_error")
 GPT2_ORDER_NUMERIC, GPT2_ORDER_LEXICOGRAPHIC = 0, 1
 GPT2_GEMM_BF16, GPT2_GEMM_MXFP8 = 0, 1
@@ -89,6 +89,7 @@ def lib():
         L.gpt2_gen_length.argtypes = [vp]
         L.gpt2_gen_prefill.argtypes = [vp, vp, i32, vp, vp]
         L.gpt2_gen_decode.argtypes = [vp, vp, vp, vp]
+        L.gpt2_gen_decode_noalloc.argtypes = [vp, vp, vp, vp]
         L.gpt2_sample_topk.argtypes = [vp, i32, i32, i64, i32, f32, vp, vp]
         cp = ctypes.c_char_p
         L.gpt2_tokens_count.argtypes = [cp]

@@ -6,6 +6,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -699,6 +700,139 @@ struct Model {
 
 }  // namespace
 
+namespace {
+
+// Row buffers of one decode step, as byte offsets from `base`: the residual rows (three
+// in rotation), the attention output, the GELU output, the final LayerNorm output and
+// its statistics.
+struct DecodeRows {
+    char* base;
+    size_t res[3], atty, fchg, lnf, stats;
+};
+
+DecodeRows decode_rows_layout(int batch, int C, char* base, size_t* bytes) {
+    DecodeRows r{};
+    r.base = base;
+    size_t o = 0;
+    auto take = [&](size_t n) {
+        const size_t at = o;
+        o = align_up(o + n);
+        return at;
+    };
+    const size_t Bg = batch, Cs = C;
+    for (auto& x : r.res) x = take(Bg * Cs * 2);
+    r.atty = take(Bg * Cs * 2);
+    r.fchg = take(Bg * 4 * Cs * 2);
+    r.lnf = take(Bg * Cs * 2);
+    r.stats = take(Bg * 2 * 4);
+    if (bytes) *bytes = o;
+    return r;
+}
+
+// Static decode scratch of gpt2_gen_decode_noalloc: one copy per GPU, held until the
+// process ends.  Host code never uses the array's name as an address (on the host it
+// is a stand-in, not device memory): each device's address is looked up once with
+// hipGetSymbolAddress and kept here.
+constexpr size_t kDecodeScratchBytes = 384 * 1024;
+__device__ __align__(256) char scratch[kDecodeScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch address on the calling thread's current device (looked up on first use).
+int decode_scratch_ptr(char** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(GPT2_E_HIP, "hipGetDevice failed");
+    if (dev < 0 || dev >= kMaxDevices) return fail(GPT2_E_INVAL, "device index out of range for the static scratch");
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(GPT2_E_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+        g_scratch_ptr[dev] = (char*)p;
+    }
+    *out = g_scratch_ptr[dev];
+    return GPT2_OK;
+}
+
+int decode_check(gpt2_gen* g, const int32_t* d_tokens, float* d_logits) {
+    if (!g || !d_tokens || !d_logits) return fail(GPT2_E_INVAL, "generation state, tokens and logits are required");
+    if (!g->ready) return fail(GPT2_E_STATE, "decode needs a preceding prefill");
+    if (g->len >= g->max_len) return fail(GPT2_E_SIZE, "the cache is full (length == max_len)");
+    return GPT2_OK;
+}
+
+// One decode step with the step's row buffers at `rows` (the generation state's own
+// memory, or the static scratch of gpt2_gen_decode_noalloc); arguments already checked.
+int decode_step(gpt2_gen* g, const int32_t* d_tokens, float* d_logits, hipStream_t s, const DecodeRows& rows) {
+    gpt2_arena* a = g->a;
+    const int C = a->cfg.channels, L = a->cfg.num_layers, NH = a->cfg.num_heads, V = a->cfg.vocab_size;
+    const int Bg = g->batch, t = g->len;
+    const int64_t C3 = 3 * (int64_t)C, row = (int64_t)g->max_len * C3;
+    auto buf = [&](size_t off) { return (bf16*)(g->base + off); };          // the key/value cache
+    auto rb = [&](size_t off) { return (bf16*)(rows.base + off); };          // the step's rows
+    const float* master = at<float>(a, a->params);
+    const bf16* w16 = at<bf16>(a, a->params16);
+    auto lp = [&](int l, int i) { return a->o_layer[l * P_N + i]; };
+    // x' = LayerNorm(x) with the gains / shifts at `ln` (if >= 0), then x' W^T
+    auto skinny = [&](const bf16* x, int64_t ldx, int64_t ln, int64_t woff, int N, int K, void* Cout, int64_t ldc,
+                      bf16* C2, const bf16* R, const float* bias, int epi) -> int {
+        SkinnyArgs k{};
+        k.x = x; k.ldx = ldx; k.W = w16 + woff; k.ldw = K; k.C = Cout; k.ldc = ldc; k.C2 = C2;
+        k.R = R; k.ldr = C; k.bias = bias; k.M = Bg; k.N = N; k.K = K;
+        if (ln >= 0) {
+            k.ln_w = master + ln;
+            k.ln_b = master + ln + K;
+        }
+        return hip_check(skinny_gemm(k, epi, s), "skinny gemm");
+    };
+    int rc;
+    // x = wte[token] + wpe[t] for the one new row of every sequence
+    const bool rot = a->pos_enc == GPT2_POS_ROTARY;
+    CHECK(encoder_forward<bf16>(rb(rows.res[0]), d_tokens, master + a->o_wte, rot ? nullptr : master + a->o_wpe, Bg, 1,
+                                C, s, t),
+          "encoder");
+    int cur = 0;
+    for (int l = 0; l < L; ++l) {
+        bf16* xin = rb(rows.res[cur]);
+        bf16* res2 = rb(rows.res[(cur + 1) % 3]);
+        bf16* res3 = rb(rows.res[(cur + 2) % 3]);
+        bf16* cache = buf(g->cache) + (int64_t)l * Bg * row;
+        // ln_1, then q|k|v of the new rows straight into cache row t of each sequence
+        if ((rc = skinny(xin, C, lp(l, P_LN1W), lp(l, P_QKVW), 3 * C, C, cache + (int64_t)t * C3, row, nullptr,
+                         nullptr, master + lp(l, P_QKVB), EPI_BIAS)))
+            return rc;
+        if (rot)  // the new rows' q and k, all at position t
+            CHECK(rope_apply<bf16>(cache + (int64_t)t * C3, row, Bg, 2 * C, C / NH, 1, t, at<float2>(a, a->rope), false,
+                                   s),
+                  "rope");
+        CHECK(attention_decode(rb(rows.atty), cache, Bg, t + 1, C, NH, row, s), "attention");
+        if ((rc = skinny(rb(rows.atty), C, -1, lp(l, P_PROJW), C, C, res2, C, nullptr, xin, master + lp(l, P_PROJB),
+                         EPI_BIAS_RES)))
+            return rc;
+        // ln_2, c_fc + GELU
+        if ((rc = skinny(res2, C, lp(l, P_LN2W), lp(l, P_FCW), 4 * C, C, nullptr, 4 * C, rb(rows.fchg), nullptr,
+                         master + lp(l, P_FCB), EPI_BIAS_GELU)))
+            return rc;
+        if ((rc = skinny(rb(rows.fchg), 4 * C, -1, lp(l, P_FCPW), C, 4 * C, res3, C, nullptr, res2,
+                         master + lp(l, P_FCPB), EPI_BIAS_RES)))
+            return rc;
+        cur = (cur + 2) % 3;
+    }
+    // ln_f on its own (the lm_head product has thousands of blocks), then the next-token
+    // logits (tied lm_head), fp32 [batch, V]
+    CHECK(layernorm_forward<bf16>(rb(rows.lnf), (float*)(rows.base + rows.stats), rb(rows.res[cur]), master + a->o_lnfw,
+                                  master + a->o_lnfb, Bg, C, s),
+          "lnf");
+    if ((rc = skinny(rb(rows.lnf), C, -1, a->o_wte, V, C, d_logits, V, nullptr, nullptr, nullptr, EPI_F32))) return rc;
+    g->len = t + 1;
+    return GPT2_OK;
+}
+
+
+}  // namespace
+
 extern "C" {
 
 const char* gpt2_last_error(void) { return g_error.c_str(); }
@@ -1050,71 +1184,27 @@ int gpt2_gen_prefill(gpt2_gen* g, const int32_t* d_tokens, int32_t n, float* d_l
 }
 
 int gpt2_gen_decode(gpt2_gen* g, const int32_t* d_tokens, float* d_logits, void* stream) {
-    if (!g || !d_tokens || !d_logits) return fail(GPT2_E_INVAL, "generation state, tokens and logits are required");
-    if (!g->ready) return fail(GPT2_E_STATE, "decode needs a preceding prefill");
-    if (g->len >= g->max_len) return fail(GPT2_E_SIZE, "the cache is full (length == max_len)");
-    gpt2_arena* a = g->a;
-    hipStream_t s = (hipStream_t)stream;
-    const int C = a->cfg.channels, L = a->cfg.num_layers, NH = a->cfg.num_heads, V = a->cfg.vocab_size;
-    const int Bg = g->batch, t = g->len;
-    const int64_t C3 = 3 * (int64_t)C, row = (int64_t)g->max_len * C3;
-    auto buf = [&](size_t off) { return (bf16*)(g->base + off); };
-    const float* master = at<float>(a, a->params);
-    const bf16* w16 = at<bf16>(a, a->params16);
-    auto lp = [&](int l, int i) { return a->o_layer[l * P_N + i]; };
-    // x' = LayerNorm(x) with the gains / shifts at `ln` (if >= 0), then x' W^T
-    auto skinny = [&](const bf16* x, int64_t ldx, int64_t ln, int64_t woff, int N, int K, void* Cout, int64_t ldc,
-                      bf16* C2, const bf16* R, const float* bias, int epi) -> int {
-        SkinnyArgs k{};
-        k.x = x; k.ldx = ldx; k.W = w16 + woff; k.ldw = K; k.C = Cout; k.ldc = ldc; k.C2 = C2;
-        k.R = R; k.ldr = C; k.bias = bias; k.M = Bg; k.N = N; k.K = K;
-        if (ln >= 0) {
-            k.ln_w = master + ln;
-            k.ln_b = master + ln + K;
-        }
-        return hip_check(skinny_gemm(k, epi, s), "skinny gemm");
-    };
-    int rc;
-    // x = wte[token] + wpe[t] for the one new row of every sequence
-    const bool rot = a->pos_enc == GPT2_POS_ROTARY;
-    CHECK(encoder_forward<bf16>(buf(g->res[0]), d_tokens, master + a->o_wte, rot ? nullptr : master + a->o_wpe, Bg, 1,
-                                C, s, t),
-          "encoder");
-    int cur = 0;
-    for (int l = 0; l < L; ++l) {
-        bf16* xin = buf(g->res[cur]);
-        bf16* res2 = buf(g->res[(cur + 1) % 3]);
-        bf16* res3 = buf(g->res[(cur + 2) % 3]);
-        bf16* cache = buf(g->cache) + (int64_t)l * Bg * row;
-        // ln_1, then q|k|v of the new rows straight into cache row t of each sequence
-        if ((rc = skinny(xin, C, lp(l, P_LN1W), lp(l, P_QKVW), 3 * C, C, cache + (int64_t)t * C3, row, nullptr,
-                         nullptr, master + lp(l, P_QKVB), EPI_BIAS)))
-            return rc;
-        if (rot)  // the new rows' q and k, all at position t
-            CHECK(rope_apply<bf16>(cache + (int64_t)t * C3, row, Bg, 2 * C, C / NH, 1, t, at<float2>(a, a->rope), false,
-                                   s),
-                  "rope");
-        CHECK(attention_decode(buf(g->atty), cache, Bg, t + 1, C, NH, row, s), "attention");
-        if ((rc = skinny(buf(g->atty), C, -1, lp(l, P_PROJW), C, C, res2, C, nullptr, xin, master + lp(l, P_PROJB),
-                         EPI_BIAS_RES)))
-            return rc;
-        // ln_2, c_fc + GELU
-        if ((rc = skinny(res2, C, lp(l, P_LN2W), lp(l, P_FCW), 4 * C, C, nullptr, 4 * C, buf(g->fchg), nullptr,
-                         master + lp(l, P_FCB), EPI_BIAS_GELU)))
-            return rc;
-        if ((rc = skinny(buf(g->fchg), 4 * C, -1, lp(l, P_FCPW), C, 4 * C, res3, C, nullptr, res2,
-                         master + lp(l, P_FCPB), EPI_BIAS_RES)))
-            return rc;
-        cur = (cur + 2) % 3;
-    }
-    // ln_f on its own (the lm_head product has thousands of blocks), then the next-token
-    // logits (tied lm_head), fp32 [batch, V]
-    CHECK(layernorm_forward<bf16>(buf(g->lnf), (float*)(g->base + g->stats), buf(g->res[cur]), master + a->o_lnfw,
-                                  master + a->o_lnfb, Bg, C, s),
-          "lnf");
-    if ((rc = skinny(buf(g->lnf), C, -1, a->o_wte, V, C, d_logits, V, nullptr, nullptr, nullptr, EPI_F32))) return rc;
-    g->len = t + 1;
-    return GPT2_OK;
+    int rc = decode_check(g, d_tokens, d_logits);
+    if (rc) return rc;
+    const DecodeRows rows{g->base, {g->res[0], g->res[1], g->res[2]}, g->atty, g->fchg, g->lnf, g->stats};
+    return decode_step(g, d_tokens, d_logits, (hipStream_t)stream, rows);
+}
+
+int gpt2_gen_decode_noalloc(gpt2_gen* g, const int32_t* d_tokens, float* d_logits, void* stream) {
+    if (!g) return fail(GPT2_E_INVAL, "generation state is NULL");
+    size_t need = 0;
+    const DecodeRows lay = decode_rows_layout(g->batch, g->a->cfg.channels, nullptr, &need);
+    if (need > kDecodeScratchBytes)
+        return fail(GPT2_E_SIZE, "decode rows need " + std::to_string(need) + " bytes, more than the " +
+                                     std::to_string(kDecodeScratchBytes) +
+                                     "-byte static scratch (batch * channels at most about 19660)");
+    int rc = decode_check(g, d_tokens, d_logits);
+    if (rc) return rc;
+    char* ptr = nullptr;
+    if ((rc = decode_scratch_ptr(&ptr))) return rc;
+    DecodeRows rows = lay;
+    rows.base = ptr;
+    return decode_step(g, d_tokens, d_logits, (hipStream_t)stream, rows);
 }
 
 // Host-side top-k sampling ("GPT-2 from scratch with torch", 生成样本): keep the k largest
