@@ -525,40 +525,56 @@ __device__ __forceinline__ void online_merge(float& m, float& s, float m2, float
 
 // The first REG 16-byte vectors of each thread's share of the row stay in registers
 // between the two passes, so the logits are read from memory once (rows up to
-// REG * 1024 vectors; longer rows re-read the rest).
+// REG * 1024 vectors; longer rows re-read the rest).  Each thread first takes the
+// maximum of its values, then sums 2^((z - m) log2 e) with one v_exp_f32 per value
+// (log2 e folded into a multiply-add); the block merges the (max, sum) pairs.  The
+// gradient pass spends one more exponential per value, with 1/(B*T) folded into the
+// exponent's offset; the -1/(B*T) of the target column is added by the one thread
+// whose vector holds it.
 template <class T>
 __global__ __launch_bounds__(1024) void crossentropy_kernel(T* logits, float* losses, const int32_t* targets, int V,
                                                             int64_t ldz, float dscale) {
     constexpr int KV = Vec16<T>::N;
     constexpr int REG = 64 / KV;  // 64 values per thread: V up to 65536
+    constexpr float L2E = 1.4426950408889634f;
     const int row = blockIdx.x;
     T* z = logits + (int64_t)row * ldz;
     const int nvec = V / KV;  // full 16-byte vectors inside [0, V)
     const int y = targets[row];
     const float zy = to_f32(z[y]);
-    float m = -INFINITY, s = 0.f;
     u32x4 keep[REG];
 #pragma unroll
     for (int r = 0; r < REG; ++r) {
         const int i = threadIdx.x + r * 1024;
         if (i < nvec) keep[r] = ld16(z + i * KV);
     }
-    auto absorb = [&](const u32x4& raw) {
+    // this thread's maximum
+    float m = -INFINITY;
+    auto vmax = [&](const u32x4& raw) {
         float v[KV];
         unpack16<T>(raw, v);
-        float mx = v[0];
 #pragma unroll
-        for (int e = 1; e < KV; ++e) mx = fmaxf(mx, v[e]);
-        float ss = 0.f;
-#pragma unroll
-        for (int e = 0; e < KV; ++e) ss += __expf(v[e] - mx);
-        online_merge(m, s, mx, ss);
+        for (int e = 0; e < KV; ++e) m = fmaxf(m, v[e]);
     };
 #pragma unroll
     for (int r = 0; r < REG; ++r)
-        if (threadIdx.x + r * 1024 < nvec) absorb(keep[r]);
-    for (int i = threadIdx.x + REG * 1024; i < nvec; i += 1024) absorb(ld16(z + i * KV));
-    for (int i = nvec * KV + threadIdx.x; i < V; i += 1024) online_merge(m, s, to_f32(z[i]), 1.f);
+        if (threadIdx.x + r * 1024 < nvec) vmax(keep[r]);
+    for (int i = threadIdx.x + REG * 1024; i < nvec; i += 1024) vmax(ld16(z + i * KV));
+    for (int i = nvec * KV + threadIdx.x; i < V; i += 1024) m = fmaxf(m, to_f32(z[i]));
+    // sum of 2^((z - m) log2 e) over this thread's values
+    float s = 0.f;
+    const float mo = m == -INFINITY ? 0.f : -m * L2E;
+    auto vsum = [&](const u32x4& raw) {
+        float v[KV];
+        unpack16<T>(raw, v);
+#pragma unroll
+        for (int e = 0; e < KV; ++e) s += __builtin_amdgcn_exp2f(__builtin_fmaf(v[e], L2E, mo));
+    };
+#pragma unroll
+    for (int r = 0; r < REG; ++r)
+        if (threadIdx.x + r * 1024 < nvec) vsum(keep[r]);
+    for (int i = threadIdx.x + REG * 1024; i < nvec; i += 1024) vsum(ld16(z + i * KV));
+    for (int i = nvec * KV + threadIdx.x; i < V; i += 1024) s += __builtin_amdgcn_exp2f(__builtin_fmaf(to_f32(z[i]), L2E, mo));
     // block reduction of (m, s)
     __shared__ float sm[16], ss_[16];
 #pragma unroll
@@ -573,13 +589,17 @@ __global__ __launch_bounds__(1024) void crossentropy_kernel(T* logits, float* lo
     for (int w2 = 1; w2 < 16; ++w2) online_merge(m, s, sm[w2], ss_[w2]);
     const float lse = m + __logf(s);
     if (threadIdx.x == 0) losses[row] = lse - zy;
+    // dz = 2^(z log2 e - (lse log2 e - log2 dscale)) - [col == y] dscale
+    const float go = -(lse * L2E - __log2f(dscale));
     auto grad = [&](const u32x4& raw, int i) {
         float v[KV];
         unpack16<T>(raw, v);
 #pragma unroll
-        for (int e = 0; e < KV; ++e) {
-            const int col = i * KV + e;
-            v[e] = (__expf(v[e] - lse) - (col == y ? 1.f : 0.f)) * dscale;
+        for (int e = 0; e < KV; ++e) v[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(v[e], L2E, go));
+        if ((unsigned)(y - i * KV) < (unsigned)KV) {
+#pragma unroll
+            for (int e = 0; e < KV; ++e)
+                if (i * KV + e == y) v[e] -= dscale;
         }
         st16(z + i * KV, pack16<T>(v));
     };
@@ -591,7 +611,7 @@ __global__ __launch_bounds__(1024) void crossentropy_kernel(T* logits, float* lo
     for (int i = threadIdx.x + REG * 1024; i < nvec; i += 1024) grad(ld16(z + i * KV), i);
     for (int i = nvec * KV + threadIdx.x; i < (int)ldz; i += 1024) {
         float g = 0.f;
-        if (i < V) g = (__expf(to_f32(z[i]) - lse) - (i == y ? 1.f : 0.f)) * dscale;
+        if (i < V) g = __builtin_amdgcn_exp2f(__builtin_fmaf(to_f32(z[i]), L2E, go)) - (i == y ? dscale : 0.f);
         z[i] = from_f32<T>(g);
     }
 }
