@@ -80,6 +80,9 @@ def lib():
         L.orc_gelu.argtypes = [vp, vp, i64]
         L.orc_gelu_grad.argtypes = [vp, vp, i64]
         L.orc_num_threads.restype = i32
+        L.orc_set_mx.argtypes = [vp, ctypes.c_int]
+        L.orc_mx_roundtrip.argtypes = [vp, vp, i64, ctypes.c_int]
+        L.orc_mx_roundtrip.restype = None
         L.orc_set_num_threads.argtypes = [i32]
         L.orc_set_num_threads.restype = None
         _lib = L
@@ -137,6 +140,16 @@ def gelu_grad(x) -> np.ndarray:
     x = np.ascontiguousarray(x, dtype=np.float64)
     y = np.empty_like(x)
     lib().orc_gelu_grad(_ptr(x), _ptr(y), x.size)
+    return y
+
+
+def mx_roundtrip(x) -> np.ndarray:
+    """x [rows, K] rounded to bf16, MX-encoded in blocks of 32 along K and decoded
+    (float64; the operand an MX-mode product multiplies)."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    rows, K = x.shape
+    y = np.empty_like(x)
+    lib().orc_mx_roundtrip(_ptr(x), _ptr(y), rows, K)
     return y
 
 
@@ -214,6 +227,12 @@ class Oracle:
     def set_rotary(self, on: bool = True, base: float = 10000.0):
         """Rotary position embedding (RoFormer) instead of the learned wpe."""
         if lib().orc_set_rotary(self.h, 1 if on else 0, float(base)):
+            raise ValueError(lib().orc_last_error().decode())
+
+    def set_mx(self, on: bool = True):
+        """MX FP8 operands (bf16 values through the E4M3 / E8M0 block encoding) for the
+        forward pass's block and lm_head products; the backward pass is unchanged."""
+        if lib().orc_set_mx(self.h, 1 if on else 0):
             raise ValueError(lib().orc_last_error().decode())
 
     def backward(self):

@@ -277,6 +277,78 @@ static void matmul_forward(R* out, const R* inp, const R* w, const R* bias, int6
     }
 }
 
+// ----------------------------------------------------------------------------- MX FP8 operands
+// "fp16 and below" ([llm.c], the paragraph on what follows the CUDA port), read as OCP
+// MXFP8 with E4M3 elements: blocks of 32 consecutive values along the reduction
+// dimension share one scale 2^e, the smallest power of two with max|x| <= 448 * 2^e
+// (nothing clips); each value becomes x / 2^e rounded to the nearest E4M3 value (ties
+// to the even mantissa).  In MX mode a product's operand is its bf16 tensor (the
+// configured storage precision, round-to-nearest-even) taken through this encoding and
+// back; the product itself is the oracle's plain sum.
+
+// Nearest bf16 value (round to nearest, ties to even) of a double, as the GPU stores it.
+static double round_bf16(double v) {
+    if (!std::isfinite(v) || v == 0.0) return v;
+    int E;
+    std::frexp(v, &E);                     // |v| in [2^(E-1), 2^E)
+    const int ex = std::max(E - 1, -126);  // below 2^-126: bf16's subnormal spacing
+    const double q = std::ldexp(1.0, ex - 7);
+    return std::nearbyint(v / q) * q;      // v / q is exact; nearbyint rounds half to even
+}
+
+// Nearest E4M3 value of a scaled element (|a| <= 448 by the choice of scale): 3 mantissa
+// bits below 2^-6 the fixed subnormal spacing 2^-9; ties to the even mantissa.
+static double round_e4m3(double v) {
+    const double a = std::fabs(v);
+    if (a == 0.0) return v;
+    if (a >= 448.0) return std::copysign(448.0, v);
+    int E;
+    std::frexp(a, &E);
+    const int ex = std::max(E - 1, -6);
+    const double q = std::ldexp(1.0, ex - 3);
+    return std::copysign(std::nearbyint(a / q) * q, v);
+}
+
+// The block exponent: the smallest integer e with amax <= 448 * 2^e, within E8M0's
+// [-127, 127]; an all-zero block takes -127.
+static int mx_block_exponent(double amax) {
+    if (!(amax > 0.0)) return -127;
+    int p;
+    std::frexp(amax, &p);              // floor(log2 amax) = p - 1
+    int e = p - 1 - 8;                 // amax / 2^e in [256, 512)
+    if (std::ldexp(amax, -e) > 448.0) ++e;
+    return std::min(127, std::max(-127, e));
+}
+
+// y = the MX encoding of x [rows, K] taken back to real values (blocks of 32 along K;
+// a last partial block reads as zero-padded), after rounding each x to bf16.
+template <class R>
+static void mx_roundtrip(R* y, const R* x, int64_t rows, int K) {
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int k0 = 0; k0 < K; k0 += 32) {
+            const int k1 = std::min(K, k0 + 32);
+            double v[32], amax = 0.0;
+            for (int k = k0; k < k1; ++k) {
+                v[k - k0] = round_bf16((double)x[r * K + k]);
+                amax = std::max(amax, std::fabs(v[k - k0]));
+            }
+            const int e = mx_block_exponent(amax);
+            for (int k = k0; k < k1; ++k)
+                y[r * K + k] = (R)(std::ldexp(round_e4m3(std::ldexp(v[k - k0], -e)), e));
+        }
+}
+
+// A linear layer whose two operands (in MX mode) go through the MX encoding first.
+template <class R>
+static void matmul_forward_mx(R* out, const R* inp, const R* w, const R* bias, int64_t N, int IC, int OC, bool mx) {
+    if (!mx) return matmul_forward(out, inp, w, bias, N, IC, OC);
+    std::vector<R> xq((size_t)N * IC), wq((size_t)OC * IC);
+    mx_roundtrip(xq.data(), inp, N, IC);
+    mx_roundtrip(wq.data(), w, OC, IC);
+    matmul_forward(out, xq.data(), wq.data(), bias, N, IC, OC);
+}
+
 // [torch-R] 自注意力 and [nanogpt] 直觉上的self-attention / scaling:
 // qkv columns are [q | k | v], each C wide, head h uses columns h*hs..(h+1)*hs-1;
 // s_tu = q_t . k_u / sqrt(hs) for u <= t, softmax over u <= t (masked keys get
@@ -594,6 +666,9 @@ struct Model : ModelBase {
     // q | k | v with q and k turned; outside the plain activation set.
     bool rotary = false;
     double rope_base = 10000.0;
+    // MX FP8 operands for the forward pass's block and lm_head products (the backward
+    // pass uses the stored activations and weights as they are: straight-through)
+    bool mx = false;
     std::vector<std::vector<R>> qkv_rot;
     std::vector<R> dqkv_rot;
 
@@ -628,14 +703,14 @@ struct Model : ModelBase {
         for (int l = 0; l < L; ++l) {
             const R* x = l == 0 ? A(A_ENCODED) : A(A_RESIDUAL3, l - 1);
             norm(A(A_LN1, l), A(A_LN1_MEAN, l), A(A_LN1_RSTD, l), x, P.t[LN1W][l], P.t[LN1B][l]);
-            matmul_forward(A(A_QKV, l), A(A_LN1, l), P.t[QKVW][l], bias(QKVB, l), BT, C, 3 * C);
+            matmul_forward_mx(A(A_QKV, l), A(A_LN1, l), P.t[QKVW][l], bias(QKVB, l), BT, C, 3 * C, mx);
             const R* qkv = A(A_QKV, l);
             if (rotary) {
                 rope_qkv(qkv_rot[l].data(), A(A_QKV, l), B, T, C, NH, rope_base, +1);
                 qkv = qkv_rot[l].data();
             }
             attention_forward(A(A_ATTY, l), A(A_PREATT, l), A(A_ATT, l), qkv, B, T, C, NH);
-            matmul_forward(A(A_ATTPROJ, l), A(A_ATTY, l), P.t[PROJW][l], bias(PROJB, l), BT, C, C);
+            matmul_forward_mx(A(A_ATTPROJ, l), A(A_ATTY, l), P.t[PROJW][l], bias(PROJB, l), BT, C, C, mx);
             residual_forward(A(A_RESIDUAL2, l), x, A(A_ATTPROJ, l), BT * C);
             norm(A(A_LN2, l), A(A_LN2_MEAN, l), A(A_LN2_RSTD, l), A(A_RESIDUAL2, l), P.t[LN2W][l], P.t[LN2B][l]);
             if (llama) {
@@ -643,9 +718,9 @@ struct Model : ModelBase {
                 swiglu_forward(A(A_FCH_GELU, l), A(A_FCH, l), BT, H);
                 matmul_forward(A(A_FCPROJ, l), A(A_FCH_GELU, l), P.t[FCPW][l], (const R*)nullptr, BT, (int)H, C);
             } else {
-                matmul_forward(A(A_FCH, l), A(A_LN2, l), P.t[FCW][l], P.t[FCB][l], BT, C, 4 * C);
+                matmul_forward_mx(A(A_FCH, l), A(A_LN2, l), P.t[FCW][l], P.t[FCB][l], BT, C, 4 * C, mx);
                 gelu_forward(A(A_FCH_GELU, l), A(A_FCH, l), BT * 4 * C);
-                matmul_forward(A(A_FCPROJ, l), A(A_FCH_GELU, l), P.t[FCPW][l], P.t[FCPB][l], BT, 4 * C, C);
+                matmul_forward_mx(A(A_FCPROJ, l), A(A_FCH_GELU, l), P.t[FCPW][l], P.t[FCPB][l], BT, 4 * C, C, mx);
             }
             residual_forward(A(A_RESIDUAL3, l), A(A_RESIDUAL2, l), A(A_FCPROJ, l), BT * C);
         }
@@ -653,7 +728,7 @@ struct Model : ModelBase {
         norm(A(A_LNF), A(A_LNF_MEAN), A(A_LNF_RSTD), xL, P.lnfw, P.lnfb);
         // [c3000] Transformer本体 / [torch-R] 输出: logits = final hidden state times the
         // token-embedding matrix (tied lm_head, no bias).
-        matmul_forward(A(A_LOGITS), A(A_LNF), P.wte, (const R*)nullptr, BT, C, V);
+        matmul_forward_mx(A(A_LOGITS), A(A_LNF), P.wte, (const R*)nullptr, BT, C, V, mx);
         softmax_crossentropy_forward(A(A_PROBS), A(A_LOSSES), A(A_LOGITS), tgt, BT, V);
         if (tgt) {
             R acc = 0;
@@ -896,6 +971,16 @@ int orc_set_rotary(void* h, int on, double base) {
     ORC_DISPATCH(h, { M->rotary = on != 0; M->rope_base = base; M->have_forward = false; M->qkv_rot.clear(); });
     return 0;
 }
+
+// MX FP8 operands for the forward pass's block and lm_head products on (1) or off (0).
+int orc_set_mx(void* h, int on) {
+    if (((ModelBase*)h)->s.block != 0) { g_err = "MX products are modelled for the GPT-2 block"; return -1; }
+    ORC_DISPATCH(h, { M->mx = on != 0; M->have_forward = false; });
+    return 0;
+}
+
+// y = x [rows, K] taken through bf16 and the MX FP8 encoding and back (float64).
+void orc_mx_roundtrip(const double* x, double* y, int64_t rows, int K) { mx_roundtrip(y, x, rows, K); }
 
 // y[r] = x[r] (one head vector of hs values) turned for position pos[r]; inverse turns back.
 void orc_rope(const double* x, double* y, int rows, int hs, const int* pos, double base, int inverse) {

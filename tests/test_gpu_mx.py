@@ -5,9 +5,9 @@
   in both.
 * The block-scaled product: against the oracle's product of the dequantized
   operands (float64), to fp32 accumulation and bf16 output rounding.
-* The forward pass with MX products, against the oracle's float64 forward without
-  quantization: the tolerance there is the format's own error (see
-  MX_LOGIT_COS and MX_LOSS_REL)."""
+* The forward pass with MX products, against the oracle in MX mode (the same encoding
+  of every product's operands, float64 products) at bf16 tolerances; the oracle without
+  quantization is printed beside it (the format's own error)."""
 import numpy as np
 import pytest
 
@@ -132,18 +132,20 @@ def test_gemm_rejects_bad_shapes():
 
 
 # ---------------------------------------------------------------------------- forward pass
-# Tolerance of the forward pass with MX products against the float64 oracle without
-# quantization.  An E4M3 code carries 3 mantissa bits: each operand of a product is off
-# by at most 2^-4 relative (RMS about 2^-4 / sqrt(3) = 0.036 for uniformly placed
-# values), so a product of two quantized operands has an RMS relative error near
-# 0.05 per term, which averages over the K terms of each output: one product's
-# output is off by a relative RMS of about 0.05, a row cosine of 1 - 0.05^2 / 2.  The
-# logits come after 4 L + 1 such products whose errors partly compound (measured:
-# cosine 0.9990 for 2 layers, 0.9924 for GPT-2 124M's 12, loss within 3e-4
-# relative); the bounds leave room for that growth, while a wrong scale, code or
-# layout gives cosines near 0 and losses off by whole units.
-MX_LOGIT_COS = 0.98
-MX_LOSS_REL = 2e-2
+# The forward pass with MX products is compared with the oracle in MX mode (each of the
+# five forward products multiplies its bf16 input and weight through the same MX
+# encoding, in float64): what remains is the GPU's bf16 storage of the activations, its
+# fp32 accumulation, and the elements whose bf16 value differs by an ulp and so land on
+# the other side of an E4M3 rounding boundary (an eighth of their value apart); such
+# flips compound over the layers: measured min logit-row cosines 0.99935 (2 layers) and
+# 0.9953 (GPT-2 124M, 12 layers, loss within 1e-4).  Bounds: the stated bf16 loss
+# tolerance and a row cosine of 0.99.  The tight pin is layer by layer
+# (test_mx_products_layer_by_layer): every product fed the GPU's own stored bf16 input,
+# against the oracle's encoding and a float64 product.  The plain oracle is printed
+# beside (the format's own error: cosine about 0.993 at GPT-2 124M).
+MX_ORACLE_LOSS_ABS = 2e-2
+MX_ORACLE_COS = 0.99
+MX_PREFIX_LOSS_ABS = 5e-2
 
 
 def _forward_case(w, params, x, y):
@@ -167,7 +169,15 @@ def _forward_case(w, params, x, y):
     o = oracle_model(w, params, prec="f64")
     ref_loss = o.forward(x, y)
     ref = o.act("logits").reshape(w.B * w.T, -1)
-    return bf, mxr, ref_loss, ref
+    o.set_mx(True)
+    mx_ref_loss = o.forward(x, y)
+    mx_ref = o.act("logits").reshape(w.B * w.T, -1)
+    o.close()
+    return bf, mxr, (ref_loss, ref), (mx_ref_loss, mx_ref)
+
+
+def _row_cos(z, ref):
+    return min(cosine(z[r], ref[r]) for r in range(ref.shape[0]))
 
 
 @pytest.mark.parametrize("name,m,B,T", [("small", ModelShape(160, 301, 2, 2, 128), 2, 64),
@@ -177,18 +187,47 @@ def test_mx_forward_against_the_oracle(name, m, B, T):
     announce(f"mx_forward_{name}", L=m.num_layers, C=m.channels, B=B, T=T)
     params = rand_params(m, seed=50) if name == "small" else synth.init_params(m)
     x, y = synth.inputs_targets(w)
-    (bf_loss, bf_z), (mx_loss, mx_z), ref_loss, ref = _forward_case(w, params, x, y)
+    (bf_loss, bf_z), (mx_loss, mx_z), (ref_loss, ref), (mref_loss, mref) = _forward_case(w, params, x, y)
     V = m.vocab_size
     bf_z, mx_z = bf_z[:, :V], mx_z[:, :V]
-    cos_mx = min(cosine(mx_z[r], ref[r]) for r in range(ref.shape[0]))
-    cos_bf = min(cosine(bf_z[r], ref[r]) for r in range(ref.shape[0]))
-    print(f"loss: oracle {ref_loss:.6f} bf16 {bf_loss:.6f} mxfp8 {mx_loss:.6f} "
-          f"(rel {abs(mx_loss - ref_loss) / ref_loss:.2e}); min row cosine bf16 {cos_bf:.6f} mxfp8 {cos_mx:.6f}; "
-          f"max |dz| bf16 {np.abs(bf_z - ref).max():.3g} mxfp8 {np.abs(mx_z - ref).max():.3g}", flush=True)
-    assert abs(mx_loss - ref_loss) <= MX_LOSS_REL * ref_loss
-    assert cos_mx >= MX_LOGIT_COS
+    cos_mx, cos_plain, cos_bf = _row_cos(mx_z, mref), _row_cos(mx_z, ref), _row_cos(bf_z, ref)
+    mean_mx = float(np.mean([cosine(mx_z[r], mref[r]) for r in range(mref.shape[0])]))
+    print(f"mean row cosine MX vs MX oracle {mean_mx:.6f}", flush=True)
+    print(f"loss: MX oracle {mref_loss:.6f} GPU MX {mx_loss:.6f} (|d| {abs(mx_loss - mref_loss):.2e}); "
+          f"oracle {ref_loss:.6f} GPU bf16 {bf_loss:.6f}; min row cosine: MX vs MX oracle {cos_mx:.6f}, "
+          f"MX vs plain oracle {cos_plain:.6f}, bf16 vs plain oracle {cos_bf:.6f}", flush=True)
+    assert abs(mx_loss - mref_loss) <= MX_ORACLE_LOSS_ABS
+    assert cos_mx >= MX_ORACLE_COS
     # the quantization must actually be on: MX logits differ from the bf16 path's
     assert np.abs(mx_z - bf_z).max() > 0
+
+
+def test_mx_training_gradients_against_the_oracle():
+    # A training step with MX forward products: the backward pass takes the stored bf16
+    # activations and weights as they are (straight-through), on both sides.
+    from transformer_lm_fwd_amd import binding as b
+    m = ModelShape(160, 301, 2, 2, 128)
+    w = Workload("mx_grad", m, 2, 64, "bf16", "uniform", index=54)
+    announce("mx_training_gradients", L=m.num_layers, C=m.channels, B=w.B, T=w.T)
+    params = rand_params(m, seed=54)
+    x, y = synth.inputs_targets(w)
+    a = gpu_arena(w, params)
+    a.set_gemm_format(b.GPT2_GEMM_MXFP8)
+    a.forward(x, y)
+    loss = a.loss()
+    a.backward()
+    g = to_np(a.tensor(b.T_GRADS)).ravel()
+    a.close()
+    o = oracle_model(w, params, prec="f64")
+    o.set_mx(True)
+    ref = o.forward(x, y)
+    o.backward()
+    gr = o.get("grads")
+    o.close()
+    cos = cosine(g, gr)
+    print(f"MX step: loss GPU {loss:.6f} MX oracle {ref:.6f}; flat gradient cosine {cos:.6f}", flush=True)
+    assert abs(loss - ref) <= MX_ORACLE_LOSS_ABS
+    assert cos >= 0.999
 
 
 def test_mx_weights_follow_every_update():
@@ -248,6 +287,78 @@ def test_empty_calls_are_no_ops():
     assert L.gpt2_mx_gemm(p, p, 128, p, p, 128, p, 64, 4, 0, 128, 0, None, None, None, None) == 0
 
 
+def _mx_op(x):
+    """The operand an MX product multiplies (oracle/mx.py's encoder): the bf16 values x
+    [rows, K], zero-padded to whole 32-blocks, encoded and decoded."""
+    R, K = x.shape
+    Kp = (K + 31) // 32 * 32
+    return mx.dequantize(*mx.quantize(np.pad(x, ((0, 0), (0, Kp - K)))))[:, :K]
+
+
+def _bf16_np(x):
+    import torch
+    return torch.tensor(np.asarray(x, dtype=np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+
+
+@pytest.mark.parametrize("name,m,B,T", [("small", ModelShape(160, 301, 2, 2, 128), 2, 64),
+                                        ("gpt2_124m", synth.WORKLOADS["gpt2_124m_b8t1024_bf16"].model, 4, 64),
+                                        ("gpt2_350m", synth.WORKLOADS["gpt2_350m_b8t1024_bf16_zipf"].model, 2, 32)])
+def test_mx_products_layer_by_layer(name, m, B, T):
+    # Every MX product of the forward pass, fed the GPU's own stored bf16 input (so no
+    # upstream difference can flip a code): qkv, the attention projection with its
+    # residual, c_fc with GELU, the c_fc projection with its residual, the tied lm_head.
+    # Reference: oracle/mx.py's encoding of input and bf16 weight, float64 product, the
+    # bias and residual added in float64; tolerance: fp32 accumulation (as in the GEMM
+    # test) plus the bf16 rounding of the stored output.
+    from transformer_lm_fwd_amd import binding as b
+    w = Workload(f"mx_ltl_{name}", m, B, T, "bf16", "uniform", index=55)
+    announce(f"mx_products_layer_by_layer_{name}", L=m.num_layers, C=m.channels, B=B, T=T)
+    params = rand_params(m, seed=55) if name == "small" else synth.init_params(m)
+    x, _ = synth.inputs_targets(w)
+    a = gpu_arena(w, params)
+    a.set_gemm_format(b.GPT2_GEMM_MXFP8)
+    a.forward(x)
+    offs = synth.param_offsets(m)
+
+    def act(tid, l=0):
+        return to_np(a.tensor(tid, l)).astype(np.float64)
+
+    def P(name):
+        o, n = offs[name]
+        return np.asarray(params[o:o + n], dtype=np.float64)
+
+    worst = 0.0
+
+    def check(label, out, inp, wname, bias=None, resid=None, gelu_out=None):
+        nonlocal worst
+        Wm = _bf16_np(P(wname).reshape(-1, inp.shape[1]))
+        A, Bm = _mx_op(inp), _mx_op(Wm)
+        prod = A @ Bm.T
+        if bias is not None:
+            prod = prod + bias
+        acc_err = 4 * inp.shape[1] * 2.0 ** -24 * (np.abs(A) @ np.abs(Bm).T)
+        ref = prod if resid is None else prod + resid
+        err = np.abs(out - ref)
+        tol = 2.0 ** -8 * np.abs(ref) + acc_err + 1e-30
+        worst = max(worst, float((err / tol).max()))
+        assert np.all(err <= tol), (label, float((err / tol).max()))
+        if gelu_out is not None:
+            g = oracle.gelu(prod)
+            assert np.all(np.abs(gelu_out - g) <= 1.13 * acc_err + 2.0 ** -8 * np.abs(g) + 1e-6), label + " gelu"
+
+    for l in range(m.num_layers):
+        h = f"h{l}."
+        xin = act(b.T_ENCODED) if l == 0 else act(b.T_RESIDUAL3, l - 1)
+        check(f"qkv{l}", act(b.T_QKV, l), act(b.T_LN1, l), h + "qkv.w", P(h + "qkv.b"))
+        check(f"proj{l}", act(b.T_RESIDUAL2, l), act(b.T_ATTY, l), h + "proj.w", P(h + "proj.b"), resid=xin)
+        check(f"fc{l}", act(b.T_FCH, l), act(b.T_LN2, l), h + "fc.w", P(h + "fc.b"), gelu_out=act(b.T_FCH_GELU, l))
+        check(f"fcproj{l}", act(b.T_RESIDUAL3, l), act(b.T_FCH_GELU, l), h + "fcproj.w", P(h + "fcproj.b"),
+              resid=act(b.T_RESIDUAL2, l))
+    check("lm_head", act(b.T_LOGITS), act(b.T_LNF), "wte")
+    a.close()
+    print(f"{4 * m.num_layers + 1} MX products within bounds (largest error / bound {worst:.3f})", flush=True)
+
+
 @pytest.mark.parametrize("B,T", [(1, 1), (3, 37)])
 def test_mx_forward_single_position_and_ragged_rows(B, T):
     # B*T = 1 and 111 rows: one partial 128-row tile of every MX product
@@ -256,33 +367,41 @@ def test_mx_forward_single_position_and_ragged_rows(B, T):
     announce("mx_forward_edge", B=B, T=T)
     params = rand_params(m, seed=53)
     x, y = synth.inputs_targets(w)
-    (bf_loss, bf_z), (mx_loss, mx_z), ref_loss, ref = _forward_case(w, params, x, y)
+    _, (mx_loss, mx_z), _, (mref_loss, mref) = _forward_case(w, params, x, y)
     V = m.vocab_size
-    cos = min(cosine(mx_z[r, :V], ref[r]) for r in range(ref.shape[0]))
-    print(f"loss oracle {ref_loss:.6f} mxfp8 {mx_loss:.6f}; min row cosine {cos:.6f}", flush=True)
-    assert abs(mx_loss - ref_loss) <= MX_LOSS_REL * ref_loss and cos >= MX_LOGIT_COS
+    cos = _row_cos(mx_z[:, :V], mref)
+    print(f"loss MX oracle {mref_loss:.6f} GPU MX {mx_loss:.6f}; min row cosine {cos:.6f}", flush=True)
+    assert abs(mx_loss - mref_loss) <= MX_ORACLE_LOSS_ABS and cos >= MX_ORACLE_COS
 
 
-def test_mx_forward_gpt2_350m_full_size_against_the_bf16_path():
-    # GPT-2 350M at B=8, T=1024 (beyond the oracle at this size): the MX forward must keep
-    # the bf16 forward's logits' direction and loss within the format's tolerance
+def test_mx_forward_gpt2_350m_full_size_sampled_prefixes():
+    # GPT-2 350M at B=8, T=1024 with MX products: by causality, positions 0..63 of a
+    # sequence depend only on its first 64 tokens, so the oracle in MX mode on those
+    # prefixes gives their logits and losses exactly.
     from transformer_lm_fwd_amd import binding as b
     w = synth.WORKLOADS["gpt2_350m_b8t1024_bf16_zipf"]
     announce("mx_forward_350m", B=w.B, T=w.T)
+    params = synth.init_params(w.model)
     x, y = synth.inputs_targets(w)
-    a = gpu_arena(w, synth.init_params(w.model))
-    rows = np.unique(np.r_[0, w.B * w.T - 1, np.random.default_rng(1).integers(0, w.B * w.T, 62)])
-    V = w.model.vocab_size
-
-    def run():
-        a.forward(x)
-        z = to_np(a.tensor(b.T_LOGITS)[rows]).astype(np.float64)[:, :V]
-        a.forward(x, y)
-        return a.loss(), z
-
-    lb, zb = run()
+    a = gpu_arena(w, params)
     a.set_gemm_format(b.GPT2_GEMM_MXFP8)
-    lm, zm = run()
-    cos = min(cosine(zm[i], zb[i]) for i in range(len(rows)))
-    print(f"350M loss bf16 {lb:.5f} mxfp8 {lm:.5f}; min sampled row cosine {cos:.6f}", flush=True)
-    assert abs(lm - lb) <= MX_LOSS_REL * lb and cos >= MX_LOGIT_COS
+    V, t0 = w.model.vocab_size, 64
+    a.forward(x)
+    z = to_np(a.tensor(b.T_LOGITS)).astype(np.float64).reshape(w.B, w.T, -1)
+    a.forward(x, y)
+    losses = to_np(a.tensor(b.T_LOSSES)).reshape(w.B, w.T)
+    a.close()
+    for row in (0, w.B - 1):
+        o = oracle_model(w, params, B=1, T=t0)
+        o.set_mx(True)
+        o.forward(x[row:row + 1, :t0], y[row:row + 1, :t0])
+        ref_z = o.act("logits").reshape(t0, -1)
+        ref_l = o.act("losses")
+        o.close()
+        cos = _row_cos(z[row, :t0, :V], ref_z)
+        dm = abs(float(np.mean(losses[row, :t0])) - float(np.mean(ref_l)))
+        print(f"row {row}: positions < {t0}: |mean loss - MX oracle| = {dm:.3g}, min row cosine {cos:.6f}",
+              flush=True)
+        # a mean over 64 positions of one sequence after 24 layers of E4M3 code flips
+        # (measured up to 0.022); the products themselves are pinned layer by layer
+        assert dm <= MX_PREFIX_LOSS_ABS and cos >= MX_ORACLE_COS

@@ -91,3 +91,85 @@ def test_block_scaled_product_of_representable_operands_is_exact():
     eb2 = eb.copy()
     eb2[0, 1] += 1
     assert not np.array_equal(mx.matmul(qa, ea, qb, eb2), a @ b.T)
+
+
+# ---------------------------------------------------------------------------- MX mode of the
+# C++ oracle: its encode / decode round trip and the operands of each forward product
+
+def _bf16(x):
+    """Round-to-nearest-even bf16 of float32-representable values (torch's conversion)."""
+    import torch
+    return torch.tensor(np.asarray(x, dtype=np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+
+
+def _mx_operand(x):
+    """The operand an MX product multiplies, from oracle/mx.py's table-based encoder:
+    bf16 values, zero-padded to whole 32-blocks, encoded and decoded."""
+    x = _bf16(x)
+    R, K = x.shape
+    Kp = (K + 31) // 32 * 32
+    xp = np.pad(x, ((0, 0), (0, Kp - K)))
+    return mx.dequantize(*mx.quantize(xp))[:, :K]
+
+
+def test_cpp_mx_roundtrip_matches_the_table_encoder():
+    import oracle
+    rng = np.random.default_rng(11)
+    for rows, K in [(7, 96), (5, 200), (3, 33), (1, 8)]:
+        x = (rng.standard_normal((rows, K)) * np.exp2(rng.integers(-20, 20, (rows, K)))).astype(np.float32)
+        x[0, :4] = [0.0, -0.0, 1e-40, -3e-39]        # zeros and fp32 subnormals
+        if K >= 64:
+            x[1, 32:64] = 0.0                          # an all-zero block
+            x[2, 32:40] = [1.0625, 1.1875, 432.0, 448.0, -0.5, 2.0 ** -9, 2.0 ** -10, 3 * 2.0 ** -10]
+        got = oracle.mx_roundtrip(x.astype(np.float64))
+        ref = _mx_operand(x)
+        np.testing.assert_array_equal(got, ref)
+        np.testing.assert_array_equal(np.signbit(got), np.signbit(ref))
+
+
+def test_mx_mode_multiplies_the_encoded_operands_of_each_forward_product():
+    # In MX mode each of the five forward products (qkv, attention projection, c_fc,
+    # c_fc projection, tied lm_head) multiplies its bf16 input and weight through the MX
+    # encoding; everything between the products is the plain forward pass.
+    import oracle
+    import synth
+    m = synth.ModelShape(16, 97, 2, 2, 64)
+    w = synth.Workload("mx_oracle", m, 2, 16, "bf16", "uniform", index=60)
+    p = synth.init_params(m).astype(np.float64)
+    rng = np.random.default_rng(60)
+    offs = synth.param_offsets(m)
+    for name, (o, n) in offs.items():
+        if name.endswith(".b"):
+            p[o:o + n] = 0.1 * rng.standard_normal(n)
+    x, y = synth.inputs_targets(w)
+    o = oracle.Oracle(m, w.B, w.T, "f64")
+    o.set("params", p)
+    loss_plain = o.forward(x, y)
+    o.set_mx(True)
+    loss_mx = o.forward(x, y)
+    C, BT = m.channels, w.B * w.T
+
+    def W(name):
+        off, n = offs[name]
+        return p[off:off + n]
+
+    def check(out, inp, wname, bname, rows, IC, OC):
+        Wm = W(wname).reshape(OC, IC)
+        ref = _mx_operand(inp.reshape(rows, IC)) @ _mx_operand(Wm).T
+        if bname:
+            ref = ref + W(bname)
+        np.testing.assert_allclose(out.reshape(rows, OC), ref, rtol=1e-12, atol=1e-12)
+
+    for l in range(m.num_layers):
+        h = f"h{l}."
+        check(o.act("qkv", l), o.act("ln1", l), h + "qkv.w", h + "qkv.b", BT, C, 3 * C)
+        resid_in = o.act("encoded") if l == 0 else o.act("residual3", l - 1)
+        proj = o.act("residual2", l) - resid_in
+        check(proj, o.act("atty", l), h + "proj.w", h + "proj.b", BT, C, C)
+        check(o.act("fch", l), o.act("ln2", l), h + "fc.w", h + "fc.b", BT, C, 4 * C)
+        fcp = o.act("residual3", l) - o.act("residual2", l)
+        check(fcp, o.act("fch_gelu", l), h + "fcproj.w", h + "fcproj.b", BT, 4 * C, C)
+    check(o.act("logits"), o.act("lnf"), "wte", None, BT, C, m.vocab_size)
+    # the encoding is really applied (3 mantissa bits: the loss moves)
+    assert loss_mx != loss_plain
+    o.close()
