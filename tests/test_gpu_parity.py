@@ -261,6 +261,34 @@ def test_fused_backward_adamw_matches_separate_calls(dtype, NH):
         np.testing.assert_array_equal(u, f)
 
 
+@pytest.mark.parametrize("dtype,NH,B,T", [("bf16", 2, 3, 64), ("bf16", 4, 4, 37), ("fp32", 4, 2, 33)])
+def test_forward_over_two_streams_matches_one_stream_bitwise(dtype, NH, B, T):
+    # The forward pass runs the batch as two groups of sequences on two streams; with the
+    # launch profiler on it runs as one pass on one stream.  Activations, logits, losses
+    # and the gradient of the logits must not depend on which.
+    b = _b()
+    w = Workload("split", ModelShape(96, 211, 2, NH, 128), B, T, dtype, "uniform", index=29)
+    announce(f"two_stream_forward_{dtype}_B{B}", w)
+    p = rand_params(w.model, seed=12)
+    x, y = synth.inputs_targets(w)
+    a = gpu_arena(w, p)
+    ids = [(b.T_LOGITS, 0), (b.T_LOSSES, 0), (b.T_LNF, 0), (b.T_LNF_STATS, 0)] + \
+          [(getattr(b, t), l) for l in range(w.model.num_layers)
+           for t in ("T_LN1", "T_QKV", "T_ATTY", "T_ATT_LSE", "T_RESIDUAL2", "T_FCH", "T_FCH_GELU", "T_RESIDUAL3")]
+    runs = []
+    for single in (True, False):
+        b.profile(single)
+        a.forward(x, y)
+        import torch
+        torch.cuda.synchronize()
+        b.profile(False)
+        runs.append([a.loss()] + [to_np(a.tensor(t, l)).copy() for t, l in ids])
+    assert runs[0][0] == runs[1][0]
+    for u, v in zip(runs[0][1:], runs[1][1:]):
+        np.testing.assert_array_equal(u, v)
+    a.close()
+
+
 def test_zero_final_gains_give_ln_V_on_gpu():
     # "从头搭建GPT(Andrej Karpathy) 笔记", 计算loss: all-zero logits cost exactly ln V, and
     # d loss / d z = (1/V - onehot)/(B T).

@@ -331,6 +331,18 @@ struct Model {
         C = a->cfg.channels; L = a->cfg.num_layers; NH = a->cfg.num_heads; V = a->cfg.vocab_size;
         Vp = a->Vp; B = Be; S = Se; BT = B * S; P = a->cfg.max_seq_len;
     }
+    // A forward pass over the Bg sequences b0 .. b0 + Bg - 1 of a batch (rows b0 S ..):
+    // every per-row and per-sequence kernel sees only those rows, so the passes over two
+    // such groups are independent and can run on two streams.
+    int b0 = 0;
+    bool side_group = false;  // runs on the side stream beside a main-stream group
+    Model(gpt2_arena* ar, hipStream_t st, int Bg, int Se, int first, bool side = false) : Model(ar, st, Bg, Se) {
+        b0 = first;
+        side_group = side;
+    }
+    int64_t r0() const { return (int64_t)b0 * S; }
+    T* arow(size_t off, int64_t width) const { return act(off) + r0() * width; }
+    float* frow(size_t off, int64_t width) const { return f32(off) + r0() * width; }
     float* master(int64_t off) const { return at<float>(a, a->params) + off; }
     float* grad(int64_t off) const { return at<float>(a, a->grads) + off; }
     // GEMM weight operand: the bf16 copy in BF16 mode, the master in FP32 mode.
@@ -364,8 +376,9 @@ struct Model {
         g.M = M; g.N = N; g.K = K; g.lda = lda; g.ldb = ldb; g.ldc = ldc;
         apply_extra(g, ex);
         // main-stream products use their own split-K workspace (the side stream's is busy
-        // during backward)
-        CHECK(gemm<T>(g, ak, bk, epi, f32(a->ws_main), a->ws_main_floats, s), "gemm");
+        // during backward); the side group of a split forward pass splits no product
+        CHECK(gemm<T>(g, ak, bk, epi, side_group ? nullptr : f32(a->ws_main), side_group ? 0 : a->ws_main_floats, s),
+              "gemm");
         return GPT2_OK;
     }
 
@@ -433,6 +446,89 @@ struct Model {
         return gemm_call(X, K, true, weight(w_off), K, true, Y, ldc, BT, N, K, epi, bias, R, C2, ex);
     }
 
+    // The forward pass over this model's rows (all of them unless it is one group of
+    // a split pass): activations, logits and, with targets, the per-row losses and their
+    // gradient (scaled by dscale = 1 / (rows of the whole batch)).  inp / tgt point at the
+    // whole batch.
+    int forward_rows(const int32_t* inp, const int32_t* tgt, float dscale) {
+        inp += r0();
+        if (tgt) tgt += r0();
+        CHECK(encoder_forward<T>(arow(a->encoded, C), inp, master(a->o_wte), rotary() ? nullptr : master(a->o_wpe),
+                                 BT, S, C, s),
+              "encoder");
+        for (int l = 0; l < L; ++l) {
+            const LayerActs& x = a->la[l];
+            const T* xin = l == 0 ? arow(a->encoded, C) : arow(a->la[l - 1].res3, C);
+            const MxBuf mi = mx_in(), mg = mx_gelu();
+            CHECK(layernorm_forward<T>(arow(x.ln1, C), frow(x.ln1s, 2), xin, master(lp(l, P_LN1W)), pb(lp(l, P_LN1B)),
+                                       BT, C, s, mi.q, mi.ld, mi.s, llama()),
+                  "ln1");
+            int rc;
+            // qkv = ln1 W_qkv^T + b
+            // with rotary positions the bf16 products turn q and k in their epilogue
+            const bool fuse_rope = rotary() && sizeof(T) == 2;
+            EpiExtra rx;
+            if (fuse_rope) rx.rope = rope_tab(), rx.period = S, rx.hs = C / NH, rx.cols = 2 * C;
+            if ((rc = fwd_gemm(arow(x.ln1, C), C, lp(l, P_QKVW), 4 * l, 3 * C, arow(x.qkv, 3 * C), 3 * C, EPI_BIAS,
+                               pb(lp(l, P_QKVB)), nullptr, nullptr, mi, MxBuf{}, rx)))
+                return rc;
+            if (rotary() && !fuse_rope)  // turn q and k of every head for its position (in place)
+                CHECK(rope_apply<T>(arow(x.qkv, 3 * C), 3 * C, BT, 2 * C, C / NH, S, 0, rope_tab(), false, s), "rope");
+            CHECK(attention_forward<T>(arow(x.atty, C), f32(x.lse) + (int64_t)b0 * NH * S, arow(x.qkv, 3 * C), B, S,
+                                       C, NH, s),
+                  "attention");
+            // res2 = xin + atty W_proj^T + b
+            if ((rc = fwd_gemm(arow(x.atty, C), C, lp(l, P_PROJW), 4 * l + 1, C, arow(x.res2, C), C, EPI_BIAS_RES,
+                               pb(lp(l, P_PROJB)), xin)))
+                return rc;
+            CHECK(layernorm_forward<T>(arow(x.ln2, C), frow(x.ln2s, 2), arow(x.res2, C), master(lp(l, P_LN2W)),
+                                       pb(lp(l, P_LN2B)), BT, C, s, mi.q, mi.ld, mi.s, llama()),
+                  "ln2");
+            if (llama()) {
+                // (g | u) = ln2 W_gu^T (interleaved), h = silu(g) u, res3 = res2 + h W_down^T
+                const int H = (int)a->H;
+                EpiExtra sx;  // bf16: the product's epilogue writes h itself
+                if (sizeof(T) == 2) sx.swiglu = (bf16*)arow(x.fchg, a->F2), sx.ld_swiglu = H;
+                if ((rc = fwd_gemm(arow(x.ln2, C), C, lp(l, P_FCW), 4 * l + 2, 2 * H, arow(x.fch, a->F1), 2 * H,
+                                   EPI_BIAS, nullptr, nullptr, nullptr, MxBuf{}, MxBuf{}, sx)))
+                    return rc;
+                if (sizeof(T) != 2)
+                    CHECK(swiglu_forward<T>(arow(x.fchg, a->F2), arow(x.fch, a->F1), BT, H, s), "swiglu");
+                if ((rc = fwd_gemm(arow(x.fchg, a->F2), H, lp(l, P_FCPW), 4 * l + 3, C, arow(x.res3, C), C,
+                                   EPI_BIAS_RES, nullptr, arow(x.res2, C))))
+                    return rc;
+                continue;
+            }
+            // fch = ln2 W_fc^T + b, fchg = gelu(fch)
+            if ((rc = fwd_gemm(arow(x.ln2, C), C, lp(l, P_FCW), 4 * l + 2, 4 * C, arow(x.fch, 4 * C), 4 * C,
+                               EPI_BIAS_GELU, master(lp(l, P_FCB)), nullptr, arow(x.fchg, 4 * C), mi, mg)))
+                return rc;
+            // res3 = res2 + fchg W_fcproj^T + b
+            if ((rc = fwd_gemm(arow(x.fchg, 4 * C), 4 * C, lp(l, P_FCPW), 4 * l + 3, C, arow(x.res3, C), C,
+                               EPI_BIAS_RES, master(lp(l, P_FCPB)), arow(x.res2, C), nullptr, mg)))
+                return rc;
+        }
+        const MxBuf mi = mx_in();
+        CHECK(layernorm_forward<T>(arow(a->lnf, C), frow(a->lnfs, 2), arow(a->la[L - 1].res3, C), master(a->o_lnfw),
+                                   pb(a->o_lnfb), BT, C, s, mi.q, mi.ld, mi.s, llama()),
+              "lnf");
+        // logits = lnf wte^T (tied lm_head, no bias); row stride Vp
+        int rc;
+        if ((rc = fwd_gemm(arow(a->lnf, C), C, a->o_wte, 4 * L, V, arow(a->logits, Vp), Vp, EPI_BIAS, nullptr,
+                           nullptr, nullptr, mi)))
+            return rc;
+        if (tgt)
+            CHECK(crossentropy_fused<T>(arow(a->logits, Vp), f32(a->losses) + r0(), tgt, BT, V, Vp, dscale, s),
+                  "crossentropy");
+        return GPT2_OK;
+    }
+
+    // The forward pass.  Without MX products (whose quantized-input buffers are shared)
+    // and outside the launch profiler, a batch of two or more sequences is split into two
+    // groups whose passes run on the main and the side stream at once: each kernel of one
+    // group then fills the units the other's leaves idle (a product with few output tiles,
+    // an epilogue, a LayerNorm).  Every per-row and per-sequence result is the same as in
+    // one pass, bit for bit.
     int forward(const int32_t* inp, const int32_t* tgt) {
         if (a->gemm_format == GPT2_GEMM_MXFP8 && a->mx_stale) {
             int rc = mx_refresh();
@@ -442,71 +538,21 @@ struct Model {
             CHECK(rope_table(rope_tab_mut(), P, C / NH, 10000.0, s), "rope table");
             a->rope_ready = true;
         }
-        CHECK(encoder_forward<T>(act(a->encoded), inp, master(a->o_wte), rotary() ? nullptr : master(a->o_wpe), BT, S,
-                                 C, s),
-              "encoder");
-        for (int l = 0; l < L; ++l) {
-            const LayerActs& x = a->la[l];
-            const T* xin = l == 0 ? act(a->encoded) : act(a->la[l - 1].res3);
-            const MxBuf mi = mx_in(), mg = mx_gelu();
-            CHECK(layernorm_forward<T>(act(x.ln1), f32(x.ln1s), xin, master(lp(l, P_LN1W)), pb(lp(l, P_LN1B)), BT, C,
-                                       s, mi.q, mi.ld, mi.s, llama()),
-                  "ln1");
-            int rc;
-            // qkv = ln1 W_qkv^T + b
-            // with rotary positions the bf16 products turn q and k in their epilogue
-            const bool fuse_rope = rotary() && sizeof(T) == 2;
-            EpiExtra rx;
-            if (fuse_rope) rx.rope = rope_tab(), rx.period = S, rx.hs = C / NH, rx.cols = 2 * C;
-            if ((rc = fwd_gemm(act(x.ln1), C, lp(l, P_QKVW), 4 * l, 3 * C, act(x.qkv), 3 * C, EPI_BIAS,
-                               pb(lp(l, P_QKVB)), nullptr, nullptr, mi, MxBuf{}, rx)))
-                return rc;
-            if (rotary() && !fuse_rope)  // turn q and k of every head for its position (in place)
-                CHECK(rope_apply<T>(act(x.qkv), 3 * C, BT, 2 * C, C / NH, S, 0, rope_tab(), false, s), "rope");
-            CHECK(attention_forward<T>(act(x.atty), f32(x.lse), act(x.qkv), B, S, C, NH, s), "attention");
-            // res2 = xin + atty W_proj^T + b
-            if ((rc = fwd_gemm(act(x.atty), C, lp(l, P_PROJW), 4 * l + 1, C, act(x.res2), C, EPI_BIAS_RES,
-                               pb(lp(l, P_PROJB)), xin)))
-                return rc;
-            CHECK(layernorm_forward<T>(act(x.ln2), f32(x.ln2s), act(x.res2), master(lp(l, P_LN2W)),
-                                       pb(lp(l, P_LN2B)), BT, C, s, mi.q, mi.ld, mi.s, llama()),
-                  "ln2");
-            if (llama()) {
-                // (g | u) = ln2 W_gu^T (interleaved), h = silu(g) u, res3 = res2 + h W_down^T
-                const int H = (int)a->H;
-                EpiExtra sx;  // bf16: the product's epilogue writes h itself
-                if (sizeof(T) == 2) sx.swiglu = (bf16*)act(x.fchg), sx.ld_swiglu = H;
-                if ((rc = fwd_gemm(act(x.ln2), C, lp(l, P_FCW), 4 * l + 2, 2 * H, act(x.fch), 2 * H, EPI_BIAS, nullptr,
-                                   nullptr, nullptr, MxBuf{}, MxBuf{}, sx)))
-                    return rc;
-                if (sizeof(T) != 2) CHECK(swiglu_forward<T>(act(x.fchg), act(x.fch), BT, H, s), "swiglu");
-                if ((rc = fwd_gemm(act(x.fchg), H, lp(l, P_FCPW), 4 * l + 3, C, act(x.res3), C, EPI_BIAS_RES, nullptr,
-                                   act(x.res2))))
-                    return rc;
-                continue;
-            }
-            // fch = ln2 W_fc^T + b, fchg = gelu(fch)
-            if ((rc = fwd_gemm(act(x.ln2), C, lp(l, P_FCW), 4 * l + 2, 4 * C, act(x.fch), 4 * C, EPI_BIAS_GELU,
-                               master(lp(l, P_FCB)), nullptr, act(x.fchg), mi, mg)))
-                return rc;
-            // res3 = res2 + fchg W_fcproj^T + b
-            if ((rc = fwd_gemm(act(x.fchg), 4 * C, lp(l, P_FCPW), 4 * l + 3, C, act(x.res3), C, EPI_BIAS_RES,
-                               master(lp(l, P_FCPB)), act(x.res2), nullptr, mg)))
-                return rc;
-        }
-        const MxBuf mi = mx_in();
-        CHECK(layernorm_forward<T>(act(a->lnf), f32(a->lnfs), act(a->la[L - 1].res3), master(a->o_lnfw),
-                                   pb(a->o_lnfb), BT, C, s, mi.q, mi.ld, mi.s, llama()),
-              "lnf");
-        // logits = lnf wte^T (tied lm_head, no bias); row stride Vp
+        const float dscale = 1.0f / BT;
+        const bool split = B >= 2 && !mx_on() && !profiling() && b0 == 0;
         int rc;
-        if ((rc = fwd_gemm(act(a->lnf), C, a->o_wte, 4 * L, V, act(a->logits), Vp, EPI_BIAS, nullptr, nullptr, nullptr,
-                           mi)))
-            return rc;
-        if (tgt) {
-            CHECK(crossentropy_fused<T>(act(a->logits), f32(a->losses), tgt, BT, V, Vp, 1.0f / BT, s), "crossentropy");
-            CHECK(mean_loss(f32(a->loss), f32(a->losses), BT, s), "mean loss");
+        if (!split) {
+            if ((rc = forward_rows(inp, tgt, dscale))) return rc;
+        } else {
+            if ((rc = ensure_streams(a))) return rc;
+            const int B1 = B / 2;
+            Model<T> m0(a, s, B1, S, 0), m1(a, a->side, B - B1, S, B1, true);
+            if ((rc = stream_wait(a, a->side, s))) return rc;
+            if ((rc = m1.forward_rows(inp, tgt, dscale))) return rc;
+            if ((rc = m0.forward_rows(inp, tgt, dscale))) return rc;
+            if ((rc = stream_wait(a, s, a->side))) return rc;
         }
+        if (tgt) CHECK(mean_loss(f32(a->loss), f32(a->losses), BT, s), "mean loss");
         return GPT2_OK;
     }
 
