@@ -219,8 +219,13 @@ __global__ __launch_bounds__(256) void attn_fwd_mfma64(bf16* out, float* lse, co
 #pragma unroll
         for (int i = 1; i < 32; ++i) mt = fmaxf(mt, x[i]);
         mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-        const float mn = fmaxf(m, mt * c);
-        if (__any(mn > m)) {  // rescale only when some running maximum grew
+        // The reference m moves only when a score exceeds it by more than 2^8 (and on the
+        // first tile): probabilities 2^(x c - m) then stay below 256, exact enough in
+        // fp32 and bf16, and the rescale of o and l is rare instead of almost every tile.
+        // The result does not depend on the reference beyond rounding (o / l and
+        // m + log2 l are invariant).
+        const float mn = mt * c > m + 8.0f ? mt * c : m;
+        if (__any(mn > m)) {
             const float corr = fast_exp2(m - mn);
             l *= corr;
 #pragma unroll
@@ -230,16 +235,26 @@ __global__ __launch_bounds__(256) void attn_fwd_mfma64(bf16* out, float* lse, co
             }
         }
         m = mn;
+        // row sums of the bf16 probabilities (the values P V multiplies), two per
+        // v_dot2c_f32_bf16 against (1, 1)
+        typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+        const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4) {
             if (k0 + 16 * s4 > qw + 31) break;  // remaining slices are all masked for this wave
             float p[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                p[e] = fast_exp2(__builtin_fmaf(x[8 * s4 + e], c, -mn));
-                l += p[e];
-            }
+            for (int e = 0; e < 8; ++e) p[e] = fast_exp2(__builtin_fmaf(x[8 * s4 + e], c, -mn));
             const u32x4 pk = pack16<bf16>(p);
+            // (the words are taken out of the vector one by one: a bit cast of a vector
+            // element, bit_cast(bf16x2_t, pk[j]), compiles to pk[0] for every j)
+            const uint32_t wd[4] = {pk.x, pk.y, pk.z, pk.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                bf16x2_t two;
+                __builtin_memcpy(&two, &wd[j], 4);
+                l = __builtin_amdgcn_fdot2_f32_bf16(two, ones, l, false);
+            }
 #pragma unroll
             for (int dt = 0; dt < 2; ++dt) o[dt] = mfma32(fv.read(sV, dt, s4), pk, o[dt]);
         }
@@ -423,6 +438,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_mfma64(bf16* dqkv, const bf16
     const float2 ldq = make_float2(myq < T ? lse[(int64_t)bh * T + myq] * LOG2E : 0.f, Dq);
     if (g == 0 && myq < T) LD[(int64_t)bh * T + myq] = ldq;
     f32x16 dq[2] = {zero16(), zero16()};
+    f32x16 negD;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) negD[i] = -Dq;
 
     const dsc_t dsc = make_dsc(base, (uint32_t)(T * C3 * 2));
     const TileDma tk(w, lane, C + h * HS, C3), tv(w, lane, 2 * C + h * HS, C3);
@@ -454,11 +472,24 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_mfma64(bf16* dqkv, const bf16
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
             if (k0 + 32 * st > qw + 31) continue;
-            f32x16 sc = zero16(), dp = zero16();
+            // the sub-tile's fragments are all requested before its first product
+            u32x4 kr[4], vr[4], kt[2][2];
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                sc = mfma32(fk.read(sK, st, ks), qf[ks], sc);
-                dp = mfma32(fk.read(sV, st, ks), gf[ks], dp);
+                kr[ks] = fk.read(sK, st, ks);
+                vr[ks] = fk.read(sV, st, ks);
+            }
+#pragma unroll
+            for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+                for (int dt = 0; dt < 2; ++dt) kt[sl][dt] = ft.read(sK, dt, 2 * st + sl);
+            // dP - D directly: the dP product starts from -D (this lane's query is the
+            // accumulator column, so one register block serves every tile)
+            f32x16 sc = zero16(), dp = negD;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                sc = mfma32(kr[ks], qf[ks], sc);
+                dp = mfma32(vr[ks], gf[ks], dp);
             }
 #pragma unroll
             for (int sl = 0; sl < 2; ++sl) {
@@ -471,10 +502,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_mfma64(bf16* dqkv, const bf16
                         if (32 * st + 16 * sl + e > lim) pv[e] = 0.f;
                 }
 #pragma unroll
-                for (int e = 0; e < 8; ++e) ds[e] = pv[e] * (dp[8 * sl + e] - ldq.y);
+                for (int e = 0; e < 8; ++e) ds[e] = pv[e] * dp[8 * sl + e];
                 const u32x4 dd = pack16<bf16>(ds);
 #pragma unroll
-                for (int dt = 0; dt < 2; ++dt) dq[dt] = mfma32(dd, ft.read(sK, dt, 2 * st + sl), dq[dt]);
+                for (int dt = 0; dt < 2; ++dt) dq[dt] = mfma32(dd, kt[sl][dt], dq[dt]);
             }
         }
     }
