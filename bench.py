@@ -116,6 +116,12 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy 1 GiB device-to-device 5 times (a kernel of known traffic for the "
                          "FETCH_SIZE / WRITE_SIZE counter calibration) and exit")
+    ap.add_argument("--launch-order", default=None,
+                    help="write the kernel names of the profiled steps' launches, in launch order, to this JSON file "
+                         "(to match a counter trace of the same steps dispatch by dispatch)")
+    ap.add_argument("--mfma-probe", action="store_true",
+                    help="only measure the matrix cores' sustained rate for three MFMA forms (gpt2_mfma_peak, "
+                         "register operands, no memory traffic), five times each, print one JSON line and exit")
     ap.add_argument("--unfused", action="store_true",
                     help="call gpt2_backward and gpt2_adamw_step separately instead of gpt2_backward_adamw")
     ap.add_argument("--decode", action="store_true",
@@ -153,6 +159,19 @@ def main():
 
     import synth
     from transformer_lm_fwd_amd import Arena, binding
+
+    if args.mfma_probe:
+        torch.cuda.set_device(0)
+        kinds = {"bf16_32x32x16": binding.MFMA_BF16_32X32X16, "bf16_16x16x32": binding.MFMA_BF16_16X16X32,
+                 "mxfp8_32x32x64": binding.MFMA_MXFP8_32X32X64}
+        peaks = {"bf16_32x32x16": 2500.0, "bf16_16x16x32": 2500.0, "mxfp8_32x32x64": 5000.0}
+        out = {}
+        for name, kind in kinds.items():
+            r = [binding.mfma_peak(kind) for _ in range(5)]
+            out[name] = {"tflops_runs": [round(v, 1) for v in r], "tflops_best": round(max(r), 1),
+                         "published_peak": peaks[name], "frac_of_published": round(max(r) / peaks[name], 4)}
+        print(json.dumps({"mfma_probe": out, "unit": "TFLOP/s"}), flush=True)
+        return
 
     if args.decode:
         return decode_bench(args)
@@ -224,6 +243,9 @@ def main():
     if args.kernel_table:
         with open(args.kernel_table, "w") as f:
             json.dump({"workload": w.name, "profile_steps": args.profile_steps, "kernels": stats}, f, indent=1)
+    if args.launch_order:
+        with open(args.launch_order, "w") as f:
+            json.dump({"workload": w.name, "profile_steps": args.profile_steps, "launches": binding.profile_order()}, f)
     roof = None
     if stats:
         dom = stats[0]
@@ -509,10 +531,37 @@ def mx_forward_bench(args):
 
     ms_bf, loss_bf = timed(binding.GPT2_GEMM_BF16)
     ms_mx, loss_mx = timed(binding.GPT2_GEMM_MXFP8)
+
+    def timed_step(fmt):
+        # full training steps (forward with the format's products, the bf16 backward,
+        # AdamW fused into it), from the same starting weights for both formats
+        arena.load_params(params)
+        arena.tensor(binding.T_ADAM_M).zero_()
+        arena.tensor(binding.T_ADAM_V).zero_()
+        arena.set_gemm_format(fmt)
+        t = 0
+        for _ in range(max(1, args.warmup)):
+            t += 1
+            arena.step(xt, yt, w, t, check_ids=False)
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(args.steps):
+            t += 1
+            arena.step(xt, yt, w, t, check_ids=False)
+        end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / args.steps, arena.loss()
+
+    st_bf, sl_bf = timed_step(binding.GPT2_GEMM_BF16)
+    st_mx, sl_mx = timed_step(binding.GPT2_GEMM_MXFP8)
+    arena.load_params(params)
     tokens = w.B * w.T
     value = tokens / (ms_mx / 1e3)
     log(f"[bench] forward: bf16 {ms_bf:.3f} ms ({tokens / ms_bf:,.0f}K tok/s, loss {loss_bf:.5f}); "
         f"mxfp8 {ms_mx:.3f} ms ({tokens / ms_mx:,.0f}K tok/s, loss {loss_mx:.5f})")
+    log(f"[bench] training step (MX or bf16 forward, bf16 backward, AdamW): bf16 {st_bf:.3f} ms "
+        f"({tokens / st_bf:,.0f}K tok/s); mxfp8 forward {st_mx:.3f} ms ({tokens / st_mx:,.0f}K tok/s)")
 
     binding.profile(True)
     pk = max(1, args.profile_steps)
@@ -563,6 +612,11 @@ def mx_forward_bench(args):
                    "heads": m.num_heads, "channels": m.channels, "vocab": m.vocab_size},
         "bf16_forward": {"ms_per_step": round(ms_bf, 5), "value": round(tokens / (ms_bf / 1e3), 1),
                          "loss": loss_bf},
+        "training_step": {"mxfp8_forward": {"ms_per_step": round(st_mx, 5),
+                                            "value": round(tokens / (st_mx / 1e3), 1), "loss": sl_mx},
+                          "bf16": {"ms_per_step": round(st_bf, 5), "value": round(tokens / (st_bf / 1e3), 1),
+                                   "loss": sl_bf},
+                          "unit": "tokens/s", "note": "MX FP8 forward products, bf16 backward, AdamW"},
         "mxfp8_loss": loss_mx,
         "roofline": roof, "cpu_baseline": cpu,
     }

@@ -196,6 +196,13 @@ int gpt2_profile(int enable);
  * Errors: GPT2_E_HIP if an event cannot be read. */
 int gpt2_profile_read(gpt2_kernel_stat* out, int32_t max_entries, int32_t* n_entries);
 
+/* Order of the recorded launches: out[i] (i < max_entries) receives the index, in
+ * the name-sorted array gpt2_profile_read fills, of the i-th launch recorded since
+ * gpt2_profile(1); *n_entries receives the number of recorded launches.  Each
+ * recorded launch is one kernel dispatch of the library, so a trace of the same
+ * steps can be matched to kernel names dispatch by dispatch.  No GPU work. */
+int gpt2_profile_order(int32_t* out, int32_t max_entries, int32_t* n_entries);
+
 /* Matrix-core rate probe (measurement only).  Launches, on `stream`, a kernel in
  * which every wave of 2 per SIMD issues independent chains of one MFMA form on
  * register operands (no memory traffic), times four launches with HIP events,

@@ -26,7 +26,7 @@ T_LN2, T_LN2_STATS, T_FCH, T_FCH_GELU, T_RESIDUAL3 = 22, 23, 24, 25, 26
 
 EXPORTS = ("gpt2_alloc_arena", "gpt2_free_arena", "gpt2_sync_weights", "gpt2_forward", "gpt2_backward",
            "gpt2_adamw_step", "gpt2_backward_adamw", "gpt2_tensor_info", "gpt2_num_parameters", "gpt2_profile",
-           "gpt2_profile_read", "gpt2_gen_alloc", "gpt2_gen_free", "gpt2_gen_length", "gpt2_gen_prefill",
+           "gpt2_profile_read", "gpt2_profile_order", "gpt2_gen_alloc", "gpt2_gen_free", "gpt2_gen_length", "gpt2_gen_prefill",
            "gpt2_gen_decode", "gpt2_sample_topk", "gpt2_tokens_count", "gpt2_tokens_batch",
            "gpt2_params_permute", "gpt2_checkpoint_write", "gpt2_checkpoint_read", "gpt2_set_position_encoding",
            "gpt2_num_parameters_block", "gpt2_alloc_arena_block",
@@ -83,6 +83,7 @@ def lib():
         L.gpt2_last_error.restype = ctypes.c_char_p
         L.gpt2_profile.argtypes = [ctypes.c_int]
         L.gpt2_profile_read.argtypes = [ctypes.POINTER(gpt2_kernel_stat), i32, ctypes.POINTER(i32)]
+        L.gpt2_profile_order.argtypes = [ctypes.POINTER(i32), i32, ctypes.POINTER(i32)]
         L.gpt2_mfma_peak.argtypes = [i32, ctypes.POINTER(ctypes.c_double), vp]
         L.gpt2_gen_alloc.argtypes = [vp, i32, i32, vp, sz, ctypes.POINTER(sz), ctypes.POINTER(vp)]
         L.gpt2_gen_free.argtypes = [vp]
@@ -154,6 +155,16 @@ def profile_read():
     _check(lib().gpt2_profile_read(arr, n.value, ctypes.byref(n)))
     return [dict(name=r.name.decode(), launches=int(r.launches), total_ms=float(r.total_ms), flops=float(r.flops),
                  bytes=float(r.bytes)) for r in arr[:n.value]]
+
+
+def profile_order():
+    """Kernel names of the recorded launches in launch order (one entry per dispatch)."""
+    names = [s["name"] for s in profile_read()]
+    n = ctypes.c_int32(0)
+    _check(lib().gpt2_profile_order(None, 0, ctypes.byref(n)))
+    arr = (ctypes.c_int32 * max(1, n.value))()
+    _check(lib().gpt2_profile_order(arr, n.value, ctypes.byref(n)))
+    return [names[i] for i in arr[:n.value]]
 
 
 MFMA_BF16_32X32X16, MFMA_BF16_16X16X32, MFMA_MXFP8_32X32X64 = 0, 1, 2

@@ -106,6 +106,21 @@ int gpt2_profile_read(gpt2_kernel_stat* out, int32_t max_entries, int32_t* n_ent
     return GPT2_OK;
 }
 
+int gpt2_profile_order(int32_t* out, int32_t max_entries, int32_t* n_entries) {
+    std::lock_guard<std::mutex> lk(gpt2::g_mu);
+    std::map<std::string, int32_t> rank;
+    for (const auto& r : gpt2::g_recs) rank.emplace(r.name, 0);
+    int32_t k = 0;
+    for (auto& kv : rank) kv.second = k++;
+    int32_t n = 0;
+    for (const auto& r : gpt2::g_recs) {
+        if (out && n < max_entries) out[n] = rank[r.name];
+        ++n;
+    }
+    if (n_entries) *n_entries = n;
+    return GPT2_OK;
+}
+
 }  // extern "C"
 
 // ---------------------------------------------------------------- matrix-core rate probe
@@ -124,6 +139,22 @@ typedef int i32x8_p __attribute__((ext_vector_type(8)));
 
 constexpr int NCH = 4;
 
+// Operand bits that look like trained-model data (mixed signs, full mantissas): the
+// matrix cores draw more power on such data than on small integers or zeros, and the
+// clock they hold under load follows.
+__device__ __forceinline__ uint32_t probe_bits(int lane, int e) {
+    uint32_t h = (uint32_t)(lane * 8 + e) * 2654435761u;
+    h ^= h >> 15;
+    h *= 2246822519u;
+    h ^= h >> 13;
+    // E4M3 bytes / bf16 halves with exponents near 1: keep sign and mantissa bits random
+    return (h & 0x87878787u) | 0x30303030u;
+}
+__device__ __forceinline__ float probe_value(int lane, int e) {
+    const uint32_t h = probe_bits(lane, e);
+    return ((float)(h & 0xffffu) / 65536.0f - 0.5f) * 0.125f;
+}
+
 template <int KIND>
 __global__ __launch_bounds__(256) void mfma_rate_kernel(int iters, float* sink, int store) {
     const int lane = threadIdx.x & 63;
@@ -136,14 +167,14 @@ __global__ __launch_bounds__(256) void mfma_rate_kernel(int iters, float* sink, 
         if constexpr (KIND == 0) {
             bf16x8_p a, b;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) a[e] = (__bf16)(float)(lane + e), b[e] = (__bf16)(float)(lane - e);
+            for (int e = 0; e < 8; ++e) a[e] = (__bf16)probe_value(lane, e), b[e] = (__bf16)probe_value(lane + 64, e);
             for (int i = 0; i < iters; ++i)
 #pragma unroll
                 for (int c = 0; c < NCH; ++c) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
         } else {
             i32x8_p a, b;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) a[e] = 0x38383838 + lane, b[e] = 0x30303030 + e;
+            for (int e = 0; e < 8; ++e) a[e] = (int)probe_bits(lane, e), b[e] = (int)probe_bits(lane + 64, e);
             for (int i = 0; i < iters; ++i)
 #pragma unroll
                 for (int c = 0; c < NCH; ++c)
@@ -165,7 +196,7 @@ __global__ __launch_bounds__(256) void mfma_rate_kernel(int iters, float* sink, 
             for (int e = 0; e < 4; ++e) acc[c][e] = 0.f;
         bf16x8_p a, b;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) a[e] = (__bf16)(float)(lane + e), b[e] = (__bf16)(float)(lane - e);
+        for (int e = 0; e < 8; ++e) a[e] = (__bf16)probe_value(lane, e), b[e] = (__bf16)probe_value(lane + 64, e);
         for (int i = 0; i < iters; ++i)
 #pragma unroll
             for (int c = 0; c < NCH; ++c) acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[c], 0, 0, 0);
