@@ -91,7 +91,10 @@ int gpt2_free_arena(gpt2_arena* arena);
  * master parameters directly (e.g. loading weights). */
 int gpt2_sync_weights(gpt2_arena* arena, void* stream);
 
-/* Forward pass.
+/* Forward pass of the GPT-2 block stack ("GPT-2 from scratch with torch", 模型结构:
+ * token and position embeddings, L pre-LayerNorm blocks of causal self-attention and a
+ * GELU MLP, final LayerNorm, logits through the tied token embedding; the loss is the
+ * mean softmax cross-entropy, "从头搭建GPT(Andrej Karpathy) 笔记", 计算loss).
  *  d_inputs   device int32 [B, T] token ids, row-major, each in [0, vocab_size).
  *  d_targets  device int32 [B, T] next-token ids (inputs shifted by one), or NULL.
  * Without targets the logits [B*T, padded_vocab] are left in GPT2_T_LOGITS.
@@ -100,18 +103,42 @@ int gpt2_sync_weights(gpt2_arena* arena, void* stream);
  * d loss / d logits, ready for gpt2_backward.  Ids are not range-checked on the
  * device: an id outside [0, vocab_size) is undefined behaviour (the Python
  * binding checks them on the host).  Both arrays must stay valid until the
- * enqueued work has run (the backward pass reads d_inputs again). */
+ * enqueued work has run (the backward pass reads d_inputs again).  With B >= 2 (and
+ * the MX format and the launch profiler off) the batch runs as two groups of
+ * sequences, one of them on the arena's second stream (gpt2_set_side_stream), forked
+ * from and joined back into `stream`; the results are bitwise those of one pass. */
 int gpt2_forward(gpt2_arena* arena, const int32_t* d_inputs, const int32_t* d_targets, void* stream);
 
+/* Validation loss: the mean over `num_batches` batches of the forward pass's mean loss
+ * ("1000 行 C 代码完成 GPT-2 训练的 LLM.c", 快速开始吧: the trainer reports a val loss
+ * averaged over a fixed number of validation batches).
+ *  d_inputs, d_targets  device int32 [num_batches, B, T] token ids and next-token ids
+ *  d_loss               device fp32 scalar receiving the mean (batch means added in
+ *                       batch order, each times 1/num_batches)
+ * No backward pass may follow (GPT2_E_STATE until the next gpt2_forward with targets).
+ * Errors: GPT2_E_INVAL for NULL pointers or num_batches < 1; those of gpt2_forward. */
+int gpt2_eval_loss(gpt2_arena* arena, const int32_t* d_inputs, const int32_t* d_targets, int32_t num_batches,
+                   float* d_loss, void* stream);
+
 /* Backward pass of the last forward (which must have had targets, else
- * GPT2_E_STATE).  Overwrites every fp32 parameter gradient (GPT2_T_GRADS): one
- * micro-batch per step, no accumulation.  The parameter-gradient products run on
- * a second, library-owned stream (created on the first call, destroyed by
- * gpt2_free_arena) that forks from and joins back into `stream` with events, so
- * all of the pass is ordered before whatever the caller enqueues on `stream`
- * next.  Results are bitwise reproducible run to run.  Two passes on the same
- * arena must not be enqueued on different streams concurrently. */
+ * GPT2_E_STATE): the gradient of the mean loss with respect to every parameter, by
+ * the chain rule through the forward's layers in reverse ("1000 行 C 代码完成 GPT-2
+ * 训练的 LLM.c": forward, backward and update, each layer's backward hand-written).
+ * Overwrites every fp32 parameter gradient (GPT2_T_GRADS): one micro-batch per step,
+ * no accumulation.  The parameter-gradient products run on the arena's second stream
+ * (gpt2_set_side_stream) that forks from and joins back into `stream` with events, so
+ * all of the pass is ordered before whatever the caller enqueues on `stream` next.
+ * Results are bitwise reproducible run to run.  Two passes on the same arena must not
+ * be enqueued on different streams concurrently. */
 int gpt2_backward(gpt2_arena* arena, void* stream);
+
+/* Gives the arena the second stream its forward and backward passes overlap work on
+ * (a stream of the same device, other than the ones the passes are called with).  The
+ * caller keeps ownership: it must outlive every pass enqueued until the next call or
+ * gpt2_free_arena.  NULL (the default) lets the library create its own stream on first
+ * use and destroy it in gpt2_free_arena; a stream the library created earlier is
+ * synchronized and destroyed here.  Errors: GPT2_E_INVAL for a NULL arena, GPT2_E_HIP. */
+int gpt2_set_side_stream(gpt2_arena* arena, void* stream);
 
 /* AdamW over every parameter ("1000 行 C 代码...": the loop ends with an Adam
  * update; decoupled weight decay, bias correction, t counted from 1):
@@ -160,7 +187,11 @@ enum gpt2_tensor_id {
     GPT2_T_RESIDUAL3 = 26   /* act [B*T, C] block output                               */
 };
 
-/* Where a tensor lives in the arena.  All outputs may be NULL.
+/* Where a tensor lives in the arena (the single up-front allocation of "1000 行 C 代码
+ * 完成 GPT-2 训练的 LLM.c", laid out by gpt2_alloc_arena).  All outputs may be NULL.
+ * A layer index and a two-dimensional shape with a row stride are part of the answer:
+ * per-layer tensors are addressed one layer at a time, and some rows are padded
+ * (the logits to a multiple of 64 columns).
  *  byte_offset  from device_base (256-byte aligned)
  *  rows, cols   logical shape; row_stride >= cols elements between rows
  *  dtype        GPT2_FP32 or GPT2_BF16 ("act" tensors follow the arena dtype)

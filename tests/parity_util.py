@@ -66,7 +66,7 @@ def per_tensor(vec, m):
 
 
 def report(label, d):
-    print(label + ": " + ", ".join(f"{k}={v:.3g}" for k, v in d.items()), flush=True)
+    print(label + ": " + ", ".join(f"{k}={v:.5g}" for k, v in d.items()), flush=True)
 
 
 def rand_params(m, seed=7):

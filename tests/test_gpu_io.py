@@ -88,3 +88,17 @@ def test_eval_loss_over_a_token_file_matches_the_oracle(tmp_path):
         ref += o.forward(x, y) / 3
     print(f"eval loss {got:.7f} oracle {ref:.7f}", flush=True)
     assert abs(got - ref) <= FP32_LOSS_REL * abs(ref)
+    # the mean is taken behind the C ABI in batch order: averaging the per-batch
+    # forward losses one by one gives it to a few fp32 ulps (a fused multiply-add may
+    # round once where this sum rounds twice)
+    by_one = np.float32(0.0)
+    for i in range(3):
+        x, y = oracle.token_batch(ids, w.B, w.T, i)
+        a.forward(x, y)
+        by_one = np.float32(by_one + np.float32(a.loss()) * np.float32(1 / 3))
+    assert abs(got - float(by_one)) <= 4 * float(np.spacing(by_one))
+    # the logits now hold a validation batch's gradient: no backward pass may follow
+    a.eval_loss(path, 1)
+    with pytest.raises(b.Gpt2Error):
+        a.backward()
+    a.close()

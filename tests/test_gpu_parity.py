@@ -239,6 +239,31 @@ def test_step_is_deterministic(dtype, NH):
     np.testing.assert_array_equal(outs[0][1], outs[1][1])
 
 
+def test_caller_side_stream_matches_library_stream():
+    # The second stream of the forward and backward passes may be the caller's (the
+    # binding passes a torch stream) or one the library creates: results are bitwise
+    # the same.
+    import ctypes
+    b = _b()
+    w = Workload("side", ModelShape(160, 301, 2, 2, 128), 4, 96, "bf16", "zipf", index=30)
+    announce("side_stream_bf16", w)
+    p = rand_params(w.model, seed=13)
+    x, y = synth.inputs_targets(w)
+    outs = []
+    for own in (False, True):
+        a = gpu_arena(w, p)
+        if own:
+            b._check(b.lib().gpt2_set_side_stream(a.h, None))
+        for t in (1, 2):
+            a.step(x, y, w, t)
+        a.forward(x, y)
+        outs.append([a.loss()] + [to_np(a.tensor(i)).copy() for i in (b.T_PARAMS, b.T_GRADS, b.T_LOGITS)])
+        a.close()
+    assert outs[0][0] == outs[1][0]
+    for u, v in zip(outs[0][1:], outs[1][1:]):
+        np.testing.assert_array_equal(u, v)
+
+
 @pytest.mark.parametrize("dtype,NH", [("fp32", 4), ("bf16", 2)])
 def test_fused_backward_adamw_matches_separate_calls(dtype, NH):
     # gpt2_backward_adamw reorders only when each AdamW update runs; gradients,

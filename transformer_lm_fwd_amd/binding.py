@@ -26,7 +26,7 @@ T_LN2, T_LN2_STATS, T_FCH, T_FCH_GELU, T_RESIDUAL3 = 22, 23, 24, 25, 26
 
 EXPORTS = ("gpt2_alloc_arena", "gpt2_free_arena", "gpt2_sync_weights", "gpt2_forward", "gpt2_backward",
            "gpt2_adamw_step", "gpt2_backward_adamw", "gpt2_tensor_info", "gpt2_num_parameters", "gpt2_profile",
-           "gpt2_profile_read", "gpt2_profile_order", "gpt2_gen_alloc", "gpt2_gen_free", "gpt2_gen_length", "gpt2_gen_prefill",
+           "gpt2_profile_read", "gpt2_profile_order", "gpt2_set_side_stream", "gpt2_eval_loss", "gpt2_gen_alloc", "gpt2_gen_free", "gpt2_gen_length", "gpt2_gen_prefill",
            "gpt2_gen_decode", "gpt2_sample_topk", "gpt2_tokens_count", "gpt2_tokens_batch",
            "gpt2_params_permute", "gpt2_checkpoint_write", "gpt2_checkpoint_read", "gpt2_set_position_encoding",
            "gpt2_num_parameters_block", "gpt2_alloc_arena_block",
@@ -84,6 +84,9 @@ def lib():
         L.gpt2_profile.argtypes = [ctypes.c_int]
         L.gpt2_profile_read.argtypes = [ctypes.POINTER(gpt2_kernel_stat), i32, ctypes.POINTER(i32)]
         L.gpt2_profile_order.argtypes = [ctypes.POINTER(i32), i32, ctypes.POINTER(i32)]
+        L.gpt2_set_side_stream.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        L.gpt2_eval_loss.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, i32, ctypes.c_void_p,
+                                     ctypes.c_void_p]
         L.gpt2_mfma_peak.argtypes = [i32, ctypes.POINTER(ctypes.c_double), vp]
         L.gpt2_gen_alloc.argtypes = [vp, i32, i32, vp, sz, ctypes.POINTER(sz), ctypes.POINTER(vp)]
         L.gpt2_gen_free.argtypes = [vp]
@@ -201,6 +204,10 @@ class Arena:
                                             ctypes.c_void_p(self.base.data_ptr()), self.nbytes, None,
                                             ctypes.byref(h)))
         self.h = h
+        # the second stream of the forward and backward passes comes from torch
+        # (default priority), like the memory
+        self.side_stream = torch.cuda.Stream(device=self.buf.device)
+        _check(lib().gpt2_set_side_stream(self.h, ctypes.c_void_p(self.side_stream.cuda_stream)))
         self.n_params = num_parameters(m)
         self._inputs = None
         self._targets = None
@@ -278,15 +285,18 @@ class Arena:
     def loss(self) -> float:
         return float(self.tensor(T_LOSS).item())
 
-    def eval_loss(self, path: str, num_batches: int, first: int = 0) -> float:
+    def eval_loss(self, path: str, num_batches: int, first: int = 0, stream=None) -> float:
         """Mean forward loss over batches first .. first + num_batches - 1 of an int32
-        token file (the validation loss of a training run; no backward pass)."""
-        total = 0.0
-        for i in range(first, first + num_batches):
-            x, y = tokens_batch(path, self.B, self.T, i)
-            self.forward(x, y)
-            total += self.loss()
-        return total / num_batches
+        token file (the validation loss of a training run; no backward pass): the
+        batches are read on the host and the mean is taken by gpt2_eval_loss."""
+        import torch
+        xs, ys = zip(*(tokens_batch(path, self.B, self.T, i) for i in range(first, first + num_batches)))
+        x = torch.stack([self._ids(v) for v in xs])
+        y = torch.stack([self._ids(v) for v in ys])
+        out = torch.empty(1, dtype=torch.float32, device=self.base.device)
+        _check(lib().gpt2_eval_loss(self.h, ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(y.data_ptr()),
+                                    num_batches, ctypes.c_void_p(out.data_ptr()), _stream_ptr(stream)))
+        return float(out.item())
 
     # ------------------------------------------------------------------ checkpoints
     def save_checkpoint(self, path: str, step: int, moments: bool = True) -> None:

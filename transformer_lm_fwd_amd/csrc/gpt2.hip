@@ -63,10 +63,13 @@ struct gpt2_arena {
     bool loss_ready;
     bool census_armed = false;  // the token census holds its idle state (set by the first backward)
     const int32_t* inputs;
-    // Backward concurrency: parameter-gradient work runs on `side`.  rd_* mark the
-    // side stream's last read of each ring buffer; fork events order side work
-    // after main-stream producers.  Created on the first backward pass.
+    // Concurrency: parameter-gradient work of the backward pass and one half of a split
+    // forward pass run on `side`.  rd_* mark the side stream's last read of each ring
+    // buffer; fork events order side work after main-stream producers.  The stream is
+    // the caller's (gpt2_set_side_stream) or, failing that, created on first use.
     hipStream_t side = nullptr;
+    bool side_owned = false;
+    bool events_ready = false;
     hipEvent_t rd_res[4] = {}, rd_fch[2] = {}, rd_qkv[2] = {}, ev_wte = nullptr, ev_end = nullptr;
     hipEvent_t fork[8] = {};
     int fork_next = 0;
@@ -264,15 +267,21 @@ int hip_check(hipError_t e, const char* what) {
     } while (0)
 
 int ensure_streams(gpt2_arena* a) {
-    if (a->side) return GPT2_OK;
-    if (hipStreamCreateWithFlags(&a->side, hipStreamNonBlocking) != hipSuccess)
-        return fail(GPT2_E_HIP, "cannot create the side stream");
+    if (!a->side) {
+        if (hipStreamCreateWithFlags(&a->side, hipStreamNonBlocking) != hipSuccess) {
+            a->side = nullptr;
+            return fail(GPT2_E_HIP, "cannot create the side stream");
+        }
+        a->side_owned = true;
+    }
+    if (a->events_ready) return GPT2_OK;
     auto mk = [](hipEvent_t* e) { return hipEventCreateWithFlags(e, hipEventDisableTiming) == hipSuccess; };
     bool ok = mk(&a->ev_wte) && mk(&a->ev_end);
     for (auto& e : a->rd_res) ok = ok && mk(&e);
     for (auto& e : a->rd_fch) ok = ok && mk(&e);
     for (auto& e : a->rd_qkv) ok = ok && mk(&e);
     for (auto& e : a->fork) ok = ok && mk(&e);
+    a->events_ready = ok;
     return ok ? GPT2_OK : fail(GPT2_E_HIP, "cannot create events");
 }
 
@@ -286,16 +295,21 @@ int stream_wait(gpt2_arena* a, hipStream_t to, hipStream_t from) {
 }
 
 void destroy_streams(gpt2_arena* a) {
-    if (!a->side) return;
-    hipStreamDestroy(a->side);
-    auto rm = [](hipEvent_t e) { if (e) hipEventDestroy(e); };
+    if (a->side && a->side_owned) hipStreamDestroy(a->side);
+    a->side = nullptr;
+    a->side_owned = false;
+    if (!a->events_ready) return;
+    auto rm = [](hipEvent_t& e) {
+        if (e) hipEventDestroy(e);
+        e = nullptr;
+    };
     rm(a->ev_wte);
     rm(a->ev_end);
-    for (auto e : a->rd_res) rm(e);
-    for (auto e : a->rd_fch) rm(e);
-    for (auto e : a->rd_qkv) rm(e);
-    for (auto e : a->fork) rm(e);
-    a->side = nullptr;
+    for (auto& e : a->rd_res) rm(e);
+    for (auto& e : a->rd_fch) rm(e);
+    for (auto& e : a->rd_qkv) rm(e);
+    for (auto& e : a->fork) rm(e);
+    a->events_ready = false;
 }
 
 // AdamW hyper-parameters with the bias corrections of step t folded in.
@@ -964,6 +978,18 @@ int gpt2_sync_weights(gpt2_arena* a, void* stream) {
     return GPT2_OK;
 }
 
+int gpt2_set_side_stream(gpt2_arena* a, void* stream) {
+    if (!a) return fail(GPT2_E_INVAL, "arena is NULL");
+    if (a->side && a->side_owned) {
+        // work already enqueued there must not be cut off by the destroy
+        if (hipStreamSynchronize(a->side) != hipSuccess) return fail(GPT2_E_HIP, "hipStreamSynchronize");
+        hipStreamDestroy(a->side);
+    }
+    a->side = (hipStream_t)stream;
+    a->side_owned = false;
+    return GPT2_OK;
+}
+
 int gpt2_forward(gpt2_arena* a, const int32_t* d_inputs, const int32_t* d_targets, void* stream) {
     if (!a || !d_inputs) return fail(GPT2_E_INVAL, "arena and inputs are required");
     a->loss_ready = false;
@@ -972,6 +998,24 @@ int gpt2_forward(gpt2_arena* a, const int32_t* d_inputs, const int32_t* d_target
                                    : Model<float>(a, (hipStream_t)stream).forward(d_inputs, d_targets);
     if (rc == GPT2_OK && d_targets) a->loss_ready = true;
     return rc;
+}
+
+int gpt2_eval_loss(gpt2_arena* a, const int32_t* d_inputs, const int32_t* d_targets, int32_t num_batches,
+                   float* d_loss, void* stream) {
+    if (!a || !d_inputs || !d_targets || !d_loss) return fail(GPT2_E_INVAL, "arena, tokens and loss are required");
+    if (num_batches < 1) return fail(GPT2_E_INVAL, "num_batches must be >= 1");
+    const int64_t bt = (int64_t)a->B * a->T;
+    const float scale = 1.0f / (float)num_batches;
+    hipStream_t s = (hipStream_t)stream;
+    for (int32_t i = 0; i < num_batches; ++i) {
+        int rc = gpt2_forward(a, d_inputs + i * bt, d_targets + i * bt, stream);
+        if (rc) return rc;
+        if ((rc = hip_check(scaled_accumulate(d_loss, at<float>(a, a->loss), scale, i == 0, s), "loss mean")))
+            return rc;
+    }
+    a->loss_ready = false;  // the logits hold the last batch's gradient, not a step's
+    a->inputs = nullptr;
+    return GPT2_OK;
 }
 
 int gpt2_backward(gpt2_arena* a, void* stream) {

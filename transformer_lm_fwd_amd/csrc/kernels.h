@@ -114,6 +114,7 @@ template <class T>
 hipError_t crossentropy_fused(T* logits, float* losses, const int32_t* targets, int N, int V, int64_t ldz,
                               float dscale, hipStream_t s);
 hipError_t mean_loss(float* loss, const float* losses, int N, hipStream_t s);
+hipError_t scaled_accumulate(float* dst, const float* src, float scale, bool first, hipStream_t s);
 // dwte[tok] += dx rows (deterministic), dwpe[t] = sum_b dx[b, t] for t < T, 0 for T <= t < P.
 // first / count: int [V] scratch, INT_MAX / 0 on entry (token_census_reset) and on return.
 // AdamW of a parameter range inside another kernel (p null: no update).

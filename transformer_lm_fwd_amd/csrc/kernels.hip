@@ -638,6 +638,18 @@ __global__ __launch_bounds__(1024) void mean_loss_kernel(float* loss, const floa
     }
 }
 
+// dst = src * scale (first) or dst += src * scale: a mean over a sequence of scalars
+// enqueued one by one on a stream, added in that order.
+__global__ void scaled_accumulate_kernel(float* dst, const float* src, float scale, int first) {
+    if (threadIdx.x == 0) dst[0] = first ? src[0] * scale : dst[0] + src[0] * scale;
+}
+
+hipError_t scaled_accumulate(float* dst, const float* src, float scale, bool first, hipStream_t s) {
+    ProfScope prof(s, "scaled_accumulate", 0, 12.0);
+    hipLaunchKernelGGL(scaled_accumulate_kernel, dim3(1), dim3(64), 0, s, dst, src, scale, first ? 1 : 0);
+    return hipGetLastError();
+}
+
 hipError_t mean_loss(float* loss, const float* losses, int N, hipStream_t s) {
     ProfScope prof(s, "mean_loss", 0, 4.0 * N);
     hipLaunchKernelGGL(mean_loss_kernel, dim3(1), dim3(1024), 0, s, loss, losses, N);
