@@ -83,6 +83,8 @@ def lib():
         L.orc_set_mx.argtypes = [vp, ctypes.c_int]
         L.orc_mx_roundtrip.argtypes = [vp, vp, i64, ctypes.c_int]
         L.orc_mx_roundtrip.restype = None
+        L.orc_matmul_backward_input_mx.argtypes = [vp, vp, i64, ctypes.c_int, ctypes.c_int, vp]
+        L.orc_matmul_backward_input_mx.restype = None
         L.orc_set_num_threads.argtypes = [i32]
         L.orc_set_num_threads.restype = None
         _lib = L
@@ -150,6 +152,19 @@ def mx_roundtrip(x) -> np.ndarray:
     rows, K = x.shape
     y = np.empty_like(x)
     lib().orc_mx_roundtrip(_ptr(x), _ptr(y), rows, K)
+    return y
+
+
+def matmul_backward_input_mx(dout, w) -> np.ndarray:
+    """dinp = dout [N, OC] w [OC, IC] with both operands through bf16 and the MX
+    encoding in blocks of 32 along OC (dout's rows, and the columns of w)."""
+    dout = np.ascontiguousarray(dout, dtype=np.float64)
+    w = np.ascontiguousarray(w, dtype=np.float64)
+    N, OC = dout.shape
+    OC2, IC = w.shape
+    assert OC == OC2
+    y = np.empty((N, IC), np.float64)
+    lib().orc_matmul_backward_input_mx(_ptr(dout), _ptr(w), N, IC, OC, _ptr(y))
     return y
 
 
@@ -229,10 +244,13 @@ class Oracle:
         if lib().orc_set_rotary(self.h, 1 if on else 0, float(base)):
             raise ValueError(lib().orc_last_error().decode())
 
-    def set_mx(self, on: bool = True):
+    def set_mx(self, on=True):
         """MX FP8 operands (bf16 values through the E4M3 / E8M0 block encoding) for the
-        forward pass's block and lm_head products; the backward pass is unchanged."""
-        if lib().orc_set_mx(self.h, 1 if on else 0):
+        forward pass's block and lm_head products (on = True or 1), and with on = 2 also
+        for the backward pass's input-gradient products of the same layers; the weight
+        gradients keep the plain operands (straight-through)."""
+        mode = int(on) if not isinstance(on, bool) else (1 if on else 0)
+        if lib().orc_set_mx(self.h, mode):
             raise ValueError(lib().orc_last_error().decode())
 
     def backward(self):

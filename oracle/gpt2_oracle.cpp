@@ -522,9 +522,9 @@ static void swiglu_backward(R* dgu, const R* dout, const R* gu, int64_t N, int64
         }
 }
 
+// Input gradient of a linear layer: dinp [N, IC] += dout [N, OC] w [OC, IC].
 template <class R>
-static void matmul_backward(R* dinp, R* dw, R* dbias, const R* dout, const R* inp, const R* w,
-                            int64_t N, int IC, int OC) {
+static void matmul_backward_input(R* dinp, const R* dout, const R* w, int64_t N, int IC, int OC) {
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < N; ++i) {
         R* dx = dinp + i * IC;
@@ -535,6 +535,28 @@ static void matmul_backward(R* dinp, R* dw, R* dbias, const R* dout, const R* in
             for (int k = 0; k < IC; ++k) dx[k] += g * wr[k];
         }
     }
+}
+
+// The same with both operands taken through the MX encoding along the contraction
+// (OC): dout's rows in blocks of 32 outputs, and for every input feature k the column
+// w[:, k] in blocks of 32 outputs -- the rows of w^T, the layout a matrix core takes.
+template <class R>
+static void matmul_backward_input_mx(R* dinp, const R* dout, const R* w, int64_t N, int IC, int OC) {
+    std::vector<R> dq((size_t)N * OC), wt((size_t)IC * OC), wtq((size_t)IC * OC), wq((size_t)OC * IC);
+    mx_roundtrip(dq.data(), dout, N, OC);
+    for (int j = 0; j < OC; ++j)
+        for (int k = 0; k < IC; ++k) wt[(size_t)k * OC + j] = w[(size_t)j * IC + k];
+    mx_roundtrip(wtq.data(), wt.data(), IC, OC);
+    for (int j = 0; j < OC; ++j)
+        for (int k = 0; k < IC; ++k) wq[(size_t)j * IC + k] = wtq[(size_t)k * OC + j];
+    matmul_backward_input(dinp, dq.data(), wq.data(), N, IC, OC);
+}
+
+template <class R>
+static void matmul_backward(R* dinp, R* dw, R* dbias, const R* dout, const R* inp, const R* w,
+                            int64_t N, int IC, int OC, bool mx_dx = false) {
+    if (mx_dx) matmul_backward_input_mx(dinp, dout, w, N, IC, OC);
+    else matmul_backward_input(dinp, dout, w, N, IC, OC);
 #pragma omp parallel for schedule(static)
     for (int j = 0; j < OC; ++j) {
         R* dwr = dw + (int64_t)j * IC;
@@ -667,8 +689,10 @@ struct Model : ModelBase {
     bool rotary = false;
     double rope_base = 10000.0;
     // MX FP8 operands for the forward pass's block and lm_head products (the backward
-    // pass uses the stored activations and weights as they are: straight-through)
-    bool mx = false;
+    // pass uses the stored activations and weights as they are: straight-through);
+    // mx_dx: also for the input-gradient products of those layers in the backward pass
+    // (the weight gradients keep the plain operands)
+    bool mx = false, mx_dx = false;
     std::vector<std::vector<R>> qkv_rot;
     std::vector<R> dqkv_rot;
 
@@ -756,7 +780,7 @@ struct Model : ModelBase {
             if (llama) rmsnorm_backward(dx, dw, dy, x, w, rstd, BT, C);
             else layernorm_backward(dx, dw, db, dy, x, w, mean, rstd, BT, C);
         };
-        matmul_backward(dA(A_LNF), G.wte, (R*)nullptr, dA(A_LOGITS), A(A_LNF), P.wte, BT, C, V);
+        matmul_backward(dA(A_LNF), G.wte, (R*)nullptr, dA(A_LOGITS), A(A_LNF), P.wte, BT, C, V, mx_dx);
         R* dxL = dA(A_RESIDUAL3, L - 1);
         norm_bwd(dxL, G.lnfw, G.lnfb, dA(A_LNF), A(A_RESIDUAL3, L - 1), P.lnfw, A(A_LNF_MEAN), A(A_LNF_RSTD));
         for (int l = L - 1; l >= 0; --l) {
@@ -774,17 +798,17 @@ struct Model : ModelBase {
                                 (int)(2 * H));
             } else {
                 matmul_backward(dA(A_FCH_GELU, l), G.t[FCPW][l], G.t[FCPB][l], dA(A_FCPROJ, l), A(A_FCH_GELU, l),
-                                P.t[FCPW][l], BT, 4 * C, C);
+                                P.t[FCPW][l], BT, 4 * C, C, mx_dx);
                 gelu_backward(dA(A_FCH, l), A(A_FCH, l), dA(A_FCH_GELU, l), BT * 4 * C);
                 matmul_backward(dA(A_LN2, l), G.t[FCW][l], G.t[FCB][l], dA(A_FCH, l), A(A_LN2, l), P.t[FCW][l], BT, C,
-                                4 * C);
+                                4 * C, mx_dx);
             }
             norm_bwd(dres2, G.t[LN2W][l], G.t[LN2B][l], dA(A_LN2, l), A(A_RESIDUAL2, l), P.t[LN2W][l],
                      A(A_LN2_MEAN, l), A(A_LN2_RSTD, l));
             // residual2 = x + attproj
             for (int64_t i = 0; i < BT * C; ++i) { dx[i] += dres2[i]; dA(A_ATTPROJ, l)[i] += dres2[i]; }
             matmul_backward(dA(A_ATTY, l), G.t[PROJW][l], gbias(PROJB, l), dA(A_ATTPROJ, l), A(A_ATTY, l),
-                            P.t[PROJW][l], BT, C, C);
+                            P.t[PROJW][l], BT, C, C, mx_dx && !llama);
             if (rotary) {
                 // gradients reach the turned q | k | v, then turn back to the qkv product's output
                 dqkv_rot.assign((size_t)3 * BT * C, R(0));
@@ -796,7 +820,7 @@ struct Model : ModelBase {
                                    A(A_ATT, l), B, T, C, NH);
             }
             matmul_backward(dA(A_LN1, l), G.t[QKVW][l], gbias(QKVB, l), dA(A_QKV, l), A(A_LN1, l), P.t[QKVW][l], BT, C,
-                            3 * C);
+                            3 * C, mx_dx && !llama);
             norm_bwd(dx, G.t[LN1W][l], G.t[LN1B][l], dA(A_LN1, l), x, P.t[LN1W][l], A(A_LN1_MEAN, l),
                      A(A_LN1_RSTD, l));
         }
@@ -972,11 +996,20 @@ int orc_set_rotary(void* h, int on, double base) {
     return 0;
 }
 
-// MX FP8 operands for the forward pass's block and lm_head products on (1) or off (0).
-int orc_set_mx(void* h, int on) {
+// MX FP8 operands: 0 off, 1 for the forward pass's block and lm_head products, 2 for
+// those and for the backward pass's input-gradient products of the same layers.
+int orc_set_mx(void* h, int mode) {
     if (((ModelBase*)h)->s.block != 0) { g_err = "MX products are modelled for the GPT-2 block"; return -1; }
-    ORC_DISPATCH(h, { M->mx = on != 0; M->have_forward = false; });
+    if (mode < 0 || mode > 2) { g_err = "MX mode must be 0, 1 or 2"; return -1; }
+    ORC_DISPATCH(h, { M->mx = mode >= 1; M->mx_dx = mode == 2; M->have_forward = false; });
     return 0;
+}
+
+// dinp [N, IC] = dout [N, OC] w [OC, IC] with both operands through bf16 and the MX
+// encoding along OC (float64).
+void orc_matmul_backward_input_mx(const double* dout, const double* w, int64_t N, int IC, int OC, double* dinp) {
+    std::fill(dinp, dinp + N * IC, 0.0);
+    matmul_backward_input_mx(dinp, dout, w, N, IC, OC);
 }
 
 // y = x [rows, K] taken through bf16 and the MX FP8 encoding and back (float64).

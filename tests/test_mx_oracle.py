@@ -173,3 +173,79 @@ def test_mx_mode_multiplies_the_encoded_operands_of_each_forward_product():
     # the encoding is really applied (3 mantissa bits: the loss moves)
     assert loss_mx != loss_plain
     o.close()
+
+
+def test_cpp_mx_input_gradient_product_matches_the_table_encoder():
+    # dinp = dout w with dout's rows and w's columns (the rows of w^T) encoded in
+    # blocks of 32 along the contraction; OC = 40 leaves a partial block, IC = 24 is
+    # not a multiple of anything in particular.
+    import oracle
+    rng = np.random.default_rng(12)
+    for N, IC, OC in [(6, 24, 40), (3, 64, 96), (2, 8, 33)]:
+        dout = (rng.standard_normal((N, OC)) * np.exp2(rng.integers(-8, 8, (N, OC)))).astype(np.float32)
+        # rows of w at very different scales: a block along OC then spans magnitudes
+        # 2^20 apart (its small values land on E4M3's subnormal steps), a block along
+        # IC does not, so the two directions encode differently
+        w = (rng.standard_normal((OC, IC)) * 0.02 * np.exp2(rng.integers(-10, 10, (OC, 1)))).astype(np.float32)
+        ref = _mx_operand(dout) @ _mx_operand(w.T).T
+        got = oracle.matmul_backward_input_mx(dout, w)
+        np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-14)
+        # a transposed reading (blocks along IC instead of OC) is a different product
+        wrong = _mx_operand(dout) @ _mx_operand(w)
+        assert not np.allclose(got, wrong, rtol=1e-9, atol=1e-12)
+
+
+def test_mx_mode_2_encodes_the_operands_of_each_input_gradient_product():
+    # MX mode 2: the backward pass's input-gradient products of the five forward
+    # products multiply MX-encoded operands (the upstream gradient's rows and the
+    # weight's columns, blocks of 32 along the layer's outputs); the weight gradients
+    # and everything else keep the plain values (straight-through).
+    import oracle
+    import synth
+    m = synth.ModelShape(16, 97, 2, 2, 64)
+    w = synth.Workload("mx_dx_oracle", m, 2, 16, "bf16", "uniform", index=61)
+    p = synth.init_params(m).astype(np.float64)
+    rng = np.random.default_rng(61)
+    offs = synth.param_offsets(m)
+    for name, (off, n) in offs.items():
+        if name.endswith(".b"):
+            p[off:off + n] = 0.1 * rng.standard_normal(n)
+    x, y = synth.inputs_targets(w)
+    o = oracle.Oracle(m, w.B, w.T, "f64")
+    o.set("params", p)
+    o.set_mx(1)
+    loss1 = o.forward(x, y)
+    o.backward()
+    g1 = o.get("grads")
+    o.set_mx(2)
+    loss2 = o.forward(x, y)
+    o.backward()
+    g2 = o.get("grads")
+    assert loss1 == loss2          # the forward pass is the same in modes 1 and 2
+    assert not np.array_equal(g1, g2)
+    C, BT, V = m.channels, w.B * w.T, m.vocab_size
+
+    def W(name):
+        off, n = offs[name]
+        return p[off:off + n]
+
+    def check_dx(dinp, dout, wname, IC, OC):
+        Wm = W(wname).reshape(OC, IC)
+        ref = _mx_operand(dout.reshape(BT, OC)) @ _mx_operand(Wm.T).T
+        np.testing.assert_allclose(dinp.reshape(BT, IC), ref, rtol=1e-12, atol=1e-13)
+
+    def check_dw(gname, dout, inp, IC, OC):
+        off, n = offs[gname]
+        ref = dout.reshape(BT, OC).T @ inp.reshape(BT, IC)
+        np.testing.assert_allclose(g2[off:off + n].reshape(OC, IC), ref, rtol=1e-10, atol=1e-13)
+
+    for l in range(m.num_layers):
+        h = f"h{l}."
+        check_dx(o.act("dln1", l), o.act("dqkv", l), h + "qkv.w", C, 3 * C)
+        check_dx(o.act("datty", l), o.act("dattproj", l), h + "proj.w", C, C)
+        check_dx(o.act("dfch_gelu", l), o.act("dfcproj", l), h + "fcproj.w", 4 * C, C)
+        check_dx(o.act("dln2", l), o.act("dfch", l), h + "fc.w", C, 4 * C)
+        check_dw(h + "qkv.w", o.act("dqkv", l), o.act("ln1", l), C, 3 * C)
+        check_dw(h + "fcproj.w", o.act("dfcproj", l), o.act("fch_gelu", l), 4 * C, C)
+    check_dx(o.act("dlnf"), o.act("dlogits"), "wte", C, V)
+    o.close()
