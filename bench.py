@@ -555,13 +555,16 @@ def mx_forward_bench(args):
 
     st_bf, sl_bf = timed_step(binding.GPT2_GEMM_BF16)
     st_mx, sl_mx = timed_step(binding.GPT2_GEMM_MXFP8)
+    st_dx, sl_dx = timed_step(binding.GPT2_GEMM_MXFP8_DX)
+    arena.set_gemm_format(binding.GPT2_GEMM_MXFP8)
     arena.load_params(params)
     tokens = w.B * w.T
     value = tokens / (ms_mx / 1e3)
     log(f"[bench] forward: bf16 {ms_bf:.3f} ms ({tokens / ms_bf:,.0f}K tok/s, loss {loss_bf:.5f}); "
         f"mxfp8 {ms_mx:.3f} ms ({tokens / ms_mx:,.0f}K tok/s, loss {loss_mx:.5f})")
     log(f"[bench] training step (MX or bf16 forward, bf16 backward, AdamW): bf16 {st_bf:.3f} ms "
-        f"({tokens / st_bf:,.0f}K tok/s); mxfp8 forward {st_mx:.3f} ms ({tokens / st_mx:,.0f}K tok/s)")
+        f"({tokens / st_bf:,.0f}K tok/s); mxfp8 forward {st_mx:.3f} ms ({tokens / st_mx:,.0f}K tok/s); "
+        f"mxfp8 forward + input gradients {st_dx:.3f} ms ({tokens / st_dx:,.0f}K tok/s)")
 
     binding.profile(True)
     pk = max(1, args.profile_steps)
@@ -616,6 +619,9 @@ def mx_forward_bench(args):
                                             "value": round(tokens / (st_mx / 1e3), 1), "loss": sl_mx},
                           "bf16": {"ms_per_step": round(st_bf, 5), "value": round(tokens / (st_bf / 1e3), 1),
                                    "loss": sl_bf},
+                          "mxfp8_forward_and_input_gradients": {
+                              "ms_per_step": round(st_dx, 5), "value": round(tokens / (st_dx / 1e3), 1),
+                              "loss": sl_dx},
                           "unit": "tokens/s", "note": "MX FP8 forward products, bf16 backward, AdamW"},
         "mxfp8_loss": loss_mx,
         "roofline": roof, "cpu_baseline": cpu,

@@ -423,26 +423,43 @@ int gpt2_set_position_encoding(gpt2_arena* arena, int32_t mode, float base, void
  * k-block 4t + j - so that a tile of rows streams its scales in one piece.
  * --------------------------------------------------------------------------- */
 
-/* GEMM formats of an arena's forward products. */
+/* GEMM formats of an arena's products. */
 enum gpt2_gemm_format {
-    GPT2_GEMM_BF16 = 0,  /* the arena's dtype (default)                                   */
-    GPT2_GEMM_MXFP8 = 1, /* the block (qkv, attention projection, fc, fc projection) and
-                            lm_head products of gpt2_forward / gpt2_gen_prefill run on MX
-                            codes; everything else, and the backward pass, unchanged */
+    GPT2_GEMM_BF16 = 0,     /* the arena's dtype (default)                                   */
+    GPT2_GEMM_MXFP8 = 1,    /* the block (qkv, attention projection, fc, fc projection) and
+                               lm_head products of gpt2_forward / gpt2_gen_prefill run on MX
+                               codes; everything else, and the backward pass, unchanged */
+    GPT2_GEMM_MXFP8_DX = 2, /* as GPT2_GEMM_MXFP8, and the backward pass's input-gradient
+                               products of the same five layers (dX = dY W) run on MX codes
+                               of dY's rows and of W's columns (the rows of W^T, blocks of 32
+                               along the layer's outputs); the weight gradients stay bf16 */
 };
 
-/* Gives a bf16 arena the device memory the MX format needs: codes and scales of the
- * forward weights (made from the bf16 weight copy at the first MX forward after any
- * change of the weights: gpt2_sync_weights, gpt2_adamw_step, gpt2_backward_adamw) and
- * one buffer for the quantized input of the product at hand.  device_base NULL: only
+/* Gives a bf16 arena the device memory the MX formats need: codes and scales of the
+ * forward weights and of their transposes (made from the bf16 weight copy at the first
+ * MX forward after any change of the weights: gpt2_sync_weights, gpt2_adamw_step,
+ * gpt2_backward_adamw; the transposes only under GPT2_GEMM_MXFP8_DX), buffers for the
+ * quantized input of the product at hand and for the upstream gradient of an
+ * input-gradient product (up to B*T x vocab), and a bf16 staging buffer for one
+ * transposed weight.  device_base NULL: only
  * *required_bytes is set.  The memory stays the caller's; it must outlive the arena's
  * use of the MX format.  Errors: GPT2_E_INVAL (NULL arena, not GPT2_BF16),
  * GPT2_E_ALIGN (not 256-byte aligned), GPT2_E_SIZE (too small). */
 int gpt2_mx_attach(gpt2_arena* arena, void* device_base, size_t device_bytes, size_t* required_bytes);
 
-/* Selects the format of the forward products.  Errors: GPT2_E_INVAL (unknown format),
- * GPT2_E_STATE (GPT2_GEMM_MXFP8 before gpt2_mx_attach). */
+/* Selects the format of the products.  Errors: GPT2_E_INVAL (unknown format, an MX
+ * format for a Llama-style arena), GPT2_E_STATE (an MX format before gpt2_mx_attach). */
 int gpt2_set_gemm_format(gpt2_arena* arena, int32_t format);
+
+/* Codes and scales of forward weight `index` (0 <= index <= 4 L: 4 l + 0..3 are layer l's
+ * qkv, attention projection, fc and fc projection weights, 4 L the tied token
+ * embedding), as byte offsets into the memory given to gpt2_mx_attach: with
+ * transposed = 0 the codes of W [rows = outputs, ld = inputs rounded up to 128], with
+ * transposed = 1 those of W^T [rows = inputs, ld = outputs rounded up to 128] (made only
+ * under GPT2_GEMM_MXFP8_DX).  Valid after a forward pass in the format.  Errors:
+ * GPT2_E_INVAL, GPT2_E_STATE (no MX memory). */
+int gpt2_mx_weight_codes(const gpt2_arena* arena, int32_t index, int32_t transposed, size_t* codes_offset,
+                         size_t* scales_offset, int64_t* rows, int64_t* ld);
 
 /* The arena's MX input buffers, as byte offsets into the memory given to
  * gpt2_mx_attach: codes [rows, ld] and scales [ld / 128][rows][4] of
@@ -466,6 +483,8 @@ enum gpt2_mx_epilogue {
     GPT2_EPI_BIAS = 0,      /* C = A B^T + bias                                    */
     GPT2_EPI_BIAS_RES = 1,  /* C = residual + A B^T + bias (residual [M, ldc])     */
     GPT2_EPI_BIAS_GELU = 2, /* C = A B^T + bias, C2 = GELU(C) (C2 [M, ldc])         */
+    GPT2_EPI_GELU_BWD = 3,  /* C = (A B^T) * GELU'(residual) (no bias): the GELU
+                               input's gradient, residual = the GELU input [M, ldc] */
 };
 
 /* The block-scaled product C = A B^T on MX operands, fp32 accumulation, bf16 output:

@@ -405,3 +405,128 @@ def test_mx_forward_gpt2_350m_full_size_sampled_prefixes():
         # a mean over 64 positions of one sequence after 24 layers of E4M3 code flips
         # (measured up to 0.022); the products themselves are pinned layer by layer
         assert dm <= MX_PREFIX_LOSS_ABS and cos >= MX_ORACLE_COS
+
+
+def test_gemm_gelu_backward_epilogue():
+    # GPT2_EPI_GELU_BWD: C = (A B^T) * GELU'(pre), the GELU input's gradient.  GELU' is
+    # at most 1.13 in magnitude, so the product's accumulation error passes through
+    # scaled by that, then the bf16 rounding of C.
+    import torch
+    from transformer_lm_fwd_amd import binding as b
+    M, N, K = 200, 264, 256
+    announce("mx_gemm_gelu_bwd", M=M, N=N, K=K)
+    ops, A, Bm = _mx_case(M, N, K, seed=19)
+    rng = np.random.default_rng(16)
+    pre = torch.tensor(rng.standard_normal((M, N)) * 2, dtype=torch.float32).to(torch.bfloat16).cuda()
+    prod = A @ Bm.T
+    got = to_np(b.mx_gemm(*ops, b.GPT2_EPI_GELU_BWD, None, pre)).astype(np.float64)
+    gg = oracle.gelu_grad(to_np(pre).astype(np.float64))
+    ref = prod * gg
+    acc_err = _tol(A, Bm, prod) - 2.0 ** -8 * np.abs(prod)
+    assert np.all(np.abs(got - ref) <= 1.13 * acc_err + 2.0 ** -8 * np.abs(ref) + 1e-6)
+
+
+def test_mx_dx_transposed_weight_codes_equal_the_quantizer_of_the_transposes():
+    # Under GPT2_GEMM_MXFP8_DX the forward pass's code refresh also makes the codes of
+    # every weight's transpose (blocks of 32 along the layer's outputs): they must equal
+    # the quantizer run on the transposed bf16 weights, bit for bit, with the columns
+    # past the outputs (the vocabulary's padding for the tied embedding) as zero.
+    import torch
+    from transformer_lm_fwd_amd import binding as b
+    m = ModelShape(160, 301, 2, 2, 128)
+    w = Workload("mx_dx_codes", m, 2, 64, "bf16", "uniform", index=62)
+    announce("mx_dx_weight_codes", L=m.num_layers, C=m.channels, V=m.vocab_size)
+    x, y = synth.inputs_targets(w)
+    a = gpu_arena(w, rand_params(m, seed=62))
+    a.set_gemm_format(b.GPT2_GEMM_MXFP8_DX)
+    a.forward(x, y)
+    torch.cuda.synchronize()
+    p16 = a.tensor(b.T_PARAMS_BF16).view(-1)
+    offs = synth.param_offsets(m)
+    C = m.channels
+    names = [("h0.qkv.w", 3 * C, C), ("h0.proj.w", C, C), ("h1.fc.w", 4 * C, C), ("h1.fcproj.w", C, 4 * C),
+             ("wte", m.vocab_size, C)]
+    idx = [0, 1, 6, 7, 4 * m.num_layers]
+    for (name, rows, k), i in zip(names, idx):
+        off, n = offs[name]
+        W = p16[off:off + n].view(rows, k)
+        rp = (rows + 127) // 128 * 128
+        wt = torch.zeros(k, rp, dtype=torch.bfloat16, device=W.device)
+        wt[:, :rows] = W.t()
+        q_ref, s_ref = b.mx_quantize(wt)
+        q, s = a.mx_weight_codes(i, transposed=True)
+        assert tuple(q.shape) == (k, rp)
+        assert torch.equal(q, q_ref[:, :rp]), name
+        assert torch.equal(s, s_ref), name
+        # and the forward codes are those of W itself
+        qf, sf = a.mx_weight_codes(i, transposed=False)
+        q_f, s_f = b.mx_quantize(W.contiguous())
+        assert torch.equal(qf, q_f[:, :qf.shape[1]]) and torch.equal(sf, s_f), name
+    a.close()
+
+
+def test_mx_dx_training_gradients_against_the_oracle():
+    # GPT2_GEMM_MXFP8_DX: MX forward products and MX input-gradient products on both
+    # sides (the oracle's MX mode 2); weight gradients from the plain operands.
+    from transformer_lm_fwd_amd import binding as b
+    m = ModelShape(160, 301, 2, 2, 128)
+    w = Workload("mx_dx_grad", m, 2, 64, "bf16", "uniform", index=63)
+    announce("mx_dx_training_gradients", L=m.num_layers, C=m.channels, B=w.B, T=w.T)
+    params = rand_params(m, seed=63)
+    x, y = synth.inputs_targets(w)
+    a = gpu_arena(w, params)
+    a.set_gemm_format(b.GPT2_GEMM_MXFP8)
+    a.forward(x, y)
+    loss1 = a.loss()
+    a.backward()
+    g1 = to_np(a.tensor(b.T_GRADS)).ravel().copy()
+    a.set_gemm_format(b.GPT2_GEMM_MXFP8_DX)
+    a.forward(x, y)
+    loss = a.loss()
+    a.backward()
+    g = to_np(a.tensor(b.T_GRADS)).ravel().copy()
+    a.close()
+    assert loss == loss1              # the forward pass does not depend on the dX format
+    o = oracle_model(w, params, prec="f64")
+    o.set_mx(2)
+    ref = o.forward(x, y)
+    o.backward()
+    gr = o.get("grads")
+    o.set_mx(1)
+    o.forward(x, y)
+    o.backward()
+    gr1 = o.get("grads")
+    o.close()
+    cos, cos1 = cosine(g, gr), cosine(g, gr1)
+    print(f"MX dX step: loss GPU {loss:.6f} MX oracle {ref:.6f}; flat gradient cosine {cos:.6f} "
+          f"(against the oracle without MX input gradients: {cos1:.6f}; GPU modes 1 vs 2: {cosine(g, g1):.6f})",
+          flush=True)
+    assert abs(loss - ref) <= MX_ORACLE_LOSS_ABS
+    assert cos >= 0.999
+    assert not np.array_equal(g, g1)
+
+
+def test_mx_dx_step_trains_and_switching_back_restores_bf16():
+    from transformer_lm_fwd_amd import binding as b
+    w = Workload("mx_dx_train", ModelShape(160, 301, 2, 2, 128), 2, 64, "bf16", "uniform", index=64)
+    announce("mx_dx_train", B=w.B, T=w.T)
+    x, y = synth.inputs_targets(w)
+    p = rand_params(w.model, seed=64)
+    r = gpu_arena(w, p)
+    r.forward(x, y)
+    r.backward()
+    g_bf16 = to_np(r.tensor(b.T_GRADS)).copy()
+    r.close()
+    a = gpu_arena(w, p)
+    a.set_gemm_format(b.GPT2_GEMM_MXFP8_DX)
+    losses = []
+    for t in (1, 2, 3):
+        a.step(x, y, w, t)
+        losses.append(a.loss())
+    assert losses[-1] < losses[0]
+    a.load_params(p)
+    a.set_gemm_format(b.GPT2_GEMM_BF16)
+    a.forward(x, y)
+    a.backward()
+    np.testing.assert_array_equal(to_np(a.tensor(b.T_GRADS)), g_bf16)
+    a.close()

@@ -26,7 +26,7 @@ T_LN2, T_LN2_STATS, T_FCH, T_FCH_GELU, T_RESIDUAL3 = 22, 23, 24, 25, 26
 
 EXPORTS = ("gpt2_alloc_arena", "gpt2_free_arena", "gpt2_sync_weights", "gpt2_forward", "gpt2_backward",
            "gpt2_adamw_step", "gpt2_backward_adamw", "gpt2_tensor_info", "gpt2_num_parameters", "gpt2_profile",
-           "gpt2_profile_read", "gpt2_profile_order", "gpt2_set_side_stream", "gpt2_eval_loss", "gpt2_gen_alloc", "gpt2_gen_free", "gpt2_gen_length", "gpt2_gen_prefill",
+           "gpt2_profile_read", "gpt2_profile_order", "gpt2_set_side_stream", "gpt2_eval_loss", "gpt2_mx_weight_codes", "gpt2_gen_alloc", "gpt2_gen_free", "gpt2_gen_length", "gpt2_gen_prefill",
            "gpt2_gen_decode", "gpt2_sample_topk", "gpt2_tokens_count", "gpt2_tokens_batch",
            "gpt2_params_permute", "gpt2_checkpoint_write", "gpt2_checkpoint_read", "gpt2_set_position_encoding",
            "gpt2_num_parameters_block", "gpt2_alloc_arena_block",
@@ -34,10 +34,10 @@ EXPORTS = ("gpt2_alloc_arena", "gpt2_free_arena", "gpt2_sync_weights", "gpt2_for
            "gpt2_set_gemm_format", "gpt2_mx_buffer", "gpt2_mx_quantize", "gpt2_mx_gemm", "gpt2_mfma_peak", "gpt2_gen_decode_noalloc",
            "gpt2_last_error")
 GPT2_ORDER_NUMERIC, GPT2_ORDER_LEXICOGRAPHIC = 0, 1
-GPT2_GEMM_BF16, GPT2_GEMM_MXFP8 = 0, 1
+GPT2_GEMM_BF16, GPT2_GEMM_MXFP8, GPT2_GEMM_MXFP8_DX = 0, 1, 2
 GPT2_POS_LEARNED, GPT2_POS_ROTARY = 0, 1
 GPT2_BLOCK_GPT2, GPT2_BLOCK_LLAMA = 0, 1
-GPT2_EPI_BIAS, GPT2_EPI_BIAS_RES, GPT2_EPI_BIAS_GELU = 0, 1, 2
+GPT2_EPI_BIAS, GPT2_EPI_BIAS_RES, GPT2_EPI_BIAS_GELU, GPT2_EPI_GELU_BWD = 0, 1, 2, 3
 GPT2_MX_BUF_INPUT, GPT2_MX_BUF_GELU = 0, 1
 
 
@@ -110,6 +110,8 @@ def lib():
         L.gpt2_set_gemm_format.argtypes = [vp, i32]
         L.gpt2_mx_buffer.argtypes = [vp, i32, ctypes.POINTER(sz), ctypes.POINTER(sz), ctypes.POINTER(i64),
                                      ctypes.POINTER(i64)]
+        L.gpt2_mx_weight_codes.argtypes = [vp, i32, i32, ctypes.POINTER(sz), ctypes.POINTER(sz), ctypes.POINTER(i64),
+                                           ctypes.POINTER(i64)]
         L.gpt2_mx_quantize.argtypes = [vp, i64, i32, i32, vp, i64, vp, vp]
         L.gpt2_mx_gemm.argtypes = [vp, vp, i64, vp, vp, i64, vp, i64, i32, i32, i32, i32, vp, vp, vp, vp]
         for name in EXPORTS:
@@ -336,10 +338,11 @@ class Arena:
 
     # ------------------------------------------------------------------ MX FP8 products
     def set_gemm_format(self, fmt: int) -> None:
-        """GPT2_GEMM_BF16 or GPT2_GEMM_MXFP8 for the forward products; the first switch to
-        MXFP8 gives the arena its MX memory (a torch uint8 buffer on the same device)."""
+        """GPT2_GEMM_BF16, GPT2_GEMM_MXFP8 (forward products) or GPT2_GEMM_MXFP8_DX (and the
+        backward pass's input-gradient products); the first switch to an MX format gives
+        the arena its MX memory (a torch uint8 buffer on the same device)."""
         import torch
-        if fmt == GPT2_GEMM_MXFP8 and getattr(self, "_mx", None) is None:
+        if fmt in (GPT2_GEMM_MXFP8, GPT2_GEMM_MXFP8_DX) and getattr(self, "_mx", None) is None:
             need = ctypes.c_size_t(0)
             _check(lib().gpt2_mx_attach(self.h, None, 0, ctypes.byref(need)))
             buf = torch.empty(int(need.value) + 256, dtype=torch.uint8, device=self.base.device)
@@ -347,6 +350,18 @@ class Arena:
             _check(lib().gpt2_mx_attach(self.h, ctypes.c_void_p(buf.data_ptr() + pad), int(need.value), None))
             self._mx = buf
         _check(lib().gpt2_set_gemm_format(self.h, fmt))
+
+    def mx_weight_codes(self, index: int, transposed: bool = False):
+        """Views (codes [rows, ld] uint8, scales [ld / 128, rows, 4] uint8) of the MX codes
+        of forward weight `index` or of its transpose (gpt2_mx_weight_codes)."""
+        qo, so, rows, ld = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_int64(), ctypes.c_int64()
+        _check(lib().gpt2_mx_weight_codes(self.h, index, 1 if transposed else 0, ctypes.byref(qo), ctypes.byref(so),
+                                          ctypes.byref(rows), ctypes.byref(ld)))
+        pad = (-self._mx.data_ptr()) % 256
+        base = self._mx[pad:]
+        r, k = rows.value, ld.value
+        return (base[qo.value:qo.value + r * k].view(r, k),
+                base[so.value:so.value + r * k // 32].view(k // 128, r, 4))
 
     def mx_buffer(self, which: int):
         """Views (codes [rows, ld] uint8, scales [ld / 128, rows, 4] uint8) of one of the

@@ -957,7 +957,8 @@ static hipError_t launch_mx(const GemmArgs& e, int K, uint32_t ab, uint32_t bb, 
     const char* name;
     {
         std::string n = std::string("gemm_mxfp8_xwT_") +
-                        (EPI == EPI_BIAS ? "bias" : EPI == EPI_BIAS_RES ? "bias_res" : "bias_gelu") + "_" +
+                        (EPI == EPI_BIAS ? "bias" : EPI == EPI_BIAS_RES ? "bias_res" :
+                         EPI == EPI_BIAS_GELU ? "bias_gelu" : "gelu_bwd") + "_" +
                         std::to_string(e.M) + "x" + std::to_string(e.N) + "x" + std::to_string(K);
         std::lock_guard<std::mutex> lk(mu);
         name = names.insert(n).first->c_str();
@@ -987,8 +988,9 @@ hipError_t gemm_mx(const GemmArgs& a, int epi, hipStream_t s) {
     if (a.K <= 0 || a.K % 128 || a.lda % 16 || a.ldb % 16 || a.ldc % 8 || a.lda < a.K || a.ldb < a.K)
         return hipErrorInvalidValue;
     if (!a.A || !a.B || !a.C || !a.sa || !a.sb || a.srows_a < a.M || a.srows_b < a.N) return hipErrorInvalidValue;
-    if (epi == EPI_BIAS_RES && !a.R) return hipErrorInvalidValue;
+    if ((epi == EPI_BIAS_RES || epi == EPI_GELU_BWD) && !a.R) return hipErrorInvalidValue;
     if (epi == EPI_BIAS_GELU && !a.C2) return hipErrorInvalidValue;
+    if (epi == EPI_GELU_BWD && (a.bias || a.q2)) return hipErrorInvalidValue;
     const int64_t ab = (int64_t)a.M * a.lda, bb = (int64_t)a.N * a.ldb;
     const int64_t sab = (int64_t)(a.K / 128) * a.srows_a * 4, sbb = (int64_t)(a.K / 128) * a.srows_b * 4;
     if (ab >= (int64_t)1 << 32 || bb >= (int64_t)1 << 32 || sab >= (int64_t)1 << 32 || sbb >= (int64_t)1 << 32)
@@ -1003,6 +1005,7 @@ hipError_t gemm_mx(const GemmArgs& a, int epi, hipStream_t s) {
         case EPI_BIAS: return launch_mx<EPI_BIAS>(e, a.K, (uint32_t)ab, (uint32_t)bb, s);
         case EPI_BIAS_RES: return launch_mx<EPI_BIAS_RES>(e, a.K, (uint32_t)ab, (uint32_t)bb, s);
         case EPI_BIAS_GELU: return launch_mx<EPI_BIAS_GELU>(e, a.K, (uint32_t)ab, (uint32_t)bb, s);
+        case EPI_GELU_BWD: return launch_mx<EPI_GELU_BWD>(e, a.K, (uint32_t)ab, (uint32_t)bb, s);
     }
     return hipErrorInvalidValue;
 }

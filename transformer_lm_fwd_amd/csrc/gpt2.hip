@@ -86,6 +86,11 @@ struct gpt2_arena {
     std::vector<size_t> mxq, mxs;  // [L * 4 + 1]: qkv, proj, fc, fc-proj per layer, then wte
     size_t mx_in_q = 0, mx_in_s = 0;    // codes of a C-wide product input (LayerNorm, attention)
     size_t mx_act_q = 0, mx_act_s = 0;  // codes of the 4C-wide GELU output
+    // GPT2_GEMM_MXFP8_DX: codes of every forward weight's transpose W^T (blocks along
+    // the layer's outputs), the upstream gradient of the input-gradient product at hand,
+    // and the bf16 transpose a weight passes through on its way to codes
+    std::vector<size_t> mxqT, mxsT;
+    size_t mx_dy_q = 0, mx_dy_s = 0, mx_tr = 0;
 };
 
 // Incremental generation over an arena's parameters (bf16): the key/value cache holds
@@ -252,6 +257,23 @@ size_t mx_layout(gpt2_arena& a) {
     a.mx_in_s = take((size_t)BT * k1 / 32);
     a.mx_act_q = take((size_t)BT * k4);
     a.mx_act_s = take((size_t)BT * k4 / 32);
+    // transposed weights: [k, rows rounded to 128] codes; the widest transpose (wte^T,
+    // C x V) sizes the bf16 staging buffer
+    a.mxqT.assign(4 * L + 1, 0);
+    a.mxsT.assign(4 * L + 1, 0);
+    size_t tr = 0;
+    for (int i = 0; i <= 4 * L; ++i) {
+        int64_t rows, k;
+        mx_weight_shape(a, i, &rows, &k);
+        a.mxqT[i] = take((size_t)k * round128(rows));
+        a.mxsT[i] = take((size_t)k * round128(rows) / 32);
+        tr = std::max(tr, (size_t)k * round128(rows) * 2);
+    }
+    // upstream gradients: up to BT x V (the tied lm_head's), else BT x 4C
+    const int64_t kdy = std::max(round128(a.cfg.vocab_size), k4);
+    a.mx_dy_q = take((size_t)BT * kdy);
+    a.mx_dy_s = take((size_t)BT * kdy / 32);
+    a.mx_tr = take(tr);
     return o;
 }
 
@@ -415,12 +437,42 @@ struct Model {
             const int64_t off = i == 4 * L ? a->o_wte : lp(i / 4, which[i % 4]);
             CHECK(mx_quantize(w16 + off, k, (int)rows, (int)k, mxp(a->mxq[i]), round128(k), mxp(a->mxs[i]), s),
                   "mx weights");
+            if (a->gemm_format == GPT2_GEMM_MXFP8_DX) {  // W^T through bf16 staging, then codes
+                const int64_t rp = round128(rows);
+                bf16* tr = (bf16*)mxp(a->mx_tr);
+                CHECK(transpose_bf16(w16 + off, k, (int)rows, (int)k, tr, rp, (int)rp, s), "mx transpose");
+                CHECK(mx_quantize(tr, rp, (int)k, (int)rp, mxp(a->mxqT[i]), rp, mxp(a->mxsT[i]), s), "mx weights^T");
+            }
         }
         a->mx_stale = false;
         return GPT2_OK;
     }
 
-    bool mx_on() const { return sizeof(T) == 2 && a->gemm_format == GPT2_GEMM_MXFP8; }
+    bool mx_on() const {
+        return sizeof(T) == 2 && (a->gemm_format == GPT2_GEMM_MXFP8 || a->gemm_format == GPT2_GEMM_MXFP8_DX);
+    }
+    bool mx_dx_on() const { return sizeof(T) == 2 && a->gemm_format == GPT2_GEMM_MXFP8_DX; }
+
+    // An input-gradient product dX = dY W (+ GELU' epilogue) with dY [BT, K] (row stride
+    // ldy) and W [K, N] the weight of forward product `wi`: bf16, or with
+    // GPT2_GEMM_MXFP8_DX dY's rows and W^T's rows (made at the forward pass's code
+    // refresh) on MX codes.
+    int dx_gemm(const T* dy, int64_t ldy, int K, int wi, int64_t w_off, void* out, int64_t ldc, int N, int epi,
+                const void* R = nullptr) {
+        if constexpr (sizeof(T) == 2) {
+            if (mx_dx_on()) {
+                const int64_t Kp = round128(K);
+                CHECK(mx_quantize((const bf16*)dy, ldy, BT, K, mxp(a->mx_dy_q), Kp, mxp(a->mx_dy_s), s), "mx dY");
+                GemmArgs g{};
+                g.A = mxp(a->mx_dy_q); g.B = mxp(a->mxqT[wi]); g.C = out; g.R = R;
+                g.M = BT; g.N = N; g.K = (int)Kp; g.lda = Kp; g.ldb = Kp; g.ldc = ldc;
+                g.sa = mxp(a->mx_dy_s); g.sb = mxp(a->mxsT[wi]); g.srows_a = BT; g.srows_b = N;
+                CHECK(gemm_mx(g, epi, s), "mx gemm dX");
+                return GPT2_OK;
+            }
+        }
+        return gemm_call(dy, ldy, true, weight(w_off), N, false, out, ldc, BT, N, K, epi, nullptr, R);
+    }
     // MX codes of a product input: `codes` in buffer (q, s) with row stride ldq.
     struct MxBuf {
         uint8_t* q = nullptr;
@@ -544,7 +596,7 @@ struct Model {
     // an epilogue, a LayerNorm).  Every per-row and per-sequence result is the same as in
     // one pass, bit for bit.
     int forward(const int32_t* inp, const int32_t* tgt) {
-        if (a->gemm_format == GPT2_GEMM_MXFP8 && a->mx_stale) {
+        if ((a->gemm_format == GPT2_GEMM_MXFP8 || a->gemm_format == GPT2_GEMM_MXFP8_DX) && a->mx_stale) {
             int rc = mx_refresh();
             if (rc) return rc;
         }
@@ -651,7 +703,10 @@ struct Model {
             CHECK(gemm<T>(g, false, false, EPI_F32, f32(a->ws), a->ws_floats, SD), "gemm");
         }
         if (!opt && (rc = mark(a->ev_wte, SD))) return rc;
-        if ((rc = gemm_call(dz, Vp, true, weight(a->o_wte), C, false, dbuf, C, BT, C, V, EPI_BIAS))) return rc;
+        // (the tied lm_head's upstream gradient is zero in its padded columns V .. Vp - 1)
+        if ((rc = mx_dx_on() ? dx_gemm(dz, Vp, (int)Vp, 4 * L, a->o_wte, dbuf, C, C, EPI_BIAS)
+                             : gemm_call(dz, Vp, true, weight(a->o_wte), C, false, dbuf, C, BT, C, V, EPI_BIAS)))
+            return rc;
         AdamwRows wte_opt{};
         if (opt) {
             // rows of wte no token of the batch touches have their final gradient now: update
@@ -695,16 +750,15 @@ struct Model {
                                     nullptr, nullptr, bx)))
                     return rc;
                 if (sizeof(T) != 2) CHECK(swiglu_backward<T>(dfch, dh, act(x.fch), BT, H, M), "swiglu backward");
-            } else if ((rc = gemm_call(din, C, true, weight(lp(l, P_FCPW)), 4 * C, false, dfch, 4 * C, BT, 4 * C, C,
-                                       EPI_GELU_BWD, nullptr, act(x.fch)))) {
+            } else if ((rc = dx_gemm(din, C, C, 4 * l + 3, lp(l, P_FCPW), dfch, 4 * C, 4 * C, EPI_GELU_BWD,
+                                     act(x.fch)))) {
                 return rc;
             }
             // c_fc: side: dW = dfch^T ln2, db = colsum(dfch); main: dln2 = dfch W_fc
             if ((rc = stream_wait(a, SD, M))) return rc;
             if ((rc = side_dw(dfch, (int)F1, act(x.ln2), C, lp(l, P_FCW), bias_off(lp(l, P_FCB))))) return rc;
             if ((rc = mark(a->rd_fch[p], SD))) return rc;
-            if ((rc = gemm_call(dfch, F1, true, weight(lp(l, P_FCW)), C, false, dbuf, C, BT, C, (int)F1, EPI_BIAS)))
-                return rc;
+            if ((rc = dx_gemm(dfch, F1, (int)F1, 4 * l + 2, lp(l, P_FCW), dbuf, C, C, EPI_BIAS))) return rc;
             // ln_2: dmid = din + LN backward
             if ((rc = wait(M, a->rd_res[i_mid]))) return rc;
             CHECK(layernorm_backward<T>(dmid, din, grad(lp(l, P_LN2W)), gb(lp(l, P_LN2B)), dbuf, act(x.res2),
@@ -715,8 +769,7 @@ struct Model {
             if ((rc = stream_wait(a, SD, M))) return rc;
             if ((rc = side_dw(dmid, C, act(x.atty), C, lp(l, P_PROJW), bias_off(lp(l, P_PROJB))))) return rc;
             if ((rc = mark(a->rd_res[i_mid], SD))) return rc;
-            if ((rc = gemm_call(dmid, C, true, weight(lp(l, P_PROJW)), C, false, dbuf, C, BT, C, C, EPI_BIAS)))
-                return rc;
+            if ((rc = dx_gemm(dmid, C, C, 4 * l + 1, lp(l, P_PROJW), dbuf, C, C, EPI_BIAS))) return rc;
             // attention
             if ((rc = wait(M, a->rd_qkv[p]))) return rc;
             CHECK(attention_backward<T>(dqkv, f32(a->dsum), dbuf, act(x.atty), act(x.qkv), f32(x.lse), B, S, C, NH, M),
@@ -727,8 +780,7 @@ struct Model {
             if ((rc = stream_wait(a, SD, M))) return rc;
             if ((rc = side_dw(dqkv, 3 * C, act(x.ln1), C, lp(l, P_QKVW), bias_off(lp(l, P_QKVB))))) return rc;
             if ((rc = mark(a->rd_qkv[p], SD))) return rc;
-            if ((rc = gemm_call(dqkv, 3 * C, true, weight(lp(l, P_QKVW)), C, false, dbuf, C, BT, C, 3 * C, EPI_BIAS)))
-                return rc;
+            if ((rc = dx_gemm(dqkv, 3 * C, 3 * C, 4 * l, lp(l, P_QKVW), dbuf, C, C, EPI_BIAS))) return rc;
             // ln_1: dout = dmid + LN backward (= d xin)
             if ((rc = wait(M, a->rd_res[i_out]))) return rc;
             CHECK(layernorm_backward<T>(dout, dmid, grad(lp(l, P_LN1W)), gb(lp(l, P_LN1B)), dbuf, xin, f32(x.ln1s),
@@ -1084,9 +1136,10 @@ int gpt2_set_gemm_format(gpt2_arena* a, int32_t format) {
         a->gemm_format = format;
         return GPT2_OK;
     }
-    if (format != GPT2_GEMM_MXFP8) return fail(GPT2_E_INVAL, "unknown GEMM format");
+    if (format != GPT2_GEMM_MXFP8 && format != GPT2_GEMM_MXFP8_DX) return fail(GPT2_E_INVAL, "unknown GEMM format");
     if (a->block != GPT2_BLOCK_GPT2) return fail(GPT2_E_INVAL, "MX products are built for the GPT-2 block");
-    if (!a->mx) return fail(GPT2_E_STATE, "GPT2_GEMM_MXFP8 needs memory from gpt2_mx_attach");
+    if (!a->mx) return fail(GPT2_E_STATE, "the MX formats need memory from gpt2_mx_attach");
+    if (a->dtype != GPT2_BF16) return fail(GPT2_E_INVAL, "the MX formats are built for bf16 arenas");
     a->gemm_format = format;
     a->mx_stale = true;
     return GPT2_OK;
@@ -1108,6 +1161,27 @@ int gpt2_mx_buffer(const gpt2_arena* a, int32_t which, size_t* codes_offset, siz
         *ld = round128(4 * C);
     } else {
         return fail(GPT2_E_INVAL, "unknown MX buffer");
+    }
+    return GPT2_OK;
+}
+
+int gpt2_mx_weight_codes(const gpt2_arena* a, int32_t index, int32_t transposed, size_t* codes_offset,
+                         size_t* scales_offset, int64_t* rows, int64_t* ld) {
+    if (!a || !codes_offset || !scales_offset || !rows || !ld) return fail(GPT2_E_INVAL, "NULL argument");
+    if (!a->mx) return fail(GPT2_E_STATE, "no MX memory attached");
+    if (index < 0 || index > 4 * a->cfg.num_layers) return fail(GPT2_E_INVAL, "weight index out of range");
+    int64_t r, k;
+    mx_weight_shape(*a, index, &r, &k);
+    if (transposed) {
+        *codes_offset = a->mxqT[index];
+        *scales_offset = a->mxsT[index];
+        *rows = k;
+        *ld = round128(r);
+    } else {
+        *codes_offset = a->mxq[index];
+        *scales_offset = a->mxs[index];
+        *rows = r;
+        *ld = round128(k);
     }
     return GPT2_OK;
 }
@@ -1138,9 +1212,12 @@ int gpt2_mx_gemm(const void* d_qa, const void* d_sa, int64_t lda, const void* d_
         case GPT2_EPI_BIAS: epi = EPI_BIAS; break;
         case GPT2_EPI_BIAS_RES: epi = EPI_BIAS_RES; break;
         case GPT2_EPI_BIAS_GELU: epi = EPI_BIAS_GELU; break;
+        case GPT2_EPI_GELU_BWD: epi = EPI_GELU_BWD; break;
         default: return fail(GPT2_E_INVAL, "unknown epilogue");
     }
     if (epi == EPI_BIAS_RES && !d_residual) return fail(GPT2_E_INVAL, "GPT2_EPI_BIAS_RES needs the residual");
+    if (epi == EPI_GELU_BWD && (!d_residual || d_bias))
+        return fail(GPT2_E_INVAL, "GPT2_EPI_GELU_BWD needs the GELU input and takes no bias");
     if (epi == EPI_BIAS_GELU && !d_c2) return fail(GPT2_E_INVAL, "GPT2_EPI_BIAS_GELU needs the second output");
     if ((int64_t)M * lda >= ((int64_t)1 << 32) || (int64_t)N * ldb >= ((int64_t)1 << 32))
         return fail(GPT2_E_SIZE, "operands over 4 GiB");

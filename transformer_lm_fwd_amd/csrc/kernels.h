@@ -150,6 +150,8 @@ hipError_t splitk_reduce(float* out, const float* ws, int splits, int64_t n, int
 // sc [Kp / 128][R][4] (see GemmArgs).  Scale of a block: the smallest 2^e with
 // amax <= 448 * 2^e (e in [-127, 127], all-zero blocks -127); codes: x / 2^e rounded
 // to nearest even.
+// y [K, ldy] = x [R, ldx]^T, columns R .. Rp - 1 of y zero (bf16).
+hipError_t transpose_bf16(const bf16* x, int64_t ldx, int R, int K, bf16* y, int64_t ldy, int Rp, hipStream_t s);
 hipError_t mx_quantize(const bf16* x, int64_t ldx, int R, int K, uint8_t* q, int64_t ldq, uint8_t* sc,
                        hipStream_t s);
 // C = A B^T (+ the epilogue) for MX operands: A codes [M, K] (lda bytes), B codes

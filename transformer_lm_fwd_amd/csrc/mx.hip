@@ -44,7 +44,36 @@ __global__ __launch_bounds__(256) void mx_quantize_kernel(const bf16* __restrict
     if ((c & 15) == 0) *(uint32_t*)(sc + ((int64_t)(c / 16) * R + row) * 4) = word;
 }
 
+// y [K, ldy] = x [R, ldx]^T over a 64 x 64 tile per block (through LDS, rows padded
+// by 2 elements against bank conflicts); columns R .. Rp - 1 of y are written as zero.
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const bf16* __restrict__ x, int64_t ldx, int R, int K,
+                                                             bf16* __restrict__ y, int64_t ldy, int Rp) {
+    __shared__ uint16_t t[64][66];
+    const int r0 = blockIdx.y * 64, k0 = blockIdx.x * 64;
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;  // 64 x 4 threads
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int r = r0 + ty + 4 * i, k = k0 + tx;
+        t[ty + 4 * i][tx] = (r < R && k < K) ? x[(int64_t)r * ldx + k].x : (uint16_t)0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int k = k0 + ty + 4 * i, r = r0 + tx;
+        if (k < K && r < Rp) y[(int64_t)k * ldy + r] = bf16{t[tx][ty + 4 * i]};
+    }
+}
+
 }  // namespace
+
+hipError_t transpose_bf16(const bf16* x, int64_t ldx, int R, int K, bf16* y, int64_t ldy, int Rp, hipStream_t s) {
+    if (R <= 0 || K <= 0) return hipSuccess;
+    if (ldx < K || Rp < R || ldy < Rp) return hipErrorInvalidValue;
+    ProfScope prof(s, "transpose_bf16", 0.0, 2.0 * R * K + 2.0 * K * Rp);
+    hipLaunchKernelGGL(transpose_bf16_kernel, dim3((K + 63) / 64, (Rp + 63) / 64), dim3(256), 0, s, x, ldx, R, K, y,
+                       ldy, Rp);
+    return hipGetLastError();
+}
 
 hipError_t mx_quantize(const bf16* x, int64_t ldx, int R, int K, uint8_t* q, int64_t ldq, uint8_t* sc,
                        hipStream_t s) {
