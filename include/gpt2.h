@@ -440,8 +440,7 @@ enum gpt2_gemm_format {
  * MX forward after any change of the weights: gpt2_sync_weights, gpt2_adamw_step,
  * gpt2_backward_adamw; the transposes only under GPT2_GEMM_MXFP8_DX), buffers for the
  * quantized input of the product at hand and for the upstream gradient of an
- * input-gradient product (up to B*T x vocab), and a bf16 staging buffer for one
- * transposed weight.  device_base NULL: only
+ * input-gradient product (up to B*T x vocab).  device_base NULL: only
  * *required_bytes is set.  The memory stays the caller's; it must outlive the arena's
  * use of the MX format.  Errors: GPT2_E_INVAL (NULL arena, not GPT2_BF16),
  * GPT2_E_ALIGN (not 256-byte aligned), GPT2_E_SIZE (too small). */

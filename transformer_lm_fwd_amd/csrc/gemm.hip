@@ -752,6 +752,20 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a, int
                 }
                 if (full) {
                     st16(C + o, pack16<bf16>(v));
+                    if constexpr (EPI == EPI_GELU_BWD) {
+                        // MX codes of the stored output (the next input-gradient product's
+                        // upstream gradient), grouped as for the GELU output below
+                        if (a.q2) {
+                            float t[8];
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) t[e] = v[e];
+                            round_bf16_8(t);
+                            uint32_t cw[2];
+                            const uint32_t word = mx_stage_word(mx_quant8(t, cw));
+                            *(uint2*)(a.q2 + (int64_t)row * a.ldq2 + col) = make_uint2(cw[0], cw[1]);
+                            if ((tid & 15) == 0) *(uint32_t*)(a.s2 + ((int64_t)(col / 128) * a.M + row) * 4) = word;
+                        }
+                    }
                     if constexpr (EPI == EPI_BIAS && XTRA) {
                         if (a.swiglu) {  // 4 (gate, up) pairs -> 4 hidden units
                             float gu[8], h[8];
@@ -984,13 +998,14 @@ static hipError_t launch_mx(const GemmArgs& e, int K, uint32_t ab, uint32_t bb, 
 
 hipError_t gemm_mx(const GemmArgs& a, int epi, hipStream_t s) {
     if (a.M <= 0 || a.N <= 0) return hipSuccess;
-    if (a.q2 && (epi != EPI_BIAS_GELU || a.N % 128 || !a.s2 || a.ldq2 < a.N || a.ldq2 % 16)) return hipErrorInvalidValue;
+    if (a.q2 && ((epi != EPI_BIAS_GELU && epi != EPI_GELU_BWD) || a.N % 128 || !a.s2 || a.ldq2 < a.N || a.ldq2 % 16))
+        return hipErrorInvalidValue;
     if (a.K <= 0 || a.K % 128 || a.lda % 16 || a.ldb % 16 || a.ldc % 8 || a.lda < a.K || a.ldb < a.K)
         return hipErrorInvalidValue;
     if (!a.A || !a.B || !a.C || !a.sa || !a.sb || a.srows_a < a.M || a.srows_b < a.N) return hipErrorInvalidValue;
     if ((epi == EPI_BIAS_RES || epi == EPI_GELU_BWD) && !a.R) return hipErrorInvalidValue;
     if (epi == EPI_BIAS_GELU && !a.C2) return hipErrorInvalidValue;
-    if (epi == EPI_GELU_BWD && (a.bias || a.q2)) return hipErrorInvalidValue;
+    if (epi == EPI_GELU_BWD && a.bias) return hipErrorInvalidValue;
     const int64_t ab = (int64_t)a.M * a.lda, bb = (int64_t)a.N * a.ldb;
     const int64_t sab = (int64_t)(a.K / 128) * a.srows_a * 4, sbb = (int64_t)(a.K / 128) * a.srows_b * 4;
     if (ab >= (int64_t)1 << 32 || bb >= (int64_t)1 << 32 || sab >= (int64_t)1 << 32 || sbb >= (int64_t)1 << 32)

@@ -87,10 +87,12 @@ struct gpt2_arena {
     size_t mx_in_q = 0, mx_in_s = 0;    // codes of a C-wide product input (LayerNorm, attention)
     size_t mx_act_q = 0, mx_act_s = 0;  // codes of the 4C-wide GELU output
     // GPT2_GEMM_MXFP8_DX: codes of every forward weight's transpose W^T (blocks along
-    // the layer's outputs), the upstream gradient of the input-gradient product at hand,
-    // and the bf16 transpose a weight passes through on its way to codes
+    // the layer's outputs) and of the upstream gradient of the input-gradient product
+    // at hand
     std::vector<size_t> mxqT, mxsT;
-    size_t mx_dy_q = 0, mx_dy_s = 0, mx_tr = 0;
+    size_t mx_dy_q = 0, mx_dy_s = 0;    // up to B*T x vocab: the product at hand's upstream gradient
+    size_t mx_dy2_q = 0, mx_dy2_s = 0;  // B*T x 4C: written by the GELU' product for the next one
+    bool dlogits_codes = false;         // the last loss forward wrote the codes of d loss / d logits
 };
 
 // Incremental generation over an arena's parameters (bf16): the key/value cache holds
@@ -257,23 +259,21 @@ size_t mx_layout(gpt2_arena& a) {
     a.mx_in_s = take((size_t)BT * k1 / 32);
     a.mx_act_q = take((size_t)BT * k4);
     a.mx_act_s = take((size_t)BT * k4 / 32);
-    // transposed weights: [k, rows rounded to 128] codes; the widest transpose (wte^T,
-    // C x V) sizes the bf16 staging buffer
+    // transposed weights: [k, rows rounded to 128] codes
     a.mxqT.assign(4 * L + 1, 0);
     a.mxsT.assign(4 * L + 1, 0);
-    size_t tr = 0;
     for (int i = 0; i <= 4 * L; ++i) {
         int64_t rows, k;
         mx_weight_shape(a, i, &rows, &k);
         a.mxqT[i] = take((size_t)k * round128(rows));
         a.mxsT[i] = take((size_t)k * round128(rows) / 32);
-        tr = std::max(tr, (size_t)k * round128(rows) * 2);
     }
     // upstream gradients: up to BT x V (the tied lm_head's), else BT x 4C
     const int64_t kdy = std::max(round128(a.cfg.vocab_size), k4);
     a.mx_dy_q = take((size_t)BT * kdy);
     a.mx_dy_s = take((size_t)BT * kdy / 32);
-    a.mx_tr = take(tr);
+    a.mx_dy2_q = take((size_t)BT * k4);
+    a.mx_dy2_s = take((size_t)BT * k4 / 32);
     return o;
 }
 
@@ -430,20 +430,48 @@ struct Model {
     // MX codes and scales of the forward weights from the bf16 copy.
     int mx_refresh() {
         const bf16* w16 = at<bf16>(a, a->params16);
-        for (int i = 0; i <= 4 * L; ++i) {
+        // the codes of W and (for the input-gradient products) of W^T, from one read of W;
+        // each of the four block weights in one launch over all layers (the layer-major
+        // arena and the code layout put layer l + 1's copy at a fixed stride from layer l's)
+        const bool dx = a->gemm_format == GPT2_GEMM_MXFP8_DX;
+        static constexpr int which[4] = {P_QKVW, P_PROJW, P_FCW, P_FCPW};
+        auto codes = [&](int i, int64_t off, int n, const MxWeightStrides& bs) {
             int64_t rows, k;
             mx_weight_shape(*a, i, &rows, &k);
-            static constexpr int which[4] = {P_QKVW, P_PROJW, P_FCW, P_FCPW};
-            const int64_t off = i == 4 * L ? a->o_wte : lp(i / 4, which[i % 4]);
-            CHECK(mx_quantize(w16 + off, k, (int)rows, (int)k, mxp(a->mxq[i]), round128(k), mxp(a->mxs[i]), s),
-                  "mx weights");
-            if (a->gemm_format == GPT2_GEMM_MXFP8_DX) {  // W^T through bf16 staging, then codes
-                const int64_t rp = round128(rows);
-                bf16* tr = (bf16*)mxp(a->mx_tr);
-                CHECK(transpose_bf16(w16 + off, k, (int)rows, (int)k, tr, rp, (int)rp, s), "mx transpose");
-                CHECK(mx_quantize(tr, rp, (int)k, (int)rp, mxp(a->mxqT[i]), rp, mxp(a->mxsT[i]), s), "mx weights^T");
+            return hip_check(mx_weight_codes(w16 + off, k, (int)rows, (int)k, mxp(a->mxq[i]), round128(k),
+                                             mxp(a->mxs[i]), dx ? mxp(a->mxqT[i]) : nullptr, round128(rows),
+                                             dx ? mxp(a->mxsT[i]) : nullptr, s, n, bs),
+                             "mx weights");
+        };
+        int rc;
+        for (int t = 0; t < 4; ++t) {
+            MxWeightStrides bs;
+            bool uniform = L > 1;
+            if (uniform) {
+                bs.w = lp(1, which[t]) - lp(0, which[t]);
+                bs.q = (int64_t)(a->mxq[t + 4] - a->mxq[t]);
+                bs.sq = (int64_t)(a->mxs[t + 4] - a->mxs[t]);
+                bs.qt = (int64_t)(a->mxqT[t + 4] - a->mxqT[t]);
+                bs.sqt = (int64_t)(a->mxsT[t + 4] - a->mxsT[t]);
+                // (the kernel's vector accesses need these alignments of the strides)
+                uniform = bs.w % 8 == 0 && bs.q % 16 == 0 && bs.sq % 4 == 0 && bs.qt % 16 == 0 && bs.sqt % 4 == 0;
+                for (int l = 1; l < L; ++l) {
+                    const int i = 4 * l + t;
+                    uniform = uniform && lp(l, which[t]) - lp(l - 1, which[t]) == bs.w &&
+                              (int64_t)(a->mxq[i] - a->mxq[i - 4]) == bs.q &&
+                              (int64_t)(a->mxs[i] - a->mxs[i - 4]) == bs.sq &&
+                              (int64_t)(a->mxqT[i] - a->mxqT[i - 4]) == bs.qt &&
+                              (int64_t)(a->mxsT[i] - a->mxsT[i - 4]) == bs.sqt;
+                }
+            }
+            if (uniform) {  // every layer's copy of this weight in one launch
+                if ((rc = codes(t, lp(0, which[t]), L, bs))) return rc;
+            } else {
+                for (int l = 0; l < L; ++l)
+                    if ((rc = codes(4 * l + t, lp(l, which[t]), 1, MxWeightStrides{}))) return rc;
             }
         }
+        if ((rc = codes(4 * L, a->o_wte, 1, MxWeightStrides{}))) return rc;
         a->mx_stale = false;
         return GPT2_OK;
     }
@@ -453,26 +481,6 @@ struct Model {
     }
     bool mx_dx_on() const { return sizeof(T) == 2 && a->gemm_format == GPT2_GEMM_MXFP8_DX; }
 
-    // An input-gradient product dX = dY W (+ GELU' epilogue) with dY [BT, K] (row stride
-    // ldy) and W [K, N] the weight of forward product `wi`: bf16, or with
-    // GPT2_GEMM_MXFP8_DX dY's rows and W^T's rows (made at the forward pass's code
-    // refresh) on MX codes.
-    int dx_gemm(const T* dy, int64_t ldy, int K, int wi, int64_t w_off, void* out, int64_t ldc, int N, int epi,
-                const void* R = nullptr) {
-        if constexpr (sizeof(T) == 2) {
-            if (mx_dx_on()) {
-                const int64_t Kp = round128(K);
-                CHECK(mx_quantize((const bf16*)dy, ldy, BT, K, mxp(a->mx_dy_q), Kp, mxp(a->mx_dy_s), s), "mx dY");
-                GemmArgs g{};
-                g.A = mxp(a->mx_dy_q); g.B = mxp(a->mxqT[wi]); g.C = out; g.R = R;
-                g.M = BT; g.N = N; g.K = (int)Kp; g.lda = Kp; g.ldb = Kp; g.ldc = ldc;
-                g.sa = mxp(a->mx_dy_s); g.sb = mxp(a->mxsT[wi]); g.srows_a = BT; g.srows_b = N;
-                CHECK(gemm_mx(g, epi, s), "mx gemm dX");
-                return GPT2_OK;
-            }
-        }
-        return gemm_call(dy, ldy, true, weight(w_off), N, false, out, ldc, BT, N, K, epi, nullptr, R);
-    }
     // MX codes of a product input: `codes` in buffer (q, s) with row stride ldq.
     struct MxBuf {
         uint8_t* q = nullptr;
@@ -483,6 +491,48 @@ struct Model {
     MxBuf mx_gelu() const {
         // the fc epilogue writes the GELU codes itself when 4C is a multiple of 128
         return mx_on() && (4 * C) % 128 == 0 ? MxBuf{mxp(a->mx_act_q), mxp(a->mx_act_s), round128(4 * C)} : MxBuf{};
+    }
+
+    // An input-gradient product dX = dY W (+ GELU' epilogue) with dY [BT, K] (row stride
+    // ldy) and W [K, N] the weight of forward product `wi`: bf16, or with
+    // GPT2_GEMM_MXFP8_DX dY's rows and W^T's rows (made at the forward pass's code
+    // refresh) on MX codes.
+    // codes of a C-wide upstream gradient written by the LayerNorm backward (the buffer of
+    // the product at hand: each is consumed by the next input-gradient product on the
+    // same stream before the next LayerNorm backward writes it again)
+    MxBuf dy_codes() const {
+        return mx_dx_on() && !llama() ? MxBuf{mxp(a->mx_dy_q), mxp(a->mx_dy_s), round128(C)} : MxBuf{};
+    }
+
+    // codes of the c_fc input gradient, written by the GELU' product's epilogue when 4C
+    // is a multiple of 128 (its 16-thread groups then cover whole 128-column stages)
+    MxBuf dfch_codes() const {
+        return mx_dx_on() && !llama() && (4 * C) % 128 == 0
+                   ? MxBuf{mxp(a->mx_dy2_q), mxp(a->mx_dy2_s), round128(4 * C)}
+                   : MxBuf{};
+    }
+
+    // `codes`: dY's codes when its producer wrote them, else dY is quantized here;
+    // `out_codes`: the GELU' product also writes the codes of its output.
+    int dx_gemm(const T* dy, int64_t ldy, int K, int wi, int64_t w_off, void* out, int64_t ldc, int N, int epi,
+                const void* R = nullptr, MxBuf codes = MxBuf{}, MxBuf out_codes = MxBuf{}) {
+        if constexpr (sizeof(T) == 2) {
+            if (mx_dx_on()) {
+                const int64_t Kp = round128(K);
+                if (!codes.q) {
+                    codes = MxBuf{mxp(a->mx_dy_q), mxp(a->mx_dy_s), Kp};
+                    CHECK(mx_quantize((const bf16*)dy, ldy, BT, K, codes.q, Kp, codes.s, s), "mx dY");
+                }
+                GemmArgs g{};
+                g.A = codes.q; g.B = mxp(a->mxqT[wi]); g.C = out; g.R = R;
+                g.M = BT; g.N = N; g.K = (int)Kp; g.lda = codes.ld; g.ldb = Kp; g.ldc = ldc;
+                g.sa = codes.s; g.sb = mxp(a->mxsT[wi]); g.srows_a = BT; g.srows_b = N;
+                g.q2 = out_codes.q; g.s2 = out_codes.s; g.ldq2 = out_codes.ld;
+                CHECK(gemm_mx(g, epi, s), "mx gemm dX");
+                return GPT2_OK;
+            }
+        }
+        return gemm_call(dy, ldy, true, weight(w_off), N, false, out, ldc, BT, N, K, epi, nullptr, R);
     }
 
     // A forward product Y = X W^T (+ epilogue) with X [BT, K] dense and W (N, K) at
@@ -583,9 +633,15 @@ struct Model {
         if ((rc = fwd_gemm(arow(a->lnf, C), C, a->o_wte, 4 * L, V, arow(a->logits, Vp), Vp, EPI_BIAS, nullptr,
                            nullptr, nullptr, mi)))
             return rc;
-        if (tgt)
-            CHECK(crossentropy_fused<T>(arow(a->logits, Vp), f32(a->losses) + r0(), tgt, BT, V, Vp, dscale, s),
+        if (tgt) {
+            // the MX input-gradient format takes the codes of d loss / d logits from here
+            const bool dz_codes = mx_dx_on() && r0() == 0 && BT == (int64_t)a->B * a->T;
+            CHECK(crossentropy_fused<T>(arow(a->logits, Vp), f32(a->losses) + r0(), tgt, BT, V, Vp, dscale, s,
+                                        dz_codes ? mxp(a->mx_dy_q) : nullptr, round128(V),
+                                        dz_codes ? mxp(a->mx_dy_s) : nullptr),
                   "crossentropy");
+            a->dlogits_codes = dz_codes;
+        }
         return GPT2_OK;
     }
 
@@ -704,9 +760,13 @@ struct Model {
         }
         if (!opt && (rc = mark(a->ev_wte, SD))) return rc;
         // (the tied lm_head's upstream gradient is zero in its padded columns V .. Vp - 1)
-        if ((rc = mx_dx_on() ? dx_gemm(dz, Vp, (int)Vp, 4 * L, a->o_wte, dbuf, C, C, EPI_BIAS)
-                             : gemm_call(dz, Vp, true, weight(a->o_wte), C, false, dbuf, C, BT, C, V, EPI_BIAS)))
+        if (mx_dx_on()) {
+            const MxBuf dzc = a->dlogits_codes ? MxBuf{mxp(a->mx_dy_q), mxp(a->mx_dy_s), round128(V)} : MxBuf{};
+            if ((rc = dx_gemm(dz, Vp, (int)Vp, 4 * L, a->o_wte, dbuf, C, C, EPI_BIAS, nullptr, dzc))) return rc;
+        } else if ((rc = gemm_call(dz, Vp, true, weight(a->o_wte), C, false, dbuf, C, BT, C, V, EPI_BIAS))) {
             return rc;
+        }
+        a->dlogits_codes = false;
         AdamwRows wte_opt{};
         if (opt) {
             // rows of wte no token of the batch touches have their final gradient now: update
@@ -721,9 +781,10 @@ struct Model {
         }
         int cur = 0;
         if ((rc = wait(M, a->rd_res[0]))) return rc;
+        const MxBuf dyc = dy_codes();  // LayerNorm backward outputs feed the next dX product
         CHECK(layernorm_backward<T>(act(a->dres[0]), (const T*)nullptr, grad(a->o_lnfw), gb(a->o_lnfb), dbuf,
                                     act(a->la[L - 1].res3), f32(a->lnfs), master(a->o_lnfw), BT, C, part,
-                                    a->partial_floats, M, llama()),
+                                    a->partial_floats, M, llama(), dyc.q, dyc.ld, dyc.s),
               "lnf backward");
         const int64_t F1 = a->F1, F2 = a->F2;
         auto bias_off = [&](int64_t off) -> int64_t { return llama() ? -1 : off; };
@@ -751,25 +812,27 @@ struct Model {
                     return rc;
                 if (sizeof(T) != 2) CHECK(swiglu_backward<T>(dfch, dh, act(x.fch), BT, H, M), "swiglu backward");
             } else if ((rc = dx_gemm(din, C, C, 4 * l + 3, lp(l, P_FCPW), dfch, 4 * C, 4 * C, EPI_GELU_BWD,
-                                     act(x.fch)))) {
+                                     act(x.fch), dyc, dfch_codes()))) {
                 return rc;
             }
             // c_fc: side: dW = dfch^T ln2, db = colsum(dfch); main: dln2 = dfch W_fc
             if ((rc = stream_wait(a, SD, M))) return rc;
             if ((rc = side_dw(dfch, (int)F1, act(x.ln2), C, lp(l, P_FCW), bias_off(lp(l, P_FCB))))) return rc;
             if ((rc = mark(a->rd_fch[p], SD))) return rc;
-            if ((rc = dx_gemm(dfch, F1, (int)F1, 4 * l + 2, lp(l, P_FCW), dbuf, C, C, EPI_BIAS))) return rc;
+            if ((rc = dx_gemm(dfch, F1, (int)F1, 4 * l + 2, lp(l, P_FCW), dbuf, C, C, EPI_BIAS, nullptr,
+                              dfch_codes())))
+                return rc;
             // ln_2: dmid = din + LN backward
             if ((rc = wait(M, a->rd_res[i_mid]))) return rc;
             CHECK(layernorm_backward<T>(dmid, din, grad(lp(l, P_LN2W)), gb(lp(l, P_LN2B)), dbuf, act(x.res2),
                                         f32(x.ln2s), master(lp(l, P_LN2W)), BT, C, part, a->partial_floats, M,
-                                        llama()),
+                                        llama(), dyc.q, dyc.ld, dyc.s),
                   "ln2 backward");
             // attn c_proj: side: dW = dmid^T atty, db; main: datty = dmid W_proj
             if ((rc = stream_wait(a, SD, M))) return rc;
             if ((rc = side_dw(dmid, C, act(x.atty), C, lp(l, P_PROJW), bias_off(lp(l, P_PROJB))))) return rc;
             if ((rc = mark(a->rd_res[i_mid], SD))) return rc;
-            if ((rc = dx_gemm(dmid, C, C, 4 * l + 1, lp(l, P_PROJW), dbuf, C, C, EPI_BIAS))) return rc;
+            if ((rc = dx_gemm(dmid, C, C, 4 * l + 1, lp(l, P_PROJW), dbuf, C, C, EPI_BIAS, nullptr, dyc))) return rc;
             // attention
             if ((rc = wait(M, a->rd_qkv[p]))) return rc;
             CHECK(attention_backward<T>(dqkv, f32(a->dsum), dbuf, act(x.atty), act(x.qkv), f32(x.lse), B, S, C, NH, M),
@@ -783,8 +846,11 @@ struct Model {
             if ((rc = dx_gemm(dqkv, 3 * C, 3 * C, 4 * l, lp(l, P_QKVW), dbuf, C, C, EPI_BIAS))) return rc;
             // ln_1: dout = dmid + LN backward (= d xin)
             if ((rc = wait(M, a->rd_res[i_out]))) return rc;
+            // (layer 0's output feeds no product: no codes)
+            const MxBuf dyc1 = l > 0 ? dyc : MxBuf{};
             CHECK(layernorm_backward<T>(dout, dmid, grad(lp(l, P_LN1W)), gb(lp(l, P_LN1B)), dbuf, xin, f32(x.ln1s),
-                                        master(lp(l, P_LN1W)), BT, C, part, a->partial_floats, M, llama()),
+                                        master(lp(l, P_LN1W)), BT, C, part, a->partial_floats, M, llama(), dyc1.q,
+                                        dyc1.ld, dyc1.s),
                   "ln1 backward");
             cur = i_out;
             if (opt) {  // layer l's gradients are complete and its weights no longer read

@@ -96,7 +96,8 @@ hipError_t layernorm_forward(T* out, float* stats, const T* inp, const float* w,
 template <class T>
 hipError_t layernorm_backward(T* dres, const T* dres_in, float* dw, float* db, const T* dout, const T* inp,
                               const float* stats, const float* w, int N, int C, float* partial, size_t partial_floats,
-                              hipStream_t s, bool rms = false);  // rms: RMSNorm, db may be null
+                              hipStream_t s, bool rms = false, uint8_t* q = nullptr, int64_t ldq = 0,
+                              uint8_t* sc = nullptr);  // rms: RMSNorm, db may be null; q: MX codes of dres (bf16)
 // The two halves of layernorm_backward, for callers that run them on different streams.
 template <class T>
 hipError_t layernorm_backward_dx(T* dres, const T* dres_in, const T* dout, const T* inp, const float* stats,
@@ -112,7 +113,8 @@ hipError_t bias_grad(float* dbias, const T* dout, int M, int N, int64_t ld, floa
 // overwritten by (softmax(z_i) - onehot(y_i)) * dscale; padding columns V..ldz-1 zeroed.
 template <class T>
 hipError_t crossentropy_fused(T* logits, float* losses, const int32_t* targets, int N, int V, int64_t ldz,
-                              float dscale, hipStream_t s);
+                              float dscale, hipStream_t s, uint8_t* q = nullptr, int64_t ldq = 0,
+                              uint8_t* sc = nullptr);
 hipError_t mean_loss(float* loss, const float* losses, int N, hipStream_t s);
 hipError_t scaled_accumulate(float* dst, const float* src, float scale, bool first, hipStream_t s);
 // dwte[tok] += dx rows (deterministic), dwpe[t] = sum_b dx[b, t] for t < T, 0 for T <= t < P.
@@ -150,8 +152,17 @@ hipError_t splitk_reduce(float* out, const float* ws, int splits, int64_t n, int
 // sc [Kp / 128][R][4] (see GemmArgs).  Scale of a block: the smallest 2^e with
 // amax <= 448 * 2^e (e in [-127, 127], all-zero blocks -127); codes: x / 2^e rounded
 // to nearest even.
-// y [K, ldy] = x [R, ldx]^T, columns R .. Rp - 1 of y zero (bf16).
-hipError_t transpose_bf16(const bf16* x, int64_t ldx, int R, int K, bf16* y, int64_t ldy, int Rp, hipStream_t s);
+// MX codes of a weight W [R, K] (bf16): blocks along K into (q, sq) and, with qt, blocks
+// along R -- the rows of W^T, rows past R as zero -- into (qt, sqt); layouts as
+// mx_quantize's.
+// With batch > 1, `batch` equally shaped weights at the given element / byte strides
+// (one per layer) in one launch.
+struct MxWeightStrides {
+    int64_t w = 0, q = 0, sq = 0, qt = 0, sqt = 0;
+};
+hipError_t mx_weight_codes(const bf16* w, int64_t ldw, int R, int K, uint8_t* q, int64_t ldq, uint8_t* sq,
+                           uint8_t* qt, int64_t ldqt, uint8_t* sqt, hipStream_t s, int batch = 1,
+                           const MxWeightStrides& bs = MxWeightStrides{});
 hipError_t mx_quantize(const bf16* x, int64_t ldx, int R, int K, uint8_t* q, int64_t ldq, uint8_t* sc,
                        hipStream_t s);
 // C = A B^T (+ the epilogue) for MX operands: A codes [M, K] (lda bytes), B codes

@@ -379,7 +379,8 @@ template <class T, int MAXCH, int RPW>
 __global__ __launch_bounds__(512) void layernorm_backward_fused_kernel(T* dres, float* partial, const T* dres_in,
                                                                        const T* dout, const T* inp,
                                                                        const float* stats, const float* w, int N,
-                                                                       int C, bool rms) {
+                                                                       int C, bool rms, uint8_t* q, int64_t ldq,
+                                                                       uint8_t* sc) {
     constexpr int KV = Vec16<T>::N;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     float wv[MAXCH][KV], aw[MAXCH][KV], ab[MAXCH][KV];
@@ -441,11 +442,23 @@ __global__ __launch_bounds__(512) void layernorm_backward_fused_kernel(T* dres, 
 #pragma unroll
         for (int ch = 0; ch < MAXCH; ++ch) {
             const int c = (ch * 64 + lane) * KV;
-            if (c < C) {
-                float o[KV];
+            float o[KV];
 #pragma unroll
-                for (int e = 0; e < KV; ++e) o[e] = rstd * (g[ch][e] - s1 - xh[ch][e] * s2) + prev[ch][e];
-                st16(dx + c, pack16<T>(o));
+            for (int e = 0; e < KV; ++e) o[e] = c < C ? rstd * (g[ch][e] - s1 - xh[ch][e] * s2) + prev[ch][e] : 0.f;
+            if (c < C) st16(dx + c, pack16<T>(o));
+            if constexpr (sizeof(T) == 2) {
+                // MX codes of the stored row (the next input-gradient product's upstream
+                // gradient): lanes 4j .. 4j+3 a 32-block, 16j .. 16j+15 a 128-stage; the
+                // columns past C quantize as zeros
+                if (q) {  // block-uniform
+                    round_bf16_8(o);
+                    uint32_t cw[2];
+                    const uint32_t word = mx_stage_word(mx_quant8(o, cw));
+                    if (c < ldq) {
+                        *(uint2*)(q + (int64_t)row * ldq + c) = make_uint2(cw[0], cw[1]);
+                        if ((lane & 15) == 0) *(uint32_t*)(sc + ((int64_t)(c / 128) * N + row) * 4) = word;
+                    }
+                }
             }
         }
     }
@@ -469,8 +482,9 @@ __global__ __launch_bounds__(512) void layernorm_backward_fused_kernel(T* dres, 
 template <class T>
 hipError_t layernorm_backward(T* dres, const T* dres_in, float* dw, float* db, const T* dout, const T* inp,
                               const float* stats, const float* w, int N, int C, float* partial, size_t partial_floats,
-                              hipStream_t s, bool rms) {
+                              hipStream_t s, bool rms, uint8_t* q, int64_t ldq, uint8_t* sc) {
     constexpr int KV = Vec16<T>::N;
+    if (q && (sizeof(T) != 2 || !sc || ldq % 128 || ldq < C)) return hipErrorInvalidValue;
     const int ch = cdiv(C, 64 * KV);
     // rows per wave: about 256 blocks for the step's 8192 rows, fewer rows for small inputs
     int rpw = 1;
@@ -480,13 +494,17 @@ hipError_t layernorm_backward(T* dres, const T* dres_in, float* dw, float* db, c
     if ((size_t)nb * 2 * C > partial_floats || ch > 2 || (rpw != 1 && rpw != 2 && rpw != 4)) {
         hipError_t e = layernorm_backward_dx<T>(dres, dres_in, dout, inp, stats, w, N, C, s, rms);
         if (e != hipSuccess) return e;
+        if (q) {  // (codes of the written rows by the standalone quantizer)
+            if constexpr (sizeof(T) == 2) e = mx_quantize((const bf16*)dres, C, N, C, q, ldq, sc, s);
+            if (e != hipSuccess) return e;
+        }
         return layernorm_param_grads<T>(dw, db, dout, inp, stats, N, C, partial, partial_floats, s);
     }
     {
         ProfScope prof(s, "layernorm_bwd", 0, (double)N * C * sizeof(T) * (dres_in ? 4 : 3) + 8.0 * N + 8.0 * nb * C);
 #define LNB_LAUNCH(MC, R)                                                                                             \
     hipLaunchKernelGGL((layernorm_backward_fused_kernel<T, MC, R>), dim3(nb), dim3(512), 0, s, dres, partial, dres_in, \
-                       dout, inp, stats, w, N, C, rms)
+                       dout, inp, stats, w, N, C, rms, q, ldq, sc)
 #define LNB_RPW(MC)                            \
     if (rpw == 1) LNB_LAUNCH(MC, 1);           \
     else if (rpw == 2) LNB_LAUNCH(MC, 2);      \
@@ -533,7 +551,8 @@ __device__ __forceinline__ void online_merge(float& m, float& s, float m2, float
 // whose vector holds it.
 template <class T>
 __global__ __launch_bounds__(1024) void crossentropy_kernel(T* logits, float* losses, const int32_t* targets, int V,
-                                                            int64_t ldz, float dscale) {
+                                                            int64_t ldz, float dscale, uint8_t* q, int64_t ldq,
+                                                            uint8_t* sc, int nrows) {
     constexpr int KV = Vec16<T>::N;
     constexpr int REG = 64 / KV;  // 64 values per thread: V up to 65536
     constexpr float L2E = 1.4426950408889634f;
@@ -614,13 +633,39 @@ __global__ __launch_bounds__(1024) void crossentropy_kernel(T* logits, float* lo
         if (i < V) g = __builtin_amdgcn_exp2f(__builtin_fmaf(to_f32(z[i]), L2E, go)) - (i == y ? dscale : 0.f);
         z[i] = from_f32<T>(g);
     }
+    if constexpr (sizeof(T) == 2) {
+        // MX codes of the stored gradient row (the tied lm_head's input-gradient product
+        // takes them): read back from L2 once the block's stores are done, 4 threads per
+        // 32-block, 16 per 128-value stage; columns past ldz are zero
+        if (q) {  // block-uniform
+            __syncthreads();
+            const int nq = (int)(ldq / KV);
+            for (int r = 0; r < (nq + 1023) / 1024; ++r) {  // every lane runs every round
+                const int i = threadIdx.x + r * 1024;
+                float v[KV];
+                if (i < nq && (int64_t)(i + 1) * KV <= ldz) unpack16<T>(ld16(z + i * KV), v);
+                else
+#pragma unroll
+                    for (int e = 0; e < KV; ++e) v[e] = 0.f;
+                uint32_t cw[2];
+                const uint32_t word = mx_stage_word(mx_quant8(v, cw));
+                if (i < nq) {
+                    *(uint2*)(q + (int64_t)row * ldq + i * KV) = make_uint2(cw[0], cw[1]);
+                    if ((i & 15) == 0) *(uint32_t*)(sc + ((int64_t)(i / 16) * nrows + row) * 4) = word;
+                }
+            }
+        }
+    }
 }
 
 template <class T>
 hipError_t crossentropy_fused(T* logits, float* losses, const int32_t* targets, int N, int V, int64_t ldz,
-                              float dscale, hipStream_t s) {
-    ProfScope prof(s, "crossentropy", 0, 2.0 * N * ldz * sizeof(T) + 8.0 * N);
-    hipLaunchKernelGGL(crossentropy_kernel<T>, dim3(N), dim3(1024), 0, s, logits, losses, targets, V, ldz, dscale);
+                              float dscale, hipStream_t s, uint8_t* q, int64_t ldq, uint8_t* sc) {
+    if (q && (sizeof(T) != 2 || !sc || ldq % 128 || ldq < ldz || ldz % 8)) return hipErrorInvalidValue;
+    ProfScope prof(s, q ? "crossentropy_mx" : "crossentropy", 0,
+                   2.0 * N * ldz * sizeof(T) + 8.0 * N + (q ? N * ldq * (1 + 1 / 32.) : 0.0));
+    hipLaunchKernelGGL(crossentropy_kernel<T>, dim3(N), dim3(1024), 0, s, logits, losses, targets, V, ldz, dscale, q,
+                       ldq, sc, N);
     return hipGetLastError();
 }
 
@@ -980,13 +1025,15 @@ hipError_t splitk_reduce_bf16(bf16* C, int64_t ldc, const float* ws, int splits,
     template hipError_t layernorm_forward<T>(T*, float*, const T*, const float*, const float*, int, int,         \
                                              hipStream_t, uint8_t*, int64_t, uint8_t*, bool);                    \
     template hipError_t layernorm_backward<T>(T*, const T*, float*, float*, const T*, const T*, const float*,   \
-                                              const float*, int, int, float*, size_t, hipStream_t, bool);              \
+                                              const float*, int, int, float*, size_t, hipStream_t, bool, uint8_t*,   \
+                                              int64_t, uint8_t*);                                                     \
     template hipError_t layernorm_backward_dx<T>(T*, const T*, const T*, const T*, const float*, const float*,   \
                                                  int, int, hipStream_t, bool);                                   \
     template hipError_t layernorm_param_grads<T>(float*, float*, const T*, const T*, const float*, int, int,     \
                                                  float*, size_t, hipStream_t);                                    \
     template hipError_t bias_grad<T>(float*, const T*, int, int, int64_t, float*, size_t, hipStream_t);          \
-    template hipError_t crossentropy_fused<T>(T*, float*, const int32_t*, int, int, int64_t, float, hipStream_t); \
+    template hipError_t crossentropy_fused<T>(T*, float*, const int32_t*, int, int, int64_t, float, hipStream_t,     \
+                                              uint8_t*, int64_t, uint8_t*);                                      \
     template hipError_t encoder_backward<T>(float*, float*, const T*, const int32_t*, int, int, int, int, int*,  \
                                             int*, hipStream_t, bool, const AdamwRows&);
 GPT2_INST(float)
