@@ -6,17 +6,13 @@
 //   forward   Y  = X  W^T : A = X  (k-contiguous), B = W (k-contiguous)
 //   dX        dX = dY W   : A = dY (k-contiguous), B = W (n-contiguous)
 //   dW        dW = dY^T X : A = dY (m-contiguous), B = X (n-contiguous)
-// Tiles are staged through LDS always k-contiguous, so the MFMA fragment reads
-// are one 16-byte LDS read per lane in every layout: a k-contiguous operand is
-// copied as is, an mn-contiguous one is loaded as KV x KV blocks (KV elements
-// per 16 bytes) and transposed in registers on the way to LDS.
-//
-// MFMA use (wave64): v_mfma_f32_16x16x32_bf16 for bf16 operands and
-// v_mfma_f32_16x16x4_f32 for fp32 operands.  Lane l supplies row (l % 16) of
-// its 16-row A block and column (l % 16) of its 16-column B block, with a
-// group of k values selected by l / 16; the accumulator of lane l holds rows
-// 4*(l/16) .. +3 of column l % 16.  The reduction over k does not depend on
-// which k a lane group takes as long as A and B agree, so both read the same
+// bf16 operands go from global memory straight into LDS (buffer loads to LDS) in
+// the layout they have in memory; a k-contiguous tile is read back with
+// ds_read_b128 and an mn-contiguous one with the transposing ds_read_b64_tr_b16,
+// so no operand is transposed in registers.  bf16 products use
+// v_mfma_f32_32x32x16_bf16, fp32 products v_mfma_f32_16x16x4_f32 on tiles staged
+// through registers.  The sum over k does not depend on which k values a lane
+// group supplies as long as A and B agree, so both operands use the same per-lane
 // k offsets.
 #include <algorithm>
 #include <mutex>
@@ -286,10 +282,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs a, int k_pe
 // exactly the valid rows of each matrix, so reads past the end return zero and
 // the K loop has no bounds checks.  One such load writes 64 consecutive 16-byte
 // LDS slots (lane order); a tile's layout is chosen by which global chunk each
-// lane fetches.  Two LDS stages: the loads for tile k+1 are in flight while tile
-// k is multiplied; one barrier per tile.
-//   k-contiguous operand: LDS row = one mn index, 64 k = 128 bytes; the 16-byte
-//     chunk c of row r sits at slot c ^ swz(r).  Fragment reads: ds_read_b128.
+// lane fetches.  Two or three LDS stages: the loads for the next tiles are in
+// flight while tile k is multiplied; one barrier per tile.
+//   k-contiguous operand: LDS row = one mn index, BK k (64, or 32 in the
+//     half-depth instance); the 16-byte chunk c of row r sits at slot c ^ swz(r).
+//     Fragment reads: ds_read_b128.
 //   mn-contiguous operand: LDS row = one k, ROWS mn values; chunk c of row k sits
 //     at slot c ^ hsw(k).  Fragment reads: two ds_read_b64_tr_b16, which hand lane
 //     j of each 16-lane group element e of the 8-byte word addressed by lane
@@ -300,12 +297,21 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs a, int k_pe
 // of 64 read as zero (true when K % 64 == 0, or when the row padding holds zeros).
 
 
-constexpr int GBK = 64;  // k per tile
+constexpr int GBK = 64;  // k per tile of the default (and every MX) instance
 
-// k-contiguous tiles: any 8 consecutive rows read at one logical chunk (fragment
-// reads) and the 8 chunks of one row fall on distinct 16-byte bank groups.
-__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
-__device__ __forceinline__ int lds_pos(int r, int chunk) { return r * GBK + ((chunk ^ swz(r)) << 3); }
+// k-contiguous tiles of BK k per row (BK / 8 chunks of 16 bytes): chunk c of row r
+// sits at slot c ^ swz(r).  BK = 64: any 8 consecutive rows read at one logical
+// chunk (fragment reads) and the 8 chunks of one row fall on distinct 16-byte bank
+// groups.  BK = 32 (two rows per 128 bytes): the rows of any 8, and of any 16,
+// consecutive lanes of a fragment read fall on distinct 16-byte bank groups.
+template <int BK> __device__ __forceinline__ int swz(int r) {
+    static_assert(BK == 64 || BK == 32, "k per tile");
+    if constexpr (BK == 64) return (r ^ (r >> 3)) & 7;
+    else return ((r >> 1) ^ (r >> 3)) & 3;
+}
+template <int BK> __device__ __forceinline__ int lds_pos(int r, int chunk) {
+    return r * BK + ((chunk ^ swz<BK>(r)) << 3);
+}
 // mn-contiguous tiles (at least 16 chunks per row): chunk c of row k sits at slot
 // c ^ 2 (k % 4) ^ 8 ((c / 2) % 2).  The 4 consecutive k rows one 16-lane group reads
 // (32 bytes each) land on 4 distinct 32-byte bank groups, and the neighbouring group
@@ -317,15 +323,16 @@ __device__ __forceinline__ int mn_chunk(int k, int slot) {
 }
 
 
-// Per-lane global offsets of one operand tile (ROWS mn x 64 k) in 1 KB wave loads.
-template <bool KC, int ROWS, int NW>
+// Per-lane global offsets of one operand tile (ROWS mn x BK k) in 1 KB wave loads.
+template <bool KC, int ROWS, int NW, int BK = GBK>
 struct DmaTile {
-    static constexpr int NI = ROWS * GBK * 2 / 1024;  // wave loads per tile
+    static constexpr int NI = ROWS * BK * 2 / 1024;  // wave loads per tile
     static_assert(NI % NW == 0, "wave loads per tile must divide among the waves");
     static constexpr int PW = NI / NW;
     static constexpr int CPR = ROWS / 8;           // mn-contiguous: chunks per k row
     static_assert(KC || CPR >= 16, "mn-contiguous tiles need at least 16 chunks per row");
-    static constexpr int RPI = KC ? 8 : 64 / CPR;  // rows per wave load
+    static constexpr int KCH = BK / 8;             // k-contiguous: chunks per mn row
+    static constexpr int RPI = KC ? 64 / KCH : 64 / CPR;  // rows per wave load
     uint32_t voff[PW];
     uint32_t kstep;  // bytes per k element
     __device__ __forceinline__ void init(int wave, int lane, int row0, int64_t ld) {
@@ -333,8 +340,8 @@ struct DmaTile {
         for (int j = 0; j < PW; ++j) {
             const int q = wave + NW * j;
             if constexpr (KC) {
-                const int r = q * 8 + (lane >> 3);
-                const int c = (lane & 7) ^ swz(r);
+                const int r = q * RPI + (int)((unsigned)lane / KCH);
+                const int c = (lane & (KCH - 1)) ^ swz<BK>(r);
                 voff[j] = (uint32_t)(((int64_t)(row0 + r) * ld + c * 8) * 2);
             } else {
                 const int kr = q * RPI + lane / CPR;
@@ -357,10 +364,10 @@ __device__ __forceinline__ void dma_issue(const dsc_t& d, uint32_t wtile, const 
 
 // Byte offsets in a tile of the MFMA fragment at mn offset f0, k slice ks
 // (lane l: mn f0 + l % 32, k 16 ks + 8 (l / 32) .. +7).
-template <bool KC, int ROWS>
+template <bool KC, int ROWS, int BK = GBK>
 __device__ __forceinline__ void frag_offsets(int lane, int f0, int ks, int* o) {
     if constexpr (KC) {
-        o[0] = lds_pos(f0 + (lane & 31), 2 * ks + (lane >> 5)) * 2;
+        o[0] = lds_pos<BK>(f0 + (lane & 31), 2 * ks + (lane >> 5)) * 2;
         o[1] = 0;
     } else {
         const int g = lane >> 4, i = lane & 15;
@@ -412,15 +419,20 @@ __device__ __forceinline__ bool tile_of_block(int bid, int tiles_m, int tiles_n,
 // scale words of its rows (1 KB for A, 1 KB for B), loaded by waves 0 and 1.
 // XTRA: the bias epilogue's options (GemmArgs rope / swiglu / swiglu_gu) are compiled in
 // only for the products that use them.
-template <bool AK, bool BKC, int EPI, int BM, int BN, int WM, int WN, int ST = 2, bool MX = false, bool XTRA = false>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a, int k_per_split, int64_t split_stride,
-                                                                 uint32_t a_bytes, uint32_t b_bytes) {
+// BK: k per tile, 64, or 32 for the half-depth instance whose 72 KB of LDS and at most
+// 128 registers per lane let two blocks share a CU (one block's epilogue then runs
+// beside the other's main loop).
+template <bool AK, bool BKC, int EPI, int BM, int BN, int WM, int WN, int ST = 2, bool MX = false, bool XTRA = false,
+          int BK = GBK>
+__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(BK == 32 ? 4 : 2)))
+void gemm_bf16_kernel(GemmArgs a, int k_per_split, int64_t split_stride, uint32_t a_bytes, uint32_t b_bytes) {
     constexpr int NW = WM * WN, NT = 64 * NW;
     using MT = MfmaTraits<bf16>;
     constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
-    static_assert(!MX || (AK && BKC && BM <= 256 && BN <= 256 && NW >= 2), "MX: forward layout, <= 256 rows per scale load");
+    static_assert(!MX || (AK && BKC && BM <= 256 && BN <= 256 && NW >= 2 && BK == 64),
+                  "MX: forward layout, <= 256 rows per scale load, 128 codes per k-tile");
     constexpr int SCALE_ELEMS = MX ? 1024 : 0;  // 2 KB of scale words per stage
-    constexpr int SA = BM * GBK, STAGE = (BM + BN) * GBK + SCALE_ELEMS;
+    constexpr int SA = BM * BK, STAGE = (BM + BN) * BK + SCALE_ELEMS;
     constexpr int LDS_ELEMS = ST * STAGE;
     __shared__ __attribute__((aligned(16))) bf16 lds[LDS_ELEMS];
 
@@ -431,14 +443,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a, int
     const int m0 = tm * BM, n0 = tn * BN;
     const int kbeg = blockIdx.z * k_per_split;
     const int kend = min(a.K, kbeg + k_per_split);
-    const int nk = kend > kbeg ? (kend - kbeg + GBK - 1) / GBK : 0;
+    const int nk = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
     const dsc_t ra = make_dsc(a.A, a_bytes), rb = make_dsc(a.B, b_bytes);
     // MX scale words: wave 0 loads A's, wave 1 B's (64 lanes x 16 bytes = 256 rows)
     const int wv = __builtin_amdgcn_readfirstlane(wave);  // the wave index, known to be uniform
     dsc_t rsc{};
     uint32_t srow0 = 0, sstride = 0;
     if constexpr (MX) {
-        const uint32_t nstage = (uint32_t)(a.K / GBK);  // k-stages of the whole product
+        const uint32_t nstage = (uint32_t)(a.K / BK);  // k-stages of the whole product
         if (wv == 0) rsc = make_dsc(a.sa, nstage * (uint32_t)a.srows_a * 4u), srow0 = m0, sstride = (uint32_t)a.srows_a;
         if (wv == 1) rsc = make_dsc(a.sb, nstage * (uint32_t)a.srows_b * 4u), srow0 = n0, sstride = (uint32_t)a.srows_b;
     }
@@ -447,12 +459,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a, int
     auto scale_issue = [&](uint32_t wstage, int ktile) {
         if constexpr (MX) {
             if (wv < 2)
-                dma16(rsc, wstage + (uint32_t)((BM + BN) * GBK * 2), (uint32_t)lane * 16u,
+                dma16(rsc, wstage + (uint32_t)((BM + BN) * BK * 2), (uint32_t)lane * 16u,
                       ((uint32_t)ktile * sstride + srow0) * 4u);
         }
     };
-    using TA = DmaTile<AK, BM, NW>;
-    using TB = DmaTile<BKC, BN, NW>;
+    using TA = DmaTile<AK, BM, NW, BK>;
+    using TB = DmaTile<BKC, BN, NW, BK>;
     TA ta;
     TB tb;
     ta.init(wave, lane, m0, a.lda);
@@ -466,13 +478,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a, int
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-    int fa[TM][GBK / 16][2], fb[TN][GBK / 16][2];
+    int fa[TM][BK / 16][2], fb[TN][BK / 16][2];
 #pragma unroll
-    for (int ks = 0; ks < GBK / 16; ++ks) {
+    for (int ks = 0; ks < BK / 16; ++ks) {
 #pragma unroll
-        for (int i = 0; i < TM; ++i) frag_offsets<AK, BM>(lane, (wm * TM + i) * 32, ks, fa[i][ks]);
+        for (int i = 0; i < TM; ++i) frag_offsets<AK, BM, BK>(lane, (wm * TM + i) * 32, ks, fa[i][ks]);
 #pragma unroll
-        for (int j = 0; j < TN; ++j) frag_offsets<BKC, BN>(lane, (wn * TN + j) * 32, ks, fb[j][ks]);
+        for (int j = 0; j < TN; ++j) frag_offsets<BKC, BN, BK>(lane, (wn * TN + j) * 32, ks, fb[j][ks]);
     }
     // Fragments of k-slice ks + 1 are read while the MFMAs of slice ks run.
     // `dma(ks)` issues the share of the next tile's loads that goes with k-slice ks.
@@ -481,7 +493,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a, int
     // of its row's stage word shifted right by 8 g.
     auto compute_mx = [&](const bf16* st, auto&& dma) {
         typedef int v8i __attribute__((ext_vector_type(8)));
-        const uint32_t* swa = (const uint32_t*)(st + (BM + BN) * GBK);
+        const uint32_t* swa = (const uint32_t*)(st + (BM + BN) * BK);
         const uint32_t* swb = swa + 256;
         const int sh = 8 * (lane >> 5);
         uint32_t sca[TM], scb[TN];
@@ -530,9 +542,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a, int
 #pragma unroll
         for (int j = 0; j < TN; ++j) xb[0][j] = frag_read<BKC>(st + SA, fb[j][0]);
 #pragma unroll
-        for (int ks = 0; ks < GBK / 16; ++ks) {
+        for (int ks = 0; ks < BK / 16; ++ks) {
             const int cb = ks & 1, nb = cb ^ 1;
-            if (ks + 1 < GBK / 16) {
+            if (ks + 1 < BK / 16) {
 #pragma unroll
                 for (int i = 0; i < TM; ++i) xa[nb][i] = frag_read<AK>(st, fa[i][ks + 1]);
 #pragma unroll
@@ -553,8 +565,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a, int
 #pragma unroll
     for (int s0 = 0; s0 < ST - 1; ++s0)
         if (s0 < nk) {
-            const uint32_t k1 = (uint32_t)(kbeg + s0 * GBK);
-            scale_issue(lbase + s0 * STAGE * 2, kbeg / GBK + s0);
+            const uint32_t k1 = (uint32_t)(kbeg + s0 * BK);
+            scale_issue(lbase + s0 * STAGE * 2, kbeg / BK + s0);
             dma_issue<TA::PW, NW>(ra, lbase + s0 * STAGE * 2, ta.voff, k1 * ta.kstep);
             dma_issue<TB::PW, NW>(rb, lbase + (s0 * STAGE + SA) * 2, tb.voff, k1 * tb.kstep);
         }
@@ -563,7 +575,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a, int
     // 8 m values of chunk t % RCPR and adds the k rows t / RCPR + RROWS p.
     constexpr bool RS = !AK && EPI == EPI_F32;
     constexpr int RCPR = BM / 8, RROWS = NT / RCPR;
-    static_assert(!RS || (NT % RCPR == 0 && GBK % RROWS == 0), "row-sum thread mapping");
+    static_assert(!RS || (NT % RCPR == 0 && BK % RROWS == 0), "row-sum thread mapping");
     const bool do_rs = RS && a.rowsum && n0 == 0;
     float rs[8];
 #pragma unroll
@@ -579,14 +591,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a, int
         // The next tile's loads: with three or more stages they go out spread over this
         // tile's k-slices (evening out the load and LDS-write traffic); with two, the
         // one tile of slack is needed and they all go out first.
-        constexpr int SPREAD = ST >= 3 ? GBK / 16 : 1;
+        constexpr int SPREAD = ST >= 3 ? BK / 16 : 1;
         const bool more = kt + ST - 1 < nk;
         const int nst = cur == 0 ? ST - 1 : cur - 1;
         const uint32_t nxt = lbase + (uint32_t)(nst * STAGE * 2);
-        const uint32_t k1 = (uint32_t)(kbeg + (kt + ST - 1) * GBK);
+        const uint32_t k1 = (uint32_t)(kbeg + (kt + ST - 1) * BK);
         auto dma = [&](int ks) {
             if (!more) return;
-            if (ks == 0) scale_issue(nxt, kbeg / GBK + kt + ST - 1);
+            if (ks == 0) scale_issue(nxt, kbeg / BK + kt + ST - 1);
 #pragma unroll
             for (int j = 0; j < TA::PW; ++j)
                 if (j % SPREAD == ks) dma16(ra, nxt + (uint32_t)(NW * j) * 1024u, ta.voff[j], k1 * ta.kstep);
@@ -600,7 +612,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a, int
                 const bf16* at = lds + cur * STAGE;
                 const int c = tid % RCPR;
 #pragma unroll
-                for (int p = 0; p < GBK / RROWS; ++p) {
+                for (int p = 0; p < BK / RROWS; ++p) {
                     const int kr = tid / RCPR + p * RROWS;
                     float v[8];
                     unpack16<bf16>(*(const u32x4*)(at + kr * BM + mn_slot(kr, c) * 8), v);
@@ -849,6 +861,21 @@ static hipError_t launch(const GemmArgs& a, int splits, int k_per_split, int64_t
                 dim3 grid((nt + 7) / 8 * 8, 1, splits);
                 hipLaunchKernelGGL((gemm_bf16_kernel<AK, BKC, EPI, 128, 256, 2, 4, 3, false, true>), grid, dim3(512), 0,
                                    s, a, k_per_split, split_stride, (uint32_t)ab, (uint32_t)bb);
+                return hipGetLastError();
+            }
+        }
+        // GELU epilogues (c_fc forward, the GELU-input gradient) with at least 384
+        // 128 x 256 tiles: the half-depth instance (72 KB of LDS, 4 waves per SIMD)
+        // runs two blocks per CU, so one block's epilogue overlaps the other's main
+        // loop (GELU-input gradient at 8192 x 3072 x 768: 59.6 -> 50.4 us, same bits;
+        // 384 takes in the forward pass's half-batch c_fc products, which run two at a
+        // time).  Products with fewer tiles or a long K are slower with it (up to 24 %).
+        if constexpr (AK && (EPI == EPI_GELU_BWD || EPI == EPI_BIAS_GELU)) {
+            const int nt = ((a.N + 255) / 256) * ((a.M + 127) / 128);
+            if (splits == 1 && nt >= 384) {
+                hipLaunchKernelGGL((gemm_bf16_kernel<AK, BKC, EPI, 128, 256, 2, 4, 3, false, false, 32>),
+                                   dim3((nt + 7) / 8 * 8), dim3(512), 0, s, a, k_per_split, split_stride,
+                                   (uint32_t)ab, (uint32_t)bb);
                 return hipGetLastError();
             }
         }
