@@ -462,21 +462,26 @@ __global__ __launch_bounds__(512) void layernorm_backward_fused_kernel(T* dres, 
             }
         }
     }
-    __shared__ float red[8][2][MAXCH * 64 * KV];
-#pragma unroll
-    for (int ch = 0; ch < MAXCH; ++ch)
-#pragma unroll
-        for (int e = 0; e < KV; ++e) {
-            red[wave][0][(ch * 64 + lane) * KV + e] = aw[ch][e];
-            red[wave][1][(ch * 64 + lane) * KV + e] = ab[ch][e];
-        }
-    __syncthreads();
+    // The eight wave sums go through 16 KB of LDS, one (sum, chunk) pair at a time, so
+    // that a block fits beside a 144 KB matrix-product block of the other stream.
+    __shared__ float red[8][64 * KV];
     float* out = partial + (int64_t)blockIdx.x * 2 * C;
-    for (int i = threadIdx.x; i < 2 * C; i += 512) {
-        const int sidx = i / C, c = i % C;
-        out[i] = ((red[0][sidx][c] + red[1][sidx][c]) + (red[2][sidx][c] + red[3][sidx][c])) +
-                 ((red[4][sidx][c] + red[5][sidx][c]) + (red[6][sidx][c] + red[7][sidx][c]));
-    }
+#pragma unroll
+    for (int sidx = 0; sidx < 2; ++sidx)
+#pragma unroll
+        for (int ch = 0; ch < MAXCH; ++ch) {
+            if (ch * 64 * KV >= C) break;  // block-uniform
+#pragma unroll
+            for (int e = 0; e < KV; ++e) red[wave][lane * KV + e] = sidx == 0 ? aw[ch][e] : ab[ch][e];
+            __syncthreads();
+            for (int i = threadIdx.x; i < 64 * KV; i += 512) {
+                const int c = ch * 64 * KV + i;
+                if (c < C)
+                    out[sidx * C + c] = ((red[0][i] + red[1][i]) + (red[2][i] + red[3][i])) +
+                                        ((red[4][i] + red[5][i]) + (red[6][i] + red[7][i]));
+            }
+            __syncthreads();
+        }
 }
 
 template <class T>
