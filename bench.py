@@ -583,6 +583,34 @@ def mx_forward_bench(args):
     if args.kernel_table:
         with open(args.kernel_table, "w") as f:
             json.dump({"workload": w.name + "_mxfp8_forward", "profile_steps": pk, "kernels": stats}, f, indent=1)
+
+    # and of training steps with MX forward and input-gradient products (the backward's
+    # weight gradients and the optimizer stay bf16 / fp32)
+    arena.load_params(params)
+    arena.tensor(binding.T_ADAM_M).zero_()
+    arena.tensor(binding.T_ADAM_V).zero_()
+    arena.set_gemm_format(binding.GPT2_GEMM_MXFP8_DX)
+    arena.step(xt, yt, w, 1, check_ids=False)
+    torch.cuda.synchronize()
+    binding.profile(True)
+    for t in range(2, 2 + pk):
+        arena.step(xt, yt, w, t, check_ids=False)
+    torch.cuda.synchronize()
+    binding.profile(False)
+    stats_dx = sorted(binding.profile_read(), key=lambda s: -s["total_ms"])
+    tot_dx = sum(s["total_ms"] for s in stats_dx)
+    log(f"[bench] kernel profile over {pk} training steps with MX forward and input-gradient products "
+        f"({tot_dx / pk:.3f} ms/step in kernels):")
+    for s in stats_dx:
+        avg = s["total_ms"] / s["launches"]
+        tf = s["flops"] / (s["total_ms"] / 1e3) / 1e12
+        log(f"  {s['name']:<44} {s['launches']:5d} launches {s['total_ms'] / pk:7.3f} ms/step "
+            f"({100 * s['total_ms'] / tot_dx:5.1f}%) avg {avg * 1e3:8.2f} us  {tf:7.1f} TFLOP/s")
+    if args.kernel_table:
+        with open(args.kernel_table.replace(".json", "_dx_step.json"), "w") as f:
+            json.dump({"workload": w.name + "_mxfp8_dx_step", "profile_steps": pk, "kernels": stats_dx}, f, indent=1)
+    arena.set_gemm_format(binding.GPT2_GEMM_MXFP8)
+    arena.load_params(params)
     dom = next(s for s in stats if s["name"].startswith("gemm_mxfp8"))
     avg_s = dom["total_ms"] / dom["launches"] / 1e3
     ach = dom["flops"] / dom["launches"] / avg_s / 1e12
