@@ -426,6 +426,33 @@ def test_gemm_gelu_backward_epilogue():
     assert np.all(np.abs(got - ref) <= 1.13 * acc_err + 2.0 ** -8 * np.abs(ref) + 1e-6)
 
 
+def test_gemm_gelu_epilogues_with_64_code_k_tiles():
+    # At 384 or more output tiles the two GELU epilogues run with 64-code k-tiles (two
+    # blocks per CU): 4096 x 3072 x 768 has exactly 384.  Sampled rows against the oracle's
+    # product, with the tolerances of the small-shape epilogue tests above.
+    import torch
+    from transformer_lm_fwd_amd import binding as b
+    M, N, K = 4096, 3072, 768
+    announce("mx_gemm_gelu_64code_tiles", M=M, N=N, K=K)
+    ops, A, Bm = _mx_case(M, N, K, seed=23)
+    rng = np.random.default_rng(24)
+    rows = np.unique(np.r_[0, 1, M - 1, rng.integers(0, M, 48)])
+    bias = torch.tensor(rng.standard_normal(N).astype(np.float32)).cuda()
+    prod = A[rows] @ Bm.T
+    tol = _tol(A[rows], Bm, prod)
+    pre, post = b.mx_gemm(*ops, b.GPT2_EPI_BIAS_GELU, bias)
+    pre, post = to_np(pre).astype(np.float64)[rows], to_np(post).astype(np.float64)[rows]
+    pb = prod + to_np(bias).astype(np.float64)
+    assert np.all(np.abs(pre - pb) <= _tol(A[rows], Bm, pb) + 2.0 ** -8)
+    g = oracle.gelu(pb)
+    acc_err = tol - 2.0 ** -8 * np.abs(prod)
+    assert np.all(np.abs(post - g) <= 1.13 * acc_err + 2.0 ** -8 * np.abs(g) + 1e-6)
+    x = torch.tensor(rng.standard_normal((M, N)) * 2, dtype=torch.float32).to(torch.bfloat16).cuda()
+    got = to_np(b.mx_gemm(*ops, b.GPT2_EPI_GELU_BWD, None, x)).astype(np.float64)[rows]
+    ref = prod * oracle.gelu_grad(to_np(x).astype(np.float64)[rows])
+    assert np.all(np.abs(got - ref) <= 1.13 * acc_err + 2.0 ** -8 * np.abs(ref) + 1e-6)
+
+
 def test_mx_dx_transposed_weight_codes_equal_the_quantizer_of_the_transposes():
     # Under GPT2_GEMM_MXFP8_DX the forward pass's code refresh also makes the codes of
     # every weight's transpose (blocks of 32 along the layer's outputs): they must equal

@@ -432,8 +432,8 @@ void gemm_bf16_kernel(GemmArgs a, int k_per_split, int64_t split_stride, uint32_
     constexpr int NW = WM * WN, NT = 64 * NW;
     using MT = MfmaTraits<bf16>;
     constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
-    static_assert(!MX || (AK && BKC && BM <= 256 && BN <= 256 && NW >= 2 && BK == 64),
-                  "MX: forward layout, <= 256 rows per scale load, 128 codes per k-tile");
+    static_assert(!MX || (AK && BKC && BM <= 256 && BN <= 256 && NW >= 2),
+                  "MX: forward layout, <= 256 rows per scale load");
     constexpr int SCALE_ELEMS = MX ? 1024 : 0;  // 2 KB of scale words per stage
     constexpr int SA = BM * BK, STAGE = (BM + BN) * BK + SCALE_ELEMS;
     constexpr int LDS_ELEMS = ST * STAGE;
@@ -453,17 +453,18 @@ void gemm_bf16_kernel(GemmArgs a, int k_per_split, int64_t split_stride, uint32_
     dsc_t rsc{};
     uint32_t srow0 = 0, sstride = 0;
     if constexpr (MX) {
-        const uint32_t nstage = (uint32_t)(a.K / BK);  // k-stages of the whole product
-        if (wv == 0) rsc = make_dsc(a.sa, nstage * (uint32_t)a.srows_a * 4u), srow0 = m0, sstride = (uint32_t)a.srows_a;
-        if (wv == 1) rsc = make_dsc(a.sb, nstage * (uint32_t)a.srows_b * 4u), srow0 = n0, sstride = (uint32_t)a.srows_b;
+        const uint32_t nwords = (uint32_t)(a.K / GBK);  // scale words per row: one per 128 codes
+        if (wv == 0) rsc = make_dsc(a.sa, nwords * (uint32_t)a.srows_a * 4u), srow0 = m0, sstride = (uint32_t)a.srows_a;
+        if (wv == 1) rsc = make_dsc(a.sb, nwords * (uint32_t)a.srows_b * 4u), srow0 = n0, sstride = (uint32_t)a.srows_b;
     }
     // `wstage`: this wave's 1 KB slot address in the stage (stage base + wave KB), so
-    // wave 0 lands on the A scale words and wave 1 on B's
+    // wave 0 lands on the A scale words and wave 1 on B's.  With 64-code k-tiles (BK =
+    // 32) two consecutive tiles share a word; each stage holds its own copy.
     auto scale_issue = [&](uint32_t wstage, int ktile) {
         if constexpr (MX) {
             if (wv < 2)
                 dma16(rsc, wstage + (uint32_t)((BM + BN) * BK * 2), (uint32_t)lane * 16u,
-                      ((uint32_t)ktile * sstride + srow0) * 4u);
+                      ((uint32_t)ktile / (GBK / BK) * sstride + srow0) * 4u);
         }
     };
     using TA = DmaTile<AK, BM, NW, BK>;
@@ -537,6 +538,39 @@ void gemm_bf16_kernel(GemmArgs a, int k_per_split, int64_t split_stride, uint32_
             for (int j = 0; j < TN; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(xa[1][i], xb[1][j], acc[i][j], 0, 0, 2,
                                                                             (int)sca[i], 2, (int)scb[j]);
+    };
+    // MX with 64-code k-tiles: one MFMA k-slice per stage, on half `par` of the rows'
+    // 128-code scale words (lane group g's byte 2 par + g, brought to byte 0).
+    auto compute_mx64 = [&](const bf16* st, int par, auto&& dma) {
+        typedef int v8i __attribute__((ext_vector_type(8)));
+        const uint32_t* swa = (const uint32_t*)(st + (BM + BN) * BK);
+        const uint32_t* swb = swa + 256;
+        const int sh = 8 * (lane >> 5) + 16 * par;
+        uint32_t sca[TM], scb[TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) sca[i] = swa[(wm * TM + i) * 32 + (lane & 31)] >> sh;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) scb[j] = swb[(wn * TN + j) * 32 + (lane & 31)] >> sh;
+        v8i xa[TM], xb[TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const u32x4 lo = frag_read<AK>(st, fa[i][0]), hi = frag_read<AK>(st, fa[i][1]);
+            xa[i] = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const u32x4 lo = frag_read<BKC>(st + SA, fb[j][0]), hi = frag_read<BKC>(st + SA, fb[j][1]);
+            xb[j] = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        }
+        dma(0);
+        dma(1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(xa[i], xb[j], acc[i][j], 0, 0, 0,
+                                                                            (int)sca[i], 0, (int)scb[j]);
     };
     auto compute = [&](const bf16* st, auto&& dma) {
         u32x4 xa[2][TM], xb[2][TN];
@@ -624,7 +658,8 @@ void gemm_bf16_kernel(GemmArgs a, int k_per_split, int64_t split_stride, uint32_
                 }
             }
         }
-        if constexpr (MX) compute_mx(lds + cur * STAGE, dma);
+        if constexpr (MX && BK == 32) compute_mx64(lds + cur * STAGE, (kbeg / BK + kt) & 1, dma);
+        else if constexpr (MX) compute_mx(lds + cur * STAGE, dma);
         else compute(lds + cur * STAGE, dma);
         cur = cur + 1 == ST ? 0 : cur + 1;
     }
@@ -1033,6 +1068,15 @@ static hipError_t launch_mx(const GemmArgs& e, int K, uint32_t ab, uint32_t bb, 
     if constexpr (EPI == EPI_BIAS) {
         if (e.rope || e.swiglu) {
             hipLaunchKernelGGL((gemm_bf16_kernel<true, true, EPI, 128, 256, 2, 4, 3, true, true>),
+                               dim3((nt + 7) / 8 * 8), dim3(512), 0, s, e, e.K, (int64_t)0, ab, bb);
+            return hipGetLastError();
+        }
+    }
+    // The GELU epilogues with at least 384 tiles: 64-code k-tiles (78 KB of LDS, at
+    // most 128 registers), two blocks per CU, as for the bf16 products.
+    if constexpr (EPI == EPI_BIAS_GELU || EPI == EPI_GELU_BWD) {
+        if (nt >= 384) {
+            hipLaunchKernelGGL((gemm_bf16_kernel<true, true, EPI, 128, 256, 2, 4, 3, true, false, 32>),
                                dim3((nt + 7) / 8 * 8), dim3(512), 0, s, e, e.K, (int64_t)0, ab, bb);
             return hipGetLastError();
         }
