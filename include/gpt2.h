@@ -464,9 +464,13 @@ int gpt2_mx_weight_codes(const gpt2_arena* arena, int32_t index, int32_t transpo
  * gpt2_mx_attach: codes [rows, ld] and scales [ld / 128][rows][4] of
  *  GPT2_MX_BUF_INPUT - the C-wide product inputs (LayerNorm outputs, attention
  *                      output); after a forward pass: ln_f's output,
- *  GPT2_MX_BUF_GELU  - the 4C-wide GELU output; after a forward pass: the last layer's.
+ *  GPT2_MX_BUF_GELU  - the 4C-wide GELU output; after a forward pass: the last layer's,
+ *  GPT2_MX_BUF_DY    - under GPT2_GEMM_MXFP8_DX, the upstream gradient of the input-gradient
+ *                      product at hand; after a forward pass with targets: the codes of the
+ *                      logits' gradient (ld = the vocabulary rounded up to 128), which the
+ *                      softmax-CE kernel writes beside the gradient itself.
  * rows = B*T.  Errors: GPT2_E_INVAL, GPT2_E_STATE (no MX memory). */
-enum gpt2_mx_buffer_id { GPT2_MX_BUF_INPUT = 0, GPT2_MX_BUF_GELU = 1 };
+enum gpt2_mx_buffer_id { GPT2_MX_BUF_INPUT = 0, GPT2_MX_BUF_GELU = 1, GPT2_MX_BUF_DY = 2 };
 int gpt2_mx_buffer(const gpt2_arena* arena, int32_t which, size_t* codes_offset, size_t* scales_offset,
                    int64_t* rows, int64_t* ld);
 

@@ -254,9 +254,10 @@ def test_mx_weights_follow_every_update():
 
 
 def test_producer_written_codes_equal_the_quantizer_of_the_stored_activations():
-    # In MX mode LayerNorm and the fc product's GELU epilogue write the codes of their
-    # bf16 outputs themselves; they must be exactly what gpt2_mx_quantize makes of the
-    # stored activations (and so, by the test above, what the oracle makes).
+    # In MX mode LayerNorm, the fc product's GELU epilogue and (MX dX format) the
+    # softmax-CE write the codes of their bf16 outputs themselves; they must be exactly
+    # what gpt2_mx_quantize makes of the stored tensors (and so, by the test above, what
+    # the oracle makes).
     from transformer_lm_fwd_amd import binding as b
     for m, B, T in [(ModelShape(160, 301, 2, 2, 128), 2, 64), (ModelShape(64, 97, 1, 3, 96), 3, 40)]:
         w = Workload("mx_fused", m, B, T, "bf16", "uniform", index=52)
@@ -274,6 +275,16 @@ def test_producer_written_codes_equal_the_quantizer_of_the_stored_activations():
             rq, rs = b.mx_quantize(a.tensor(b.T_FCH_GELU, m.num_layers - 1))
             np.testing.assert_array_equal(to_np(q), to_np(rq))
             np.testing.assert_array_equal(to_np(sc), to_np(rs))
+        # under GPT2_GEMM_MXFP8_DX the softmax-CE kernel writes the codes of the logits'
+        # gradient: from registers for the 128-value stages inside the full vectors of a
+        # row, by reading the row back for the rest (V = 301: stages 0-1, then stage 2)
+        a.set_gemm_format(b.GPT2_GEMM_MXFP8_DX)
+        a.forward(x, y)
+        q, sc = a.mx_buffer(b.GPT2_MX_BUF_DY)
+        z = a.tensor(b.T_LOGITS)  # [B*T, V] view of rows of the padded width (the CE writes the padding as 0)
+        rq, rs = b.mx_quantize(z.as_strided((z.shape[0], z.stride(0)), (z.stride(0), 1)))
+        np.testing.assert_array_equal(to_np(q), to_np(rq))
+        np.testing.assert_array_equal(to_np(sc), to_np(rs))
 
 
 def test_empty_calls_are_no_ops():

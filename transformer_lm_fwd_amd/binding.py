@@ -38,7 +38,7 @@ GPT2_GEMM_BF16, GPT2_GEMM_MXFP8, GPT2_GEMM_MXFP8_DX = 0, 1, 2
 GPT2_POS_LEARNED, GPT2_POS_ROTARY = 0, 1
 GPT2_BLOCK_GPT2, GPT2_BLOCK_LLAMA = 0, 1
 GPT2_EPI_BIAS, GPT2_EPI_BIAS_RES, GPT2_EPI_BIAS_GELU, GPT2_EPI_GELU_BWD = 0, 1, 2, 3
-GPT2_MX_BUF_INPUT, GPT2_MX_BUF_GELU = 0, 1
+GPT2_MX_BUF_INPUT, GPT2_MX_BUF_GELU, GPT2_MX_BUF_DY = 0, 1, 2
 
 
 class gpt2_config(ctypes.Structure):

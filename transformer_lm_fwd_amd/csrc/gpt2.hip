@@ -1225,6 +1225,11 @@ int gpt2_mx_buffer(const gpt2_arena* a, int32_t which, size_t* codes_offset, siz
         *codes_offset = a->mx_act_q;
         *scales_offset = a->mx_act_s;
         *ld = round128(4 * C);
+    } else if (which == GPT2_MX_BUF_DY) {
+        if (a->gemm_format != GPT2_GEMM_MXFP8_DX) return fail(GPT2_E_STATE, "the dY buffer exists in the MX dX format only");
+        *codes_offset = a->mx_dy_q;
+        *scales_offset = a->mx_dy_s;
+        *ld = round128(a->cfg.vocab_size);
     } else {
         return fail(GPT2_E_INVAL, "unknown MX buffer");
     }

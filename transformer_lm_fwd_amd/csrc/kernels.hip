@@ -626,6 +626,21 @@ __global__ __launch_bounds__(1024) void crossentropy_kernel(T* logits, float* lo
                 if (i * KV + e == y) v[e] -= dscale;
         }
         st16(z + i * KV, pack16<T>(v));
+        if constexpr (sizeof(T) == 2) {
+            // MX codes of a 128-value stage that lies wholly among the full vectors come
+            // from the registers (its 16 lanes all run this branch); the rest are read
+            // back below
+            if (q && (i | 15) < nvec) {
+                float t[KV];
+#pragma unroll
+                for (int e = 0; e < KV; ++e) t[e] = v[e];
+                round_bf16_8(t);
+                uint32_t cw[2];
+                const uint32_t word = mx_stage_word(mx_quant8(t, cw));
+                *(uint2*)(q + (int64_t)row * ldq + i * KV) = make_uint2(cw[0], cw[1]);
+                if ((i & 15) == 0) *(uint32_t*)(sc + ((int64_t)(i / 16) * nrows + row) * 4) = word;
+            }
+        }
     };
 #pragma unroll
     for (int r = 0; r < REG; ++r) {
@@ -640,13 +655,14 @@ __global__ __launch_bounds__(1024) void crossentropy_kernel(T* logits, float* lo
     }
     if constexpr (sizeof(T) == 2) {
         // MX codes of the stored gradient row (the tied lm_head's input-gradient product
-        // takes them): read back from L2 once the block's stores are done, 4 threads per
-        // 32-block, 16 per 128-value stage; columns past ldz are zero
+        // takes them) from the stage that holds the row's end on: read back from L2 once
+        // the block's stores are done, 4 threads per 32-block, 16 per 128-value stage;
+        // columns past ldz are zero
         if (q) {  // block-uniform
             __syncthreads();
-            const int nq = (int)(ldq / KV);
-            for (int r = 0; r < (nq + 1023) / 1024; ++r) {  // every lane runs every round
-                const int i = threadIdx.x + r * 1024;
+            const int nq = (int)(ldq / KV), nvs = nvec & ~15;
+            for (int r = 0; r < (nq - nvs + 1023) / 1024; ++r) {  // every lane runs every round
+                const int i = nvs + threadIdx.x + r * 1024;
                 float v[KV];
                 if (i < nq && (int64_t)(i + 1) * KV <= ldz) unpack16<T>(ld16(z + i * KV), v);
                 else
