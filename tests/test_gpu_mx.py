@@ -370,6 +370,34 @@ def test_mx_products_layer_by_layer(name, m, B, T):
     print(f"{4 * m.num_layers + 1} MX products within bounds (largest error / bound {worst:.3f})", flush=True)
 
 
+def test_attention_written_codes_give_the_projection_bit_for_bit():
+    # With MX products the attention kernel writes the codes of its output (head size
+    # 64, C % 128 == 0) instead of a separate quantizer pass.  The attention projection
+    # recomputed with gpt2_mx_quantize's codes of the stored output (same weight codes,
+    # bias and residual, same kernel) must give the arena's result bit for bit.
+    import torch
+    from transformer_lm_fwd_amd import binding as b
+    for name, m, B, T in [("small", ModelShape(160, 301, 2, 2, 128), 2, 64),
+                          ("gpt2_124m", synth.WORKLOADS["gpt2_124m_b8t1024_bf16"].model, 2, 128)]:
+        w = Workload(f"mx_attcodes_{name}", m, B, T, "bf16", "uniform", index=57)
+        announce(f"mx_attention_codes_{name}", C=m.channels, NH=m.num_heads, B=B, T=T)
+        params = rand_params(m, seed=57) if name == "small" else synth.init_params(m)
+        x, _ = synth.inputs_targets(w)
+        a = gpu_arena(w, params)
+        a.set_gemm_format(b.GPT2_GEMM_MXFP8)
+        a.forward(x)
+        offs = synth.param_offsets(m)
+        for l in range(m.num_layers):
+            o, n = offs[f"h{l}.proj.b"]
+            bias = torch.tensor(np.asarray(params[o:o + n], dtype=np.float32)).cuda()
+            xin = a.tensor(b.T_ENCODED) if l == 0 else a.tensor(b.T_RESIDUAL3, l - 1)
+            qa, sa = b.mx_quantize(a.tensor(b.T_ATTY, l))
+            qb, sb = a.mx_weight_codes(4 * l + 1)
+            got = b.mx_gemm(qa, sa, qb, sb, b.GPT2_EPI_BIAS_RES, bias, xin)
+            np.testing.assert_array_equal(to_np(got), to_np(a.tensor(b.T_RESIDUAL2, l)))
+        a.close()
+
+
 @pytest.mark.parametrize("B,T", [(1, 1), (3, 37)])
 def test_mx_forward_single_position_and_ragged_rows(B, T):
     # B*T = 1 and 111 rows: one partial 128-row tile of every MX product

@@ -274,9 +274,16 @@ static hipError_t attn_bwd_hs(T* dqkv, float* dsum, const T* dout, const T* out,
 }
 
 template <class T>
-hipError_t attention_forward(T* out, float* lse, const T* qkv, int B, int T_, int C, int NH, hipStream_t s) {
+hipError_t attention_forward(T* out, float* lse, const T* qkv, int B, int T_, int C, int NH, hipStream_t s,
+                             uint8_t* q, int64_t ldq, uint8_t* sc, bool* coded) {
+    if (coded) *coded = false;
     if constexpr (sizeof(T) == 2) {
-        if (C / NH == 64) return attention_forward_mfma64(out, lse, qkv, B, T_, C, NH, s);
+        if (C / NH == 64) {
+            const bool codes = q && sc && C % 128 == 0 && ldq >= C && ldq % 16 == 0;
+            if (coded) *coded = codes;
+            return attention_forward_mfma64(out, lse, qkv, B, T_, C, NH, s, codes ? q : nullptr, ldq,
+                                            codes ? sc : nullptr);
+        }
     }
     switch (C / NH) {
         case 16: return attn_fwd_hs<T, 16>(out, lse, qkv, B, T_, C, NH, s);
@@ -302,8 +309,10 @@ hipError_t attention_backward(T* dqkv, float* dsum, const T* dout, const T* out,
     return hipErrorInvalidValue;
 }
 
-template hipError_t attention_forward<float>(float*, float*, const float*, int, int, int, int, hipStream_t);
-template hipError_t attention_forward<bf16>(bf16*, float*, const bf16*, int, int, int, int, hipStream_t);
+template hipError_t attention_forward<float>(float*, float*, const float*, int, int, int, int, hipStream_t, uint8_t*,
+                                             int64_t, uint8_t*, bool*);
+template hipError_t attention_forward<bf16>(bf16*, float*, const bf16*, int, int, int, int, hipStream_t, uint8_t*,
+                                            int64_t, uint8_t*, bool*);
 template hipError_t attention_backward<float>(float*, float*, const float*, const float*, const float*, const float*,
                                               int, int, int, int, hipStream_t);
 template hipError_t attention_backward<bf16>(bf16*, float*, const bf16*, const bf16*, const bf16*, const float*, int,

@@ -25,6 +25,7 @@
 
 #include "kernels.h"
 #include "lds_dma.h"
+#include "mx_quant.h"
 
 namespace gpt2 {
 namespace {
@@ -151,7 +152,10 @@ struct FragT {
 // row-wise (ds_read_b128), V^T fragments with transposed reads.
 constexpr int FST = 2;
 
-__global__ __launch_bounds__(256) void attn_fwd_mfma64(bf16* out, float* lse, const bf16* qkv, int T, int C, int NH) {
+// q, sc non-null: also the MX FP8 codes (row stride ldq bytes) and scales ([C / 128][rows][4])
+// of the stored output, for a following MX product (C % 128 == 0).
+__global__ __launch_bounds__(256) void attn_fwd_mfma64(bf16* out, float* lse, const bf16* qkv, int T, int C, int NH,
+                                                       uint8_t* q, int64_t ldq, uint8_t* sc) {
     __shared__ __attribute__((aligned(1024))) bf16 sbuf[FST][2][64 * 64];  // [stage][K | V]
     const int nqt = (T + 127) / 128;
     // blocks are dispatched x-fastest: every head's longest query tile goes first
@@ -271,6 +275,37 @@ __global__ __launch_bounds__(256) void attn_fwd_mfma64(bf16* out, float* lse, co
                 store4_bf16(y + 32 * dt + 8 * i4 + 4 * g, o[dt][4 * i4] * inv, o[dt][4 * i4 + 1] * inv,
                             o[dt][4 * i4 + 2] * inv, o[dt][4 * i4 + 3] * inv);
         if (g == 0) lse[(int64_t)bh * T + myq] = (m + __log2f(l)) / LOG2E;
+    }
+    if (q) {  // kernel-uniform
+        // A 32-value block (columns 32 dt .. +31 of this head) of the lane's query row is
+        // held by the lane (its 16 values) and the lane 32 apart (the other 16): the block
+        // maximum of the stored (bf16-rounded) values, then the lane's codes, as
+        // mx_quant8 makes them.  Every lane takes part in the exchange; rows past T store
+        // nothing.
+        const float inv = 1.0f / l;
+        const int64_t row = (int64_t)b * T + myq, nrows = (int64_t)gridDim.x / NH * T;
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) {
+            float t[16];
+            float amax = 0.f;
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                t[k] = __uint_as_float((uint32_t)f32_to_bf16_bits(o[dt][k] * inv) << 16);
+                amax = fmaxf(amax, fabsf(t[k]));
+            }
+            amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+            const int ex = mx_exponent(amax);
+            const int col = h * HS + 32 * dt;
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                int w4 = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(t[4 * i4], -ex),
+                                                         __builtin_amdgcn_ldexpf(t[4 * i4 + 1], -ex), 0, false);
+                w4 = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(t[4 * i4 + 2], -ex),
+                                                     __builtin_amdgcn_ldexpf(t[4 * i4 + 3], -ex), w4, true);
+                if (myq < T) *(uint32_t*)(q + row * ldq + col + 8 * i4 + 4 * g) = (uint32_t)w4;
+            }
+            if (g == 0 && myq < T) sc[((int64_t)(col / 128) * nrows + row) * 4 + (col % 128) / 32] = (uint8_t)(ex + 127);
+        }
     }
 }
 
@@ -523,11 +558,13 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_mfma64(bf16* dqkv, const bf16
 
 // ============================================================================ launchers
 hipError_t attention_forward_mfma64(bf16* out, float* lse, const bf16* qkv, int B, int T, int C, int NH,
-                                    hipStream_t s) {
+                                    hipStream_t s, uint8_t* q, int64_t ldq, uint8_t* sc) {
+    if (q && (!sc || C % 128 || ldq < C || ldq % 16)) return hipErrorInvalidValue;
     const double pairs = (double)B * NH * T * (T + 1) / 2;
-    ProfScope prof(s, "attn_fwd_mfma64", 4.0 * HS * pairs, 2.0 * B * T * NH * HS * 4 + 4.0 * B * NH * T);
+    ProfScope prof(s, q ? "attn_fwd_mfma64_mx" : "attn_fwd_mfma64", 4.0 * HS * pairs,
+                   2.0 * B * T * NH * HS * 4 + 4.0 * B * NH * T + (q ? (double)B * T * C * (1 + 1 / 32.) : 0.0));
     dim3 grid(B * NH, (T + 127) / 128);
-    hipLaunchKernelGGL(attn_fwd_mfma64, grid, dim3(256), 0, s, out, lse, qkv, T, C, NH);
+    hipLaunchKernelGGL(attn_fwd_mfma64, grid, dim3(256), 0, s, out, lse, qkv, T, C, NH, q, ldq, sc);
     return hipGetLastError();
 }
 

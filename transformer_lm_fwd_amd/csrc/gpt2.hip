@@ -590,12 +590,14 @@ struct Model {
                 return rc;
             if (rotary() && !fuse_rope)  // turn q and k of every head for its position (in place)
                 CHECK(rope_apply<T>(arow(x.qkv, 3 * C), 3 * C, BT, 2 * C, C / NH, S, 0, rope_tab(), false, s), "rope");
+            // (with MX products the attention kernel writes its output's codes when it can)
+            bool att_coded = false;
             CHECK(attention_forward<T>(arow(x.atty, C), f32(x.lse) + (int64_t)b0 * NH * S, arow(x.qkv, 3 * C), B, S,
-                                       C, NH, s),
+                                       C, NH, s, mi.q, mi.ld, mi.s, &att_coded),
                   "attention");
             // res2 = xin + atty W_proj^T + b
             if ((rc = fwd_gemm(arow(x.atty, C), C, lp(l, P_PROJW), 4 * l + 1, C, arow(x.res2, C), C, EPI_BIAS_RES,
-                               pb(lp(l, P_PROJB)), xin)))
+                               pb(lp(l, P_PROJB)), xin, nullptr, att_coded ? mi : MxBuf{})))
                 return rc;
             CHECK(layernorm_forward<T>(arow(x.ln2, C), frow(x.ln2s, 2), arow(x.res2, C), master(lp(l, P_LN2W)),
                                        pb(lp(l, P_LN2B)), BT, C, s, mi.q, mi.ld, mi.s, llama()),

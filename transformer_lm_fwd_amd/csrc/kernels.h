@@ -192,8 +192,11 @@ hipError_t splitk_reduce_bf16(bf16* C, int64_t ldc, const float* ws, int splits,
 
 // ---------------------------------------------------------------- attention
 // qkv [B*T, 3C] (q | k | v, head h at columns h*hs), out [B*T, C], lse fp32 [B, NH, T].
+// q, sc (bf16 only): MX FP8 codes [B*T, ldq] and scales [C / 128][B*T][4] of out, written
+// by the kernel when it can (head size 64, C % 128 == 0); *coded tells whether it did.
 template <class T>
-hipError_t attention_forward(T* out, float* lse, const T* qkv, int B, int T_, int C, int NH, hipStream_t s);
+hipError_t attention_forward(T* out, float* lse, const T* qkv, int B, int T_, int C, int NH, hipStream_t s,
+                             uint8_t* q = nullptr, int64_t ldq = 0, uint8_t* sc = nullptr, bool* coded = nullptr);
 // dqkv [B*T, 3C] (overwrite) from dout [B*T, C]; `dsum` fp32 [B, NH, T, 2] scratch.
 template <class T>
 hipError_t attention_backward(T* dqkv, float* dsum, const T* dout, const T* out, const T* qkv, const float* lse,
@@ -201,7 +204,7 @@ hipError_t attention_backward(T* dqkv, float* dsum, const T* dout, const T* out,
 
 // MFMA kernels for bf16 operands with head size 64 (used by the two above when they apply).
 hipError_t attention_forward_mfma64(bf16* out, float* lse, const bf16* qkv, int B, int T_, int C, int NH,
-                                    hipStream_t s);
+                                    hipStream_t s, uint8_t* q = nullptr, int64_t ldq = 0, uint8_t* sc = nullptr);
 hipError_t attention_backward_mfma64(bf16* dqkv, float* dsum, const bf16* dout, const bf16* out, const bf16* qkv,
                                      const float* lse, int B, int T_, int C, int NH, hipStream_t s);
 
