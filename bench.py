@@ -104,6 +104,53 @@ def cpu_baseline(w, params, x, y, rotary=False, steps=2, threads_alt=8):
                              "step_s": round(best8, 3)}}
 
 
+def vendor_gemm_bench():
+    """The vendor BLAS on the step's product shapes (plain products: no bias, residual or
+    GELU epilogue, bf16 out), 5 untimed and 20 timed calls each, HIP events around the 20."""
+    import torch
+    torch.cuda.set_device(0)
+    C, BT, V = 768, 8192, 50257
+    # name, M, N, K, form: "xwT" = X[M,K] W[N,K]^T, "dyW" = dY[M,K] W[K,N], "dyTx" = dY[K,M]^T X[K,N]
+    shapes = [("qkv forward", BT, 3 * C, C, "xwT"), ("attention projection forward", BT, C, C, "xwT"),
+              ("c_fc forward", BT, 4 * C, C, "xwT"), ("c_fc projection forward", BT, C, 4 * C, "xwT"),
+              ("lm_head forward", BT, V, C, "xwT"),
+              ("c_fc projection dX", BT, 4 * C, C, "dyW"), ("c_fc dX", BT, C, 4 * C, "dyW"),
+              ("attention projection dX", BT, C, C, "dyW"), ("qkv dX", BT, C, 3 * C, "dyW"),
+              ("lm_head dX", BT, C, V, "dyW"),
+              ("c_fc projection dW", C, 4 * C, BT, "dyTx"), ("c_fc dW", 4 * C, C, BT, "dyTx"),
+              ("attention projection dW", C, C, BT, "dyTx"), ("qkv dW", 3 * C, C, BT, "dyTx"),
+              ("lm_head dW", V, C, BT, "dyTx")]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1)
+    out = {}
+    for name, M, N, K, form in shapes:
+        def rnd(r, c):
+            return torch.randn(r, c, device="cuda", dtype=torch.bfloat16, generator=g)
+        if form == "xwT":
+            a, b = rnd(M, K), rnd(N, K)
+            f = lambda: torch.matmul(a, b.t())
+        elif form == "dyW":
+            a, b = rnd(M, K), rnd(K, N)
+            f = lambda: torch.matmul(a, b)
+        else:
+            a, b = rnd(K, M), rnd(K, N)
+            f = lambda: torch.matmul(a.t(), b)
+        for _ in range(5):
+            f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(20):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / 20
+        out[name] = {"M": M, "N": N, "K": K, "us": round(us, 1), "tflops": round(2.0 * M * N * K / us / 1e6, 1)}
+        log(f"  {name:30s} {M:6d} x {N:6d} x {K:6d}  {us:8.1f} us  {out[name]['tflops']:7.1f} TFLOP/s")
+        del a, b
+    print(json.dumps({"vendor_gemm": out, "library": "torch.matmul (bf16)", "unit": "us"}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -134,6 +181,10 @@ def main():
                          "bf16 forward (prints its own JSON line)")
     ap.add_argument("--io", action="store_true",
                     help="time the host I/O of a run: token-file batches, checkpoint write / read (own JSON line)")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="only time the vendor BLAS (torch.matmul in bf16) on the training step's fifteen product "
+                         "shapes, as a point of comparison for this library's GEMM kernels, print one JSON line "
+                         "and exit")
     ap.add_argument("--decode-batch", type=int, default=8)
     ap.add_argument("--prompt", type=int, default=512)
     args = ap.parse_args()
@@ -156,6 +207,9 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copies": 5}), flush=True)
         return
+
+    if args.vendor_gemm:
+        return vendor_gemm_bench()
 
     import synth
     from transformer_lm_fwd_amd import Arena, binding

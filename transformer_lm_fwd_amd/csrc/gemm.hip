@@ -806,6 +806,10 @@ void gemm_bf16_kernel(GemmArgs a, int k_per_split, int64_t split_stride, uint32_
                     // operands from the caches (702 -> 636 us, and the softmax-CE that reads
                     // them 332 -> 313 us)
                     if constexpr (BM == 256 && EPI == EPI_BIAS) __builtin_nontemporal_store(pack16<bf16>(v), (u32x4*)(C + o));
+                    // the GELU input, read again only by the backward pass: non-temporal too,
+                    // so the GELU output stays cached for the product that reads it next
+                    // (c_fc projection forward 52.7 -> 50.6 us in the step, -0.04 ms/step)
+                    else if constexpr (EPI == EPI_BIAS_GELU) __builtin_nontemporal_store(pack16<bf16>(v), (u32x4*)(C + o));
                     else st16(C + o, pack16<bf16>(v));
                     if constexpr (EPI == EPI_GELU_BWD) {
                         // MX codes of the stored output (the next input-gradient product's
