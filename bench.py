@@ -151,6 +151,50 @@ def vendor_gemm_bench():
     print(json.dumps({"vendor_gemm": out, "library": "torch.matmul (bf16)", "unit": "us"}), flush=True)
 
 
+def vendor_attention_bench():
+    """PyTorch's fused attention (scaled_dot_product_attention, causal, bf16, restricted to the
+    flash and memory-efficient backends so that no unfused path runs) at the step's attention
+    shape, B=8, 12 heads, T=1024, head size 64, on contiguous [B, heads, T, 64] tensors:
+    forward alone, then forward + backward, 5 untimed and 20 timed calls each."""
+    import torch
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    torch.cuda.set_device(0)
+    B, NH, T, hs = 8, 12, 1024, 64
+    g = torch.Generator(device="cuda")
+    g.manual_seed(2)
+    q, k, v, do = (torch.randn(B, NH, T, hs, device="cuda", dtype=torch.bfloat16, generator=g) for _ in range(4))
+    q.requires_grad_(True)
+    k.requires_grad_(True)
+    v.requires_grad_(True)
+    out = {}
+    with sdpa_kernel([SDPBackend.FLASH_ATTENTION, SDPBackend.EFFICIENT_ATTENTION]):
+        def fwd():
+            with torch.no_grad():
+                return torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True)
+
+        def fwd_bwd():
+            o = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True)
+            torch.autograd.grad(o, (q, k, v), do)  # fresh gradients: no accumulation kernels
+
+        for name, f in (("forward", fwd), ("forward + backward", fwd_bwd)):
+            for _ in range(5):
+                f()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(20):
+                f()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / 20
+            pairs = B * NH * T * (T + 1) / 2
+            flops = (4 if name == "forward" else 12) * hs * pairs
+            out[name] = {"us": round(us, 1), "tflops": round(flops / us / 1e6, 1)}
+            log(f"  attention {name:20s} {us:8.1f} us  {out[name]['tflops']:7.1f} TFLOP/s (causal pairs only)")
+    print(json.dumps({"vendor_attention": out, "library": "torch scaled_dot_product_attention (bf16, causal)",
+                      "shape": {"B": B, "heads": NH, "T": T, "head_size": hs}, "unit": "us"}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -185,6 +229,9 @@ def main():
                     help="only time the vendor BLAS (torch.matmul in bf16) on the training step's fifteen product "
                          "shapes, as a point of comparison for this library's GEMM kernels, print one JSON line "
                          "and exit")
+    ap.add_argument("--vendor-attention", action="store_true",
+                    help="only time PyTorch's fused causal attention (flash / memory-efficient backends, bf16) at "
+                         "the step's attention shape, forward and forward + backward, print one JSON line and exit")
     ap.add_argument("--decode-batch", type=int, default=8)
     ap.add_argument("--prompt", type=int, default=512)
     args = ap.parse_args()
@@ -210,6 +257,8 @@ def main():
 
     if args.vendor_gemm:
         return vendor_gemm_bench()
+    if args.vendor_attention:
+        return vendor_attention_bench()
 
     import synth
     from transformer_lm_fwd_amd import Arena, binding
