@@ -395,13 +395,14 @@ __device__ __forceinline__ u32x4 frag_read(const bf16* tile, const int* o) {
 // sequence, and that sequence walks groups of GROUP_M tile rows column by column: the
 // blocks an XCD runs together share A row-tiles and B column-tiles in its L2
 // instead of every XCD fetching every operand tile.  Returns false for padding.
-// GROUP_M (measured on the step's shapes): 4 for products with a short K (at most
-// 1024 per block) and at most 32 column tiles - the qkv, c_fc and c_fc-input-gradient
-// products, 5-12 % faster than with 8 - and 8 otherwise: the vocabulary-sized products
-// and the split-K weight gradients are 2-3 % slower with 4.
-__device__ __forceinline__ bool tile_of_block(int bid, int tiles_m, int tiles_n, int k_per_block, int& tm, int& tn) {
+// GROUP_M (measured on the step's shapes): 4 for products with at most 32 column tiles
+// - the short-K qkv, c_fc and c_fc-input-gradient products 5-12 % faster than with 8,
+// and with the half-depth weight-gradient instance the long-K ones too (tied-embedding
+// dX 585 -> 554 us, -0.09 ms/step over two boxes) - and 8 for the vocabulary-wide
+// lm_head forward.
+__device__ __forceinline__ bool tile_of_block(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
     constexpr int XCDS = 8;
-    const int GROUP_M = (k_per_block <= 1024 && tiles_n <= 32) ? 4 : 8;
+    const int GROUP_M = tiles_n <= 32 ? 4 : 8;
     const int nt = tiles_m * tiles_n, per = (nt + XCDS - 1) / XCDS;
     const int t = (bid % XCDS) * per + bid / XCDS;
     if (t >= nt) return false;
@@ -442,7 +443,7 @@ void gemm_bf16_kernel(GemmArgs a, int k_per_split, int64_t split_stride, uint32_
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
     int tm, tn;
-    if (!tile_of_block(blockIdx.x, (a.M + BM - 1) / BM, (a.N + BN - 1) / BN, min(a.K, k_per_split), tm, tn)) return;
+    if (!tile_of_block(blockIdx.x, (a.M + BM - 1) / BM, (a.N + BN - 1) / BN, tm, tn)) return;
     const int m0 = tm * BM, n0 = tn * BN;
     const int kbeg = blockIdx.z * k_per_split;
     const int kend = min(a.K, kbeg + k_per_split);
